@@ -1,0 +1,31 @@
+"""KV compaction of the accepted path (oracle; test infrastructure only).
+
+The accepted tokens are recorded for the next round (EAGLE-p2 §3 EAGLE:
+accepted tokens and their features are recorded for subsequent drafting).
+With the tree's keys/values written at cache slots [L, L+N), recording the
+accepted path [0, a1, ..., am] means slot L+j takes the contents of slot
+L+path[j] for j = 0..m, and the committed length becomes L+m+1.
+
+Written as an out-of-place gather from the untouched input, so there is no
+question of reading a slot after it was overwritten.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def kv_compact(k_cache, v_cache, kv_len, kv_src, accept_len):
+    """k_cache/v_cache [B, Hkv, Lmax, d] (any dtype), kv_src [B, N] (absolute
+    source slots, -1 padded), accept_len [B].  Returns (k, v, new_kv_len)."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    new_len = np.array(kv_len, dtype=np.int32, copy=True)
+    for b in range(k_out.shape[0]):
+        L = int(kv_len[b])
+        m = int(accept_len[b])
+        for j in range(m + 1):
+            src = int(kv_src[b][j])
+            k_out[b, :, L + j] = k_cache[b, :, src]
+            v_out[b, :, L + j] = v_cache[b, :, src]
+        new_len[b] = L + m + 1
+    return k_out, v_out, new_len
