@@ -1,0 +1,253 @@
+"""Benchmark of the tree-verification step on one MI355X.
+
+One step = the whole hot path over one batch: tree mask (eagle_tree_build),
+tree attention (eagle_tree_attn), vocabulary statistics + acceptance walk
+(eagle_verify_accept) and KV compaction (eagle_kv_compact), in that data
+order on one stream.  The workload is the LLaMA2-7B-shaped layer (batch 1,
+32 MHA heads, head dim 128, 2048 committed tokens, 26-node static tree,
+vocabulary 32000), seeded and synthetic, at temperature 1 (temperature 0 is
+reported beside it).
+
+Inputs are resident in HBM before timing.  The step sequence is captured in a
+HIP graph (as a serving loop would run it) and rotates through enough copies
+of the inputs that the 256 MB Infinity Cache cannot serve repeats.  Prints
+one JSON line on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "llama2-7b"
+ROTATE_BYTES = 1 << 30
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "tree_attn_llama2-7b_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "tree_attention_verification_parent_amd", "csrc", "tree_attn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+class Step:
+    """Device buffers and pre-allocated outputs for one rotation slot."""
+
+    def __init__(self, s, torch, ev, copies: int):
+        dev = torch.device("cuda")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        bf = lambda a: t(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        cfg = s.cfg
+        self.cfg, self.T = cfg, s.T
+        self.parents = t(s.parents)
+        self.kv_len = t(s.kv_len)
+        self.tokens = t(s.tokens)
+        self.uniforms = t(s.uniforms)
+        q0, k0, v0 = bf(s.q), bf(s.k_cache), bf(s.v_cache)
+        lg0 = t(s.target_logits)
+        dp0 = t(s.draft_probs) if s.draft_probs is not None else None
+        self.slots = []
+        for i in range(copies):
+            self.slots.append(dict(
+                q=q0.clone(), k=k0.clone(), v=v0.clone(), logits=lg0.clone(),
+                draft=None if dp0 is None else dp0.clone()))
+        B, N, V = cfg.B, cfg.N, cfg.V
+        self.anc = torch.empty((B, N), dtype=torch.int64, device=dev)
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.pos = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q0)
+        self.attn_ws = ev.alloc_workspace(ev.tree_attn_workspace_bytes(B, N, cfg.Hq, cfg.Hkv, cfg.d, s.Lmax))
+        self.ver_ws = ev.alloc_workspace(ev.verify_accept_workspace_bytes(B, N, V))
+        self.res = dict(
+            accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+            path=torch.empty((B, N), dtype=torch.int32, device=dev),
+            accepted_tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+            bonus=torch.empty(B, dtype=torch.int32, device=dev),
+            kv_src=torch.empty((B, N), dtype=torch.int32, device=dev))
+        self.new_len = torch.empty_like(self.kv_len)
+        self.ev = ev
+
+    def attention(self, i):
+        sl = self.slots[i % len(self.slots)]
+        self.ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
+                          workspace=self.attn_ws)
+
+    def run(self, i):
+        ev = self.ev
+        sl = self.slots[i % len(self.slots)]
+        ev.tree_build(self.parents, self.kv_len, anc=self.anc, depth=self.depth, pos=self.pos)
+        ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
+                     workspace=self.attn_ws)
+        ev.verify_accept(self.tokens, sl["draft"], sl["logits"], self.parents, self.kv_len, self.T,
+                         self.uniforms, outputs=self.res, workspace=self.ver_ws)
+        ev.kv_compact(sl["k"], sl["v"], self.kv_len, self.res["kv_src"], self.res["accept_len"],
+                      new_kv_len=self.new_len)
+
+
+def graph_of(torch, fn, count):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)  # warm the allocator / kernels outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps=1):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3  # seconds
+
+
+def measure(torch, ev, W, T, steps, warmup):
+    cfg = W.get(WORKLOAD)
+    s = W.make_step(cfg, T)
+    per_slot = cfg.attn_bytes() + 2 * cfg.vocab_bytes()
+    copies = max(2, math.ceil(ROTATE_BYTES / per_slot))
+    st = Step(s, torch, ev, copies)
+    log(f"[bench] T={T}: {copies} rotation slots of {per_slot / 1e6:.1f} MB")
+    g_warm = graph_of(torch, st.run, max(1, warmup))
+    g_step = graph_of(torch, st.run, steps)
+    time_graph(torch, g_warm)
+    t_step = time_graph(torch, g_step) / steps
+    # attention alone, same rotation, back-to-back launches in one graph
+    g_attn = graph_of(torch, st.attention, steps)
+    time_graph(torch, g_attn)
+    t_attn = time_graph(torch, g_attn) / steps
+    acc = st.res["accept_len"].cpu().numpy()
+    return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, accept_len=int(acc[0]), copies=copies)
+
+
+def cpu_baseline(W, T, budget_s=12.0):
+    """The oracle, untuned, on this host: whole steps on the same workload until
+    the time budget is spent."""
+    import oracle
+    from oracle.walk import as_arrays
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cfg = W.get(WORKLOAD)
+    s = W.make_step(cfg, T)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+        walks = oracle.verify_batch(s.tokens, s.draft_probs, s.target_logits, s.parents, s.kv_len,
+                                    T, s.uniforms)
+        a = as_arrays(walks, cfg.N)
+        oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, a["kv_src"], a["accept_len"])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=cfg.B * cfg.N * done / el, unit="tokens/s", cores=int(blas_threads),
+                kind="oracle",
+                sample=f"{done} whole steps of the {cfg.name} workload at T={T} "
+                       f"(fp64 NumPy oracle, {el:.1f} s)")
+
+
+def pmc_traffic(attn_bytes):
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    try:
+        d = json.load(open(PMC_SUMMARY))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None  # kernel changed since the counters were taken
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the verification step is built and timed "
+              "on a single MI355X (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tree_attention_verification_parent_amd as ev
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ev.lib()
+    r1 = measure(torch, ev, W, 1.0, args.steps, args.warmup)
+    r0 = measure(torch, ev, W, 0.0, args.steps, args.warmup)
+    cfg = r1["cfg"]
+    tokens = cfg.B * cfg.N
+    attn_bytes = cfg.attn_bytes()
+    achieved = attn_bytes / r1["t_attn"] / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(W, 1.0, args.cpu_budget)
+    line = {
+        "metric": "verified draft-tree tokens/sec (tree-attn+accept) at 7B shape; % HBM roofline",
+        "value": tokens / r1["t_step"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r1["t_step"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} layer verify step, T=1", "batch": cfg.B,
+                   "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.d, "kv_len": cfg.L,
+                   "tree_nodes": cfg.N, "vocab": cfg.V, "temperature": 1.0,
+                   "rotation_slots": r1["copies"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic(attn_bytes),
+                     "kernel": "tree_attn", "bytes_per_launch": attn_bytes,
+                     "us_per_launch": r1["t_attn"] * 1e6},
+        "cpu_baseline": cpu,
+        "step_hbm_frac": (attn_bytes + cfg.vocab_bytes()) / r1["t_step"] / 1e9 / HBM_PEAK_GBS,
+        "t0": {"value": tokens / r0["t_step"], "ms_per_step": r0["t_step"] * 1e3,
+               "attn_us": r0["t_attn"] * 1e6, "accept_len": r0["accept_len"]},
+        "accept_len_t1": r1["accept_len"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

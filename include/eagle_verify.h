@@ -1,0 +1,208 @@
+/*
+ * eagle_verify.h — C ABI of the tree-verification step of EAGLE-style
+ * speculative sampling, for AMD Instinct MI355X (gfx950).
+ *
+ * The step verifies a tree-structured draft with one target forward (tree
+ * attention) and then walks the tree, accepting drafted tokens with
+ * probability min(1, p/p_hat) and resampling from the adjusted distribution
+ * on rejection (EAGLE: Speculative Sampling Requires Rethinking Feature
+ * Uncertainty, paperlayer.ai summary of arXiv 2401.15077: §2 Preliminaries,
+ * §3 EAGLE, A.1 Tree Structure, A.2 Multi-Round Speculative Sampling).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers marked "device" are device (HBM) addresses on the current
+ *     HIP device; pointers marked "host" are host memory.  The caller owns
+ *     every buffer; the library never allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and return; none synchronises the host.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Layouts are row-major and contiguous, as annotated [outer, ..., inner].
+ *   - Tree topology: node 0 is the root (parent -1); for i >= 1,
+ *     0 <= parent[i] < i.  N counts the root, 1 <= N <= 64.
+ *   - Host-detectable errors (null pointers, bad sizes, unsupported shapes,
+ *     a too-small workspace) return a non-zero status before anything is
+ *     enqueued; eagle_last_error() then describes it (thread-local).
+ *   - Data errors only visible on the device (a bad parent, a kv_len that
+ *     leaves no room for the tree, a token outside the vocabulary, a
+ *     non-finite logit) never fault: the kernels stay in bounds, OR a bit
+ *     into seq_flags[b] (when seq_flags is non-NULL) and produce defined
+ *     but meaningless results for that sequence.
+ */
+#ifndef EAGLE_VERIFY_H
+#define EAGLE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define EAGLE_API __attribute__((visibility("default")))
+#else
+#define EAGLE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int eagle_status_t;
+
+#define EAGLE_OK                    0
+#define EAGLE_ERR_INVALID_ARGUMENT  1  /* null pointer, size out of range       */
+#define EAGLE_ERR_UNSUPPORTED       2  /* shape outside what the kernels cover  */
+#define EAGLE_ERR_HIP               3  /* HIP runtime error (no device, launch) */
+#define EAGLE_ERR_WORKSPACE         4  /* workspace NULL or too small           */
+
+/* Bits OR-ed into seq_flags[b] by the kernels. */
+#define EAGLE_FLAG_BAD_PARENT   1  /* parent array violates the tree rules  */
+#define EAGLE_FLAG_BAD_KV_LEN   2  /* kv_len[b] < 0 or kv_len[b] + N > Lmax */
+#define EAGLE_FLAG_BAD_TOKEN    4  /* a drafted token outside [0, V)        */
+#define EAGLE_FLAG_NONFINITE    8  /* NaN or Inf in a target logit row      */
+
+/* Message for the last non-zero status returned on this thread. */
+EAGLE_API const char* eagle_last_error(void);
+
+/* Version of this ABI (incremented on any signature change). */
+EAGLE_API int eagle_abi_version(void);
+
+/*
+ * Host-only check of parent arrays (host [B, N] int32).  Returns EAGLE_OK or
+ * EAGLE_ERR_INVALID_ARGUMENT naming the first offending (b, i).  Touches no
+ * device.
+ */
+EAGLE_API eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B, int N);
+
+/*
+ * Zero-fill `bytes` of device memory at `ptr` with a kernel (no memset node,
+ * so it may be captured in a HIP graph).  Workspaces must be zero before
+ * their first use; every call that uses one leaves it zero again.
+ */
+EAGLE_API eagle_status_t eagle_workspace_clear(void* ptr, size_t bytes, void* stream);
+
+/*
+ * Tree mask builder.  Each drafted node attends to its ancestors (EAGLE,
+ * paperlayer.ai summary, §3 EAGLE: tree attention; A.1 Tree Structure).
+ *
+ *   parents  device [B, N] int32
+ *   kv_len   device [B] int32 or NULL: committed length L of each sequence
+ *   anc      device [B, N] uint64 out: bit j of anc[b, i] set iff node j lies
+ *            on the path root..i (i included)
+ *   depth    device [B, N] int32 out or NULL: depth of node i (root 0)
+ *   pos      device [B, N] int32 out or NULL: L + depth (position id of node
+ *            i, for the caller's rotary embedding); needs kv_len
+ *   seq_flags device [B] int32 or NULL (EAGLE_FLAG_BAD_PARENT)
+ * A bad parent is treated as the root, so anc stays within [0, N).
+ */
+EAGLE_API eagle_status_t eagle_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
+                                uint64_t* anc, int32_t* depth, int32_t* pos,
+                                int32_t* seq_flags, void* stream);
+
+/*
+ * Workspace bytes eagle_tree_attn needs for this shape (a function of the
+ * shape alone, so it can be sized once per model).
+ */
+EAGLE_API size_t eagle_tree_attn_workspace(int B, int N, int Hq, int Hkv, int d, int Lmax);
+
+/*
+ * Tree attention: every draft node against the committed KV cache and its
+ * own ancestors, in one pass (EAGLE, paperlayer.ai summary, §2 Preliminaries
+ * and §3 EAGLE: the target verifies the whole tree in a single forward).
+ *
+ * For sequence b, node i, query head h (KV head g = h * Hkv / Hq):
+ *   keys  J = {0 .. L-1} U {L + j : bit j of anc[b, i]},  L = kv_len[b]
+ *   out[b, i, h] = sum_{k in J} softmax_k(sm_scale * q.K[g, k]) V[g, k]
+ *
+ *   q        device [B, N, Hq, d] bf16
+ *   k_cache  device [B, Hkv, Lmax, d] bf16; slots [L, L+N) hold the tree's
+ *   v_cache           own keys/values (written by the caller)
+ *   kv_len   device [B] int32; needs 0 <= L and L + N <= Lmax
+ *   anc      device [B, N] uint64 from eagle_tree_build
+ *   sm_scale softmax scale; <= 0 selects 1/sqrt(d)
+ *   out      device [B, N, Hq, d] bf16 (round to nearest even); fp32 inside
+ *   workspace device, eagle_tree_attn_workspace() bytes, zero before first use
+ *   seq_flags device [B] int32 or NULL (EAGLE_FLAG_BAD_KV_LEN; that
+ *            sequence's output is zero)
+ * Supported: d in {64, 128}; Hq % Hkv == 0; 1 <= N <= 64; Lmax >= N.
+ */
+EAGLE_API eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                               const int32_t* kv_len, const uint64_t* anc,
+                               int B, int N, int Hq, int Hkv, int d, int Lmax, float sm_scale,
+                               uint16_t* out, void* workspace, size_t workspace_bytes,
+                               int32_t* seq_flags, void* stream);
+
+/* Workspace bytes eagle_verify_accept needs for this shape. */
+EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
+
+/*
+ * Acceptance walk over the draft tree (multi-round speculative sampling:
+ * EAGLE, paperlayer.ai summary, §2 Preliminaries and A.2; Algorithm 1's
+ * inputs are the target distribution, the candidates and their draft
+ * distributions, B Detailed results).
+ *
+ * Target distribution of node i: p_i = softmax(target_logits[b, i] / T) for
+ * T > 0, one-hot of its argmax (lowest id on ties) for T = 0.  Starting at
+ * the root, the candidates c of the current node j are tested in ascending
+ * node order against the current distribution r (initially p_j):
+ *   T > 0: ratio = r(t_c) / q_c(t_c); accept iff uniforms[b, c] < ratio
+ *          (ratio = +inf if q_c(t_c) = 0 < r(t_c)); on rejection
+ *          r <- norm(max(0, r - q_c)) (kept unchanged if that has no mass)
+ *   T = 0: accept iff t_c == argmax p_j
+ * On acceptance the walk descends to c; when a node has no candidate left
+ * the final token is drawn from r by inverse CDF with uniforms[b, 0]
+ * (T = 0: the argmax).
+ *
+ *   draft_tokens  device [B, N] int32; [b, 0] is the root token (not tested)
+ *   draft_probs   device [B, N, V] fp32; row i = distribution token i was drawn
+ *                 from (row 0 unused); may be NULL when T == 0
+ *   target_logits device [B, N, V] fp32; row i = target logits after node i
+ *   parents       device [B, N] int32
+ *   kv_len        device [B] int32 (for kv_src_slots)
+ *   temperature   >= 0, finite
+ *   uniforms      device [B, N] fp32 in [0, 1)
+ * Outputs (device):
+ *   accept_len      [B]    m = accepted draft nodes (root and final token excluded)
+ *   path            [B, N] accepted node ids, path[b, 0] = 0; -1 after m
+ *   accepted_tokens [B, N] draft_tokens of path[1..m]; -1 after m - 1
+ *   bonus_token     [B]    the final token drawn at the last accepted node
+ *   kv_src_slots    [B, N] kv_len[b] + path[b, j] for j <= m; -1 after
+ *   out_probs       [B, N, V] or NULL: p_i for every node (parity checks)
+ *   out_final_dist  [B, V] or NULL: the distribution the final token came from
+ *   out_ratio       [B, N] or NULL: ratio used for each tested node, NaN for
+ *                   untested ones (T = 0: 1 for a match, 0 otherwise)
+ *   seq_flags       [B] int32 or NULL (BAD_TOKEN, NONFINITE, BAD_PARENT)
+ * Supported: 1 <= V <= 32768; 1 <= N <= 64.
+ */
+EAGLE_API eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* draft_probs,
+                                   const float* target_logits, const int32_t* parents,
+                                   const int32_t* kv_len, int B, int N, int V, float temperature,
+                                   const float* uniforms,
+                                   int32_t* accept_len, int32_t* path, int32_t* accepted_tokens,
+                                   int32_t* bonus_token, int32_t* kv_src_slots,
+                                   float* out_probs, float* out_final_dist, float* out_ratio,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t* seq_flags, void* stream);
+
+/*
+ * KV compaction: record the accepted path in the cache (EAGLE, paperlayer.ai
+ * summary, §3 EAGLE: accepted tokens are recorded for the next round).  For
+ * every sequence b, KV head and j = 0..accept_len[b], slot kv_len[b] + j of
+ * k_cache and v_cache takes the contents of slot kv_src_slots[b, j]
+ * (in place); new_kv_len[b] = kv_len[b] + accept_len[b] + 1.
+ *
+ *   k_cache, v_cache device [B, Hkv, Lmax, d] bf16, updated in place
+ *   kv_len, kv_src_slots, accept_len: device, as produced above; source
+ *            slots must satisfy kv_len + j <= src < Lmax and increase with j
+ *            (true for every path the walk emits); others set
+ *            EAGLE_FLAG_BAD_KV_LEN and leave that sequence unchanged
+ *   new_kv_len device [B] int32 out; must not alias kv_len
+ * Supported: d in {64, 128}; 1 <= N <= 64.
+ */
+EAGLE_API eagle_status_t eagle_kv_compact(uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                const int32_t* kv_src_slots, const int32_t* accept_len,
+                                int B, int N, int Hkv, int d, int Lmax,
+                                int32_t* new_kv_len, int32_t* seq_flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE_VERIFY_H */

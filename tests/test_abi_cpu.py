@@ -1,0 +1,132 @@
+"""The C-ABI library loads on the host, exports what the header declares and
+rejects bad arguments before touching a device (no kernel launches here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tree_attention_verification_parent_amd as ev
+from tree_attention_verification_parent_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            names |= set(re.findall(r"EAGLE_API\s+[\w\s\*]+?\b(eagle_\w+)\s*\(", text))
+    return names
+
+
+def test_header_symbols_are_exported():
+    names = _declared()
+    assert {"eagle_tree_attn", "eagle_verify_accept", "eagle_kv_compact", "eagle_tree_build"} <= names
+    lib = ev.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(binding._SIGNATURES)
+
+
+def test_abi_version():
+    assert ev.abi_version() == 1
+
+
+def test_validate_tree_host():
+    ev.validate_tree_host([[-1, 0, 0, 1]])
+    ev.validate_tree_host(np.array([[-1]], dtype=np.int32))
+    with pytest.raises(ev.EagleError, match=r"parents\[1, 2\]"):
+        ev.validate_tree_host([[-1, 0, 1], [-1, 0, 2]])
+    with pytest.raises(ev.EagleError, match=r"expected -1"):
+        ev.validate_tree_host([[0, 0]])
+    with pytest.raises(ev.EagleError):
+        ev.validate_tree_host(np.full((1, 65), 0, dtype=np.int32))
+
+
+def _status(fn, *args):
+    return getattr(ev.lib(), fn)(*args)
+
+
+def test_attention_argument_errors():
+    L = ev.lib()
+    f = lambda *a: L.eagle_tree_attn(*a)
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    base = dict(B=1, N=8, Hq=4, Hkv=4, d=64, Lmax=136)
+
+    def call(ptrs=ok, ws=FAKE, ws_bytes=1 << 30, scale=0.0, **kw):
+        p = dict(base, **kw)
+        return f(*ptrs, p["B"], p["N"], p["Hq"], p["Hkv"], p["d"], p["Lmax"], scale, FAKE, ws,
+                 ws_bytes, None, None)
+
+    assert call(ptrs=(None,) + ok[1:]) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(d=96) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(N=65) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(N=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(Lmax=4) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(B=-1) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(scale=float("nan")) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    need = L.eagle_tree_attn_workspace(1, 8, 4, 4, 64, 136)
+    assert need > 0
+    assert call(ws=None) == binding.EAGLE_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == binding.EAGLE_ERR_WORKSPACE
+    assert "workspace" in L.eagle_last_error().decode()
+    assert call(B=0) == binding.EAGLE_OK  # empty batch: nothing to do
+
+
+def test_workspace_sizes():
+    L = ev.lib()
+    assert L.eagle_tree_attn_workspace(1, 26, 32, 32, 128, 2074) > 0
+    assert L.eagle_tree_attn_workspace(1, 26, 32, 32, 96, 2074) == 0
+    assert L.eagle_tree_attn_workspace(0, 26, 32, 32, 128, 2074) == 0
+    assert L.eagle_verify_accept_workspace(1, 26, 32000) >= 26 * 16
+    assert L.eagle_verify_accept_workspace(1, 26, 40000) == 0
+
+
+def test_verify_argument_errors():
+    L = ev.lib()
+
+    def call(B=1, N=8, V=1000, T=1.0, draft=FAKE, ws=FAKE, ws_bytes=1 << 30, outs=FAKE):
+        return L.eagle_verify_accept(FAKE, draft, FAKE, FAKE, FAKE, B, N, V, T, FAKE, outs, FAKE,
+                                     FAKE, FAKE, FAKE, None, None, None, ws, ws_bytes, None, None)
+
+    assert call(V=40000) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(V=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(T=-1.0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(T=float("inf")) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(draft=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(outs=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(ws=None) == binding.EAGLE_ERR_WORKSPACE
+    assert call(ws_bytes=16) == binding.EAGLE_ERR_WORKSPACE
+    assert call(N=65) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(B=0) == binding.EAGLE_OK
+
+
+def test_compact_and_build_argument_errors():
+    L = ev.lib()
+    same = ctypes.c_void_p(0x2000)
+    assert L.eagle_kv_compact(FAKE, FAKE, same, FAKE, FAKE, 1, 8, 4, 64, 136, same, None,
+                              None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert L.eagle_kv_compact(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 80, 136, FAKE, None,
+                              None) == binding.EAGLE_ERR_UNSUPPORTED
+    assert L.eagle_kv_compact(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 64, 136, FAKE, None,
+                              None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert L.eagle_tree_build(None, None, 1, 8, FAKE, None, None, None, None) == \
+        binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert L.eagle_tree_build(FAKE, None, 1, 8, FAKE, None, FAKE, None, None) == \
+        binding.EAGLE_ERR_INVALID_ARGUMENT  # pos needs kv_len
+    assert L.eagle_tree_build(FAKE, None, 1, 70, FAKE, None, None, None, None) == \
+        binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert L.eagle_workspace_clear(None, 0, None) == binding.EAGLE_OK
+    assert L.eagle_workspace_clear(None, 16, None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding._ptr(torch.zeros(3), name="x")

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP library through the C ABI against the CPU oracle.
+
+Tolerances: bf16 attention outputs within 2e-2 absolute (fp32 accumulate);
+fp32 target probabilities within 1e-5 relative; accepted path, tokens, final
+token and KV source slots bit-exact given the same uniforms, except for
+sequences where the oracle flags a draw with |u - threshold| < 1e-6, which
+are counted and reported; KV compaction bit-exact.
+"""
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verification_parent_amd as ev
+import workloads as W
+from oracle.walk import as_arrays
+from workloads import trees
+
+from gpu_util import bf, bits, compare_walks, dev, oracle_walks, run_attention, run_verify, say
+
+pytestmark = pytest.mark.gpu
+ATOL_ATTN = 2e-2
+
+
+# ---------------------------------------------------------------------------- tree mask
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_build_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    B, N = 9, int(rng.integers(1, 65))
+    parents = np.stack([trees.random_tree(rng, N, int(rng.integers(1, 64))) for _ in range(B)])
+    parents[0] = trees.chain(N)
+    parents[1] = trees.star(N)
+    kv_len = rng.integers(0, 5000, size=B).astype(np.int32)
+    say(f"tree_build seed={seed} B={B} N={N}")
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    anc, depth, pos = ev.tree_build(dev(parents), dev(kv_len), seq_flags=flags)
+    torch.cuda.synchronize()
+    ref = oracle.ancestor_masks(parents)
+    assert np.array_equal(anc.cpu().numpy().view(np.uint64), ref)
+    dref = np.stack([oracle.depths(parents[b]) for b in range(B)])
+    assert np.array_equal(depth.cpu().numpy(), dref)
+    assert np.array_equal(pos.cpu().numpy(), kv_len[:, None] + dref)
+    assert flags.cpu().numpy().sum() == 0
+
+
+def test_tree_build_flags_bad_parents():
+    parents = np.array([[-1, 0, 1, 3], [-1, 0, 0, 1], [5, 0, 1, 2]], dtype=np.int32)
+    flags = torch.zeros(3, dtype=torch.int32, device="cuda")
+    say("tree_build bad parents")
+    anc, _, _ = ev.tree_build(dev(parents), seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [ev.binding.FLAG_BAD_PARENT, 0, ev.binding.FLAG_BAD_PARENT]
+    a = anc.cpu().numpy().view(np.uint64)
+    assert int(a[0, 3]) == (1 | (1 << 3))  # bad link hangs off the root
+    assert (a < (1 << 4)).all()
+
+
+# ---------------------------------------------------------------------------- attention
+ATTN_CASES = [
+    # name, B, N, Hq, Hkv, d, kv_lens
+    ("tiny-shape", 1, 8, 4, 4, 64, [128]),
+    ("one-node", 2, 1, 4, 4, 128, [300, 0]),
+    ("ragged-mha-d128", 3, 26, 8, 8, 128, [0, 77, 531]),
+    ("gqa2-d64", 2, 13, 8, 4, 64, [200, 129]),
+    ("gqa4", 2, 26, 16, 4, 128, [300, 65]),
+    ("gqa8-N26", 2, 26, 16, 2, 128, [257, 1000]),
+    ("gqa8-N60", 1, 60, 16, 2, 128, [700]),
+    ("max-nodes", 2, 64, 4, 2, 128, [190, 3]),
+    ("wide-group", 1, 40, 32, 2, 64, [350]),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_matches_oracle(case):
+    name, B, N, Hq, Hkv, d, kv_lens = case
+    cfg = W.shrink(W.get(0), B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
+    rng = np.random.default_rng(len(name))
+    parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(B)])
+    s = W.make_step(cfg, 1.0, seed=zlib.crc32(name.encode()) % 1000, kv_lens=kv_lens, parents=parents)
+    say(f"attention {name}")
+    got, _, _, _ = run_attention(s)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "3", "7", "32"])
+def test_attention_split_counts_agree(splits, monkeypatch):
+    cfg = W.shrink(W.get(1), B=2, L=600, Hq=8, Hkv=8, V=16)
+    s = W.make_step(cfg, 1.0, seed=5, kv_lens=[600, 213])
+    monkeypatch.setenv("EAGLE_ATTN_SPLITS", splits)
+    say(f"attention splits={splits}")
+    got, _, _, _ = run_attention(s)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    assert np.abs(got - ref).max() < ATOL_ATTN
+
+
+def test_attention_chain_and_scale():
+    cfg = W.shrink(W.get(0), B=1, N=16, Hq=4, Hkv=2, d=128, V=16)
+    s = W.make_step(cfg, 1.0, seed=3, parents=trees.chain(16), kv_lens=[333])
+    say("attention chain + explicit scale")
+    got, _, _, _ = run_attention(s, sm_scale=0.05)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, sm_scale=0.05)
+    assert np.abs(got - ref).max() < ATOL_ATTN
+
+
+def test_attention_bad_kv_len_flags_and_zeroes():
+    cfg = W.shrink(W.get(0), B=2, V=16)
+    s = W.make_step(cfg, 1.0, seed=1)
+    kv = s.kv_len.copy()
+    kv[1] = s.k_cache.shape[2]  # no room for the tree
+    flags = torch.zeros(2, dtype=torch.int32, device="cuda")
+    say("attention bad kv_len")
+    anc, _, _ = ev.tree_build(dev(s.parents))
+    out = ev.tree_attn(bf(s.q), bf(s.k_cache), bf(s.v_cache), dev(kv), anc, seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [0, ev.binding.FLAG_BAD_KV_LEN]
+    assert (out[1].float().cpu().numpy() == 0).all()
+    ref = oracle.tree_attention(s.q[:1], s.k_cache[:1], s.v_cache[:1], s.kv_len[:1], s.parents[:1])
+    assert np.abs(out[:1].float().cpu().numpy() - ref).max() < ATOL_ATTN
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_attention_full_configs_sampled(idx):
+    cfg = W.get(idx)
+    s = W.make_step(cfg, cfg.temperatures[-1])
+    say(f"attention full config {cfg.name}")
+    got, _, _, _ = run_attention(s)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(idx)
+    nrow = 48
+    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.N)), int(rng.integers(cfg.Hq)))
+            for _ in range(nrow)]
+    rows += [(cfg.B - 1, cfg.N - 1, cfg.Hq - 1), (0, 0, 0)]
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, rows=rows)
+    sub = np.stack([got[b, i, h] for b, i, h in rows])
+    err = np.abs(sub - ref).max()
+    say(f"  sampled max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
+def test_attention_deterministic():
+    cfg = W.get(1)
+    s = W.make_step(cfg, 1.0)
+    say("attention determinism")
+    a, _, _, _ = run_attention(s)
+    b, _, _, _ = run_attention(s)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------- verification
+def _check_probs(gpu_probs, step):
+    B, N, V = step.target_logits.shape
+    for b in range(B):
+        for i in range(N):
+            p = oracle.target_distribution(step.target_logits[b, i], step.T)
+            np.testing.assert_allclose(gpu_probs[b, i].astype(np.float64), p, rtol=1e-5, atol=1e-35)
+
+
+@pytest.mark.parametrize("idx,T", [(0, 1.0), (1, 0.0), (1, 1.0), (2, 1.0), (3, 0.0), (3, 1.0), (4, 1.0)])
+def test_verify_full_configs(idx, T):
+    cfg = W.get(idx)
+    s = W.make_step(cfg, T, with_attention=False)
+    say(f"verify full config {cfg.name} T={T}")
+    gpu = run_verify(s, want_probs=idx <= 2)
+    walks = oracle_walks(s)
+    compared, excused = compare_walks(gpu, s, walks)
+    say(f"  compared {compared} sequences, {excused} excused near ties; "
+        f"accept_len {gpu['accept_len'].tolist()[:8]}")
+    assert compared >= 1
+    if "probs" in gpu:
+        _check_probs(gpu["probs"], s)
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 1000, 1001, 4096, 4097, 32768])
+@pytest.mark.parametrize("T", [0.0, 0.6, 1.0])
+def test_verify_vocab_sizes(V, T):
+    cfg = W.shrink(W.get(0), B=6, N=12, V=V)
+    s = W.make_step(cfg, T, seed=V * 7 + int(T * 10), with_attention=False)
+    say(f"verify V={V} T={T}")
+    gpu = run_verify(s, want_probs=True)
+    compared, excused = compare_walks(gpu, s, oracle_walks(s))
+    assert compared + excused == cfg.B
+    _check_probs(gpu["probs"], s)
+
+
+@pytest.mark.parametrize("shape", ["one-node", "chain", "star", "max"])
+def test_verify_tree_shapes(shape):
+    N = {"one-node": 1, "chain": 20, "star": 30, "max": 64}[shape]
+    par = {"one-node": trees.chain(1), "chain": trees.chain(N), "star": trees.star(N)}.get(shape)
+    cfg = W.shrink(W.get(0), B=16, N=N, V=500, sigma_d=0.3)
+    s = W.make_step(cfg, 1.0, seed=N, parents=par, with_attention=False)
+    say(f"verify tree shape {shape}")
+    gpu = run_verify(s)
+    compared, excused = compare_walks(gpu, s, oracle_walks(s))
+    assert compared >= 12
+
+
+def test_verify_zero_draft_mass_and_bad_tokens():
+    cfg = W.shrink(W.get(0), B=4, N=8, V=64)
+    s = W.make_step(cfg, 1.0, seed=9, with_attention=False)
+    # zero draft mass on the drafted token of node 1 in every sequence
+    for b in range(cfg.B):
+        s.draft_probs[b, 1, s.tokens[b, 1]] = 0.0
+    say("verify zero draft mass")
+    gpu = run_verify(s)
+    compare_walks(gpu, s, oracle_walks(s))
+    assert np.isinf(gpu["ratio"][:, 1]).all()
+    # an out-of-vocabulary token is flagged and rejected, never read out of bounds
+    s.tokens[2, 3] = 10 ** 6
+    s.tokens[3, 5] = -4
+    flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    say("verify bad tokens")
+    gpu = run_verify(s, flags=flags)
+    f = flags.cpu().numpy()
+    assert f[2] & ev.binding.FLAG_BAD_TOKEN and f[3] & ev.binding.FLAG_BAD_TOKEN
+    assert f[0] == 0 and f[1] == 0
+
+
+def test_verify_nonfinite_logits_flagged():
+    cfg = W.shrink(W.get(0), B=3, N=5, V=100)
+    s = W.make_step(cfg, 1.0, seed=2, with_attention=False)
+    s.target_logits[1, 2, 7] = np.nan
+    s.target_logits[2, 0, 0] = np.inf
+    flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    say("verify non-finite logits")
+    run_verify(s, flags=flags)
+    f = flags.cpu().tolist()
+    assert f[0] == 0 and f[1] & ev.binding.FLAG_NONFINITE and f[2] & ev.binding.FLAG_NONFINITE
+
+
+def test_verify_deterministic():
+    s = W.make_step(W.get(4), 1.0, with_attention=False)
+    say("verify determinism")
+    a = run_verify(s, want_final_dist=False)
+    b = run_verify(s, want_final_dist=False)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True)
+
+
+def test_verify_chi_square_on_gpu():
+    """Distribution preservation on the device: the first emitted token of many
+    independent tiny sequences (fresh drafts from q, fresh uniforms) follows
+    the root's target distribution."""
+    import scipy.stats
+    V, N, B = 8, 8, 200_000
+    rng = np.random.default_rng(11)
+    parents = trees.random_tree(rng, N, 4)
+    lg = (rng.standard_normal((N, V)) * 2).astype(np.float32)
+    dl = lg + rng.standard_normal((N, V)).astype(np.float32)
+    qd = np.exp(dl - dl.max(1, keepdims=True))
+    qd = (qd / qd.sum(1, keepdims=True)).astype(np.float32)
+    q = np.zeros((N, V), dtype=np.float32)
+    for c in range(1, N):
+        q[c] = qd[parents[c]]
+    toks = np.zeros((B, N), dtype=np.int32)
+    for c in range(1, N):
+        cdf = np.cumsum(q[c].astype(np.float64) / q[c].sum())
+        toks[:, c] = np.minimum(np.searchsorted(cdf, rng.random(B), side="right"), V - 1)
+    u = rng.random((B, N), dtype=np.float32)
+    say("verify chi-square B=200000")
+    res = ev.verify_accept(dev(toks), dev(np.broadcast_to(q, (B, N, V))), dev(np.broadcast_to(lg, (B, N, V))),
+                           dev(np.broadcast_to(parents, (B, N))), dev(np.zeros(B, np.int32)), 1.0, dev(u))
+    torch.cuda.synchronize()
+    m = res["accept_len"].cpu().numpy()
+    first = np.where(m >= 1, res["accepted_tokens"].cpu().numpy()[:, 0], res["bonus"].cpu().numpy())
+    p = oracle.target_distribution(lg[0], 1.0)
+    counts = np.bincount(first, minlength=V)
+    pval = scipy.stats.chisquare(counts, p * B).pvalue
+    say(f"  chi-square p-value {pval:.3g}")
+    assert pval > 1e-3
+
+
+# ---------------------------------------------------------------------------- compaction
+@pytest.mark.parametrize("idx,T", [(0, 1.0), (1, 1.0), (3, 0.0), (4, 1.0)])
+def test_full_step_with_compaction(idx, T):
+    cfg = W.get(idx)
+    s = W.make_step(cfg, T)
+    say(f"full step {cfg.name} T={T}")
+    gpu = run_verify(s, want_final_dist=False, want_ratio=False)
+    k, v = bf(s.k_cache), bf(s.v_cache)
+    new_len = ev.kv_compact(k, v, dev(s.kv_len), dev(gpu["kv_src"]), dev(gpu["accept_len"]))
+    torch.cuda.synchronize()
+    kr, vr, nl = oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, gpu["kv_src"], gpu["accept_len"])
+    assert np.array_equal(bits(k), kr)
+    assert np.array_equal(bits(v), vr)
+    assert np.array_equal(new_len.cpu().numpy(), nl)
+
+
+def test_compaction_rejects_bad_slots():
+    cfg = W.shrink(W.get(0), B=3, V=16)
+    s = W.make_step(cfg, 1.0, seed=4)
+    L = cfg.L
+    src = np.full((3, cfg.N), -1, dtype=np.int32)
+    src[0, :3] = [L, L + 2, L + 3]          # valid, overlapping source/destination
+    src[1, :3] = [L, L + 3, L + 2]          # not increasing
+    src[2, :2] = [L, L + cfg.N + 5]         # beyond Lmax
+    m = np.array([2, 2, 1], dtype=np.int32)
+    k, v = bf(s.k_cache), bf(s.v_cache)
+    flags = torch.zeros(3, dtype=torch.int32, device="cuda")
+    say("compaction bad slots")
+    nl = ev.kv_compact(k, v, dev(s.kv_len), dev(src), dev(m), seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [0, ev.binding.FLAG_BAD_KV_LEN, ev.binding.FLAG_BAD_KV_LEN]
+    assert nl.cpu().tolist() == [L + 3, L, L]
+    kb = bits(k)
+    kr, _, _ = oracle.kv_compact(s.k_cache[:1], s.v_cache[:1], s.kv_len[:1], src[:1], m[:1])
+    assert np.array_equal(kb[:1], kr)
+    assert np.array_equal(kb[1:], s.k_cache[1:])

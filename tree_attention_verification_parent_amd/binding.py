@@ -1,0 +1,214 @@
+"""Python binding of libeagle_verify.so (the C ABI in include/eagle_verify.h).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+HIP stream.  If the shared library is missing, every call raises; there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libeagle_verify.so"
+
+EAGLE_OK = 0
+EAGLE_ERR_INVALID_ARGUMENT = 1
+EAGLE_ERR_UNSUPPORTED = 2
+EAGLE_ERR_HIP = 3
+EAGLE_ERR_WORKSPACE = 4
+
+FLAG_BAD_PARENT = 1
+FLAG_BAD_KV_LEN = 2
+FLAG_BAD_TOKEN = 4
+FLAG_NONFINITE = 8
+
+
+class EagleError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"eagle status {status}: {message}")
+        self.status = status
+
+
+_LIB = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "eagle_last_error": (ctypes.c_char_p, []),
+    "eagle_abi_version": (_I, []),
+    "eagle_validate_tree_host": (_I, [_P, _I, _I]),
+    "eagle_workspace_clear": (_I, [_P, _SZ, _P]),
+    "eagle_tree_build": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P]),
+    "eagle_tree_attn_workspace": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "eagle_tree_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P]),
+    "eagle_verify_accept_workspace": (_SZ, [_I, _I, _I]),
+    "eagle_verify_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _SZ, _P, _P]),
+    "eagle_kv_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+}
+
+
+def library_path() -> str:
+    return os.environ.get("EAGLE_VERIFY_LIB") or os.path.join(PKG_DIR, LIB_NAME)
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m "
+                               "tree_attention_verification_parent_amd.build` first")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != EAGLE_OK:
+        raise EagleError(status, lib().eagle_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def abi_version() -> int:
+    return lib().eagle_abi_version()
+
+
+def validate_tree_host(parents) -> None:
+    """Host-side check of a [B, N] int32 parent array (numpy or CPU tensor)."""
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+    if arr.ndim == 1:
+        arr = arr[None]
+    B, N = arr.shape
+    _check(lib().eagle_validate_tree_host(arr.ctypes.data, B, N))
+
+
+def workspace_clear(ws: torch.Tensor, stream=None) -> None:
+    _check(lib().eagle_workspace_clear(_ptr(ws, name="workspace"), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
+
+
+def tree_build(parents: torch.Tensor, kv_len: Optional[torch.Tensor] = None, *, anc=None,
+               depth=None, pos=None, seq_flags=None, stream=None):
+    """Ancestor masks (int64 tensor holding the uint64 bits), depth and position ids."""
+    B, N = parents.shape
+    if anc is None:
+        anc = torch.empty((B, N), dtype=torch.int64, device=parents.device)
+        depth = torch.empty((B, N), dtype=torch.int32, device=parents.device)
+        if kv_len is not None:
+            pos = torch.empty((B, N), dtype=torch.int32, device=parents.device)
+    _check(lib().eagle_tree_build(_ptr(parents, torch.int32, "parents"),
+                                  _ptr(kv_len, torch.int32, "kv_len"), B, N, _ptr(anc), _ptr(depth),
+                                  _ptr(pos), _ptr(seq_flags, torch.int32, "seq_flags"),
+                                  _stream(stream)))
+    return anc, depth, pos
+
+
+def tree_attn_workspace_bytes(B, N, Hq, Hkv, d, Lmax) -> int:
+    return int(lib().eagle_tree_attn_workspace(B, N, Hq, Hkv, d, Lmax))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def tree_attn(q, k_cache, v_cache, kv_len, anc, *, sm_scale: float = 0.0, out=None,
+              workspace=None, seq_flags=None, stream=None):
+    """q [B,N,Hq,d] bf16; k/v [B,Hkv,Lmax,d] bf16; kv_len [B] int32; anc [B,N] int64."""
+    B, N, Hq, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(tree_attn_workspace_bytes(B, N, Hq, Hkv, d, Lmax), q.device)
+    _check(lib().eagle_tree_attn(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(kv_len, torch.int32, "kv_len"),
+        _ptr(anc, torch.int64, "anc"), B, N, Hq, Hkv, d, Lmax, float(sm_scale),
+        _ptr(out, torch.bfloat16, "out"), _ptr(workspace, name="workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(seq_flags, torch.int32, "seq_flags"),
+        _stream(stream)))
+    return out
+
+
+def verify_accept_workspace_bytes(B, N, V) -> int:
+    return int(lib().eagle_verify_accept_workspace(B, N, V))
+
+
+def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, temperature, uniforms,
+                  *, want_probs=False, want_final_dist=False, want_ratio=False, outputs=None,
+                  workspace=None, seq_flags=None, stream=None):
+    """Acceptance walk; returns a dict of device tensors (see include/eagle_verify.h)."""
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    o = outputs or {}
+    if not o:
+        o["accept_len"] = torch.empty(B, dtype=torch.int32, device=dev)
+        o["path"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        o["accepted_tokens"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        o["bonus"] = torch.empty(B, dtype=torch.int32, device=dev)
+        o["kv_src"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        if want_probs:
+            o["probs"] = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+        if want_final_dist:
+            o["final_dist"] = torch.empty((B, V), dtype=torch.float32, device=dev)
+        if want_ratio:
+            o["ratio"] = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(verify_accept_workspace_bytes(B, N, V), dev)
+    _check(lib().eagle_verify_accept(
+        _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(draft_probs, torch.float32, "draft_probs"),
+        _ptr(target_logits, torch.float32, "target_logits"), _ptr(parents, torch.int32, "parents"),
+        _ptr(kv_len, torch.int32, "kv_len"), B, N, V, float(temperature),
+        _ptr(uniforms, torch.float32, "uniforms"),
+        _ptr(o["accept_len"]), _ptr(o["path"]), _ptr(o["accepted_tokens"]), _ptr(o["bonus"]),
+        _ptr(o["kv_src"]), _ptr(o.get("probs")), _ptr(o.get("final_dist")), _ptr(o.get("ratio")),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
+    return o
+
+
+def kv_compact(k_cache, v_cache, kv_len, kv_src, accept_len, *, new_kv_len=None, seq_flags=None,
+               stream=None):
+    B, Hkv, Lmax, d = k_cache.shape
+    N = kv_src.shape[1]
+    if new_kv_len is None:
+        new_kv_len = torch.empty_like(kv_len)
+    _check(lib().eagle_kv_compact(
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(kv_len, torch.int32, "kv_len"), _ptr(kv_src, torch.int32, "kv_src"),
+        _ptr(accept_len, torch.int32, "accept_len"), B, N, Hkv, d, Lmax,
+        _ptr(new_kv_len, torch.int32, "new_kv_len"), _ptr(seq_flags, torch.int32, "seq_flags"),
+        _stream(stream)))
+    return new_kv_len

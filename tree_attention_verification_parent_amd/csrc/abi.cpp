@@ -1,0 +1,184 @@
+// C ABI of the verification step: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Every check here happens before anything
+// is enqueued; the kernels themselves guard what only the device can see.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "eagle_verify.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+eagle_status_t fail(eagle_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+eagle_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return EAGLE_OK;
+  return fail(EAGLE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool tree_size_ok(int N) { return N >= 1 && N <= 64; }
+
+}  // namespace
+
+extern "C" {
+
+const char* eagle_last_error(void) { return g_last_error.c_str(); }
+
+int eagle_abi_version(void) { return 1; }
+
+eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B, int N) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (B > 0 && !parents) return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents is NULL");
+  for (int b = 0; b < B; ++b) {
+    const int32_t* p = parents + (size_t)b * N;
+    if (p[0] != -1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents[%d, 0] = %d, expected -1", b, p[0]);
+    for (int i = 1; i < N; ++i)
+      if (p[i] < 0 || p[i] >= i)
+        return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents[%d, %d] = %d violates 0 <= parent < %d", b,
+                    i, p[i], i);
+  }
+  return EAGLE_OK;
+}
+
+eagle_status_t eagle_workspace_clear(void* ptr, size_t bytes, void* stream) {
+  if (bytes == 0) return EAGLE_OK;
+  if (!ptr) return fail(EAGLE_ERR_INVALID_ARGUMENT, "workspace pointer is NULL");
+  return hip_status(eagle::launch_fill_zero(ptr, bytes, as_stream(stream)), "workspace clear");
+}
+
+eagle_status_t eagle_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
+                                uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* seq_flags,
+                                void* stream) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (B == 0) return EAGLE_OK;
+  if (!parents || !anc) return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents and anc must be non-NULL");
+  if (pos && !kv_len) return fail(EAGLE_ERR_INVALID_ARGUMENT, "pos needs kv_len");
+  return hip_status(eagle::launch_tree_build(parents, kv_len, B, N, anc, depth, pos, seq_flags,
+                                             as_stream(stream)),
+                    "tree build launch");
+}
+
+static eagle_status_t check_attn_shape(int B, int N, int Hq, int Hkv, int d, int Lmax) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (Hkv < 1 || Hq < 1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (Hq % Hkv) return fail(EAGLE_ERR_UNSUPPORTED, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 64 && d != 128) return fail(EAGLE_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  if (Lmax < N) return fail(EAGLE_ERR_INVALID_ARGUMENT, "Lmax (%d) must be >= N (%d)", Lmax, N);
+  const double wgs = (double)B * Hkv * (((double)Hq / Hkv * N + 15) / 16) * 64;
+  if (wgs > 2.0e9) return fail(EAGLE_ERR_UNSUPPORTED, "problem too large for one launch");
+  return EAGLE_OK;
+}
+
+size_t eagle_tree_attn_workspace(int B, int N, int Hq, int Hkv, int d, int Lmax) {
+  if (check_attn_shape(B, N, Hq, Hkv, d, Lmax) != EAGLE_OK || B == 0) return 0;
+  return eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax));
+}
+
+eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                               const int32_t* kv_len, const uint64_t* anc, int B, int N, int Hq,
+                               int Hkv, int d, int Lmax, float sm_scale, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, int32_t* seq_flags,
+                               void* stream) {
+  eagle_status_t st = check_attn_shape(B, N, Hq, Hkv, d, Lmax);
+  if (st != EAGLE_OK) return st;
+  if (B == 0) return EAGLE_OK;
+  if (!q || !k_cache || !v_cache || !kv_len || !anc || !out)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, kv_len, anc and out must be non-NULL");
+  if (!isfinite(sm_scale)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  const eagle::AttnPlan plan = eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax);
+  const size_t need = eagle::tree_attn_workspace_bytes(plan);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EAGLE_ERR_WORKSPACE, "tree attention needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(eagle::launch_tree_attn(plan, q, k_cache, v_cache, kv_len, anc, B, N, Hq, Hkv,
+                                            Lmax, scale_log2, out, workspace, seq_flags,
+                                            as_stream(stream)),
+                    "tree attention launch");
+}
+
+static eagle_status_t check_verify_shape(int B, int N, int V) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (V < 1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "V must be >= 1 (got %d)", V);
+  if (V > 32768) return fail(EAGLE_ERR_UNSUPPORTED, "V = %d exceeds 32768", V);
+  if ((double)B * N > 1.0e8) return fail(EAGLE_ERR_UNSUPPORTED, "B * N too large");
+  return EAGLE_OK;
+}
+
+size_t eagle_verify_accept_workspace(int B, int N, int V) {
+  if (check_verify_shape(B, N, V) != EAGLE_OK || B == 0) return 0;
+  return eagle::verify_workspace_bytes(eagle::plan_verify(B, N, V));
+}
+
+eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* draft_probs,
+                                   const float* target_logits, const int32_t* parents,
+                                   const int32_t* kv_len, int B, int N, int V, float temperature,
+                                   const float* uniforms, int32_t* accept_len, int32_t* path,
+                                   int32_t* accepted_tokens, int32_t* bonus_token,
+                                   int32_t* kv_src_slots, float* out_probs, float* out_final_dist,
+                                   float* out_ratio, void* workspace, size_t workspace_bytes,
+                                   int32_t* seq_flags, void* stream) {
+  eagle_status_t st = check_verify_shape(B, N, V);
+  if (st != EAGLE_OK) return st;
+  if (!isfinite(temperature) || temperature < 0.f)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "temperature must be finite and >= 0");
+  if (B == 0) return EAGLE_OK;
+  if (!draft_tokens || !target_logits || !parents || !kv_len || !uniforms)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "draft_tokens, target_logits, parents, kv_len and uniforms must be non-NULL");
+  if (temperature > 0.f && !draft_probs)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "draft_probs is required when temperature > 0");
+  if (!accept_len || !path || !accepted_tokens || !bonus_token || !kv_src_slots)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "accept_len, path, accepted_tokens, bonus_token and kv_src_slots must be non-NULL");
+  const eagle::VerifyPlan plan = eagle::plan_verify(B, N, V);
+  const size_t need = eagle::verify_workspace_bytes(plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(EAGLE_ERR_WORKSPACE, "verification needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, target_logits, parents,
+                                         kv_len, B, N, temperature, uniforms, accept_len, path,
+                                         accepted_tokens, bonus_token, kv_src_slots, out_probs,
+                                         out_final_dist, out_ratio, workspace, seq_flags,
+                                         as_stream(stream)),
+                    "verification launch");
+}
+
+eagle_status_t eagle_kv_compact(uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                const int32_t* kv_src_slots, const int32_t* accept_len, int B,
+                                int N, int Hkv, int d, int Lmax, int32_t* new_kv_len,
+                                int32_t* seq_flags, void* stream) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (Hkv < 1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "Hkv must be >= 1");
+  if (d != 64 && d != 128) return fail(EAGLE_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  if (Lmax < N) return fail(EAGLE_ERR_INVALID_ARGUMENT, "Lmax (%d) must be >= N (%d)", Lmax, N);
+  if (B == 0) return EAGLE_OK;
+  if (!k_cache || !v_cache || !kv_len || !kv_src_slots || !accept_len || !new_kv_len)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "cache, kv_len, kv_src_slots, accept_len and new_kv_len must be non-NULL");
+  if (new_kv_len == kv_len) return fail(EAGLE_ERR_INVALID_ARGUMENT, "new_kv_len must not alias kv_len");
+  if ((double)B * Hkv > 2.0e9) return fail(EAGLE_ERR_UNSUPPORTED, "B * Hkv too large");
+  return hip_status(eagle::launch_kv_compact(k_cache, v_cache, kv_len, kv_src_slots, accept_len, B, N,
+                                             Hkv, d, Lmax, new_kv_len, seq_flags, as_stream(stream)),
+                    "kv compaction launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Host-side launchers of the gfx950 kernels (one per .hip file); the C ABI in
+// abi.cpp validates arguments and calls these.  All return a hipError_t from
+// the launch and never synchronise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eagle {
+
+hipError_t launch_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
+                             uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* flags,
+                             hipStream_t s);
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+// Tree attention -----------------------------------------------------------
+struct AttnPlan {
+  int d;
+  int G;          // query heads per KV head
+  int M;          // query rows per (b, kv head) = G * N
+  int rows_per_wg;
+  int qgroups;    // ceil(M / rows_per_wg)
+  int units;      // B * Hkv * qgroups
+  int splits;     // KV splits per unit
+  int variant;    // kernel instantiation index
+  int kt;         // keys per tile
+  size_t ws_partials;  // bytes of split partials
+  size_t ws_counters;  // bytes of per-unit counters
+};
+
+AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax);
+size_t tree_attn_workspace_bytes(const AttnPlan& p);
+
+hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* kv_len, const uint64_t* anc,
+                            int B, int N, int Hq, int Hkv, int Lmax, float scale_log2,
+                            uint16_t* out, void* ws, int32_t* flags, hipStream_t s);
+
+// Verification (vocabulary statistics + acceptance walk) -------------------
+struct VerifyPlan {
+  int V;
+  int chunks;          // vocabulary chunks per row in the statistics pass
+  int walk_threads;    // threads of the walk block
+  size_t ws_stats;     // per-row statistics
+  size_t ws_partials;  // per-chunk partial statistics
+  size_t ws_counters;  // per-row counters
+};
+
+VerifyPlan plan_verify(int B, int N, int V);
+size_t verify_workspace_bytes(const VerifyPlan& p);
+
+hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
+                         const float* logits, const int32_t* parents, const int32_t* kv_len,
+                         int B, int N, float T, const float* uniforms, int32_t* accept_len,
+                         int32_t* path, int32_t* acc_tokens, int32_t* bonus, int32_t* kv_src,
+                         float* out_probs, float* out_final, float* out_ratio, void* ws,
+                         int32_t* flags, hipStream_t s);
+
+// KV compaction ------------------------------------------------------------
+hipError_t launch_kv_compact(uint16_t* k, uint16_t* v, const int32_t* kv_len,
+                             const int32_t* kv_src, const int32_t* accept_len, int B, int N,
+                             int Hkv, int d, int Lmax, int32_t* new_len, int32_t* flags,
+                             hipStream_t s);
+
+}  // namespace eagle

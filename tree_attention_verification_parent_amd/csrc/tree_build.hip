@@ -1,0 +1,88 @@
+// Tree-mask builder: parent array -> ancestor bitmask, depth, position id.
+//
+// Each drafted node attends to its own ancestors (EAGLE, paperlayer.ai
+// summary, §3 EAGLE: tree attention; A.1 Tree Structure).  One wavefront per
+// sequence, lane i owning node i (N <= 64).  Ancestor sets come from pointer
+// jumping over the parent links: after r rounds a lane has OR-ed in the masks
+// of its 2^r nearest ancestors, so 6 rounds cover any depth below 64.
+#include "common.h"
+#include "launch.h"
+
+namespace eagle {
+
+__global__ __launch_bounds__(256) void tree_build_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ kv_len, int B, int N,
+    uint64_t* __restrict__ anc, int32_t* __restrict__ depth, int32_t* __restrict__ pos,
+    int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (b >= B) return;  // uniform per wavefront
+  const bool live = lane < N;
+  int par = live ? parents[(size_t)b * N + lane] : -1;
+  bool bad = false;
+  if (live) {
+    if (lane == 0) {
+      bad = par != -1;
+      par = -1;
+    } else if (par < 0 || par >= lane) {
+      bad = true;
+      par = 0;  // a malformed link hangs off the root, keeping the mask in range
+    }
+  }
+  uint64_t a = live ? (1ull << lane) : 0ull;
+  int cnt = par >= 0 ? 1 : 0;
+  int jump = par;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = jump >= 0 ? jump : lane;
+    const uint64_t a_j = __shfl(a, src);
+    const int cnt_j = __shfl(cnt, src);
+    const int jump_j = __shfl(jump, src);
+    if (jump >= 0) {
+      a |= a_j;
+      cnt += cnt_j;
+      jump = jump_j;
+    }
+  }
+  if (live) {
+    const size_t o = (size_t)b * N + lane;
+    anc[o] = a;
+    if (depth) depth[o] = cnt;
+    if (pos) pos[o] = kv_len[b] + cnt;
+  }
+  const uint64_t any_bad = __ballot(bad);
+  if (flags && any_bad && lane == 0) atomicOr(flags + b, EAGLE_FLAG_BAD_PARENT);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* __restrict__ p, size_t bytes) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t head = (16 - ((uintptr_t)p & 15)) & 15;
+  const size_t h = head < bytes ? head : bytes;
+  for (size_t i = tid; i < h; i += stride) p[i] = 0;
+  uint4* q = reinterpret_cast<uint4*>(p + h);
+  const size_t n16 = (bytes - h) / 16;
+  for (size_t i = tid; i < n16; i += stride) q[i] = make_uint4(0, 0, 0, 0);
+  for (size_t i = h + n16 * 16 + tid; i < bytes; i += stride) p[i] = 0;
+}
+
+hipError_t launch_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
+                             uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* flags,
+                             hipStream_t s) {
+  const int per_block = 4;
+  const int grid = (B + per_block - 1) / per_block;
+  tree_build_kernel<<<grid, per_block * kWave, 0, s>>>(parents, kv_len, B, N, anc, depth, pos,
+                                                       flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  size_t blocks = (bytes / 16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint8_t*>(ptr), bytes);
+  return hipGetLastError();
+}
+
+}  // namespace eagle

@@ -222,7 +222,8 @@ def make_step(cfg: VerifyConfig, T: float, seed: Optional[int] = None, *,
                 dl = lg.astype(np.float64) + r_drf.standard_normal(V) * cfg.sigma_d
                 if T == 0:
                     top = np.argsort(-dl, kind="stable")[: len(ch[j])]
-                    tokens[b, ch[j]] = top
+                    # more children than vocabulary entries: ranks wrap around
+                    tokens[b, ch[j]] = np.resize(top, len(ch[j]))
                 else:
                     qd = _draft_dist(dl, T).astype(np.float32)
                     pw = qd.astype(np.float64)
