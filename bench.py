@@ -150,11 +150,11 @@ def cpu_baseline(W, T, budget_s=12.0):
     the time budget is spent."""
     import oracle
     from oracle.walk import as_arrays
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+    from threadpoolctl import threadpool_limits
+    # The oracle is single-threaded Python + NumPy; pin BLAS to one thread so
+    # the reported core count is the one actually used.
+    limiter = threadpool_limits(limits=1)
+    blas_threads = 1
     cfg = W.get(WORKLOAD)
     s = W.make_step(cfg, T)
     done = 0
@@ -169,6 +169,7 @@ def cpu_baseline(W, T, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    limiter.unregister() if hasattr(limiter, "unregister") else None
     return dict(value=cfg.B * cfg.N * done / el, unit="tokens/s", cores=int(blas_threads),
                 kind="oracle",
                 sample=f"{done} whole steps of the {cfg.name} workload at T={T} "

@@ -7,25 +7,31 @@
 // KV head against L+N keys, HBM-bound on the bf16 K/V stream.
 //
 // Work decomposition
-//   unit  = (b, kv head, query group of <= RW rows); split = a contiguous range
-//   of KV tiles.  One 256-thread workgroup per (unit, split).  Workgroup ids
-//   are laid out so every split of a unit lands on one XCD (blocks go to XCDs
-//   round robin), keeping its partials and counter in that XCD's L2.
-//   Inside a workgroup the 4 waves form a WQ x WK grid: WQ waves over query
-//   blocks of 16 rows, WK waves over 32-key chunks of each tile.
+//   unit  = (b, kv head, group of RW query rows); split = a contiguous range of
+//   32-key chunks.  One 256-thread workgroup per (unit, split).  Workgroup ids
+//   are laid out so that all splits of a unit run on one XCD (blocks go to XCDs
+//   round robin), keeping a unit's partials in that XCD's caches.
 //
-// Per tile (KT keys): all 256 threads stream K and V with 16-byte coalesced
-// loads into registers (issued one tile ahead), then store K row-major and V
-// transposed into LDS, so every wave of the workgroup (all G*N queries of the
-// KV head) reuses one copy of the tile.  Each wave computes
-//   S^T[32 keys x 16 queries] = K Q^T   with v_mfma_f32_16x16x32_bf16
-//   (keys on MFMA rows; the K rows are permuted so that each lane ends up
-//    holding 8 consecutive keys of one query column),
-// applies the tree mask, runs the online softmax with cross-lane shuffles,
-// packs P^T to bf16 in registers and accumulates
-//   O^T[d x 16 queries] += V^T P^T      with the same MFMA.
-// Splits write (m, l, O) partials; the last workgroup of a unit to finish
-// (atomic ticket) merges them with log-sum-exp weights and writes bf16 output.
+// Two kernels, picked by the number of query rows per KV head:
+//   ring  (M <= 32, e.g. multi-head attention): every wave owns a private ring
+//         of 32-key chunk slots in LDS, filled by direct-to-LDS loads
+//         (global_load_lds_dwordx4) issued ahead, so the whole split is in
+//         flight from the start with no staging registers and no barriers in
+//         the main loop.  Each wave computes all query rows against its own
+//         chunks; the four waves merge at the end.
+//   tile  (larger M, grouped-query attention): the 256 threads stage each tile
+//         of keys into LDS (K row-major, V transposed) and the waves split the
+//         query rows, so one copy of the tile serves all G*N queries.
+// Both compute S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16
+// (keys on MFMA rows: the K rows are permuted so each lane ends up holding 8
+// consecutive keys of one query column, exactly the k-slots of P^T), apply the
+// tree mask, and run the online softmax with cross-lane shuffles.
+//
+// Splits publish (O / l, log2-sum-exp) partials with device-coherent stores;
+// the last split of a unit to finish (atomic ticket) merges them.  No
+// whole-cache writeback or invalidate is needed: the partial stores and loads
+// are relaxed agent-scope atomics (coherent across XCDs), and every thread
+// waits for its stores to complete before the ticket is taken.
 #include <stdlib.h>
 
 #include "common.h"
@@ -33,8 +39,517 @@
 
 namespace eagle {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* kv_len;
+  const uint64_t* anc;
+  uint16_t* out;
+  float* part_o;     // [units * splits * RW * D]  O / l of each split
+  float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
+  int32_t* counters; // [units]
+  int32_t* flags;
+  int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
+  float scale_log2;
+};
+
+// Swizzle of 16-byte slots within a key row of a 32-key chunk: slot p of row r
+// holds the global slot p ^ swz(r).  Conflict-free for both the K fragment
+// reads (8 rows {0-3, 8-11} or {4-7, 12-15}) and the transposed V reads
+// (4 consecutive rows, two adjacent slots each).
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
+
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent1(float* p, float a) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(a), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent2(float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ float load_coherent1(float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
+}
+
+// Online softmax update of one 16-query block from this lane's 8 scores
+// (already scaled to the log2 domain and masked).  Returns the bf16 P^T fragment.
+template <int NDB>
+__device__ __forceinline__ bf16x8 softmax_step(const float (&x)[8], float& m_run, float& l_run,
+                                               f32x4 (&acc)[NDB]) {
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+  float psum = 0.f;
+  bf16x8 pf;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float pj = __builtin_amdgcn_exp2f(x[j] - m_use);
+    psum += pj;
+    pf[j] = (__bf16)pj;
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+  return pf;
+}
+
+// Valid keys among key0..key0+7 as an 8-bit mask, without branches: committed
+// keys (< L) plus the ancestor bits of the query's node.  (A branchy form of
+// this test was miscompiled for the first of the eight scores.)
+__device__ __forceinline__ uint32_t key_mask8(int key0, int L, uint64_t anc) {
+  const int below = L - key0;
+  const uint32_t pre = below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
+  const int tk0 = -below;
+  const uint32_t tre = tk0 >= 0 ? (tk0 < 64 ? (uint32_t)(anc >> tk0) & 0xffu : 0u)
+                                : (tk0 > -8 ? (uint32_t)(anc << -tk0) & 0xffu : 0u);
+  return pre | tre;
+}
+
+// Write the final bf16 rows, or publish this split's partial and, when this
+// workgroup is the last split of its unit, merge all partials.  acc/m/l hold
+// the lane's query column for QBW blocks starting at row r0 of the unit.
+template <int D, int RW, int QBW>
+__device__ void finish_split(const AttnArgs& a, int unit, int split, int qgroup, int b, int kvh,
+                             bool bad, bool active, int r0, f32x4 (&acc)[QBW][D / 16],
+                             float (&m_run)[QBW], float (&l_run)[QBW], uint8_t* lds, int* s_ticket) {
+  constexpr int NDB = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int N = a.N, G = a.G, M = a.M;
+  if (a.splits == 1) {
+    if (active) {
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) {
+        const int row = qgroup * RW + r0 + qb * 16 + c;
+        if (row >= M) continue;
+        const int i = row / G;
+        const int h = kvh * G + (row - i * G);
+        uint16_t* orow = a.out + (((size_t)b * N + i) * a.Hq + h) * D;
+        const float inv = (bad || l_run[qb] == 0.f) ? 0.f : 1.f / l_run[qb];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const f32x4 o = acc[qb][db] * inv;
+          *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * g) =
+              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+      }
+    }
+    return;
+  }
+
+  // Stage this split's normalised rows in LDS (row-major fp32) so that the
+  // device-coherent stores below are fully coalesced.
+  const int rows = min(RW, M - qgroup * RW);
+  float* stage = reinterpret_cast<float*>(lds);  // [RW][D + 1]: last column = log2-sum-exp
+  constexpr int SD = D + 1;
+  if (active) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const int rl = r0 + qb * 16 + c;
+      const float inv = l_run[qb] == 0.f ? 0.f : 1.f / l_run[qb];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const f32x4 o = acc[qb][db] * inv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stage[rl * SD + db * 16 + 4 * g + e] = o[e];
+      }
+      if (g == 0) stage[rl * SD + D] = l_run[qb] == 0.f ? -INFINITY : m_run[qb] + __log2f(l_run[qb]);
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
+  for (int it = tid; it < rows * (D / 2); it += 256) {
+    const int rl = it / (D / 2), d2 = it - rl * (D / 2);
+    store_coherent2(a.part_o + (pbase + rl) * D + 2 * d2, stage[rl * SD + 2 * d2],
+                    stage[rl * SD + 2 * d2 + 1]);
+  }
+  for (int rl = tid; rl < rows; rl += 256) store_coherent1(a.part_lse + pbase + rl, stage[rl * SD + D]);
+  // The partial stores are device-coherent; waiting for them to complete
+  // before the ticket is taken orders them before it for every reader.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    *s_ticket = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*s_ticket != a.splits - 1) return;
+
+  // Last split of this unit: merge every split's partial.  Weights per row
+  // first (one coherent load per split and row), then the rows, with
+  // consecutive lanes reading consecutive float pairs.
+  const int S = a.splits;
+  const size_t ub = (size_t)unit * S * RW;
+  float* wts = stage;  // [RW][33]: 32 weights + inverse total, reuses the staging area
+  for (int rl = tid; rl < rows; rl += 256) {
+    float w[32];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < 32; ++sp) {
+      w[sp] = sp < S ? load_coherent1(a.part_lse + ub + (size_t)sp * RW + rl) : -INFINITY;
+      mt = fmaxf(mt, w[sp]);
+    }
+    const float mu = mt == -INFINITY ? 0.f : mt;
+    float tot = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < 32; ++sp) {
+      w[sp] = __builtin_amdgcn_exp2f(w[sp] - mu);
+      tot += w[sp];
+    }
+    const float inv = (bad || tot == 0.f) ? 0.f : 1.f / tot;
+#pragma unroll
+    for (int sp = 0; sp < 32; ++sp) wts[rl * 33 + sp] = w[sp] * inv;
+  }
+  __syncthreads();
+  constexpr int D2 = D / 2;
+  constexpr int BATCH = 4;  // float pairs in flight per split group per thread
+  for (int it0 = tid; it0 < rows * D2; it0 += 256 * BATCH) {
+    float ox[BATCH], oy[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) ox[k] = oy[k] = 0.f;
+    for (int sp0 = 0; sp0 < S; sp0 += 8) {
+      float2 pv[BATCH][8];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int it = it0 + k * 256;
+        const int rl = it / D2, d2 = it - (it / D2) * D2;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          pv[k][q] = (it < rows * D2 && sp0 + q < S)
+                         ? load_coherent2(a.part_o + (ub + (size_t)(sp0 + q) * RW + rl) * D + 2 * d2)
+                         : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int it = it0 + k * 256;
+        const int rl = it < rows * D2 ? it / D2 : 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float w = sp0 + q < S ? wts[rl * 33 + sp0 + q] : 0.f;
+          ox[k] += w * pv[k][q].x;
+          oy[k] += w * pv[k][q].y;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int it = it0 + k * 256;
+      if (it >= rows * D2) continue;
+      const int rl = it / D2, d2 = it - rl * D2;
+      const int row = qgroup * RW + rl;
+      const int i = row / G;
+      const int h = kvh * G + (row - i * G);
+      *reinterpret_cast<uint32_t*>(a.out + (((size_t)b * N + i) * a.Hq + h) * D + 2 * d2) =
+          pack_bf16x2(ox[k], oy[k]);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup -> (unit, split), XCD-aware; validates kv_len.
+struct UnitCtx {
+  int unit, split, qgroup, pair, kvh, b, L, total;
+  bool bad;
+};
+
+__device__ __forceinline__ bool decode_unit(const AttnArgs& a, UnitCtx& u) {
+  const int w = blockIdx.x;
+  const int xcd = w % kNumXCDs;
+  const int slot = w / kNumXCDs;
+  u.split = slot % a.splits;
+  u.unit = (slot / a.splits) * kNumXCDs + xcd;
+  if (u.unit >= a.units) return false;
+  u.qgroup = u.unit % a.qgroups;
+  u.pair = u.unit / a.qgroups;
+  u.kvh = u.pair % a.Hkv;
+  u.b = u.pair / a.Hkv;
+  int L = a.kv_len[u.b];
+  u.bad = L < 0 || L > a.Lmax - a.N;
+  if (u.bad) {
+    L = 0;
+    if (a.flags && u.split == 0 && u.qgroup == 0 && u.kvh == 0 && threadIdx.x == 0)
+      atomicOr(a.flags + u.b, EAGLE_FLAG_BAD_KV_LEN);
+  }
+  u.L = L;
+  u.total = L + a.N;
+  return true;
+}
+
+// Q fragments (MFMA B operand) and tree masks of QBW query blocks at unit row r0.
+template <int D, int QBW, int RW>
+__device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u, int r0,
+                                             bf16x8 (&qf)[QBW][D / 32], uint64_t (&anc_q)[QBW]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int N = a.N, G = a.G;
+  const uint64_t nmask = N == 64 ? ~0ull : (1ull << N) - 1ull;
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int row = u.qgroup * RW + r0 + qb * 16 + c;
+    if (row < a.M) {
+      const int i = row / G;
+      const int h = u.kvh * G + (row - i * G);
+      const uint16_t* qrow = a.q + (((size_t)u.b * N + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
+      anc_q[qb] = a.anc[(size_t)u.b * N + i] & nmask;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) qf[qb][ks] = bf16x8{};
+      anc_q[qb] = 0;
+    }
+  }
+}
+
+// Merge the states of the waves that hold the same query rows (o-th such wave
+// at index base + o * stride), into wave 0 of the group, through LDS.
+template <int QBW, int NDB, int NW>
+__device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_run)[QBW],
+                                            float (&l_run)[QBW], float* mb, int me, int first,
+                                            int stride) {
+  constexpr int PER_WAVE = QBW * NDB * 256 + QBW * 32;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  __syncthreads();
+  if (me != first) {
+    float* my = mb + me * PER_WAVE;
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(my + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
+      if (g == 0) {
+        my[QBW * NDB * 256 + qb * 32 + c] = m_run[qb];
+        my[QBW * NDB * 256 + qb * 32 + 16 + c] = l_run[qb];
+      }
+    }
+  }
+  __syncthreads();
+  if (me == first) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      float mt = m_run[qb];
+#pragma unroll
+      for (int o = 1; o < NW; ++o)
+        mt = fmaxf(mt, mb[(first + o * stride) * PER_WAVE + QBW * NDB * 256 + qb * 32 + c]);
+      const float mu = mt == -INFINITY ? 0.f : mt;
+      const float fs = __builtin_amdgcn_exp2f(m_run[qb] - mu);
+      float lt = l_run[qb] * fs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[qb][db] *= fs;
+#pragma unroll
+      for (int o = 1; o < NW; ++o) {
+        const float* other = mb + (first + o * stride) * PER_WAVE;
+        const float fo = __builtin_amdgcn_exp2f(other[QBW * NDB * 256 + qb * 32 + c] - mu);
+        lt += other[QBW * NDB * 256 + qb * 32 + 16 + c] * fo;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[qb][db] += *reinterpret_cast<const f32x4*>(other + ((qb * NDB + db) * 64 + lane) * 4) * fo;
+      }
+      m_run[qb] = mt;
+      l_run[qb] = lt;
+    }
+  }
+  __syncthreads();  // the merge buffers may now be reused
+}
+
+// ============================================================================
+// ring kernel: per-wave LDS rings filled by direct-to-LDS loads
+// ============================================================================
+template <int D_, int QBW_>
+struct RingShape {
+  static constexpr int D = D_;
+  static constexpr int QBW = QBW_;
+  static constexpr int RING = 2;                  // chunk slots per wave
+  static constexpr int MAT_BYTES = 32 * D * 2;    // K (or V) of one 32-key chunk
+  static constexpr int SLOT_BYTES = 2 * MAT_BYTES;
+  static constexpr int SPR = D / 8;               // 16-byte slots per key row
+  static constexpr int RPL = 64 / SPR;            // key rows per wave-wide direct load
+  static constexpr int LPM = 32 / RPL;            // direct loads per matrix
+  static constexpr int LPC = 2 * LPM;             // direct loads per chunk
+  static constexpr int NKS = D / 32, NDB = D / 16;
+  static constexpr int RW = 16 * QBW;
+  static constexpr int LDS_RING = 4 * RING * SLOT_BYTES;
+  static constexpr int LDS_MERGE = 4 * (QBW * NDB * 256 + QBW * 32) * 4;
+  static constexpr int LDS_STAGE = RW * (D + 1) * 4;
+  static constexpr int LDS_A = LDS_RING > LDS_MERGE ? LDS_RING : LDS_MERGE;
+  static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
+  static_assert(LPC == 8 || LPC == 16, "vmcnt waits below assume 8 or 16 loads per chunk");
+};
+
+// Wait until the oldest outstanding chunk has landed in LDS; loads complete in
+// issue order, so at most one younger chunk (LPC loads) may remain in flight.
+template <int LPC>
+__device__ __forceinline__ void wait_chunk(bool another_in_flight) {
+  if (another_in_flight) {
+    if constexpr (LPC == 16)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+template <class S>
+__global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
+  constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NKS = S::NKS, NDB = S::NDB;
+  constexpr int SPR = S::SPR, RPL = S::RPL, LPM = S::LPM, RING = S::RING;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS_BYTES];
+  __shared__ int s_ticket;
+
+  UnitCtx u;
+  if (!decode_unit(a, u)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int L = u.L;
+
+  // This split's chunks; wave w takes chunks cb + w, cb + w + 4, ...
+  const int n_chunks = (u.total + 31) / 32;
+  const int cb = (int)((long long)u.split * n_chunks / a.splits);
+  const int ce = (int)((long long)(u.split + 1) * n_chunks / a.splits);
+  const int my_first = cb + wave;
+  const int my_n = my_first < ce ? (ce - my_first + 3) / 4 : 0;
+
+  bf16x8 qf[QBW][NKS];
+  uint64_t anc_q[QBW];
+  load_queries<D, QBW, RW>(a, u, 0, qf, anc_q);
+
+  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
+  const uint16_t* kp = a.k + kv_base;
+  const uint16_t* vp = a.v + kv_base;
+  uint8_t* ring = lds + wave * RING * S::SLOT_BYTES;
+
+  // Direct-to-LDS fill of one chunk: lane l writes 16 bytes at load base + 16 l,
+  // i.e. row t*RPL + l/SPR, slot l%SPR, which receives global slot (l%SPR)^swz(row).
+  // Rows past the last key re-read the last key (finite data, masked later).
+  const int r_in = lane / SPR, p_in = lane % SPR;
+  auto issue = [&](int gc, int slot) {
+    uint8_t* dst = ring + slot * S::SLOT_BYTES;
+#pragma unroll
+    for (int t = 0; t < LPM; ++t) {
+      const int r = t * RPL + r_in;
+      const int key = min(gc * 32 + r, u.total - 1);
+      const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
+      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(dst + t * RPL * D * 2), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < LPM; ++t) {
+      const int r = t * RPL + r_in;
+      const int key = min(gc * 32 + r, u.total - 1);
+      const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
+      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(dst + S::MAT_BYTES + t * RPL * D * 2), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[QBW][NDB];
+  float m_run[QBW], l_run[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int i = 0; i < RING; ++i)
+    if (i < my_n) issue(my_first + 4 * i, i);
+
+  for (int i = 0; i < my_n; ++i) {
+    const int gc = my_first + 4 * i;
+    const int slot = i % RING;
+    wait_chunk<S::LPC>(i + 1 < my_n);
+    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(ring + slot * S::SLOT_BYTES);
+    const uint8_t* Vb = ring + slot * S::SLOT_BYTES + S::MAT_BYTES;
+
+    f32x4 s[QBW][2];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
+      const int kr = 8 * (c >> 2) + 4 * hlf + (c & 3);
+      const int sw = swz(kr);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kc + kr * D + (((ks * 4 + g) ^ sw) * 8));
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb)
+          s[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], s[qb][hlf], 0, 0, 0);
+      }
+    }
+    const int key0 = gc * 32 + 8 * g;
+    const bool need_mask = gc * 32 + 32 > L;
+    bf16x8 pf[QBW];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s[qb][j >> 2][j & 3] * a.scale_log2;
+      if (need_mask) {
+        const uint32_t ok = key_mask8(key0, L, anc_q[qb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
+      }
+      pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
+    }
+    // V^T fragments by transposed LDS reads: lane (g, c) gets V[8g + j][16db + c],
+    // j = 0..7, as two 4-element halves.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      short4_t h2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int vr = 8 * g + 4 * h + (c >> 2);
+        const int ps = (2 * db + ((c & 3) >> 1)) ^ swz(vr);
+        const uint8_t* src = Vb + vr * D * 2 + ps * 16 + (c & 1) * 8;
+        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(src));
+      }
+      const bf16x8 vf =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
+    }
+    if (i + RING < my_n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
+      issue(my_first + 4 * (i + RING), slot);
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    l_run[qb] += __shfl_xor(l_run[qb], 16);
+    l_run[qb] += __shfl_xor(l_run[qb], 32);
+  }
+  // wave_barrier-free rings are idle now; fold the four waves into wave 0
+  merge_waves<QBW, NDB, 4>(acc, m_run, l_run, reinterpret_cast<float*>(lds), wave, 0, 1);
+  finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wave == 0, 0, acc,
+                           m_run, l_run, lds, &s_ticket);
+}
+
+// ============================================================================
+// tile kernel: shared LDS tiles, waves split the query rows (grouped queries)
+// ============================================================================
 template <int D_, int QBW_, int WQ_, int KC_>
-struct AttnShape {
+struct TileShape {
   static constexpr int D = D_;
   static constexpr int QBW = QBW_;          // 16-row query blocks per wave
   static constexpr int WQ = WQ_;            // waves across query blocks
@@ -48,29 +563,14 @@ struct AttnShape {
   static constexpr int KG = 256 / CPR;      // key quads per staging pass
   static constexpr int NQ = KT / 4;         // key quads per tile
   static constexpr int PASSES = (NQ + KG - 1) / KG;
-  static constexpr int NKS = D / 32;        // MFMA k-steps over d
-  static constexpr int NDB = D / 16;        // 16-wide d blocks of the output
-  static constexpr int LDS_TILE = (KT * KS + D * VS) * 2;        // bytes
+  static constexpr int NKS = D / 32;
+  static constexpr int NDB = D / 16;
+  static constexpr int LDS_TILE = (KT * KS + D * VS) * 2;
   static constexpr int LDS_MERGE = WK > 1 ? 4 * (QBW * NDB * 256 + QBW * 32) * 4 : 0;
-  static constexpr int LDS_WEIGHTS = RW * 32 * 4;  // split-merge weights, <= 32 splits
-  static constexpr int LDS_BYTES0 = LDS_TILE > LDS_MERGE ? LDS_TILE : LDS_MERGE;
-  static constexpr int LDS_BYTES = LDS_BYTES0 > LDS_WEIGHTS ? LDS_BYTES0 : LDS_WEIGHTS;
+  static constexpr int LDS_STAGE = RW * (D + 1) * 4;
+  static constexpr int LDS_A = LDS_TILE > LDS_MERGE ? LDS_TILE : LDS_MERGE;
+  static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
   static_assert(NQ >= 8 && (NQ & (NQ - 1)) == 0, "V^T swizzle needs >= 8 key quads, power of 2");
-};
-
-struct AttnArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const int32_t* kv_len;
-  const uint64_t* anc;
-  uint16_t* out;
-  float* part_o;     // [units * splits * RW * D]
-  float2* part_ml;   // [units * splits * RW]
-  int32_t* counters; // [units]
-  int32_t* flags;
-  int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
-  float scale_log2;
 };
 
 __device__ __forceinline__ uint32_t pick_half(uint32_t w, int hi) {
@@ -78,7 +578,7 @@ __device__ __forceinline__ uint32_t pick_half(uint32_t w, int hi) {
 }
 
 template <class S>
-__global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
   constexpr int D = S::D, QBW = S::QBW, WQ = S::WQ, KC = S::KC, KT = S::KT, RW = S::RW;
   constexpr int KS = S::KS, VS = S::VS, CPR = S::CPR, KG = S::KG, NQ = S::NQ;
   constexpr int NKS = S::NKS, NDB = S::NDB;
@@ -87,64 +587,28 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   uint16_t* Ks = reinterpret_cast<uint16_t*>(lds_raw);
   uint16_t* Vt = Ks + KT * KS;
 
+  UnitCtx u;
+  if (!decode_unit(a, u)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wq = wave % WQ;
   const int wk = wave / WQ;
-  const int g = lane >> 4;   // lane group: MFMA k-slot group / output row quad
-  const int c = lane & 15;   // MFMA row (A) / column (B, C)
-
-  // ---- workgroup -> (unit, split), XCD-aware --------------------------------
-  const int w = blockIdx.x;
-  const int xcd = w % kNumXCDs;
-  const int slot = w / kNumXCDs;
-  const int split = slot % a.splits;
-  const int unit = (slot / a.splits) * kNumXCDs + xcd;
-  if (unit >= a.units) return;
-  const int qgroup = unit % a.qgroups;
-  const int pair = unit / a.qgroups;
-  const int kvh = pair % a.Hkv;
-  const int b = pair / a.Hkv;
-  const int N = a.N, G = a.G, M = a.M;
-
-  int L = a.kv_len[b];
-  const bool bad = L < 0 || L > a.Lmax - N;
-  if (bad) {
-    L = 0;
-    if (a.flags && split == 0 && qgroup == 0 && kvh == 0 && tid == 0)
-      atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
-  }
-  const int total = L + N;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int L = u.L, total = u.total;
   const int n_tiles = (total + KT - 1) / KT;
-  const int t_begin = (int)((long long)split * n_tiles / a.splits);
-  const int t_end = (int)((long long)(split + 1) * n_tiles / a.splits);
+  const int t_begin = (int)((long long)u.split * n_tiles / a.splits);
+  const int t_end = (int)((long long)(u.split + 1) * n_tiles / a.splits);
 
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
+  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
   const uint16_t* kp = a.k + kv_base;
   const uint16_t* vp = a.v + kv_base;
 
-  // ---- this wave's query rows: Q fragments (MFMA B operand) and tree masks ----
-  const int row0 = qgroup * RW + wq * QBW * 16;
+  const int r0 = wq * QBW * 16;
   bf16x8 qf[QBW][NKS];
   uint64_t anc_q[QBW];
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const int row = row0 + qb * 16 + c;
-    if (row < M) {
-      const int i = row / G;
-      const int h = kvh * G + (row - i * G);
-      const uint16_t* qrow = a.q + (((size_t)b * N + i) * a.Hq + h) * D;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
-      anc_q[qb] = a.anc[(size_t)b * N + i] & (N == 64 ? ~0ull : (1ull << N) - 1ull);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] = bf16x8{};
-      anc_q[qb] = 0;
-    }
-  }
+  load_queries<D, QBW, RW>(a, u, r0, qf, anc_q);
 
   f32x4 acc[QBW][NDB];
   float m_run[QBW], l_run[QBW];
@@ -156,7 +620,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging: thread -> (16-byte chunk dc of a key row, key quad kq) -------
+  // staging: thread -> (16-byte chunk dc of a key row, key quad kq)
   const int dc = tid % CPR;
   const int kq0 = tid / CPR;
   u32x4 kreg[S::PASSES][4], vreg[S::PASSES][4];
@@ -215,13 +679,12 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     const bool need_mask = tile_base + KT > L;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const int chunk = wk * KC + kc;  // 32-key chunk within the tile
+      const int chunk = wk * KC + kc;
       f32x4 s[QBW][2];
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
-        // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
         const int krow = chunk * 32 + 8 * (c >> 2) + 4 * hlf + (c & 3);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -231,7 +694,6 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
             s[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], s[qb][hlf], 0, 0, 0);
         }
       }
-      // Lane (g, c) now holds scores of query column c for keys chunk*32 + 8g + j, j = 4*hlf + r.
       const int key0 = tile_base + chunk * 32 + 8 * g;
       bf16x8 pf[QBW];
 #pragma unroll
@@ -240,40 +702,12 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = s[qb][j >> 2][j & 3] * a.scale_log2;
         if (need_mask) {
-          // Valid keys among key0..key0+7 as an 8-bit mask, built without branches:
-          // committed keys (< L) plus the ancestor bits of this query's node.
-          const int below = L - key0;  // how many of the 8 keys are committed
-          const uint32_t pre = below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
-          const int tk0 = -below;      // tree index of key0
-          const uint64_t am = anc_q[qb];
-          const uint32_t tre = tk0 >= 0 ? (tk0 < 64 ? (uint32_t)(am >> tk0) & 0xffu : 0u)
-                                        : (tk0 > -8 ? (uint32_t)(am << -tk0) & 0xffu : 0u);
-          const uint32_t ok = pre | tre;
+          const uint32_t ok = key_mask8(key0, L, anc_q[qb]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
         }
-        float mx = x[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-        float psum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pj = __builtin_amdgcn_exp2f(x[j] - m_use);
-          psum += pj;
-          pf[qb][j] = (__bf16)pj;
-        }
-        l_run[qb] = l_run[qb] * alpha + psum;
-        m_run[qb] = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+        pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
       }
-      // O^T[d, q] += V^T[d, keys] P^T[keys, q]; lane (g, c) supplies d = db*16 + c and
-      // keys chunk*32 + 8g .. +7 (quads 2g, 2g+1 of the chunk, swizzled by d >> 4 = db).
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 16 + c;
@@ -288,155 +722,32 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- per-query totals across the four lanes of a column ---------------------
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
-
-  // ---- merge the WK key-waves of each query group through LDS ---------------
   if constexpr (S::WK > 1) {
-    __syncthreads();  // tile buffers are free
-    float* mb = reinterpret_cast<float*>(lds_raw);
-    constexpr int PER_WAVE = QBW * NDB * 256 + QBW * 32;
-    if (wk > 0) {
-      float* my = mb + wave * PER_WAVE;
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          *reinterpret_cast<f32x4*>(my + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
-        if (g == 0) {
-          my[QBW * NDB * 256 + qb * 32 + c] = m_run[qb];
-          my[QBW * NDB * 256 + qb * 32 + 16 + c] = l_run[qb];
-        }
-      }
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        float mt = m_run[qb];
-#pragma unroll
-        for (int o = 1; o < S::WK; ++o)
-          mt = fmaxf(mt, mb[(o * WQ + wq) * PER_WAVE + QBW * NDB * 256 + qb * 32 + c]);
-        const float mu = mt == -INFINITY ? 0.f : mt;
-        const float fs = __builtin_amdgcn_exp2f(m_run[qb] - mu);
-        float lt = l_run[qb] * fs;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] *= fs;
-#pragma unroll
-        for (int o = 1; o < S::WK; ++o) {
-          const float* other = mb + (o * WQ + wq) * PER_WAVE;
-          const float fo = __builtin_amdgcn_exp2f(other[QBW * NDB * 256 + qb * 32 + c] - mu);
-          lt += other[QBW * NDB * 256 + qb * 32 + 16 + c] * fo;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[qb][db] += *reinterpret_cast<const f32x4*>(other + ((qb * NDB + db) * 64 + lane) * 4) * fo;
-        }
-        m_run[qb] = mt;
-        l_run[qb] = lt;
-      }
-    }
+    merge_waves<QBW, NDB, S::WK>(acc, m_run, l_run, reinterpret_cast<float*>(lds_raw), wave, wq, WQ);
+  } else {
+    __syncthreads();  // tile buffers may be reused for the split weights
   }
-
-  // ---- output ----------------------------------------------------------------
-  if (a.splits == 1) {
-    if (wk == 0) {
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        const int row = row0 + qb * 16 + c;
-        if (row >= M) continue;
-        const int i = row / G;
-        const int h = kvh * G + (row - i * G);
-        uint16_t* orow = a.out + (((size_t)b * N + i) * a.Hq + h) * D;
-        const float inv = bad ? 0.f : 1.f / l_run[qb];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const f32x4 o = acc[qb][db] * inv;
-          const uint32_t lo = float_to_bf16_bits(o[0]) | ((uint32_t)float_to_bf16_bits(o[1]) << 16);
-          const uint32_t up = float_to_bf16_bits(o[2]) | ((uint32_t)float_to_bf16_bits(o[3]) << 16);
-          *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * g) = u32x2{lo, up};
-        }
-      }
-    }
-    return;
-  }
-
-  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
-  if (wk == 0) {
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      const int rl = wq * QBW * 16 + qb * 16 + c;  // row within the unit
-      if (qgroup * RW + rl >= M) continue;
-      float* po = a.part_o + (pbase + rl) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(po + db * 16 + 4 * g) = acc[qb][db];
-      if (g == 0) a.part_ml[pbase + rl] = make_float2(m_run[qb], l_run[qb]);
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(a.counters + unit, 1);
-  __syncthreads();
-  if (s_ticket != a.splits - 1) return;
-
-  // Last split of this unit: merge all partials.
-  __threadfence();
-  const int rows = min(RW, M - qgroup * RW);
-  const int S_ = a.splits;
-  float* wts = reinterpret_cast<float*>(lds_raw);  // [rows][S_] merge weights
-  for (int r = tid; r < rows; r += 256) {
-    const size_t ub = (size_t)unit * S_ * RW;
-    float mt = -INFINITY;
-    for (int sp = 0; sp < S_; ++sp) mt = fmaxf(mt, a.part_ml[ub + (size_t)sp * RW + r].x);
-    const float mu = mt == -INFINITY ? 0.f : mt;
-    float lt = 0.f;
-    for (int sp = 0; sp < S_; ++sp) {
-      const float2 ml = a.part_ml[ub + (size_t)sp * RW + r];
-      const float f = __builtin_amdgcn_exp2f(ml.x - mu);
-      wts[r * S_ + sp] = f;
-      lt += ml.y * f;
-    }
-    const float inv = (bad || lt == 0.f) ? 0.f : 1.f / lt;
-    for (int sp = 0; sp < S_; ++sp) wts[r * S_ + sp] *= inv;
-  }
-  __syncthreads();
-  constexpr int D4 = D / 4;
-  for (int it = tid; it < rows * D4; it += 256) {
-    const int r = it / D4;
-    const int d4 = it - r * D4;
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < S_; ++sp) {
-      const f32x4 po = *reinterpret_cast<const f32x4*>(
-          a.part_o + (((size_t)unit * S_ + sp) * RW + r) * D + d4 * 4);
-      o += po * wts[r * S_ + sp];
-    }
-    const int row = qgroup * RW + r;
-    const int i = row / G;
-    const int h = kvh * G + (row - i * G);
-    uint16_t* orow = a.out + (((size_t)b * N + i) * a.Hq + h) * D + d4 * 4;
-    const uint32_t lo = float_to_bf16_bits(o[0]) | ((uint32_t)float_to_bf16_bits(o[1]) << 16);
-    const uint32_t up = float_to_bf16_bits(o[2]) | ((uint32_t)float_to_bf16_bits(o[3]) << 16);
-    *reinterpret_cast<u32x2*>(orow) = u32x2{lo, up};
-  }
-  if (tid == 0) atomicExch(a.counters + unit, 0);
+  finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wk == 0, r0, acc,
+                           m_run, l_run, lds_raw, &s_ticket);
 }
 
 // ---- variants ----------------------------------------------------------------
-// index: 0 = 1 query block/WG (4 key waves), 1 = 2 blocks (4 key waves),
-//        2 = 4 blocks (2x2), 3 = 8 blocks (4 query waves x 2), 4 = 16 blocks (4x4)
+// 0: ring, 1 query block      1: ring, 2 query blocks
+// 2: tile, 4 blocks (2x2)     3: tile, 8 blocks (4 query waves)   4: tile, 16 blocks
 struct VariantInfo {
   int rw;
-  int kt;
+  int keys_per_piece;  // split granularity in keys
 };
 
-static VariantInfo variant_info(int variant, int d) {
-  (void)d;
+static VariantInfo variant_info(int variant) {
   switch (variant) {
-    case 0: return {16, 128};
-    case 1: return {32, 128};
+    case 0: return {16, 32};
+    case 1: return {32, 32};
     case 2: return {64, 64};
     case 3: return {128, 64};
     default: return {256, 64};
@@ -446,11 +757,11 @@ static VariantInfo variant_info(int variant, int d) {
 template <int D>
 static void* variant_kernel(int variant) {
   switch (variant) {
-    case 0: return (void*)tree_attn_kernel<AttnShape<D, 1, 1, 1>>;
-    case 1: return (void*)tree_attn_kernel<AttnShape<D, 2, 1, 1>>;
-    case 2: return (void*)tree_attn_kernel<AttnShape<D, 2, 2, 1>>;
-    case 3: return (void*)tree_attn_kernel<AttnShape<D, 2, 4, 2>>;
-    default: return (void*)tree_attn_kernel<AttnShape<D, 4, 4, 2>>;
+    case 0: return (void*)tree_attn_ring_kernel<RingShape<D, 1>>;
+    case 1: return (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
+    case 2: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 2, 1>>;
+    case 3: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 4, 2>>;
+    default: return (void*)tree_attn_tile_kernel<TileShape<D, 4, 4, 2>>;
   }
 }
 
@@ -469,23 +780,37 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   int variant = nqb <= 1 ? 0 : nqb <= 2 ? 1 : nqb <= 4 ? 2 : nqb <= 8 ? 3 : 4;
   variant = env_int("EAGLE_ATTN_VARIANT", variant);
   if (variant < 0 || variant > 4) variant = 4;
-  const VariantInfo vi = variant_info(variant, d);
+  const VariantInfo vi = variant_info(variant);
   p.variant = variant;
   p.rows_per_wg = vi.rw;
-  p.kt = vi.kt;
+  p.kt = vi.keys_per_piece;
   p.qgroups = (p.M + vi.rw - 1) / vi.rw;
   p.units = B * Hkv * p.qgroups;
-  const int tiles = (Lmax + vi.kt - 1) / vi.kt;
+  const int pieces = (Lmax + vi.keys_per_piece - 1) / vi.keys_per_piece;
   const int padded_units = ((p.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
-  int splits = (2 * kNumCUs + padded_units - 1) / padded_units;
+  // Aim for one workgroup per CU: a ring workgroup keeps up to eight 32-key
+  // chunks in flight and fills its CU's LDS; more splits only lengthen the
+  // merge, whose cost grows with splits x query rows.
+  const int target = kNumCUs;
+  int splits = (target + padded_units - 1) / padded_units;
   splits = env_int("EAGLE_ATTN_SPLITS", splits);
-  if (splits > tiles) splits = tiles;
-  if (splits > 32) splits = 32;  // the merge keeps rows x splits weights in LDS
+  if (splits > pieces) splits = pieces;
+  if (splits > 32) splits = 32;  // the merge holds up to 32 weights per row in registers
   if (splits < 1) splits = 1;
   p.splits = splits;
-  p.ws_partials = splits > 1 ? (size_t)p.units * splits * vi.rw * (d * 4 + 8) : 0;
+  p.ws_partials = splits > 1 ? (size_t)p.units * splits * vi.rw * (d * 4 + 4) : 0;
   p.ws_counters = splits > 1 ? (size_t)p.units * 4 : 0;
   return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t tree_attn_workspace_bytes(const AttnPlan& p) {
+  if (p.splits <= 1) return 0;
+  const size_t cnt = align256((size_t)p.units * 4);
+  const size_t lse = align256((size_t)p.units * p.splits * p.rows_per_wg * 4);
+  const size_t o = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
+  return cnt + lse + o;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
@@ -500,11 +825,11 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.anc = anc;
   a.out = out;
   uint8_t* w = static_cast<uint8_t*>(ws);
+  const size_t cnt = align256((size_t)plan.units * 4);
+  const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
   a.counters = reinterpret_cast<int32_t*>(w);
-  const size_t cnt_bytes = (plan.ws_counters + 255) & ~size_t(255);
-  a.part_ml = reinterpret_cast<float2*>(w + cnt_bytes);
-  const size_t ml_bytes = ((size_t)plan.units * plan.splits * plan.rows_per_wg * 8 + 255) & ~size_t(255);
-  a.part_o = reinterpret_cast<float*>(w + cnt_bytes + ml_bytes);
+  a.part_lse = reinterpret_cast<float*>(w + cnt);
+  a.part_o = reinterpret_cast<float*>(w + cnt + lse);
   a.flags = flags;
   a.B = B;
   a.N = N;
@@ -522,14 +847,6 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
   void* args[] = {&a};
   return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
-}
-
-size_t tree_attn_workspace_bytes(const AttnPlan& p) {
-  if (p.splits <= 1) return 0;
-  const size_t cnt_bytes = (p.ws_counters + 255) & ~size_t(255);
-  const size_t ml_bytes = ((size_t)p.units * p.splits * p.rows_per_wg * 8 + 255) & ~size_t(255);
-  const size_t o_bytes = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
-  return cnt_bytes + ml_bytes + o_bytes;
 }
 
 }  // namespace eagle
