@@ -140,6 +140,8 @@ def tree_attn_workspace_bytes(B, N, Hq, Hkv, d, Lmax) -> int:
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Device workspace of `nbytes` (zero-filled, as the verification
+    workspace requires before its first use)."""
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 

@@ -26,8 +26,6 @@ struct AttnPlan {
   int splits;     // KV splits per unit
   int variant;    // kernel instantiation index
   int kt;         // keys per tile
-  size_t ws_partials;  // bytes of split partials
-  size_t ws_counters;  // bytes of per-unit counters
 };
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax);

@@ -27,11 +27,11 @@
 // consecutive keys of one query column, exactly the k-slots of P^T), apply the
 // tree mask, and run the online softmax with cross-lane shuffles.
 //
-// Splits publish (O / l, log2-sum-exp) partials with device-coherent stores;
-// the last split of a unit to finish (atomic ticket) merges them.  No
-// whole-cache writeback or invalidate is needed: the partial stores and loads
-// are relaxed agent-scope atomics (coherent across XCDs), and every thread
-// waits for its stores to complete before the ticket is taken.
+// With more than one split, every split writes its normalised rows O / l and
+// log2-sum-exp with coalesced stores, and a small merge kernel on the same
+// stream (one wave per query row, spread over the whole GPU) combines them.
+// The kernel boundary makes the partials visible; no cross-workgroup
+// synchronisation is needed inside the attention kernel.
 #include <stdlib.h>
 
 #include "common.h"
@@ -50,7 +50,6 @@ struct AttnArgs {
   uint16_t* out;
   float* part_o;     // [units * splits * RW * D]  O / l of each split
   float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
-  int32_t* counters; // [units]
   int32_t* flags;
   int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
   float scale_log2;
@@ -62,41 +61,40 @@ struct AttnArgs {
 // (4 consecutive rows, two adjacent slots each).
 __device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
 
-__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent1(float* p, float a) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(a), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent2(float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-__device__ __forceinline__ float load_coherent1(float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
 }
 
 // Online softmax update of one 16-query block from this lane's 8 scores
-// (already scaled to the log2 domain and masked).  Returns the bf16 P^T fragment.
+// (already scaled to the log2 domain and masked).  Returns the bf16 P^T
+// fragment.  The running max m_run is shared by the four lanes of a query
+// column (the MFMA sums their keys) and is raised lazily: only when some
+// lane of the wave sees a score more than LAZY above it does the wave take
+// the column max with cross-lane shuffles and rescale its accumulators, so
+// in the common case a chunk needs no shuffles and no rescale.  Exponents
+// stay below 2^LAZY, far inside fp32 and bf16 range; the result is the same
+// softmax whichever reference max is used.
+constexpr float LAZY = 8.f;
+
 template <int NDB>
 __device__ __forceinline__ bf16x8 softmax_step(const float (&x)[8], float& m_run, float& l_run,
                                                f32x4 (&acc)[NDB]) {
   float mx = x[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+  if (__ballot(mx > m_run + LAZY)) {  // wave-uniform
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new > m_run) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+  }
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
   float psum = 0.f;
   bf16x8 pf;
 #pragma unroll
@@ -105,10 +103,7 @@ __device__ __forceinline__ bf16x8 softmax_step(const float (&x)[8], float& m_run
     psum += pj;
     pf[j] = (__bf16)pj;
   }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+  l_run += psum;
   return pf;
 }
 
@@ -124,13 +119,13 @@ __device__ __forceinline__ uint32_t key_mask8(int key0, int L, uint64_t anc) {
   return pre | tre;
 }
 
-// Write the final bf16 rows, or publish this split's partial and, when this
-// workgroup is the last split of its unit, merge all partials.  acc/m/l hold
-// the lane's query column for QBW blocks starting at row r0 of the unit.
+// Write the final bf16 rows (one split) or this split's partial (O / l and
+// log2-sum-exp).  acc/m/l hold the lane's query column for QBW blocks starting
+// at row r0 of the unit.
 template <int D, int RW, int QBW>
 __device__ void finish_split(const AttnArgs& a, int unit, int split, int qgroup, int b, int kvh,
                              bool bad, bool active, int r0, f32x4 (&acc)[QBW][D / 16],
-                             float (&m_run)[QBW], float (&l_run)[QBW], uint8_t* lds, int* s_ticket) {
+                             float (&m_run)[QBW], float (&l_run)[QBW], uint8_t* lds) {
   constexpr int NDB = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int N = a.N, G = a.G, M = a.M;
@@ -156,110 +151,31 @@ __device__ void finish_split(const AttnArgs& a, int unit, int split, int qgroup,
   }
 
   // Stage this split's normalised rows in LDS (row-major fp32) so that the
-  // device-coherent stores below are fully coalesced.
+  // partial stores are coalesced 16-byte stores; the merge kernel that
+  // follows on the stream combines the splits.
   const int rows = min(RW, M - qgroup * RW);
-  float* stage = reinterpret_cast<float*>(lds);  // [RW][D + 1]: last column = log2-sum-exp
-  constexpr int SD = D + 1;
+  float* stage = reinterpret_cast<float*>(lds);  // [RW][D + 4]: column D = log2-sum-exp
+  constexpr int SD = D + 4;
   if (active) {
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       const int rl = r0 + qb * 16 + c;
       const float inv = l_run[qb] == 0.f ? 0.f : 1.f / l_run[qb];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const f32x4 o = acc[qb][db] * inv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) stage[rl * SD + db * 16 + 4 * g + e] = o[e];
-      }
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(stage + rl * SD + db * 16 + 4 * g) = acc[qb][db] * inv;
       if (g == 0) stage[rl * SD + D] = l_run[qb] == 0.f ? -INFINITY : m_run[qb] + __log2f(l_run[qb]);
     }
   }
   __syncthreads();
   const size_t pbase = ((size_t)unit * a.splits + split) * RW;
-  for (int it = tid; it < rows * (D / 2); it += 256) {
-    const int rl = it / (D / 2), d2 = it - rl * (D / 2);
-    store_coherent2(a.part_o + (pbase + rl) * D + 2 * d2, stage[rl * SD + 2 * d2],
-                    stage[rl * SD + 2 * d2 + 1]);
+  constexpr int D4 = D / 4;
+  for (int it = tid; it < rows * D4; it += 256) {
+    const int rl = it / D4, d4 = it - rl * D4;
+    *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + 4 * d4) =
+        *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
   }
-  for (int rl = tid; rl < rows; rl += 256) store_coherent1(a.part_lse + pbase + rl, stage[rl * SD + D]);
-  // The partial stores are device-coherent; waiting for them to complete
-  // before the ticket is taken orders them before it for every reader.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    *s_ticket = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (*s_ticket != a.splits - 1) return;
-
-  // Last split of this unit: merge every split's partial.  Weights per row
-  // first (one coherent load per split and row), then the rows, with
-  // consecutive lanes reading consecutive float pairs.
-  const int S = a.splits;
-  const size_t ub = (size_t)unit * S * RW;
-  float* wts = stage;  // [RW][33]: 32 weights + inverse total, reuses the staging area
-  for (int rl = tid; rl < rows; rl += 256) {
-    float w[32];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < 32; ++sp) {
-      w[sp] = sp < S ? load_coherent1(a.part_lse + ub + (size_t)sp * RW + rl) : -INFINITY;
-      mt = fmaxf(mt, w[sp]);
-    }
-    const float mu = mt == -INFINITY ? 0.f : mt;
-    float tot = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < 32; ++sp) {
-      w[sp] = __builtin_amdgcn_exp2f(w[sp] - mu);
-      tot += w[sp];
-    }
-    const float inv = (bad || tot == 0.f) ? 0.f : 1.f / tot;
-#pragma unroll
-    for (int sp = 0; sp < 32; ++sp) wts[rl * 33 + sp] = w[sp] * inv;
-  }
-  __syncthreads();
-  constexpr int D2 = D / 2;
-  constexpr int BATCH = 4;  // float pairs in flight per split group per thread
-  for (int it0 = tid; it0 < rows * D2; it0 += 256 * BATCH) {
-    float ox[BATCH], oy[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) ox[k] = oy[k] = 0.f;
-    for (int sp0 = 0; sp0 < S; sp0 += 8) {
-      float2 pv[BATCH][8];
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        const int it = it0 + k * 256;
-        const int rl = it / D2, d2 = it - (it / D2) * D2;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          pv[k][q] = (it < rows * D2 && sp0 + q < S)
-                         ? load_coherent2(a.part_o + (ub + (size_t)(sp0 + q) * RW + rl) * D + 2 * d2)
-                         : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        const int it = it0 + k * 256;
-        const int rl = it < rows * D2 ? it / D2 : 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float w = sp0 + q < S ? wts[rl * 33 + sp0 + q] : 0.f;
-          ox[k] += w * pv[k][q].x;
-          oy[k] += w * pv[k][q].y;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int it = it0 + k * 256;
-      if (it >= rows * D2) continue;
-      const int rl = it / D2, d2 = it - rl * D2;
-      const int row = qgroup * RW + rl;
-      const int i = row / G;
-      const int h = kvh * G + (row - i * G);
-      *reinterpret_cast<uint32_t*>(a.out + (((size_t)b * N + i) * a.Hq + h) * D + 2 * d2) =
-          pack_bf16x2(ox[k], oy[k]);
-    }
-  }
-  if (tid == 0) __hip_atomic_store(a.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int rl = tid; rl < rows; rl += 256) a.part_lse[pbase + rl] = stage[rl * SD + D];
 }
 
 // Workgroup -> (unit, split), XCD-aware; validates kv_len.
@@ -386,7 +302,7 @@ struct RingShape {
   static constexpr int RW = 16 * QBW;
   static constexpr int LDS_RING = 4 * RING * SLOT_BYTES;
   static constexpr int LDS_MERGE = 4 * (QBW * NDB * 256 + QBW * 32) * 4;
-  static constexpr int LDS_STAGE = RW * (D + 1) * 4;
+  static constexpr int LDS_STAGE = RW * (D + 4) * 4;
   static constexpr int LDS_A = LDS_RING > LDS_MERGE ? LDS_RING : LDS_MERGE;
   static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
   static_assert(LPC == 8 || LPC == 16, "vmcnt waits below assume 8 or 16 loads per chunk");
@@ -411,7 +327,6 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
   constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NKS = S::NKS, NDB = S::NDB;
   constexpr int SPR = S::SPR, RPL = S::RPL, LPM = S::LPM, RING = S::RING;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS_BYTES];
-  __shared__ int s_ticket;
 
   UnitCtx u;
   if (!decode_unit(a, u)) return;
@@ -542,7 +457,7 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
   // wave_barrier-free rings are idle now; fold the four waves into wave 0
   merge_waves<QBW, NDB, 4>(acc, m_run, l_run, reinterpret_cast<float*>(lds), wave, 0, 1);
   finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wave == 0, 0, acc,
-                           m_run, l_run, lds, &s_ticket);
+                           m_run, l_run, lds);
 }
 
 // ============================================================================
@@ -567,7 +482,7 @@ struct TileShape {
   static constexpr int NDB = D / 16;
   static constexpr int LDS_TILE = (KT * KS + D * VS) * 2;
   static constexpr int LDS_MERGE = WK > 1 ? 4 * (QBW * NDB * 256 + QBW * 32) * 4 : 0;
-  static constexpr int LDS_STAGE = RW * (D + 1) * 4;
+  static constexpr int LDS_STAGE = RW * (D + 4) * 4;
   static constexpr int LDS_A = LDS_TILE > LDS_MERGE ? LDS_TILE : LDS_MERGE;
   static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
   static_assert(NQ >= 8 && (NQ & (NQ - 1)) == 0, "V^T swizzle needs >= 8 key quads, power of 2");
@@ -583,7 +498,6 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
   constexpr int KS = S::KS, VS = S::VS, CPR = S::CPR, KG = S::KG, NQ = S::NQ;
   constexpr int NKS = S::NKS, NDB = S::NDB;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::LDS_BYTES];
-  __shared__ int s_ticket;
   uint16_t* Ks = reinterpret_cast<uint16_t*>(lds_raw);
   uint16_t* Vt = Ks + KT * KS;
 
@@ -733,7 +647,62 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
     __syncthreads();  // tile buffers may be reused for the split weights
   }
   finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wk == 0, r0, acc,
-                           m_run, l_run, lds_raw, &s_ticket);
+                           m_run, l_run, lds_raw);
+}
+
+// ============================================================================
+// merge kernel: one wave per query row combines the splits' partials
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
+  constexpr int PER_LANE = D / 64;  // 1 or 2 floats per lane
+  const int lane = threadIdx.x & 63;
+  const int grow = blockIdx.x * 4 + (threadIdx.x >> 6);  // global row over units x RW
+  const int unit = grow / RW;
+  const int rl = grow - unit * RW;
+  if (unit >= a.units) return;
+  const int qgroup = unit % a.qgroups;
+  const int pair = unit / a.qgroups;
+  const int kvh = pair % a.Hkv;
+  const int b = pair / a.Hkv;
+  const int row = qgroup * RW + rl;
+  if (row >= a.M) return;
+  const int S = a.splits;
+  const size_t base = (size_t)unit * S * RW + rl;
+  // log2-sum-exp of each split (lanes 0..S-1), then normalised weights
+  const float lse = lane < S ? a.part_lse[base + (size_t)lane * RW] : -INFINITY;
+  const float mt = wave_max(lse);
+  const float mu = mt == -INFINITY ? 0.f : mt;
+  const float w = __builtin_amdgcn_exp2f(lse - mu);
+  const float tot = wave_sum_f(w);
+  const int L = a.kv_len[b];
+  const bool bad = L < 0 || L > a.Lmax - a.N;
+  const float inv = (bad || tot == 0.f) ? 0.f : 1.f / tot;
+  float o[PER_LANE];
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) o[e] = 0.f;
+  for (int sp0 = 0; sp0 < S; sp0 += 8) {
+    float v[8][PER_LANE];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float* src = a.part_o + (base + (size_t)(sp0 + q) * RW) * D + lane * PER_LANE;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) v[q][e] = sp0 + q < S ? src[e] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float wq = __shfl(w, (sp0 + q) & 63) * inv;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; ++e) o[e] += sp0 + q < S ? wq * v[q][e] : 0.f;
+    }
+  }
+  const int i = row / a.G;
+  const int h = kvh * a.G + (row - i * a.G);
+  uint16_t* orow = a.out + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PER_LANE;
+  if constexpr (PER_LANE == 2)
+    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0], o[1]);
+  else
+    orow[0] = float_to_bf16_bits(o[0]);
 }
 
 // ---- variants ----------------------------------------------------------------
@@ -795,11 +764,9 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   int splits = (target + padded_units - 1) / padded_units;
   splits = env_int("EAGLE_ATTN_SPLITS", splits);
   if (splits > pieces) splits = pieces;
-  if (splits > 32) splits = 32;  // the merge holds up to 32 weights per row in registers
+  if (splits > 64) splits = 64;  // the merge keeps one split weight per lane
   if (splits < 1) splits = 1;
   p.splits = splits;
-  p.ws_partials = splits > 1 ? (size_t)p.units * splits * vi.rw * (d * 4 + 4) : 0;
-  p.ws_counters = splits > 1 ? (size_t)p.units * 4 : 0;
   return p;
 }
 
@@ -807,10 +774,9 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t tree_attn_workspace_bytes(const AttnPlan& p) {
   if (p.splits <= 1) return 0;
-  const size_t cnt = align256((size_t)p.units * 4);
   const size_t lse = align256((size_t)p.units * p.splits * p.rows_per_wg * 4);
   const size_t o = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
-  return cnt + lse + o;
+  return lse + o;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
@@ -825,11 +791,9 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.anc = anc;
   a.out = out;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const size_t cnt = align256((size_t)plan.units * 4);
   const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
-  a.counters = reinterpret_cast<int32_t*>(w);
-  a.part_lse = reinterpret_cast<float*>(w + cnt);
-  a.part_o = reinterpret_cast<float*>(w + cnt + lse);
+  a.part_lse = reinterpret_cast<float*>(w);
+  a.part_o = reinterpret_cast<float*>(w + lse);
   a.flags = flags;
   a.B = B;
   a.N = N;
@@ -846,7 +810,15 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   const dim3 grid((unsigned)(padded_units * plan.splits));
   void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
   void* args[] = {&a};
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+  hipError_t err = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+  if (err != hipSuccess || plan.splits == 1) return err;
+  const int rw = plan.rows_per_wg;
+  const dim3 mgrid((unsigned)((plan.units * rw + 3) / 4));
+  if (plan.d == 64)
+    tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a, rw);
+  else
+    tree_attn_merge_kernel<128><<<mgrid, 256, 0, s>>>(a, rw);
+  return hipGetLastError();
 }
 
 }  // namespace eagle
