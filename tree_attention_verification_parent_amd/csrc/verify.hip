@@ -1,4 +1,5 @@
-// Vocabulary statistics and the acceptance walk of the verification step.
+// Acceptance walk of the verification step: temperature softmax, multi-round
+// speculative sampling over the draft tree, final-token draw.
 //
 // Speculative sampling accepts a drafted token t with probability
 // min(1, p(t)/p_hat(t)) and, after a rejection, draws from an adjusted
@@ -8,18 +9,23 @@
 // B, the inputs of the procedure).  At temperature 0 the target emits its most
 // probable token (EAGLE-2 overview blog, §1).
 //
-// Two kernels:
-//   vocab_stats  row-parallel over every (sequence, node) target row and
-//                vocabulary chunk: running max and sum of exp((x - max)/T)
-//                (or the argmax at T = 0) per chunk, merged by the last chunk
-//                of each row to finish; flags non-finite logits.
-//   walk         one workgroup per sequence.  The scalar walk reads the row
-//                statistics; a rejection streams the candidate's draft row
-//                once and updates the residual r <- max(0, r/Z - q), held in
-//                registers across the workgroup (V <= 32768), with its mass
-//                summed in fp64.  The final token is an fp64 inverse-CDF scan.
-// A third kernel writes the normalised target rows when the caller asks for
-// them (parity checks only).
+// Layout of the work: one workgroup per tree node, all nodes at once.  The
+// outcome at a node (which candidate it accepts, or which token it would emit
+// if none) depends only on that node's own row, its candidates' draft rows
+// and the uniforms, never on the rest of the walk, so every node computes it
+// speculatively in parallel; the last node of a sequence to finish (atomic
+// ticket) then follows the accepted candidates from the root, a scalar walk.
+//
+// Per node j with candidates c_1..c_k (ascending) and T > 0:
+//   U_0 = exp((l_j - max) / T) (unnormalised target), C_0 = sum U_0
+//   ratio_s = U_{s-1}[t_s] / (C_{s-1} q_s[t_s])       (accept iff u_s < ratio_s)
+//   U_s = max(0, U_{s-1} - C_{s-1} q_s),  C_s = sum U_s  (kept if C_s = 0)
+// U_s / C_s is the adjusted distribution norm(max(0, r - q)) after s
+// rejections.  The rows live in registers across the workgroup (V <= 32768);
+// the next candidate's draft row is prefetched while the current one is
+// consumed; each candidate costs one workgroup barrier, which publishes the
+// partial masses and the next candidate's U element together.  Masses and the
+// inverse-CDF scan of the final draw accumulate in fp64.
 #include <limits.h>
 #include <stdlib.h>
 
@@ -28,234 +34,124 @@
 
 namespace eagle {
 
-struct RowStat {
-  float m;     // row max (T > 0) or max value (T = 0)
-  int amax;    // argmax, lowest id on ties
-  double S;    // sum_v exp((x_v - m) / T)
-};
-
 __device__ __forceinline__ float scaled_exp(float x, float m, float T, bool unit_T) {
   const float z = unit_T ? (x - m) : (x - m) / T;
   return expf(z);
 }
 
-// Combine (m, s) partial softmax statistics.
-__device__ __forceinline__ void ms_combine(float& m, double& s, float mo, double so, float T,
-                                           bool unit_T) {
-  const float mn = fmaxf(m, mo);
-  if (mn == -INFINITY) {
-    m = mn;
-    s = 0.0;
-    return;
-  }
-  const double a = s == 0.0 ? 0.0 : s * (double)scaled_exp(m, mn, T, unit_T);
-  const double bb = so == 0.0 ? 0.0 : so * (double)scaled_exp(mo, mn, T, unit_T);
-  m = mn;
-  s = a + bb;
-}
-
-// Argmax combine: greater value wins, equal values keep the lower id.
-__device__ __forceinline__ void am_combine(float& v, int& i, float vo, int io) {
-  if (vo > v || (vo == v && io < i)) {
-    v = vo;
-    i = io;
-  }
-}
-
-struct StatsArgs {
-  const float* logits;
-  RowStat* stats;
-  RowStat* part;
-  int32_t* counters;
-  int32_t* flags;
-  int rows, N, V, chunks;
-  float T;
+// Per-node results published for the walk (device-coherent stores/loads).
+struct NodeResults {
+  int32_t* acc;      // [B*N] accepted candidate, -1 if none
+  int32_t* bonus;    // [B*N] token drawn if the walk ends here
+  float* ratio;      // [B*N] ratio of node c as tested by its parent's chain
+  int32_t* ntested;  // [B*N] candidates of the node that its chain tested
+  int32_t* counter;  // [B] per-sequence tickets (zero between calls)
 };
 
-__global__ __launch_bounds__(256) void vocab_stats_kernel(StatsArgs a) {
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x / a.chunks;
-  const int ch = blockIdx.x - row * a.chunks;
-  const int V = a.V;
-  const bool vec = (V & 3) == 0;
-  const int V4 = V >> 2;
-  // chunk boundaries in units of 4 elements when vectorised
-  int v0, v1;
-  if (vec) {
-    v0 = (int)((long long)ch * V4 / a.chunks) * 4;
-    v1 = (int)((long long)(ch + 1) * V4 / a.chunks) * 4;
-  } else {
-    v0 = (int)((long long)ch * V / a.chunks);
-    v1 = (int)((long long)(ch + 1) * V / a.chunks);
-  }
-  const float* x = a.logits + (size_t)row * V;
-  const float T = a.T;
-  const bool greedy = T == 0.f;
-  const bool unit_T = T == 1.f;
-  bool nonfinite = false;
-
-  float m = -INFINITY;
-  double s = 0.0;
-  float sf = 0.f;
-  int am = INT_MAX;
-  auto visit = [&](float xv, int v) {
-    if (!isfinite(xv)) {
-      nonfinite = true;
-      return;
-    }
-    if (greedy) {
-      if (xv > m) {  // ids visited in increasing order per thread: first max kept
-        m = xv;
-        am = v;
-      }
-    } else if (xv > m) {
-      sf = sf * scaled_exp(m, xv, T, unit_T) + 1.f;
-      m = xv;
-    } else {
-      sf += scaled_exp(xv, m, T, unit_T);
-    }
-  };
-  if (vec) {
-    for (int v = v0 + 4 * tid; v < v1; v += 4 * 256) {
-      const float4 q = *reinterpret_cast<const float4*>(x + v);
-      visit(q.x, v);
-      visit(q.y, v + 1);
-      visit(q.z, v + 2);
-      visit(q.w, v + 3);
-    }
-  } else {
-    for (int v = v0 + tid; v < v1; v += 256) visit(x[v], v);
-  }
-  s = sf;
-
-  // wave reduction
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float mo = __shfl_xor(m, off);
-    const double so = __shfl_xor(s, off);
-    const int io = __shfl_xor(am, off);
-    if (greedy)
-      am_combine(m, am, mo, io);
-    else
-      ms_combine(m, s, mo, so, T, unit_T);
-  }
-  __shared__ float sm[4];
-  __shared__ double ss[4];
-  __shared__ int si[4];
-  __shared__ int s_last;
-  const int lane = tid & 63, wv = tid >> 6;
-  const uint64_t bad = __ballot(nonfinite);
-  if (lane == 0) {
-    sm[wv] = m;
-    ss[wv] = s;
-    si[wv] = am;
-    if (bad && a.flags) atomicOr(a.flags + row / a.N, EAGLE_FLAG_NONFINITE);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    for (int k = 1; k < 4; ++k) {
-      if (greedy)
-        am_combine(m, am, sm[k], si[k]);
-      else
-        ms_combine(m, s, sm[k], ss[k], T, unit_T);
-    }
-    RowStat r;
-    r.m = m;
-    r.amax = am == INT_MAX ? 0 : am;
-    r.S = s;
-    if (a.chunks == 1) {
-      a.stats[row] = r;
-    } else {
-      a.part[(size_t)row * a.chunks + ch] = r;
-      __threadfence();
-      s_last = atomicAdd(a.counters + row, 1) == a.chunks - 1;
-    }
-  }
-  if (a.chunks == 1) return;
-  __syncthreads();
-  if (!s_last || tid != 0) return;
-  __threadfence();
-  RowStat acc = a.part[(size_t)row * a.chunks];
-  float mm = acc.m;
-  double S = acc.S;
-  int ai = acc.amax;
-  for (int k = 1; k < a.chunks; ++k) {
-    const RowStat p = a.part[(size_t)row * a.chunks + k];
-    if (greedy)
-      am_combine(mm, ai, p.m, p.amax);
-    else
-      ms_combine(mm, S, p.m, p.S, T, unit_T);
-  }
-  RowStat out;
-  out.m = mm;
-  out.amax = ai;
-  out.S = S;
-  a.stats[row] = out;
-  atomicExch(a.counters + row, 0);
-}
-
-// ---------------------------------------------------------------------------
-struct WalkArgs {
+struct VArgs {
   const int32_t* tokens;
   const float* draft;
   const float* logits;
   const int32_t* parents;
   const int32_t* kv_len;
   const float* uniforms;
-  const RowStat* stats;
   int32_t* accept_len;
   int32_t* path;
   int32_t* acc_tokens;
   int32_t* bonus;
   int32_t* kv_src;
+  float* out_probs;
   float* out_final;
   float* out_ratio;
   int32_t* flags;
+  NodeResults nr;
   int N, V;
   float T;
 };
 
+__device__ __forceinline__ void st_c(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_c(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_c(int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_c(float* p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 template <int BLOCK>
-__device__ double block_sum_d(double v, double* red) {
+struct Shared {
+  int par[64], tok[64], kids[64];
+  float u[64], qt[64];
+  float ratio[64];
+  int nk;
+  double red[BLOCK / 64];
+  float redf[BLOCK / 64];
+  int redi[BLOCK / 64];
+  double gsum[8];
+  float next_u[2];  // next candidate's U element: [0] after the update, [1] before
+  int acc, bonus, term;
+  int path[64];
+};
+
+template <int BLOCK>
+__device__ __forceinline__ double block_sum(double v, Shared<BLOCK>& sh) {
   v = wave_sum(v);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t += red[i];
+  for (int i = 0; i < BLOCK / 64; ++i) t += sh.red[i];
   return t;
 }
 
 template <int BLOCK>
-__device__ int block_min_i(int v, int* red) {
+__device__ __forceinline__ float block_max(float v, Shared<BLOCK>& sh) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.redf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < BLOCK / 64; ++i) t = fmaxf(t, sh.redf[i]);
+  return t;
+}
+
+template <int BLOCK>
+__device__ __forceinline__ int block_min_i(int v, Shared<BLOCK>& sh) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.redi[threadIdx.x >> 6] = v;
   __syncthreads();
   int t = INT_MAX;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t = min(t, red[i]);
+  for (int i = 0; i < BLOCK / 64; ++i) t = min(t, sh.redi[i]);
   return t;
 }
 
 template <int BLOCK>
-__device__ int block_max_i(int v, int* red) {
+__device__ __forceinline__ int block_max_i(int v, Shared<BLOCK>& sh) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.redi[threadIdx.x >> 6] = v;
   __syncthreads();
   int t = INT_MIN;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t = max(t, red[i]);
+  for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.redi[i]);
   return t;
 }
 
-// Exclusive prefix over the workgroup (thread order), fp64.
+// Exclusive prefix over the workgroup in thread order, fp64.
 template <int BLOCK>
-__device__ double block_excl_scan_d(double v, double* red) {
+__device__ __forceinline__ double block_excl_scan(double v, Shared<BLOCK>& sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   double incl = v;
 #pragma unroll
@@ -264,293 +160,460 @@ __device__ double block_excl_scan_d(double v, double* red) {
     if (lane >= off) incl += o;
   }
   __syncthreads();
-  if (lane == 63) red[wv] = incl;
+  if (lane == 63) sh.red[wv] = incl;
   __syncthreads();
   double before = 0.0;
-  for (int i = 0; i < wv; ++i) before += red[i];
+  for (int i = 0; i < wv; ++i) before += sh.red[i];
   return before + incl - v;
 }
 
-// Element layout of a vocabulary row across the workgroup: group k, thread t
-// owns elements (k * BLOCK + t) * 4 + e, e = 0..3.
+// A vocabulary row across the workgroup: thread t owns elements
+// (k * BLOCK + t) * 4 + e, k < NPT, e < 4.
 template <int BLOCK, int NPT>
-__global__ __launch_bounds__(BLOCK) void walk_kernel(WalkArgs a) {
-  const int b = blockIdx.x;
+struct Row {
+  float4 v[NPT];
+};
+
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void load_row(Row<BLOCK, NPT>& r, const float* src, int V) {
   const int tid = threadIdx.x;
-  const int N = a.N, V = a.V;
-  const float T = a.T;
-  const bool greedy = T == 0.f;
-  const bool unit_T = T == 1.f;
-  const bool vec = (V & 3) == 0;
-
-  __shared__ int s_par[64], s_tok[64], s_am[64];
-  __shared__ float s_m[64], s_lt[64], s_qt[64], s_u[64], s_ratio[64];
-  __shared__ double s_S[64];
-  __shared__ double red[BLOCK / 64];
-  __shared__ int redi[BLOCK / 64];
-  __shared__ double s_gsum[NPT];
-  __shared__ float s_rt;
-  __shared__ int s_path[64];
-
-  const int L = a.kv_len[b];
-  bool tok_bad = false;
-  if (tid < N) {
-    const size_t o = (size_t)b * N + tid;
-    int par = a.parents[o];
-    if (tid == 0 || par < 0 || par >= tid) par = tid == 0 ? -1 : 0;
-    const int tk = a.tokens[o];
-    s_par[tid] = par;
-    s_tok[tid] = tk;
-    s_u[tid] = a.uniforms[o];
-    s_ratio[tid] = __int_as_float(0x7fc00000);  // NaN: untested
-    const RowStat st = a.stats[o];
-    s_m[tid] = st.m;
-    s_S[tid] = st.S;
-    s_am[tid] = st.amax;
-    float lt = 0.f, qt = 0.f;
-    if (tid > 0) {
-      if (tk < 0 || tk >= V) {
-        tok_bad = true;
-      } else if (!greedy) {
-        lt = a.logits[((size_t)b * N + par) * V + tk];
-        qt = a.draft[o * V + tk];
-      }
-    }
-    s_lt[tid] = lt;
-    s_qt[tid] = qt;
-  }
-  if (__ballot(tok_bad) && (tid & 63) == 0 && a.flags) atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
-  __syncthreads();
-
-  float4 r[NPT];
-  double Z = 0.0;
-  bool have_r = false;
-
-  auto load4 = [&](const float* rowp, int k) -> float4 {
-    const int e0 = (k * BLOCK + tid) * 4;
-    if (vec) {
-      if (e0 < V) return *reinterpret_cast<const float4*>(rowp + e0);
-      return make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float4 o;
-    o.x = e0 + 0 < V ? rowp[e0 + 0] : 0.f;
-    o.y = e0 + 1 < V ? rowp[e0 + 1] : 0.f;
-    o.z = e0 + 2 < V ? rowp[e0 + 2] : 0.f;
-    o.w = e0 + 3 < V ? rowp[e0 + 3] : 0.f;
-    return o;
-  };
-  auto valid = [&](int k, int e) { return (k * BLOCK + tid) * 4 + e < V; };
-
-  // r <- exp((logits[node] - m) / T) (unnormalised p_node), Z <- its sum.
-  auto materialize = [&](int node) {
-    const float* rowp = a.logits + ((size_t)b * N + node) * V;
-    const float m = s_m[node];
+  if ((V & 3) == 0) {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const float4 x = load4(rowp, k);
-      r[k].x = valid(k, 0) ? scaled_exp(x.x, m, T, unit_T) : 0.f;
-      r[k].y = valid(k, 1) ? scaled_exp(x.y, m, T, unit_T) : 0.f;
-      r[k].z = valid(k, 2) ? scaled_exp(x.z, m, T, unit_T) : 0.f;
-      r[k].w = valid(k, 3) ? scaled_exp(x.w, m, T, unit_T) : 0.f;
-    }
-    Z = s_S[node];
-    have_r = true;
-  };
-
-  // r <- max(0, r/Z - q_c), Z <- sum; kept unchanged if the new mass is zero.
-  auto residual = [&](int cnode) {
-    const float* qrow = a.draft + ((size_t)b * N + cnode) * V;
-    const float zf = (float)Z;
-    float4 rn[NPT];
-    double part = 0.0;
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const float4 q = load4(qrow, k);
-      rn[k].x = fmaxf(0.f, r[k].x / zf - q.x);
-      rn[k].y = fmaxf(0.f, r[k].y / zf - q.y);
-      rn[k].z = fmaxf(0.f, r[k].z / zf - q.z);
-      rn[k].w = fmaxf(0.f, r[k].w / zf - q.w);
-      part += (double)rn[k].x + (double)rn[k].y + ((double)rn[k].z + (double)rn[k].w);
-    }
-    const double Zn = block_sum_d<BLOCK>(part, red);
-    if (Zn > 0.0) {
-#pragma unroll
-      for (int k = 0; k < NPT; ++k) r[k] = rn[k];
-      Z = Zn;
-    }
-  };
-
-  // r[t] broadcast through LDS.
-  auto fetch_r = [&](int t) -> float {
-    __syncthreads();
-    const int quad = t >> 2, e = t & 3;
-    const int k = quad / BLOCK, owner = quad - k * BLOCK;
-    if (owner == tid) {
-#pragma unroll
-      for (int kk = 0; kk < NPT; ++kk)
-        if (kk == k) s_rt = e == 0 ? r[kk].x : e == 1 ? r[kk].y : e == 2 ? r[kk].z : r[kk].w;
-    }
-    __syncthreads();
-    return s_rt;
-  };
-
-  int cur = 0;
-  int m_acc = 0;
-  if (tid == 0) s_path[0] = 0;
-  for (;;) {
-    int accepted = -1;
-    for (int cnode = cur + 1; cnode < N; ++cnode) {
-      if (s_par[cnode] != cur) continue;
-      const int tk = s_tok[cnode];
-      const bool tok_ok = tk >= 0 && tk < V;
-      double ratio;
-      if (greedy) {
-        ratio = (tok_ok && tk == s_am[cur]) ? 1.0 : 0.0;
-      } else {
-        double rt;
-        if (!tok_ok) {
-          rt = 0.0;
-        } else if (!have_r) {
-          rt = (double)scaled_exp(s_lt[cnode], s_m[cur], T, unit_T) / s_S[cur];
-        } else {
-          rt = (double)fetch_r(tk) / Z;
-        }
-        const double qt = s_qt[cnode];
-        ratio = qt > 0.0 ? rt / qt : (rt > 0.0 ? (double)INFINITY : 0.0);
-      }
-      if (tid == 0) s_ratio[cnode] = (float)ratio;
-      const bool ok = greedy ? ratio == 1.0 : (double)s_u[cnode] < ratio;
-      if (ok) {
-        accepted = cnode;
-        break;
-      }
-      if (!greedy) {
-        if (!have_r) materialize(cur);
-        residual(cnode);
-      }
-    }
-    if (accepted < 0) break;
-    ++m_acc;
-    if (tid == 0) s_path[m_acc] = accepted;
-    cur = accepted;
-    have_r = false;
-  }
-
-  // ---- final token -------------------------------------------------------------
-  int bonus;
-  if (greedy) {
-    bonus = s_am[cur];
-    if (a.out_final) {
-      float* fo = a.out_final + (size_t)b * V;
-      for (int v = tid; v < V; v += BLOCK) fo[v] = v == bonus ? 1.f : 0.f;
+      const int e0 = (k * BLOCK + tid) * 4;
+      r.v[k] = e0 < V ? *reinterpret_cast<const float4*>(src + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
-    if (!have_r) materialize(cur);
-    double gs[NPT];
-#pragma unroll
-    for (int k = 0; k < NPT; ++k)
-      gs[k] = (double)r[k].x + (double)r[k].y + ((double)r[k].z + (double)r[k].w);
-    // group totals in fixed order
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const double t = block_sum_d<BLOCK>(gs[k], red);
-      if (tid == 0) s_gsum[k] = t;
+      const int e0 = (k * BLOCK + tid) * 4;
+      r.v[k].x = e0 + 0 < V ? src[e0 + 0] : 0.f;
+      r.v[k].y = e0 + 1 < V ? src[e0 + 1] : 0.f;
+      r.v[k].z = e0 + 2 < V ? src[e0 + 2] : 0.f;
+      r.v[k].w = e0 + 3 < V ? src[e0 + 3] : 0.f;
     }
-    __syncthreads();
-    double ztot = 0.0;
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) ztot += s_gsum[k];
-    const double thr = (double)s_u[0] * ztot;
-    double run = 0.0;
-    int kstar = -1;
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      if (kstar < 0 && run + s_gsum[k] > thr) kstar = k;
-      if (kstar < 0) run += s_gsum[k];
-    }
-    int cand = INT_MAX;
-    if (kstar >= 0) {
-      float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-      double tsum = 0.0;
-#pragma unroll
-      for (int k = 0; k < NPT; ++k)
-        if (k == kstar) {
-          rv = r[k];
-          tsum = gs[k];
-        }
-      (void)tsum;
-      const double before = run + block_excl_scan_d<BLOCK>(
-                                      (double)rv.x + (double)rv.y + ((double)rv.z + (double)rv.w), red);
-      const int base = (kstar * BLOCK + tid) * 4;
-      double f = before;
-      const float ev[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f += (double)ev[e];
-        if (cand == INT_MAX && f > thr && base + e < V) cand = base + e;
-      }
-    }
-    int pick = block_min_i<BLOCK>(cand, redi);
-    if (pick == INT_MAX) {  // rounding left no crossing: last id with mass
-      int last = -1;
-#pragma unroll
-      for (int k = 0; k < NPT; ++k) {
-        const int base = (k * BLOCK + tid) * 4;
-        if (r[k].x > 0.f && base + 0 < V) last = max(last, base + 0);
-        if (r[k].y > 0.f && base + 1 < V) last = max(last, base + 1);
-        if (r[k].z > 0.f && base + 2 < V) last = max(last, base + 2);
-        if (r[k].w > 0.f && base + 3 < V) last = max(last, base + 3);
-      }
-      pick = block_max_i<BLOCK>(last, redi);
-      if (pick < 0) pick = 0;
-    }
-    bonus = pick;
-    if (a.out_final) {
-      float* fo = a.out_final + (size_t)b * V;
-      const float zf = (float)Z;
-#pragma unroll
-      for (int k = 0; k < NPT; ++k) {
-        const int base = (k * BLOCK + tid) * 4;
-        if (base + 0 < V) fo[base + 0] = r[k].x / zf;
-        if (base + 1 < V) fo[base + 1] = r[k].y / zf;
-        if (base + 2 < V) fo[base + 2] = r[k].z / zf;
-        if (base + 3 < V) fo[base + 3] = r[k].w / zf;
-      }
-    }
-  }
-
-  __syncthreads();
-  if (tid < N) {
-    const size_t o = (size_t)b * N + tid;
-    const bool on = tid <= m_acc;
-    const int node = on ? s_path[tid] : -1;
-    a.path[o] = node;
-    a.kv_src[o] = on ? L + node : -1;
-    a.acc_tokens[o] = tid < m_acc ? s_tok[s_path[tid + 1]] : -1;
-    if (a.out_ratio) a.out_ratio[o] = s_ratio[tid];
-  }
-  if (tid == 0) {
-    a.accept_len[b] = m_acc;
-    a.bonus[b] = bonus;
   }
 }
 
-// Normalised target rows for parity checks: p = exp((x - m)/T) / S, or one-hot.
-__global__ __launch_bounds__(256) void probs_kernel(const float* __restrict__ logits,
-                                                    const RowStat* __restrict__ stats, int V,
-                                                    int chunks, float T, float* __restrict__ out) {
-  const int row = blockIdx.x / chunks;
-  const int ch = blockIdx.x - row * chunks;
-  const int v0 = (int)((long long)ch * V / chunks), v1 = (int)((long long)(ch + 1) * V / chunks);
-  const RowStat st = stats[row];
-  const float* x = logits + (size_t)row * V;
-  float* o = out + (size_t)row * V;
+__device__ __forceinline__ float comp(const float4& f, int e) {
+  return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
+}
+
+template <int BLOCK, int NPT>
+__device__ __forceinline__ float row_elem(const Row<BLOCK, NPT>& r, int k, int e) {
+  float out = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NPT; ++kk)
+    if (kk == k) out = comp(r.v[kk], e);
+  return out;
+}
+
+// Target row of node j: U = exp((x - m)/T) with its mass C (T > 0), or the
+// argmax (T = 0).  Flags non-finite logits.  Returns the argmax (T = 0).
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int target_row(const VArgs a, int b, int node, Row<BLOCK, NPT>& U, double& C, float& m,
+                          Shared<BLOCK>& sh) {
+  const int tid = threadIdx.x, V = a.V;
+  const float T = a.T;
   const bool unit_T = T == 1.f;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
-    if (T == 0.f)
-      o[v] = v == st.amax ? 1.f : 0.f;
+  load_row<BLOCK, NPT>(U, a.logits + ((size_t)b * a.N + node) * V, V);
+  bool nonfinite = false;
+  float lm = -INFINITY;
+  int li = INT_MAX;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = (k * BLOCK + tid) * 4 + e;
+      const float x = comp(U.v[k], e);
+      if (idx < V) {
+        if (!isfinite(x)) nonfinite = true;
+        else if (x > lm) {  // ids visited in increasing order within a thread
+          lm = x;
+          li = idx;
+        }
+      }
+    }
+  }
+  if (__ballot(nonfinite) && (tid & 63) == 0 && a.flags) atomicOr(a.flags + b, EAGLE_FLAG_NONFINITE);
+  if (T == 0.f) {
+    // argmax: max value, then the lowest id holding it
+    const float mx = block_max<BLOCK>(lm, sh);
+    const int am = block_min_i<BLOCK>(lm == mx ? li : INT_MAX, sh);
+    m = mx;
+    return am == INT_MAX ? 0 : am;
+  }
+  m = block_max<BLOCK>(lm, sh);
+  double part = 0.0;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    float4& f = U.v[k];
+    const int e0 = (k * BLOCK + tid) * 4;
+    f.x = e0 + 0 < V && isfinite(f.x) ? scaled_exp(f.x, m, T, unit_T) : 0.f;
+    f.y = e0 + 1 < V && isfinite(f.y) ? scaled_exp(f.y, m, T, unit_T) : 0.f;
+    f.z = e0 + 2 < V && isfinite(f.z) ? scaled_exp(f.z, m, T, unit_T) : 0.f;
+    f.w = e0 + 3 < V && isfinite(f.w) ? scaled_exp(f.w, m, T, unit_T) : 0.f;
+    part += (double)f.x + (double)f.y + ((double)f.z + (double)f.w);
+  }
+  C = block_sum<BLOCK>(part, sh);
+  return 0;
+}
+
+// Inverse-CDF draw from U / sum(U) with uniform u: the smallest id whose
+// cumulative mass exceeds u * sum; if rounding leaves none, the last id with
+// mass.  fp64 accumulation.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V, Shared<BLOCK>& sh) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const double t = block_sum<BLOCK>(
+        (double)U.v[k].x + (double)U.v[k].y + ((double)U.v[k].z + (double)U.v[k].w), sh);
+    if (tid == 0) sh.gsum[k] = t;
+  }
+  __syncthreads();
+  double ztot = 0.0;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) ztot += sh.gsum[k];
+  const double thr = (double)u * ztot;
+  double run = 0.0;
+  int kstar = -1;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    if (kstar < 0 && run + sh.gsum[k] > thr) kstar = k;
+    if (kstar < 0) run += sh.gsum[k];
+  }
+  int cand = INT_MAX;
+  if (kstar >= 0) {
+    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      if (k == kstar) rv = U.v[k];
+    const double before =
+        run + block_excl_scan<BLOCK>((double)rv.x + (double)rv.y + ((double)rv.z + (double)rv.w), sh);
+    const int base = (kstar * BLOCK + tid) * 4;
+    double f = before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f += (double)comp(rv, e);
+      if (cand == INT_MAX && f > thr && base + e < V) cand = base + e;
+    }
+  }
+  int pick = block_min_i<BLOCK>(cand, sh);
+  if (pick == INT_MAX) {
+    int last = -1;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = (k * BLOCK + tid) * 4 + e;
+        if (idx < V && comp(U.v[k], e) > 0.f) last = idx;
+      }
+    pick = block_max_i<BLOCK>(last, sh);
+    if (pick < 0) pick = 0;
+  }
+  return pick;
+}
+
+// Draft rows are prefetched into LDS with direct-to-LDS loads: thread t's
+// float4 k lands at LDS float4 k*BLOCK + t, the same place it would occupy in
+// the row, so each thread reads back only what it loaded itself (its own
+// vmcnt wait suffices, no barrier).  Rows whose length is not a multiple of 4
+// are loaded straight into registers instead.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void issue_row_lds(const float* src, int V, float4* qlds) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const int e0 = (k * BLOCK + tid) * 4;
+    if (e0 < V)
+      __builtin_amdgcn_global_load_lds(src + e0,
+          (__attribute__((address_space(3))) void*)(qlds + k * BLOCK + wave * 64), 16, 0, 0);
+  }
+}
+
+// The multi-round chain at one node: tests its candidates in order (stopping
+// at the first acceptance when `stop_at_accept`), leaving the adjusted row in
+// U (unnormalised, mass C).  Candidate s's ratio goes to sh.ratio[s].  Returns
+// the index (into sh.kids) of the accepted candidate, or -1.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int run_chain(const VArgs a, int b, Row<BLOCK, NPT>& U, double& C, int nk,
+                         bool stop_at_accept, Shared<BLOCK>& sh, float4* qlds) {
+  const int tid = threadIdx.x, V = a.V, N = a.N;
+  if (nk == 0) return -1;
+  const bool vec = (V & 3) == 0;
+  auto qrow = [&](int s) { return a.draft + ((size_t)b * N + sh.kids[s]) * V; };
+  auto owner_of = [&](int t, int& k, int& e) {
+    const int quad = t >> 2;
+    k = quad / BLOCK;
+    e = t & 3;
+    return quad - k * BLOCK;
+  };
+  if (vec) issue_row_lds<BLOCK, NPT>(qrow(0), V, qlds);
+  float ut = 0.f;
+  {
+    const int t = sh.tok[sh.kids[0]];
+    if (t >= 0 && t < V) {
+      int k, e;
+      if (owner_of(t, k, e) == tid) sh.next_u[0] = row_elem<BLOCK, NPT>(U, k, e);
+    }
+    __syncthreads();
+    ut = (t >= 0 && t < V) ? sh.next_u[0] : 0.f;
+    __syncthreads();
+  }
+  // this thread's float4 k of the current draft row
+  auto qv = [&](int k, int s) -> float4 {
+    const int e0 = (k * BLOCK + tid) * 4;
+    if (e0 >= V) return make_float4(0.f, 0.f, 0.f, 0.f);
+    if (vec) return qlds[k * BLOCK + tid];
+    const float* src = qrow(s) + e0;
+    float4 q;
+    q.x = src[0];
+    q.y = e0 + 1 < V ? src[1] : 0.f;
+    q.z = e0 + 2 < V ? src[2] : 0.f;
+    q.w = e0 + 3 < V ? src[3] : 0.f;
+    return q;
+  };
+  for (int s = 0; s < nk; ++s) {
+    const int c = sh.kids[s];
+    const int t = sh.tok[c];
+    const bool tok_ok = t >= 0 && t < V;
+    const double qt = tok_ok ? (double)sh.qt[c] : 0.0;
+    const double num = tok_ok ? (double)ut : 0.0;
+    double ratio;
+    if (qt > 0.0)
+      ratio = num / (C * qt);
     else
-      o[v] = (float)((double)scaled_exp(x[v], st.m, T, unit_T) / st.S);
+      ratio = num > 0.0 ? (double)INFINITY : 0.0;
+    if (tid == 0) sh.ratio[s] = (float)ratio;
+    if (stop_at_accept && (double)sh.u[c] < ratio) return s;
+    // rejection: U <- max(0, U - C q_s).  Mass first (U kept until it is known
+    // to be non-zero), then the update; q_s is read from LDS both times.
+    if (vec) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
+    const float cf = (float)C;
+    double part = 0.0;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const float4 q = qv(k, s);
+      const float4 w = U.v[k];
+      part += (double)fmaxf(0.f, w.x - cf * q.x) + (double)fmaxf(0.f, w.y - cf * q.y) +
+              ((double)fmaxf(0.f, w.z - cf * q.z) + (double)fmaxf(0.f, w.w - cf * q.w));
+    }
+    // next candidate's element, after and before this update
+    int tn = -1;
+    if (s + 1 < nk) {
+      int kn, en;
+      tn = sh.tok[sh.kids[s + 1]];
+      if (tn >= 0 && tn < V && owner_of(tn, kn, en) == tid) {
+        const float w = row_elem<BLOCK, NPT>(U, kn, en);
+        float q = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPT; ++k)
+          if (k == kn) q = comp(qv(k, s), en);
+        sh.next_u[0] = fmaxf(0.f, w - cf * q);
+        sh.next_u[1] = w;
+      }
+    }
+    const double Cn = block_sum<BLOCK>(part, sh);  // its barriers publish next_u too
+    const bool commit = Cn > 0.0;
+    if (commit) {
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        const float4 q = qv(k, s);
+        U.v[k].x = fmaxf(0.f, U.v[k].x - cf * q.x);
+        U.v[k].y = fmaxf(0.f, U.v[k].y - cf * q.y);
+        U.v[k].z = fmaxf(0.f, U.v[k].z - cf * q.z);
+        U.v[k].w = fmaxf(0.f, U.v[k].w - cf * q.w);
+      }
+      C = Cn;
+    }
+    if (s + 1 < nk) {
+      ut = (tn >= 0 && tn < V) ? sh.next_u[commit ? 0 : 1] : 0.f;
+      if (vec) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads done before the refill
+        issue_row_lds<BLOCK, NPT>(qrow(s + 1), V, qlds);
+      }
+    }
+    __syncthreads();  // next_u may be rewritten in the next round
+  }
+  return -1;
+}
+
+template <int BLOCK, int NPT, bool GREEDY, bool PARITY>
+__global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
+  __shared__ Shared<BLOCK> sh;
+  __shared__ float4 qlds[NPT * BLOCK];
+  const int N = a.N, V = a.V;
+  const int b = blockIdx.x / N;
+  const int j = blockIdx.x - b * N;
+  const int tid = threadIdx.x;
+  constexpr bool greedy = GREEDY;
+  const size_t ob = (size_t)b * N;
+
+  // tree, tokens, uniforms, gathered draft mass of each node's own token
+  bool tok_bad = false;
+  if (tid < N) {
+    int par = a.parents[ob + tid];
+    if (tid == 0 || par < 0 || par >= tid) par = tid == 0 ? -1 : 0;
+    const int tk = a.tokens[ob + tid];
+    sh.par[tid] = par;
+    sh.tok[tid] = tk;
+    sh.u[tid] = a.uniforms[ob + tid];
+    float qt = 0.f;
+    if (tid > 0) {
+      if (tk < 0 || tk >= V)
+        tok_bad = true;
+      else if (!greedy && par == j)
+        qt = a.draft[(ob + tid) * V + tk];
+    }
+    sh.qt[tid] = qt;
+  }
+  if (j == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
+    atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
+  __syncthreads();
+  if (tid == 0) {
+    int nk = 0;
+    for (int c = j + 1; c < N; ++c)
+      if (sh.par[c] == j) sh.kids[nk++] = c;
+    sh.nk = nk;
+  }
+  __syncthreads();
+  const int nk = sh.nk;
+
+  Row<BLOCK, NPT> U;
+  double C = 1.0;
+  float m = 0.f;
+  const int am = target_row<BLOCK, NPT>(a, b, j, U, C, m, sh);
+
+  if (PARITY && a.out_probs) {
+    float* po = a.out_probs + (ob + j) * V;
+    const float inv = greedy ? 0.f : (float)(1.0 / C);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = (k * BLOCK + tid) * 4 + e;
+        if (idx < V) po[idx] = greedy ? (idx == am ? 1.f : 0.f) : (float)((double)comp(U.v[k], e) / C);
+      }
+  }
+
+  int acc = -1, bonus = am, ntested = nk;
+  if constexpr (GREEDY) {
+    for (int s = 0; s < nk; ++s) {
+      const int c = sh.kids[s];
+      const bool ok = sh.tok[c] == am;
+      if (tid == 0) sh.ratio[s] = ok ? 1.f : 0.f;
+      if (ok) {
+        acc = c;
+        ntested = s + 1;
+        break;
+      }
+    }
+  } else {
+    const int si = run_chain<BLOCK, NPT>(a, b, U, C, nk, true, sh, qlds);
+    if (si >= 0) {
+      acc = sh.kids[si];
+      ntested = si + 1;
+    } else {
+      bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh);
+    }
+  }
+  __syncthreads();
+
+  // publish this node's outcome; the last node of the sequence walks the tree
+  if (tid == 0) {
+    st_c(a.nr.acc + ob + j, acc);
+    st_c(a.nr.bonus + ob + j, bonus);
+    st_c(a.nr.ntested + ob + j, ntested);
+  }
+  if (tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int ticket = __hip_atomic_fetch_add(a.nr.counter + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.acc = ticket == N - 1;
+  }
+  __syncthreads();
+  if (!sh.acc) return;
+
+  // ---- walk (last node workgroup of sequence b) ------------------------------
+  if (tid == 0) {
+    int cur = 0, m_acc = 0;
+    sh.path[0] = 0;
+    for (;;) {
+      const int nx = ld_c(a.nr.acc + ob + cur);
+      if (nx < 0 || nx <= cur || nx >= N) break;  // nx > cur for any valid walk
+      sh.path[++m_acc] = nx;
+      cur = nx;
+    }
+    sh.term = cur;
+    sh.bonus = ld_c(a.nr.bonus + ob + cur);
+    sh.nk = m_acc;
+    __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const int m_acc = sh.nk;
+  if (tid < N) {
+    const size_t o = ob + tid;
+    const bool on = tid <= m_acc;
+    const int node = on ? sh.path[tid] : -1;
+    a.path[o] = node;
+    a.kv_src[o] = on ? a.kv_len[b] + node : -1;
+    a.acc_tokens[o] = tid < m_acc ? sh.tok[sh.path[tid + 1]] : -1;
+  }
+  if (tid == 0) {
+    a.accept_len[b] = m_acc;
+    a.bonus[b] = sh.bonus;
+  }
+  if (PARITY && a.out_ratio) {
+    // tested nodes: the candidates each path node's chain tested
+    if (tid < N) {
+      const int c = tid;
+      float r = __int_as_float(0x7fc00000);
+      if (c > 0) {
+        const int p = sh.par[c];
+        bool on_path = false;
+        for (int k = 0; k <= m_acc; ++k) on_path |= sh.path[k] == p;
+        if (on_path) {
+          int rank = 0;
+          for (int x = p + 1; x < c; ++x) rank += sh.par[x] == p;
+          if (rank < ld_c(a.nr.ntested + ob + p)) r = ld_c(a.nr.ratio + ob + c);
+        }
+      }
+      a.out_ratio[ob + c] = r;
+    }
+  }
+  if (PARITY && a.out_final) {
+    // the distribution of the final token: recompute the terminal's chain
+    const int term = sh.term;
+    __syncthreads();
+    if (tid == 0) {
+      int nk2 = 0;
+      for (int c = term + 1; c < N; ++c)
+        if (sh.par[c] == term) sh.kids[nk2++] = c;
+      sh.nk = nk2;
+    }
+    if (tid < N) {
+      const int tk = sh.tok[tid];
+      sh.qt[tid] = (!greedy && tid > 0 && sh.par[tid] == term && tk >= 0 && tk < V)
+                       ? a.draft[(ob + tid) * V + tk] : 0.f;
+    }
+    __syncthreads();
+    float* fo = a.out_final + (size_t)b * V;
+    if constexpr (GREEDY) {
+      const int bt = sh.bonus;
+      for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
+    } else {
+      target_row<BLOCK, NPT>(a, b, term, U, C, m, sh);
+      run_chain<BLOCK, NPT>(a, b, U, C, sh.nk, false, sh, qlds);
+#pragma unroll
+      for (int k = 0; k < NPT; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = (k * BLOCK + tid) * 4 + e;
+          if (idx < V) fo[idx] = (float)((double)comp(U.v[k], e) / C);
+        }
+    }
   }
 }
 
@@ -558,25 +621,19 @@ __global__ __launch_bounds__(256) void probs_kernel(const float* __restrict__ lo
 VerifyPlan plan_verify(int B, int N, int V) {
   VerifyPlan p{};
   p.V = V;
-  const int rows = B * N;
-  int chunks = (2 * kNumCUs + rows - 1) / rows;
-  const int max_chunks = (V + 1023) / 1024;
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  const char* e = getenv("EAGLE_VOCAB_CHUNKS");
-  if (e && *e) chunks = atoi(e) < 1 ? 1 : atoi(e);
-  p.chunks = chunks;
   p.walk_threads = V > 4096 ? 1024 : 256;
-  p.ws_stats = (size_t)rows * sizeof(RowStat);
-  p.ws_partials = chunks > 1 ? (size_t)rows * chunks * sizeof(RowStat) : 0;
-  p.ws_counters = chunks > 1 ? (size_t)rows * 4 : 0;
+  const size_t nodes = (size_t)B * N;
+  p.ws_stats = nodes * 16;  // acc, bonus, ratio, ntested
+  p.ws_counters = (size_t)B * 4;
+  p.ws_partials = 0;
+  p.chunks = 1;
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t verify_workspace_bytes(const VerifyPlan& p) {
-  return align256(p.ws_counters) + align256(p.ws_stats) + align256(p.ws_partials);
+  return align256(p.ws_counters) + align256(p.ws_stats);
 }
 
 hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
@@ -586,56 +643,47 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
                          float* out_probs, float* out_final, float* out_ratio, void* ws,
                          int32_t* flags, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  int32_t* counters = reinterpret_cast<int32_t*>(w);
-  RowStat* stats = reinterpret_cast<RowStat*>(w + align256(plan.ws_counters));
-  RowStat* part = reinterpret_cast<RowStat*>(w + align256(plan.ws_counters) + align256(plan.ws_stats));
-  const int rows = B * N;
-
-  StatsArgs sa{};
-  sa.logits = logits;
-  sa.stats = stats;
-  sa.part = part;
-  sa.counters = counters;
-  sa.flags = flags;
-  sa.rows = rows;
-  sa.N = N;
-  sa.V = plan.V;
-  sa.chunks = plan.chunks;
-  sa.T = T;
-  vocab_stats_kernel<<<rows * plan.chunks, 256, 0, s>>>(sa);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  if (out_probs) {
-    const int pchunks = (plan.V + 4095) / 4096;
-    probs_kernel<<<rows * pchunks, 256, 0, s>>>(logits, stats, plan.V, pchunks, T, out_probs);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-
-  WalkArgs wa{};
-  wa.tokens = tokens;
-  wa.draft = draft;
-  wa.logits = logits;
-  wa.parents = parents;
-  wa.kv_len = kv_len;
-  wa.uniforms = uniforms;
-  wa.stats = stats;
-  wa.accept_len = accept_len;
-  wa.path = path;
-  wa.acc_tokens = acc_tokens;
-  wa.bonus = bonus;
-  wa.kv_src = kv_src;
-  wa.out_final = out_final;
-  wa.out_ratio = out_ratio;
-  wa.flags = flags;
-  wa.N = N;
-  wa.V = plan.V;
-  wa.T = T;
+  const size_t nodes = (size_t)B * N;
+  VArgs a{};
+  a.tokens = tokens;
+  a.draft = draft;
+  a.logits = logits;
+  a.parents = parents;
+  a.kv_len = kv_len;
+  a.uniforms = uniforms;
+  a.accept_len = accept_len;
+  a.path = path;
+  a.acc_tokens = acc_tokens;
+  a.bonus = bonus;
+  a.kv_src = kv_src;
+  a.out_probs = out_probs;
+  a.out_final = out_final;
+  a.out_ratio = out_ratio;
+  a.flags = flags;
+  a.nr.counter = reinterpret_cast<int32_t*>(w);
+  uint8_t* nb = w + align256(plan.ws_counters);
+  a.nr.acc = reinterpret_cast<int32_t*>(nb);
+  a.nr.bonus = reinterpret_cast<int32_t*>(nb + nodes * 4);
+  a.nr.ratio = reinterpret_cast<float*>(nb + nodes * 8);
+  a.nr.ntested = reinterpret_cast<int32_t*>(nb + nodes * 12);
+  a.N = N;
+  a.V = plan.V;
+  a.T = T;
+  const unsigned grid = (unsigned)nodes;
+  const bool greedy = T == 0.f;
+  const bool parity = out_probs || out_final || out_ratio;
+#define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                   \
+  do {                                                                                 \
+    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true><<<grid, BLK, 0, s>>>(a);     \
+    else if (greedy) verify_node_kernel<BLK, NPT, true, false><<<grid, BLK, 0, s>>>(a);         \
+    else if (parity) verify_node_kernel<BLK, NPT, false, true><<<grid, BLK, 0, s>>>(a);         \
+    else verify_node_kernel<BLK, NPT, false, false><<<grid, BLK, 0, s>>>(a);                    \
+  } while (0)
   if (plan.walk_threads == 1024)
-    walk_kernel<1024, 8><<<B, 1024, 0, s>>>(wa);
+    EAGLE_LAUNCH_VERIFY(1024, 8);
   else
-    walk_kernel<256, 4><<<B, 256, 0, s>>>(wa);
+    EAGLE_LAUNCH_VERIFY(256, 4);
+#undef EAGLE_LAUNCH_VERIFY
   return hipGetLastError();
 }
 
