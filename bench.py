@@ -14,6 +14,10 @@ of the inputs that the 256 MB Infinity Cache cannot serve repeats.  Prints
 one JSON line on stdout.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+`--pmc-capture` runs the same steps eagerly (no graph) followed by a
+calibration copy of known size, for rocprofv3 counter passes; it prints one
+JSON line naming what it ran and does not time anything.
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD = "llama2-7b"
 ROTATE_BYTES = 1 << 30
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "tree_attn_llama2-7b_pmc.json")
+COPY_BYTES = 256 << 20  # calibration copy for the counter passes
 
 
 def log(*a):
@@ -87,6 +92,11 @@ class Step:
         self.ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
                           workspace=self.attn_ws)
 
+    def verify(self, i):
+        sl = self.slots[i % len(self.slots)]
+        self.ev.verify_accept(self.tokens, sl["draft"], sl["logits"], self.parents, self.kv_len,
+                              self.T, self.uniforms, outputs=self.res, workspace=self.ver_ws)
+
     def run(self, i):
         ev = self.ev
         sl = self.slots[i % len(self.slots)]
@@ -137,12 +147,43 @@ def measure(torch, ev, W, T, steps, warmup):
     g_step = graph_of(torch, st.run, steps)
     time_graph(torch, g_warm)
     t_step = time_graph(torch, g_step) / steps
-    # attention alone, same rotation, back-to-back launches in one graph
+    acc = st.res["accept_len"].cpu().numpy()
+    # candidates the walk tested (ratio is NaN for untested nodes): every
+    # rejected one costs its draft row on top of the target rows
+    sl = st.slots[0]
+    o = ev.verify_accept(st.tokens, sl["draft"], sl["logits"], st.parents, st.kv_len, st.T,
+                         st.uniforms, want_ratio=True)
+    tested = int((~torch.isnan(o["ratio"])).sum().item())
+    rejected = tested - int(o["accept_len"].sum().item())
+    # attention alone and the walk alone, same rotation, back-to-back launches
+    # in one graph each
     g_attn = graph_of(torch, st.attention, steps)
     time_graph(torch, g_attn)
     t_attn = time_graph(torch, g_attn) / steps
-    acc = st.res["accept_len"].cpu().numpy()
-    return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, accept_len=int(acc[0]), copies=copies)
+    g_ver = graph_of(torch, st.verify, steps)
+    time_graph(torch, g_ver)
+    t_ver = time_graph(torch, g_ver) / steps
+    walk_bytes = cfg.vocab_bytes() + (4 * cfg.V * rejected if T > 0 else 0)
+    return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, t_verify=t_ver, accept_len=int(acc[0]),
+                copies=copies, walk_bytes=walk_bytes, rejected=rejected)
+
+
+def pmc_capture(torch, ev, W, steps):
+    """Eager steps at T=1 over the rotation, then the calibration copy."""
+    cfg = W.get(WORKLOAD)
+    s = W.make_step(cfg, 1.0)
+    per_slot = cfg.attn_bytes() + 2 * cfg.vocab_bytes()
+    st = Step(s, torch, ev, max(2, math.ceil(ROTATE_BYTES / per_slot)))
+    for i in range(steps):
+        st.run(i)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_capture": cfg.name, "steps": steps, "copy_bytes": COPY_BYTES}),
+          flush=True)
 
 
 def cpu_baseline(W, T, budget_s=12.0):
@@ -185,7 +226,7 @@ def pmc_traffic(attn_bytes):
         return None
     if d.get("kernel_source_sha") != kernel_source_hash():
         return None  # kernel changed since the counters were taken
-    return d.get("hbm_bytes_per_launch")
+    return d.get("tree_attn_hbm_bytes_per_launch")
 
 
 def main():
@@ -195,6 +236,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--pmc-capture", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification step is built and timed "
@@ -210,12 +252,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ev.lib()
+    if args.pmc_capture:
+        pmc_capture(torch, ev, W, args.steps)
+        return
     r1 = measure(torch, ev, W, 1.0, args.steps, args.warmup)
     r0 = measure(torch, ev, W, 0.0, args.steps, args.warmup)
     cfg = r1["cfg"]
     tokens = cfg.B * cfg.N
     attn_bytes = cfg.attn_bytes()
     achieved = attn_bytes / r1["t_attn"] / 1e9
+    vocab_bytes = r1["walk_bytes"]  # target rows + the draft row of every rejected candidate
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -242,9 +288,15 @@ def main():
                      "kernel": "tree_attn", "bytes_per_launch": attn_bytes,
                      "us_per_launch": r1["t_attn"] * 1e6},
         "cpu_baseline": cpu,
-        "step_hbm_frac": (attn_bytes + cfg.vocab_bytes()) / r1["t_step"] / 1e9 / HBM_PEAK_GBS,
+        "kernels_us": {"tree_attn": r1["t_attn"] * 1e6, "verify_accept": r1["t_verify"] * 1e6},
+        "verify_roofline": {"bound": "hbm", "bytes_per_launch": vocab_bytes,
+                            "rejected_candidates": r1["rejected"],
+                            "achieved": vocab_bytes / r1["t_verify"] / 1e9,
+                            "frac": vocab_bytes / r1["t_verify"] / 1e9 / HBM_PEAK_GBS},
+        "step_hbm_frac": (attn_bytes + vocab_bytes) / r1["t_step"] / 1e9 / HBM_PEAK_GBS,
         "t0": {"value": tokens / r0["t_step"], "ms_per_step": r0["t_step"] * 1e3,
-               "attn_us": r0["t_attn"] * 1e6, "accept_len": r0["accept_len"]},
+               "attn_us": r0["t_attn"] * 1e6, "verify_us": r0["t_verify"] * 1e6,
+               "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
     }
     print(json.dumps(line), flush=True)
