@@ -21,23 +21,34 @@
 //   ratio_s = U_{s-1}[t_s] / (C_{s-1} q_s[t_s])       (accept iff u_s < ratio_s)
 //   U_s = max(0, U_{s-1} - C_{s-1} q_s),  C_s = sum U_s  (kept if C_s = 0)
 // U_s / C_s is the adjusted distribution norm(max(0, r - q)) after s
-// rejections.  The rows live in registers across the workgroup (V <= 32768);
-// the next candidate's draft row is prefetched while the current one is
-// consumed; each candidate costs one workgroup barrier, which publishes the
-// partial masses and the next candidate's U element together.  Masses and the
-// inverse-CDF scan of the final draw accumulate in fp64.
+// rejections.
+//
+// A node's critical path is a sequence of full-vocabulary passes, each ending
+// in a workgroup reduction, so the kernel is built around short passes:
+//   * the row lives in registers across the 1024-thread workgroup (8 float4
+//     per thread at V <= 32768), entries past V padded so no pass needs a
+//     bounds check;
+//   * a candidate's draft row is prefetched into LDS with direct-to-LDS loads
+//     (each thread's float4 lands where that thread reads it back, so no
+//     barrier guards the buffer) and is read once: the pass builds the updated
+//     row W = max(0, U - C q) in a second register row (the two rows swap
+//     roles each candidate), and the next row's prefetch is issued as soon as
+//     this thread's reads are done;
+//   * wave reductions use DPP within rows of 16 lanes and readlane across the
+//     four rows; a workgroup reduction takes one barrier (two alternating
+//     LDS slot sets);
+//   * masses: fp32 pairwise sums per thread, fp64 across threads, in a fixed
+//     order (deterministic).  The final draw scans in fp64.
+#include <float.h>
 #include <limits.h>
 #include <stdlib.h>
+
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
 
 namespace eagle {
-
-__device__ __forceinline__ float scaled_exp(float x, float m, float T, bool unit_T) {
-  const float z = unit_T ? (x - m) : (x - m) / T;
-  return expf(z);
-}
 
 // Per-node results published for the walk (device-coherent stores/loads).
 struct NodeResults {
@@ -84,373 +95,650 @@ __device__ __forceinline__ float ld_c(float* p) {
       __hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-template <int BLOCK>
+// ---- wave reductions ---------------------------------------------------------
+// DPP lane permutations within a row of 16: swap neighbours, swap pairs, mirror
+// each half row, mirror the row.  After the four steps every lane of a row
+// holds the row's result (the operations are commutative, so both lanes of a
+// pair compute the same value bit for bit); readlane combines the four rows in
+// a fixed order, giving every lane the same wave result.
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  return __hiloint2double(dpp_i<CTRL>(__double2hiint(v)), dpp_i<CTRL>(__double2loint(v)));
+}
+__device__ __forceinline__ int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+__device__ __forceinline__ double wave_allsum(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_allmin_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  return min(min(lane_i(v, 0), lane_i(v, 16)), min(lane_i(v, 32), lane_i(v, 48)));
+}
+__device__ __forceinline__ int wave_allmax_i(int v) {
+  v = max(v, dpp_i<kDppXor1>(v));
+  v = max(v, dpp_i<kDppXor2>(v));
+  v = max(v, dpp_i<kDppHalfMirror>(v));
+  v = max(v, dpp_i<kDppMirror>(v));
+  return max(max(lane_i(v, 0), lane_i(v, 16)), max(lane_i(v, 32), lane_i(v, 48)));
+}
+
+template <int BLOCK, int NPT>
 struct Shared {
+  static constexpr int NW = BLOCK / 64;
   int par[64], tok[64], kids[64];
-  float u[64], qt[64];
+  float u[64];
   float ratio[64];
+  float qt[64 * 64];  // qt[k*64 + i] = q_{kid k}(t_{kid i}) for k <= i (T > 0)
   int nk;
-  double red[BLOCK / 64];
-  float redf[BLOCK / 64];
-  int redi[BLOCK / 64];
-  double gsum[8];
-  float next_u[2];  // next candidate's U element: [0] after the update, [1] before
-  int acc, bonus, term;
+  // workgroup reductions: two slot sets, used alternately (see rb below)
+  double rd[2][NW];
+  float rf[2][NW];
+  int ri[2][NW];
+  float nu[2][2];  // next candidate's U element: [0] after the update, [1] before
+  double sel_before;
+  int sel_entry;
+  int pick;
+  int last, term;
+  int wacc[64], wbonus[64], wnt[64];
   int path[64];
 };
 
-template <int BLOCK>
-__device__ __forceinline__ double block_sum(double v, Shared<BLOCK>& sh) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+// Workgroup reductions.  `rb` selects the slot set and flips on every call;
+// all threads make the same sequence of calls, so a slot set is rewritten
+// only after the barrier of the reduction in between, which every reader of
+// its previous contents has passed: one barrier per reduction suffices.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ double block_sum(double v, Shared<BLOCK, NPT>& sh, int& rb) {
+  v = wave_allsum(v);
+  const int buf = rb;
+  rb ^= 1;
+  if ((threadIdx.x & 63) == 0) sh.rd[buf][threadIdx.x >> 6] = v;
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t += sh.red[i];
+  for (int i = 0; i < BLOCK / 64; ++i) t += sh.rd[buf][i];
   return t;
 }
 
-template <int BLOCK>
-__device__ __forceinline__ float block_max(float v, Shared<BLOCK>& sh) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.redf[threadIdx.x >> 6] = v;
+template <int BLOCK, int NPT>
+__device__ __forceinline__ float block_max(float v, Shared<BLOCK, NPT>& sh, int& rb) {
+  v = wave_allmax(v);
+  const int buf = rb;
+  rb ^= 1;
+  if ((threadIdx.x & 63) == 0) sh.rf[buf][threadIdx.x >> 6] = v;
   __syncthreads();
   float t = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t = fmaxf(t, sh.redf[i]);
+  for (int i = 0; i < BLOCK / 64; ++i) t = fmaxf(t, sh.rf[buf][i]);
   return t;
 }
 
-template <int BLOCK>
-__device__ __forceinline__ int block_min_i(int v, Shared<BLOCK>& sh) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.redi[threadIdx.x >> 6] = v;
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int block_min_i(int v, Shared<BLOCK, NPT>& sh, int& rb) {
+  v = wave_allmin_i(v);
+  const int buf = rb;
+  rb ^= 1;
+  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
   __syncthreads();
   int t = INT_MAX;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t = min(t, sh.redi[i]);
+  for (int i = 0; i < BLOCK / 64; ++i) t = min(t, sh.ri[buf][i]);
   return t;
 }
 
-template <int BLOCK>
-__device__ __forceinline__ int block_max_i(int v, Shared<BLOCK>& sh) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.redi[threadIdx.x >> 6] = v;
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& rb) {
+  v = wave_allmax_i(v);
+  const int buf = rb;
+  rb ^= 1;
+  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
   __syncthreads();
   int t = INT_MIN;
 #pragma unroll
-  for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.redi[i]);
+  for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.ri[buf][i]);
   return t;
 }
 
-// Exclusive prefix over the workgroup in thread order, fp64.
-template <int BLOCK>
-__device__ __forceinline__ double block_excl_scan(double v, Shared<BLOCK>& sh) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  double incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  __syncthreads();
-  if (lane == 63) sh.red[wv] = incl;
-  __syncthreads();
-  double before = 0.0;
-  for (int i = 0; i < wv; ++i) before += sh.red[i];
-  return before + incl - v;
-}
-
+// ---- rows --------------------------------------------------------------------
 // A vocabulary row across the workgroup: thread t owns elements
-// (k * BLOCK + t) * 4 + e, k < NPT, e < 4.
+// (k * BLOCK + t) * 4 + e, k < NPT, e < 4 ("slab" k, coalesced float4 loads).
 template <int BLOCK, int NPT>
 struct Row {
   float4 v[NPT];
 };
 
+__device__ __forceinline__ float comp(const float4& f, int e) {
+  return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
+}
+
+// Logit row into registers; entries past V read as -FLT_MAX (no mass, never
+// the maximum of a row that has a finite entry).
 template <int BLOCK, int NPT>
-__device__ __forceinline__ void load_row(Row<BLOCK, NPT>& r, const float* src, int V) {
+__device__ __forceinline__ void load_logits(Row<BLOCK, NPT>& r, const float* src, int V) {
   const int tid = threadIdx.x;
+  // every load is issued at an in-range address and the padding selected
+  // afterwards, so the loads need no branches
   if ((V & 3) == 0) {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      r.v[k] = e0 < V ? *reinterpret_cast<const float4*>(src + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = e0 < V;
+      const float4 x = *reinterpret_cast<const float4*>(src + (in ? e0 : 0));
+      r.v[k] = in ? x : make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      r.v[k].x = e0 + 0 < V ? src[e0 + 0] : 0.f;
-      r.v[k].y = e0 + 1 < V ? src[e0 + 1] : 0.f;
-      r.v[k].z = e0 + 2 < V ? src[e0 + 2] : 0.f;
-      r.v[k].w = e0 + 3 < V ? src[e0 + 3] : 0.f;
+      const float x0 = src[min(e0 + 0, V - 1)], x1 = src[min(e0 + 1, V - 1)];
+      const float x2 = src[min(e0 + 2, V - 1)], x3 = src[min(e0 + 3, V - 1)];
+      r.v[k].x = e0 + 0 < V ? x0 : -FLT_MAX;
+      r.v[k].y = e0 + 1 < V ? x1 : -FLT_MAX;
+      r.v[k].z = e0 + 2 < V ? x2 : -FLT_MAX;
+      r.v[k].w = e0 + 3 < V ? x3 : -FLT_MAX;
     }
   }
 }
 
-__device__ __forceinline__ float comp(const float4& f, int e) {
-  return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
+// exp(z) for z <= 0 as 2^(z log2 e) with the rounding error of the product
+// carried as a first-order correction (relative error ~2 ulp).  Arguments
+// below -110 (results below the fp32 range) are clamped, which keeps the
+// correction finite for the -FLT_MAX padding.
+__device__ __forceinline__ float exp_neg(float z) {
+  z = fmaxf(z, -110.f);
+  constexpr float kL2E = 1.44269502162933349609375f;  // log2(e), fp32 head
+  constexpr float kL2ELo = 1.925963033500011e-08f;    // log2(e) - kL2E
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float t = z * kL2E;
+  const float err = fmaf(z, kL2ELo, fmaf(z, kL2E, -t));
+  const float r = __builtin_amdgcn_exp2f(t);
+  return fmaf(r, err * kLn2, r);
 }
 
-template <int BLOCK, int NPT>
-__device__ __forceinline__ float row_elem(const Row<BLOCK, NPT>& r, int k, int e) {
-  float out = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < NPT; ++kk)
-    if (kk == k) out = comp(r.v[kk], e);
-  return out;
+__device__ __forceinline__ float sum4(const float4& f) { return (f.x + f.y) + (f.z + f.w); }
+
+template <int NPT>
+__device__ __forceinline__ float pairwise(const float (&s)[NPT]) {
+  if constexpr (NPT == 16) {
+    return (((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]))) +
+           (((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15])));
+  } else if constexpr (NPT == 8) {
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  } else {
+    static_assert(NPT == 4, "rows of 4, 8 or 16 float4 per thread");
+    return (s[0] + s[1]) + (s[2] + s[3]);
+  }
 }
 
-// Target row of node j: U = exp((x - m)/T) with its mass C (T > 0), or the
-// argmax (T = 0).  Flags non-finite logits.  Returns the argmax (T = 0).
-template <int BLOCK, int NPT>
-__device__ __forceinline__ int target_row(const VArgs a, int b, int node, Row<BLOCK, NPT>& U, double& C, float& m,
-                          Shared<BLOCK>& sh) {
-  const int tid = threadIdx.x, V = a.V;
-  const float T = a.T;
-  const bool unit_T = T == 1.f;
-  load_row<BLOCK, NPT>(U, a.logits + ((size_t)b * a.N + node) * V, V);
-  bool nonfinite = false;
-  float lm = -INFINITY;
-  int li = INT_MAX;
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = (k * BLOCK + tid) * 4 + e;
-      const float x = comp(U.v[k], e);
-      if (idx < V) {
-        if (!isfinite(x)) nonfinite = true;
-        else if (x > lm) {  // ids visited in increasing order within a thread
-          lm = x;
-          li = idx;
-        }
-      }
-    }
-  }
-  if (__ballot(nonfinite) && (tid & 63) == 0 && a.flags) atomicOr(a.flags + b, EAGLE_FLAG_NONFINITE);
-  if (T == 0.f) {
-    // argmax: max value, then the lowest id holding it
-    const float mx = block_max<BLOCK>(lm, sh);
-    const int am = block_min_i<BLOCK>(lm == mx ? li : INT_MAX, sh);
-    m = mx;
-    return am == INT_MAX ? 0 : am;
-  }
-  m = block_max<BLOCK>(lm, sh);
-  double part = 0.0;
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    float4& f = U.v[k];
-    const int e0 = (k * BLOCK + tid) * 4;
-    f.x = e0 + 0 < V && isfinite(f.x) ? scaled_exp(f.x, m, T, unit_T) : 0.f;
-    f.y = e0 + 1 < V && isfinite(f.y) ? scaled_exp(f.y, m, T, unit_T) : 0.f;
-    f.z = e0 + 2 < V && isfinite(f.z) ? scaled_exp(f.z, m, T, unit_T) : 0.f;
-    f.w = e0 + 3 < V && isfinite(f.w) ? scaled_exp(f.w, m, T, unit_T) : 0.f;
-    part += (double)f.x + (double)f.y + ((double)f.z + (double)f.w);
-  }
-  C = block_sum<BLOCK>(part, sh);
-  return 0;
+// The scaled exponent of one logit, exactly as the row pass computes it
+// (non-finite logits have no mass).
+__device__ __forceinline__ float target_entry(float x, float m, bool unit, float invT) {
+  x = isfinite(x) ? x : -FLT_MAX;
+  return exp_neg(unit ? x - m : (x - m) * invT);
 }
 
-// Inverse-CDF draw from U / sum(U) with uniform u: the smallest id whose
-// cumulative mass exceeds u * sum; if rounding leaves none, the last id with
-// mass.  fp64 accumulation.
-template <int BLOCK, int NPT>
-__device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V, Shared<BLOCK>& sh) {
+// Target row statistics of one node from its logits (already in U): flags
+// non-finite logits (they are given no mass); T = 0 returns the lowest-index
+// argmax; T > 0 turns U into exp((l - max)/T) and returns its mass in C.
+// before_sum(buf, m, unit, invT) runs before the mass reduction, whose
+// barrier (slot set buf, also returned in sum_buf) publishes what it writes.
+template <int BLOCK, int NPT, bool GREEDY, typename F>
+__device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
+                                            double& C, int& sum_buf, F&& before_sum,
+                                            Shared<BLOCK, NPT>& sh, int& rb) {
   const int tid = threadIdx.x;
+  // x * 0 is NaN exactly for non-finite x: one fma per entry
+  float bad = 0.f;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
-    const double t = block_sum<BLOCK>(
-        (double)U.v[k].x + (double)U.v[k].y + ((double)U.v[k].z + (double)U.v[k].w), sh);
-    if (tid == 0) sh.gsum[k] = t;
+    bad = fmaf(U.v[k].x, 0.f, bad);
+    bad = fmaf(U.v[k].y, 0.f, bad);
+    bad = fmaf(U.v[k].z, 0.f, bad);
+    bad = fmaf(U.v[k].w, 0.f, bad);
   }
-  __syncthreads();
-  double ztot = 0.0;
+  const bool nonfinite = bad != bad;
+  if (nonfinite) {
 #pragma unroll
-  for (int k = 0; k < NPT; ++k) ztot += sh.gsum[k];
-  const double thr = (double)u * ztot;
-  double run = 0.0;
-  int kstar = -1;
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    if (kstar < 0 && run + sh.gsum[k] > thr) kstar = k;
-    if (kstar < 0) run += sh.gsum[k];
-  }
-  int cand = INT_MAX;
-  if (kstar >= 0) {
-    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < NPT; ++k)
-      if (k == kstar) rv = U.v[k];
-    const double before =
-        run + block_excl_scan<BLOCK>((double)rv.x + (double)rv.y + ((double)rv.z + (double)rv.w), sh);
-    const int base = (kstar * BLOCK + tid) * 4;
-    double f = before;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f += (double)comp(rv, e);
-      if (cand == INT_MAX && f > thr && base + e < V) cand = base + e;
+    for (int k = 0; k < NPT; ++k) {
+      float4& f = U.v[k];
+      f.x = isfinite(f.x) ? f.x : -FLT_MAX;
+      f.y = isfinite(f.y) ? f.y : -FLT_MAX;
+      f.z = isfinite(f.z) ? f.z : -FLT_MAX;
+      f.w = isfinite(f.w) ? f.w : -FLT_MAX;
     }
   }
-  int pick = block_min_i<BLOCK>(cand, sh);
-  if (pick == INT_MAX) {
-    int last = -1;
+  if (__ballot(nonfinite) && (tid & 63) == 0 && flags) atomicOr(flags + b, EAGLE_FLAG_NONFINITE);
+
+  if constexpr (GREEDY) {
+    float lm = -INFINITY;
+    int li = INT_MAX;
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int idx = (k * BLOCK + tid) * 4 + e;
-        if (idx < V && comp(U.v[k], e) > 0.f) last = idx;
+        const float x = comp(U.v[k], e);
+        const bool gt = x > lm;  // ids increase with (k, e): first maximum kept
+        lm = gt ? x : lm;
+        li = gt ? (k * BLOCK + tid) * 4 + e : li;
       }
-    pick = block_max_i<BLOCK>(last, sh);
-    if (pick < 0) pick = 0;
+    const float mx = block_max<BLOCK, NPT>(lm, sh, rb);
+    const int am = block_min_i<BLOCK, NPT>(lm == mx ? li : INT_MAX, sh, rb);
+    C = 1.0;
+    sum_buf = 0;
+    return am == INT_MAX ? 0 : am;
+  } else {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
+    const float m = block_max<BLOCK, NPT>(lm, sh, rb);
+    const bool unit = T == 1.f;
+    const float invT = 1.f / T;
+    float s[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      float4& f = U.v[k];
+      f.x = exp_neg(unit ? f.x - m : (f.x - m) * invT);  // already finite
+      f.y = exp_neg(unit ? f.y - m : (f.y - m) * invT);
+      f.z = exp_neg(unit ? f.z - m : (f.z - m) * invT);
+      f.w = exp_neg(unit ? f.w - m : (f.w - m) * invT);
+      s[k] = sum4(f);
+    }
+    sum_buf = rb;
+    before_sum(sum_buf, m, unit, invT);
+    C = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s), sh, rb);
+    return 0;
   }
-  return pick;
 }
 
-// Draft rows are prefetched into LDS with direct-to-LDS loads: thread t's
-// float4 k lands at LDS float4 k*BLOCK + t, the same place it would occupy in
-// the row, so each thread reads back only what it loaded itself (its own
-// vmcnt wait suffices, no barrier).  Rows whose length is not a multiple of 4
-// are loaded straight into registers instead.
+// Children of node j in ascending order into sh.kids / sh.nk.  Wave 0 only;
+// the caller synchronises.
 template <int BLOCK, int NPT>
-__device__ __forceinline__ void issue_row_lds(const float* src, int V, float4* qlds) {
+__device__ __forceinline__ void find_kids(int N, int j, Shared<BLOCK, NPT>& sh) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  const bool kid = lane < N && lane > j && sh.par[lane] == j;
+  const uint64_t mask = __ballot(kid);
+  if (kid) sh.kids[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+  if (lane == 0) sh.nk = __popcll(mask);
+}
+
+// f(std::integral_constant<int, J>) for J = 0..N-1, unrolled.
+template <typename F, int... J>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// Position of q_{kid k}(t_{kid i}), k <= i < nk, in sh.qt.
+__device__ __forceinline__ int tri(int k, int i, int) { return k * 64 + i; }
+
+// A draft row -> LDS with direct-to-LDS loads: thread t's float4 k lands at
+// LDS float4 k*BLOCK + t, where only thread t reads it back.  Slots past V are
+// not loaded (zeroed once by node_setup).  V % 4 == 0.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void issue_row_lds(const float* row, int V, float4* qlds) {
   const int tid = threadIdx.x, wave = tid >> 6;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
     const int e0 = (k * BLOCK + tid) * 4;
     if (e0 < V)
-      __builtin_amdgcn_global_load_lds(src + e0,
+      __builtin_amdgcn_global_load_lds(row + e0,
           (__attribute__((address_space(3))) void*)(qlds + k * BLOCK + wave * 64), 16, 0, 0);
   }
 }
 
+// One candidate of the multi-round chain at a node: the ratio test of
+// candidate s against the current row `cur` (mass C, entry ut at the
+// candidate's token) and, on rejection, the adjusted row into `nxt`.
+// Returns true if the candidate is accepted; otherwise `nxt` holds the current
+// row afterwards (the update, or a copy of `cur` in the rare case that the
+// update leaves no mass).  Lane i < nk of wave 0 carries `val`, the current
+// row's entry at candidate i's token, updated with the same fp32 operations as
+// the row (so bit-identical to it) from the gathered sh.qt table.  With VEC,
+// row s is in (or arriving in) qlds and row s+1's prefetch is issued here.
+template <int BLOCK, int NPT, bool VEC>
+__device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<BLOCK, NPT>& cur,
+                                           Row<BLOCK, NPT>& nxt, double& C, float& ut, float& val,
+                                           int s, int nk, bool stop_at_accept,
+                                           Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
+  const int tid = threadIdx.x, V = a.V;
+  auto qrow = [&](int i) { return a.draft + (ob + sh.kids[i]) * V; };
+  const int c = sh.kids[s];
+  const int t = sh.tok[c];
+  const bool tok_ok = t >= 0 && t < V;
+  const double qt = tok_ok ? (double)sh.qt[tri(s, s, nk)] : 0.0;
+  const double num = tok_ok ? (double)ut : 0.0;
+  // ratio = num / (C qt); accept iff u < ratio, tested without the division
+  // (q = 0: ratio is +inf when num > 0, else 0)
+  const double den = C * qt;
+  const bool accept = qt > 0.0 ? (double)sh.u[c] * den < num : num > 0.0;
+  if (tid == 0)
+    sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
+  if (stop_at_accept && accept) return true;
+  // rejection: nxt = max(0, cur - C q_s) and its mass, one read of q_s
+  if (VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
+  const float cf = (float)C;
+  const bool more = s + 1 < nk;
+  const float* qs = qrow(s);
+  float ps[NPT];
+  float4 qv[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    if constexpr (VEC) {
+      qv[k] = qlds[k * BLOCK + tid];
+    } else {
+      const int e0 = (k * BLOCK + tid) * 4;
+      const float x0 = qs[min(e0 + 0, V - 1)], x1 = qs[min(e0 + 1, V - 1)];
+      const float x2 = qs[min(e0 + 2, V - 1)], x3 = qs[min(e0 + 3, V - 1)];
+      qv[k] = make_float4(e0 + 0 < V ? x0 : 0.f, e0 + 1 < V ? x1 : 0.f, e0 + 2 < V ? x2 : 0.f,
+                          e0 + 3 < V ? x3 : 0.f);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const float4 q = qv[k];
+    float4& w = nxt.v[k];
+    w.x = fmaxf(0.f, fmaf(-cf, q.x, cur.v[k].x));
+    w.y = fmaxf(0.f, fmaf(-cf, q.y, cur.v[k].y));
+    w.z = fmaxf(0.f, fmaf(-cf, q.z, cur.v[k].z));
+    w.w = fmaxf(0.f, fmaf(-cf, q.w, cur.v[k].w));
+    ps[k] = sum4(w);
+  }
+  // next candidate's entry, after and before this update (its tracking lane),
+  // published by the reduction's barrier
+  const int buf = rb;
+  int tn = -1;
+  if (more) {
+    tn = sh.tok[sh.kids[s + 1]];
+    if (tid == s + 1) {
+      sh.nu[buf][0] = fmaxf(0.f, fmaf(-cf, sh.qt[tri(s, tid, nk)], val));
+      sh.nu[buf][1] = val;
+    }
+    if constexpr (VEC) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of q_s done
+      issue_row_lds<BLOCK, NPT>(qrow(s + 1), V, qlds);
+    }
+  }
+  const double Cn = block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);
+  const bool commit = Cn > 0.0;
+  if (commit) {
+    C = Cn;
+    if (tid > s && tid < nk) val = fmaxf(0.f, fmaf(-cf, sh.qt[tri(s, tid, nk)], val));
+  } else {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) nxt.v[k] = cur.v[k];
+  }
+  if (more) ut = (tn >= 0 && tn < V) ? sh.nu[buf][commit ? 0 : 1] : 0.f;
+  return false;
+}
+
 // The multi-round chain at one node: tests its candidates in order (stopping
 // at the first acceptance when `stop_at_accept`), leaving the adjusted row in
-// U (unnormalised, mass C).  Candidate s's ratio goes to sh.ratio[s].  Returns
-// the index (into sh.kids) of the accepted candidate, or -1.
-template <int BLOCK, int NPT>
-__device__ __forceinline__ int run_chain(const VArgs a, int b, Row<BLOCK, NPT>& U, double& C, int nk,
-                         bool stop_at_accept, Shared<BLOCK>& sh, float4* qlds) {
-  const int tid = threadIdx.x, V = a.V, N = a.N;
-  if (nk == 0) return -1;
-  const bool vec = (V & 3) == 0;
-  auto qrow = [&](int s) { return a.draft + ((size_t)b * N + sh.kids[s]) * V; };
-  auto owner_of = [&](int t, int& k, int& e) {
-    const int quad = t >> 2;
-    k = quad / BLOCK;
-    e = t & 3;
-    return quad - k * BLOCK;
-  };
-  if (vec) issue_row_lds<BLOCK, NPT>(qrow(0), V, qlds);
-  float ut = 0.f;
-  {
-    const int t = sh.tok[sh.kids[0]];
-    if (t >= 0 && t < V) {
-      int k, e;
-      if (owner_of(t, k, e) == tid) sh.next_u[0] = row_elem<BLOCK, NPT>(U, k, e);
-    }
-    __syncthreads();
-    ut = (t >= 0 && t < V) ? sh.next_u[0] : 0.f;
-    __syncthreads();
-  }
-  // this thread's float4 k of the current draft row
-  auto qv = [&](int k, int s) -> float4 {
-    const int e0 = (k * BLOCK + tid) * 4;
-    if (e0 >= V) return make_float4(0.f, 0.f, 0.f, 0.f);
-    if (vec) return qlds[k * BLOCK + tid];
-    const float* src = qrow(s) + e0;
-    float4 q;
-    q.x = src[0];
-    q.y = e0 + 1 < V ? src[1] : 0.f;
-    q.z = e0 + 2 < V ? src[2] : 0.f;
-    q.w = e0 + 3 < V ? src[3] : 0.f;
-    return q;
-  };
-  for (int s = 0; s < nk; ++s) {
-    const int c = sh.kids[s];
-    const int t = sh.tok[c];
-    const bool tok_ok = t >= 0 && t < V;
-    const double qt = tok_ok ? (double)sh.qt[c] : 0.0;
-    const double num = tok_ok ? (double)ut : 0.0;
-    double ratio;
-    if (qt > 0.0)
-      ratio = num / (C * qt);
-    else
-      ratio = num > 0.0 ? (double)INFINITY : 0.0;
-    if (tid == 0) sh.ratio[s] = (float)ratio;
-    if (stop_at_accept && (double)sh.u[c] < ratio) return s;
-    // rejection: U <- max(0, U - C q_s).  Mass first (U kept until it is known
-    // to be non-zero), then the update; q_s is read from LDS both times.
-    if (vec) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
-    const float cf = (float)C;
-    double part = 0.0;
+// U (unnormalised, mass C).  ut is U's entry at the first candidate's token,
+// val the per-lane candidate entries (see chain_step).  Candidate s's ratio
+// goes to sh.ratio[s].  Returns the index (into sh.kids) of the accepted
+// candidate, or -1.  With VEC (V % 4 == 0) the first candidate's row prefetch
+// must already be issued.  Two rows alternate as current and next, so a step
+// moves no registers.
+template <int BLOCK, int NPT, bool VEC>
+__device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, NPT>& U, double& C,
+                                         float ut, float val, int nk, bool stop_at_accept,
+                                         Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
+  Row<BLOCK, NPT> W;
+  for (int s = 0; s < nk; s += 2) {
+    if (chain_step<BLOCK, NPT, VEC>(a, ob, U, W, C, ut, val, s, nk, stop_at_accept, sh, qlds, rb))
+      return s;
+    if (s + 1 >= nk) {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const float4 q = qv(k, s);
-      const float4 w = U.v[k];
-      part += (double)fmaxf(0.f, w.x - cf * q.x) + (double)fmaxf(0.f, w.y - cf * q.y) +
-              ((double)fmaxf(0.f, w.z - cf * q.z) + (double)fmaxf(0.f, w.w - cf * q.w));
+      for (int k = 0; k < NPT; ++k) U.v[k] = W.v[k];
+      break;
     }
-    // next candidate's element, after and before this update
-    int tn = -1;
-    if (s + 1 < nk) {
-      int kn, en;
-      tn = sh.tok[sh.kids[s + 1]];
-      if (tn >= 0 && tn < V && owner_of(tn, kn, en) == tid) {
-        const float w = row_elem<BLOCK, NPT>(U, kn, en);
-        float q = 0.f;
-#pragma unroll
-        for (int k = 0; k < NPT; ++k)
-          if (k == kn) q = comp(qv(k, s), en);
-        sh.next_u[0] = fmaxf(0.f, w - cf * q);
-        sh.next_u[1] = w;
-      }
-    }
-    const double Cn = block_sum<BLOCK>(part, sh);  // its barriers publish next_u too
-    const bool commit = Cn > 0.0;
-    if (commit) {
-#pragma unroll
-      for (int k = 0; k < NPT; ++k) {
-        const float4 q = qv(k, s);
-        U.v[k].x = fmaxf(0.f, U.v[k].x - cf * q.x);
-        U.v[k].y = fmaxf(0.f, U.v[k].y - cf * q.y);
-        U.v[k].z = fmaxf(0.f, U.v[k].z - cf * q.z);
-        U.v[k].w = fmaxf(0.f, U.v[k].w - cf * q.w);
-      }
-      C = Cn;
-    }
-    if (s + 1 < nk) {
-      ut = (tn >= 0 && tn < V) ? sh.next_u[commit ? 0 : 1] : 0.f;
-      if (vec) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads done before the refill
-        issue_row_lds<BLOCK, NPT>(qrow(s + 1), V, qlds);
-      }
-    }
-    __syncthreads();  // next_u may be rewritten in the next round
+    if (chain_step<BLOCK, NPT, VEC>(a, ob, W, U, C, ut, val, s + 1, nk, stop_at_accept, sh, qlds,
+                                    rb))
+      return s + 1;
   }
   return -1;
 }
 
-template <int BLOCK, int NPT, bool GREEDY, bool PARITY>
+// Set-up of one node's chain after the tree is in LDS and the node's logits
+// were issued into U: its children, the first candidate's row prefetch, the
+// table qt[k][i] = q_{kid k}(t_{kid i}) and each candidate's own logit
+// (gathered while the row pass runs), then the row statistics.  Returns the
+// argmax (T = 0); sets C, ut (U at the first candidate's token) and, on lane
+// i < nk of wave 0, val = U at candidate i's token.
+template <int BLOCK, int NPT, bool GREEDY, bool VEC>
+__device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, int b,
+                                          int32_t* flags, Row<BLOCK, NPT>& U, double& C, float& ut,
+                                          float& val, Shared<BLOCK, NPT>& sh, float4* qlds,
+                                          int& rb) {
+  const int tid = threadIdx.x, V = a.V;
+  find_kids<BLOCK, NPT>(a.N, node, sh);
+  __syncthreads();
+  const int nk = sh.nk;
+  int sum_buf = 0;
+  ut = 0.f;
+  val = 0.f;
+  if constexpr (GREEDY) {
+    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, sum_buf,
+                                          [](int, float, bool, float) {}, sh, rb);
+  } else {
+    if constexpr (VEC) {
+      // slots past V are never loaded: zero this thread's (the pass reads them)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k)
+        if ((k * BLOCK + tid) * 4 >= V) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (nk > 0) issue_row_lds<BLOCK, NPT>(a.draft + (ob + sh.kids[0]) * V, V, qlds);
+    }
+    constexpr int G = (64 * 64 + BLOCK - 1) / BLOCK;
+    float g[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const int f = r * BLOCK + tid;
+      const int k = f / 64, i = f & 63;
+      g[r] = 0.f;
+      if (k <= i && i < nk) {
+        const int t = sh.tok[sh.kids[i]];
+        if (t >= 0 && t < V) g[r] = a.draft[(ob + sh.kids[k]) * V + t];
+      }
+    }
+    float lt = 0.f;
+    int t_own = -1;
+    if (tid < nk) {
+      t_own = sh.tok[sh.kids[tid]];
+      if (t_own >= 0 && t_own < V) lt = a.logits[(ob + node) * V + t_own];
+    }
+    target_stats<BLOCK, NPT, false>(
+        U, a.T, b, flags, C, sum_buf,
+        [&](int buf, float m, bool unit, float invT) {
+#pragma unroll
+          for (int r = 0; r < G; ++r) {
+            const int f = r * BLOCK + tid;
+            const int k = f / 64, i = f & 63;
+            if (k <= i && i < nk) sh.qt[tri(k, i, nk)] = g[r];
+          }
+          if (tid < nk) {
+            val = target_entry(lt, m, unit, invT);
+            if (tid == 0) sh.nu[buf][1] = val;
+          }
+        },
+        sh, rb);
+    if (nk > 0) {
+      const int t0 = sh.tok[sh.kids[0]];
+      ut = (t0 >= 0 && t0 < V) ? sh.nu[sum_buf][1] : 0.f;
+    }
+    return 0;
+  }
+}
+
+// Inverse-CDF draw from U / sum(U) with uniform u: the smallest id whose
+// cumulative mass exceeds u * sum; if rounding leaves none, the last id with
+// mass.  fp64 cumulative sums in id order.  The masses of the 4-id groups are
+// laid out in LDS in id order (`part`, NPT*BLOCK doubles, free memory); each
+// thread then owns NPT consecutive groups, each wave 64 threads of them: the
+// wave totals locate the wave, a lane scan the thread, its groups the group
+// and the group's owner the id.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V,
+                                           Shared<BLOCK, NPT>& sh, double* part, int& rb) {
+  constexpr int NW = BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+    part[k * BLOCK + tid] =
+        (((double)U.v[k].x + (double)U.v[k].y) + (double)U.v[k].z) + (double)U.v[k].w;
+  __syncthreads();
+  double e[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) e[i] = part[tid * NPT + i];
+  double own = 0.0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) own += e[i];
+  const double wt = wave_allsum(own);
+  const int wbuf = rb;
+  rb ^= 1;
+  if (lane == 0) sh.rd[wbuf][wave] = wt;
+  if (tid == 0) sh.pick = -1;
+  __syncthreads();
+  double Z = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) Z += sh.rd[wbuf][i];
+  const double thr = (double)u * Z;
+  int ws = NW - 1;  // rounding may leave no crossing: then the last wave
+  double before_w = 0.0, run = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const double nx = run + sh.rd[wbuf][i];
+    if (ws == NW - 1 && i < NW - 1 && nx > thr) {
+      ws = i;
+      before_w = run;
+    }
+    if (i == NW - 1 && ws == NW - 1) before_w = run;
+    run = nx;
+  }
+  if (wave == ws) {
+    double incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const uint64_t hm = __ballot(before_w + incl > thr);
+    const int L = hm ? __ffsll((unsigned long long)hm) - 1 : 63;
+    if (lane == L) {
+      double f = before_w + (incl - own);
+      int sel = -1;
+      double before_e = 0.0;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        if (sel < 0 && f + e[i] > thr) {
+          sel = i;
+          before_e = f;
+        }
+        f += e[i];
+      }
+      if (sel < 0) {  // rounding: the lane's last group
+        sel = NPT - 1;
+        before_e = f - e[NPT - 1];
+      }
+      sh.sel_entry = tid * NPT + sel;
+      sh.sel_before = before_e;
+    }
+  }
+  __syncthreads();
+  {
+    const int entry = sh.sel_entry;
+    const int ks = entry / BLOCK, ts = entry - ks * BLOCK;
+    if (tid == ts) {
+      float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < NPT; ++k)
+        if (k == ks) rv = U.v[k];
+      const int id0 = entry * 4;
+      double f = sh.sel_before;
+      int cand = -1, lastpos = -1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float x = comp(rv, c);
+        f += (double)x;
+        if (id0 + c < V && x > 0.f) {
+          lastpos = id0 + c;
+          if (cand < 0 && f > thr) cand = id0 + c;
+        }
+      }
+      sh.pick = cand >= 0 ? cand : lastpos;
+    }
+  }
+  __syncthreads();
+  int pick = sh.pick;
+  if (pick < 0) {
+    int last = -1;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = (k * BLOCK + tid) * 4 + c;
+        if (idx < V && comp(U.v[k], c) > 0.f) last = idx;
+      }
+    pick = block_max_i<BLOCK, NPT>(last, sh, rb);
+    if (pick < 0) pick = 0;
+  }
+  return pick;
+}
+
+template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC>
 __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
-  __shared__ Shared<BLOCK> sh;
-  __shared__ float4 qlds[NPT * BLOCK];
+  __shared__ Shared<BLOCK, NPT> sh;
+  __shared__ float4 qlds[GREEDY ? 1 : NPT * BLOCK];  // draft-row prefetch
   const int N = a.N, V = a.V;
   const int b = blockIdx.x / N;
   const int j = blockIdx.x - b * N;
   const int tid = threadIdx.x;
-  constexpr bool greedy = GREEDY;
   const size_t ob = (size_t)b * N;
+  int rb = 0;
 
-  // tree, tokens, uniforms, gathered draft mass of each node's own token
+  // the node's logit row first: its latency overlaps the tree set-up
+  Row<BLOCK, NPT> U;
+  load_logits<BLOCK, NPT>(U, a.logits + (ob + j) * V, V);
+
+  // tree, tokens, uniforms
   bool tok_bad = false;
   if (tid < N) {
     int par = a.parents[ob + tid];
@@ -459,41 +747,24 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     sh.par[tid] = par;
     sh.tok[tid] = tk;
     sh.u[tid] = a.uniforms[ob + tid];
-    float qt = 0.f;
-    if (tid > 0) {
-      if (tk < 0 || tk >= V)
-        tok_bad = true;
-      else if (!greedy && par == j)
-        qt = a.draft[(ob + tid) * V + tk];
-    }
-    sh.qt[tid] = qt;
+    tok_bad = tid > 0 && (tk < 0 || tk >= V);
   }
   if (j == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
     atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
   __syncthreads();
-  if (tid == 0) {
-    int nk = 0;
-    for (int c = j + 1; c < N; ++c)
-      if (sh.par[c] == j) sh.kids[nk++] = c;
-    sh.nk = nk;
-  }
-  __syncthreads();
-  const int nk = sh.nk;
-
-  Row<BLOCK, NPT> U;
   double C = 1.0;
-  float m = 0.f;
-  const int am = target_row<BLOCK, NPT>(a, b, j, U, C, m, sh);
+  float ut = 0.f, val = 0.f;
+  const int am = node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, C, ut, val, sh, qlds, rb);
+  const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
     float* po = a.out_probs + (ob + j) * V;
-    const float inv = greedy ? 0.f : (float)(1.0 / C);
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = (k * BLOCK + tid) * 4 + e;
-        if (idx < V) po[idx] = greedy ? (idx == am ? 1.f : 0.f) : (float)((double)comp(U.v[k], e) / C);
+        if (idx < V) po[idx] = GREEDY ? (idx == am ? 1.f : 0.f) : (float)((double)comp(U.v[k], e) / C);
       }
   }
 
@@ -510,14 +781,16 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
       }
     }
   } else {
-    const int si = run_chain<BLOCK, NPT>(a, b, U, C, nk, true, sh, qlds);
+    const int si = run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, nk, true, sh, qlds, rb);
     if (si >= 0) {
       acc = sh.kids[si];
       ntested = si + 1;
     } else {
-      bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh);
+      bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh, reinterpret_cast<double*>(qlds), rb);
     }
   }
+  // a prefetch left in flight by an early acceptance must land before exit
+  if (!GREEDY && VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // publish this node's outcome; the last node of the sequence walks the tree
@@ -531,23 +804,29 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   __syncthreads();
   if (tid == 0) {
     const int ticket = __hip_atomic_fetch_add(a.nr.counter + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.acc = ticket == N - 1;
+    sh.last = ticket == N - 1;
   }
   __syncthreads();
-  if (!sh.acc) return;
+  if (!sh.last) return;
 
   // ---- walk (last node workgroup of sequence b) ------------------------------
+  if (tid < N) {
+    sh.wacc[tid] = ld_c(a.nr.acc + ob + tid);
+    sh.wbonus[tid] = ld_c(a.nr.bonus + ob + tid);
+    sh.wnt[tid] = ld_c(a.nr.ntested + ob + tid);
+  }
+  __syncthreads();
   if (tid == 0) {
     int cur = 0, m_acc = 0;
     sh.path[0] = 0;
     for (;;) {
-      const int nx = ld_c(a.nr.acc + ob + cur);
+      const int nx = sh.wacc[cur];
       if (nx < 0 || nx <= cur || nx >= N) break;  // nx > cur for any valid walk
       sh.path[++m_acc] = nx;
       cur = nx;
     }
     sh.term = cur;
-    sh.bonus = ld_c(a.nr.bonus + ob + cur);
+    sh.pick = sh.wbonus[cur];
     sh.nk = m_acc;
     __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -563,7 +842,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   }
   if (tid == 0) {
     a.accept_len[b] = m_acc;
-    a.bonus[b] = sh.bonus;
+    a.bonus[b] = sh.pick;
   }
   if (PARITY && a.out_ratio) {
     // tested nodes: the candidates each path node's chain tested
@@ -577,7 +856,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
         if (on_path) {
           int rank = 0;
           for (int x = p + 1; x < c; ++x) rank += sh.par[x] == p;
-          if (rank < ld_c(a.nr.ntested + ob + p)) r = ld_c(a.nr.ratio + ob + c);
+          if (rank < sh.wnt[p]) r = ld_c(a.nr.ratio + ob + c);
         }
       }
       a.out_ratio[ob + c] = r;
@@ -586,26 +865,15 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   if (PARITY && a.out_final) {
     // the distribution of the final token: recompute the terminal's chain
     const int term = sh.term;
-    __syncthreads();
-    if (tid == 0) {
-      int nk2 = 0;
-      for (int c = term + 1; c < N; ++c)
-        if (sh.par[c] == term) sh.kids[nk2++] = c;
-      sh.nk = nk2;
-    }
-    if (tid < N) {
-      const int tk = sh.tok[tid];
-      sh.qt[tid] = (!greedy && tid > 0 && sh.par[tid] == term && tk >= 0 && tk < V)
-                       ? a.draft[(ob + tid) * V + tk] : 0.f;
-    }
+    const int bt = sh.pick;
     __syncthreads();
     float* fo = a.out_final + (size_t)b * V;
     if constexpr (GREEDY) {
-      const int bt = sh.bonus;
       for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
     } else {
-      target_row<BLOCK, NPT>(a, b, term, U, C, m, sh);
-      run_chain<BLOCK, NPT>(a, b, U, C, sh.nk, false, sh, qlds);
+      load_logits<BLOCK, NPT>(U, a.logits + (ob + term) * V, V);
+      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, C, ut, val, sh, qlds, rb);
+      run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, sh.nk, false, sh, qlds, rb);
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
 #pragma unroll
@@ -672,12 +940,15 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   const unsigned grid = (unsigned)nodes;
   const bool greedy = T == 0.f;
   const bool parity = out_probs || out_final || out_ratio;
-#define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                   \
-  do {                                                                                 \
-    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true><<<grid, BLK, 0, s>>>(a);     \
-    else if (greedy) verify_node_kernel<BLK, NPT, true, false><<<grid, BLK, 0, s>>>(a);         \
-    else if (parity) verify_node_kernel<BLK, NPT, false, true><<<grid, BLK, 0, s>>>(a);         \
-    else verify_node_kernel<BLK, NPT, false, false><<<grid, BLK, 0, s>>>(a);                    \
+  const bool vec = (plan.V & 3) == 0;
+#define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                        \
+  do {                                                                                      \
+    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true><<<grid, BLK, 0, s>>>(a);    \
+    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true><<<grid, BLK, 0, s>>>(a);        \
+    else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true><<<grid, BLK, 0, s>>>(a); \
+    else if (parity) verify_node_kernel<BLK, NPT, false, true, false><<<grid, BLK, 0, s>>>(a);       \
+    else if (vec) verify_node_kernel<BLK, NPT, false, false, true><<<grid, BLK, 0, s>>>(a);          \
+    else verify_node_kernel<BLK, NPT, false, false, false><<<grid, BLK, 0, s>>>(a);                  \
   } while (0)
   if (plan.walk_threads == 1024)
     EAGLE_LAUNCH_VERIFY(1024, 8);
