@@ -119,7 +119,8 @@ EAGLE_API size_t eagle_tree_attn_workspace(int B, int N, int Hq, int Hkv, int d,
  *   sm_scale softmax scale; <= 0 selects 1/sqrt(d)
  *   out      device [B, N, Hq, d] bf16 (round to nearest even); fp32 inside
  *   workspace device, eagle_tree_attn_workspace() bytes (split partials; any
- *            contents, may be 0 bytes when no split is needed)
+ *            contents; calls that overlap must not share it; may be 0 bytes
+ *            when no split is needed)
  *   seq_flags device [B] int32 or NULL (EAGLE_FLAG_BAD_KV_LEN; that
  *            sequence's output is zero)
  * Supported: d in {64, 128}; Hq % Hkv == 0; 1 <= N <= 64; Lmax >= N.

@@ -99,10 +99,12 @@ def test_attention_split_counts_agree(splits, monkeypatch):
     assert np.abs(got - ref).max() < ATOL_ATTN
 
 
-def test_attention_chain_and_scale():
-    cfg = W.shrink(W.get(0), B=1, N=16, Hq=4, Hkv=2, d=128, V=16)
-    s = W.make_step(cfg, 1.0, seed=3, parents=trees.chain(16), kv_lens=[333])
-    say("attention chain + explicit scale")
+@pytest.mark.parametrize("N,Hq,Hkv,d", [(16, 4, 2, 128), (32, 4, 4, 64)])
+def test_attention_chain_and_scale(N, Hq, Hkv, d):
+    # a chain is the deepest tree: every node attends to all earlier tree keys
+    cfg = W.shrink(W.get(0), B=1, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
+    s = W.make_step(cfg, 1.0, seed=3, parents=trees.chain(N), kv_lens=[333])
+    say(f"attention chain N={N} + explicit scale")
     got, _, _, _ = run_attention(s, sm_scale=0.05)
     ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, sm_scale=0.05)
     assert np.abs(got - ref).max() < ATOL_ATTN

@@ -44,6 +44,84 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// ---- wave reductions ---------------------------------------------------------
+// DPP lane permutations within a row of 16: swap neighbours, swap pairs, mirror
+// each half row, mirror the row.  After the four steps every lane of a row
+// holds the row's result (the operations are commutative, so both lanes of a
+// pair compute the same value bit for bit); readlane combines the four rows in
+// a fixed order, giving every lane the same wave result.
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  return __hiloint2double(dpp_i<CTRL>(__double2hiint(v)), dpp_i<CTRL>(__double2loint(v)));
+}
+__device__ __forceinline__ int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+__device__ __forceinline__ double wave_allsum(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_allmin_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  return min(min(lane_i(v, 0), lane_i(v, 16)), min(lane_i(v, 32), lane_i(v, 48)));
+}
+__device__ __forceinline__ int wave_allmax_i(int v) {
+  v = max(v, dpp_i<kDppXor1>(v));
+  v = max(v, dpp_i<kDppXor2>(v));
+  v = max(v, dpp_i<kDppHalfMirror>(v));
+  v = max(v, dpp_i<kDppMirror>(v));
+  return max(max(lane_i(v, 0), lane_i(v, 16)), max(lane_i(v, 32), lane_i(v, 48)));
+}
+
+// Sums of M values over the wave at once (the M reductions interleave, so
+// their latencies overlap); every lane receives every sum.
+template <int M>
+__device__ __forceinline__ void wave_allsum_n(float (&v)[M]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i) v[i] += dpp_f<kDppXor1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < M; ++i) v[i] += dpp_f<kDppXor2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < M; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < M; ++i) v[i] += dpp_f<kDppMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    v[i] = (lane_f(v[i], 0) + lane_f(v[i], 16)) + (lane_f(v[i], 32) + lane_f(v[i], 48));
+}
+
 // Number of compute units the grids are shaped for (MI355X: 8 XCDs x 32 CUs).
 constexpr int kNumCUs = 256;
 constexpr int kNumXCDs = 8;

@@ -52,6 +52,7 @@ struct AttnArgs {
   float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
   int32_t* flags;
   int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
+  int tree_in_merge;  // the merge adds each query's tree keys (ring variants)
   float scale_log2;
 };
 
@@ -285,92 +286,184 @@ __device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_ru
 }
 
 // ============================================================================
-// ring kernel: per-wave LDS rings filled by direct-to-LDS loads
+// ring kernel: committed prefix only, one direct-to-LDS chunk slot per wave
 // ============================================================================
+// Eight waves, each with one 32-key K/V slot in LDS.  The chunks of a split
+// are dealt to them round robin; a wave waits for its chunk, computes it and
+// refills the slot with its next chunk, while the other seven keep theirs in
+// flight (two waves per SIMD hide each other's MFMA and softmax latency).
+// The split ranges are laid over the cache capacity Lmax - N, not over
+// kv_len, so the first loads go out before anything else is read; keys at or
+// past kv_len are masked.  The tree keys (each query's ancestors and itself)
+// are left to the merge kernel, which makes every wave's share of a split the
+// same.
+constexpr int kRingThreads = 64 * 8;
+
 template <int D_, int QBW_>
 struct RingShape {
   static constexpr int D = D_;
   static constexpr int QBW = QBW_;
-  static constexpr int RING = 2;                  // chunk slots per wave
+  static constexpr int NWAVE = 8;
+  static constexpr int THREADS = 64 * NWAVE;
   static constexpr int MAT_BYTES = 32 * D * 2;    // K (or V) of one 32-key chunk
   static constexpr int SLOT_BYTES = 2 * MAT_BYTES;
   static constexpr int SPR = D / 8;               // 16-byte slots per key row
   static constexpr int RPL = 64 / SPR;            // key rows per wave-wide direct load
   static constexpr int LPM = 32 / RPL;            // direct loads per matrix
-  static constexpr int LPC = 2 * LPM;             // direct loads per chunk
   static constexpr int NKS = D / 32, NDB = D / 16;
   static constexpr int RW = 16 * QBW;
-  static constexpr int LDS_RING = 4 * RING * SLOT_BYTES;
-  static constexpr int LDS_MERGE = 4 * (QBW * NDB * 256 + QBW * 32) * 4;
-  static constexpr int LDS_STAGE = RW * (D + 4) * 4;
-  static constexpr int LDS_A = LDS_RING > LDS_MERGE ? LDS_RING : LDS_MERGE;
-  static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
-  static_assert(LPC == 8 || LPC == 16, "vmcnt waits below assume 8 or 16 loads per chunk");
+  static constexpr int ACC_BYTES = QBW * NDB * 256 * 4;  // one wave's accumulators
+  static_assert(ACC_BYTES <= SLOT_BYTES, "a wave's state is parked in its own slot");
+  static constexpr int LDS_RING = NWAVE * SLOT_BYTES;
+  static constexpr int LDS_ML = NWAVE * QBW * 32 * 4;   // each wave's m and l
+  static constexpr int LDS_STAGE = RW * (D + 4) * 4;    // the combined split partial
+  static constexpr int LDS_BYTES = LDS_RING + LDS_ML + LDS_STAGE;
 };
 
-// Wait until the oldest outstanding chunk has landed in LDS; loads complete in
-// issue order, so at most one younger chunk (LPC loads) may remain in flight.
-template <int LPC>
-__device__ __forceinline__ void wait_chunk(bool another_in_flight) {
-  if (another_in_flight) {
-    if constexpr (LPC == 16)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+// The NWAVE waves' online-softmax states for the same query rows combined in
+// one round: every wave parks its accumulators in its own (now idle) slot and
+// its m, l beside the ring; after one barrier the waves share out the
+// (query block, d block) tiles of the result, each combining all NWAVE states
+// of its tiles, and write the split's normalised rows and log2-sum-exp to the
+// staging area ([RW][D + 4], column D = log2-sum-exp).
+template <int QBW, int NDB, int NWAVE, int SLOT_BYTES>
+__device__ __forceinline__ void fold_waves(const f32x4 (&acc)[QBW][NDB], const float (&m_run)[QBW],
+                                           const float (&l_run)[QBW], uint8_t* lds, float* ml,
+                                           float* stage, int wave) {
+  constexpr int D = NDB * 16, SD = D + 4;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  float* mine = reinterpret_cast<float*>(lds + wave * SLOT_BYTES);
+  if (wave < NWAVE) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(mine + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
+      if (g == 0) {
+        ml[(wave * QBW + qb) * 32 + c] = m_run[qb];
+        ml[(wave * QBW + qb) * 32 + 16 + c] = l_run[qb];
+      }
+    }
+  }
+  __syncthreads();
+  for (int it = wave; it < QBW * NDB && wave < NWAVE; it += NWAVE) {
+    const int qb = it / NDB, db = it - qb * NDB;
+    float ms[NWAVE], mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      ms[w] = ml[(w * QBW + qb) * 32 + c];
+      mt = fmaxf(mt, ms[w]);
+    }
+    const float mu = mt == -INFINITY ? 0.f : mt;
+    float lt = 0.f;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const float f = __builtin_amdgcn_exp2f(ms[w] - mu);
+      lt += ml[(w * QBW + qb) * 32 + 16 + c] * f;
+      o += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds + w * SLOT_BYTES) +
+                                           ((qb * NDB + db) * 64 + lane) * 4) * f;
+    }
+    const int rl = qb * 16 + c;
+    const float inv = lt == 0.f ? 0.f : 1.f / lt;
+    *reinterpret_cast<f32x4*>(stage + rl * SD + db * 16 + 4 * g) = o * inv;
+    if (db == 0 && g == 0) stage[rl * SD + D] = lt == 0.f ? -INFINITY : mt + __log2f(lt);
+  }
+  __syncthreads();
+}
+
+// Valid committed keys among key0..key0+7 (keys below L) as an 8-bit mask.
+__device__ __forceinline__ uint32_t prefix_mask8(int key0, int L) {
+  const int below = L - key0;
+  return below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
+}
+
+template <int D>
+__device__ __forceinline__ void load_pair(const uint16_t* p, float (&x)[D / 64]) {
+  if constexpr (D / 64 == 2) {
+    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = bf16_bits_to_float(w2 & 0xffffu);
+    x[1] = bf16_bits_to_float(w2 >> 16);
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    x[0] = bf16_bits_to_float(p[0]);
   }
 }
 
 template <class S>
-__global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
+__global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) {
   constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NKS = S::NKS, NDB = S::NDB;
-  constexpr int SPR = S::SPR, RPL = S::RPL, LPM = S::LPM, RING = S::RING;
+  constexpr int SPR = S::SPR, RPL = S::RPL, LPM = S::LPM, NWAVE = S::NWAVE;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS_BYTES];
-
-  UnitCtx u;
-  if (!decode_unit(a, u)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int L = u.L;
 
-  // This split's chunks; wave w takes chunks cb + w, cb + w + 4, ...
-  const int n_chunks = (u.total + 31) / 32;
-  const int cb = (int)((long long)u.split * n_chunks / a.splits);
-  const int ce = (int)((long long)(u.split + 1) * n_chunks / a.splits);
+  // workgroup -> (unit, split): all splits of a unit on one XCD
+  const int xcd = blockIdx.x % kNumXCDs, slotw = blockIdx.x / kNumXCDs;
+  const int split = slotw % a.splits;
+  const int unit = (slotw / a.splits) * kNumXCDs + xcd;
+  if (unit >= a.units) return;
+  const int kvh = unit % a.Hkv;  // qgroups == 1 for ring variants
+  const int b = unit / a.Hkv;
+
+  // this split's chunks of the capacity prefix; wave w takes cb + w, cb + w + NWAVE, ...
+  const int Lp = a.Lmax - a.N;
+  const int n_chunks = (Lp + 31) / 32;
+  const int cb = (int)((long long)split * n_chunks / a.splits);
+  const int ce = (int)((long long)(split + 1) * n_chunks / a.splits);
   const int my_first = cb + wave;
-  const int my_n = my_first < ce ? (ce - my_first + 3) / 4 : 0;
+  const int my_n = my_first < ce ? (ce - my_first + NWAVE - 1) / NWAVE : 0;
 
-  bf16x8 qf[QBW][NKS];
-  uint64_t anc_q[QBW];
-  load_queries<D, QBW, RW>(a, u, 0, qf, anc_q);
-
-  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
+  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   const uint16_t* kp = a.k + kv_base;
   const uint16_t* vp = a.v + kv_base;
-  uint8_t* ring = lds + wave * RING * S::SLOT_BYTES;
+  uint8_t* slot = lds + wave * S::SLOT_BYTES;
 
   // Direct-to-LDS fill of one chunk: lane l writes 16 bytes at load base + 16 l,
   // i.e. row t*RPL + l/SPR, slot l%SPR, which receives global slot (l%SPR)^swz(row).
-  // Rows past the last key re-read the last key (finite data, masked later).
+  // Rows past the prefix re-read its last key (finite data, masked later).
   const int r_in = lane / SPR, p_in = lane % SPR;
-  auto issue = [&](int gc, int slot) {
-    uint8_t* dst = ring + slot * S::SLOT_BYTES;
+  auto issue = [&](int gc) {
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
-      const int key = min(gc * 32 + r, u.total - 1);
+      const int key = min(gc * 32 + r, Lp - 1);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(dst + t * RPL * D * 2), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(slot + t * RPL * D * 2), 16, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
-      const int key = min(gc * 32 + r, u.total - 1);
+      const int key = min(gc * 32 + r, Lp - 1);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(dst + S::MAT_BYTES + t * RPL * D * 2), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(slot + S::MAT_BYTES + t * RPL * D * 2), 16, 0, 0);
     }
   };
+  if (my_n > 0) issue(my_first);
+
+  // committed length, then the queries (needed only once the first chunk is in)
+  int L = a.kv_len[b];
+  const bool bad = L < 0 || L > Lp;
+  if (bad) {
+    L = 0;
+    if (a.flags && split == 0 && kvh == 0 && tid == 0) atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+  }
+  const int rows = min(RW, a.M);
+  bf16x8 qf[QBW][NKS];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int row = qb * 16 + c;
+    if (row < a.M) {
+      const int i = row / a.G;
+      const int h = kvh * a.G + (row - i * a.G);
+      const uint16_t* qrow = a.q + (((size_t)b * a.N + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] = bf16x8{};
+    }
+  }
 
   f32x4 acc[QBW][NDB];
   float m_run[QBW], l_run[QBW];
@@ -382,20 +475,15 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-#pragma unroll
-  for (int i = 0; i < RING; ++i)
-    if (i < my_n) issue(my_first + 4 * i, i);
-
   for (int i = 0; i < my_n; ++i) {
-    const int gc = my_first + 4 * i;
-    const int slot = i % RING;
-    wait_chunk<S::LPC>(i + 1 < my_n);
-    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(ring + slot * S::SLOT_BYTES);
-    const uint8_t* Vb = ring + slot * S::SLOT_BYTES + S::MAT_BYTES;
+    const int gc = my_first + NWAVE * i;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
+    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
+    const uint8_t* Vb = slot + S::MAT_BYTES;
 
-    f32x4 s[QBW][2];
+    f32x4 sc[QBW][2];
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QBW; ++qb) sc[qb][0] = sc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hlf = 0; hlf < 2; ++hlf) {
       // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
@@ -406,19 +494,19 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kc + kr * D + (((ks * 4 + g) ^ sw) * 8));
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb)
-          s[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], s[qb][hlf], 0, 0, 0);
+          sc[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[qb][hlf], 0, 0, 0);
       }
     }
     const int key0 = gc * 32 + 8 * g;
     const bool need_mask = gc * 32 + 32 > L;
+    const uint32_t ok = prefix_mask8(key0, L);
     bf16x8 pf[QBW];
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = s[qb][j >> 2][j & 3] * a.scale_log2;
+      for (int j = 0; j < 8; ++j) x[j] = sc[qb][j >> 2][j & 3] * a.scale_log2;
       if (need_mask) {
-        const uint32_t ok = key_mask8(key0, L, anc_q[qb]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
       }
@@ -443,9 +531,9 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
       for (int qb = 0; qb < QBW; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
     }
-    if (i + RING < my_n) {
+    if (i + 1 < my_n) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
-      issue(my_first + 4 * (i + RING), slot);
+      issue(gc + NWAVE);
     }
   }
 
@@ -454,10 +542,20 @@ __global__ __launch_bounds__(256) void tree_attn_ring_kernel(AttnArgs a) {
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
-  // wave_barrier-free rings are idle now; fold the four waves into wave 0
-  merge_waves<QBW, NDB, 4>(acc, m_run, l_run, reinterpret_cast<float*>(lds), wave, 0, 1);
-  finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wave == 0, 0, acc,
-                           m_run, l_run, lds);
+  // this split's partial (O / l and log2-sum-exp), staged in LDS so that the
+  // stores are coalesced; the merge kernel adds the tree keys and combines
+  float* ml = reinterpret_cast<float*>(lds + S::LDS_RING);
+  float* stage = reinterpret_cast<float*>(lds + S::LDS_RING + S::LDS_ML);
+  fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(acc, m_run, l_run, lds, ml, stage, wave);
+  constexpr int SD = D + 4;
+  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
+  constexpr int D4 = D / 4;
+  for (int it = tid; it < rows * D4; it += S::THREADS) {
+    const int rl = it / D4, d4 = it - rl * D4;
+    *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + 4 * d4) =
+        *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
+  }
+  for (int rl = tid; rl < rows; rl += S::THREADS) a.part_lse[pbase + rl] = stage[rl * SD + D];
 }
 
 // ============================================================================
@@ -651,58 +749,118 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
 }
 
 // ============================================================================
-// merge kernel: one wave per query row combines the splits' partials
+// merge: one wave per query row combines the splits' partials and, for the
+// ring variants, adds the query's tree keys (its ancestors and itself)
 // ============================================================================
 template <int D>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
-  constexpr int PER_LANE = D / 64;  // 1 or 2 floats per lane
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, int RW) {
+  constexpr int PL = D / 64;  // 1 or 2 elements per lane
+  constexpr int TB = 8;       // tree keys in flight per batch
   const int lane = threadIdx.x & 63;
-  const int grow = blockIdx.x * 4 + (threadIdx.x >> 6);  // global row over units x RW
-  const int unit = grow / RW;
-  const int rl = grow - unit * RW;
-  if (unit >= a.units) return;
   const int qgroup = unit % a.qgroups;
   const int pair = unit / a.qgroups;
   const int kvh = pair % a.Hkv;
   const int b = pair / a.Hkv;
   const int row = qgroup * RW + rl;
   if (row >= a.M) return;
-  const int S = a.splits;
-  const size_t base = (size_t)unit * S * RW + rl;
-  // log2-sum-exp of each split (lanes 0..S-1), then normalised weights
-  const float lse = lane < S ? a.part_lse[base + (size_t)lane * RW] : -INFINITY;
-  const float mt = wave_max(lse);
-  const float mu = mt == -INFINITY ? 0.f : mt;
-  const float w = __builtin_amdgcn_exp2f(lse - mu);
-  const float tot = wave_sum_f(w);
-  const int L = a.kv_len[b];
-  const bool bad = L < 0 || L > a.Lmax - a.N;
-  const float inv = (bad || tot == 0.f) ? 0.f : 1.f / tot;
-  float o[PER_LANE];
-#pragma unroll
-  for (int e = 0; e < PER_LANE; ++e) o[e] = 0.f;
-  for (int sp0 = 0; sp0 < S; sp0 += 8) {
-    float v[8][PER_LANE];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float* src = a.part_o + (base + (size_t)(sp0 + q) * RW) * D + lane * PER_LANE;
-#pragma unroll
-      for (int e = 0; e < PER_LANE; ++e) v[q][e] = sp0 + q < S ? src[e] : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float wq = __shfl(w, (sp0 + q) & 63) * inv;
-#pragma unroll
-      for (int e = 0; e < PER_LANE; ++e) o[e] += sp0 + q < S ? wq * v[q][e] : 0.f;
-    }
-  }
   const int i = row / a.G;
   const int h = kvh * a.G + (row - i * a.G);
-  uint16_t* orow = a.out + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PER_LANE;
-  if constexpr (PER_LANE == 2)
-    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0], o[1]);
+  const int S = a.splits;
+  const size_t base = (size_t)unit * S * RW + rl;
+  // independent loads first: length, tree mask, query, split partials
+  const int L = a.kv_len[b];
+  const uint64_t nmask = a.N == 64 ? ~0ull : (1ull << a.N) - 1ull;
+  uint64_t am = a.tree_in_merge ? a.anc[(size_t)b * a.N + i] & nmask : 0ull;
+  float qv[PL];
+  load_pair<D>(a.q + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PL, qv);
+  const float lse = lane < S ? a.part_lse[base + (size_t)lane * RW] : -INFINITY;
+  const bool bad = L < 0 || L > a.Lmax - a.N;
+
+  // splits: state (m, l, o) with o relative to 2^m
+  float m = wave_max(lse);
+  const float mu0 = m == -INFINITY ? 0.f : m;
+  const float w = __builtin_amdgcn_exp2f(lse - mu0);
+  float l = wave_sum_f(w);
+  float o[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) o[e] = 0.f;
+  for (int sp0 = 0; sp0 < S; sp0 += 8) {
+    float v[8][PL];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float* src = a.part_o + (base + (size_t)(sp0 + q) * RW) * D + lane * PL;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) v[q][e] = sp0 + q < S ? src[e] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float wq = __shfl(w, (sp0 + q) & 63);
+#pragma unroll
+      for (int e = 0; e < PL; ++e) o[e] += sp0 + q < S ? wq * v[q][e] : 0.f;
+    }
+  }
+
+  // tree keys: slot L + j for every ancestor j of node i (itself included)
+  if (!bad) {
+    const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D + lane * PL;
+    while (am) {
+      float kk[TB][PL], vv[TB][PL];
+      int nb = 0;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        // absent entries re-read key L (in range) and are dropped below
+        const int j = am ? __ffsll((unsigned long long)am) - 1 : 0;
+        if (am) {
+          am &= am - 1;
+          nb = t + 1;
+        }
+        const size_t off = kv_base + (size_t)(L + j) * D;
+        load_pair<D>(a.k + off, kk[t]);
+        load_pair<D>(a.v + off, vv[t]);
+      }
+      float sc[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) d = fmaf(qv[e], kk[t][e], d);
+        sc[t] = d;
+      }
+      wave_allsum_n<TB>(sc);
+      float mb = m;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        sc[t] = t < nb ? sc[t] * a.scale_log2 : -INFINITY;
+        mb = fmaxf(mb, sc[t]);
+      }
+      const float fs = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
+      l *= fs;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) o[e] *= fs;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const float pt = t < nb ? __builtin_amdgcn_exp2f(sc[t] - mb) : 0.f;
+        l += pt;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) o[e] = fmaf(pt, vv[t][e], o[e]);
+      }
+      m = mb;
+    }
+  }
+  const float inv = (bad || l == 0.f) ? 0.f : 1.f / l;
+  uint16_t* orow = a.out + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PL;
+  if constexpr (PL == 2)
+    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
   else
-    orow[0] = float_to_bf16_bits(o[0]);
+    orow[0] = float_to_bf16_bits(o[0] * inv);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
+  const int grow = blockIdx.x * 4 + (threadIdx.x >> 6);  // global row over units x RW
+  const int unit = grow / RW;
+  if (unit >= a.units) return;
+  merge_row<D>(a, unit, grow - unit * RW, RW);
 }
 
 // ---- variants ----------------------------------------------------------------
@@ -725,6 +883,8 @@ static VariantInfo variant_info(int variant) {
 
 template <int D>
 static void* variant_kernel(int variant) {
+  static_assert(RingShape<D, 1>::THREADS == kRingThreads && RingShape<D, 2>::THREADS == kRingThreads,
+                "ring launch size");
   switch (variant) {
     case 0: return (void*)tree_attn_ring_kernel<RingShape<D, 1>>;
     case 1: return (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
@@ -772,8 +932,9 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: [split log2-sum-exp | split O].
 size_t tree_attn_workspace_bytes(const AttnPlan& p) {
-  if (p.splits <= 1) return 0;
+  if (p.splits <= 1 && p.variant > 1) return 0;  // ring variants always stage partials
   const size_t lse = align256((size_t)p.units * p.splits * p.rows_per_wg * 4);
   const size_t o = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
   return lse + o;
@@ -790,6 +951,7 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.kv_len = kv_len;
   a.anc = anc;
   a.out = out;
+  const bool ring = plan.variant <= 1;
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
   a.part_lse = reinterpret_cast<float*>(w);
@@ -807,11 +969,12 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.splits = plan.splits;
   a.scale_log2 = scale_log2;
   const int padded_units = ((plan.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
+  a.tree_in_merge = ring ? 1 : 0;
   const dim3 grid((unsigned)(padded_units * plan.splits));
   void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
   void* args[] = {&a};
-  hipError_t err = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
-  if (err != hipSuccess || plan.splits == 1) return err;
+  hipError_t err = hipLaunchKernel(fn, grid, dim3(ring ? kRingThreads : 256), args, 0, s);
+  if (err != hipSuccess || (plan.splits == 1 && !ring)) return err;  // ring variants always merge
   const int rw = plan.rows_per_wg;
   const dim3 mgrid((unsigned)((plan.units * rw + 3) / 4));
   if (plan.d == 64)
