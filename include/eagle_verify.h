@@ -57,6 +57,9 @@ typedef int eagle_status_t;
 #define EAGLE_FLAG_BAD_KV_LEN   2  /* kv_len[b] < 0 or kv_len[b] + N > Lmax */
 #define EAGLE_FLAG_BAD_TOKEN    4  /* a drafted token outside [0, V)        */
 #define EAGLE_FLAG_NONFINITE    8  /* NaN or Inf in a target logit row      */
+#define EAGLE_FLAG_TIMEOUT     16  /* a cross-workgroup wait gave up; the  */
+                                   /* sequence's walk outputs are in range */
+                                   /* but not meaningful                   */
 
 /* Message for the last non-zero status returned on this thread. */
 EAGLE_API const char* eagle_last_error(void);
@@ -73,8 +76,10 @@ EAGLE_API eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B,
 
 /*
  * Zero-fill `bytes` of device memory at `ptr` with a kernel (no memset node,
- * so it may be captured in a HIP graph).  Workspaces must be zero before
- * their first use; every call that uses one leaves it zero again.
+ * so it may be captured in a HIP graph).  eagle_verify_accept's workspace
+ * must be zero before its first use; each call leaves its counters and
+ * exchange words zero again (the rest holds per-call scratch), so it is
+ * cleared once.
  */
 EAGLE_API eagle_status_t eagle_workspace_clear(void* ptr, size_t bytes, void* stream);
 
@@ -170,8 +175,15 @@ EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
  *   out_final_dist  [B, V] or NULL: the distribution the final token came from
  *   out_ratio       [B, N] or NULL: ratio used for each tested node, NaN for
  *                   untested ones (T = 0: 1 for a match, 0 otherwise)
- *   seq_flags       [B] int32 or NULL (BAD_TOKEN, NONFINITE, BAD_PARENT)
+ *   seq_flags       [B] int32 or NULL (BAD_TOKEN, NONFINITE, BAD_PARENT,
+ *                   TIMEOUT)
  * Supported: 1 <= V <= 32768; 1 <= N <= 64.
+ * With T > 0, no out_* buffer, V % 4 == 0, 28672 < V <= 32768 and B * N <= 32
+ * each node's row is split over 8 workgroups that exchange partial sums through
+ * the workspace and wait for one another; they all fit the GPU at once, so the
+ * waits end unless other work holds the compute units for a long time, in
+ * which case a bounded wait gives up and sets EAGLE_FLAG_TIMEOUT.  Results of
+ * the split path equal the unsplit one's up to the rounding of the masses.
  */
 EAGLE_API eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* draft_probs,
                                    const float* target_logits, const int32_t* parents,

@@ -244,6 +244,60 @@ def test_verify_deterministic():
         assert np.array_equal(a[k], b[k], equal_nan=True)
 
 
+# Split rows: at large vocabularies with at most 32 nodes the sampling path
+# without parity outputs spreads each node's row over 8 workgroups that
+# exchange fixed-point partial sums; the outputs must match the oracle, repeat
+# bit for bit, raise no flag and leave the workspace zero.
+SPLIT_CASES = {
+    "7b-seed0": dict(B=1, N=26, V=32000, T=1.0, seed=0),
+    "7b-seed1": dict(B=1, N=26, V=32000, T=1.0, seed=1),
+    "7b-T0.6": dict(B=1, N=26, V=32000, T=0.6, seed=2),
+    "32-nodes": dict(B=2, N=16, V=32768, T=1.0, seed=3),
+    "min-vocab": dict(B=1, N=26, V=28676, T=1.0, seed=4),
+    "star": dict(B=1, N=32, V=32000, T=1.0, seed=5, parents="star"),
+    "chain": dict(B=1, N=20, V=32000, T=1.0, seed=6, parents="chain"),
+    "one-node": dict(B=3, N=1, V=32000, T=1.0, seed=7, parents="chain"),
+}
+
+
+def _al256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_verify_split_rows(case):
+    c = SPLIT_CASES[case]
+    B, N, V = c["B"], c["N"], c["V"]
+    par = {"star": trees.star, "chain": trees.chain}[c["parents"]](N) if "parents" in c else None
+    cfg = W.shrink(W.get(1), B=B, N=N, V=V, sigma_d=0.5 if case == "star" else W.get(1).sigma_d)
+    s = W.make_step(cfg, c["T"], seed=c["seed"], parents=par, with_attention=False)
+    nbytes = ev.binding.verify_accept_workspace_bytes(B, N, V)
+    assert nbytes >= B * N * 72 * 9 * 8  # the plan reserved exchange words
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for rep in range(2):
+        flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+        say(f"verify split rows {case} call {rep}")
+        res = ev.verify_accept(dev(s.tokens), dev(s.draft_probs), dev(s.target_logits), dev(s.parents),
+                               dev(s.kv_len), s.T, dev(s.uniforms), workspace=ws, seq_flags=flags)
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().numpy() for k, v in res.items()})
+        assert flags.cpu().tolist() == [0] * B
+        # what must start at zero is zero again: the per-sequence tickets, the
+        # per-node phase counts and the exchange words (the workspace layout
+        # of csrc/verify.hip: tickets | per-node results | exchange words)
+        cnt, stats = _al256(4 * B), _al256(20 * B * N)
+        w = ws.cpu().numpy()
+        assert not w[:cnt].any()
+        assert not w[cnt + 16 * B * N: cnt + 20 * B * N].any()
+        assert not w[cnt + stats:].any()
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    compared, excused = compare_walks(outs[0], s, oracle_walks(s))
+    say(f"  compared {compared}, excused {excused}; accept_len {outs[0]['accept_len'].tolist()}")
+    assert compared + excused == B
+
+
 def test_verify_chi_square_on_gpu():
     """Distribution preservation on the device: the first emitted token of many
     independent tiny sequences (fresh drafts from q, fresh uniforms) follows

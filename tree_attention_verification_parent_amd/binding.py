@@ -26,6 +26,7 @@ FLAG_BAD_PARENT = 1
 FLAG_BAD_KV_LEN = 2
 FLAG_BAD_TOKEN = 4
 FLAG_NONFINITE = 8
+FLAG_TIMEOUT = 16
 
 
 class EagleError(RuntimeError):

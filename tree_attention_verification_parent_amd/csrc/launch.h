@@ -41,8 +41,9 @@ struct VerifyPlan {
   int V;
   int chunks;          // vocabulary chunks per row in the statistics pass
   int walk_threads;    // threads of the walk block
+  int parts;           // workgroups per node on the sampling path (split rows)
   size_t ws_stats;     // per-row statistics
-  size_t ws_partials;  // per-chunk partial statistics
+  size_t ws_partials;  // exchange words of split rows
   size_t ws_counters;  // per-row counters
 };
 

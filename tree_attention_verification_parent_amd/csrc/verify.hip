@@ -56,6 +56,7 @@ struct NodeResults {
   int32_t* bonus;    // [B*N] token drawn if the walk ends here
   float* ratio;      // [B*N] ratio of node c as tested by its parent's chain
   int32_t* ntested;  // [B*N] candidates of the node that its chain tested
+  int32_t* nphase;   // [B*N] exchange phases the node used (split rows)
   int32_t* counter;  // [B] per-sequence tickets (zero between calls)
 };
 
@@ -76,7 +77,10 @@ struct VArgs {
   float* out_ratio;
   int32_t* flags;
   NodeResults nr;
+  unsigned long long* xwords;  // [B*N][kXPhases][kXWords] exchange words (split rows; zero between calls)
   int N, V;
+  int nodes;  // B * N
+  int P;      // workgroups per node (split rows when > 1)
   float T;
 };
 
@@ -111,8 +115,13 @@ struct Shared {
   double sel_before;
   int sel_entry;
   int pick;
+  double gd[2];  // split rows: broadcast of the cross-workgroup results
+  float gf[2];
+  int xabort;    // split rows: a wait timed out, later waits are skipped
+  int own;       // split rows: this part holds the final draw's crossing
+  double own_start, own_thr;
   int last, term;
-  int wacc[64], wbonus[64], wnt[64];
+  int wacc[64], wbonus[64], wnt[64], wph[64];
   int path[64];
 };
 
@@ -170,6 +179,91 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.ri[buf][i]);
   return t;
+}
+
+// ---- split rows ----------------------------------------------------------------
+// With P > 1 the P workgroups of a node each hold a slice of the row and every
+// workgroup reduction is completed across them through exchange words in the
+// workspace (one 64-bit atomic per workgroup and phase, then polling; the
+// P workgroups run on one XCD and are all resident, which the host checks).
+// Sums travel as fixed point relative to a known bound (value << 8 | count),
+// so the total is an exact integer sum, the same in every workgroup; a max
+// travels as an order-preserving 32-bit key with a separate count.  A wait
+// that exceeds kSpinCap polls sets EAGLE_FLAG_TIMEOUT and skips later waits.
+constexpr int kXWords = 9;         // exchange words per phase (the final draw uses P + 1)
+constexpr int kXPhases = 72;       // phases per node: row statistics, candidates, draw
+constexpr int kMaxParts = 8;
+constexpr int kSpinCap = 1 << 20;
+constexpr double kFix = 4503599627370496.0;  // 2^52
+
+struct Grp {
+  unsigned long long* words;  // this node's exchange words
+  int P, part, phase;
+  int base, len;              // this part's slice of the row: ids [base, base + len)
+  int32_t* flags;
+  int b;
+};
+
+__device__ __forceinline__ unsigned long long* grp_phase_words(Grp& g) {
+  return g.words + (size_t)g.phase * kXWords;
+}
+
+// Polls *w until its low 8 bits reach `need`; returns the last value read.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, unsigned long long cur,
+                                                       int need, Grp& g, Shared<BLOCK, NPT>& sh) {
+  int it = 0;
+  while ((int)(cur & 0xffull) < need && !sh.xabort) {
+    if (++it > kSpinCap) {
+      sh.xabort = 1;
+      if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
+      break;
+    }
+    cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return cur;
+}
+
+// Sum over the node's workgroups of v >= 0, with 0 <= total <= 8 * scale (the
+// fixed-point total, shifted left by 8, stays below 2^64).
+template <int BLOCK, int NPT>
+__device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared<BLOCK, NPT>& sh,
+                                          int& rb) {
+  v = block_sum<BLOCK, NPT>(v, sh, rb);
+  if (g.P == 1) return v;
+  const int slot = g.phase & 1;
+  if (threadIdx.x == 0) {
+    unsigned long long* w = grp_phase_words(g);
+    const unsigned long long q = (unsigned long long)fmax(0.0, rint(v / scale * kFix));
+    const unsigned long long add = (q << 8) | 1ull;
+    unsigned long long cur = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    cur = grp_wait<BLOCK, NPT>(w, cur, g.P, g, sh);
+    sh.gd[slot] = (double)(cur >> 8) * (scale / kFix);
+  }
+  ++g.phase;
+  __syncthreads();
+  return sh.gd[slot];
+}
+
+template <int BLOCK, int NPT>
+__device__ __forceinline__ float grp_max(float v, Grp& g, Shared<BLOCK, NPT>& sh, int& rb) {
+  v = block_max<BLOCK, NPT>(v, sh, rb);
+  if (g.P == 1) return v;
+  const int slot = g.phase & 1;
+  if (threadIdx.x == 0) {
+    unsigned long long* w = grp_phase_words(g);
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t key = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(w), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the key is in before the count
+    unsigned long long cur = __hip_atomic_fetch_add(w + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1ull;
+    grp_wait<BLOCK, NPT>(w + 1, cur, g.P, g, sh);
+    const uint32_t k = __hip_atomic_load(reinterpret_cast<uint32_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.gf[slot] = __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+  }
+  ++g.phase;
+  __syncthreads();
+  return sh.gf[slot];
 }
 
 // ---- rows --------------------------------------------------------------------
@@ -257,7 +351,7 @@ __device__ __forceinline__ float target_entry(float x, float m, bool unit, float
 // barrier (slot set buf, also returned in sum_buf) publishes what it writes.
 template <int BLOCK, int NPT, bool GREEDY, typename F>
 __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
-                                            double& C, int& sum_buf, F&& before_sum,
+                                            double& C, int& sum_buf, F&& before_sum, Grp& grp,
                                             Shared<BLOCK, NPT>& sh, int& rb) {
   const int tid = threadIdx.x;
   // x * 0 is NaN exactly for non-finite x: one fma per entry
@@ -304,7 +398,7 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
-    const float m = block_max<BLOCK, NPT>(lm, sh, rb);
+    const float m = grp_max<BLOCK, NPT>(lm, grp, sh, rb);
     const bool unit = T == 1.f;
     const float invT = 1.f / T;
     float s[NPT];
@@ -319,7 +413,7 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
     }
     sum_buf = rb;
     before_sum(sum_buf, m, unit, invT);
-    C = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s), sh, rb);
+    C = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(s), 32768.0, grp, sh, rb);  // entries <= 1, V <= 32768
     return 0;
   }
 }
@@ -376,10 +470,12 @@ __device__ __forceinline__ void issue_row_lds(const float* row, int V, float4* q
 template <int BLOCK, int NPT, bool VEC>
 __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<BLOCK, NPT>& cur,
                                            Row<BLOCK, NPT>& nxt, double& C, float& ut, float& val,
-                                           int s, int nk, bool stop_at_accept,
+                                           int s, int nk, bool stop_at_accept, Grp& grp,
                                            Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   const int tid = threadIdx.x, V = a.V;
-  auto qrow = [&](int i) { return a.draft + (ob + sh.kids[i]) * V; };
+  // this workgroup's slice of candidate i's draft row (the whole row when P = 1)
+  auto qrow = [&](int i) { return a.draft + (ob + sh.kids[i]) * V + grp.base; };
+  const int len = grp.len;
   const int c = sh.kids[s];
   const int t = sh.tok[c];
   const bool tok_ok = t >= 0 && t < V;
@@ -405,10 +501,10 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
       qv[k] = qlds[k * BLOCK + tid];
     } else {
       const int e0 = (k * BLOCK + tid) * 4;
-      const float x0 = qs[min(e0 + 0, V - 1)], x1 = qs[min(e0 + 1, V - 1)];
-      const float x2 = qs[min(e0 + 2, V - 1)], x3 = qs[min(e0 + 3, V - 1)];
-      qv[k] = make_float4(e0 + 0 < V ? x0 : 0.f, e0 + 1 < V ? x1 : 0.f, e0 + 2 < V ? x2 : 0.f,
-                          e0 + 3 < V ? x3 : 0.f);
+      const float x0 = qs[min(e0 + 0, len - 1)], x1 = qs[min(e0 + 1, len - 1)];
+      const float x2 = qs[min(e0 + 2, len - 1)], x3 = qs[min(e0 + 3, len - 1)];
+      qv[k] = make_float4(e0 + 0 < len ? x0 : 0.f, e0 + 1 < len ? x1 : 0.f, e0 + 2 < len ? x2 : 0.f,
+                          e0 + 3 < len ? x3 : 0.f);
     }
   }
 #pragma unroll
@@ -433,10 +529,10 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
     }
     if constexpr (VEC) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of q_s done
-      issue_row_lds<BLOCK, NPT>(qrow(s + 1), V, qlds);
+      issue_row_lds<BLOCK, NPT>(qrow(s + 1), len, qlds);
     }
   }
-  const double Cn = block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);
+  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, grp, sh, rb);  // Cn <= C
   const bool commit = Cn > 0.0;
   if (commit) {
     C = Cn;
@@ -459,19 +555,19 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
 // moves no registers.
 template <int BLOCK, int NPT, bool VEC>
 __device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, NPT>& U, double& C,
-                                         float ut, float val, int nk, bool stop_at_accept,
+                                         float ut, float val, int nk, bool stop_at_accept, Grp& grp,
                                          Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   Row<BLOCK, NPT> W;
   for (int s = 0; s < nk; s += 2) {
-    if (chain_step<BLOCK, NPT, VEC>(a, ob, U, W, C, ut, val, s, nk, stop_at_accept, sh, qlds, rb))
+    if (chain_step<BLOCK, NPT, VEC>(a, ob, U, W, C, ut, val, s, nk, stop_at_accept, grp, sh, qlds, rb))
       return s;
     if (s + 1 >= nk) {
 #pragma unroll
       for (int k = 0; k < NPT; ++k) U.v[k] = W.v[k];
       break;
     }
-    if (chain_step<BLOCK, NPT, VEC>(a, ob, W, U, C, ut, val, s + 1, nk, stop_at_accept, sh, qlds,
-                                    rb))
+    if (chain_step<BLOCK, NPT, VEC>(a, ob, W, U, C, ut, val, s + 1, nk, stop_at_accept, grp, sh,
+                                    qlds, rb))
       return s + 1;
   }
   return -1;
@@ -486,8 +582,8 @@ __device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, N
 template <int BLOCK, int NPT, bool GREEDY, bool VEC>
 __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, int b,
                                           int32_t* flags, Row<BLOCK, NPT>& U, double& C, float& ut,
-                                          float& val, Shared<BLOCK, NPT>& sh, float4* qlds,
-                                          int& rb) {
+                                          float& val, Grp& grp, Shared<BLOCK, NPT>& sh,
+                                          float4* qlds, int& rb) {
   const int tid = threadIdx.x, V = a.V;
   find_kids<BLOCK, NPT>(a.N, node, sh);
   __syncthreads();
@@ -497,14 +593,14 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
   val = 0.f;
   if constexpr (GREEDY) {
     return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, sum_buf,
-                                          [](int, float, bool, float) {}, sh, rb);
+                                          [](int, float, bool, float) {}, grp, sh, rb);
   } else {
     if constexpr (VEC) {
-      // slots past V are never loaded: zero this thread's (the pass reads them)
+      // slots past the slice are never loaded: zero this thread's (the pass reads them)
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
-        if ((k * BLOCK + tid) * 4 >= V) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (nk > 0) issue_row_lds<BLOCK, NPT>(a.draft + (ob + sh.kids[0]) * V, V, qlds);
+        if ((k * BLOCK + tid) * 4 >= grp.len) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (nk > 0) issue_row_lds<BLOCK, NPT>(a.draft + (ob + sh.kids[0]) * V + grp.base, grp.len, qlds);
     }
     constexpr int G = (64 * 64 + BLOCK - 1) / BLOCK;
     float g[G];
@@ -538,7 +634,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
             if (tid == 0) sh.nu[buf][1] = val;
           }
         },
-        sh, rb);
+        grp, sh, rb);
     if (nk > 0) {
       const int t0 = sh.tok[sh.kids[0]];
       ut = (t0 >= 0 && t0 < V) ? sh.nu[sum_buf][1] : 0.f;
@@ -554,9 +650,13 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
 // thread then owns NPT consecutive groups, each wave 64 threads of them: the
 // wave totals locate the wave, a lane scan the thread, its groups the group
 // and the group's owner the id.
+// With `given`, the row is one slice of a split row: the search starts at
+// mass `start` and stops at threshold `thr_given` instead of u * sum.
 template <int BLOCK, int NPT>
 __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V,
-                                           Shared<BLOCK, NPT>& sh, double* part, int& rb) {
+                                           Shared<BLOCK, NPT>& sh, double* part, int& rb,
+                                           bool given = false, double start = 0.0,
+                                           double thr_given = 0.0) {
   constexpr int NW = BLOCK / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -579,9 +679,9 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   double Z = 0.0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) Z += sh.rd[wbuf][i];
-  const double thr = (double)u * Z;
+  const double thr = given ? thr_given : (double)u * Z;
   int ws = NW - 1;  // rounding may leave no crossing: then the last wave
-  double before_w = 0.0, run = 0.0;
+  double before_w = start, run = start;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const double nx = run + sh.rd[wbuf][i];
@@ -662,20 +762,80 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   return pick;
 }
 
-template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC>
+// Final draw over a split row: every part adds its slice mass (fixed point
+// relative to C) to the total word and to the prefix word of every later
+// part, so each part learns the exact integer mass before its slice and the
+// total; the one part whose slice holds u * total searches its slice.
+// Returns the drawn id in the owning part, -1 in the others.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, double C, Grp& g,
+                                          Shared<BLOCK, NPT>& sh, double* part, int& rb) {
+  float s4[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) s4[k] = sum4(U.v[k]);
+  double mine = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s4), sh, rb);
+  if (threadIdx.x == 0) {
+    unsigned long long* w = grp_phase_words(g);
+    const unsigned long long q = (unsigned long long)fmax(0.0, rint(mine / C * kFix));
+    const unsigned long long add = (q << 8) | 1ull;
+    unsigned long long tot = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    for (int p2 = g.part + 1; p2 < g.P; ++p2)
+      __hip_atomic_fetch_add(w + p2, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tot = grp_wait<BLOCK, NPT>(w, tot, g.P, g, sh);
+    unsigned long long before = 0;
+    if (g.part > 0) {
+      const unsigned long long pw = __hip_atomic_load(w + g.part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      before = grp_wait<BLOCK, NPT>(w + g.part, pw, g.part, g, sh) >> 8;
+    }
+    const double Zi = (double)(tot >> 8), thr_i = (double)u * Zi;
+    const double lo = (double)before, hi = (double)(before + q);
+    sh.own = lo <= thr_i && (thr_i < hi || g.part == g.P - 1);
+    sh.own_start = lo * (C / kFix);
+    sh.own_thr = thr_i * (C / kFix);
+  }
+  ++g.phase;
+  __syncthreads();
+  if (!sh.own) return -1;
+  const int pick = inverse_cdf<BLOCK, NPT>(U, u, g.len, sh, part, rb, true, sh.own_start, sh.own_thr);
+  return g.base + pick;
+}
+
+template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
+  static_assert(!SPLIT || (!GREEDY && !PARITY && VEC), "split rows: sampling path only");
   __shared__ Shared<BLOCK, NPT> sh;
   __shared__ float4 qlds[GREEDY ? 1 : NPT * BLOCK];  // draft-row prefetch
   const int N = a.N, V = a.V;
-  const int b = blockIdx.x / N;
-  const int j = blockIdx.x - b * N;
   const int tid = threadIdx.x;
+  // Workgroup -> (node, part).  Split rows: workgroup i runs on XCD i % 8, and
+  // the P parts of a node take slots with the same i % 8 (one L2 for their
+  // exchange words); slots past the last node exit at once.
+  int node = blockIdx.x, part = 0;
+  if constexpr (SPLIT) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    part = slot % a.P;
+    node = (slot / a.P) * 8 + xcd;
+    if (node >= a.nodes) return;
+  }
+  const int b = node / N;
+  const int j = node - b * N;
   const size_t ob = (size_t)b * N;
   int rb = 0;
+  Grp grp{nullptr, 1, 0, 0, 0, V, a.flags, b};
+  if constexpr (SPLIT) {
+    const int s4 = ((V >> 2) + a.P - 1) / a.P;  // float4 per part
+    grp.words = a.xwords + (size_t)node * kXPhases * kXWords;
+    grp.P = a.P;
+    grp.part = part;
+    grp.base = part * s4 * 4;
+    grp.len = min(V - grp.base, s4 * 4);
+    if (tid == 0) sh.xabort = 0;
+  }
 
-  // the node's logit row first: its latency overlaps the tree set-up
+  // the node's logit row (this part's slice) first: its latency overlaps the
+  // tree set-up
   Row<BLOCK, NPT> U;
-  load_logits<BLOCK, NPT>(U, a.logits + (ob + j) * V, V);
+  load_logits<BLOCK, NPT>(U, a.logits + (ob + j) * V + grp.base, grp.len);
 
   // tree, tokens, uniforms
   bool tok_bad = false;
@@ -688,12 +848,13 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     sh.u[tid] = a.uniforms[ob + tid];
     tok_bad = tid > 0 && (tk < 0 || tk >= V);
   }
-  if (j == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
+  if (j == 0 && part == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
     atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
   __syncthreads();
   double C = 1.0;
   float ut = 0.f, val = 0.f;
-  const int am = node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, C, ut, val, sh, qlds, rb);
+  const int am =
+      node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, C, ut, val, grp, sh, qlds, rb);
   const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
@@ -720,10 +881,12 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
       }
     }
   } else {
-    const int si = run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, nk, true, sh, qlds, rb);
+    const int si = run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, nk, true, grp, sh, qlds, rb);
     if (si >= 0) {
       acc = sh.kids[si];
       ntested = si + 1;
+    } else if constexpr (SPLIT) {
+      bonus = split_draw<BLOCK, NPT>(U, sh.u[0], C, grp, sh, reinterpret_cast<double*>(qlds), rb);
     } else {
       bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh, reinterpret_cast<double*>(qlds), rb);
     }
@@ -732,27 +895,33 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   if (!GREEDY && VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // publish this node's outcome; the last node of the sequence walks the tree
+  // publish this node's outcome (split rows: part 0, and the part that drew
+  // the final token); the last workgroup of the sequence walks the tree
   if (tid == 0) {
-    st_c(a.nr.acc + ob + j, acc);
-    st_c(a.nr.bonus + ob + j, bonus);
-    st_c(a.nr.ntested + ob + j, ntested);
+    if (part == 0) {
+      st_c(a.nr.acc + ob + j, acc);
+      st_c(a.nr.ntested + ob + j, ntested);
+    }
+    if (!SPLIT || (acc >= 0 ? part == 0 : bonus >= 0)) st_c(a.nr.bonus + ob + j, bonus);
+    if (SPLIT)
+      __hip_atomic_fetch_max(a.nr.nphase + ob + j, grp.phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);
+  if (part == 0 && tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const int ticket = __hip_atomic_fetch_add(a.nr.counter + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.last = ticket == N - 1;
+    sh.last = ticket == N * grp.P - 1;
   }
   __syncthreads();
   if (!sh.last) return;
 
-  // ---- walk (last node workgroup of sequence b) ------------------------------
+  // ---- walk (last workgroup of sequence b) -----------------------------------
   if (tid < N) {
     sh.wacc[tid] = ld_c(a.nr.acc + ob + tid);
     sh.wbonus[tid] = ld_c(a.nr.bonus + ob + tid);
     sh.wnt[tid] = ld_c(a.nr.ntested + ob + tid);
+    if (SPLIT) sh.wph[tid] = min(ld_c(a.nr.nphase + ob + tid), kXPhases);
   }
   __syncthreads();
   if (tid == 0) {
@@ -765,18 +934,29 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
       cur = nx;
     }
     sh.term = cur;
-    sh.pick = sh.wbonus[cur];
+    // in range even if a timed-out exchange left the slot unwritten
+    sh.pick = min(max(sh.wbonus[cur], 0), V - 1);
     sh.nk = m_acc;
     __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if constexpr (SPLIT) {
+    // every workgroup of the sequence is past its last exchange: zero the
+    // words its nodes used, and the phase counts, for the next call
+    for (int n = 0; n < N; ++n) {
+      unsigned long long* w = a.xwords + (ob + n) * kXPhases * kXWords;
+      for (int i = tid; i < sh.wph[n] * kXWords; i += BLOCK)
+        __hip_atomic_store(w + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid < N) st_c(a.nr.nphase + ob + tid, 0);
   }
   __syncthreads();
   const int m_acc = sh.nk;
   if (tid < N) {
     const size_t o = ob + tid;
     const bool on = tid <= m_acc;
-    const int node = on ? sh.path[tid] : -1;
-    a.path[o] = node;
-    a.kv_src[o] = on ? a.kv_len[b] + node : -1;
+    const int pn = on ? sh.path[tid] : -1;
+    a.path[o] = pn;
+    a.kv_src[o] = on ? a.kv_len[b] + pn : -1;
     a.acc_tokens[o] = tid < m_acc ? sh.tok[sh.path[tid + 1]] : -1;
   }
   if (tid == 0) {
@@ -810,9 +990,10 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     if constexpr (GREEDY) {
       for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
     } else {
+      Grp whole{nullptr, 1, 0, 0, 0, V, nullptr, b};
       load_logits<BLOCK, NPT>(U, a.logits + (ob + term) * V, V);
-      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, C, ut, val, sh, qlds, rb);
-      run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, sh.nk, false, sh, qlds, rb);
+      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, C, ut, val, whole, sh, qlds, rb);
+      run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, sh.nk, false, whole, sh, qlds, rb);
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
 #pragma unroll
@@ -825,14 +1006,25 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Split rows pay off where a node's chain is long per workgroup: large
+// vocabularies with few nodes, so that all B * N * P workgroups are resident
+// at once (one per CU at most), which the exchange waits rely on.
+static int verify_parts(int B, int N, int V) {
+  const size_t nodes = (size_t)B * N;
+  if ((V & 3) != 0 || V <= 28672 || V > 32768) return 1;
+  if (nodes * kMaxParts > (size_t)kNumCUs) return 1;
+  return kMaxParts;
+}
+
 VerifyPlan plan_verify(int B, int N, int V) {
   VerifyPlan p{};
   p.V = V;
-  p.walk_threads = V > 4096 ? 1024 : 256;
+  p.parts = verify_parts(B, N, V);
+  p.walk_threads = p.parts > 1 ? 256 : V > 4096 ? 1024 : 256;
   const size_t nodes = (size_t)B * N;
-  p.ws_stats = nodes * 16;  // acc, bonus, ratio, ntested
+  p.ws_stats = nodes * 20;  // acc, bonus, ratio, ntested, nphase
   p.ws_counters = (size_t)B * 4;
-  p.ws_partials = 0;
+  p.ws_partials = p.parts > 1 ? nodes * kXPhases * kXWords * 8 : 0;  // exchange words
   p.chunks = 1;
   return p;
 }
@@ -840,7 +1032,7 @@ VerifyPlan plan_verify(int B, int N, int V) {
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t verify_workspace_bytes(const VerifyPlan& p) {
-  return align256(p.ws_counters) + align256(p.ws_stats);
+  return align256(p.ws_counters) + align256(p.ws_stats) + align256(p.ws_partials);
 }
 
 hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
@@ -873,23 +1065,35 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   a.nr.bonus = reinterpret_cast<int32_t*>(nb + nodes * 4);
   a.nr.ratio = reinterpret_cast<float*>(nb + nodes * 8);
   a.nr.ntested = reinterpret_cast<int32_t*>(nb + nodes * 12);
+  a.nr.nphase = reinterpret_cast<int32_t*>(nb + nodes * 16);
+  a.xwords = reinterpret_cast<unsigned long long*>(nb + align256(plan.ws_stats));
   a.N = N;
   a.V = plan.V;
+  a.nodes = (int)nodes;
+  a.P = 1;
   a.T = T;
   const unsigned grid = (unsigned)nodes;
   const bool greedy = T == 0.f;
   const bool parity = out_probs || out_final || out_ratio;
   const bool vec = (plan.V & 3) == 0;
+  if (plan.parts > 1 && !greedy && !parity && vec) {
+    // node slots rounded up to a multiple of the 8 XCDs, P parts each
+    a.P = plan.parts;
+    const unsigned sgrid = (unsigned)(((nodes + 7) / 8) * 8 * plan.parts);
+    verify_node_kernel<256, 4, false, false, true, true><<<sgrid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
 #define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                        \
   do {                                                                                      \
-    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true><<<grid, BLK, 0, s>>>(a);    \
-    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true><<<grid, BLK, 0, s>>>(a);        \
-    else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true><<<grid, BLK, 0, s>>>(a); \
-    else if (parity) verify_node_kernel<BLK, NPT, false, true, false><<<grid, BLK, 0, s>>>(a);       \
-    else if (vec) verify_node_kernel<BLK, NPT, false, false, true><<<grid, BLK, 0, s>>>(a);          \
-    else verify_node_kernel<BLK, NPT, false, false, false><<<grid, BLK, 0, s>>>(a);                  \
+    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true, false><<<grid, BLK, 0, s>>>(a);    \
+    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true, false><<<grid, BLK, 0, s>>>(a);        \
+    else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true, false><<<grid, BLK, 0, s>>>(a); \
+    else if (parity) verify_node_kernel<BLK, NPT, false, true, false, false><<<grid, BLK, 0, s>>>(a);       \
+    else if (vec) verify_node_kernel<BLK, NPT, false, false, true, false><<<grid, BLK, 0, s>>>(a);          \
+    else verify_node_kernel<BLK, NPT, false, false, false, false><<<grid, BLK, 0, s>>>(a);                  \
   } while (0)
-  if (plan.walk_threads == 1024)
+  // the row must fit one workgroup unless it is split
+  if (plan.V > 4096)
     EAGLE_LAUNCH_VERIFY(1024, 8);
   else
     EAGLE_LAUNCH_VERIFY(256, 4);
