@@ -15,6 +15,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load of the wave (a workgroup-scope
+// release covers global memory), which would pull a prefetch issued before
+// the barrier onto the critical path; this one lets such loads stay in
+// flight.  Loads that land in LDS (global_load_lds) are not ordered by it:
+// their data is only read back by the thread that issued them, after its own
+// vmcnt wait.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -111,7 +111,6 @@ struct Shared {
   double rd[2][NW];
   float rf[2][NW];
   int ri[2][NW];
-  float nu[2][2];  // next candidate's U element: [0] after the update, [1] before
   double sel_before;
   int sel_entry;
   int pick;
@@ -122,10 +121,13 @@ struct Shared {
   double own_start, own_thr;
   int last, term;
   int wacc[64], wbonus[64], wnt[64], wph[64];
+  float l2sink[64];  // split rows: destination of the L2 prefetch (never read)
   int path[64];
 };
 
-// Workgroup reductions.  `rb` selects the slot set and flips on every call;
+// Workgroup reductions over the BLOCK row threads (a split-row workgroup's
+// extra exchange and prefetch waves hold no row data: they take part in the
+// barriers and read the result).  `rb` selects the slot set and flips on every call;
 // all threads make the same sequence of calls, so a slot set is rewritten
 // only after the barrier of the reduction in between, which every reader of
 // its previous contents has passed: one barrier per reduction suffices.
@@ -134,8 +136,8 @@ __device__ __forceinline__ double block_sum(double v, Shared<BLOCK, NPT>& sh, in
   v = wave_allsum(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0) sh.rd[buf][threadIdx.x >> 6] = v;
-  __syncthreads();
+  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.rd[buf][threadIdx.x >> 6] = v;
+  barrier_lds();
   double t = 0.0;
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t += sh.rd[buf][i];
@@ -147,8 +149,8 @@ __device__ __forceinline__ float block_max(float v, Shared<BLOCK, NPT>& sh, int&
   v = wave_allmax(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0) sh.rf[buf][threadIdx.x >> 6] = v;
-  __syncthreads();
+  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.rf[buf][threadIdx.x >> 6] = v;
+  barrier_lds();
   float t = -INFINITY;
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t = fmaxf(t, sh.rf[buf][i]);
@@ -160,8 +162,8 @@ __device__ __forceinline__ int block_min_i(int v, Shared<BLOCK, NPT>& sh, int& r
   v = wave_allmin_i(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
-  __syncthreads();
+  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.ri[buf][threadIdx.x >> 6] = v;
+  barrier_lds();
   int t = INT_MAX;
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t = min(t, sh.ri[buf][i]);
@@ -173,8 +175,8 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
   v = wave_allmax_i(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
-  __syncthreads();
+  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.ri[buf][threadIdx.x >> 6] = v;
+  barrier_lds();
   int t = INT_MIN;
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.ri[buf][i]);
@@ -184,13 +186,18 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
 // ---- split rows ----------------------------------------------------------------
 // With P > 1 the P workgroups of a node each hold a slice of the row and every
 // workgroup reduction is completed across them through exchange words in the
-// workspace (one 64-bit atomic per workgroup and phase, then polling; the
-// P workgroups run on one XCD and are all resident, which the host checks).
+// workspace (64-bit atomics, then polling; the P workgroups run on one XCD
+// and are all resident, which the host checks).  A split workgroup has two
+// waves beyond its BLOCK row threads.  One does the exchange: its polling
+// loads never queue behind a row prefetch (a wave's vector loads complete in
+// order), so the prefetch of the next draft row stays in flight across the
+// exchange.  The other only brings the node's later draft rows into L2 at
+// the start, for the same reason.
 // Sums travel as fixed point relative to a known bound (value << 8 | count),
 // so the total is an exact integer sum, the same in every workgroup; a max
 // travels as an order-preserving 32-bit key with a separate count.  A wait
 // that exceeds kSpinCap polls sets EAGLE_FLAG_TIMEOUT and skips later waits.
-constexpr int kXWords = 9;         // exchange words per phase (the final draw uses P + 1)
+constexpr int kXWords = 9;         // words per phase (a sum: one per row wave; the final draw: P)
 constexpr int kXPhases = 72;       // phases per node: row statistics, candidates, draw
 constexpr int kMaxParts = 8;
 constexpr int kSpinCap = 1 << 20;
@@ -202,6 +209,7 @@ struct Grp {
   int base, len;              // this part's slice of the row: ids [base, base + len)
   int32_t* flags;
   int b;
+  int xt;                     // the thread that exchanges (lane 0 of the exchange wave)
 };
 
 __device__ __forceinline__ unsigned long long* grp_phase_words(Grp& g) {
@@ -213,6 +221,7 @@ template <int BLOCK, int NPT>
 __device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, unsigned long long cur,
                                                        int need, Grp& g, Shared<BLOCK, NPT>& sh) {
   int it = 0;
+#pragma nounroll
   while ((int)(cur & 0xffull) < need && !sh.xabort) {
     if (++it > kSpinCap) {
       sh.xabort = 1;
@@ -225,24 +234,70 @@ __device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, un
 }
 
 // Sum over the node's workgroups of v >= 0, with 0 <= total <= 8 * scale (the
-// fixed-point total, shifted left by 8, stays below 2^64).
+// fixed-point total, shifted left by 8, stays below 2^64).  mid() runs on
+// every thread while the exchange is in flight (after the workgroup reduction
+// when P = 1); it must issue no memory access from the exchange wave.
+// Split rows: every row wave adds its own partial (fixed point, count 1) to
+// the phase word of its wave index without waiting, so no workgroup barrier
+// precedes the exchange; the exchange wave polls the BLOCK / 64 words until
+// each holds P arrivals, and their integer total is the same in every
+// workgroup.
+template <int BLOCK, int NPT, typename F>
+__device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared<BLOCK, NPT>& sh,
+                                          int& rb, F&& mid) {
+  constexpr int NW = BLOCK / 64;
+  // (split rows run 256-thread workgroups; wider ones always have P = 1)
+  if (NW > kXWords || g.P == 1) {
+    v = block_sum<BLOCK, NPT>(v, sh, rb);
+    mid();
+    return v;
+  }
+  const int tid = threadIdx.x;
+  const int slot = g.phase & 1;
+  unsigned long long* w = grp_phase_words(g);
+  if (tid < BLOCK) {
+    v = wave_allsum(v);
+    if ((tid & 63) == 0) {
+      const unsigned long long q = (unsigned long long)fmax(0.0, rint(v * (kFix / scale)));
+      __hip_atomic_fetch_add(w + (tid >> 6), (q << 8) | 1ull, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  mid();  // guarded by the caller: no loads from the exchange wave
+  if (tid == g.xt) {
+    unsigned long long tot = 0;
+    int it = 0;
+#pragma nounroll
+    for (;;) {
+      constexpr int NX = NW <= kXWords ? NW : 1;
+      unsigned long long c[NX];
+#pragma unroll
+      for (int i = 0; i < NX; ++i)
+        c[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool done = true;
+      tot = 0;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        done = done && (int)(c[i] & 0xffull) >= g.P;
+        tot += c[i] >> 8;
+      }
+      if (done || sh.xabort) break;
+      if (++it > kSpinCap) {
+        sh.xabort = 1;
+        if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
+        break;
+      }
+    }
+    sh.gd[slot] = (double)tot * (scale / kFix);
+  }
+  ++g.phase;
+  barrier_lds();
+  return sh.gd[slot];
+}
 template <int BLOCK, int NPT>
 __device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared<BLOCK, NPT>& sh,
                                           int& rb) {
-  v = block_sum<BLOCK, NPT>(v, sh, rb);
-  if (g.P == 1) return v;
-  const int slot = g.phase & 1;
-  if (threadIdx.x == 0) {
-    unsigned long long* w = grp_phase_words(g);
-    const unsigned long long q = (unsigned long long)fmax(0.0, rint(v / scale * kFix));
-    const unsigned long long add = (q << 8) | 1ull;
-    unsigned long long cur = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
-    cur = grp_wait<BLOCK, NPT>(w, cur, g.P, g, sh);
-    sh.gd[slot] = (double)(cur >> 8) * (scale / kFix);
-  }
-  ++g.phase;
-  __syncthreads();
-  return sh.gd[slot];
+  return grp_sum<BLOCK, NPT>(v, scale, g, sh, rb, [] {});
 }
 
 template <int BLOCK, int NPT>
@@ -250,7 +305,7 @@ __device__ __forceinline__ float grp_max(float v, Grp& g, Shared<BLOCK, NPT>& sh
   v = block_max<BLOCK, NPT>(v, sh, rb);
   if (g.P == 1) return v;
   const int slot = g.phase & 1;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == g.xt) {
     unsigned long long* w = grp_phase_words(g);
     const uint32_t bits = __float_as_uint(v);
     const uint32_t key = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
@@ -262,8 +317,17 @@ __device__ __forceinline__ float grp_max(float v, Grp& g, Shared<BLOCK, NPT>& sh
     sh.gf[slot] = __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
   }
   ++g.phase;
-  __syncthreads();
+  barrier_lds();
   return sh.gf[slot];
+}
+
+// True in the waves that hold row data (all but a split workgroup's exchange
+// wave).  Read from the first lane so the compiler sees a wave-uniform
+// branch: loads issued under it then land in their destination registers
+// without a merge copy that would wait for them.
+template <int BLOCK>
+__device__ __forceinline__ bool row_wave() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x) < BLOCK;
 }
 
 // ---- rows --------------------------------------------------------------------
@@ -285,11 +349,12 @@ __device__ __forceinline__ void load_logits(Row<BLOCK, NPT>& r, const float* src
   const int tid = threadIdx.x;
   // every load is issued at an in-range address and the padding selected
   // afterwards, so the loads need no branches
+  const bool row = tid < BLOCK;  // not an extra wave of a split workgroup
   if ((V & 3) == 0) {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      const bool in = e0 < V;
+      const bool in = row && e0 < V;
       const float4 x = *reinterpret_cast<const float4*>(src + (in ? e0 : 0));
       r.v[k] = in ? x : make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
     }
@@ -299,10 +364,10 @@ __device__ __forceinline__ void load_logits(Row<BLOCK, NPT>& r, const float* src
       const int e0 = (k * BLOCK + tid) * 4;
       const float x0 = src[min(e0 + 0, V - 1)], x1 = src[min(e0 + 1, V - 1)];
       const float x2 = src[min(e0 + 2, V - 1)], x3 = src[min(e0 + 3, V - 1)];
-      r.v[k].x = e0 + 0 < V ? x0 : -FLT_MAX;
-      r.v[k].y = e0 + 1 < V ? x1 : -FLT_MAX;
-      r.v[k].z = e0 + 2 < V ? x2 : -FLT_MAX;
-      r.v[k].w = e0 + 3 < V ? x3 : -FLT_MAX;
+      r.v[k].x = row && e0 + 0 < V ? x0 : -FLT_MAX;
+      r.v[k].y = row && e0 + 1 < V ? x1 : -FLT_MAX;
+      r.v[k].z = row && e0 + 2 < V ? x2 : -FLT_MAX;
+      r.v[k].w = row && e0 + 3 < V ? x3 : -FLT_MAX;
     }
   }
 }
@@ -458,49 +523,79 @@ __device__ __forceinline__ void issue_row_lds(const float* row, int V, float4* q
   }
 }
 
+// The candidates of a node, one per lane (lane i < nk holds candidate i, in
+// every wave; lanes past nk hold tok = -1): node id, drafted token (-1 if
+// outside the vocabulary), its uniform and q_i(t_i).  Read with readlane, so
+// a chain step needs no LDS lookups to test its candidate.
+struct Cand {
+  int kid, tok;
+  float u, q;
+};
+
+// Brings rows into this XCD's L2 ahead of use: one 4-byte direct-to-LDS load
+// per 128-byte line, into a scratch LDS word nothing reads.  Written as
+// inline assembly (M0 saved and restored around it) so the compiler does not
+// treat the transfer as a pending LDS write that every later LDS read must
+// wait for; the hardware counts it like any vector load, so later waits can
+// only become longer, never too short.
+__device__ __forceinline__ void l2_touch(const float* p, uint32_t sink_lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(sink_lds), "v"(p)
+      : "memory");
+}
+
 // One candidate of the multi-round chain at a node: the ratio test of
 // candidate s against the current row `cur` (mass C, entry ut at the
 // candidate's token) and, on rejection, the adjusted row into `nxt`.
 // Returns true if the candidate is accepted; otherwise `nxt` holds the current
 // row afterwards (the update, or a copy of `cur` in the rare case that the
-// update leaves no mass).  Lane i < nk of wave 0 carries `val`, the current
-// row's entry at candidate i's token, updated with the same fp32 operations as
-// the row (so bit-identical to it) from the gathered sh.qt table.  With VEC,
-// row s is in (or arriving in) qlds and row s+1's prefetch is issued here.
-template <int BLOCK, int NPT, bool VEC>
+// update leaves no mass).  Lane i < nk of every wave carries `val`, the
+// current row's entry at candidate i's token, updated with the same fp32
+// operations as the row (so bit-identical to it) from the gathered sh.qt
+// table.  The next candidate's draft row is prefetched while this one's
+// reduction runs: with RP into the registers qn (split rows; row s is in qn
+// on entry and row s + 1 is loaded into it once read), else with VEC into
+// qlds by direct-to-LDS loads.
+template <int BLOCK, int NPT, bool VEC, bool RP, bool RATIO>
 __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<BLOCK, NPT>& cur,
                                            Row<BLOCK, NPT>& nxt, double& C, float& ut, float& val,
-                                           int s, int nk, bool stop_at_accept, Grp& grp,
-                                           Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
-  const int tid = threadIdx.x, V = a.V;
+                                           const Cand& cd, float4 (&qn)[NPT], int s, int nk,
+                                           bool stop_at_accept, Grp& grp, Shared<BLOCK, NPT>& sh,
+                                           float4* qlds, int& rb) {
+  const int tid = threadIdx.x, lane = tid & 63, V = a.V;
   // this workgroup's slice of candidate i's draft row (the whole row when P = 1)
-  auto qrow = [&](int i) { return a.draft + (ob + sh.kids[i]) * V + grp.base; };
+  auto qrow = [&](int i) { return a.draft + (ob + lane_i(cd.kid, i)) * V + grp.base; };
   const int len = grp.len;
-  const int c = sh.kids[s];
-  const int t = sh.tok[c];
-  const bool tok_ok = t >= 0 && t < V;
-  const double qt = tok_ok ? (double)sh.qt[tri(s, s, nk)] : 0.0;
+  const bool tok_ok = lane_i(cd.tok, s) >= 0;
+  const double qt = tok_ok ? (double)lane_f(cd.q, s) : 0.0;
   const double num = tok_ok ? (double)ut : 0.0;
   // ratio = num / (C qt); accept iff u < ratio, tested without the division
   // (q = 0: ratio is +inf when num > 0, else 0)
   const double den = C * qt;
-  const bool accept = qt > 0.0 ? (double)sh.u[c] * den < num : num > 0.0;
-  if (tid == 0)
+  const bool accept = qt > 0.0 ? (double)lane_f(cd.u, s) * den < num : num > 0.0;
+  if (RATIO && tid == 0)
     sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
   if (stop_at_accept && accept) return true;
   // rejection: nxt = max(0, cur - C q_s) and its mass, one read of q_s
-  if (VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
+  const float q_lane = sh.qt[tri(s, lane, nk)];  // q_s at candidate `lane`'s token
+  if (VEC && !RP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
   const float cf = (float)C;
   const bool more = s + 1 < nk;
-  const float* qs = qrow(s);
   float ps[NPT];
   float4 qv[NPT];
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
-    if constexpr (VEC) {
+    const int e0 = (k * BLOCK + tid) * 4;
+    if constexpr (RP) {
+      qv[k] = tid < BLOCK && e0 < len ? qn[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if constexpr (VEC) {
       qv[k] = qlds[k * BLOCK + tid];
     } else {
-      const int e0 = (k * BLOCK + tid) * 4;
+      const float* qs = qrow(s);
       const float x0 = qs[min(e0 + 0, len - 1)], x1 = qs[min(e0 + 1, len - 1)];
       const float x2 = qs[min(e0 + 2, len - 1)], x3 = qs[min(e0 + 3, len - 1)];
       qv[k] = make_float4(e0 + 0 < len ? x0 : 0.f, e0 + 1 < len ? x1 : 0.f, e0 + 2 < len ? x2 : 0.f,
@@ -517,31 +612,35 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
     w.w = fmaxf(0.f, fmaf(-cf, q.w, cur.v[k].w));
     ps[k] = sum4(w);
   }
-  // next candidate's entry, after and before this update (its tracking lane),
-  // published by the reduction's barrier
-  const int buf = rb;
-  int tn = -1;
-  if (more) {
-    tn = sh.tok[sh.kids[s + 1]];
-    if (tid == s + 1) {
-      sh.nu[buf][0] = fmaxf(0.f, fmaf(-cf, sh.qt[tri(s, tid, nk)], val));
-      sh.nu[buf][1] = val;
-    }
-    if constexpr (VEC) {
+  const float vnew = fmaxf(0.f, fmaf(-cf, q_lane, val));
+  if constexpr (VEC && !RP) {
+    if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of q_s done
       issue_row_lds<BLOCK, NPT>(qrow(s + 1), len, qlds);
     }
   }
-  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, grp, sh, rb);  // Cn <= C
+  // RP: row s + 1's loads are issued once this workgroup's partial mass is
+  // handed to the exchange, so they overlap it (addresses clamped into the
+  // slice, len >= 4; the tail is zeroed on use)
+  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, grp, sh, rb, [&] {
+    if constexpr (RP) {
+      if (more && row_wave<BLOCK>()) {
+        const float* qs = qrow(s + 1);
+#pragma unroll
+        for (int k = 0; k < NPT; ++k)
+          qn[k] = *reinterpret_cast<const float4*>(qs + min((k * BLOCK + tid) * 4, len - 4));
+      }
+    }
+  });  // Cn <= C
   const bool commit = Cn > 0.0;
   if (commit) {
     C = Cn;
-    if (tid > s && tid < nk) val = fmaxf(0.f, fmaf(-cf, sh.qt[tri(s, tid, nk)], val));
+    if (lane > s) val = vnew;
   } else {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) nxt.v[k] = cur.v[k];
   }
-  if (more) ut = (tn >= 0 && tn < V) ? sh.nu[buf][commit ? 0 : 1] : 0.f;
+  if (more) ut = lane_f(val, s + 1);
   return false;
 }
 
@@ -549,44 +648,43 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
 // at the first acceptance when `stop_at_accept`), leaving the adjusted row in
 // U (unnormalised, mass C).  ut is U's entry at the first candidate's token,
 // val the per-lane candidate entries (see chain_step).  Candidate s's ratio
-// goes to sh.ratio[s].  Returns the index (into sh.kids) of the accepted
-// candidate, or -1.  With VEC (V % 4 == 0) the first candidate's row prefetch
-// must already be issued.  Two rows alternate as current and next, so a step
-// moves no registers.
-template <int BLOCK, int NPT, bool VEC>
+// goes to sh.ratio[s] (RATIO).  Returns the index of the accepted candidate,
+// or -1.  The first candidate's row prefetch (RP: into qn) must already be
+// issued.  One copy of the step's code (the loop is not unrolled: the step
+// is long, and a kernel that starts with a cold instruction cache pays for
+// every line of straight code once); the next row is moved into U after each
+// step.
+template <int BLOCK, int NPT, bool VEC, bool RP, bool RATIO>
 __device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, NPT>& U, double& C,
-                                         float ut, float val, int nk, bool stop_at_accept, Grp& grp,
+                                         float ut, float val, const Cand& cd, float4 (&qn)[NPT],
+                                         int nk, bool stop_at_accept, Grp& grp,
                                          Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   Row<BLOCK, NPT> W;
-  for (int s = 0; s < nk; s += 2) {
-    if (chain_step<BLOCK, NPT, VEC>(a, ob, U, W, C, ut, val, s, nk, stop_at_accept, grp, sh, qlds, rb))
+#pragma nounroll
+  for (int s = 0; s < nk; ++s) {
+    if (chain_step<BLOCK, NPT, VEC, RP, RATIO>(a, ob, U, W, C, ut, val, cd, qn, s, nk,
+                                               stop_at_accept, grp, sh, qlds, rb))
       return s;
-    if (s + 1 >= nk) {
 #pragma unroll
-      for (int k = 0; k < NPT; ++k) U.v[k] = W.v[k];
-      break;
-    }
-    if (chain_step<BLOCK, NPT, VEC>(a, ob, W, U, C, ut, val, s + 1, nk, stop_at_accept, grp, sh,
-                                    qlds, rb))
-      return s + 1;
+    for (int k = 0; k < NPT; ++k) U.v[k] = W.v[k];
   }
   return -1;
 }
 
 // Set-up of one node's chain after the tree is in LDS and the node's logits
-// were issued into U: its children, the first candidate's row prefetch, the
-// table qt[k][i] = q_{kid k}(t_{kid i}) and each candidate's own logit
-// (gathered while the row pass runs), then the row statistics.  Returns the
-// argmax (T = 0); sets C, ut (U at the first candidate's token) and, on lane
-// i < nk of wave 0, val = U at candidate i's token.
-template <int BLOCK, int NPT, bool GREEDY, bool VEC>
+// were issued into U: its children (sh.kids, and per lane in cd), the first
+// candidate's row prefetch, the table qt[k][i] = q_{kid k}(t_{kid i}) and
+// each candidate's own logit (gathered while the row pass runs), then the
+// row statistics.  Returns the argmax (T = 0); sets C, ut (U at the first
+// candidate's token) and, on lane i < nk, val = U at candidate i's token.
+template <int BLOCK, int NPT, bool GREEDY, bool VEC, bool RP>
 __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, int b,
                                           int32_t* flags, Row<BLOCK, NPT>& U, double& C, float& ut,
-                                          float& val, Grp& grp, Shared<BLOCK, NPT>& sh,
-                                          float4* qlds, int& rb) {
-  const int tid = threadIdx.x, V = a.V;
+                                          float& val, Cand& cd, float4 (&qn)[NPT], Grp& grp,
+                                          Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
+  const int tid = threadIdx.x, lane = tid & 63, V = a.V;
   find_kids<BLOCK, NPT>(a.N, node, sh);
-  __syncthreads();
+  barrier_lds();
   const int nk = sh.nk;
   int sum_buf = 0;
   ut = 0.f;
@@ -595,12 +693,43 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
     return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, sum_buf,
                                           [](int, float, bool, float) {}, grp, sh, rb);
   } else {
-    if constexpr (VEC) {
-      // slots past the slice are never loaded: zero this thread's (the pass reads them)
+    cd.kid = 0;
+    cd.tok = -1;
+    cd.u = 0.f;
+    cd.q = 0.f;
+    if (lane < nk) {
+      cd.kid = sh.kids[lane];
+      const int t = sh.tok[cd.kid];
+      cd.tok = t >= 0 && t < V ? t : -1;
+      cd.u = sh.u[cd.kid];
+    }
+    if (nk > 0) {
+      const float* q0 = a.draft + (ob + lane_i(cd.kid, 0)) * V + grp.base;
+      if constexpr (RP) {
+        if (row_wave<BLOCK>()) {
 #pragma unroll
-      for (int k = 0; k < NPT; ++k)
-        if ((k * BLOCK + tid) * 4 >= grp.len) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (nk > 0) issue_row_lds<BLOCK, NPT>(a.draft + (ob + sh.kids[0]) * V + grp.base, grp.len, qlds);
+          for (int k = 0; k < NPT; ++k)
+            qn[k] = *reinterpret_cast<const float4*>(q0 + min((k * BLOCK + tid) * 4, grp.len - 4));
+        } else if (__builtin_amdgcn_readfirstlane(tid) >= BLOCK + 64) {
+          // the prefetch wave: the later candidates' slices into L2 now, so
+          // that each step's one-row-ahead register prefetch finds them
+          // there (from a wave that waits on no load of its own, as the
+          // transfers complete in order with every other load of a wave)
+          const int lines = (grp.len + 31) / 32;
+          const uint32_t sink =
+              (uint32_t)(size_t)(__attribute__((address_space(3))) float*)&sh.l2sink[0];
+          for (int c = 1; c < nk; ++c) {
+            const float* row = a.draft + (ob + lane_i(cd.kid, c)) * V + grp.base;
+            for (int l = lane; l < lines; l += 64) l2_touch(row + l * 32, sink);
+          }
+        }
+      } else if constexpr (VEC) {
+        // slots past the slice are never loaded: zero this thread's (the pass reads them)
+#pragma unroll
+        for (int k = 0; k < NPT; ++k)
+          if ((k * BLOCK + tid) * 4 >= grp.len) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+        issue_row_lds<BLOCK, NPT>(q0, grp.len, qlds);
+      }
     }
     constexpr int G = (64 * 64 + BLOCK - 1) / BLOCK;
     float g[G];
@@ -609,36 +738,28 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
       const int f = r * BLOCK + tid;
       const int k = f / 64, i = f & 63;
       g[r] = 0.f;
-      if (k <= i && i < nk) {
+      if (tid < BLOCK && k <= i && i < nk) {
         const int t = sh.tok[sh.kids[i]];
         if (t >= 0 && t < V) g[r] = a.draft[(ob + sh.kids[k]) * V + t];
       }
     }
     float lt = 0.f;
-    int t_own = -1;
-    if (tid < nk) {
-      t_own = sh.tok[sh.kids[tid]];
-      if (t_own >= 0 && t_own < V) lt = a.logits[(ob + node) * V + t_own];
-    }
+    if (cd.tok >= 0) lt = a.logits[(ob + node) * V + cd.tok];
     target_stats<BLOCK, NPT, false>(
         U, a.T, b, flags, C, sum_buf,
-        [&](int buf, float m, bool unit, float invT) {
+        [&](int, float m, bool unit, float invT) {
 #pragma unroll
           for (int r = 0; r < G; ++r) {
             const int f = r * BLOCK + tid;
             const int k = f / 64, i = f & 63;
-            if (k <= i && i < nk) sh.qt[tri(k, i, nk)] = g[r];
+            if (tid < BLOCK && k <= i && i < nk) sh.qt[tri(k, i, nk)] = g[r];
           }
-          if (tid < nk) {
-            val = target_entry(lt, m, unit, invT);
-            if (tid == 0) sh.nu[buf][1] = val;
-          }
+          if (lane < nk) val = target_entry(lt, m, unit, invT);
         },
         grp, sh, rb);
-    if (nk > 0) {
-      const int t0 = sh.tok[sh.kids[0]];
-      ut = (t0 >= 0 && t0 < V) ? sh.nu[sum_buf][1] : 0.f;
-    }
+    // the table is published by the mass reduction's barrier
+    if (lane < nk) cd.q = sh.qt[tri(lane, lane, nk)];
+    ut = lane_f(val, 0);
     return 0;
   }
 }
@@ -659,23 +780,26 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
                                            double thr_given = 0.0) {
   constexpr int NW = BLOCK / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool row = tid < BLOCK;  // not an extra wave of a split workgroup (no mass)
+  if (row) {
 #pragma unroll
-  for (int k = 0; k < NPT; ++k)
-    part[k * BLOCK + tid] =
-        (((double)U.v[k].x + (double)U.v[k].y) + (double)U.v[k].z) + (double)U.v[k].w;
-  __syncthreads();
+    for (int k = 0; k < NPT; ++k)
+      part[k * BLOCK + tid] =
+          (((double)U.v[k].x + (double)U.v[k].y) + (double)U.v[k].z) + (double)U.v[k].w;
+  }
+  barrier_lds();
   double e[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) e[i] = part[tid * NPT + i];
+  for (int i = 0; i < NPT; ++i) e[i] = row ? part[tid * NPT + i] : 0.0;
   double own = 0.0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) own += e[i];
   const double wt = wave_allsum(own);
   const int wbuf = rb;
   rb ^= 1;
-  if (lane == 0) sh.rd[wbuf][wave] = wt;
+  if (lane == 0 && row) sh.rd[wbuf][wave] = wt;
   if (tid == 0) sh.pick = -1;
-  __syncthreads();
+  barrier_lds();
   double Z = 0.0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) Z += sh.rd[wbuf][i];
@@ -721,7 +845,7 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
       sh.sel_before = before_e;
     }
   }
-  __syncthreads();
+  barrier_lds();
   {
     const int entry = sh.sel_entry;
     const int ks = entry / BLOCK, ts = entry - ks * BLOCK;
@@ -745,7 +869,7 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
       sh.pick = cand >= 0 ? cand : lastpos;
     }
   }
-  __syncthreads();
+  barrier_lds();
   int pick = sh.pick;
   if (pick < 0) {
     int last = -1;
@@ -754,7 +878,7 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int idx = (k * BLOCK + tid) * 4 + c;
-        if (idx < V && comp(U.v[k], c) > 0.f) last = idx;
+        if (row && idx < V && comp(U.v[k], c) > 0.f) last = idx;
       }
     pick = block_max_i<BLOCK, NPT>(last, sh, rb);
     if (pick < 0) pick = 0;
@@ -774,7 +898,7 @@ __device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, dou
 #pragma unroll
   for (int k = 0; k < NPT; ++k) s4[k] = sum4(U.v[k]);
   double mine = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s4), sh, rb);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == g.xt) {
     unsigned long long* w = grp_phase_words(g);
     const unsigned long long q = (unsigned long long)fmax(0.0, rint(mine / C * kFix));
     const unsigned long long add = (q << 8) | 1ull;
@@ -794,14 +918,15 @@ __device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, dou
     sh.own_thr = thr_i * (C / kFix);
   }
   ++g.phase;
-  __syncthreads();
+  barrier_lds();
   if (!sh.own) return -1;
   const int pick = inverse_cdf<BLOCK, NPT>(U, u, g.len, sh, part, rb, true, sh.own_start, sh.own_thr);
   return g.base + pick;
 }
 
+// BLOCK row threads; split rows add an exchange wave and a prefetch wave.
 template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC, bool SPLIT>
-__global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
+__global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kernel(VArgs a) {
   static_assert(!SPLIT || (!GREEDY && !PARITY && VEC), "split rows: sampling path only");
   __shared__ Shared<BLOCK, NPT> sh;
   __shared__ float4 qlds[GREEDY ? 1 : NPT * BLOCK];  // draft-row prefetch
@@ -821,7 +946,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   const int j = node - b * N;
   const size_t ob = (size_t)b * N;
   int rb = 0;
-  Grp grp{nullptr, 1, 0, 0, 0, V, a.flags, b};
+  Grp grp{nullptr, 1, 0, 0, 0, V, a.flags, b, 0};
   if constexpr (SPLIT) {
     const int s4 = ((V >> 2) + a.P - 1) / a.P;  // float4 per part
     grp.words = a.xwords + (size_t)node * kXPhases * kXWords;
@@ -829,6 +954,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     grp.part = part;
     grp.base = part * s4 * 4;
     grp.len = min(V - grp.base, s4 * 4);
+    grp.xt = BLOCK;
     if (tid == 0) sh.xabort = 0;
   }
 
@@ -850,11 +976,13 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   }
   if (j == 0 && part == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
     atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
-  __syncthreads();
+  barrier_lds();
   double C = 1.0;
   float ut = 0.f, val = 0.f;
-  const int am =
-      node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, C, ut, val, grp, sh, qlds, rb);
+  Cand cd{0, -1, 0.f, 0.f};
+  float4 qn[NPT];  // split rows: draft-row prefetch registers
+  const int am = node_setup<BLOCK, NPT, GREEDY, VEC, SPLIT>(a, ob, j, b, a.flags, U, C, ut, val, cd,
+                                                             qn, grp, sh, qlds, rb);
   const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
@@ -881,7 +1009,8 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
       }
     }
   } else {
-    const int si = run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, nk, true, grp, sh, qlds, rb);
+    const int si = run_chain<BLOCK, NPT, VEC, SPLIT, PARITY>(a, ob, U, C, ut, val, cd, qn, nk, true,
+                                                             grp, sh, qlds, rb);
     if (si >= 0) {
       acc = sh.kids[si];
       ntested = si + 1;
@@ -906,7 +1035,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     if (SPLIT)
       __hip_atomic_fetch_max(a.nr.nphase + ob + j, grp.phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (part == 0 && tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);
+  if (PARITY && tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);  // read by out_ratio only
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
@@ -944,7 +1073,7 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     // words its nodes used, and the phase counts, for the next call
     for (int n = 0; n < N; ++n) {
       unsigned long long* w = a.xwords + (ob + n) * kXPhases * kXWords;
-      for (int i = tid; i < sh.wph[n] * kXWords; i += BLOCK)
+      for (int i = tid; i < sh.wph[n] * kXWords; i += (int)blockDim.x)
         __hip_atomic_store(w + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid < N) st_c(a.nr.nphase + ob + tid, 0);
@@ -990,10 +1119,12 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     if constexpr (GREEDY) {
       for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
     } else {
-      Grp whole{nullptr, 1, 0, 0, 0, V, nullptr, b};
+      Grp whole{nullptr, 1, 0, 0, 0, V, nullptr, b, 0};
       load_logits<BLOCK, NPT>(U, a.logits + (ob + term) * V, V);
-      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, C, ut, val, whole, sh, qlds, rb);
-      run_chain<BLOCK, NPT, VEC>(a, ob, U, C, ut, val, sh.nk, false, whole, sh, qlds, rb);
+      node_setup<BLOCK, NPT, false, VEC, false>(a, ob, term, b, nullptr, U, C, ut, val, cd, qn, whole,
+                                                sh, qlds, rb);
+      run_chain<BLOCK, NPT, VEC, false, false>(a, ob, U, C, ut, val, cd, qn, sh.nk, false, whole, sh,
+                                               qlds, rb);
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
 #pragma unroll
@@ -1080,7 +1211,7 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
     // node slots rounded up to a multiple of the 8 XCDs, P parts each
     a.P = plan.parts;
     const unsigned sgrid = (unsigned)(((nodes + 7) / 8) * 8 * plan.parts);
-    verify_node_kernel<256, 4, false, false, true, true><<<sgrid, 256, 0, s>>>(a);
+    verify_node_kernel<256, 4, false, false, true, true><<<sgrid, 256 + 128, 0, s>>>(a);
     return hipGetLastError();
   }
 #define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                        \
