@@ -123,9 +123,10 @@ EAGLE_API size_t eagle_tree_attn_workspace(int B, int N, int Hq, int Hkv, int d,
  *   anc      device [B, N] uint64 from eagle_tree_build
  *   sm_scale softmax scale; <= 0 selects 1/sqrt(d)
  *   out      device [B, N, Hq, d] bf16 (round to nearest even); fp32 inside
- *   workspace device, eagle_tree_attn_workspace() bytes (split partials; any
- *            contents; calls that overlap must not share it; may be 0 bytes
- *            when no split is needed)
+ *   workspace device, eagle_tree_attn_workspace() bytes (per-head tickets
+ *            and split partials; zero before its first use, left with zero
+ *            tickets; calls that overlap must not share it; 0 bytes when no
+ *            split is needed)
  *   seq_flags device [B] int32 or NULL (EAGLE_FLAG_BAD_KV_LEN; that
  *            sequence's output is zero)
  * Supported: d in {64, 128}; Hq % Hkv == 0; 1 <= N <= 64; Lmax >= N.

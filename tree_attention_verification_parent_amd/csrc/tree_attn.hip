@@ -28,10 +28,11 @@
 // tree mask, and run the online softmax with cross-lane shuffles.
 //
 // With more than one split, every split writes its normalised rows O / l and
-// log2-sum-exp with coalesced stores, and a small merge kernel on the same
-// stream (one wave per query row, spread over the whole GPU) combines them.
-// The kernel boundary makes the partials visible; no cross-workgroup
-// synchronisation is needed inside the attention kernel.
+// log2-sum-exp with coalesced stores.  Ring variants combine them in the
+// kernel: the unit's last split to finish (a per-unit ticket) reads the other
+// splits' partials from the XCD's L2 and writes the output.  Tile variants
+// leave them to a small merge kernel on the same stream (one wave per query
+// row), whose kernel boundary makes the partials visible.
 #include <stdlib.h>
 
 #include "common.h"
@@ -51,8 +52,8 @@ struct AttnArgs {
   float* part_o;     // [units * splits * RW * D]  O / l of each split
   float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
   int32_t* flags;
+  int32_t* tickets;  // [units] splits finished (ring variants; zero between calls)
   int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
-  int tree_in_merge;  // the merge adds each query's tree keys (ring variants)
   float scale_log2;
 };
 
@@ -294,9 +295,9 @@ __device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_ru
 // flight (two waves per SIMD hide each other's MFMA and softmax latency).
 // The split ranges are laid over the cache capacity Lmax - N, not over
 // kv_len, so the first loads go out before anything else is read; keys at or
-// past kv_len are masked.  The tree keys (each query's ancestors and itself)
-// are left to the merge kernel, which makes every wave's share of a split the
-// same.
+// past kv_len are masked.  The tree keys (each query's ancestors and itself,
+// N <= 32 of them) are one more chunk, masked by the ancestor bits, for one
+// wave of the last split.
 constexpr int kRingThreads = 64 * 8;
 
 template <int D_, int QBW_>
@@ -378,17 +379,6 @@ __device__ __forceinline__ uint32_t prefix_mask8(int key0, int L) {
   return below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
 }
 
-template <int D>
-__device__ __forceinline__ void load_pair(const uint16_t* p, float (&x)[D / 64]) {
-  if constexpr (D / 64 == 2) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(p);
-    x[0] = bf16_bits_to_float(w2 & 0xffffu);
-    x[1] = bf16_bits_to_float(w2 >> 16);
-  } else {
-    x[0] = bf16_bits_to_float(p[0]);
-  }
-}
-
 template <class S>
 __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) {
   constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NKS = S::NKS, NDB = S::NDB;
@@ -418,27 +408,32 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   const uint16_t* vp = a.v + kv_base;
   uint8_t* slot = lds + wave * S::SLOT_BYTES;
 
-  // Direct-to-LDS fill of one chunk: lane l writes 16 bytes at load base + 16 l,
-  // i.e. row t*RPL + l/SPR, slot l%SPR, which receives global slot (l%SPR)^swz(row).
-  // Rows past the prefix re-read its last key (finite data, masked later).
+  // Direct-to-LDS fill of 32 keys from key0: lane l writes 16 bytes at load
+  // base + 16 l, i.e. row t*RPL + l/SPR, slot l%SPR, which receives global
+  // slot (l%SPR)^swz(row).  Rows past key_max re-read it (finite data, masked
+  // later).
   const int r_in = lane / SPR, p_in = lane % SPR;
-  auto issue = [&](int gc) {
+  auto issue_keys = [&](int key0, int key_max) {
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
-      const int key = min(gc * 32 + r, Lp - 1);
+      const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
       __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(slot + t * RPL * D * 2), 16, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
-      const int key = min(gc * 32 + r, Lp - 1);
+      const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
       __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(slot + S::MAT_BYTES + t * RPL * D * 2), 16, 0, 0);
     }
   };
+  auto issue = [&](int gc) { issue_keys(gc * 32, Lp - 1); };
   if (my_n > 0) issue(my_first);
+  // The tree keys [L, L + N) (N <= 32 here) are one more masked chunk, taken
+  // by the wave of the last split with the fewest prefix chunks.
+  const bool tree_wave = split == a.splits - 1 && wave == (ce - cb) % NWAVE;
 
   // committed length, then the queries (needed only once the first chunk is in)
   int L = a.kv_len[b];
@@ -446,6 +441,17 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   if (bad) {
     L = 0;
     if (a.flags && split == 0 && kvh == 0 && tid == 0) atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+  }
+  if (tree_wave && my_n == 0) issue_keys(L, L + a.N - 1);
+  // the tree wave's rows' ancestor masks: bit t of anc[row] admits key L + t
+  uint64_t anc_q[QBW];
+  if (tree_wave) {
+    const uint64_t nmask = a.N == 64 ? ~0ull : (1ull << a.N) - 1ull;
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const int row = qb * 16 + c;
+      anc_q[qb] = row < a.M ? a.anc[(size_t)b * a.N + row / a.G] & nmask : 0ull;
+    }
   }
   const int rows = min(RW, a.M);
   bf16x8 qf[QBW][NKS];
@@ -475,7 +481,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int i = 0; i < my_n; ++i) {
+  const int my_chunks = my_n + (tree_wave ? 1 : 0);
+  for (int i = 0; i < my_chunks; ++i) {
+    const bool tree_chunk = i == my_n;
     const int gc = my_first + NWAVE * i;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
     const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
@@ -498,8 +506,8 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       }
     }
     const int key0 = gc * 32 + 8 * g;
-    const bool need_mask = gc * 32 + 32 > L;
-    const uint32_t ok = prefix_mask8(key0, L);
+    const bool need_mask = tree_chunk || gc * 32 + 32 > L;
+    const uint32_t ok_prefix = prefix_mask8(key0, L);
     bf16x8 pf[QBW];
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
@@ -507,6 +515,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = sc[qb][j >> 2][j & 3] * a.scale_log2;
       if (need_mask) {
+        const uint32_t ok = tree_chunk ? (uint32_t)(anc_q[qb] >> (8 * g)) & 0xffu : ok_prefix;
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
       }
@@ -531,9 +540,12 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       for (int qb = 0; qb < QBW; ++qb)
         acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
     }
-    if (i + 1 < my_n) {
+    if (i + 1 < my_chunks) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
-      issue(gc + NWAVE);
+      if (i + 1 < my_n)
+        issue(gc + NWAVE);
+      else
+        issue_keys(L, L + a.N - 1);
     }
   }
 
@@ -543,19 +555,102 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
   // this split's partial (O / l and log2-sum-exp), staged in LDS so that the
-  // stores are coalesced; the merge kernel adds the tree keys and combines
+  // stores are coalesced
   float* ml = reinterpret_cast<float*>(lds + S::LDS_RING);
   float* stage = reinterpret_cast<float*>(lds + S::LDS_RING + S::LDS_ML);
   fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(acc, m_run, l_run, lds, ml, stage, wave);
   constexpr int SD = D + 4;
-  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
   constexpr int D4 = D / 4;
+  auto out_row = [&](int rl) {
+    const int i = rl / a.G;
+    const int h = kvh * a.G + (rl - i * a.G);
+    return a.out + (((size_t)b * a.N + i) * a.Hq + h) * D;
+  };
+  if (a.splits == 1) {
+    for (int it = tid; it < rows * D4; it += S::THREADS) {
+      const int rl = it / D4, d4 = it - rl * D4;
+      const f32x4 o = bad ? f32x4{0.f, 0.f, 0.f, 0.f}
+                          : *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
+      *reinterpret_cast<u32x2*>(out_row(rl) + 4 * d4) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+    return;
+  }
+  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
   for (int it = tid; it < rows * D4; it += S::THREADS) {
     const int rl = it / D4, d4 = it - rl * D4;
     *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + 4 * d4) =
         *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
   }
   for (int rl = tid; rl < rows; rl += S::THREADS) a.part_lse[pbase + rl] = stage[rl * SD + D];
+
+  // The unit's last split to finish combines the partials.  All splits of a
+  // unit run on one XCD, so its L2 is where they meet: each workgroup's
+  // stores have reached it (vmcnt) before the workgroup takes its ticket,
+  // and the combining workgroup's loads miss its own L1, which held none of
+  // these lines since the kernel started.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* last = reinterpret_cast<int*>(ml);
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(a.tickets + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = done == a.splits - 1;
+    if (done == a.splits - 1) __hip_atomic_store(a.tickets + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!*last) return;
+  // (row, 4 columns) items: w_s = 2^(lse_s - max), o = sum w_s O_s / sum w_s.
+  // The splits go in batches of 8, and a thread's two items share a batch,
+  // so that every load of a batch is issued before any is used.
+  const size_t ub = (size_t)unit * a.splits * RW;
+  const int total = rows * D4;
+  for (int it0 = tid; it0 < total; it0 += 2 * S::THREADS) {
+    const int its[2] = {it0, it0 + S::THREADS};
+    float mt[2] = {-INFINITY, -INFINITY}, lt[2] = {0.f, 0.f};
+    f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      float ls[2][8];
+      f32x4 os[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int it = its[u] < total ? its[u] : it0;  // a duplicate item is never stored
+        const int rl = it / D4, d4 = it - rl * D4;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const bool in = s0 + q < a.splits;
+          const size_t r = ub + (size_t)(in ? s0 + q : 0) * RW + rl;  // in range either way
+          ls[u][q] = in ? a.part_lse[r] : -INFINITY;
+          os[u][q] = in ? *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * d4)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float mb = mt[u];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mb = fmaxf(mb, ls[u][q]);
+        if (mb == -INFINITY) continue;
+        const float f = mt[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt[u] - mb);
+        lt[u] *= f;
+        o[u] *= f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float w = ls[u][q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u][q] - mb);
+          lt[u] += w;
+          o[u] += os[u][q] * w;
+        }
+        mt[u] = mb;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (its[u] >= total) continue;
+      const int rl = its[u] / D4, d4 = its[u] - rl * D4;
+      const float inv = (bad || lt[u] == 0.f) ? 0.f : 1.f / lt[u];
+      *reinterpret_cast<u32x2*>(out_row(rl) + 4 * d4) =
+          u32x2{pack_bf16x2(o[u][0] * inv, o[u][1] * inv), pack_bf16x2(o[u][2] * inv, o[u][3] * inv)};
+    }
+  }
 }
 
 // ============================================================================
@@ -749,13 +844,11 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
 }
 
 // ============================================================================
-// merge: one wave per query row combines the splits' partials and, for the
-// ring variants, adds the query's tree keys (its ancestors and itself)
+// merge (tile variants): one wave per query row combines the splits' partials
 // ============================================================================
 template <int D>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, int RW) {
   constexpr int PL = D / 64;  // 1 or 2 elements per lane
-  constexpr int TB = 8;       // tree keys in flight per batch
   const int lane = threadIdx.x & 63;
   const int qgroup = unit % a.qgroups;
   const int pair = unit / a.qgroups;
@@ -767,20 +860,13 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, i
   const int h = kvh * a.G + (row - i * a.G);
   const int S = a.splits;
   const size_t base = (size_t)unit * S * RW + rl;
-  // independent loads first: length, tree mask, query, split partials
   const int L = a.kv_len[b];
-  const uint64_t nmask = a.N == 64 ? ~0ull : (1ull << a.N) - 1ull;
-  uint64_t am = a.tree_in_merge ? a.anc[(size_t)b * a.N + i] & nmask : 0ull;
-  float qv[PL];
-  load_pair<D>(a.q + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PL, qv);
   const float lse = lane < S ? a.part_lse[base + (size_t)lane * RW] : -INFINITY;
   const bool bad = L < 0 || L > a.Lmax - a.N;
-
-  // splits: state (m, l, o) with o relative to 2^m
-  float m = wave_max(lse);
+  const float m = wave_max(lse);
   const float mu0 = m == -INFINITY ? 0.f : m;
   const float w = __builtin_amdgcn_exp2f(lse - mu0);
-  float l = wave_sum_f(w);
+  const float l = wave_sum_f(w);
   float o[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) o[e] = 0.f;
@@ -797,54 +883,6 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, i
       const float wq = __shfl(w, (sp0 + q) & 63);
 #pragma unroll
       for (int e = 0; e < PL; ++e) o[e] += sp0 + q < S ? wq * v[q][e] : 0.f;
-    }
-  }
-
-  // tree keys: slot L + j for every ancestor j of node i (itself included)
-  if (!bad) {
-    const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D + lane * PL;
-    while (am) {
-      float kk[TB][PL], vv[TB][PL];
-      int nb = 0;
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        // absent entries re-read key L (in range) and are dropped below
-        const int j = am ? __ffsll((unsigned long long)am) - 1 : 0;
-        if (am) {
-          am &= am - 1;
-          nb = t + 1;
-        }
-        const size_t off = kv_base + (size_t)(L + j) * D;
-        load_pair<D>(a.k + off, kk[t]);
-        load_pair<D>(a.v + off, vv[t]);
-      }
-      float sc[TB];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < PL; ++e) d = fmaf(qv[e], kk[t][e], d);
-        sc[t] = d;
-      }
-      wave_allsum_n<TB>(sc);
-      float mb = m;
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        sc[t] = t < nb ? sc[t] * a.scale_log2 : -INFINITY;
-        mb = fmaxf(mb, sc[t]);
-      }
-      const float fs = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
-      l *= fs;
-#pragma unroll
-      for (int e = 0; e < PL; ++e) o[e] *= fs;
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        const float pt = t < nb ? __builtin_amdgcn_exp2f(sc[t] - mb) : 0.f;
-        l += pt;
-#pragma unroll
-        for (int e = 0; e < PL; ++e) o[e] = fmaf(pt, vv[t][e], o[e]);
-      }
-      m = mb;
     }
   }
   const float inv = (bad || l == 0.f) ? 0.f : 1.f / l;
@@ -932,12 +970,16 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [split log2-sum-exp | split O].
+// Workspace: [unit tickets (ring variants) | split log2-sum-exp | split O].
+static size_t ticket_bytes(const AttnPlan& p) {
+  return p.variant <= 1 && p.splits > 1 ? align256((size_t)p.units * 4) : 0;
+}
+
 size_t tree_attn_workspace_bytes(const AttnPlan& p) {
-  if (p.splits <= 1 && p.variant > 1) return 0;  // ring variants always stage partials
+  if (p.splits <= 1) return 0;
   const size_t lse = align256((size_t)p.units * p.splits * p.rows_per_wg * 4);
   const size_t o = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
-  return lse + o;
+  return ticket_bytes(p) + lse + o;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
@@ -953,9 +995,11 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.out = out;
   const bool ring = plan.variant <= 1;
   uint8_t* w = static_cast<uint8_t*>(ws);
+  const size_t tk = ticket_bytes(plan);
   const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
-  a.part_lse = reinterpret_cast<float*>(w);
-  a.part_o = reinterpret_cast<float*>(w + lse);
+  a.tickets = reinterpret_cast<int32_t*>(w);
+  a.part_lse = reinterpret_cast<float*>(w + tk);
+  a.part_o = reinterpret_cast<float*>(w + tk + lse);
   a.flags = flags;
   a.B = B;
   a.N = N;
@@ -969,12 +1013,12 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.splits = plan.splits;
   a.scale_log2 = scale_log2;
   const int padded_units = ((plan.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
-  a.tree_in_merge = ring ? 1 : 0;
   const dim3 grid((unsigned)(padded_units * plan.splits));
   void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
   void* args[] = {&a};
   hipError_t err = hipLaunchKernel(fn, grid, dim3(ring ? kRingThreads : 256), args, 0, s);
-  if (err != hipSuccess || (plan.splits == 1 && !ring)) return err;  // ring variants always merge
+  // ring variants combine their splits in the kernel
+  if (err != hipSuccess || plan.splits == 1 || ring) return err;
   const int rw = plan.rows_per_wg;
   const dim3 mgrid((unsigned)((plan.units * rw + 3) / 4));
   if (plan.d == 64)
