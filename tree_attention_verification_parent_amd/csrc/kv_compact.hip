@@ -49,6 +49,13 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(uint16_t* __restrict__ 
   __syncthreads();
   if (!s_ok) return;
 
+  // rows already in place (source slot L + j, e.g. the root, and every node
+  // of a chain-shaped path) are neither read nor written; if none moves the
+  // workgroup is done
+  int first_move = m + 1;
+  for (int j = m; j >= 0; --j)
+    if (s_src[j] != L + j) first_move = j;
+  if (first_move > m) return;
   const size_t head = ((size_t)b * Hkv + h) * (size_t)Lmax * D;
   const int items = (m + 1) * CPR * 2;
   u32x4 buf[MAX_ITEMS];
@@ -60,7 +67,8 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(uint16_t* __restrict__ 
       const int rem = it - which * (m + 1) * CPR;
       const int j = rem / CPR, ch = rem - j * CPR;
       const uint16_t* base = which ? v : k;
-      buf[n] = *reinterpret_cast<const u32x4*>(base + head + (size_t)s_src[j] * D + ch * 8);
+      if (s_src[j] != L + j)
+        buf[n] = *reinterpret_cast<const u32x4*>(base + head + (size_t)s_src[j] * D + ch * 8);
     }
   }
   __syncthreads();

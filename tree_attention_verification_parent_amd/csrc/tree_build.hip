@@ -18,6 +18,8 @@ __global__ __launch_bounds__(256) void tree_build_kernel(
   const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (b >= B) return;  // uniform per wavefront
   const bool live = lane < N;
+  // both loads first: the position ids need the committed length
+  const int L = pos && live ? kv_len[b] : 0;
   int par = live ? parents[(size_t)b * N + lane] : -1;
   bool bad = false;
   if (live) {
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void tree_build_kernel(
     const size_t o = (size_t)b * N + lane;
     anc[o] = a;
     if (depth) depth[o] = cnt;
-    if (pos) pos[o] = kv_len[b] + cnt;
+    if (pos) pos[o] = L + cnt;
   }
   const uint64_t any_bad = __ballot(bad);
   if (flags && any_bad && lane == 0) atomicOr(flags + b, EAGLE_FLAG_BAD_PARENT);
