@@ -201,7 +201,15 @@ constexpr int kXWords = 9;         // words per phase (a sum: one per row wave; 
 constexpr int kXPhases = 72;       // phases per node: row statistics, candidates, draw
 constexpr int kMaxParts = 8;
 constexpr int kSpinCap = 1 << 20;
-constexpr double kFix = 4503599627370496.0;  // 2^52
+constexpr double kFix = 1125899906842624.0;  // 2^50
+
+// round(x) for 0 <= x < 2^51 as an integer: adding 1.5 * 2^52 leaves a sum
+// whose last mantissa bit weighs 1, so the addition itself rounds to nearest
+// (even), and the integer is the difference of the bit patterns.
+__device__ __forceinline__ unsigned long long fix_round(double x) {
+  constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
+  return (unsigned long long)(__double_as_longlong(x + kMagic) - __double_as_longlong(kMagic));
+}
 
 struct Grp {
   unsigned long long* words;  // this node's exchange words
@@ -233,8 +241,8 @@ __device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, un
   return cur;
 }
 
-// Sum over the node's workgroups of v >= 0, with 0 <= total <= 8 * scale (the
-// fixed-point total, shifted left by 8, stays below 2^64).  mid() runs on
+// Sum over the node's workgroups of v >= 0, with 0 <= total <= scale; inv is
+// kFix / scale (computed by the caller ahead of the reduction).  mid() runs on
 // every thread while the exchange is in flight (after the workgroup reduction
 // when P = 1); it must issue no memory access from the exchange wave.
 // Split rows: every row wave adds its own partial (fixed point, count 1) to
@@ -243,8 +251,8 @@ __device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, un
 // each holds P arrivals, and their integer total is the same in every
 // workgroup.
 template <int BLOCK, int NPT, typename F>
-__device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared<BLOCK, NPT>& sh,
-                                          int& rb, F&& mid) {
+__device__ __forceinline__ double grp_sum(double v, double scale, double inv, Grp& g,
+                                          Shared<BLOCK, NPT>& sh, int& rb, F&& mid) {
   constexpr int NW = BLOCK / 64;
   // (split rows run 256-thread workgroups; wider ones always have P = 1)
   if (NW > kXWords || g.P == 1) {
@@ -258,7 +266,7 @@ __device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared
   if (tid < BLOCK) {
     v = wave_allsum(v);
     if ((tid & 63) == 0) {
-      const unsigned long long q = (unsigned long long)fmax(0.0, rint(v * (kFix / scale)));
+      const unsigned long long q = fix_round(v * inv);
       __hip_atomic_fetch_add(w + (tid >> 6), (q << 8) | 1ull, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -295,9 +303,9 @@ __device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared
   return sh.gd[slot];
 }
 template <int BLOCK, int NPT>
-__device__ __forceinline__ double grp_sum(double v, double scale, Grp& g, Shared<BLOCK, NPT>& sh,
-                                          int& rb) {
-  return grp_sum<BLOCK, NPT>(v, scale, g, sh, rb, [] {});
+__device__ __forceinline__ double grp_sum(double v, double scale, double inv, Grp& g,
+                                          Shared<BLOCK, NPT>& sh, int& rb) {
+  return grp_sum<BLOCK, NPT>(v, scale, inv, g, sh, rb, [] {});
 }
 
 template <int BLOCK, int NPT>
@@ -478,7 +486,8 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
     }
     sum_buf = rb;
     before_sum(sum_buf, m, unit, invT);
-    C = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(s), 32768.0, grp, sh, rb);  // entries <= 1, V <= 32768
+    // entries <= 1, V <= 32768
+    C = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(s), 32768.0, kFix / 32768.0, grp, sh, rb);
     return 0;
   }
 }
@@ -577,6 +586,7 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
   // (q = 0: ratio is +inf when num > 0, else 0)
   const double den = C * qt;
   const bool accept = qt > 0.0 ? (double)lane_f(cd.u, s) * den < num : num > 0.0;
+  const double inv = kFix / C;  // for the mass exchange; its latency hides behind the pass
   if (RATIO && tid == 0)
     sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
   if (stop_at_accept && accept) return true;
@@ -622,7 +632,7 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
   // RP: row s + 1's loads are issued once this workgroup's partial mass is
   // handed to the exchange, so they overlap it (addresses clamped into the
   // slice, len >= 4; the tail is zeroed on use)
-  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, grp, sh, rb, [&] {
+  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, inv, grp, sh, rb, [&] {
     if constexpr (RP) {
       if (more && row_wave<BLOCK>()) {
         const float* qs = qrow(s + 1);
@@ -900,7 +910,7 @@ __device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, dou
   double mine = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s4), sh, rb);
   if (threadIdx.x == g.xt) {
     unsigned long long* w = grp_phase_words(g);
-    const unsigned long long q = (unsigned long long)fmax(0.0, rint(mine / C * kFix));
+    const unsigned long long q = fix_round(mine * (kFix / C));
     const unsigned long long add = (q << 8) | 1ull;
     unsigned long long tot = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
     for (int p2 = g.part + 1; p2 < g.P; ++p2)
@@ -963,9 +973,12 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
   Row<BLOCK, NPT> U;
   load_logits<BLOCK, NPT>(U, a.logits + (ob + j) * V + grp.base, grp.len);
 
-  // tree, tokens, uniforms
+  // tree, tokens, uniforms; the committed length too (only the walk needs it,
+  // and it would be a round trip of its own there)
   bool tok_bad = false;
+  int Lkv = 0;
   if (tid < N) {
+    Lkv = a.kv_len[b];
     int par = a.parents[ob + tid];
     if (tid == 0 || par < 0 || par >= tid) par = tid == 0 ? -1 : 0;
     const int tk = a.tokens[ob + tid];
@@ -1085,7 +1098,7 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
     const bool on = tid <= m_acc;
     const int pn = on ? sh.path[tid] : -1;
     a.path[o] = pn;
-    a.kv_src[o] = on ? a.kv_len[b] + pn : -1;
+    a.kv_src[o] = on ? Lkv + pn : -1;
     a.acc_tokens[o] = tid < m_acc ? sh.tok[sh.path[tid + 1]] : -1;
   }
   if (tid == 0) {
