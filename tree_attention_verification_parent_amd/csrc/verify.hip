@@ -99,6 +99,8 @@ __device__ __forceinline__ float ld_c(float* p) {
       __hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+constexpr int kMaxParts = 8;  // split rows: workgroups per node
+
 template <int BLOCK, int NPT>
 struct Shared {
   static constexpr int NW = BLOCK / 64;
@@ -116,9 +118,8 @@ struct Shared {
   int pick;
   double gd[2];  // split rows: broadcast of the cross-workgroup results
   float gf[2];
+  double pm[kMaxParts];  // split rows: each part's mass of the current row
   int xabort;    // split rows: a wait timed out, later waits are skipped
-  int own;       // split rows: this part holds the final draw's crossing
-  double own_start, own_thr;
   int last, term;
   int wacc[64], wbonus[64], wnt[64], wph[64];
   float l2sink[64];  // split rows: destination of the L2 prefetch (never read)
@@ -193,13 +194,16 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
 // order), so the prefetch of the next draft row stays in flight across the
 // exchange.  The other only brings the node's later draft rows into L2 at
 // the start, for the same reason.
-// Sums travel as fixed point relative to a known bound (value << 8 | count),
-// so the total is an exact integer sum, the same in every workgroup; a max
-// travels as an order-preserving 32-bit key with a separate count.  A wait
-// that exceeds kSpinCap polls sets EAGLE_FLAG_TIMEOUT and skips later waits.
-constexpr int kXWords = 9;         // words per phase (a sum: one per row wave; the final draw: P)
-constexpr int kXPhases = 72;       // phases per node: row statistics, candidates, draw
-constexpr int kMaxParts = 8;
+// Sums travel as fixed point relative to a known bound: every row wave of
+// every part writes its partial (value << 8 | 1, never zero) to a slot of its
+// own, and the exchange wave reads the P x 4 slots until all are written, so
+// every part forms the same exact integer total, and the same per-part
+// masses, which the final draw uses to find the part that holds its crossing
+// without another exchange.  A max travels as an order-preserving 32-bit
+// key with a separate count.  A wait that exceeds kSpinCap polls sets
+// EAGLE_FLAG_TIMEOUT and skips later waits.
+constexpr int kXWords = kMaxParts * 4;  // words per phase: one per (part, row wave)
+constexpr int kXPhases = 72;            // phases per node: row statistics, candidates
 constexpr int kSpinCap = 1 << 20;
 constexpr double kFix = 1125899906842624.0;  // 2^50
 
@@ -255,48 +259,46 @@ __device__ __forceinline__ double grp_sum(double v, double scale, double inv, Gr
                                           Shared<BLOCK, NPT>& sh, int& rb, F&& mid) {
   constexpr int NW = BLOCK / 64;
   // (split rows run 256-thread workgroups; wider ones always have P = 1)
-  if (NW > kXWords || g.P == 1) {
+  if (NW != 4 || g.P == 1) {
     v = block_sum<BLOCK, NPT>(v, sh, rb);
     mid();
     return v;
   }
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int slot = g.phase & 1;
   unsigned long long* w = grp_phase_words(g);
   if (tid < BLOCK) {
     v = wave_allsum(v);
-    if ((tid & 63) == 0) {
-      const unsigned long long q = fix_round(v * inv);
-      __hip_atomic_fetch_add(w + (tid >> 6), (q << 8) | 1ull, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (lane == 0)  // an add into a zero word: atomics meet at the memory side, as the polls do
+      __hip_atomic_fetch_add(w + g.part * NW + (tid >> 6), (fix_round(v * inv) << 8) | 1ull,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   mid();  // guarded by the caller: no loads from the exchange wave
-  if (tid == g.xt) {
-    unsigned long long tot = 0;
+  if ((tid >> 6) == (g.xt >> 6)) {
+    // the exchange wave: lane l < P * NW reads slot l (part l / NW)
+    const int nslots = g.P * NW;
+    unsigned long long x = 1ull;
     int it = 0;
 #pragma nounroll
     for (;;) {
-      constexpr int NX = NW <= kXWords ? NW : 1;
-      unsigned long long c[NX];
-#pragma unroll
-      for (int i = 0; i < NX; ++i)
-        c[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bool done = true;
-      tot = 0;
-#pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        done = done && (int)(c[i] & 0xffull) >= g.P;
-        tot += c[i] >> 8;
-      }
-      if (done || sh.xabort) break;
+      if (lane < nslots) x = __hip_atomic_load(w + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(x != 0ull) || sh.xabort) break;
       if (++it > kSpinCap) {
-        sh.xabort = 1;
-        if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
+        if (lane == 0) {
+          sh.xabort = 1;
+          if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
+        }
         break;
       }
     }
-    sh.gd[slot] = (double)tot * (scale / kFix);
+    // integers below 2^53: exact in fp64, in any order
+    double q = lane < nslots ? (double)(x >> 8) : 0.0;
+    q += dpp_d<kDppXor1>(q);  // the NW = 4 waves of a part are one quad
+    q += dpp_d<kDppXor2>(q);
+    const double tot = wave_allsum(lane < nslots && (lane & 3) == 0 ? q : 0.0);
+    const double unit = scale / kFix;
+    if (tot > 0.0 && lane < nslots && (lane & 3) == 0) sh.pm[lane >> 2] = q * unit;
+    if (lane == 0) sh.gd[slot] = tot * unit;
   }
   ++g.phase;
   barrier_lds();
@@ -896,41 +898,23 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   return pick;
 }
 
-// Final draw over a split row: every part adds its slice mass (fixed point
-// relative to C) to the total word and to the prefix word of every later
-// part, so each part learns the exact integer mass before its slice and the
-// total; the one part whose slice holds u * total searches its slice.
+// Final draw over a split row.  The exchange that produced the row's mass
+// left every part's mass of it in sh.pm, identical in every part, so each
+// part knows the mass before its slice and the total without another
+// exchange; the one part whose slice holds u * total searches its slice.
 // Returns the drawn id in the owning part, -1 in the others.
 template <int BLOCK, int NPT>
-__device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, double C, Grp& g,
+__device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, Grp& g,
                                           Shared<BLOCK, NPT>& sh, double* part, int& rb) {
-  float s4[NPT];
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) s4[k] = sum4(U.v[k]);
-  double mine = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s4), sh, rb);
-  if (threadIdx.x == g.xt) {
-    unsigned long long* w = grp_phase_words(g);
-    const unsigned long long q = fix_round(mine * (kFix / C));
-    const unsigned long long add = (q << 8) | 1ull;
-    unsigned long long tot = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
-    for (int p2 = g.part + 1; p2 < g.P; ++p2)
-      __hip_atomic_fetch_add(w + p2, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tot = grp_wait<BLOCK, NPT>(w, tot, g.P, g, sh);
-    unsigned long long before = 0;
-    if (g.part > 0) {
-      const unsigned long long pw = __hip_atomic_load(w + g.part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      before = grp_wait<BLOCK, NPT>(w + g.part, pw, g.part, g, sh) >> 8;
-    }
-    const double Zi = (double)(tot >> 8), thr_i = (double)u * Zi;
-    const double lo = (double)before, hi = (double)(before + q);
-    sh.own = lo <= thr_i && (thr_i < hi || g.part == g.P - 1);
-    sh.own_start = lo * (C / kFix);
-    sh.own_thr = thr_i * (C / kFix);
+  double tot = 0.0, lo = 0.0;
+  for (int p = 0; p < g.P; ++p) {  // fixed order: the same sums in every part
+    if (p == g.part) lo = tot;
+    tot += sh.pm[p];
   }
-  ++g.phase;
-  barrier_lds();
-  if (!sh.own) return -1;
-  const int pick = inverse_cdf<BLOCK, NPT>(U, u, g.len, sh, part, rb, true, sh.own_start, sh.own_thr);
+  const double thr = (double)u * tot;
+  const bool own = lo <= thr && (thr < lo + sh.pm[g.part] || g.part == g.P - 1);
+  if (!own) return -1;
+  const int pick = inverse_cdf<BLOCK, NPT>(U, u, g.len, sh, part, rb, true, lo, thr);
   return g.base + pick;
 }
 
@@ -1028,7 +1012,7 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
       acc = sh.kids[si];
       ntested = si + 1;
     } else if constexpr (SPLIT) {
-      bonus = split_draw<BLOCK, NPT>(U, sh.u[0], C, grp, sh, reinterpret_cast<double*>(qlds), rb);
+      bonus = split_draw<BLOCK, NPT>(U, sh.u[0], grp, sh, reinterpret_cast<double*>(qlds), rb);
     } else {
       bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh, reinterpret_cast<double*>(qlds), rb);
     }
