@@ -154,6 +154,32 @@ def test_attention_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("idx", [0, 1])
+def test_attention_workspace_reuse(idx):
+    """The ring kernel combines its splits through per-unit tickets in the
+    workspace: one workspace serves repeated calls with identical results and
+    is left with zero tickets (units = B * Hkv for the ring shapes)."""
+    cfg = W.get(idx)
+    s = W.make_step(cfg, 1.0)
+    kv_len = dev(s.kv_len)
+    anc, _, _ = ev.tree_build(dev(s.parents), kv_len)
+    nbytes = ev.binding.tree_attn_workspace_bytes(cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.d, s.Lmax)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    q, k, v = bf(s.q), bf(s.k_cache), bf(s.v_cache)
+    outs = []
+    for rep in range(3):
+        say(f"attention workspace reuse {cfg.name} call {rep}")
+        out = ev.tree_attn(q, k, v, kv_len, anc, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy())
+        tickets = ws[: cfg.B * cfg.Hkv * 4].cpu().numpy()
+        assert not tickets.any()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    ref, _, _, _ = run_attention(s)
+    assert np.array_equal(outs[0], ref)
+
+
 # ---------------------------------------------------------------------------- verification
 def _check_probs(gpu_probs, step):
     B, N, V = step.target_logits.shape

@@ -119,6 +119,8 @@ struct Shared {
   double gd[2];  // split rows: broadcast of the cross-workgroup results
   float gf[2];
   double pm[kMaxParts];  // split rows: each part's mass of the current row
+  float mp[kMaxParts];   // split rows: each part's own logit maximum
+  float fp[kMaxParts];   // split rows: exp((m_p - max) / T), each part's scale
   int xabort;    // split rows: a wait timed out, later waits are skipped
   int last, term;
   int wacc[64], wbonus[64], wnt[64], wph[64];
@@ -202,7 +204,7 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
 // without another exchange.  A max travels as an order-preserving 32-bit
 // key with a separate count.  A wait that exceeds kSpinCap polls sets
 // EAGLE_FLAG_TIMEOUT and skips later waits.
-constexpr int kXWords = kMaxParts * 4;  // words per phase: one per (part, row wave)
+constexpr int kXWords = kMaxParts * 5;  // words per phase: one per (part, row wave), one per part
 constexpr int kXPhases = 72;            // phases per node: row statistics, candidates
 constexpr int kSpinCap = 1 << 20;
 constexpr double kFix = 1125899906842624.0;  // 2^50
@@ -419,6 +421,77 @@ __device__ __forceinline__ float target_entry(float x, float m, bool unit, float
   return exp_neg(unit ? x - m : (x - m) * invT);
 }
 
+// Split rows: a row's maximum and mass in one exchange.  Each part has
+// scaled its slice by its own maximum m_loc (U = exp((l - m_loc) / T),
+// entries <= 1, 1024 per row wave).  Every row wave adds its partial mass to
+// its slot and wave 0 also posts m_loc (an order-preserving key); every part
+// then forms, with the same operations, the maximum M, the factors
+// f_p = exp((m_p - M) / T), each part's mass f_p S_p and the total in a fixed
+// order.  The caller rescales its slice by f_part.  Returns the total.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ double grp_stats(double v, float m_loc, bool unit, float invT, Grp& g,
+                                            Shared<BLOCK, NPT>& sh) {
+  constexpr int NW = BLOCK / 64;
+  static_assert(NW == 4, "split rows: four row waves");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int slot = g.phase & 1;
+  unsigned long long* w = grp_phase_words(g);
+  const int nsum = g.P * NW;
+  if (tid < BLOCK) {
+    v = wave_allsum(v);
+    if (lane == 0) {
+      __hip_atomic_fetch_add(w + g.part * NW + (tid >> 6), (fix_round(v * (kFix / 1024.0)) << 8) | 1ull,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        const uint32_t bits = __float_as_uint(m_loc);
+        const uint32_t key = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+        __hip_atomic_fetch_add(w + nsum + g.part, ((unsigned long long)key << 8) | 1ull,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if ((tid >> 6) == (g.xt >> 6)) {
+    // the exchange wave: lanes [0, nsum) read the mass slots, lanes
+    // [nsum, nsum + P) the maxima
+    const int nslots = nsum + g.P;
+    unsigned long long x = 1ull;
+    int it = 0;
+#pragma nounroll
+    for (;;) {
+      if (lane < nslots) x = __hip_atomic_load(w + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(x != 0ull) || sh.xabort) break;
+      if (++it > kSpinCap) {
+        if (lane == 0) {
+          sh.xabort = 1;
+          if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
+        }
+        break;
+      }
+    }
+    const bool is_max = lane >= nsum && lane < nslots;
+    const uint32_t k = (uint32_t)(x >> 8);
+    const float mp = is_max ? __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k) : -INFINITY;
+    const float M = wave_allmax(mp);
+    const float f = is_max ? exp_neg(unit ? mp - M : (mp - M) * invT) : 0.f;
+    if (is_max) {
+      sh.mp[lane - nsum] = mp;
+      sh.fp[lane - nsum] = f;
+    }
+    // integers below 2^53: exact in fp64, in any order
+    double q = lane < nsum ? (double)(x >> 8) : 0.0;
+    q += dpp_d<kDppXor1>(q);  // the NW = 4 waves of a part are one quad
+    q += dpp_d<kDppXor2>(q);
+    const float fq = __shfl(f, nsum + (lane >> 2));  // the factor of this lane's part
+    const double mass = lane < nsum && (lane & 3) == 0 ? (double)fq * q * (1024.0 / kFix) : 0.0;
+    const double tot = wave_allsum(mass);
+    if (lane < nsum && (lane & 3) == 0) sh.pm[lane >> 2] = mass;
+    if (lane == 0) sh.gd[slot] = tot;
+  }
+  ++g.phase;
+  barrier_lds();
+  return sh.gd[slot];
+}
+
 // Target row statistics of one node from its logits (already in U): flags
 // non-finite logits (they are given no mass); T = 0 returns the lowest-index
 // argmax; T > 0 turns U into exp((l - max)/T) and returns its mass in C.
@@ -473,7 +546,9 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
-    const float m = grp_max<BLOCK, NPT>(lm, grp, sh, rb);
+    const bool split = BLOCK == 256 && grp.P > 1;
+    // split rows: this part's own maximum (the global one comes with the mass)
+    const float m = split ? block_max<BLOCK, NPT>(lm, sh, rb) : grp_max<BLOCK, NPT>(lm, grp, sh, rb);
     const bool unit = T == 1.f;
     const float invT = 1.f / T;
     float s[NPT];
@@ -488,6 +563,20 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
     }
     sum_buf = rb;
     before_sum(sum_buf, m, unit, invT);
+    if constexpr (BLOCK == 256) {
+      if (split) {
+        C = grp_stats<BLOCK, NPT>((double)pairwise<NPT>(s), m, unit, invT, grp, sh);
+        const float f = sh.fp[grp.part];
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+          U.v[k].x *= f;
+          U.v[k].y *= f;
+          U.v[k].z *= f;
+          U.v[k].w *= f;
+        }
+        return 0;
+      }
+    }
     // entries <= 1, V <= 32768
     C = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(s), 32768.0, kFix / 32768.0, grp, sh, rb);
     return 0;
@@ -766,9 +855,16 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
             const int k = f / 64, i = f & 63;
             if (tid < BLOCK && k <= i && i < nk) sh.qt[tri(k, i, nk)] = g[r];
           }
-          if (lane < nk) val = target_entry(lt, m, unit, invT);
+          if (lane < nk) val = target_entry(lt, m, unit, invT);  // (split rows: redone below)
         },
         grp, sh, rb);
+    if (RP && grp.P > 1 && lane < nk && cd.tok >= 0) {
+      // split rows: the entry as the part that holds the token computed it,
+      // from that part's maximum and scale
+      const int slice = (((V >> 2) + grp.P - 1) / grp.P) * 4;
+      const int pt = cd.tok / slice;
+      val = target_entry(lt, sh.mp[pt], a.T == 1.f, 1.f / a.T) * sh.fp[pt];
+    }
     // the table is published by the mass reduction's barrier
     if (lane < nk) cd.q = sh.qt[tri(lane, lane, nk)];
     ut = lane_f(val, 0);
