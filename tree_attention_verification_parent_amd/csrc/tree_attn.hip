@@ -299,6 +299,7 @@ __device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_ru
 // N <= 32 of them) are one more chunk, masked by the ancestor bits, for one
 // wave of the last split.
 constexpr int kRingThreads = 64 * 8;
+constexpr int kNonTemporal = 2;  // cache-policy bits of a load: nt
 
 template <int D_, int QBW_>
 struct RingShape {
@@ -411,7 +412,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // Direct-to-LDS fill of 32 keys from key0: lane l writes 16 bytes at load
   // base + 16 l, i.e. row t*RPL + l/SPR, slot l%SPR, which receives global
   // slot (l%SPR)^swz(row).  Rows past key_max re-read it (finite data, masked
-  // later).
+  // later).  The stream is read once: non-temporal loads (nt) keep it from
+  // evicting the split partials that the unit's last split reads back from
+  // this XCD's L2 (the stream per XCD is about the size of its L2).
   const int r_in = lane / SPR, p_in = lane % SPR;
   auto issue_keys = [&](int key0, int key_max) {
 #pragma unroll
@@ -419,14 +422,14 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(slot + t * RPL * D * 2), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(slot + t * RPL * D * 2), 16, 0, kNonTemporal);
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(slot + S::MAT_BYTES + t * RPL * D * 2), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(slot + S::MAT_BYTES + t * RPL * D * 2), 16, 0, kNonTemporal);
     }
   };
   auto issue = [&](int gc) { issue_keys(gc * 32, Lp - 1); };
