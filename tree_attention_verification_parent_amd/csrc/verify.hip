@@ -648,6 +648,23 @@ __device__ __forceinline__ void l2_touch(const float* p, uint32_t sink_lds) {
       : "memory");
 }
 
+// True in a split workgroup's prefetch wave (the last one).
+template <int BLOCK>
+__device__ __forceinline__ bool prefetch_wave() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x) >= BLOCK + 64;
+}
+
+// Draft rows touched ahead of the chain by the prefetch wave: few enough that
+// its transfers are issued quickly (its workgroup's barriers wait for it).
+constexpr int kL2Ahead = 3;
+
+// One wave brings a row slice of len floats into L2 (one touch per line).
+__device__ __forceinline__ void l2_touch_slice(const float* row, int len, float* sink) {
+  const int lines = (len + 31) / 32;
+  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sink;
+  for (int l = threadIdx.x & 63; l < lines; l += 64) l2_touch(row + l * 32, lds);
+}
+
 // One candidate of the multi-round chain at a node: the ratio test of
 // candidate s against the current row `cur` (mass C, entry ut at the
 // candidate's token) and, on rejection, the adjusted row into `nxt`.
@@ -730,6 +747,8 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
 #pragma unroll
         for (int k = 0; k < NPT; ++k)
           qn[k] = *reinterpret_cast<const float4*>(qs + min((k * BLOCK + tid) * 4, len - 4));
+      } else if (s + 1 + kL2Ahead < nk && prefetch_wave<BLOCK>()) {
+        l2_touch_slice(qrow(s + 1 + kL2Ahead), len, sh.l2sink);
       }
     }
   });  // Cn <= C
@@ -811,18 +830,6 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
 #pragma unroll
           for (int k = 0; k < NPT; ++k)
             qn[k] = *reinterpret_cast<const float4*>(q0 + min((k * BLOCK + tid) * 4, grp.len - 4));
-        } else if (__builtin_amdgcn_readfirstlane(tid) >= BLOCK + 64) {
-          // the prefetch wave: the later candidates' slices into L2 now, so
-          // that each step's one-row-ahead register prefetch finds them
-          // there (from a wave that waits on no load of its own, as the
-          // transfers complete in order with every other load of a wave)
-          const int lines = (grp.len + 31) / 32;
-          const uint32_t sink =
-              (uint32_t)(size_t)(__attribute__((address_space(3))) float*)&sh.l2sink[0];
-          for (int c = 1; c < nk; ++c) {
-            const float* row = a.draft + (ob + lane_i(cd.kid, c)) * V + grp.base;
-            for (int l = lane; l < lines; l += 64) l2_touch(row + l * 32, sink);
-          }
         }
       } else if constexpr (VEC) {
         // slots past the slice are never loaded: zero this thread's (the pass reads them)
@@ -867,6 +874,14 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
     }
     // the table is published by the mass reduction's barrier
     if (lane < nk) cd.q = sh.qt[tri(lane, lane, nk)];
+    if (RP && prefetch_wave<BLOCK>()) {
+      // the prefetch wave: the next candidates' slices into L2, so that each
+      // step's one-row-ahead register prefetch finds them there; issued once
+      // this wave's own loads are consumed (a wave's transfers complete in
+      // order), and kept kL2Ahead rows ahead by the chain steps
+      for (int c = 1; c <= kL2Ahead && c < nk; ++c)
+        l2_touch_slice(a.draft + (ob + lane_i(cd.kid, c)) * V + grp.base, grp.len, sh.l2sink);
+    }
     ut = lane_f(val, 0);
     return 0;
   }
@@ -1140,10 +1155,15 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
 
   // ---- walk (last workgroup of sequence b) -----------------------------------
   if (tid < N) {
-    sh.wacc[tid] = ld_c(a.nr.acc + ob + tid);
-    sh.wbonus[tid] = ld_c(a.nr.bonus + ob + tid);
-    sh.wnt[tid] = ld_c(a.nr.ntested + ob + tid);
-    if (SPLIT) sh.wph[tid] = min(ld_c(a.nr.nphase + ob + tid), kXPhases);
+    // all four loads in flight before any result is used
+    const int r0 = ld_c(a.nr.acc + ob + tid);
+    const int r1 = ld_c(a.nr.bonus + ob + tid);
+    const int r2 = ld_c(a.nr.ntested + ob + tid);
+    const int r3 = SPLIT ? ld_c(a.nr.nphase + ob + tid) : 0;
+    sh.wacc[tid] = r0;
+    sh.wbonus[tid] = r1;
+    sh.wnt[tid] = r2;
+    if (SPLIT) sh.wph[tid] = min(r3, kXPhases);
   }
   __syncthreads();
   if (tid == 0) {
@@ -1163,11 +1183,15 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
   }
   if constexpr (SPLIT) {
     // every workgroup of the sequence is past its last exchange: zero the
-    // words its nodes used, and the phase counts, for the next call
+    // words its nodes used, and the phase counts, for the next call.  Wide
+    // streaming stores (a store instruction is slow to issue, so few and
+    // wide ones); the kernel's end makes them visible to the next call,
+    // whose exchanges read the words only with device-coherent atomics.
+    static_assert(kXWords % 2 == 0, "16-byte stores");
     for (int n = 0; n < N; ++n) {
-      unsigned long long* w = a.xwords + (ob + n) * kXPhases * kXWords;
-      for (int i = tid; i < sh.wph[n] * kXWords; i += (int)blockDim.x)
-        __hip_atomic_store(w + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      u32x4* w = reinterpret_cast<u32x4*>(a.xwords + (ob + n) * kXPhases * kXWords);
+      for (int i = tid; i < sh.wph[n] * (kXWords / 2); i += (int)blockDim.x)
+        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, w + i);
     }
     if (tid < N) st_c(a.nr.nphase + ob + tid, 0);
   }
