@@ -1187,10 +1187,13 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
     // streaming stores (a store instruction is slow to issue, so few and
     // wide ones); the kernel's end makes them visible to the next call,
     // whose exchanges read the words only with device-coherent atomics.
+    // Each wave takes whole nodes, so a lane issues only the stores of the
+    // nodes of its wave.
     static_assert(kXWords % 2 == 0, "16-byte stores");
-    for (int n = 0; n < N; ++n) {
+    const int nwaves = (int)blockDim.x >> 6, wave = tid >> 6, lane = tid & 63;
+    for (int n = wave; n < N; n += nwaves) {
       u32x4* w = reinterpret_cast<u32x4*>(a.xwords + (ob + n) * kXPhases * kXWords);
-      for (int i = tid; i < sh.wph[n] * (kXWords / 2); i += (int)blockDim.x)
+      for (int i = lane; i < sh.wph[n] * (kXWords / 2); i += 64)
         __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, w + i);
     }
     if (tid < N) st_c(a.nr.nphase + ob + tid, 0);
