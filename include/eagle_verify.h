@@ -197,6 +197,26 @@ EAGLE_API eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const 
                                    int32_t* seq_flags, void* stream);
 
 /*
+ * eagle_verify_accept followed by eagle_kv_compact on the result, in one
+ * launch: the workgroup that walks a sequence's tree also moves the K/V of
+ * its accepted path (EAGLE, paperlayer.ai summary, §2 Preliminaries and A.2
+ * for the walk; §3 EAGLE: accepted tokens are recorded for the next round).
+ * Outputs and effects are exactly those of the two calls in sequence with
+ * the same arguments (no out_probs / out_final_dist / out_ratio here); the
+ * cache, Hkv, d, Lmax, new_kv_len and their rules are those of
+ * eagle_kv_compact, the rest those of eagle_verify_accept (same workspace).
+ * A kv_len out of range sets EAGLE_FLAG_BAD_KV_LEN and leaves that
+ * sequence's cache unchanged (new_kv_len = kv_len).
+ */
+EAGLE_API eagle_status_t eagle_verify_accept_compact(
+    const int32_t* draft_tokens, const float* draft_probs, const float* target_logits,
+    const int32_t* parents, const int32_t* kv_len, int B, int N, int V, float temperature,
+    const float* uniforms, int32_t* accept_len, int32_t* path, int32_t* accepted_tokens,
+    int32_t* bonus_token, int32_t* kv_src_slots, uint16_t* k_cache, uint16_t* v_cache, int Hkv,
+    int d, int Lmax, int32_t* new_kv_len, void* workspace, size_t workspace_bytes,
+    int32_t* seq_flags, void* stream);
+
+/*
  * KV compaction: record the accepted path in the cache (EAGLE, paperlayer.ai
  * summary, §3 EAGLE: accepted tokens are recorded for the next round).  For
  * every sequence b, KV head and j = 0..accept_len[b], slot kv_len[b] + j of

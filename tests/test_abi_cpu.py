@@ -107,6 +107,33 @@ def test_verify_argument_errors():
     assert call(B=0) == binding.EAGLE_OK
 
 
+def test_verify_compact_argument_errors():
+    """The fused walk + compaction entry checks both halves' arguments on the
+    host, before any launch (these fake pointers are never dereferenced)."""
+    L = ev.lib()
+    same = ctypes.c_void_p(0x2000)
+
+    other = ctypes.c_void_p(0x3000)  # distinct from kv_len, which it must not alias
+
+    def call(B=1, N=8, V=1000, T=1.0, draft=FAKE, kcache=FAKE, Hkv=4, d=64, Lmax=136, kvl=FAKE,
+             new_len=other, ws=FAKE, ws_bytes=1 << 30):
+        return L.eagle_verify_accept_compact(FAKE, draft, FAKE, FAKE, kvl, B, N, V, T, FAKE, FAKE,
+                                             FAKE, FAKE, FAKE, FAKE, kcache, FAKE, Hkv, d, Lmax,
+                                             new_len, ws, ws_bytes, None, None)
+
+    assert call(V=40000) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(T=-1.0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(draft=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(kcache=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(new_len=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(kvl=same, new_len=same) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(d=80) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(Hkv=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(Lmax=4) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(ws=None) == binding.EAGLE_ERR_WORKSPACE
+    assert call(B=0) == binding.EAGLE_OK
+
+
 def test_compact_and_build_argument_errors():
     L = ev.lib()
     same = ctypes.c_void_p(0x2000)

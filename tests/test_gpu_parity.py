@@ -373,6 +373,53 @@ def test_full_step_with_compaction(idx, T):
     assert np.array_equal(new_len.cpu().numpy(), nl)
 
 
+# The fused entry point against the two separate calls it replaces: the same
+# walk outputs, the same cache bytes and new lengths.  Small draft noise makes
+# the walks accept, so path nodes actually move.
+@pytest.mark.parametrize("idx,T,sigma", [(0, 1.0, 0.05), (1, 1.0, 0.05), (1, 1.0, None),
+                                         (1, 0.0, None), (2, 1.0, 0.1), (3, 1.0, 0.1),
+                                         (4, 1.0, 0.1)])
+def test_fused_compaction_matches_separate_calls(idx, T, sigma):
+    cfg = W.get(idx)
+    if sigma is not None:
+        cfg = W.shrink(cfg, sigma_d=sigma)
+    s = W.make_step(cfg, T)
+    say(f"fused compaction {cfg.name} T={T} sigma={sigma}")
+    gpu = run_verify(s, want_final_dist=False, want_ratio=False)
+    k1, v1 = bf(s.k_cache), bf(s.v_cache)
+    nl1 = ev.kv_compact(k1, v1, dev(s.kv_len), dev(gpu["kv_src"]), dev(gpu["accept_len"]))
+    k2, v2 = bf(s.k_cache), bf(s.v_cache)
+    out = ev.verify_accept_compact(dev(s.tokens), None if s.draft_probs is None else dev(s.draft_probs),
+                                   dev(s.target_logits), dev(s.parents), dev(s.kv_len), s.T,
+                                   dev(s.uniforms), k2, v2)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "path", "accepted_tokens", "bonus", "kv_src"):
+        assert np.array_equal(out[key].cpu().numpy(), gpu[key]), key
+    assert np.array_equal(out["new_kv_len"].cpu().numpy(), nl1.cpu().numpy())
+    assert np.array_equal(bits(k1), bits(k2))
+    assert np.array_equal(bits(v1), bits(v2))
+    moved = int(sum((gpu["path"][b, 1:gpu["accept_len"][b] + 1] != np.arange(1, gpu["accept_len"][b] + 1)).sum()
+                    for b in range(cfg.B)))
+    say(f"  accept_len {gpu['accept_len'].tolist()[:8]}, moved rows {moved}")
+    if sigma is not None and idx != 0:
+        assert moved > 0
+
+
+def test_fused_compaction_flags_bad_kv_len():
+    cfg = W.shrink(W.get(0), B=3, V=64, sigma_d=0.05)
+    s = W.make_step(cfg, 1.0, seed=5)
+    s.kv_len[1] = cfg.L + 10 ** 6  # out of range: flagged, that sequence's cache untouched
+    k, v = bf(s.k_cache), bf(s.v_cache)
+    flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    out = ev.verify_accept_compact(dev(s.tokens), dev(s.draft_probs), dev(s.target_logits),
+                                   dev(s.parents), dev(s.kv_len), s.T, dev(s.uniforms), k, v,
+                                   seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist()[1] & ev.binding.FLAG_BAD_KV_LEN
+    assert int(out["new_kv_len"][1]) == int(s.kv_len[1])
+    assert np.array_equal(bits(k)[1], s.k_cache[1]) and np.array_equal(bits(v)[1], s.v_cache[1])
+
+
 def test_compaction_rejects_bad_slots():
     cfg = W.shrink(W.get(0), B=3, V=16)
     s = W.make_step(cfg, 1.0, seed=4)

@@ -53,6 +53,8 @@ _SIGNATURES = {
     "eagle_verify_accept_workspace": (_SZ, [_I, _I, _I]),
     "eagle_verify_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _SZ, _P, _P]),
+    "eagle_verify_accept_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P, _P]),
     "eagle_kv_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
 }
 
@@ -197,6 +199,42 @@ def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, tem
         _ptr(uniforms, torch.float32, "uniforms"),
         _ptr(o["accept_len"]), _ptr(o["path"]), _ptr(o["accepted_tokens"]), _ptr(o["bonus"]),
         _ptr(o["kv_src"]), _ptr(o.get("probs")), _ptr(o.get("final_dist")), _ptr(o.get("ratio")),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
+    return o
+
+
+def verify_accept_compact(draft_tokens, draft_probs, target_logits, parents, kv_len, temperature,
+                          uniforms, k_cache, v_cache, *, outputs=None, new_kv_len=None,
+                          workspace=None, seq_flags=None, stream=None):
+    """Acceptance walk and KV compaction in one launch; returns the walk's
+    outputs (as verify_accept) plus "new_kv_len"."""
+    B, N, V = target_logits.shape
+    _, Hkv, Lmax, d = k_cache.shape
+    dev = target_logits.device
+    o = dict(outputs) if outputs else {}
+    if "accept_len" not in o:
+        o["accept_len"] = torch.empty(B, dtype=torch.int32, device=dev)
+        o["path"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        o["accepted_tokens"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+        o["bonus"] = torch.empty(B, dtype=torch.int32, device=dev)
+        o["kv_src"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if new_kv_len is None:
+        new_kv_len = o.get("new_kv_len")
+    if new_kv_len is None:
+        new_kv_len = torch.empty_like(kv_len)
+    o["new_kv_len"] = new_kv_len
+    if workspace is None:
+        workspace = alloc_workspace(verify_accept_workspace_bytes(B, N, V), dev)
+    _check(lib().eagle_verify_accept_compact(
+        _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(draft_probs, torch.float32, "draft_probs"),
+        _ptr(target_logits, torch.float32, "target_logits"), _ptr(parents, torch.int32, "parents"),
+        _ptr(kv_len, torch.int32, "kv_len"), B, N, V, float(temperature),
+        _ptr(uniforms, torch.float32, "uniforms"),
+        _ptr(o["accept_len"]), _ptr(o["path"]), _ptr(o["accepted_tokens"]), _ptr(o["bonus"]),
+        _ptr(o["kv_src"]), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), Hkv, d, Lmax,
+        _ptr(new_kv_len, torch.int32, "new_kv_len"),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
         _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
     return o

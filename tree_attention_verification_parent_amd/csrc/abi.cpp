@@ -158,6 +158,51 @@ eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* dra
                                          kv_len, B, N, temperature, uniforms, accept_len, path,
                                          accepted_tokens, bonus_token, kv_src_slots, out_probs,
                                          out_final_dist, out_ratio, workspace, seq_flags,
+                                         eagle::VerifyCompact{}, as_stream(stream)),
+                    "verification launch");
+}
+
+static eagle_status_t check_compact_shape(int N, int Hkv, int d, int Lmax) {
+  if (Hkv < 1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "Hkv must be >= 1");
+  if (d != 64 && d != 128) return fail(EAGLE_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  if (Lmax < N) return fail(EAGLE_ERR_INVALID_ARGUMENT, "Lmax (%d) must be >= N (%d)", Lmax, N);
+  return EAGLE_OK;
+}
+
+eagle_status_t eagle_verify_accept_compact(
+    const int32_t* draft_tokens, const float* draft_probs, const float* target_logits,
+    const int32_t* parents, const int32_t* kv_len, int B, int N, int V, float temperature,
+    const float* uniforms, int32_t* accept_len, int32_t* path, int32_t* accepted_tokens,
+    int32_t* bonus_token, int32_t* kv_src_slots, uint16_t* k_cache, uint16_t* v_cache, int Hkv,
+    int d, int Lmax, int32_t* new_kv_len, void* workspace, size_t workspace_bytes,
+    int32_t* seq_flags, void* stream) {
+  eagle_status_t st = check_verify_shape(B, N, V);
+  if (st != EAGLE_OK) return st;
+  st = check_compact_shape(N, Hkv, d, Lmax);
+  if (st != EAGLE_OK) return st;
+  if (!isfinite(temperature) || temperature < 0.f)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "temperature must be finite and >= 0");
+  if (B == 0) return EAGLE_OK;
+  if (!draft_tokens || !target_logits || !parents || !kv_len || !uniforms)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "draft_tokens, target_logits, parents, kv_len and uniforms must be non-NULL");
+  if (temperature > 0.f && !draft_probs)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "draft_probs is required when temperature > 0");
+  if (!accept_len || !path || !accepted_tokens || !bonus_token || !kv_src_slots)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "accept_len, path, accepted_tokens, bonus_token and kv_src_slots must be non-NULL");
+  if (!k_cache || !v_cache || !new_kv_len)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "k_cache, v_cache and new_kv_len must be non-NULL");
+  if (new_kv_len == kv_len) return fail(EAGLE_ERR_INVALID_ARGUMENT, "new_kv_len must not alias kv_len");
+  if ((double)B * Hkv > 2.0e9) return fail(EAGLE_ERR_UNSUPPORTED, "B * Hkv too large");
+  const eagle::VerifyPlan plan = eagle::plan_verify(B, N, V);
+  const size_t need = eagle::verify_workspace_bytes(plan);
+  if (!workspace || workspace_bytes < need)
+    return fail(EAGLE_ERR_WORKSPACE, "verification needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const eagle::VerifyCompact kc{k_cache, v_cache, new_kv_len, Hkv, d, Lmax};
+  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, target_logits, parents,
+                                         kv_len, B, N, temperature, uniforms, accept_len, path,
+                                         accepted_tokens, bonus_token, kv_src_slots, nullptr,
+                                         nullptr, nullptr, workspace, seq_flags, kc,
                                          as_stream(stream)),
                     "verification launch");
 }

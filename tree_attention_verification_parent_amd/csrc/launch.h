@@ -50,12 +50,20 @@ struct VerifyPlan {
 VerifyPlan plan_verify(int B, int N, int V);
 size_t verify_workspace_bytes(const VerifyPlan& p);
 
+// Compaction fused into the walk (eagle_verify_accept_compact); k == nullptr: none.
+struct VerifyCompact {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t* new_len;
+  int Hkv, d, Lmax;
+};
+
 hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
                          const float* logits, const int32_t* parents, const int32_t* kv_len,
                          int B, int N, float T, const float* uniforms, int32_t* accept_len,
                          int32_t* path, int32_t* acc_tokens, int32_t* bonus, int32_t* kv_src,
                          float* out_probs, float* out_final, float* out_ratio, void* ws,
-                         int32_t* flags, hipStream_t s);
+                         int32_t* flags, const VerifyCompact& kc, hipStream_t s);
 
 // KV compaction ------------------------------------------------------------
 hipError_t launch_kv_compact(uint16_t* k, uint16_t* v, const int32_t* kv_len,

@@ -77,6 +77,7 @@ struct VArgs {
   float* out_ratio;
   int32_t* flags;
   NodeResults nr;
+  VerifyCompact kc;            // compaction fused into the walk (kc.k == nullptr: none)
   unsigned long long* xwords;  // [B*N][kXPhases][kXWords] exchange words (split rows; zero between calls)
   int N, V;
   int nodes;  // B * N
@@ -124,6 +125,8 @@ struct Shared {
   int xabort;    // split rows: a wait timed out, later waits are skipped
   int last, term;
   int wacc[64], wbonus[64], wnt[64], wph[64];
+  int mv[64];      // fused compaction: the path positions whose K/V move
+  int nmv, Lkv;
   float l2sink[64];  // split rows: destination of the L2 prefetch (never read)
   int path[64];
 };
@@ -1029,6 +1032,69 @@ __device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, Grp
   return g.base + pick;
 }
 
+// KV compaction fused into the walk (the effect of eagle_kv_compact with this
+// call's kv_src_slots and accept_len): the K/V of path node path[j] move from
+// slot L + path[j] to slot L + j, j = 1..m (the root stays).  The moving rows'
+// 16-byte chunks are taken in row order, a batch at a time, every read of a
+// batch before any of its writes (a destination may be the source of an
+// earlier path node in the same batch).  A later batch never reads what an
+// earlier one wrote: its source L + path[j'] lies past every destination
+// L + j, j < j', already written (path[j'] >= j').
+template <int BLOCK, int NPT>
+__device__ __noinline__ void fused_compact(const VerifyCompact& kc, int b, int N, int m,
+                                           int32_t* flags, Shared<BLOCK, NPT>& sh) {
+  const int tid = threadIdx.x;
+  const int L = sh.Lkv;
+  const bool ok = L >= 0 && L <= kc.Lmax - N;
+  if (tid == 0) {
+    kc.new_len[b] = ok ? L + m + 1 : L;
+    if (!ok && flags) atomicOr(flags + b, EAGLE_FLAG_BAD_KV_LEN);
+    int n = 0;
+    for (int j = 1; ok && j <= m; ++j)
+      if (sh.path[j] != j) sh.mv[n++] = j;
+    sh.nmv = n;
+  }
+  __syncthreads();
+  const int nmv = sh.nmv;
+  if (nmv == 0) return;
+  const int cpr = kc.d / 8;                   // 16-byte chunks per key row
+  const int per_head = cpr, per_mat = kc.Hkv * cpr, per_row = 2 * per_mat;
+  const int total = nmv * per_row;
+  const int nt = (int)blockDim.x;
+  constexpr int kItems = 8;                   // chunks per thread and batch
+  for (int base = 0; base < total; base += kItems * nt) {
+    u32x4 buf[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int idx = base + i * nt + tid;
+      if (idx < total) {
+        const int r = idx / per_row, rem = idx - r * per_row;
+        const int which = rem / per_mat, rem2 = rem - which * per_mat;  // 0: K, 1: V
+        const int h = rem2 / per_head, ch = rem2 - h * per_head;
+        const int j = sh.mv[r];
+        const size_t head = ((size_t)b * kc.Hkv + h) * (size_t)kc.Lmax;
+        const uint16_t* base_p = which ? kc.v : kc.k;
+        buf[i] = *reinterpret_cast<const u32x4*>(base_p + (head + L + sh.path[j]) * kc.d + ch * 8);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every read of the batch is done before any write
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int idx = base + i * nt + tid;
+      if (idx < total) {
+        const int r = idx / per_row, rem = idx - r * per_row;
+        const int which = rem / per_mat, rem2 = rem - which * per_mat;
+        const int h = rem2 / per_head, ch = rem2 - h * per_head;
+        const int j = sh.mv[r];
+        const size_t head = ((size_t)b * kc.Hkv + h) * (size_t)kc.Lmax;
+        uint16_t* base_p = which ? kc.v : kc.k;
+        *reinterpret_cast<u32x4*>(base_p + (head + L + j) * kc.d + ch * 8) = buf[i];
+      }
+    }
+  }
+}
+
 // BLOCK row threads; split rows add an exchange wave and a prefetch wave.
 template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kernel(VArgs a) {
@@ -1074,6 +1140,7 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
   int Lkv = 0;
   if (tid < N) {
     Lkv = a.kv_len[b];
+    if (tid == 0) sh.Lkv = Lkv;
     int par = a.parents[ob + tid];
     if (tid == 0 || par < 0 || par >= tid) par = tid == 0 ? -1 : 0;
     const int tk = a.tokens[ob + tid];
@@ -1212,6 +1279,7 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
     a.accept_len[b] = m_acc;
     a.bonus[b] = sh.pick;
   }
+  if (a.kc.k) fused_compact(a.kc, b, N, m_acc, a.flags, sh);
   if (PARITY && a.out_ratio) {
     // tested nodes: the candidates each path node's chain tested
     if (tid < N) {
@@ -1291,7 +1359,7 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
                          int B, int N, float T, const float* uniforms, int32_t* accept_len,
                          int32_t* path, int32_t* acc_tokens, int32_t* bonus, int32_t* kv_src,
                          float* out_probs, float* out_final, float* out_ratio, void* ws,
-                         int32_t* flags, hipStream_t s) {
+                         int32_t* flags, const VerifyCompact& kc, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t nodes = (size_t)B * N;
   VArgs a{};
@@ -1310,6 +1378,7 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   a.out_final = out_final;
   a.out_ratio = out_ratio;
   a.flags = flags;
+  a.kc = kc;
   a.nr.counter = reinterpret_cast<int32_t*>(w);
   uint8_t* nb = w + align256(plan.ws_counters);
   a.nr.acc = reinterpret_cast<int32_t*>(nb);
