@@ -1,12 +1,12 @@
 """Benchmark of the tree-verification step on one MI355X.
 
 One step = the whole hot path over one batch: tree mask (eagle_tree_build),
-tree attention (eagle_tree_attn), vocabulary statistics + acceptance walk
-(eagle_verify_accept) and KV compaction (eagle_kv_compact), in that data
-order on one stream.  The workload is the LLaMA2-7B-shaped layer (batch 1,
-32 MHA heads, head dim 128, 2048 committed tokens, 26-node static tree,
-vocabulary 32000), seeded and synthetic, at temperature 1 (temperature 0 is
-reported beside it).
+tree attention (eagle_tree_attn), then vocabulary statistics, acceptance walk
+and KV compaction in one launch (eagle_verify_accept_compact; the walking
+workgroup moves the accepted rows), in that data order on one stream.  The
+workload is the LLaMA2-7B-shaped layer (batch 1, 32 MHA heads, head dim 128,
+2048 committed tokens, 26-node static tree, vocabulary 32000), seeded and
+synthetic, at temperature 1 (temperature 0 is reported beside it).
 
 Inputs are resident in HBM before timing.  The step sequence is captured in a
 HIP graph (as a serving loop would run it) and rotates through enough copies
@@ -94,8 +94,10 @@ class Step:
 
     def verify(self, i):
         sl = self.slots[i % len(self.slots)]
-        self.ev.verify_accept(self.tokens, sl["draft"], sl["logits"], self.parents, self.kv_len,
-                              self.T, self.uniforms, outputs=self.res, workspace=self.ver_ws)
+        self.ev.verify_accept_compact(self.tokens, sl["draft"], sl["logits"], self.parents,
+                                      self.kv_len, self.T, self.uniforms, sl["k"], sl["v"],
+                                      outputs=self.res, new_kv_len=self.new_len,
+                                      workspace=self.ver_ws)
 
     def run(self, i):
         ev = self.ev
@@ -103,10 +105,10 @@ class Step:
         ev.tree_build(self.parents, self.kv_len, anc=self.anc, depth=self.depth, pos=self.pos)
         ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
                      workspace=self.attn_ws)
-        ev.verify_accept(self.tokens, sl["draft"], sl["logits"], self.parents, self.kv_len, self.T,
-                         self.uniforms, outputs=self.res, workspace=self.ver_ws)
-        ev.kv_compact(sl["k"], sl["v"], self.kv_len, self.res["kv_src"], self.res["accept_len"],
-                      new_kv_len=self.new_len)
+        ev.verify_accept_compact(self.tokens, sl["draft"], sl["logits"], self.parents,
+                                 self.kv_len, self.T, self.uniforms, sl["k"], sl["v"],
+                                 outputs=self.res, new_kv_len=self.new_len,
+                                 workspace=self.ver_ws)
 
 
 def graph_of(torch, fn, count):
@@ -288,7 +290,7 @@ def main():
                      "kernel": "tree_attn", "bytes_per_launch": attn_bytes,
                      "us_per_launch": r1["t_attn"] * 1e6},
         "cpu_baseline": cpu,
-        "kernels_us": {"tree_attn": r1["t_attn"] * 1e6, "verify_accept": r1["t_verify"] * 1e6},
+        "kernels_us": {"tree_attn": r1["t_attn"] * 1e6, "verify_accept_compact": r1["t_verify"] * 1e6},
         "verify_roofline": {"bound": "hbm", "bytes_per_launch": vocab_bytes,
                             "rejected_candidates": r1["rejected"],
                             "achieved": vocab_bytes / r1["t_verify"] / 1e9,

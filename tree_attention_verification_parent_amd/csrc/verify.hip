@@ -1034,15 +1034,16 @@ __device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, Grp
 
 // KV compaction fused into the walk (the effect of eagle_kv_compact with this
 // call's kv_src_slots and accept_len): the K/V of path node path[j] move from
-// slot L + path[j] to slot L + j, j = 1..m (the root stays).  The moving rows'
-// 16-byte chunks are taken in row order, a batch at a time, every read of a
-// batch before any of its writes (a destination may be the source of an
-// earlier path node in the same batch).  A later batch never reads what an
-// earlier one wrote: its source L + path[j'] lies past every destination
-// L + j, j < j', already written (path[j'] >= j').
+// slot L + path[j] to slot L + j, j = 1..m (the root stays).  Each thread owns
+// whole 16-byte columns (one matrix, head and chunk) and moves the moving rows
+// of its columns in increasing j, reading a batch of rows before writing them.
+// No other thread touches those addresses, and in increasing j no read can
+// see an earlier write: the source L + path[j'] of a later row lies past every
+// destination L + j, j < j', already written (path[j'] >= j').  A destination
+// may be the source of an earlier row of the same batch, whose read is done.
 template <int BLOCK, int NPT>
-__device__ __noinline__ void fused_compact(const VerifyCompact& kc, int b, int N, int m,
-                                           int32_t* flags, Shared<BLOCK, NPT>& sh) {
+__device__ inline void fused_compact(const VerifyCompact& kc, int b, int N, int m,
+                                     int32_t* flags, Shared<BLOCK, NPT>& sh) {
   const int tid = threadIdx.x;
   const int L = sh.Lkv;
   const bool ok = L >= 0 && L <= kc.Lmax - N;
@@ -1057,40 +1058,25 @@ __device__ __noinline__ void fused_compact(const VerifyCompact& kc, int b, int N
   __syncthreads();
   const int nmv = sh.nmv;
   if (nmv == 0) return;
-  const int cpr = kc.d / 8;                   // 16-byte chunks per key row
-  const int per_head = cpr, per_mat = kc.Hkv * cpr, per_row = 2 * per_mat;
-  const int total = nmv * per_row;
-  const int nt = (int)blockDim.x;
-  constexpr int kItems = 8;                   // chunks per thread and batch
-  for (int base = 0; base < total; base += kItems * nt) {
-    u32x4 buf[kItems];
+  const int cpr = kc.d / 8;                      // 16-byte chunks per key row
+  const int cols = 2 * kc.Hkv * cpr;             // K columns, then V columns
+  constexpr int kRows = 8;                       // rows per batch
+  for (int c = tid; c < cols; c += (int)blockDim.x) {
+    const int which = c >= kc.Hkv * cpr;
+    const int c2 = c - which * kc.Hkv * cpr;
+    const int h = c2 / cpr, ch = c2 - h * cpr;
+    uint16_t* col = (which ? kc.v : kc.k) +
+                    (((size_t)b * kc.Hkv + h) * (size_t)kc.Lmax + L) * kc.d + ch * 8;
+    for (int r0 = 0; r0 < nmv; r0 += kRows) {
+      u32x4 buf[kRows];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int idx = base + i * nt + tid;
-      if (idx < total) {
-        const int r = idx / per_row, rem = idx - r * per_row;
-        const int which = rem / per_mat, rem2 = rem - which * per_mat;  // 0: K, 1: V
-        const int h = rem2 / per_head, ch = rem2 - h * per_head;
-        const int j = sh.mv[r];
-        const size_t head = ((size_t)b * kc.Hkv + h) * (size_t)kc.Lmax;
-        const uint16_t* base_p = which ? kc.v : kc.k;
-        buf[i] = *reinterpret_cast<const u32x4*>(base_p + (head + L + sh.path[j]) * kc.d + ch * 8);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // every read of the batch is done before any write
+      for (int i = 0; i < kRows; ++i)
+        if (r0 + i < nmv)
+          buf[i] = *reinterpret_cast<const u32x4*>(col + (size_t)sh.path[sh.mv[r0 + i]] * kc.d);
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int idx = base + i * nt + tid;
-      if (idx < total) {
-        const int r = idx / per_row, rem = idx - r * per_row;
-        const int which = rem / per_mat, rem2 = rem - which * per_mat;
-        const int h = rem2 / per_head, ch = rem2 - h * per_head;
-        const int j = sh.mv[r];
-        const size_t head = ((size_t)b * kc.Hkv + h) * (size_t)kc.Lmax;
-        uint16_t* base_p = which ? kc.v : kc.k;
-        *reinterpret_cast<u32x4*>(base_p + (head + L + j) * kc.d + ch * 8) = buf[i];
-      }
+      for (int i = 0; i < kRows; ++i)
+        if (r0 + i < nmv)
+          *reinterpret_cast<u32x4*>(col + (size_t)sh.mv[r0 + i] * kc.d) = buf[i];
     }
   }
 }
