@@ -1,9 +1,10 @@
 """Benchmark of the tree-verification step on one MI355X.
 
-One step = the whole hot path over one batch: tree mask (eagle_tree_build),
-tree attention (eagle_tree_attn), then vocabulary statistics, acceptance walk
-and KV compaction in one launch (eagle_verify_accept_compact; the walking
-workgroup moves the accepted rows), in that data order on one stream.  The
+One step = the whole hot path over one batch in two launches, in data order
+on one stream: the tree mask (ancestor sets, depths, position ids) built
+inside the tree-attention launch (eagle_tree_attn_parents), then vocabulary
+statistics, acceptance walk and KV compaction in one launch
+(eagle_verify_accept_compact; the walking workgroup moves the accepted rows).  The
 workload is the LLaMA2-7B-shaped layer (batch 1, 32 MHA heads, head dim 128,
 2048 committed tokens, 26-node static tree, vocabulary 32000), seeded and
 synthetic, at temperature 1 (temperature 0 is reported beside it).
@@ -89,8 +90,9 @@ class Step:
 
     def attention(self, i):
         sl = self.slots[i % len(self.slots)]
-        self.ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
-                          workspace=self.attn_ws)
+        self.ev.tree_attn_parents(sl["q"], sl["k"], sl["v"], self.kv_len, self.parents,
+                                  out=self.out, anc=self.anc, depth=self.depth, pos=self.pos,
+                                  workspace=self.attn_ws)
 
     def verify(self, i):
         sl = self.slots[i % len(self.slots)]
@@ -102,9 +104,9 @@ class Step:
     def run(self, i):
         ev = self.ev
         sl = self.slots[i % len(self.slots)]
-        ev.tree_build(self.parents, self.kv_len, anc=self.anc, depth=self.depth, pos=self.pos)
-        ev.tree_attn(sl["q"], sl["k"], sl["v"], self.kv_len, self.anc, out=self.out,
-                     workspace=self.attn_ws)
+        ev.tree_attn_parents(sl["q"], sl["k"], sl["v"], self.kv_len, self.parents, out=self.out,
+                             anc=self.anc, depth=self.depth, pos=self.pos,
+                             workspace=self.attn_ws)
         ev.verify_accept_compact(self.tokens, sl["draft"], sl["logits"], self.parents,
                                  self.kv_len, self.T, self.uniforms, sl["k"], sl["v"],
                                  outputs=self.res, new_kv_len=self.new_len,

@@ -137,6 +137,31 @@ EAGLE_API eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_ca
                                uint16_t* out, void* workspace, size_t workspace_bytes,
                                int32_t* seq_flags, void* stream);
 
+/*
+ * Tree mask builder and tree attention in one launch (EAGLE, paperlayer.ai
+ * summary, A.1 Tree Structure and §3 EAGLE: the mask follows the tree's
+ * parent links).  Computes what eagle_tree_build followed by eagle_tree_attn
+ * computes: the kernel derives every node's ancestor set from `parents`
+ * itself, so `out` is bit-identical to eagle_tree_attn with the masks that
+ * eagle_tree_build returns for the same parents.
+ *
+ *   parents  device [B, N] int32 (root parent -1, 0 <= parents[i] < i)
+ *   anc, depth, pos  device [B, N] out or NULL each: the builder's outputs,
+ *            as eagle_tree_build defines them (pos = kv_len + depth), written
+ *            once per sequence by the kernel
+ *   seq_flags device [B] int32 or NULL (EAGLE_FLAG_BAD_KV_LEN as
+ *            eagle_tree_attn, EAGLE_FLAG_BAD_PARENT as eagle_tree_build; a
+ *            bad link is treated as the root)
+ * Every other argument, the workspace (eagle_tree_attn_workspace bytes) and
+ * the supported shapes are those of eagle_tree_attn.
+ */
+EAGLE_API eagle_status_t eagle_tree_attn_parents(const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* kv_len,
+                               const int32_t* parents, int B, int N, int Hq, int Hkv, int d,
+                               int Lmax, float sm_scale, uint16_t* out, uint64_t* anc,
+                               int32_t* depth, int32_t* pos, void* workspace,
+                               size_t workspace_bytes, int32_t* seq_flags, void* stream);
+
 /* Workspace bytes eagle_verify_accept needs for this shape. */
 EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
 

@@ -79,6 +79,28 @@ def test_attention_argument_errors():
     assert call(B=0) == binding.EAGLE_OK  # empty batch: nothing to do
 
 
+def test_attention_from_parents_argument_errors():
+    L = ev.lib()
+    base = dict(B=1, N=8, Hq=4, Hkv=4, d=64, Lmax=136)
+
+    def call(parents=FAKE, ws=FAKE, ws_bytes=1 << 30, scale=0.0, **kw):
+        p = dict(base, **kw)
+        return L.eagle_tree_attn_parents(FAKE, FAKE, FAKE, FAKE, parents, p["B"], p["N"], p["Hq"],
+                                         p["Hkv"], p["d"], p["Lmax"], scale, FAKE, None, None,
+                                         None, ws, ws_bytes, None, None)
+
+    assert call(parents=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert "parents" in L.eagle_last_error().decode()
+    assert call(d=96) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == binding.EAGLE_ERR_UNSUPPORTED
+    assert call(N=65) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(Lmax=4) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(scale=float("inf")) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    need = L.eagle_tree_attn_workspace(1, 8, 4, 4, 64, 136)
+    assert call(ws_bytes=need - 1) == binding.EAGLE_ERR_WORKSPACE
+    assert call(B=0) == binding.EAGLE_OK
+
+
 def test_workspace_sizes():
     L = ev.lib()
     assert L.eagle_tree_attn_workspace(1, 26, 32, 32, 128, 2074) > 0

@@ -154,6 +154,91 @@ def test_attention_deterministic():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------- mask builder fused into attention
+def _fused_vs_two_calls(s, sm_scale=0.0, outputs=True):
+    """eagle_tree_attn_parents against eagle_tree_build + eagle_tree_attn on the
+    same inputs: attention bit-identical, the builder's outputs identical."""
+    B = s.parents.shape[0]
+    parents, kv_len = dev(s.parents), dev(s.kv_len)
+    q, k, v = bf(s.q), bf(s.k_cache), bf(s.v_cache)
+    anc, depth, pos = ev.tree_build(parents, kv_len)
+    ref = ev.tree_attn(q, k, v, kv_len, anc, sm_scale=sm_scale)
+    outs = {}
+    if outputs:
+        outs = dict(anc=torch.full_like(anc, -1), depth=torch.full_like(depth, -7),
+                    pos=torch.full_like(pos, -7))
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    got = ev.tree_attn_parents(q, k, v, kv_len, parents, sm_scale=sm_scale, seq_flags=flags,
+                               **outs)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    if outputs:
+        assert torch.equal(outs["anc"], anc)
+        assert torch.equal(outs["depth"], depth)
+        assert torch.equal(outs["pos"], pos)
+    assert flags.cpu().numpy().sum() == 0
+    return got.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_from_parents_matches_oracle(case):
+    name, B, N, Hq, Hkv, d, kv_lens = case
+    cfg = W.shrink(W.get(0), B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
+    rng = np.random.default_rng(len(name) + 100)
+    parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(B)])
+    s = W.make_step(cfg, 1.0, seed=zlib.crc32(name.encode()) % 1000 + 1, kv_lens=kv_lens,
+                    parents=parents)
+    say(f"attention from parents {name}")
+    got = _fused_vs_two_calls(s)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_attention_from_parents_full_configs(idx):
+    cfg = W.get(idx)
+    s = W.make_step(cfg, cfg.temperatures[-1])
+    say(f"attention from parents, full config {cfg.name}")
+    _fused_vs_two_calls(s, outputs=idx != 2)
+
+
+def test_attention_from_parents_chain_scale_and_splits(monkeypatch):
+    cfg = W.shrink(W.get(1), B=2, L=600, Hq=8, Hkv=8, V=16)
+    s = W.make_step(cfg, 1.0, seed=9, kv_lens=[600, 213], parents=np.stack([trees.chain(26)] * 2))
+    for splits in ("1", "3"):
+        monkeypatch.setenv("EAGLE_ATTN_SPLITS", splits)
+        say(f"attention from parents chain splits={splits}")
+        got = _fused_vs_two_calls(s, sm_scale=0.07)
+        ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, sm_scale=0.07)
+        assert np.abs(got - ref).max() < ATOL_ATTN
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 2)])
+def test_attention_from_parents_flags_bad_links(Hq, Hkv):
+    """Bad links are flagged and hang off the root, as in eagle_tree_build;
+    ring (MHA) and tile (GQA) kernels alike."""
+    cfg = W.shrink(W.get(0), B=3, N=6, Hq=Hq, Hkv=Hkv, d=128, V=16)
+    s = W.make_step(cfg, 1.0, seed=4)
+    parents = np.array([[-1, 0, 1, 3, 0, 4], [-1, 0, 0, 1, 2, 2], [5, 0, 1, 2, -2, 4]],
+                       dtype=np.int32)
+    say(f"attention from parents, bad links Hq={Hq} Hkv={Hkv}")
+    p, kv_len = dev(parents), dev(s.kv_len)
+    q, k, v = bf(s.q), bf(s.k_cache), bf(s.v_cache)
+    f1 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    anc, depth, pos = ev.tree_build(p, kv_len, seq_flags=f1)
+    ref = ev.tree_attn(q, k, v, kv_len, anc)
+    f2 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    anc2 = torch.zeros_like(anc)
+    got = ev.tree_attn_parents(q, k, v, kv_len, p, anc=anc2, seq_flags=f2)
+    torch.cuda.synchronize()
+    assert f2.cpu().tolist() == [ev.binding.FLAG_BAD_PARENT, 0, ev.binding.FLAG_BAD_PARENT]
+    assert torch.equal(f1, f2)
+    assert torch.equal(anc2, anc)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("idx", [0, 1])
 def test_attention_workspace_reuse(idx):
     """The ring kernel combines its splits through per-unit tickets in the

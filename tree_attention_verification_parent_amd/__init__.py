@@ -7,6 +7,7 @@ ctypes (binding.py).  Build with `python -m
 tree_attention_verification_parent_amd.build`.
 """
 from .binding import (EagleError, abi_version, alloc_workspace, kv_compact, lib,  # noqa: F401
-                      tree_attn, tree_attn_workspace_bytes, tree_build, validate_tree_host,
+                      tree_attn, tree_attn_parents, tree_attn_workspace_bytes, tree_build,
+                      validate_tree_host,
                       verify_accept, verify_accept_compact, verify_accept_workspace_bytes,
                       workspace_clear)

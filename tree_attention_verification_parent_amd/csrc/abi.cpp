@@ -92,6 +92,29 @@ size_t eagle_tree_attn_workspace(int B, int N, int Hq, int Hkv, int d, int Lmax)
   return eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax));
 }
 
+// Shared by both attention entry points: the tree comes either as ancestor
+// masks (anc) or as parent links (parents, masks built in the kernel).
+static eagle_status_t tree_attn_call(const uint16_t* q, const uint16_t* k_cache,
+                                     const uint16_t* v_cache, const int32_t* kv_len,
+                                     const uint64_t* anc, const int32_t* parents, int B, int N,
+                                     int Hq, int Hkv, int d, int Lmax, float sm_scale,
+                                     uint16_t* out, uint64_t* anc_out, int32_t* depth_out,
+                                     int32_t* pos_out, void* workspace, size_t workspace_bytes,
+                                     int32_t* seq_flags, void* stream) {
+  const eagle::AttnPlan plan = eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax);
+  const size_t need = eagle::tree_attn_workspace_bytes(plan);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EAGLE_ERR_WORKSPACE, "tree attention needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(eagle::launch_tree_attn(plan, q, k_cache, v_cache, kv_len, anc, parents,
+                                            anc_out, depth_out, pos_out, B, N, Hq, Hkv, Lmax,
+                                            scale_log2, out, workspace, seq_flags,
+                                            as_stream(stream)),
+                    "tree attention launch");
+}
+
 eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                const int32_t* kv_len, const uint64_t* anc, int B, int N, int Hq,
                                int Hkv, int d, int Lmax, float sm_scale, uint16_t* out,
@@ -103,17 +126,28 @@ eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_cache, const
   if (!q || !k_cache || !v_cache || !kv_len || !anc || !out)
     return fail(EAGLE_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, kv_len, anc and out must be non-NULL");
   if (!isfinite(sm_scale)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
-  const eagle::AttnPlan plan = eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax);
-  const size_t need = eagle::tree_attn_workspace_bytes(plan);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(EAGLE_ERR_WORKSPACE, "tree attention needs %zu workspace bytes (got %zu)", need,
-                workspace ? workspace_bytes : (size_t)0);
-  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
-  const float scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(eagle::launch_tree_attn(plan, q, k_cache, v_cache, kv_len, anc, B, N, Hq, Hkv,
-                                            Lmax, scale_log2, out, workspace, seq_flags,
-                                            as_stream(stream)),
-                    "tree attention launch");
+  return tree_attn_call(q, k_cache, v_cache, kv_len, anc, nullptr, B, N, Hq, Hkv, d, Lmax,
+                        sm_scale, out, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                        seq_flags, stream);
+}
+
+eagle_status_t eagle_tree_attn_parents(const uint16_t* q, const uint16_t* k_cache,
+                                       const uint16_t* v_cache, const int32_t* kv_len,
+                                       const int32_t* parents, int B, int N, int Hq, int Hkv,
+                                       int d, int Lmax, float sm_scale, uint16_t* out,
+                                       uint64_t* anc, int32_t* depth, int32_t* pos,
+                                       void* workspace, size_t workspace_bytes,
+                                       int32_t* seq_flags, void* stream) {
+  eagle_status_t st = check_attn_shape(B, N, Hq, Hkv, d, Lmax);
+  if (st != EAGLE_OK) return st;
+  if (B == 0) return EAGLE_OK;
+  if (!q || !k_cache || !v_cache || !kv_len || !parents || !out)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT,
+                "q, k_cache, v_cache, kv_len, parents and out must be non-NULL");
+  if (!isfinite(sm_scale)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  return tree_attn_call(q, k_cache, v_cache, kv_len, nullptr, parents, B, N, Hq, Hkv, d, Lmax,
+                        sm_scale, out, anc, depth, pos, workspace, workspace_bytes, seq_flags,
+                        stream);
 }
 
 static eagle_status_t check_verify_shape(int B, int N, int V) {

@@ -135,6 +135,52 @@ __device__ __forceinline__ void wave_allsum_n(float (&v)[M]) {
     v[i] = (lane_f(v[i], 0) + lane_f(v[i], 16)) + (lane_f(v[i], 32) + lane_f(v[i], 48));
 }
 
+// Ancestor set, depth and link check of one tree node per lane (lane i owns
+// node i, N <= 64), from the sequence's parent array (EAGLE, paperlayer.ai
+// summary, A.1 Tree Structure: each node attends to its ancestors).  Pointer
+// jumping: after r rounds a lane has OR-ed in the masks of its 2^r nearest
+// ancestors, so 6 rounds cover any depth below 64.  A malformed link (root
+// with a parent, or a parent not below the node) is reported in `bad` and
+// replaced by the root, keeping every mask in range.  Every lane of the wave
+// must call it (cross-lane shuffles); lanes >= N return an empty set.
+struct TreeLinks {
+  uint64_t anc;
+  int depth;
+  bool bad;
+};
+
+__device__ __forceinline__ TreeLinks tree_links_wave(const int32_t* parents_b, int N) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool live = lane < N;
+  int par = live ? parents_b[lane] : -1;
+  bool bad = false;
+  if (live) {
+    if (lane == 0) {
+      bad = par != -1;
+      par = -1;
+    } else if (par < 0 || par >= lane) {
+      bad = true;
+      par = 0;
+    }
+  }
+  uint64_t a = live ? (1ull << lane) : 0ull;
+  int cnt = par >= 0 ? 1 : 0;
+  int jump = par;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = jump >= 0 ? jump : lane;
+    const uint64_t a_j = __shfl(a, src);
+    const int cnt_j = __shfl(cnt, src);
+    const int jump_j = __shfl(jump, src);
+    if (jump >= 0) {
+      a |= a_j;
+      cnt += cnt_j;
+      jump = jump_j;
+    }
+  }
+  return TreeLinks{a, cnt, bad};
+}
+
 // Number of compute units the grids are shaped for (MI355X: 8 XCDs x 32 CUs).
 constexpr int kNumCUs = 256;
 constexpr int kNumXCDs = 8;

@@ -33,6 +33,8 @@ size_t tree_attn_workspace_bytes(const AttnPlan& p);
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_len, const uint64_t* anc,
+                            const int32_t* parents, uint64_t* anc_out, int32_t* depth_out,
+                            int32_t* pos_out,
                             int B, int N, int Hq, int Hkv, int Lmax, float scale_log2,
                             uint16_t* out, void* ws, int32_t* flags, hipStream_t s);
 

@@ -47,7 +47,11 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* kv_len;
-  const uint64_t* anc;
+  const uint64_t* anc;       // ancestor masks [B, N], or null: built from parents
+  const int32_t* parents;    // [B, N] when anc is null
+  uint64_t* anc_out;         // optional tree outputs written when built here
+  int32_t* depth_out;
+  int32_t* pos_out;
   uint16_t* out;
   float* part_o;     // [units * splits * RW * D]  O / l of each split
   float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
@@ -209,6 +213,20 @@ __device__ __forceinline__ bool decode_unit(const AttnArgs& a, UnitCtx& u) {
   return true;
 }
 
+// The tree-mask builder's outputs (ancestor masks, depths, position ids
+// kv_len + depth) of sequence b, written by the one wave per sequence that
+// the kernel picks, when the masks were built from the parent links.
+__device__ __forceinline__ void write_tree_outputs(const AttnArgs& a, int b, const TreeLinks& t) {
+  const int lane = threadIdx.x & 63;
+  const size_t o = (size_t)b * a.N + lane;
+  if (lane < a.N) {
+    if (a.anc_out) a.anc_out[o] = t.anc;
+    if (a.depth_out) a.depth_out[o] = t.depth;
+    if (a.pos_out) a.pos_out[o] = a.kv_len[b] + t.depth;
+  }
+  if (__ballot(t.bad) && lane == 0 && a.flags) atomicOr(a.flags + b, EAGLE_FLAG_BAD_PARENT);
+}
+
 // Q fragments (MFMA B operand) and tree masks of QBW query blocks at unit row r0.
 template <int D, int QBW, int RW>
 __device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u, int r0,
@@ -216,9 +234,20 @@ __device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int N = a.N, G = a.G;
   const uint64_t nmask = N == 64 ? ~0ull : (1ull << N) - 1ull;
+  // masks built from the parent links: every wave derives its sequence's
+  // tree (lane = node); wave 0 of the unit's last split for KV head 0 and
+  // query group 0 writes the builder's outputs
+  uint64_t anc_w = 0;
+  if (a.parents) {
+    const TreeLinks t = tree_links_wave(a.parents + (size_t)u.b * N, N);
+    anc_w = t.anc;
+    if (u.kvh == 0 && u.qgroup == 0 && u.split == a.splits - 1 && threadIdx.x < 64)
+      write_tree_outputs(a, u.b, t);
+  }
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const int row = u.qgroup * RW + r0 + qb * 16 + c;
+    const uint64_t built = a.parents ? __shfl(anc_w, row < a.M ? row / G : 0) : 0ull;
     if (row < a.M) {
       const int i = row / G;
       const int h = u.kvh * G + (row - i * G);
@@ -226,7 +255,7 @@ __device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
         qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
-      anc_q[qb] = a.anc[(size_t)u.b * N + i] & nmask;
+      anc_q[qb] = (a.parents ? built : a.anc[(size_t)u.b * N + i]) & nmask;
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) qf[qb][ks] = bf16x8{};
@@ -450,10 +479,23 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   uint64_t anc_q[QBW];
   if (tree_wave) {
     const uint64_t nmask = a.N == 64 ? ~0ull : (1ull << a.N) - 1ull;
+    if (a.parents) {
+      // masks built here from the parent links (lane = node); the tree wave
+      // of KV head 0 also writes the builder's outputs
+      const TreeLinks t = tree_links_wave(a.parents + (size_t)b * a.N, a.N);
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      const int row = qb * 16 + c;
-      anc_q[qb] = row < a.M ? a.anc[(size_t)b * a.N + row / a.G] & nmask : 0ull;
+      for (int qb = 0; qb < QBW; ++qb) {
+        const int row = qb * 16 + c;
+        const uint64_t m = __shfl(t.anc, row < a.M ? row / a.G : 0);
+        anc_q[qb] = row < a.M ? m & nmask : 0ull;
+      }
+      if (kvh == 0) write_tree_outputs(a, b, t);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) {
+        const int row = qb * 16 + c;
+        anc_q[qb] = row < a.M ? a.anc[(size_t)b * a.N + row / a.G] & nmask : 0ull;
+      }
     }
   }
   const int rows = min(RW, a.M);
@@ -987,6 +1029,8 @@ size_t tree_attn_workspace_bytes(const AttnPlan& p) {
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_len, const uint64_t* anc,
+                            const int32_t* parents, uint64_t* anc_out, int32_t* depth_out,
+                            int32_t* pos_out,
                             int B, int N, int Hq, int Hkv, int Lmax, float scale_log2,
                             uint16_t* out, void* ws, int32_t* flags, hipStream_t s) {
   AttnArgs a{};
@@ -995,6 +1039,10 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.v = v;
   a.kv_len = kv_len;
   a.anc = anc;
+  a.parents = anc ? nullptr : parents;
+  a.anc_out = anc_out;
+  a.depth_out = depth_out;
+  a.pos_out = pos_out;
   a.out = out;
   const bool ring = plan.variant <= 1;
   uint8_t* w = static_cast<uint8_t*>(ws);

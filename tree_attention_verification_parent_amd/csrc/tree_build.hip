@@ -2,9 +2,8 @@
 //
 // Each drafted node attends to its own ancestors (EAGLE, paperlayer.ai
 // summary, §3 EAGLE: tree attention; A.1 Tree Structure).  One wavefront per
-// sequence, lane i owning node i (N <= 64).  Ancestor sets come from pointer
-// jumping over the parent links: after r rounds a lane has OR-ed in the masks
-// of its 2^r nearest ancestors, so 6 rounds cover any depth below 64.
+// sequence, lane i owning node i (N <= 64); the ancestor sets come from
+// pointer jumping over the parent links (tree_links_wave).
 #include "common.h"
 #include "launch.h"
 
@@ -18,41 +17,16 @@ __global__ __launch_bounds__(256) void tree_build_kernel(
   const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (b >= B) return;  // uniform per wavefront
   const bool live = lane < N;
-  // both loads first: the position ids need the committed length
+  // issued before the parent links: the position ids need the committed length
   const int L = pos && live ? kv_len[b] : 0;
-  int par = live ? parents[(size_t)b * N + lane] : -1;
-  bool bad = false;
-  if (live) {
-    if (lane == 0) {
-      bad = par != -1;
-      par = -1;
-    } else if (par < 0 || par >= lane) {
-      bad = true;
-      par = 0;  // a malformed link hangs off the root, keeping the mask in range
-    }
-  }
-  uint64_t a = live ? (1ull << lane) : 0ull;
-  int cnt = par >= 0 ? 1 : 0;
-  int jump = par;
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const int src = jump >= 0 ? jump : lane;
-    const uint64_t a_j = __shfl(a, src);
-    const int cnt_j = __shfl(cnt, src);
-    const int jump_j = __shfl(jump, src);
-    if (jump >= 0) {
-      a |= a_j;
-      cnt += cnt_j;
-      jump = jump_j;
-    }
-  }
+  const TreeLinks t = tree_links_wave(parents + (size_t)b * N, N);
   if (live) {
     const size_t o = (size_t)b * N + lane;
-    anc[o] = a;
-    if (depth) depth[o] = cnt;
-    if (pos) pos[o] = L + cnt;
+    anc[o] = t.anc;
+    if (depth) depth[o] = t.depth;
+    if (pos) pos[o] = L + t.depth;
   }
-  const uint64_t any_bad = __ballot(bad);
+  const uint64_t any_bad = __ballot(t.bad);
   if (flags && any_bad && lane == 0) atomicOr(flags + b, EAGLE_FLAG_BAD_PARENT);
 }
 
