@@ -145,6 +145,50 @@ def test_attention_full_configs_sampled(idx):
     assert err < ATOL_ATTN
 
 
+@pytest.mark.parametrize("variant", ["1", "4", "5"])
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_kernel_variants(case, variant, monkeypatch):
+    """Each kernel forced on every case: ring with one query group per KV head
+    (1), shared-tile (4), ring with query groups on one XCD (5); the ring
+    variants split G*N > 32 rows into query groups and take up to two chunks
+    of tree keys (N <= 64)."""
+    name, B, N, Hq, Hkv, d, kv_lens = case
+    monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
+    cfg = W.shrink(W.get(0), B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
+    rng = np.random.default_rng(len(name) + 7)
+    parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(B)])
+    s = W.make_step(cfg, 1.0, seed=zlib.crc32(name.encode()) % 1000 + 3, kv_lens=kv_lens,
+                    parents=parents)
+    say(f"attention {name} variant {variant}")
+    got = _fused_vs_two_calls(s)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
+@pytest.mark.parametrize("variant", ["4", "5"])
+@pytest.mark.parametrize("idx", [3, 4])
+def test_attention_gqa_full_configs_variants(idx, variant, monkeypatch):
+    """The grouped-query configurations at full size through both GQA kernels:
+    sampled rows against the oracle, every output finite."""
+    monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
+    cfg = W.get(idx)
+    s = W.make_step(cfg, cfg.temperatures[-1])
+    say(f"attention full config {cfg.name} variant {variant}")
+    got, _, _, _ = run_attention(s)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(idx + 50)
+    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.N)), int(rng.integers(cfg.Hq)))
+            for _ in range(32)]
+    rows += [(cfg.B - 1, cfg.N - 1, cfg.Hq - 1), (0, cfg.N - 1, 0)]
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, rows=rows)
+    sub = np.stack([got[b, i, h] for b, i, h in rows])
+    err = np.abs(sub - ref).max()
+    say(f"  sampled max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
 def test_attention_deterministic():
     cfg = W.get(1)
     s = W.make_step(cfg, 1.0)

@@ -325,15 +325,33 @@ __device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_ru
 // The split ranges are laid over the cache capacity Lmax - N, not over
 // kv_len, so the first loads go out before anything else is read; keys at or
 // past kv_len are masked.  The tree keys (each query's ancestors and itself,
-// N <= 32 of them) are one more chunk, masked by the ancestor bits, for one
-// wave of the last split.
+// N <= 64 of them) are one or two more chunks, masked by the ancestor bits,
+// for one wave of the last split.
+//
+// A workgroup holds RW query rows.  With more rows per KV head (grouped-query
+// attention, G*N > RW) the rows are cut into query groups, each a unit of its
+// own that streams the same K/V; those units sit on one XCD so that the
+// repeats come from its L2, and their loads use the default cache policy
+// instead of the non-temporal one.
 constexpr int kRingThreads = 64 * 8;
 constexpr int kNonTemporal = 2;  // cache-policy bits of a load: nt
 
-template <int D_, int QBW_>
+// One lane's 16-byte direct-to-LDS load; the cache policy is a literal in
+// each branch (a template-dependent policy argument made hipcc drop the
+// kernel instantiations without a diagnostic).
+template <int POLICY>
+__device__ __forceinline__ void load_lds16(const uint16_t* src, uint8_t* dst) {
+  if constexpr (POLICY == kNonTemporal)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, kNonTemporal);
+  else
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+template <int D_, int QBW_, int POLICY_ = kNonTemporal>
 struct RingShape {
   static constexpr int D = D_;
   static constexpr int QBW = QBW_;
+  static constexpr int POLICY = POLICY_;  // cache-policy bits of the K/V loads
   static constexpr int NWAVE = 8;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int MAT_BYTES = 32 * D * 2;    // K (or V) of one 32-key chunk
@@ -422,8 +440,16 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   const int split = slotw % a.splits;
   const int unit = (slotw / a.splits) * kNumXCDs + xcd;
   if (unit >= a.units) return;
-  const int kvh = unit % a.Hkv;  // qgroups == 1 for ring variants
-  const int b = unit / a.Hkv;
+  // unit -> (pair = b * Hkv + kvh, query group of RW rows).  The query groups
+  // of a pair are consecutive units of one XCD, so they are resident together
+  // and stream the same K/V through that XCD's L2 (read from HBM about once).
+  const int ux = unit / kNumXCDs;
+  const int qgroup = ux % a.qgroups;
+  const int pair = (ux / a.qgroups) * kNumXCDs + xcd;
+  if (pair >= a.B * a.Hkv) return;
+  const int kvh = pair % a.Hkv;
+  const int b = pair / a.Hkv;
+  const int row0 = qgroup * RW;  // first query row (of the pair's G*N) of this unit
 
   // this split's chunks of the capacity prefix; wave w takes cb + w, cb + w + NWAVE, ...
   const int Lp = a.Lmax - a.N;
@@ -451,20 +477,20 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)(slot + t * RPL * D * 2), 16, 0, kNonTemporal);
+      load_lds16<S::POLICY>(kp + off, slot + t * RPL * D * 2);
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
-      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(slot + S::MAT_BYTES + t * RPL * D * 2), 16, 0, kNonTemporal);
+      load_lds16<S::POLICY>(vp + off, slot + S::MAT_BYTES + t * RPL * D * 2);
     }
   };
   auto issue = [&](int gc) { issue_keys(gc * 32, Lp - 1); };
   if (my_n > 0) issue(my_first);
-  // The tree keys [L, L + N) (N <= 32 here) are one more masked chunk, taken
-  // by the wave of the last split with the fewest prefix chunks.
+  // The tree keys [L, L + N) are one or two more masked chunks (N <= 64),
+  // taken by the wave of the last split with the fewest prefix chunks.
   const bool tree_wave = split == a.splits - 1 && wave == (ce - cb) % NWAVE;
 
   // committed length, then the queries (needed only once the first chunk is in)
@@ -472,7 +498,8 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   const bool bad = L < 0 || L > Lp;
   if (bad) {
     L = 0;
-    if (a.flags && split == 0 && kvh == 0 && tid == 0) atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+    if (a.flags && split == 0 && kvh == 0 && qgroup == 0 && tid == 0)
+      atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
   }
   if (tree_wave && my_n == 0) issue_keys(L, L + a.N - 1);
   // the tree wave's rows' ancestor masks: bit t of anc[row] admits key L + t
@@ -485,24 +512,24 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       const TreeLinks t = tree_links_wave(a.parents + (size_t)b * a.N, a.N);
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
-        const int row = qb * 16 + c;
+        const int row = row0 + qb * 16 + c;
         const uint64_t m = __shfl(t.anc, row < a.M ? row / a.G : 0);
         anc_q[qb] = row < a.M ? m & nmask : 0ull;
       }
-      if (kvh == 0) write_tree_outputs(a, b, t);
+      if (kvh == 0 && qgroup == 0) write_tree_outputs(a, b, t);
     } else {
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
-        const int row = qb * 16 + c;
+        const int row = row0 + qb * 16 + c;
         anc_q[qb] = row < a.M ? a.anc[(size_t)b * a.N + row / a.G] & nmask : 0ull;
       }
     }
   }
-  const int rows = min(RW, a.M);
+  const int rows = min(RW, a.M - row0);
   bf16x8 qf[QBW][NKS];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    const int row = qb * 16 + c;
+    const int row = row0 + qb * 16 + c;
     if (row < a.M) {
       const int i = row / a.G;
       const int h = kvh * a.G + (row - i * a.G);
@@ -526,9 +553,10 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int my_chunks = my_n + (tree_wave ? 1 : 0);
+  const int my_chunks = my_n + (tree_wave ? (a.N + 31) / 32 : 0);
   for (int i = 0; i < my_chunks; ++i) {
-    const bool tree_chunk = i == my_n;
+    const bool tree_chunk = i >= my_n;
+    const int tree_bit0 = 32 * (i - my_n);  // anc bit of the tree chunk's first key
     const int gc = my_first + NWAVE * i;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
     const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
@@ -560,7 +588,8 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = sc[qb][j >> 2][j & 3] * a.scale_log2;
       if (need_mask) {
-        const uint32_t ok = tree_chunk ? (uint32_t)(anc_q[qb] >> (8 * g)) & 0xffu : ok_prefix;
+        const uint32_t ok =
+            tree_chunk ? (uint32_t)(anc_q[qb] >> (tree_bit0 + 8 * g)) & 0xffu : ok_prefix;
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
       }
@@ -590,7 +619,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       if (i + 1 < my_n)
         issue(gc + NWAVE);
       else
-        issue_keys(L, L + a.N - 1);
+        issue_keys(L + 32 * (i + 1 - my_n), L + a.N - 1);
     }
   }
 
@@ -607,8 +636,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   constexpr int SD = D + 4;
   constexpr int D4 = D / 4;
   auto out_row = [&](int rl) {
-    const int i = rl / a.G;
-    const int h = kvh * a.G + (rl - i * a.G);
+    const int row = row0 + rl;
+    const int i = row / a.G;
+    const int h = kvh * a.G + (row - i * a.G);
     return a.out + (((size_t)b * a.N + i) * a.Hq + h) * D;
   };
   if (a.splits == 1) {
@@ -949,6 +979,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW
 // ---- variants ----------------------------------------------------------------
 // 0: ring, 1 query block      1: ring, 2 query blocks
 // 2: tile, 4 blocks (2x2)     3: tile, 8 blocks (4 query waves)   4: tile, 16 blocks
+// 5: ring, 2 query blocks per query group, default cache policy (grouped queries)
 struct VariantInfo {
   int rw;
   int keys_per_piece;  // split granularity in keys
@@ -960,22 +991,27 @@ static VariantInfo variant_info(int variant) {
     case 1: return {32, 32};
     case 2: return {64, 64};
     case 3: return {128, 64};
+    case 5: return {32, 32};
     default: return {256, 64};
   }
 }
 
 template <int D>
 static void* variant_kernel(int variant) {
-  static_assert(RingShape<D, 1>::THREADS == kRingThreads && RingShape<D, 2>::THREADS == kRingThreads,
+  static_assert(RingShape<D, 1>::THREADS == kRingThreads && RingShape<D, 2>::THREADS == kRingThreads &&
+                    RingShape<D, 2, 0>::THREADS == kRingThreads,
                 "ring launch size");
   switch (variant) {
     case 0: return (void*)tree_attn_ring_kernel<RingShape<D, 1>>;
     case 1: return (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
     case 2: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 2, 1>>;
     case 3: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 4, 2>>;
+    case 5: return (void*)tree_attn_ring_kernel<RingShape<D, 2, 0>>;
     default: return (void*)tree_attn_tile_kernel<TileShape<D, 4, 4, 2>>;
   }
 }
+
+static bool is_ring(int variant) { return variant <= 1 || variant == 5; }
 
 static int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
@@ -989,15 +1025,28 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   p.G = Hq / Hkv;
   p.M = p.G * N;
   const int nqb = (p.M + 15) / 16;
+  const int pairs = B * Hkv;
   int variant = nqb <= 1 ? 0 : nqb <= 2 ? 1 : nqb <= 4 ? 2 : nqb <= 8 ? 3 : 4;
+  // Grouped queries: ring workgroups per query group of 32 rows when the
+  // XCD-padded units fit in two rounds of one workgroup per CU (llama2-70b
+  // shape: 448 units, 79 us against 85 us for the tile kernel); beyond that
+  // the shared-tile kernel (mixtral shape: 1024 units, 250 us against 266 us).
+  if (variant >= 2) {
+    const int ring_units = ((pairs + kNumXCDs - 1) / kNumXCDs) * kNumXCDs * ((p.M + 31) / 32);
+    if (ring_units <= 2 * kNumCUs) variant = 5;
+  }
   variant = env_int("EAGLE_ATTN_VARIANT", variant);
-  if (variant < 0 || variant > 4) variant = 4;
+  if (variant < 0 || variant > 5) variant = 4;
   const VariantInfo vi = variant_info(variant);
   p.variant = variant;
   p.rows_per_wg = vi.rw;
   p.kt = vi.keys_per_piece;
   p.qgroups = (p.M + vi.rw - 1) / vi.rw;
-  p.units = B * Hkv * p.qgroups;
+  // ring variants: the query groups of a (b, kv head) pair are consecutive
+  // units of the pair's XCD (pair mod 8), so the pairs are padded to a
+  // multiple of 8 and the padding units exit at once
+  p.units = is_ring(variant) ? ((pairs + kNumXCDs - 1) / kNumXCDs) * kNumXCDs * p.qgroups
+                             : pairs * p.qgroups;
   const int pieces = (Lmax + vi.keys_per_piece - 1) / vi.keys_per_piece;
   const int padded_units = ((p.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
   // Aim for one workgroup per CU: a ring workgroup keeps up to eight 32-key
@@ -1005,6 +1054,24 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   // merge, whose cost grows with splits x query rows.
   const int target = kNumCUs;
   int splits = (target + padded_units - 1) / padded_units;
+  if (is_ring(variant) && p.qgroups == 1) {
+    // One ring workgroup per CU (its LDS): workgroups beyond kNumCUs run in
+    // another round, so a half-empty last round costs as much as a full one.
+    // Pick the split count s minimising rounds(s) * chunks per split plus a
+    // merge cost of 1.75 chunk-times per split (fitted on MI355X: llama2-7b
+    // 6 splits, 14.9 us against 16.0 us at 8; llama2-13b 3 splits, 64 us
+    // against 85 us at 2).
+    const int n_chunks = (Lmax - N + 31) / 32;
+    float best = 0.f;
+    for (int sc = 1; sc <= 16 && sc <= n_chunks; ++sc) {
+      const int rounds = (padded_units * sc + kNumCUs - 1) / kNumCUs;
+      const float cost = (float)(rounds * ((n_chunks + sc - 1) / sc)) + 1.75f * sc;
+      if (sc == 1 || cost < best) {
+        best = cost;
+        splits = sc;
+      }
+    }
+  }
   splits = env_int("EAGLE_ATTN_SPLITS", splits);
   if (splits > pieces) splits = pieces;
   if (splits > 64) splits = 64;  // the merge keeps one split weight per lane
@@ -1017,7 +1084,7 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: [unit tickets (ring variants) | split log2-sum-exp | split O].
 static size_t ticket_bytes(const AttnPlan& p) {
-  return p.variant <= 1 && p.splits > 1 ? align256((size_t)p.units * 4) : 0;
+  return is_ring(p.variant) && p.splits > 1 ? align256((size_t)p.units * 4) : 0;
 }
 
 size_t tree_attn_workspace_bytes(const AttnPlan& p) {
@@ -1044,7 +1111,7 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.depth_out = depth_out;
   a.pos_out = pos_out;
   a.out = out;
-  const bool ring = plan.variant <= 1;
+  const bool ring = is_ring(plan.variant);
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t tk = ticket_bytes(plan);
   const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
