@@ -145,13 +145,14 @@ def test_attention_full_configs_sampled(idx):
     assert err < ATOL_ATTN
 
 
-@pytest.mark.parametrize("variant", ["1", "4", "5"])
+@pytest.mark.parametrize("variant", ["1", "4", "5", "6"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
 def test_attention_kernel_variants(case, variant, monkeypatch):
     """Each kernel forced on every case: ring with one query group per KV head
-    (1), shared-tile (4), ring with query groups on one XCD (5); the ring
-    variants split G*N > 32 rows into query groups and take up to two chunks
-    of tree keys (N <= 64)."""
+    (1), shared-tile (4), ring with query groups on one XCD (5), group kernel
+    with 256 rows sharing a ring of 64-key tiles (6); the ring variants split
+    G*N > 32 rows into query groups, and every kernel takes up to 64 tree
+    keys."""
     name, B, N, Hq, Hkv, d, kv_lens = case
     monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
     cfg = W.shrink(W.get(0), B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
@@ -167,10 +168,10 @@ def test_attention_kernel_variants(case, variant, monkeypatch):
     assert err < ATOL_ATTN
 
 
-@pytest.mark.parametrize("variant", ["4", "5"])
+@pytest.mark.parametrize("variant", ["4", "5", "6"])
 @pytest.mark.parametrize("idx", [3, 4])
 def test_attention_gqa_full_configs_variants(idx, variant, monkeypatch):
-    """The grouped-query configurations at full size through both GQA kernels:
+    """The grouped-query configurations at full size through each GQA kernel:
     sampled rows against the oracle, every output finite."""
     monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
     cfg = W.get(idx)

@@ -427,6 +427,74 @@ __device__ __forceinline__ uint32_t prefix_mask8(int key0, int L) {
   return below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
 }
 
+// One 32-key chunk in LDS (K then V, 32 rows of D bf16 each, 16-byte slots
+// of row r permuted by swz(r)) against QBW query blocks of 16 rows:
+// S^T = K Q^T on the MFMA, the tree or prefix mask, the online softmax, and
+// O^T += V^T P^T with V^T fragments from transposed LDS reads.  A tree chunk
+// admits key 8g + j of the lane's column when ancestor bit tree_bit0 + 8g + j
+// of its row's node is set; a prefix chunk by the 8-bit ok_prefix.
+template <int D, int QBW>
+__device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&qf)[QBW][D / 32],
+                                           const uint64_t (&anc_q)[QBW], f32x4 (&acc)[QBW][D / 16],
+                                           float (&m_run)[QBW], float (&l_run)[QBW],
+                                           float scale_log2, bool need_mask, bool tree_chunk,
+                                           int tree_bit0, uint32_t ok_prefix) {
+  constexpr int NKS = D / 32, NDB = D / 16, MAT_BYTES = 32 * D * 2;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
+  const uint8_t* Vb = slot + MAT_BYTES;
+
+  f32x4 sc[QBW][2];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) sc[qb][0] = sc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int hlf = 0; hlf < 2; ++hlf) {
+    // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
+    const int kr = 8 * (c >> 2) + 4 * hlf + (c & 3);
+    const int sw = swz(kr);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kc + kr * D + (((ks * 4 + g) ^ sw) * 8));
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb)
+        sc[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[qb][hlf], 0, 0, 0);
+    }
+  }
+  bf16x8 pf[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = sc[qb][j >> 2][j & 3] * scale_log2;
+    if (need_mask) {
+      const uint32_t ok =
+          tree_chunk ? (uint32_t)(anc_q[qb] >> (tree_bit0 + 8 * g)) & 0xffu : ok_prefix;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
+    }
+    pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
+  }
+  // V^T fragments by transposed LDS reads: lane (g, c) gets V[8g + j][16db + c],
+  // j = 0..7, as two 4-element halves.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    short4_t h2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int vr = 8 * g + 4 * h + (c >> 2);
+      const int ps = (2 * db + ((c & 3) >> 1)) ^ swz(vr);
+      const uint8_t* src = Vb + vr * D * 2 + ps * 16 + (c & 1) * 8;
+      h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(src));
+    }
+    const bf16x8 vf =
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb)
+      acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
+  }
+}
+
 template <class S>
 __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) {
   constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NKS = S::NKS, NDB = S::NDB;
@@ -559,61 +627,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     const int tree_bit0 = 32 * (i - my_n);  // anc bit of the tree chunk's first key
     const int gc = my_first + NWAVE * i;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
-    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
-    const uint8_t* Vb = slot + S::MAT_BYTES;
-
-    f32x4 sc[QBW][2];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) sc[qb][0] = sc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
-      const int kr = 8 * (c >> 2) + 4 * hlf + (c & 3);
-      const int sw = swz(kr);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kc + kr * D + (((ks * 4 + g) ^ sw) * 8));
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb)
-          sc[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[qb][hlf], 0, 0, 0);
-      }
-    }
-    const int key0 = gc * 32 + 8 * g;
     const bool need_mask = tree_chunk || gc * 32 + 32 > L;
-    const uint32_t ok_prefix = prefix_mask8(key0, L);
-    bf16x8 pf[QBW];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = sc[qb][j >> 2][j & 3] * a.scale_log2;
-      if (need_mask) {
-        const uint32_t ok =
-            tree_chunk ? (uint32_t)(anc_q[qb] >> (tree_bit0 + 8 * g)) & 0xffu : ok_prefix;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
-      }
-      pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
-    }
-    // V^T fragments by transposed LDS reads: lane (g, c) gets V[8g + j][16db + c],
-    // j = 0..7, as two 4-element halves.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      short4_t h2[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int vr = 8 * g + 4 * h + (c >> 2);
-        const int ps = (2 * db + ((c & 3) >> 1)) ^ swz(vr);
-        const uint8_t* src = Vb + vr * D * 2 + ps * 16 + (c & 1) * 8;
-        h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(src));
-      }
-      const bf16x8 vf =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb)
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
-    }
+    chunk_step<D, QBW>(slot, qf, anc_q, acc, m_run, l_run, a.scale_log2, need_mask, tree_chunk,
+                       tree_bit0, prefix_mask8(gc * 32 + 8 * g, L));
     if (i + 1 < my_chunks) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
       if (i + 1 < my_n)
@@ -919,6 +935,211 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
 }
 
 // ============================================================================
+// group kernel: a head group's query rows share a ring of K/V tiles in LDS
+// ============================================================================
+// Grouped-query attention with up to 256 query rows per (b, KV head): eight
+// waves, each owning 32 of the rows, compute every 64-key tile of the split
+// against their own rows, so a tile is read from HBM once for the whole
+// head group and no wave has to merge with another.  The tiles stream
+// through NBUF LDS buffers, NBUF - 1 of them in flight while one is
+// computed; each wave issues a quarter of every tile's direct-to-LDS loads.
+// Those loads are inline assembly: the compiler treats a direct-to-LDS load
+// of its own as a pending LDS write that every later LDS read waits for,
+// which would drain all buffers before each tile.  Their completion is
+// tracked here instead: before tile i a wave waits until at most its own
+// loads of the tiles after i are outstanding (vector loads complete in
+// order), and one LDS-only barrier then makes tile i whole for all waves and
+// frees the buffer of tile i - 1 for tile i + NBUF - 1.  The last split
+// also computes the tree keys [L, L + N) as one more tile.  Rows O / l and
+// log2-sum-exp of a split go straight from registers to the partials (the
+// merge kernel combines splits), or the bf16 rows to the output.
+template <int D_>
+struct GroupShape {
+  static constexpr int D = D_;
+  static constexpr int QBW = 2;                        // 16-row query blocks per wave
+  static constexpr int NWAVE = 8;
+  static constexpr int THREADS = 64 * NWAVE;
+  static constexpr int RW = 16 * QBW * NWAVE;          // 256 query rows per workgroup
+  static constexpr int MAT_BYTES = 32 * D * 2;         // K (or V) of a 32-key chunk
+  static constexpr int SLOT_BYTES = 2 * MAT_BYTES;
+  static constexpr int TILE_KEYS = 64;
+  static constexpr int TILE_BYTES = 2 * SLOT_BYTES;    // two chunks
+  static constexpr int NBUF = 4;
+  static constexpr int SPR = D / 8;                    // 16-byte slots per key row
+  static constexpr int RPL = 64 / SPR;                 // key rows per wave-wide load
+  static constexpr int LPM = 32 / RPL;                 // wave-wide loads per matrix
+  static constexpr int LPW = 2 * 2 * LPM / NWAVE;      // loads per wave per tile
+  static constexpr int LDS_BYTES = NBUF * TILE_BYTES;
+  static_assert(LPW * NWAVE == 4 * LPM, "a tile's loads split evenly over the waves");
+};
+
+// One lane's 16 bytes of global memory into LDS at lds_addr + 16 * lane (lds_addr
+// wave-uniform), issued as inline assembly (M0 saved and restored around it).
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(src)
+      : "memory");
+}
+
+// Waits until at most n of this wave's vector loads are outstanding.
+template <int LPW>
+__device__ __forceinline__ void wait_tiles_after(int tiles_after) {
+  if (tiles_after <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (tiles_after == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+}
+
+template <class S>
+__global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a) {
+  constexpr int D = S::D, QBW = S::QBW, RW = S::RW, NBUF = S::NBUF, LPW = S::LPW;
+  constexpr int SPR = S::SPR, RPL = S::RPL, LPM = S::LPM, NKS = D / 32, NDB = D / 16;
+  static_assert(NBUF == 4, "wait_tiles_after covers up to NBUF - 2 = 2 tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  // workgroup -> (unit, split) as for the shared-tile kernel: the splits of a
+  // unit share an XCD; unit = pair * qgroups + qgroup
+  UnitCtx u;
+  {
+    const int xcd = blockIdx.x % kNumXCDs, slotw = blockIdx.x / kNumXCDs;
+    u.split = slotw % a.splits;
+    u.unit = (slotw / a.splits) * kNumXCDs + xcd;
+    if (u.unit >= a.units) return;
+    u.qgroup = u.unit % a.qgroups;
+    u.pair = u.unit / a.qgroups;
+    u.kvh = u.pair % a.Hkv;
+    u.b = u.pair / a.Hkv;
+  }
+  const int r0 = wave * QBW * 16;                  // this wave's first row in the unit
+  const bool active = u.qgroup * RW + r0 < a.M;   // wave-uniform: the wave has rows
+
+  // this split's 64-key tiles of the capacity prefix; the last split adds the tree tile
+  const int Lp = a.Lmax - a.N;
+  const int n_tiles = (Lp + S::TILE_KEYS - 1) / S::TILE_KEYS;
+  const int tb = (int)((long long)u.split * n_tiles / a.splits);
+  const int te = (int)((long long)(u.split + 1) * n_tiles / a.splits);
+  const int n_pre = te - tb;
+  const bool tree_split = u.split == a.splits - 1;
+  const int n_my = n_pre + (tree_split ? 1 : 0);
+
+  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
+  const uint16_t* kp = a.k + kv_base;
+  const uint16_t* vp = a.v + kv_base;
+  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  const int r_in = lane / SPR, p_in = lane % SPR;
+  // tile position j: keys key0.. (chunk h at key0 + 32 h), rows past key_max re-read it
+  auto issue_tile = [&](int j, int key0, int key_max) {
+#pragma unroll
+    for (int e = 0; e < LPW; ++e) {
+      const int li = wave * LPW + e;
+      const int ch = li / (2 * LPM), mat = (li / LPM) & 1, t = li % LPM;
+      const int r = t * RPL + r_in;
+      const int key = min(key0 + ch * 32 + r, key_max);
+      const uint16_t* src = (mat ? vp : kp) + (size_t)key * D + (p_in ^ swz(r)) * 8;
+      const uint32_t dst = lds_base + (uint32_t)((j % NBUF) * S::TILE_BYTES + ch * S::SLOT_BYTES +
+                                                 mat * S::MAT_BYTES + t * RPL * D * 2);
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+  int L = 0;
+  auto issue = [&](int j) {
+    if (j < n_pre)
+      issue_tile(j, (tb + j) * S::TILE_KEYS, Lp - 1);
+    else
+      issue_tile(j, L, L + a.N - 1);  // the tree tile
+  };
+  // prefix tiles go out first; the tree tile needs kv_len
+  const int n_pro = min(NBUF - 1, n_my);
+  for (int j = 0; j < min(n_pro, n_pre); ++j) issue(j);
+  L = a.kv_len[u.b];
+  u.bad = L < 0 || L > Lp;
+  if (u.bad) {
+    L = 0;
+    if (a.flags && u.split == 0 && u.qgroup == 0 && u.kvh == 0 && tid == 0)
+      atomicOr(a.flags + u.b, EAGLE_FLAG_BAD_KV_LEN);
+  }
+  u.L = L;
+  u.total = L + a.N;
+  for (int j = n_pre; j < n_pro; ++j) issue(j);
+
+  bf16x8 qf[QBW][NKS];
+  uint64_t anc_q[QBW];
+  if (active) load_queries<D, QBW, RW>(a, u, r0, qf, anc_q);
+
+  f32x4 acc[QBW][NDB];
+  float m_run[QBW], l_run[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int i = 0; i < n_my; ++i) {
+    wait_tiles_after<LPW>(min(NBUF - 2, n_my - 1 - i));
+    barrier_lds();  // tile i is whole; every wave is done with tile i - 1
+    if (i + NBUF - 1 < n_my) issue(i + NBUF - 1);
+    if (!active) continue;
+    const uint8_t* tile = lds + (i % NBUF) * S::TILE_BYTES;
+    if (i < n_pre) {
+      const int key0 = (tb + i) * S::TILE_KEYS;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k0 = key0 + 32 * h;
+        chunk_step<D, QBW>(tile + h * S::SLOT_BYTES, qf, anc_q, acc, m_run, l_run, a.scale_log2,
+                           k0 + 32 > L, false, 0, prefix_mask8(k0 + 8 * g, L));
+      }
+    } else {
+      for (int h = 0; h < 2 && 32 * h < a.N; ++h)
+        chunk_step<D, QBW>(tile + h * S::SLOT_BYTES, qf, anc_q, acc, m_run, l_run, a.scale_log2,
+                           true, true, 32 * h, 0u);
+    }
+  }
+  if (!active) return;
+
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    l_run[qb] += __shfl_xor(l_run[qb], 16);
+    l_run[qb] += __shfl_xor(l_run[qb], 32);
+  }
+  const size_t pbase = ((size_t)u.unit * a.splits + u.split) * RW;
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int rl = r0 + qb * 16 + c;
+    const int row = u.qgroup * RW + rl;
+    if (row >= a.M) continue;
+    if (a.splits == 1) {
+      const int i = row / a.G;
+      const int h = u.kvh * a.G + (row - i * a.G);
+      uint16_t* orow = a.out + (((size_t)u.b * a.N + i) * a.Hq + h) * D;
+      const float inv = (u.bad || l_run[qb] == 0.f) ? 0.f : 1.f / l_run[qb];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const f32x4 o = acc[qb][db] * inv;
+        *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * g) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    } else {
+      const float inv = l_run[qb] == 0.f ? 0.f : 1.f / l_run[qb];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + db * 16 + 4 * g) = acc[qb][db] * inv;
+      if (g == 0)
+        a.part_lse[pbase + rl] = l_run[qb] == 0.f ? -INFINITY : m_run[qb] + __log2f(l_run[qb]);
+    }
+  }
+}
+
+// ============================================================================
 // merge (tile variants): one wave per query row combines the splits' partials
 // ============================================================================
 template <int D>
@@ -980,6 +1201,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW
 // 0: ring, 1 query block      1: ring, 2 query blocks
 // 2: tile, 4 blocks (2x2)     3: tile, 8 blocks (4 query waves)   4: tile, 16 blocks
 // 5: ring, 2 query blocks per query group, default cache policy (grouped queries)
+// 6: group kernel, 256 rows per workgroup sharing a ring of 64-key tiles
 struct VariantInfo {
   int rw;
   int keys_per_piece;  // split granularity in keys
@@ -992,6 +1214,7 @@ static VariantInfo variant_info(int variant) {
     case 2: return {64, 64};
     case 3: return {128, 64};
     case 5: return {32, 32};
+    case 6: return {256, 64};
     default: return {256, 64};
   }
 }
@@ -1007,6 +1230,7 @@ static void* variant_kernel(int variant) {
     case 2: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 2, 1>>;
     case 3: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 4, 2>>;
     case 5: return (void*)tree_attn_ring_kernel<RingShape<D, 2, 0>>;
+    case 6: return (void*)tree_attn_group_kernel<GroupShape<D>>;
     default: return (void*)tree_attn_tile_kernel<TileShape<D, 4, 4, 2>>;
   }
 }
@@ -1027,16 +1251,13 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   const int nqb = (p.M + 15) / 16;
   const int pairs = B * Hkv;
   int variant = nqb <= 1 ? 0 : nqb <= 2 ? 1 : nqb <= 4 ? 2 : nqb <= 8 ? 3 : 4;
-  // Grouped queries: ring workgroups per query group of 32 rows when the
-  // XCD-padded units fit in two rounds of one workgroup per CU (llama2-70b
-  // shape: 448 units, 79 us against 85 us for the tile kernel); beyond that
-  // the shared-tile kernel (mixtral shape: 1024 units, 250 us against 266 us).
-  if (variant >= 2) {
-    const int ring_units = ((pairs + kNumXCDs - 1) / kNumXCDs) * kNumXCDs * ((p.M + 31) / 32);
-    if (ring_units <= 2 * kNumCUs) variant = 5;
-  }
+  // Grouped queries: the group kernel, whose 256 rows per workgroup share a
+  // ring of K/V tiles (measured on MI355X: llama2-70b shape 67 us against 79
+  // for ring query groups and 85 for the shared-tile kernel; mixtral shape
+  // 206 us against 266 and 249).
+  if (variant >= 2) variant = 6;
   variant = env_int("EAGLE_ATTN_VARIANT", variant);
-  if (variant < 0 || variant > 5) variant = 4;
+  if (variant < 0 || variant > 6) variant = 4;
   const VariantInfo vi = variant_info(variant);
   p.variant = variant;
   p.rows_per_wg = vi.rw;
@@ -1134,7 +1355,8 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   const dim3 grid((unsigned)(padded_units * plan.splits));
   void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
   void* args[] = {&a};
-  hipError_t err = hipLaunchKernel(fn, grid, dim3(ring ? kRingThreads : 256), args, 0, s);
+  const int threads = ring ? kRingThreads : plan.variant == 6 ? GroupShape<128>::THREADS : 256;
+  hipError_t err = hipLaunchKernel(fn, grid, dim3(threads), args, 0, s);
   // ring variants combine their splits in the kernel
   if (err != hipSuccess || plan.splits == 1 || ring) return err;
   const int rw = plan.rows_per_wg;
