@@ -427,24 +427,22 @@ __device__ __forceinline__ uint32_t prefix_mask8(int key0, int L) {
   return below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
 }
 
-// One 32-key chunk in LDS (K then V, 32 rows of D bf16 each, 16-byte slots
-// of row r permuted by swz(r)) against QBW query blocks of 16 rows:
-// S^T = K Q^T on the MFMA, the tree or prefix mask, the online softmax, and
-// O^T += V^T P^T with V^T fragments from transposed LDS reads.  A tree chunk
-// admits key 8g + j of the lane's column when ancestor bit tree_bit0 + 8g + j
-// of its row's node is set; a prefix chunk by the 8-bit ok_prefix.
+// One 32-key chunk in LDS: K then V, 32 rows of D bf16 each, the 16-byte
+// slots of row r permuted by swz(r).  The chunk is computed in three parts
+// (so that a caller can overlap one chunk's softmax with another's MFMAs):
+//   chunk_qk:   S^T = K Q^T for QBW 16-row query blocks (keys on MFMA rows,
+//               permuted so lane (g, c) holds keys 8g..8g+7 of column c);
+//   chunk_soft: the tree or prefix mask and the online softmax, giving the
+//               bf16 P^T fragments (a tree chunk admits key 8g + j of the
+//               lane's column when ancestor bit tree_bit0 + 8g + j of its
+//               row's node is set, a prefix chunk by the 8-bit ok_prefix);
+//   chunk_pv:   O^T += V^T P^T with V^T fragments from transposed LDS reads.
 template <int D, int QBW>
-__device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&qf)[QBW][D / 32],
-                                           const uint64_t (&anc_q)[QBW], f32x4 (&acc)[QBW][D / 16],
-                                           float (&m_run)[QBW], float (&l_run)[QBW],
-                                           float scale_log2, bool need_mask, bool tree_chunk,
-                                           int tree_bit0, uint32_t ok_prefix) {
-  constexpr int NKS = D / 32, NDB = D / 16, MAT_BYTES = 32 * D * 2;
+__device__ __forceinline__ void chunk_qk(const uint8_t* slot, const bf16x8 (&qf)[QBW][D / 32],
+                                         f32x4 (&sc)[QBW][2]) {
+  constexpr int NKS = D / 32;
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const uint16_t* Kc = reinterpret_cast<const uint16_t*>(slot);
-  const uint8_t* Vb = slot + MAT_BYTES;
-
-  f32x4 sc[QBW][2];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) sc[qb][0] = sc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -460,7 +458,15 @@ __device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&q
         sc[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], sc[qb][hlf], 0, 0, 0);
     }
   }
-  bf16x8 pf[QBW];
+}
+
+template <int D, int QBW>
+__device__ __forceinline__ void chunk_soft(const f32x4 (&sc)[QBW][2], const uint64_t (&anc_q)[QBW],
+                                           f32x4 (&acc)[QBW][D / 16], float (&m_run)[QBW],
+                                           float (&l_run)[QBW], bf16x8 (&pf)[QBW], float scale_log2,
+                                           bool need_mask, bool tree_chunk, int tree_bit0,
+                                           uint32_t ok_prefix) {
+  const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     float x[8];
@@ -472,8 +478,16 @@ __device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&q
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
     }
-    pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
+    pf[qb] = softmax_step<D / 16>(x, m_run[qb], l_run[qb], acc[qb]);
   }
+}
+
+template <int D, int QBW>
+__device__ __forceinline__ void chunk_pv(const uint8_t* slot, const bf16x8 (&pf)[QBW],
+                                         f32x4 (&acc)[QBW][D / 16]) {
+  constexpr int NDB = D / 16, MAT_BYTES = 32 * D * 2;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const uint8_t* Vb = slot + MAT_BYTES;
   // V^T fragments by transposed LDS reads: lane (g, c) gets V[8g + j][16db + c],
   // j = 0..7, as two 4-element halves.
 #pragma unroll
@@ -493,6 +507,21 @@ __device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&q
     for (int qb = 0; qb < QBW; ++qb)
       acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
   }
+}
+
+// The three parts of one chunk in order.
+template <int D, int QBW>
+__device__ __forceinline__ void chunk_step(const uint8_t* slot, const bf16x8 (&qf)[QBW][D / 32],
+                                           const uint64_t (&anc_q)[QBW], f32x4 (&acc)[QBW][D / 16],
+                                           float (&m_run)[QBW], float (&l_run)[QBW],
+                                           float scale_log2, bool need_mask, bool tree_chunk,
+                                           int tree_bit0, uint32_t ok_prefix) {
+  f32x4 sc[QBW][2];
+  bf16x8 pf[QBW];
+  chunk_qk<D, QBW>(slot, qf, sc);
+  chunk_soft<D, QBW>(sc, anc_q, acc, m_run, l_run, pf, scale_log2, need_mask, tree_chunk,
+                     tree_bit0, ok_prefix);
+  chunk_pv<D, QBW>(slot, pf, acc);
 }
 
 template <class S>
@@ -1070,9 +1099,12 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
   u.total = L + a.N;
   for (int j = n_pre; j < n_pro; ++j) issue(j);
 
+  // every wave computes (rows past M hold zero queries and no tree bits):
+  // a wave-uniform skip inside the tile loop made the compiler copy the
+  // accumulators at every join, and the barrier paces all waves alike anyway
   bf16x8 qf[QBW][NKS];
   uint64_t anc_q[QBW];
-  if (active) load_queries<D, QBW, RW>(a, u, r0, qf, anc_q);
+  load_queries<D, QBW, RW>(a, u, r0, qf, anc_q);
 
   f32x4 acc[QBW][NDB];
   float m_run[QBW], l_run[QBW];
@@ -1084,25 +1116,33 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int i = 0; i < n_my; ++i) {
+  // prefix tiles; the tree tile (position n_pre, if this split has it) after
+  // the loop, so that the loop body has no join for the compiler to copy at
+  for (int i = 0; i < n_pre; ++i) {
     wait_tiles_after<LPW>(min(NBUF - 2, n_my - 1 - i));
     barrier_lds();  // tile i is whole; every wave is done with tile i - 1
     if (i + NBUF - 1 < n_my) issue(i + NBUF - 1);
-    if (!active) continue;
     const uint8_t* tile = lds + (i % NBUF) * S::TILE_BYTES;
-    if (i < n_pre) {
-      const int key0 = (tb + i) * S::TILE_KEYS;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k0 = key0 + 32 * h;
-        chunk_step<D, QBW>(tile + h * S::SLOT_BYTES, qf, anc_q, acc, m_run, l_run, a.scale_log2,
-                           k0 + 32 > L, false, 0, prefix_mask8(k0 + 8 * g, L));
-      }
-    } else {
-      for (int h = 0; h < 2 && 32 * h < a.N; ++h)
-        chunk_step<D, QBW>(tile + h * S::SLOT_BYTES, qf, anc_q, acc, m_run, l_run, a.scale_log2,
-                           true, true, 32 * h, 0u);
-    }
+    const int key0 = (tb + i) * S::TILE_KEYS;
+    // both chunks' S first, so each softmax overlaps MFMAs still in flight
+    f32x4 s0[QBW][2], s1[QBW][2];
+    bf16x8 pf[QBW];
+    chunk_qk<D, QBW>(tile, qf, s0);
+    chunk_qk<D, QBW>(tile + S::SLOT_BYTES, qf, s1);
+    chunk_soft<D, QBW>(s0, anc_q, acc, m_run, l_run, pf, a.scale_log2, key0 + 32 > L, false, 0,
+                       prefix_mask8(key0 + 8 * g, L));
+    chunk_pv<D, QBW>(tile, pf, acc);
+    chunk_soft<D, QBW>(s1, anc_q, acc, m_run, l_run, pf, a.scale_log2, key0 + 64 > L, false, 0,
+                       prefix_mask8(key0 + 32 + 8 * g, L));
+    chunk_pv<D, QBW>(tile + S::SLOT_BYTES, pf, acc);
+  }
+  if (tree_split) {
+    wait_tiles_after<LPW>(0);
+    barrier_lds();
+    const uint8_t* tile = lds + (n_pre % NBUF) * S::TILE_BYTES;
+    for (int h = 0; h < 2 && 32 * h < a.N; ++h)
+      chunk_step<D, QBW>(tile + h * S::SLOT_BYTES, qf, anc_q, acc, m_run, l_run, a.scale_log2,
+                         true, true, 32 * h, 0u);
   }
   if (!active) return;
 
