@@ -365,38 +365,37 @@ struct RingShape {
   static_assert(ACC_BYTES <= SLOT_BYTES, "a wave's state is parked in its own slot");
   static constexpr int LDS_RING = NWAVE * SLOT_BYTES;
   static constexpr int LDS_ML = NWAVE * QBW * 32 * 4;   // each wave's m and l
-  static constexpr int LDS_STAGE = RW * (D + 4) * 4;    // the combined split partial
-  static constexpr int LDS_BYTES = LDS_RING + LDS_ML + LDS_STAGE;
+  static constexpr int LDS_BYTES = LDS_RING + LDS_ML;
 };
 
 // The NWAVE waves' online-softmax states for the same query rows combined in
-// one round: every wave parks its accumulators in its own (now idle) slot and
-// its m, l beside the ring; after one barrier the waves share out the
-// (query block, d block) tiles of the result, each combining all NWAVE states
-// of its tiles, and write the split's normalised rows and log2-sum-exp to the
-// staging area ([RW][D + 4], column D = log2-sum-exp).
-template <int QBW, int NDB, int NWAVE, int SLOT_BYTES>
+// one round: every wave parks its accumulators (rows below `rows` only) in its
+// own (now idle) slot and its m, l beside the ring; after one barrier the
+// waves share out the (query block, d block) tiles of the result, each
+// combining all NWAVE states of its tiles, and hand every normalised tile
+// straight from registers to emit(row, d block, O / l, log2-sum-exp).
+template <int QBW, int NDB, int NWAVE, int SLOT_BYTES, typename Emit>
 __device__ __forceinline__ void fold_waves(const f32x4 (&acc)[QBW][NDB], const float (&m_run)[QBW],
                                            const float (&l_run)[QBW], uint8_t* lds, float* ml,
-                                           float* stage, int wave) {
-  constexpr int D = NDB * 16, SD = D + 4;
+                                           int wave, int rows, Emit&& emit) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   float* mine = reinterpret_cast<float*>(lds + wave * SLOT_BYTES);
-  if (wave < NWAVE) {
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
+  for (int qb = 0; qb < QBW; ++qb) {
+    if (qb * 16 + c >= rows) continue;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<f32x4*>(mine + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
-      if (g == 0) {
-        ml[(wave * QBW + qb) * 32 + c] = m_run[qb];
-        ml[(wave * QBW + qb) * 32 + 16 + c] = l_run[qb];
-      }
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(mine + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
+    if (g == 0) {
+      ml[(wave * QBW + qb) * 32 + c] = m_run[qb];
+      ml[(wave * QBW + qb) * 32 + 16 + c] = l_run[qb];
     }
   }
   __syncthreads();
-  for (int it = wave; it < QBW * NDB && wave < NWAVE; it += NWAVE) {
+  for (int it = wave; it < QBW * NDB; it += NWAVE) {
     const int qb = it / NDB, db = it - qb * NDB;
+    const int rl = qb * 16 + c;
+    if (rl >= rows) continue;
     float ms[NWAVE], mt = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
@@ -413,12 +412,9 @@ __device__ __forceinline__ void fold_waves(const f32x4 (&acc)[QBW][NDB], const f
       o += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds + w * SLOT_BYTES) +
                                            ((qb * NDB + db) * 64 + lane) * 4) * f;
     }
-    const int rl = qb * 16 + c;
     const float inv = lt == 0.f ? 0.f : 1.f / lt;
-    *reinterpret_cast<f32x4*>(stage + rl * SD + db * 16 + 4 * g) = o * inv;
-    if (db == 0 && g == 0) stage[rl * SD + D] = lt == 0.f ? -INFINITY : mt + __log2f(lt);
+    emit(rl, db, o * inv, lt == 0.f ? -INFINITY : mt + __log2f(lt));
   }
-  __syncthreads();
 }
 
 // Valid committed keys among key0..key0+7 (keys below L) as an 8-bit mask.
@@ -673,12 +669,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
-  // this split's partial (O / l and log2-sum-exp), staged in LDS so that the
-  // stores are coalesced
+  // the folded rows go from registers to the output (one split) or to this
+  // split's partial (O / l and log2-sum-exp)
   float* ml = reinterpret_cast<float*>(lds + S::LDS_RING);
-  float* stage = reinterpret_cast<float*>(lds + S::LDS_RING + S::LDS_ML);
-  fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(acc, m_run, l_run, lds, ml, stage, wave);
-  constexpr int SD = D + 4;
   constexpr int D4 = D / 4;
   auto out_row = [&](int rl) {
     const int row = row0 + rl;
@@ -687,22 +680,20 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     return a.out + (((size_t)b * a.N + i) * a.Hq + h) * D;
   };
   if (a.splits == 1) {
-    for (int it = tid; it < rows * D4; it += S::THREADS) {
-      const int rl = it / D4, d4 = it - rl * D4;
-      const f32x4 o = bad ? f32x4{0.f, 0.f, 0.f, 0.f}
-                          : *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
-      *reinterpret_cast<u32x2*>(out_row(rl) + 4 * d4) =
-          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
+    fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(
+        acc, m_run, l_run, lds, ml, wave, rows, [&](int rl, int db, f32x4 o, float) {
+          if (bad) o = f32x4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<u32x2*>(out_row(rl) + db * 16 + 4 * g) =
+              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        });
     return;
   }
   const size_t pbase = ((size_t)unit * a.splits + split) * RW;
-  for (int it = tid; it < rows * D4; it += S::THREADS) {
-    const int rl = it / D4, d4 = it - rl * D4;
-    *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + 4 * d4) =
-        *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
-  }
-  for (int rl = tid; rl < rows; rl += S::THREADS) a.part_lse[pbase + rl] = stage[rl * SD + D];
+  fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(
+      acc, m_run, l_run, lds, ml, wave, rows, [&](int rl, int db, f32x4 o, float lse) {
+        *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + db * 16 + 4 * g) = o;
+        if (db == 0 && g == 0) a.part_lse[pbase + rl] = lse;
+      });
 
   // The unit's last split to finish combines the partials.  All splits of a
   // unit run on one XCD, so its L2 is where they meet: each workgroup's
