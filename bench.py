@@ -172,6 +172,36 @@ def measure(torch, ev, W, T, steps, warmup):
                 copies=copies, walk_bytes=walk_bytes, rejected=rejected)
 
 
+def measure_feature_gather(torch, ev, W, steps):
+    """The accepted path's features gathered in path order (eagle_feature_gather)
+    at the llama2-7b shape: hidden size 4096 in bf16, the tree's deepest
+    root-to-leaf path accepted; `steps` launches in one graph."""
+    cfg = W.get(WORKLOAD)
+    s = W.make_step(cfg, 1.0, with_attention=False)
+    hidden = 4096
+    depth = np.zeros(cfg.N, dtype=np.int64)
+    for i in range(1, cfg.N):
+        depth[i] = depth[s.parents[0, i]] + 1
+    leaf = int(np.argmax(depth))
+    chain = [leaf]
+    while chain[-1] != 0:
+        chain.append(int(s.parents[0, chain[-1]]))
+    chain = chain[::-1]
+    path = np.full((cfg.B, cfg.N), -1, dtype=np.int32)
+    path[:, :len(chain)] = chain
+    m = np.full(cfg.B, len(chain) - 1, dtype=np.int32)
+    dev = torch.device("cuda")
+    feats = torch.randn((cfg.B, cfg.N, hidden), device=dev).to(torch.bfloat16)
+    out = torch.empty_like(feats)
+    tp, tm = torch.from_numpy(path).to(dev), torch.from_numpy(m).to(dev)
+    g = graph_of(torch, lambda i: ev.feature_gather(feats, tp, tm, out=out), steps)
+    time_graph(torch, g)
+    t = time_graph(torch, g) / steps
+    nbytes = 2 * cfg.B * len(chain) * hidden * 2
+    return {"us": t * 1e6, "rows": len(chain), "hidden": hidden, "dtype": "bf16",
+            "bytes_per_launch": nbytes, "achieved_GBs": nbytes / t / 1e9, "bound": "latency"}
+
+
 def pmc_capture(torch, ev, W, steps):
     """Eager steps at T=1 over the rotation, then the calibration copy."""
     cfg = W.get(WORKLOAD)
@@ -266,6 +296,7 @@ def main():
     attn_bytes = cfg.attn_bytes()
     achieved = attn_bytes / r1["t_attn"] / 1e9
     vocab_bytes = r1["walk_bytes"]  # target rows + the draft row of every rejected candidate
+    fg = measure_feature_gather(torch, ev, W, args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -302,6 +333,7 @@ def main():
                "attn_us": r0["t_attn"] * 1e6, "verify_us": r0["t_verify"] * 1e6,
                "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
+        "next_rows": {"feature_gather": fg},
     }
     print(json.dumps(line), flush=True)
 

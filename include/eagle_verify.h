@@ -60,6 +60,8 @@ typedef int eagle_status_t;
 #define EAGLE_FLAG_TIMEOUT     16  /* a cross-workgroup wait gave up; the  */
                                    /* sequence's walk outputs are in range */
                                    /* but not meaningful                   */
+#define EAGLE_FLAG_BAD_PATH    32  /* accepted path not as the walk emits  */
+                                   /* it (eagle_feature_gather)            */
 
 /* Message for the last non-zero status returned on this thread. */
 EAGLE_API const char* eagle_last_error(void);
@@ -260,6 +262,33 @@ EAGLE_API eagle_status_t eagle_kv_compact(uint16_t* k_cache, uint16_t* v_cache, 
                                 const int32_t* kv_src_slots, const int32_t* accept_len,
                                 int B, int N, int Hkv, int d, int Lmax,
                                 int32_t* new_kv_len, int32_t* seq_flags, void* stream);
+
+/*
+ * Feature gather: the features of the accepted path, in path order, for the
+ * next round's draft (EAGLE, paperlayer.ai summary, §3 EAGLE: the accepted
+ * tokens and their features are recorded, and the draft head extrapolates
+ * from the target's features).  For every sequence b and j = 0..accept_len[b],
+ * row j of out takes row path[b, j] of features; rows of out past
+ * accept_len[b] are not written.
+ *
+ *   features device [B, N, row_bytes], one row per tree node in node order
+ *            (e.g. the target's last hidden state of every node); rows are
+ *            copied as bytes, so any element type works
+ *   path, accept_len device [B, N] / [B] int32 as eagle_verify_accept emits
+ *            them: path[b, 0] = 0 and path[b, j] increasing and below N for
+ *            j <= accept_len[b] < N; a sequence that breaks this sets
+ *            EAGLE_FLAG_BAD_PATH and has no row written
+ *   row_bytes bytes per row: a positive multiple of 16, N * row_bytes < 2^35
+ *   out      device [B, N, row_bytes]; must not overlap features
+ *   seq_flags device [B] int32 or NULL
+ * Errors: EAGLE_ERR_INVALID_ARGUMENT for a bad size, NULL pointer or
+ * overlapping buffers; nothing is enqueued then.
+ * Supported: 1 <= N <= 64.
+ */
+EAGLE_API eagle_status_t eagle_feature_gather(const void* features, const int32_t* path,
+                                              const int32_t* accept_len, int B, int N,
+                                              int64_t row_bytes, void* out, int32_t* seq_flags,
+                                              void* stream);
 
 #ifdef __cplusplus
 }

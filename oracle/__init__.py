@@ -34,4 +34,4 @@ from .attention import bf16_bits_to_f64, tree_attention, tree_attention_one  # n
 from .vocab import argmax_lowest, target_distribution  # noqa: F401
 from .walk import (NEAR_TIE, WalkResult, inverse_cdf, node_round,  # noqa: F401
                    verify_batch, verify_sequence)
-from .compact import kv_compact  # noqa: F401
+from .compact import feature_gather, kv_compact  # noqa: F401

@@ -1,4 +1,5 @@
-"""KV compaction of the accepted path (oracle; test infrastructure only).
+"""KV compaction and feature gather of the accepted path (oracle; test
+infrastructure only).
 
 The accepted tokens are recorded for the next round (EAGLE-p2 §3 EAGLE:
 accepted tokens and their features are recorded for subsequent drafting).
@@ -29,3 +30,18 @@ def kv_compact(k_cache, v_cache, kv_len, kv_src, accept_len):
             v_out[b, :, L + j] = v_cache[b, :, src]
         new_len[b] = L + m + 1
     return k_out, v_out, new_len
+
+
+def feature_gather(features, path, accept_len, out):
+    """The accepted path's features in path order (EAGLE-p2 §3 EAGLE: the
+    accepted tokens and their features are recorded for the next draft).
+
+    features [B, N, ...] (one row per tree node), path [B, N] node ids
+    (path[b, 0] = 0), accept_len [B]; returns a copy of `out` whose row j of
+    sequence b is features[b, path[b, j]] for j = 0..accept_len[b], the other
+    rows unchanged."""
+    res = np.array(out, copy=True)
+    for b in range(res.shape[0]):
+        for j in range(int(accept_len[b]) + 1):
+            res[b, j] = features[b, int(path[b][j])]
+    return res

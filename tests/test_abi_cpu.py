@@ -179,3 +179,26 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         binding._ptr(torch.zeros(3), name="x")
+
+
+def test_feature_gather_argument_errors():
+    # every check happens on the host before anything is enqueued
+    L = ev.lib()
+    f, o = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    ok_args = dict(feat=f, path=FAKE, acc=FAKE, B=2, N=8, row=256, out=o)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return L.eagle_feature_gather(a["feat"], a["path"], a["acc"], a["B"], a["N"], a["row"],
+                                      a["out"], None, None)
+    assert call(B=0) == binding.EAGLE_OK
+    assert call(row=24) == binding.EAGLE_ERR_INVALID_ARGUMENT     # not a multiple of 16
+    assert call(row=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(N=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(N=65) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(B=-1) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(path=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(out=None) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    # out overlapping features: 2 * 8 * 256 bytes from 0x100000
+    assert call(out=ctypes.c_void_p(0x100000 + 4000)) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert call(row=1 << 40) == binding.EAGLE_ERR_INVALID_ARGUMENT  # N * row_bytes too large

@@ -70,6 +70,7 @@ ATTN_CASES = [
     ("gqa8-N60", 1, 60, 16, 2, 128, [700]),
     ("max-nodes", 2, 64, 4, 2, 128, [190, 3]),
     ("wide-group", 1, 40, 32, 2, 64, [350]),
+    ("gqa-ragged-edges", 3, 20, 16, 2, 128, [0, 1, 777]),
 ]
 
 
@@ -124,6 +125,25 @@ def test_attention_bad_kv_len_flags_and_zeroes():
     assert (out[1].float().cpu().numpy() == 0).all()
     ref = oracle.tree_attention(s.q[:1], s.k_cache[:1], s.v_cache[:1], s.kv_len[:1], s.parents[:1])
     assert np.abs(out[:1].float().cpu().numpy() - ref).max() < ATOL_ATTN
+
+
+def test_attention_gqa_bad_kv_len_flags_and_zeroes():
+    """Grouped queries (the group kernel, 4 splits merged by the merge kernel):
+    a sequence whose kv_len leaves no room for the tree is flagged and gets
+    zero rows; the other sequence is unaffected."""
+    cfg = W.shrink(W.get(3), B=2, L=700, V=16)
+    s = W.make_step(cfg, 1.0, seed=2)
+    kv = s.kv_len.copy()
+    kv[0] = s.k_cache.shape[2] - cfg.N + 1
+    flags = torch.zeros(2, dtype=torch.int32, device="cuda")
+    say("attention bad kv_len, grouped queries")
+    anc, _, _ = ev.tree_build(dev(s.parents))
+    out = ev.tree_attn(bf(s.q), bf(s.k_cache), bf(s.v_cache), dev(kv), anc, seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [ev.binding.FLAG_BAD_KV_LEN, 0]
+    assert (out[0].float().cpu().numpy() == 0).all()
+    ref = oracle.tree_attention(s.q[1:], s.k_cache[1:], s.v_cache[1:], s.kv_len[1:], s.parents[1:])
+    assert np.abs(out[1:].float().cpu().numpy() - ref).max() < ATOL_ATTN
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
@@ -570,3 +590,93 @@ def test_compaction_rejects_bad_slots():
     kr, _, _ = oracle.kv_compact(s.k_cache[:1], s.v_cache[:1], s.kv_len[:1], src[:1], m[:1])
     assert np.array_equal(kb[:1], kr)
     assert np.array_equal(kb[1:], s.k_cache[1:])
+
+
+# ---------------------------------------------------------------- feature gather
+def _random_paths(rng, B, N):
+    """Accepted paths as the walk emits them: 0, then a child of the previous node."""
+    parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(B)])
+    path = np.full((B, N), -1, dtype=np.int32)
+    m = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        p = [0]
+        while True:
+            kids = [c for c in range(N) if parents[b, c] == p[-1]]
+            if not kids or rng.random() < 0.2:
+                break
+            p.append(int(rng.choice(kids)))
+        m[b] = len(p) - 1
+        path[b, :len(p)] = p
+    return path, m
+
+
+@pytest.mark.parametrize("B,N,H,dtype", [(3, 26, 4096, torch.bfloat16), (5, 60, 200, torch.float32),
+                                         (1, 1, 8, torch.bfloat16), (2, 64, 1024, torch.float16)])
+def test_feature_gather_matches_oracle(B, N, H, dtype):
+    """Bit-exact against the oracle, rows past the path untouched."""
+    rng = np.random.default_rng(B * 100 + N)
+    path, m = _random_paths(rng, B, N)
+    if N == 64:  # a chain accepted to its end
+        path[0] = np.arange(N)
+        m[0] = N - 1
+    feats = torch.randn((B, N, H), generator=torch.Generator().manual_seed(N)).to(dtype)
+    out0 = torch.full((B, N, H), -3.0).to(dtype)
+    say(f"feature gather B={B} N={N} H={H} {dtype}")
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = out0.cuda()
+    ev.feature_gather(feats.cuda(), dev(path), dev(m), out=out, seq_flags=flags)
+    torch.cuda.synchronize()
+    as_bits = lambda t: t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+    ref = oracle.feature_gather(as_bits(feats), path, m, as_bits(out0))
+    assert np.array_equal(as_bits(out), ref)
+    assert not flags.cpu().numpy().any()
+
+
+def test_feature_gather_after_gpu_walk():
+    """The gather driven by the path and accept length the GPU walk wrote."""
+    cfg = W.shrink(W.get(1), B=4, N=26, V=64)
+    s = W.make_step(cfg, 1.0, seed=11, with_attention=False)
+    s.draft_probs[:] = 0  # drafts drawn from the target: q = p accepts the first child
+    for b in range(cfg.B):
+        for i in range(1, cfg.N):
+            pp = s.parents[b, i]
+            row = s.target_logits[b, pp].astype(np.float64)
+            e = np.exp(row - row.max())
+            s.draft_probs[b, i] = (e / e.sum()).astype(np.float32)
+    res = run_verify(s)
+    assert res["accept_len"].max() > 0
+    H = 512
+    feats = torch.randn((cfg.B, cfg.N, H), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    out = torch.zeros_like(feats).cuda()
+    say("feature gather after the GPU walk")
+    ev.feature_gather(feats.cuda(), dev(res["path"]), dev(res["accept_len"]), out=out)
+    torch.cuda.synchronize()
+    ref = oracle.feature_gather(feats.view(torch.int16).numpy(), res["path"], res["accept_len"],
+                                np.zeros((cfg.B, cfg.N, H), dtype=np.int16))
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref)
+
+
+def test_feature_gather_flags_bad_paths():
+    """Paths the walk never emits are flagged and leave out untouched."""
+    N, H = 8, 64
+    path = np.array([[1, 2, -1, -1, -1, -1, -1, -1],     # does not start at the root
+                     [0, 3, 3, -1, -1, -1, -1, -1],      # not increasing
+                     [0, 9, -1, -1, -1, -1, -1, -1],     # node out of range
+                     [0, 1, 2, 3, 4, 5, 6, 7],           # accept length out of range
+                     [0, 2, 5, -1, -1, -1, -1, -1]],     # fine
+                    dtype=np.int32)
+    m = np.array([1, 2, 1, 8, 2], dtype=np.int32)
+    B = len(m)
+    feats = torch.randn((B, N, H)).to(torch.bfloat16)
+    out0 = torch.full((B, N, H), 7.0).to(torch.bfloat16)
+    out = out0.cuda()
+    flags = torch.zeros(B, dtype=torch.int32, device="cuda")
+    say("feature gather bad paths")
+    ev.feature_gather(feats.cuda(), dev(path), dev(m), out=out, seq_flags=flags)
+    torch.cuda.synchronize()
+    F = ev.binding.FLAG_BAD_PATH
+    assert flags.cpu().tolist() == [F, F, F, F, 0]
+    got = out.cpu()
+    assert torch.equal(got[:4].view(torch.int16), out0[:4].view(torch.int16))
+    assert torch.equal(got[4, :3].view(torch.int16), feats[4, [0, 2, 5]].view(torch.int16))
+    assert torch.equal(got[4, 3:].view(torch.int16), out0[4, 3:].view(torch.int16))

@@ -66,3 +66,35 @@ def test_identity_path_is_a_no_op():
     k2, v2, n = oracle.kv_compact(k, k, kv_len, src, np.array([2, 0]))
     np.testing.assert_array_equal(k2, k)
     assert list(n) == [6, 6]
+
+
+# ---------------------------------------------------------------- feature gather
+def test_feature_gather_equals_library_gather():
+    # Independent formulation: numpy's take_along_axis over the node axis for
+    # the accepted rows, rows past the path left as they were.
+    rng = np.random.default_rng(3)
+    B, N, H = 5, 14, 6
+    kv_len, src, m = _walk_like_paths(rng, B, N)
+    path = np.where(src >= 0, src - kv_len[:, None], -1).astype(np.int32)
+    feats = rng.standard_normal((B, N, H)).astype(np.float32)
+    out0 = rng.standard_normal((B, N, H)).astype(np.float32)
+    got = oracle.feature_gather(feats, path, m, out0)
+    idx = np.clip(path, 0, N - 1)[:, :, None].repeat(H, axis=2)
+    gathered = np.take_along_axis(feats, idx, axis=1)
+    for b in range(B):
+        np.testing.assert_array_equal(got[b, : m[b] + 1], gathered[b, : m[b] + 1])
+        np.testing.assert_array_equal(got[b, m[b] + 1:], out0[b, m[b] + 1:])
+
+
+def test_feature_gather_special_paths():
+    # a chain accepted to the end is the identity; a rejected root keeps row 0
+    rng = np.random.default_rng(4)
+    N, H = 9, 3
+    feats = rng.standard_normal((2, N, H))
+    out0 = np.zeros((2, N, H))
+    path = np.stack([np.arange(N), np.r_[0, np.full(N - 1, -1)]]).astype(np.int32)
+    m = np.array([N - 1, 0], dtype=np.int32)
+    got = oracle.feature_gather(feats, path, m, out0)
+    np.testing.assert_array_equal(got[0], feats[0])
+    np.testing.assert_array_equal(got[1, 0], feats[1, 0])
+    assert not got[1, 1:].any()

@@ -27,6 +27,7 @@ FLAG_BAD_KV_LEN = 2
 FLAG_BAD_TOKEN = 4
 FLAG_NONFINITE = 8
 FLAG_TIMEOUT = 16
+FLAG_BAD_PATH = 32
 
 
 class EagleError(RuntimeError):
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "eagle_verify_accept_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P, _P]),
     "eagle_kv_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "eagle_feature_gather": (_I, [_P, _P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]),
 }
 
 
@@ -276,3 +278,22 @@ def kv_compact(k_cache, v_cache, kv_len, kv_src, accept_len, *, new_kv_len=None,
         _ptr(new_kv_len, torch.int32, "new_kv_len"), _ptr(seq_flags, torch.int32, "seq_flags"),
         _stream(stream)))
     return new_kv_len
+
+
+def feature_gather(features, path, accept_len, *, out=None, seq_flags=None, stream=None):
+    """out[b, j] = features[b, path[b, j]] for j = 0..accept_len[b] (rows
+    copied as bytes); features [B, N, ...] contiguous, any dtype.  Returns out
+    (rows past accept_len[b] are left as they were)."""
+    B, N = path.shape
+    if features.dim() < 2 or tuple(features.shape[:2]) != (B, N):
+        raise ValueError(f"features must be [B, N, ...] with B, N = {B}, {N}")
+    row_bytes = features[0, 0].numel() * features.element_size()
+    if out is None:
+        out = torch.empty_like(features)
+    if out.shape != features.shape or out.dtype != features.dtype:
+        raise ValueError("out must have the shape and dtype of features")
+    _check(lib().eagle_feature_gather(
+        _ptr(features, None, "features"), _ptr(path, torch.int32, "path"),
+        _ptr(accept_len, torch.int32, "accept_len"), B, N, row_bytes, _ptr(out, None, "out"),
+        _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
+    return out

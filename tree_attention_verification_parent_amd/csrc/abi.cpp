@@ -260,4 +260,28 @@ eagle_status_t eagle_kv_compact(uint16_t* k_cache, uint16_t* v_cache, const int3
                     "kv compaction launch");
 }
 
+eagle_status_t eagle_feature_gather(const void* features, const int32_t* path,
+                                    const int32_t* accept_len, int B, int N, int64_t row_bytes,
+                                    void* out, int32_t* seq_flags, void* stream) {
+  if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
+  if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "row_bytes must be a positive multiple of 16 (got %lld)",
+                (long long)row_bytes);
+  if ((double)N * (double)(row_bytes / 16) >= 2147483648.0)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "N * row_bytes must be below 2^35");
+  if (B == 0) return EAGLE_OK;
+  if ((double)B * 64.0 > 2.0e9) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B too large for one launch");
+  if (!features || !path || !accept_len || !out)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "features, path, accept_len and out must be non-NULL");
+  const uintptr_t f0 = reinterpret_cast<uintptr_t>(features);
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t bytes = (uintptr_t)B * (uintptr_t)N * (uintptr_t)row_bytes;
+  if (f0 < o0 + bytes && o0 < f0 + bytes)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "out must not overlap features");
+  return hip_status(eagle::launch_feature_gather(features, path, accept_len, B, N, row_bytes, out,
+                                                 seq_flags, as_stream(stream)),
+                    "feature gather launch");
+}
+
 }  // extern "C"

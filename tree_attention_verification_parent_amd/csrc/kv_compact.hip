@@ -7,6 +7,8 @@
 // j = 1 and written for j = 2), so a workgroup reads every row it moves into
 // registers, synchronises, and only then writes.  One workgroup per (b, KV
 // head) owns all rows of that head, so workgroups never overlap.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -97,6 +99,56 @@ hipError_t launch_kv_compact(uint16_t* k, uint16_t* v, const int32_t* kv_len,
   else
     kv_compact_kernel<128><<<grid, 256, 0, s>>>(k, v, kv_len, kv_src, accept_len, N, Hkv, Lmax,
                                                 new_len, flags);
+  return hipGetLastError();
+}
+
+// Feature gather: out[b, j] = features[b, path[b, j]] for j = 0..m, the rows
+// copied as 16-byte columns.  Out of place, so rows can be copied in any
+// order.  A sequence's rows are spread over `nb` workgroups (ids b * nb ..),
+// each thread taking (row, column) items strided over them, so that loads
+// and stores run along a row.  Every workgroup of a sequence checks the path
+// the same way; the first one flags a bad path.
+__global__ __launch_bounds__(256) void feature_gather_kernel(const u32x4* __restrict__ feat,
+                                                             const int32_t* __restrict__ path,
+                                                             const int32_t* __restrict__ accept_len,
+                                                             int N, int cols, int nb,
+                                                             u32x4* __restrict__ out,
+                                                             int32_t* __restrict__ flags) {
+  __shared__ int s_src[64];
+  __shared__ int s_ok;
+  const int b = blockIdx.x / nb;
+  const int part = blockIdx.x - b * nb;
+  const int tid = threadIdx.x;
+  const int m = accept_len[b];
+  if (tid < 64) s_src[tid] = tid < N ? path[(size_t)b * N + tid] : -1;
+  __syncthreads();
+  if (tid == 0) {
+    bool ok = m >= 0 && m < N && s_src[0] == 0;
+    for (int j = 1; ok && j <= m; ++j) ok = s_src[j] > s_src[j - 1] && s_src[j] < N;
+    s_ok = ok;
+    if (!ok && part == 0 && flags) atomicOr(flags + b, EAGLE_FLAG_BAD_PATH);
+  }
+  __syncthreads();
+  if (!s_ok) return;
+  const int total = (m + 1) * cols;
+  const size_t base = (size_t)b * N * cols;
+  for (int it = part * 256 + tid; it < total; it += nb * 256) {
+    const int j = it / cols;
+    const int col = it - j * cols;
+    out[base + (size_t)j * cols + col] = feat[base + (size_t)s_src[j] * cols + col];
+  }
+}
+
+hipError_t launch_feature_gather(const void* features, const int32_t* path,
+                                 const int32_t* accept_len, int B, int N, int64_t row_bytes,
+                                 void* out, int32_t* flags, hipStream_t s) {
+  const int cols = (int)(row_bytes / 16);
+  // enough workgroups per sequence for a full path, at most 64
+  const long long items = (long long)N * cols;
+  const int nb = (int)std::min<long long>(64, (items + 255) / 256);
+  feature_gather_kernel<<<dim3((unsigned)(B * nb)), 256, 0, s>>>(
+      static_cast<const u32x4*>(features), path, accept_len, N, cols, nb,
+      static_cast<u32x4*>(out), flags);
   return hipGetLastError();
 }
 

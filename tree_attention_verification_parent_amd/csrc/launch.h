@@ -73,4 +73,9 @@ hipError_t launch_kv_compact(uint16_t* k, uint16_t* v, const int32_t* kv_len,
                              int Hkv, int d, int Lmax, int32_t* new_len, int32_t* flags,
                              hipStream_t s);
 
+// Feature gather (out-of-place, rows as 16-byte columns) ----------------------
+hipError_t launch_feature_gather(const void* features, const int32_t* path,
+                                 const int32_t* accept_len, int B, int N, int64_t row_bytes,
+                                 void* out, int32_t* flags, hipStream_t s);
+
 }  // namespace eagle
