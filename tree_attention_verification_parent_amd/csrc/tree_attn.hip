@@ -417,6 +417,12 @@ __device__ __forceinline__ void fold_waves(const f32x4 (&acc)[QBW][NDB], const f
   }
 }
 
+// A wave-uniform 32-bit value read with a scalar load (constant address
+// space), which the compiler tracks apart from the vector loads in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Valid committed keys among key0..key0+7 (keys below L) as an 8-bit mask.
 __device__ __forceinline__ uint32_t prefix_mask8(int key0, int L) {
   const int below = L - key0;
@@ -586,8 +592,30 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // taken by the wave of the last split with the fewest prefix chunks.
   const bool tree_wave = split == a.splits - 1 && wave == (ce - cb) % NWAVE;
 
-  // committed length, then the queries (needed only once the first chunk is in)
-  int L = a.kv_len[b];
+  // A wave with three or more chunks loads its second one into registers
+  // right away, so that it is in flight with the first instead of requested
+  // once the first has been computed (the slot is busy until then); it is
+  // written to the slot in the layout a direct-to-LDS load gives.  (Measured
+  // on MI355X: llama2-13b shape, ~5 chunks per wave, 60.9 us against 62.7;
+  // with only two chunks, as at the llama2-7b shape, waiting for both before
+  // the first is computed costs more than it saves: 15.2 us against 14.2.)
+  const int my_chunks = my_n + (tree_wave ? (a.N + 31) / 32 : 0);
+  const bool pre2 = my_chunks >= 3;  // wave-uniform
+  u32x4 pre[2 * LPM];
+  auto load_pre = [&](int key0, int key_max) {
+#pragma unroll
+    for (int t = 0; t < LPM; ++t) {
+      const int r = t * RPL + r_in;
+      const size_t off = (size_t)min(key0 + r, key_max) * D + (p_in ^ swz(r)) * 8;
+      pre[t] = *reinterpret_cast<const u32x4*>(kp + off);
+      pre[LPM + t] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+  };
+  if (pre2 && 1 < my_n) load_pre((my_first + NWAVE) * 32, Lp - 1);
+
+  // committed length (a scalar load: waiting for it does not wait for the
+  // chunks' vector loads), then the queries, needed once the first chunk is in
+  int L = load_uniform(a.kv_len + b);
   const bool bad = L < 0 || L > Lp;
   if (bad) {
     L = 0;
@@ -595,6 +623,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
   }
   if (tree_wave && my_n == 0) issue_keys(L, L + a.N - 1);
+  if (pre2 && my_n <= 1) load_pre(L + 32 * (1 - my_n), L + a.N - 1);  // a tree chunk second
   // the tree wave's rows' ancestor masks: bit t of anc[row] admits key L + t
   uint64_t anc_q[QBW];
   if (tree_wave) {
@@ -646,16 +675,24 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int my_chunks = my_n + (tree_wave ? (a.N + 31) / 32 : 0);
   for (int i = 0; i < my_chunks; ++i) {
     const bool tree_chunk = i >= my_n;
     const int tree_bit0 = 32 * (i - my_n);  // anc bit of the tree chunk's first key
     const int gc = my_first + NWAVE * i;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
+    if (i == 1 && pre2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the first chunk's reads are done
+#pragma unroll
+      for (int t = 0; t < LPM; ++t) {
+        *reinterpret_cast<u32x4*>(slot + t * RPL * D * 2 + lane * 16) = pre[t];
+        *reinterpret_cast<u32x4*>(slot + S::MAT_BYTES + t * RPL * D * 2 + lane * 16) = pre[LPM + t];
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
+    }
     const bool need_mask = tree_chunk || gc * 32 + 32 > L;
     chunk_step<D, QBW>(slot, qf, anc_q, acc, m_run, l_run, a.scale_log2, need_mask, tree_chunk,
                        tree_bit0, prefix_mask8(gc * 32 + 8 * g, L));
-    if (i + 1 < my_chunks) {
+    if (i + 1 < my_chunks && !(i == 0 && pre2)) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
       if (i + 1 < my_n)
         issue(gc + NWAVE);
