@@ -1116,7 +1116,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
   // prefix tiles go out first; the tree tile needs kv_len
   const int n_pro = min(NBUF - 1, n_my);
   for (int j = 0; j < min(n_pro, n_pre); ++j) issue(j);
-  L = a.kv_len[u.b];
+  L = load_uniform(a.kv_len + u.b);  // scalar: no wait for the tiles in flight
   u.bad = L < 0 || L > Lp;
   if (u.bad) {
     L = 0;
