@@ -290,6 +290,63 @@ EAGLE_API eagle_status_t eagle_feature_gather(const void* features, const int32_
                                               int64_t row_bytes, void* out, int32_t* seq_flags,
                                               void* stream);
 
+/*
+ * EAGLE-2 dynamic draft tree (EAGLE-2 overview blog, §1 and §4 EAGLE vs
+ * EAGLE-2): the tree grows layer by layer from the draft model's
+ * confidences.  A node's value is the product of the draft probabilities
+ * along its path; each layer expands the k most valuable nodes of the layer
+ * before into their k most probable next tokens, and a final rerank keeps
+ * the N most valuable nodes (the root always) as the tree to verify.
+ *
+ * The created nodes of a sequence live in caller-owned device arrays of T
+ * entries each: created_parent [B, T] int32, created_token [B, T] int32,
+ * created_value [B, T] fp32.  Node 0 is the root (parent -1, value 1, token
+ * = the last committed token, written by the caller); nodes are numbered in
+ * creation order.  A driver runs: expand the root (R = 1), then per layer
+ * select the layer's k best, run the draft model on them, expand them; then
+ * rerank.  Values are fp32 products, ties go to the lower token id
+ * (expansion) or node id (selection, rerank).  Asynchronous on `stream`;
+ * argument errors return before anything is enqueued.
+ */
+
+/*
+ * Expansion: for sequence b and row r < R, the k tokens with the largest
+ * q[b, r, :] (ties: lower token id) become created nodes base + r*k + j,
+ * j = 0..k-1 in decreasing probability, with parent parent_node[b, r], that
+ * token, and value parent_value[b, r] * q[b, r, token].
+ *   q device [B, R, V] fp32 draft distributions (finite), V <= 32768
+ *   parent_node, parent_value device [B, R]
+ *   1 <= k <= V, base + R * k <= T
+ */
+EAGLE_API eagle_status_t eagle_dtree_expand(const float* q, int B, int R, int V, int k,
+                                       const int32_t* parent_node, const float* parent_value,
+                                       int32_t* created_parent, int32_t* created_token,
+                                       float* created_value, int T, int base, void* stream);
+
+/*
+ * Selection: out_node[b, 0..k-1] = the k created nodes among ids
+ * [first, first + M) with the largest value (ties: lower id), most valuable
+ * first; out_value their values.  1 <= k <= M <= 2048, first + M <= T.
+ */
+EAGLE_API eagle_status_t eagle_dtree_select(const float* created_value, int B, int T, int first, int M,
+                                       int k, int32_t* out_node, float* out_value, void* stream);
+
+/*
+ * Rerank: keep node 0 and the N - 1 nodes of ids [1, T_used) with the
+ * largest value (ties: lower id), renumbered in creation order (so parents
+ * precede children and shallower nodes come first).  Writes parents [B, N]
+ * (new numbering, parents[b, 0] = -1), tokens [B, N] and kept_node [B, N]
+ * (each kept node's created id, to gather its draft row or features).  A
+ * kept node whose parent was not kept (impossible when values never grow
+ * down a path) is hung off the root and sets EAGLE_FLAG_BAD_PARENT in
+ * seq_flags (device [B] int32 or NULL).  1 <= N <= 64, N <= T_used <= T,
+ * T_used <= 2049.
+ */
+EAGLE_API eagle_status_t eagle_dtree_rerank(const int32_t* created_parent, const int32_t* created_token,
+                                       const float* created_value, int B, int T, int T_used,
+                                       int N, int32_t* parents, int32_t* tokens,
+                                       int32_t* kept_node, int32_t* seq_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,3 +35,4 @@ from .vocab import argmax_lowest, target_distribution  # noqa: F401
 from .walk import (NEAR_TIE, WalkResult, inverse_cdf, node_round,  # noqa: F401
                    verify_batch, verify_sequence)
 from .compact import feature_gather, kv_compact  # noqa: F401
+from . import dynamic_tree  # noqa: F401

@@ -202,3 +202,25 @@ def test_feature_gather_argument_errors():
     # out overlapping features: 2 * 8 * 256 bytes from 0x100000
     assert call(out=ctypes.c_void_p(0x100000 + 4000)) == binding.EAGLE_ERR_INVALID_ARGUMENT
     assert call(row=1 << 40) == binding.EAGLE_ERR_INVALID_ARGUMENT  # N * row_bytes too large
+
+
+def test_dynamic_tree_argument_errors():
+    L = ev.lib()
+    E = binding.EAGLE_ERR_INVALID_ARGUMENT
+    # expand(q, B, R, V, k, parent_node, parent_value, cpar, ctok, cval, T, base, stream)
+    ex = lambda B=1, R=1, V=100, k=10, T=64, base=1, q=FAKE: L.eagle_dtree_expand(
+        q, B, R, V, k, FAKE, FAKE, FAKE, FAKE, FAKE, T, base, None)
+    assert ex(B=0) == binding.EAGLE_OK
+    assert ex(k=0) == E and ex(k=101) == E and ex(V=40000) == E
+    assert ex(base=60) == E          # base + R*k > T
+    assert ex(q=None) == E
+    # select(cval, B, T, first, M, k, out_node, out_value, stream)
+    se = lambda B=1, T=64, first=1, M=20, k=5: L.eagle_dtree_select(FAKE, B, T, first, M, k, FAKE,
+                                                                     FAKE, None)
+    assert se(B=0) == binding.EAGLE_OK
+    assert se(k=21) == E and se(M=3000) == E and se(first=50) == E
+    # rerank(cpar, ctok, cval, B, T, T_used, N, parents, tokens, kept, flags, stream)
+    rr = lambda B=1, T=64, used=40, N=26: L.eagle_dtree_rerank(FAKE, FAKE, FAKE, B, T, used, N, FAKE,
+                                                               FAKE, FAKE, None, None)
+    assert rr(B=0) == binding.EAGLE_OK
+    assert rr(N=65) == E and rr(used=20) == E and rr(used=70) == E

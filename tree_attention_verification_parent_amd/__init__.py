@@ -6,8 +6,8 @@ through the C ABI declared in include/eagle_verify.h and bound here with
 ctypes (binding.py).  Build with `python -m
 tree_attention_verification_parent_amd.build`.
 """
-from .binding import (EagleError, abi_version, alloc_workspace, feature_gather, kv_compact,  # noqa: F401
-                      lib,
+from .binding import (EagleError, abi_version, alloc_workspace, dtree_expand,  # noqa: F401
+                      dtree_rerank, dtree_select, feature_gather, kv_compact, lib,
                       tree_attn, tree_attn_parents, tree_attn_workspace_bytes, tree_build,
                       validate_tree_host,
                       verify_accept, verify_accept_compact, verify_accept_workspace_bytes,

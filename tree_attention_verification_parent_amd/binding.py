@@ -60,6 +60,9 @@ _SIGNATURES = {
                                          _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P, _P]),
     "eagle_kv_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "eagle_feature_gather": (_I, [_P, _P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]),
+    "eagle_dtree_expand": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P]),
+    "eagle_dtree_select": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "eagle_dtree_rerank": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
 }
 
 
@@ -297,3 +300,55 @@ def feature_gather(features, path, accept_len, *, out=None, seq_flags=None, stre
         _ptr(accept_len, torch.int32, "accept_len"), B, N, row_bytes, _ptr(out, None, "out"),
         _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
     return out
+
+
+# ---- EAGLE-2 dynamic tree: created nodes are [B, T] arrays (parent, token, value)
+def dtree_expand(q, parent_node, parent_value, k, created_parent, created_token, created_value,
+                 base, *, stream=None):
+    """Children of the R expanded rows of q [B, R, V]: created nodes
+    base + r*k + j take the row's j-th most probable token (ties: lower id),
+    parent parent_node[b, r] and value parent_value[b, r] * q[b, r, token]."""
+    B, R, V = q.shape
+    T = created_parent.shape[1]
+    _check(lib().eagle_dtree_expand(
+        _ptr(q, torch.float32, "q"), B, R, V, k, _ptr(parent_node, torch.int32, "parent_node"),
+        _ptr(parent_value, torch.float32, "parent_value"),
+        _ptr(created_parent, torch.int32, "created_parent"),
+        _ptr(created_token, torch.int32, "created_token"),
+        _ptr(created_value, torch.float32, "created_value"), T, base, _stream(stream)))
+
+
+def dtree_select(created_value, first, count, k, *, out_node=None, out_value=None, stream=None):
+    """The k most valuable created nodes among ids [first, first + count)
+    (ties: lower id), most valuable first: (node ids [B, k], values [B, k])."""
+    B, T = created_value.shape
+    dev = created_value.device
+    if out_node is None:
+        out_node = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out_value is None:
+        out_value = torch.empty((B, k), dtype=torch.float32, device=dev)
+    _check(lib().eagle_dtree_select(
+        _ptr(created_value, torch.float32, "created_value"), B, T, first, count, k,
+        _ptr(out_node, torch.int32, "out_node"), _ptr(out_value, torch.float32, "out_value"),
+        _stream(stream)))
+    return out_node, out_value
+
+
+def dtree_rerank(created_parent, created_token, created_value, used, N, *, seq_flags=None,
+                 stream=None):
+    """Keep the root and the N - 1 most valuable of created nodes [1, used),
+    renumbered in creation order: (parents [B, N], tokens [B, N], kept created
+    ids [B, N])."""
+    B, T = created_parent.shape
+    dev = created_parent.device
+    parents = torch.empty((B, N), dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    kept = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check(lib().eagle_dtree_rerank(
+        _ptr(created_parent, torch.int32, "created_parent"),
+        _ptr(created_token, torch.int32, "created_token"),
+        _ptr(created_value, torch.float32, "created_value"), B, T, used, N,
+        _ptr(parents, torch.int32, "parents"), _ptr(tokens, torch.int32, "tokens"),
+        _ptr(kept, torch.int32, "kept"), _ptr(seq_flags, torch.int32, "seq_flags"),
+        _stream(stream)))
+    return parents, tokens, kept

@@ -23,7 +23,8 @@ LIB_NAME = "libeagle_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "tree_build.hip", "tree_attn.hip", "verify.hip", "kv_compact.hip"]
+SOURCES = ["abi.cpp", "tree_build.hip", "tree_attn.hip", "verify.hip", "kv_compact.hip",
+           "dynamic_tree.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

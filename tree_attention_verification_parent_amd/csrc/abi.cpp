@@ -284,4 +284,56 @@ eagle_status_t eagle_feature_gather(const void* features, const int32_t* path,
                     "feature gather launch");
 }
 
+eagle_status_t eagle_dtree_expand(const float* q, int B, int R, int V, int k, const int32_t* parent_node,
+                             const float* parent_value, int32_t* created_parent,
+                             int32_t* created_token, float* created_value, int T, int base,
+                             void* stream) {
+  if (B < 0 || R < 1 || V < 1 || V > 32768 || k < 1 || k > V || base < 0 || T < 1)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT,
+                "eagle_dtree_expand: need B >= 0, R >= 1, 1 <= V <= 32768, 1 <= k <= V, base >= 0 "
+                "(got B=%d R=%d V=%d k=%d base=%d)", B, R, V, k, base);
+  if ((long long)base + (long long)R * k > T)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_expand: base + R*k = %lld exceeds T = %d",
+                (long long)base + (long long)R * k, T);
+  if ((double)B * R > 2.0e9) return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_expand: B * R too large");
+  if (B == 0) return EAGLE_OK;
+  if (!q || !parent_node || !parent_value || !created_parent || !created_token || !created_value)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_expand: NULL pointer");
+  return hip_status(eagle::launch_eagle2_expand(q, B, R, V, k, parent_node, parent_value,
+                                                created_parent, created_token, created_value, T,
+                                                base, as_stream(stream)),
+                    "eagle_dtree_expand launch");
+}
+
+eagle_status_t eagle_dtree_select(const float* created_value, int B, int T, int first, int M, int k,
+                             int32_t* out_node, float* out_value, void* stream) {
+  if (B < 0 || first < 0 || M < 1 || M > 2048 || k < 1 || k > M || (long long)first + M > T)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT,
+                "eagle_dtree_select: need B >= 0, 1 <= k <= M <= 2048, 0 <= first, first + M <= T "
+                "(got B=%d T=%d first=%d M=%d k=%d)", B, T, first, M, k);
+  if (B == 0) return EAGLE_OK;
+  if (!created_value || !out_node || !out_value)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_select: NULL pointer");
+  return hip_status(eagle::launch_eagle2_select(created_value, B, T, first, M, k, out_node,
+                                                out_value, as_stream(stream)),
+                    "eagle_dtree_select launch");
+}
+
+eagle_status_t eagle_dtree_rerank(const int32_t* created_parent, const int32_t* created_token,
+                             const float* created_value, int B, int T, int T_used, int N,
+                             int32_t* parents, int32_t* tokens, int32_t* kept_node,
+                             int32_t* seq_flags, void* stream) {
+  if (B < 0 || !tree_size_ok(N) || T_used < N || T_used > T || T_used > 2049)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT,
+                "eagle_dtree_rerank: need B >= 0, 1 <= N <= 64, N <= T_used <= min(T, 2049) "
+                "(got B=%d T=%d T_used=%d N=%d)", B, T, T_used, N);
+  if (B == 0) return EAGLE_OK;
+  if (!created_parent || !created_token || !created_value || !parents || !tokens || !kept_node)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_rerank: NULL pointer");
+  return hip_status(eagle::launch_eagle2_rerank(created_parent, created_token, created_value, B, T,
+                                                T_used, N, parents, tokens, kept_node, seq_flags,
+                                                as_stream(stream)),
+                    "eagle_dtree_rerank launch");
+}
+
 }  // extern "C"

@@ -78,4 +78,16 @@ hipError_t launch_feature_gather(const void* features, const int32_t* path,
                                  const int32_t* accept_len, int B, int N, int64_t row_bytes,
                                  void* out, int32_t* flags, hipStream_t s);
 
+// EAGLE-2 dynamic tree --------------------------------------------------------
+hipError_t launch_eagle2_expand(const float* q, int B, int R, int V, int k,
+                                const int32_t* parent_node, const float* parent_value,
+                                int32_t* cpar, int32_t* ctok, float* cval, int T, int base,
+                                hipStream_t s);
+hipError_t launch_eagle2_select(const float* cval, int B, int T, int first, int M, int k,
+                                int32_t* out_node, float* out_value, hipStream_t s);
+hipError_t launch_eagle2_rerank(const int32_t* cpar, const int32_t* ctok, const float* cval,
+                                int B, int T, int T_used, int N, int32_t* parents,
+                                int32_t* tokens, int32_t* kept_node, int32_t* flags,
+                                hipStream_t s);
+
 }  // namespace eagle
