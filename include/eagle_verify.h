@@ -316,7 +316,7 @@ EAGLE_API eagle_status_t eagle_feature_gather(const void* features, const int32_
  * token, and value parent_value[b, r] * q[b, r, token].
  *   q device [B, R, V] fp32 draft distributions (finite), V <= 32768
  *   parent_node, parent_value device [B, R]
- *   1 <= k <= V, base + R * k <= T
+ *   1 <= k <= min(V, 64), base + R * k <= T
  */
 EAGLE_API eagle_status_t eagle_dtree_expand(const float* q, int B, int R, int V, int k,
                                        const int32_t* parent_node, const float* parent_value,

@@ -212,6 +212,7 @@ def test_dynamic_tree_argument_errors():
         q, B, R, V, k, FAKE, FAKE, FAKE, FAKE, FAKE, T, base, None)
     assert ex(B=0) == binding.EAGLE_OK
     assert ex(k=0) == E and ex(k=101) == E and ex(V=40000) == E
+    assert ex(V=1000, k=65, T=2000) == E  # at most 64 children per row
     assert ex(base=60) == E          # base + R*k > T
     assert ex(q=None) == E
     # select(cval, B, T, first, M, k, out_node, out_value, stream)

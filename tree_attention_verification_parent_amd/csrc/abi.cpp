@@ -288,9 +288,9 @@ eagle_status_t eagle_dtree_expand(const float* q, int B, int R, int V, int k, co
                              const float* parent_value, int32_t* created_parent,
                              int32_t* created_token, float* created_value, int T, int base,
                              void* stream) {
-  if (B < 0 || R < 1 || V < 1 || V > 32768 || k < 1 || k > V || base < 0 || T < 1)
+  if (B < 0 || R < 1 || V < 1 || V > 32768 || k < 1 || k > V || k > 64 || base < 0 || T < 1)
     return fail(EAGLE_ERR_INVALID_ARGUMENT,
-                "eagle_dtree_expand: need B >= 0, R >= 1, 1 <= V <= 32768, 1 <= k <= V, base >= 0 "
+                "eagle_dtree_expand: need B >= 0, R >= 1, 1 <= V <= 32768, 1 <= k <= min(V, 64), base >= 0 "
                 "(got B=%d R=%d V=%d k=%d base=%d)", B, R, V, k, base);
   if ((long long)base + (long long)R * k > T)
     return fail(EAGLE_ERR_INVALID_ARGUMENT, "eagle_dtree_expand: base + R*k = %lld exceeds T = %d",

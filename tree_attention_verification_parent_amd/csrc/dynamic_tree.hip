@@ -9,16 +9,20 @@
 // follow their parent rows in order, each row's by decreasing probability);
 // ties go to the lower token id (expansion) or node id (selection, rerank).
 //
-// All three steps are top-k selections over (value, id) pairs, done as k
-// rounds of a workgroup maximum over 64-bit keys that order by value, then
-// by lower id: every thread keeps the largest of its keys below the last one
-// taken, and only the thread whose key was taken looks again.
+// All three steps are top-k selections over (value, id) pairs, compared as
+// 64-bit keys that order by value, then by lower id.  Over a vocabulary row
+// (expansion) the k keys come in k rounds of a workgroup maximum: every
+// thread keeps the largest of its keys below the last one taken, and only
+// the thread whose key was taken looks again.  Over at most 2048 created
+// nodes (selection, rerank) each key's rank is counted against all the keys
+// in LDS, and the keys of rank below k are the selection.
 #include "common.h"
 #include "launch.h"
 
 namespace eagle {
 
-constexpr int kTreeBlock = 1024;
+constexpr int kTreeBlock = 1024;   // selection and rerank
+constexpr int kExpandBlock = 512;  // expansion: two waves per SIMD keep each round short
 
 // Larger value first, then lower id (ids below 2^31); key 0 is below every
 // real key and marks "none".
@@ -35,19 +39,40 @@ __device__ __forceinline__ int key_id(unsigned long long key) {
   return 0x7fffffff - (int)(uint32_t)key;
 }
 
-// Workgroup maximum; `red` holds two sets of per-wave slots used in turn, so
-// one barrier per call suffices.
+// One DPP step of a 64-bit maximum (both halves moved by the same lane
+// permutation, compared as one key).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long x) {
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)x);
+  const unsigned long long y = ((unsigned long long)hi << 32) | lo;
+  return y > x ? y : x;
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long x, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Workgroup maximum: within a wave by DPP row steps and the four rows' lanes,
+// then across the NW waves through LDS; `red` holds two sets of per-wave
+// slots used in turn, so one barrier per call suffices.
+template <int NW>
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long x,
                                                             unsigned long long* red, int turn) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const unsigned long long y = __shfl_xor(x, o);
-    x = y > x ? y : x;
+  x = dpp_max_u64<kDppXor1>(x);
+  x = dpp_max_u64<kDppXor2>(x);
+  x = dpp_max_u64<kDppHalfMirror>(x);
+  x = dpp_max_u64<kDppMirror>(x);
+  {
+    const unsigned long long a = lane_u64(x, 0), b = lane_u64(x, 16);
+    const unsigned long long c = lane_u64(x, 32), d = lane_u64(x, 48);
+    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
+    x = ab > cd ? ab : cd;
   }
-  constexpr int NW = kTreeBlock / 64;
   unsigned long long* slot = red + (turn & 1) * NW;
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  __syncthreads();
+  barrier_lds();  // orders LDS only: no wait for this workgroup's global stores
   unsigned long long m = slot[0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) m = slot[i] > m ? slot[i] : m;
@@ -55,72 +80,115 @@ __device__ __forceinline__ unsigned long long block_max_key(unsigned long long x
 }
 
 // The k largest keys of the workgroup, largest first: emit(j, key) on every
-// thread for j = 0.. until k keys or no key is left.
-template <int EPT, typename Emit>
-__device__ __forceinline__ void block_topk(const unsigned long long (&key)[EPT], int k,
-                                           unsigned long long* red, Emit&& emit) {
-  unsigned long long m = 0;
+// thread for j = 0.. until k keys or no key is left.  A thread offers its
+// largest key not yet taken (m1) and keeps its second largest (m2) ready, so
+// it rescans its keys only when it wins a third time or more.
+template <int BLOCK, int EPT, typename KeyAt, typename Emit>
+__device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long long* red,
+                                           Emit&& emit) {
+  unsigned long long m1 = 0, m2 = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) m = key[e] > m ? key[e] : m;
+  for (int e = 0; e < EPT; ++e) {
+    const unsigned long long x = key_at(e);
+    if (x > m1) {
+      m2 = m1;
+      m1 = x;
+    } else if (x > m2) {
+      m2 = x;
+    }
+  }
+  bool m2_ready = true;
   for (int j = 0; j < k; ++j) {
-    const unsigned long long best = block_max_key(m, red, j);
+    const unsigned long long best = block_max_key<BLOCK / 64>(m1, red, j);
     if (best == 0) break;  // uniform: fewer than k keys
     emit(j, best);
-    if (m == best) {  // keys are distinct: only this thread held it
-      m = 0;
+    // keys are distinct: only one thread held it; the other waves skip this
+    // with a wave-uniform branch (predicated, the rescan cost every wave)
+    const bool won = m1 == best;
+    if (__ballot(won)) {
+      if (won) {
+        if (m2_ready) {
+          m1 = m2;  // the largest below best
+          m2_ready = false;
+        } else {
+          m1 = 0;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if (key[e] < best && key[e] > m) m = key[e];
+          for (int e = 0; e < EPT; ++e) {
+            const unsigned long long x = key_at(e);
+            if (x < best && x > m1) m1 = x;
+          }
+        }
+      }
     }
   }
 }
 
-// Expansion: one workgroup per (sequence, row); the row's V <= 32768
-// probabilities in registers (32 per thread).
-__global__ __launch_bounds__(kTreeBlock) void eagle2_expand_kernel(
+// Expansion: one workgroup per (sequence, row); the keys of the row's
+// V <= 32768 probabilities in registers (64 per thread).
+__global__ __launch_bounds__(kExpandBlock) void eagle2_expand_kernel(
     const float* __restrict__ q, int R, int V, int k, const int32_t* __restrict__ parent_node,
     const float* __restrict__ parent_value, int32_t* __restrict__ cpar,
     int32_t* __restrict__ ctok, float* __restrict__ cval, int T, int base) {
-  constexpr int EPT = 32768 / kTreeBlock;
-  __shared__ unsigned long long red[2 * kTreeBlock / 64];
+  constexpr int EPT = 32768 / kExpandBlock;
+  __shared__ unsigned long long red[2 * kExpandBlock / 64];
+  __shared__ unsigned long long taken[64];
   const int row = blockIdx.x;
   const int b = row / R, r = row - b * R;
   const float* qr = q + (size_t)row * V;
+  // every load in flight before any is used (a guarded load each waited for)
   unsigned long long key[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int t = e * kTreeBlock + threadIdx.x;
-    key[e] = t < V ? vkey(qr[t], t) : 0ull;
+    const float x = qr[min(e * kExpandBlock + (int)threadIdx.x, V - 1)];
+    key[e] = __float_as_uint(x);  // every load in flight first, keys formed below
   }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int t = e * kExpandBlock + threadIdx.x;
+    key[e] = t < V ? vkey(__uint_as_float((uint32_t)key[e]), t) : 0ull;
+  }
+  auto key_at = [&](int e) { return key[e]; };
   const float pv = parent_value[row];
   const int pn = parent_node[row];
-  block_topk<EPT>(key, k, red, [&](int j, unsigned long long best) {
-    if (threadIdx.x == 0) {
-      const size_t c = (size_t)b * T + base + r * k + j;
-      cpar[c] = pn;
-      ctok[c] = key_id(best);
-      cval[c] = pv * key_value(best);
-    }
+  block_topk<kExpandBlock, EPT>(key_at, k, red, [&](int j, unsigned long long best) {
+    if (threadIdx.x == 0) taken[j] = best;
   });
+  barrier_lds();
+  // the children, written once all are known (k <= 64)
+  if (threadIdx.x < k) {
+    const unsigned long long best = taken[threadIdx.x];
+    const size_t c = (size_t)b * T + base + r * k + threadIdx.x;
+    cpar[c] = pn;
+    ctok[c] = key_id(best);
+    cval[c] = pv * key_value(best);
+  }
+}
+
+// The keys of ids [first, first + M) (M <= 2048) of one sequence's values
+// into LDS, then emit(rank, key) for every key of rank below k (its rank =
+// the number of larger keys; keys are distinct).
+template <typename Emit>
+__device__ __forceinline__ void rank_select(const float* vals, int first, int M, int k,
+                                            unsigned long long* skey, Emit&& emit) {
+  for (int i = threadIdx.x; i < M; i += kTreeBlock) skey[i] = vkey(vals[first + i], first + i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < M; i += kTreeBlock) {
+    const unsigned long long mine = skey[i];
+    int rank = 0;
+    for (int j = 0; j < M; ++j) rank += skey[j] > mine;
+    if (rank < k) emit(rank, mine);
+  }
 }
 
 // Selection: one workgroup per sequence over ids [first, first + M), M <= 2048.
 __global__ __launch_bounds__(kTreeBlock) void eagle2_select_kernel(
     const float* __restrict__ cval, int T, int first, int M, int k, int32_t* __restrict__ out_node,
     float* __restrict__ out_value) {
-  __shared__ unsigned long long red[2 * kTreeBlock / 64];
+  __shared__ unsigned long long skey[2048];
   const int b = blockIdx.x;
-  unsigned long long key[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int i = e * kTreeBlock + threadIdx.x;
-    key[e] = i < M ? vkey(cval[(size_t)b * T + first + i], first + i) : 0ull;
-  }
-  block_topk<2>(key, k, red, [&](int j, unsigned long long best) {
-    if (threadIdx.x == 0) {
-      out_node[(size_t)b * k + j] = key_id(best);
-      out_value[(size_t)b * k + j] = key_value(best);
-    }
+  rank_select(cval + (size_t)b * T, first, M, k, skey, [&](int rank, unsigned long long key) {
+    out_node[(size_t)b * k + rank] = key_id(key);
+    out_value[(size_t)b * k + rank] = key_value(key);
   });
 }
 
@@ -130,23 +198,14 @@ __global__ __launch_bounds__(kTreeBlock) void eagle2_rerank_kernel(
     const int32_t* __restrict__ cpar, const int32_t* __restrict__ ctok,
     const float* __restrict__ cval, int T, int T_used, int N, int32_t* __restrict__ parents,
     int32_t* __restrict__ tokens, int32_t* __restrict__ kept_node, int32_t* __restrict__ flags) {
-  __shared__ unsigned long long red[2 * kTreeBlock / 64];
+  __shared__ unsigned long long skey[2048];
   __shared__ int sel[64];
   __shared__ int order[64];
   const int b = blockIdx.x;
   const size_t cb = (size_t)b * T;
-  const int M = T_used - 1;
-  unsigned long long key[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int i = e * kTreeBlock + threadIdx.x;
-    key[e] = i < M ? vkey(cval[cb + 1 + i], 1 + i) : 0ull;
-  }
-  if (threadIdx.x < 64) sel[threadIdx.x] = 0;  // the root, and padding if fewer nodes
-  __syncthreads();
-  block_topk<2>(key, N - 1, red, [&](int j, unsigned long long best) {
-    if (threadIdx.x == 0) sel[1 + j] = key_id(best);
-  });
+  if (threadIdx.x == 0) sel[0] = 0;  // the root
+  rank_select(cval + cb, 1, T_used - 1, N - 1, skey,
+              [&](int rank, unsigned long long key) { sel[1 + rank] = key_id(key); });
   __syncthreads();
   const int lane = threadIdx.x;
   // new id = number of kept ids below this one (kept ids are distinct)
@@ -181,7 +240,7 @@ hipError_t launch_eagle2_expand(const float* q, int B, int R, int V, int k,
                                 const int32_t* parent_node, const float* parent_value,
                                 int32_t* cpar, int32_t* ctok, float* cval, int T, int base,
                                 hipStream_t s) {
-  eagle2_expand_kernel<<<dim3((unsigned)(B * R)), kTreeBlock, 0, s>>>(
+  eagle2_expand_kernel<<<dim3((unsigned)(B * R)), kExpandBlock, 0, s>>>(
       q, R, V, k, parent_node, parent_value, cpar, ctok, cval, T, base);
   return hipGetLastError();
 }
