@@ -202,6 +202,50 @@ def measure_feature_gather(torch, ev, W, steps):
             "bytes_per_launch": nbytes, "achieved_GBs": nbytes / t / 1e9, "bound": "latency"}
 
 
+def measure_dynamic_tree(torch, ev, W, steps):
+    """The EAGLE-2 tree built on the GPU at the mixtral-eagle2 shape (16
+    sequences, top-10 expansion, depth 6, 60 nodes, V = 32000): root
+    expansion, then five rounds of select + expand, then the rerank; the
+    draft rows of every layer resident in HBM (the drafter that would produce
+    them is outside this library).  `steps` builds in one graph."""
+    cfg = W.get("mixtral-eagle2")
+    B, V, k, depth, N = cfg.B, cfg.V, cfg.topk, cfg.max_depth, cfg.N
+    d = torch.device("cuda")
+    gen = torch.Generator(device=d).manual_seed(7)
+    rows = [torch.rand((B, 1 if i == 0 else k, V), device=d, generator=gen) for i in range(depth)]
+    rows = [r / r.sum(dim=2, keepdim=True) for r in rows]
+    T = 1 + k + (depth - 1) * k * k
+    cp = torch.full((B, T), -1, dtype=torch.int32, device=d)
+    ct = torch.zeros((B, T), dtype=torch.int32, device=d)
+    cv = torch.ones((B, T), dtype=torch.float32, device=d)
+    root = torch.zeros((B, 1), dtype=torch.int32, device=d)
+    one = torch.ones((B, 1), dtype=torch.float32, device=d)
+    sel_n = torch.empty((B, k), dtype=torch.int32, device=d)
+    sel_v = torch.empty((B, k), dtype=torch.float32, device=d)
+
+    def build(_):
+        used, first, count = 1, 0, 1
+        for i in range(depth):
+            if i == 0:
+                ev.dtree_expand(rows[0], root, one, k, cp, ct, cv, used)
+                R = 1
+            else:
+                ev.dtree_select(cv, first, count, k, out_node=sel_n, out_value=sel_v)
+                ev.dtree_expand(rows[i], sel_n, sel_v, k, cp, ct, cv, used)
+                R = k
+            first, count = used, R * k
+            used += R * k
+        ev.dtree_rerank(cp, ct, cv, used, N)
+    n = max(1, steps // 10)
+    g = graph_of(torch, build, n)
+    time_graph(torch, g)
+    t = time_graph(torch, g) / n
+    nbytes = sum(r.numel() for r in rows) * 4
+    return {"us": t * 1e6, "batch": B, "topk": k, "depth": depth, "nodes": N, "vocab": V,
+            "launches": 2 * depth, "draft_row_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
+            "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+
 def pmc_capture(torch, ev, W, steps):
     """Eager steps at T=1 over the rotation, then the calibration copy."""
     cfg = W.get(WORKLOAD)
@@ -297,6 +341,7 @@ def main():
     achieved = attn_bytes / r1["t_attn"] / 1e9
     vocab_bytes = r1["walk_bytes"]  # target rows + the draft row of every rejected candidate
     fg = measure_feature_gather(torch, ev, W, args.steps)
+    dtree = measure_dynamic_tree(torch, ev, W, args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -333,7 +378,7 @@ def main():
                "attn_us": r0["t_attn"] * 1e6, "verify_us": r0["t_verify"] * 1e6,
                "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
-        "next_rows": {"feature_gather": fg},
+        "next_rows": {"feature_gather": fg, "dynamic_tree": dtree},
     }
     print(json.dumps(line), flush=True)
 
