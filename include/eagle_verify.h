@@ -18,7 +18,13 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Layouts are row-major and contiguous, as annotated [outer, ..., inner].
  *   - Tree topology: node 0 is the root (parent -1); for i >= 1,
- *     0 <= parent[i] < i.  N counts the root, 1 <= N <= 64.
+ *     0 <= parent[i] < i.  N counts the root, 1 <= N <= 64.  A batch of
+ *     trees of different sizes (ragged batch) pads each smaller tree with
+ *     absent nodes, parent[i] = -1 for i >= 1: an absent node is nobody's
+ *     parent or child, is never tested and never on a path; its ancestor set
+ *     is itself (depth 0), so its attention row is that of a lone node and
+ *     its token, draft row and uniform are not read by the walk.  A present
+ *     node whose parent is absent is a data error (EAGLE_FLAG_BAD_PARENT).
  *   - Host-detectable errors (null pointers, bad sizes, unsupported shapes,
  *     a too-small workspace) return a non-zero status before anything is
  *     enqueued; eagle_last_error() then describes it (thread-local).
@@ -147,7 +153,8 @@ EAGLE_API eagle_status_t eagle_tree_attn(const uint16_t* q, const uint16_t* k_ca
  * itself, so `out` is bit-identical to eagle_tree_attn with the masks that
  * eagle_tree_build returns for the same parents.
  *
- *   parents  device [B, N] int32 (root parent -1, 0 <= parents[i] < i)
+ *   parents  device [B, N] int32 (root parent -1, 0 <= parents[i] < i,
+ *            or -1 for an absent node)
  *   anc, depth, pos  device [B, N] out or NULL each: the builder's outputs,
  *            as eagle_tree_build defines them (pos = kv_len + depth), written
  *            once per sequence by the kernel

@@ -3,7 +3,10 @@
 The draft tree is verified in one target forward, each node attending to the
 committed context and to its own ancestors (EAGLE-p2 §3 EAGLE: tree
 attention; A.1 Tree Structure: disabling the tree gives a chain).  Node 0 is
-the root, and parent[i] < i for every other node.
+the root, and parent[i] < i for every other node.  A batch of trees of
+different sizes (ragged batch) pads the smaller ones with absent nodes,
+marked by parent -1: an absent node is nobody's parent or child, so it is
+never verified; its ancestor set is itself alone.
 
 Everything here chases parent pointers explicitly, one node at a time.
 """
@@ -13,10 +16,19 @@ import numpy as np
 
 
 def validate_parents(parents_row) -> bool:
+    """Root first; every other node's parent is an earlier present node, or
+    -1 for an absent node."""
     p = [int(x) for x in parents_row]
     if len(p) == 0 or p[0] != -1:
         return False
-    return all(0 <= p[i] < i for i in range(1, len(p)))
+    present = [True] + [p[i] != -1 for i in range(1, len(p))]
+    return all(p[i] == -1 or (0 <= p[i] < i and present[p[i]]) for i in range(1, len(p)))
+
+
+def present_nodes(parents_row) -> list:
+    """Node ids that are part of the tree (the root and every node with a parent)."""
+    p = [int(x) for x in parents_row]
+    return [i for i in range(len(p)) if i == 0 or p[i] != -1]
 
 
 def ancestors(parents_row) -> list:

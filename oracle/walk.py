@@ -99,9 +99,15 @@ def inverse_cdf(dist, u: float):
 
 
 def _children(parents_row):
+    """Children of every node in ascending id; absent nodes (parent -1) are
+    nobody's child."""
+    from .tree import validate_parents
+    if not validate_parents(parents_row):
+        raise ValueError("invalid parent array")
     ch = [[] for _ in range(len(parents_row))]
     for i in range(1, len(parents_row)):
-        ch[int(parents_row[i])].append(i)
+        if int(parents_row[i]) != -1:
+            ch[int(parents_row[i])].append(i)
     return ch
 
 
@@ -110,7 +116,7 @@ def verify_sequence(tokens, draft_probs, target_logits, parents, L, T, uniforms)
     at T = 0, may be None), target_logits [N, V], parents [N], uniforms [N]."""
     N, V = target_logits.shape
     for i in range(1, N):
-        if not (0 <= int(tokens[i]) < V):
+        if int(parents[i]) != -1 and not (0 <= int(tokens[i]) < V):
             raise ValueError(f"token {tokens[i]} of node {i} outside the vocabulary")
     ch = _children(parents)
     u = [float(x) for x in uniforms]

@@ -46,6 +46,12 @@ def test_validate_tree_host():
         ev.validate_tree_host([[0, 0]])
     with pytest.raises(ev.EagleError):
         ev.validate_tree_host(np.full((1, 65), 0, dtype=np.int32))
+    # ragged batches: -1 marks an absent node, which cannot be a parent
+    ev.validate_tree_host([[-1, 0, -1, 1, -1]])
+    with pytest.raises(ev.EagleError, match="absent"):
+        ev.validate_tree_host([[-1, -1, 1]])
+    with pytest.raises(ev.EagleError):
+        ev.validate_tree_host([[-1, 0, -2]])
 
 
 def _status(fn, *args):

@@ -680,3 +680,70 @@ def test_feature_gather_flags_bad_paths():
     assert torch.equal(got[:4].view(torch.int16), out0[:4].view(torch.int16))
     assert torch.equal(got[4, :3].view(torch.int16), feats[4, [0, 2, 5]].view(torch.int16))
     assert torch.equal(got[4, 3:].view(torch.int16), out0[4, 3:].view(torch.int16))
+
+
+# ---------------------------------------------------------------- ragged batches
+def _ragged_step(cfg, T, sizes, seed):
+    """A batch whose sequences' trees have `sizes` nodes, padded to cfg.N with
+    absent nodes (parent -1) spread between the present ones."""
+    rng = np.random.default_rng(seed)
+    parents = np.full((cfg.B, cfg.N), -1, dtype=np.int32)
+    for b, n in enumerate(sizes):
+        small = trees.random_tree(rng, n, 5)
+        ids = np.r_[0, np.sort(rng.choice(np.arange(1, cfg.N), size=n - 1, replace=False))]
+        for k in range(1, n):
+            parents[b, ids[k]] = ids[small[k]]
+    return W.make_step(cfg, T, seed=seed, parents=parents)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2)])
+def test_ragged_attention_and_tree_build(Hq, Hkv):
+    """Present nodes attend to the prefix and their ancestors, absent ones to
+    the prefix and themselves; no flags; ring (MHA) and group (GQA) kernels."""
+    cfg = W.shrink(W.get(1), B=4, N=26, L=300, Hq=Hq, Hkv=Hkv, V=16)
+    s = _ragged_step(cfg, 1.0, [26, 1, 9, 17], seed=Hq)
+    say(f"ragged attention Hq={Hq} Hkv={Hkv}")
+    got = _fused_vs_two_calls(s)
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    assert np.abs(got - ref).max() < ATOL_ATTN
+    anc, depth, _ = ev.tree_build(dev(s.parents), dev(s.kv_len))
+    assert np.array_equal(anc.cpu().numpy().view(np.uint64), oracle.ancestor_masks(s.parents))
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_ragged_walk_and_compaction(T):
+    """The walk never tests an absent node; outputs bit-exact against the oracle
+    (near ties excused), and the fused compaction matches the oracle's."""
+    cfg = W.shrink(W.get(1), B=5, N=26, L=64, V=300)
+    s = _ragged_step(cfg, T, [26, 1, 5, 12, 20], seed=int(T) + 40)
+    # absent nodes get tokens outside the vocabulary: never read, never flagged
+    absent = (s.parents == -1) & (np.arange(cfg.N)[None] > 0)
+    s.tokens[absent] = -5
+    flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    say(f"ragged walk T={T}")
+    res = run_verify(s, flags=flags)
+    assert not flags.cpu().numpy().any()
+    walks = oracle_walks(s)
+    compared, excused = compare_walks(res, s, walks)
+    say(f"  compared {compared}, excused {excused}")
+    ratio = res["ratio"]
+    assert np.isnan(ratio[absent]).all()
+    k3, v3 = bf(s.k_cache).clone(), bf(s.v_cache).clone()
+    fused = ev.verify_accept_compact(dev(s.tokens), None if s.draft_probs is None else dev(s.draft_probs),
+                                     dev(s.target_logits), dev(s.parents), dev(s.kv_len), T,
+                                     dev(s.uniforms), k3, v3)
+    torch.cuda.synchronize()
+    kr, vr, nl = oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, res["kv_src"], res["accept_len"])
+    assert np.array_equal(k3.view(torch.int16).cpu().numpy().view(np.uint16), kr)
+    assert np.array_equal(fused["new_kv_len"].cpu().numpy(), nl)
+
+
+def test_node_under_absent_parent_is_flagged():
+    cfg = W.shrink(W.get(0), B=2, N=6, V=16)
+    s = W.make_step(cfg, 1.0, seed=3)
+    parents = np.array([[-1, 0, -1, 2, 1, 0], [-1, 0, -1, 1, -1, 3]], dtype=np.int32)
+    flags = torch.zeros(2, dtype=torch.int32, device="cuda")
+    say("node under an absent parent")
+    ev.tree_build(dev(parents), dev(s.kv_len), seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [ev.binding.FLAG_BAD_PARENT, 0]

@@ -48,10 +48,14 @@ eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B, int N) {
   for (int b = 0; b < B; ++b) {
     const int32_t* p = parents + (size_t)b * N;
     if (p[0] != -1) return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents[%d, 0] = %d, expected -1", b, p[0]);
-    for (int i = 1; i < N; ++i)
+    for (int i = 1; i < N; ++i) {
+      if (p[i] == -1) continue;  // absent node (ragged batch padding)
       if (p[i] < 0 || p[i] >= i)
         return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents[%d, %d] = %d violates 0 <= parent < %d", b,
                     i, p[i], i);
+      if (p[i] > 0 && p[p[i]] == -1)
+        return fail(EAGLE_ERR_INVALID_ARGUMENT, "parents[%d, %d] = %d is an absent node", b, i, p[i]);
+    }
   }
   return EAGLE_OK;
 }

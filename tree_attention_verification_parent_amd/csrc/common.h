@@ -139,9 +139,11 @@ __device__ __forceinline__ void wave_allsum_n(float (&v)[M]) {
 // node i, N <= 64), from the sequence's parent array (EAGLE, paperlayer.ai
 // summary, A.1 Tree Structure: each node attends to its ancestors).  Pointer
 // jumping: after r rounds a lane has OR-ed in the masks of its 2^r nearest
-// ancestors, so 6 rounds cover any depth below 64.  A malformed link (root
-// with a parent, or a parent not below the node) is reported in `bad` and
-// replaced by the root, keeping every mask in range.  Every lane of the wave
+// ancestors, so 6 rounds cover any depth below 64.  Parent -1 marks an absent
+// node (padding of a smaller tree in a ragged batch): its set is itself
+// alone, depth 0.  A malformed link (root with a parent, a parent not below
+// the node) is reported in `bad` and replaced by the root, keeping every mask
+// in range; a present node under an absent one is reported too.  Every lane of the wave
 // must call it (cross-lane shuffles); lanes >= N return an empty set.
 struct TreeLinks {
   uint64_t anc;
@@ -158,10 +160,10 @@ __device__ __forceinline__ TreeLinks tree_links_wave(const int32_t* parents_b, i
     if (lane == 0) {
       bad = par != -1;
       par = -1;
-    } else if (par < 0 || par >= lane) {
+    } else if (par != -1 && (par < 0 || par >= lane)) {
       bad = true;
       par = 0;
-    }
+    }  // par == -1: an absent node (ragged batch padding), its own ancestor only
   }
   uint64_t a = live ? (1ull << lane) : 0ull;
   int cnt = par >= 0 ? 1 : 0;
@@ -178,6 +180,8 @@ __device__ __forceinline__ TreeLinks tree_links_wave(const int32_t* parents_b, i
       jump = jump_j;
     }
   }
+  // a present node must reach the root; one under an absent node does not
+  if (live && lane > 0 && par >= 0 && !(a & 1ull)) bad = true;
   return TreeLinks{a, cnt, bad};
 }
 

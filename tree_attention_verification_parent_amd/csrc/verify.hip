@@ -1128,12 +1128,15 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
     Lkv = a.kv_len[b];
     if (tid == 0) sh.Lkv = Lkv;
     int par = a.parents[ob + tid];
-    if (tid == 0 || par < 0 || par >= tid) par = tid == 0 ? -1 : 0;
+    if (tid == 0)
+      par = -1;
+    else if (par != -1 && (par < 0 || par >= tid))
+      par = 0;  // a bad link hangs off the root; -1 (absent node) is nobody's child
     const int tk = a.tokens[ob + tid];
     sh.par[tid] = par;
     sh.tok[tid] = tk;
     sh.u[tid] = a.uniforms[ob + tid];
-    tok_bad = tid > 0 && (tk < 0 || tk >= V);
+    tok_bad = tid > 0 && par != -1 && (tk < 0 || tk >= V);
   }
   if (j == 0 && part == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
     atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);

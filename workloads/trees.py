@@ -100,17 +100,27 @@ def static_tree(rng: np.random.Generator, n: int, max_depth: int) -> np.ndarray:
 
 
 def children_lists(parents) -> list:
+    """Children of every node; absent nodes (parent -1, ragged padding) have none
+    and are nobody's child."""
     parents = np.asarray(parents)
     ch = [[] for _ in range(len(parents))]
     for i in range(1, len(parents)):
-        ch[int(parents[i])].append(i)
+        if int(parents[i]) != -1:
+            ch[int(parents[i])].append(i)
     return ch
 
 
 def check_tree(parents) -> None:
+    """Node 0 the root; every other node's parent an earlier present node, or
+    -1 for an absent node (padding of a smaller tree in a ragged batch)."""
     parents = np.asarray(parents)
     if parents.ndim != 1 or len(parents) == 0 or parents[0] != -1:
         raise ValueError("node 0 must be the root with parent -1")
     for i in range(1, len(parents)):
-        if not (0 <= parents[i] < i):
-            raise ValueError(f"parent[{i}]={parents[i]} violates 0 <= parent < index")
+        p = int(parents[i])
+        if p == -1:
+            continue
+        if not (0 <= p < i):
+            raise ValueError(f"parent[{i}]={p} violates 0 <= parent < index")
+        if p > 0 and int(parents[p]) == -1:
+            raise ValueError(f"parent[{i}]={p} is an absent node")
