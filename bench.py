@@ -18,7 +18,9 @@ one JSON line on stdout.
 
 `--pmc-capture` runs the same steps eagerly (no graph) followed by a
 calibration copy of known size, for rocprofv3 counter passes; it prints one
-JSON line naming what it ran and does not time anything.
+JSON line naming what it ran and does not time anything.  `--profile
+attn:<config>` / `--profile dtree` run the tree attention at another
+configuration, or the EAGLE-2 tree build, eagerly for a kernel trace.
 """
 from __future__ import annotations
 
@@ -246,6 +248,35 @@ def measure_dynamic_tree(torch, ev, W, steps):
             "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
+def profile_run(torch, ev, W, name, steps):
+    """Eager launches of one workload for a rocprofv3 kernel trace (nothing is
+    timed here): `attn:<config>` runs the tree attention with the mask built in
+    at that configuration, rotating input copies as the timed runs do;
+    `dtree` runs the EAGLE-2 tree build at the mixtral-eagle2 shape."""
+    if name == "dtree":
+        measure_dynamic_tree(torch, ev, W, max(10, steps))
+    elif name.startswith("attn:"):
+        cfg = W.get(name[5:])
+        s = W.make_step(cfg, cfg.temperatures[-1])
+        d = torch.device("cuda")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+        bf = lambda a: t(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        q, k, v = bf(s.q), bf(s.k_cache), bf(s.v_cache)
+        copies = max(2, math.ceil(ROTATE_BYTES / cfg.attn_bytes()))
+        slots = [(q.clone(), k.clone(), v.clone()) for _ in range(copies)]
+        parents, kv_len = t(s.parents), t(s.kv_len)
+        ws = ev.alloc_workspace(ev.tree_attn_workspace_bytes(cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.d,
+                                                             s.Lmax))
+        out = torch.empty_like(q)
+        for i in range(steps):
+            qq, kk, vv = slots[i % copies]
+            ev.tree_attn_parents(qq, kk, vv, kv_len, parents, out=out, workspace=ws)
+    else:
+        raise SystemExit(f"unknown profile workload {name}")
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": name, "steps": steps}), flush=True)
+
+
 def pmc_capture(torch, ev, W, steps):
     """Eager steps at T=1 over the rotation, then the calibration copy."""
     cfg = W.get(WORKLOAD)
@@ -315,6 +346,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-capture", action="store_true")
+    ap.add_argument("--profile", default=None,
+                    help="attn:<config> or dtree: eager launches for a rocprofv3 trace")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification step is built and timed "
@@ -332,6 +365,9 @@ def main():
     ev.lib()
     if args.pmc_capture:
         pmc_capture(torch, ev, W, args.steps)
+        return
+    if args.profile:
+        profile_run(torch, ev, W, args.profile, args.steps)
         return
     r1 = measure(torch, ev, W, 1.0, args.steps, args.warmup)
     r0 = measure(torch, ev, W, 0.0, args.steps, args.warmup)
