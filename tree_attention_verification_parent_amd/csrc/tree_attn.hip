@@ -1208,12 +1208,21 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
 }
 
 // ============================================================================
-// merge (tile variants): one wave per query row combines the splits' partials
+// merge (group and tile kernels): the splits' partials of a query row combined
 // ============================================================================
+// A thread per 16-byte column of a row (D / 4 threads per row): it loads the
+// log2-sum-exp and the O / l column of every split, eight splits at a time
+// with every load of a batch issued before any is used, rescales online, and
+// writes four bf16 outputs.
 template <int D>
-__device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, int RW) {
-  constexpr int PL = D / 64;  // 1 or 2 elements per lane
-  const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
+  constexpr int C4 = D / 4;        // 16-byte columns per row
+  constexpr int RPB = 256 / C4;    // rows per workgroup
+  const int grow = blockIdx.x * RPB + threadIdx.x / C4;  // row over units x RW
+  const int d4 = threadIdx.x % C4;
+  const int unit = grow / RW;
+  if (unit >= a.units) return;
+  const int rl = grow - unit * RW;
   const int qgroup = unit % a.qgroups;
   const int pair = unit / a.qgroups;
   const int kvh = pair % a.Hkv;
@@ -1225,44 +1234,39 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int unit, int rl, i
   const int S = a.splits;
   const size_t base = (size_t)unit * S * RW + rl;
   const int L = a.kv_len[b];
-  const float lse = lane < S ? a.part_lse[base + (size_t)lane * RW] : -INFINITY;
   const bool bad = L < 0 || L > a.Lmax - a.N;
-  const float m = wave_max(lse);
-  const float mu0 = m == -INFINITY ? 0.f : m;
-  const float w = __builtin_amdgcn_exp2f(lse - mu0);
-  const float l = wave_sum_f(w);
-  float o[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) o[e] = 0.f;
-  for (int sp0 = 0; sp0 < S; sp0 += 8) {
-    float v[8][PL];
+  float mt = -INFINITY, lt = 0.f;
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float ls[8];
+    f32x4 os[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float* src = a.part_o + (base + (size_t)(sp0 + q) * RW) * D + lane * PL;
-#pragma unroll
-      for (int e = 0; e < PL; ++e) v[q][e] = sp0 + q < S ? src[e] : 0.f;
+      const bool in = s0 + q < S;
+      const size_t r = base + (size_t)(in ? s0 + q : 0) * RW;  // in range either way
+      ls[q] = in ? a.part_lse[r] : -INFINITY;
+      os[q] = in ? *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float mb = mt;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mb = fmaxf(mb, ls[q]);
+    if (mb == -INFINITY) continue;
+    const float f = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt - mb);
+    lt *= f;
+    o *= f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float wq = __shfl(w, (sp0 + q) & 63);
-#pragma unroll
-      for (int e = 0; e < PL; ++e) o[e] += sp0 + q < S ? wq * v[q][e] : 0.f;
+      const float w = ls[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[q] - mb);
+      lt += w;
+      o += os[q] * w;
     }
+    mt = mb;
   }
-  const float inv = (bad || l == 0.f) ? 0.f : 1.f / l;
-  uint16_t* orow = a.out + (((size_t)b * a.N + i) * a.Hq + h) * D + lane * PL;
-  if constexpr (PL == 2)
-    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  else
-    orow[0] = float_to_bf16_bits(o[0] * inv);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
-  const int grow = blockIdx.x * 4 + (threadIdx.x >> 6);  // global row over units x RW
-  const int unit = grow / RW;
-  if (unit >= a.units) return;
-  merge_row<D>(a, unit, grow - unit * RW, RW);
+  const float inv = (bad || lt == 0.f) ? 0.f : 1.f / lt;
+  uint16_t* orow = a.out + (((size_t)b * a.N + i) * a.Hq + h) * D + 4 * d4;
+  *reinterpret_cast<u32x2*>(orow) =
+      u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
 }
 
 // ---- variants ----------------------------------------------------------------
@@ -1428,7 +1432,8 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   // ring variants combine their splits in the kernel
   if (err != hipSuccess || plan.splits == 1 || ring) return err;
   const int rw = plan.rows_per_wg;
-  const dim3 mgrid((unsigned)((plan.units * rw + 3) / 4));
+  const int rows_per_block = 256 / (plan.d / 4);
+  const dim3 mgrid((unsigned)((plan.units * rw + rows_per_block - 1) / rows_per_block));
   if (plan.d == 64)
     tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a, rw);
   else
