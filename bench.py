@@ -153,6 +153,8 @@ def measure(torch, ev, W, T, steps, warmup):
     g_step = graph_of(torch, st.run, steps)
     time_graph(torch, g_warm)
     t_step = time_graph(torch, g_step) / steps
+    # spread: the mean step of a few more replays of the same graph
+    replays = sorted(time_graph(torch, g_step) / steps for _ in range(5))
     acc = st.res["accept_len"].cpu().numpy()
     # candidates the walk tested (ratio is NaN for untested nodes): every
     # rejected one costs its draft row on top of the target rows
@@ -161,6 +163,22 @@ def measure(torch, ev, W, T, steps, warmup):
                          st.uniforms, want_ratio=True)
     tested = int((~torch.isnan(o["ratio"])).sum().item())
     rejected = tested - int(o["accept_len"].sum().item())
+    # acceptance rate per depth: candidates tested at depth d (T > 0: their
+    # ratio is set; T = 0: the same candidates, taken from the walk's path)
+    depth = np.zeros(cfg.N, dtype=np.int64)
+    par = s.parents[0]
+    for i in range(1, cfg.N):
+        depth[i] = depth[par[i]] + 1
+    ratio = o["ratio"].cpu().numpy()
+    path = o["path"].cpu().numpy()
+    m = o["accept_len"].cpu().numpy()
+    alpha = {}
+    for b in range(cfg.B):
+        on = set(int(x) for x in path[b, :m[b] + 1])
+        for c in range(1, cfg.N):
+            if not np.isnan(ratio[b, c]):
+                t, a_ = alpha.get(int(depth[c]), (0, 0))
+                alpha[int(depth[c])] = (t + 1, a_ + (c in on))
     # attention alone and the walk alone, same rotation, back-to-back launches
     # in one graph each
     g_attn = graph_of(torch, st.attention, steps)
@@ -171,6 +189,7 @@ def measure(torch, ev, W, T, steps, warmup):
     t_ver = time_graph(torch, g_ver) / steps
     walk_bytes = cfg.vocab_bytes() + (4 * cfg.V * rejected if T > 0 else 0)
     return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, t_verify=t_ver, accept_len=int(acc[0]),
+                replays=replays, alpha={d: {"tested": t, "accepted": a_} for d, (t, a_) in sorted(alpha.items())},
                 copies=copies, walk_bytes=walk_bytes, rejected=rejected)
 
 
@@ -313,6 +332,7 @@ def cpu_baseline(W, T, budget_s=12.0):
         oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
         walks = oracle.verify_batch(s.tokens, s.draft_probs, s.target_logits, s.parents, s.kv_len,
                                     T, s.uniforms)
+        near_ties = sum(len(w.near_ties) for w in walks)
         a = as_arrays(walks, cfg.N)
         oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, a["kv_src"], a["accept_len"])
         done += 1
@@ -323,7 +343,8 @@ def cpu_baseline(W, T, budget_s=12.0):
     return dict(value=cfg.B * cfg.N * done / el, unit="tokens/s", cores=int(blas_threads),
                 kind="oracle",
                 sample=f"{done} whole steps of the {cfg.name} workload at T={T} "
-                       f"(fp64 NumPy oracle, {el:.1f} s)")
+                       f"(fp64 NumPy oracle, {el:.1f} s)",
+                near_ties_per_step=near_ties)
 
 
 def pmc_traffic(attn_bytes):
@@ -414,6 +435,10 @@ def main():
                "attn_us": r0["t_attn"] * 1e6, "verify_us": r0["t_verify"] * 1e6,
                "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
+        "ms_per_step_replays": [t * 1e3 for t in r1["replays"]],
+        "accepted_tokens_per_s": {"t1": cfg.B * (r1["accept_len"] + 1) / r1["t_step"],
+                                  "t0": cfg.B * (r0["accept_len"] + 1) / r0["t_step"]},
+        "alpha_per_depth": {"t1": r1["alpha"], "t0": r0["alpha"]},
         "next_rows": {"feature_gather": fg, "dynamic_tree": dtree},
     }
     print(json.dumps(line), flush=True)
