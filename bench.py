@@ -267,11 +267,22 @@ def measure_dynamic_tree(torch, ev, W, steps):
             "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
+def calibration_copy(torch):
+    """torch.neg over COPY_BYTES in and out: the known-size kernel that scales
+    the FETCH_SIZE / WRITE_SIZE readings of the same run."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
 def profile_run(torch, ev, W, name, steps):
-    """Eager launches of one workload for a rocprofv3 kernel trace (nothing is
-    timed here): `attn:<config>` runs the tree attention with the mask built in
-    at that configuration, rotating input copies as the timed runs do;
-    `dtree` runs the EAGLE-2 tree build at the mixtral-eagle2 shape."""
+    """Eager launches of one workload for rocprofv3 (nothing is timed here):
+    `attn:<config>` runs the tree attention with the mask built in at that
+    configuration, rotating input copies as the timed runs do, then the
+    calibration copy for counter passes; `dtree` runs the EAGLE-2 tree build
+    at the mixtral-eagle2 shape."""
     if name == "dtree":
         measure_dynamic_tree(torch, ev, W, max(10, steps))
     elif name.startswith("attn:"):
@@ -290,6 +301,8 @@ def profile_run(torch, ev, W, name, steps):
         for i in range(steps):
             qq, kk, vv = slots[i % copies]
             ev.tree_attn_parents(qq, kk, vv, kv_len, parents, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        calibration_copy(torch)
     else:
         raise SystemExit(f"unknown profile workload {name}")
     torch.cuda.synchronize()
@@ -305,11 +318,7 @@ def pmc_capture(torch, ev, W, steps):
     for i in range(steps):
         st.run(i)
     torch.cuda.synchronize()
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.neg(src, out=dst)
-    torch.cuda.synchronize()
+    calibration_copy(torch)
     print(json.dumps({"pmc_capture": cfg.name, "steps": steps, "copy_bytes": COPY_BYTES}),
           flush=True)
 
