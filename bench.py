@@ -153,8 +153,15 @@ def measure(torch, ev, W, T, steps, warmup):
     g_step = graph_of(torch, st.run, steps)
     time_graph(torch, g_warm)
     t_step = time_graph(torch, g_step) / steps
-    # spread: the mean step of a few more replays of the same graph
+    # spread: the mean step of a few more replays of the same graph, and the
+    # p10 / p50 / p90 of the mean step over 20 replays of a 10-step graph
     replays = sorted(time_graph(torch, g_step) / steps for _ in range(5))
+    chunk = min(10, steps)
+    g_chunk = graph_of(torch, st.run, chunk)
+    time_graph(torch, g_chunk)
+    per = np.array([time_graph(torch, g_chunk) / chunk for _ in range(20)])
+    spread = {"p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
+              "p90": float(np.percentile(per, 90))}
     acc = st.res["accept_len"].cpu().numpy()
     # candidates the walk tested (ratio is NaN for untested nodes): every
     # rejected one costs its draft row on top of the target rows
@@ -189,7 +196,7 @@ def measure(torch, ev, W, T, steps, warmup):
     t_ver = time_graph(torch, g_ver) / steps
     walk_bytes = cfg.vocab_bytes() + (4 * cfg.V * rejected if T > 0 else 0)
     return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, t_verify=t_ver, accept_len=int(acc[0]),
-                replays=replays, alpha={d: {"tested": t, "accepted": a_} for d, (t, a_) in sorted(alpha.items())},
+                replays=replays, spread=spread, alpha={d: {"tested": t, "accepted": a_} for d, (t, a_) in sorted(alpha.items())},
                 copies=copies, walk_bytes=walk_bytes, rejected=rejected)
 
 
@@ -336,14 +343,22 @@ def cpu_baseline(W, T, budget_s=12.0):
     cfg = W.get(WORKLOAD)
     s = W.make_step(cfg, T)
     done = 0
+    stage = {"tree_attention": 0.0, "verify": 0.0, "kv_compact": 0.0}
     t0 = time.perf_counter()
     while True:
+        ta = time.perf_counter()
         oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+        tb = time.perf_counter()
         walks = oracle.verify_batch(s.tokens, s.draft_probs, s.target_logits, s.parents, s.kv_len,
                                     T, s.uniforms)
         near_ties = sum(len(w.near_ties) for w in walks)
         a = as_arrays(walks, cfg.N)
+        tc = time.perf_counter()
         oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, a["kv_src"], a["accept_len"])
+        td = time.perf_counter()
+        stage["tree_attention"] += tb - ta
+        stage["verify"] += tc - tb
+        stage["kv_compact"] += td - tc
         done += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -353,7 +368,8 @@ def cpu_baseline(W, T, budget_s=12.0):
                 kind="oracle",
                 sample=f"{done} whole steps of the {cfg.name} workload at T={T} "
                        f"(fp64 NumPy oracle, {el:.1f} s)",
-                near_ties_per_step=near_ties)
+                near_ties_per_step=near_ties,
+                ms_per_stage={k: 1e3 * v / done for k, v in stage.items()})
 
 
 def pmc_traffic(attn_bytes):
@@ -445,6 +461,7 @@ def main():
                "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
         "ms_per_step_replays": [t * 1e3 for t in r1["replays"]],
+        "ms_per_step_p10_p50_p90": {k: v * 1e3 for k, v in r1["spread"].items()},
         "accepted_tokens_per_s": {"t1": cfg.B * (r1["accept_len"] + 1) / r1["t_step"],
                                   "t0": cfg.B * (r0["accept_len"] + 1) / r0["t_step"]},
         "alpha_per_depth": {"t1": r1["alpha"], "t0": r0["alpha"]},
