@@ -304,3 +304,30 @@ def test_batch_arrays_are_consistent():
         for k in range(1, m + 1):
             assert parents[b, r.path[k]] == r.path[k - 1]
             assert r.path[k] >= k
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_shared_row_residuals_have_closed_form(seed):
+    """Siblings drawn from one draft row q: after i rejections the adjusted
+    distribution is max(0, p - s_i q) / F(s_i), with F(s) = sum max(0, p - s q),
+    s_0 = 0 and s_{i+1} = s_i + F(s_i) (induction on the residual rule; a
+    residual that skipped the renormalisation, or subtracted q before
+    renormalising, breaks it).  With different rows per sibling it does not
+    hold, which the last check shows."""
+    rng = np.random.default_rng(seed)
+    V, k = 50, 6
+    p = rng.dirichlet(np.full(V, 0.3))
+    q = rng.dirichlet(np.full(V, 0.3))
+    _, states = oracle.node_round(p, list(range(k)), [q] * k)
+    F = lambda s: np.maximum(0.0, p - s * q).sum()
+    s = 0.0
+    for i in range(k + 1):
+        r, Z = states[i]
+        want = np.maximum(0.0, p - s * q)
+        np.testing.assert_allclose(r / Z, want / want.sum(), rtol=0, atol=1e-12)
+        s += F(s)
+    q2 = rng.dirichlet(np.full(V, 0.3))
+    _, states2 = oracle.node_round(p, [0, 1], [q, q2])
+    s2 = 1.0 + F(1.0)
+    want = np.maximum(0.0, p - s2 * q)
+    assert np.abs(states2[2][0] / states2[2][1] - want / want.sum()).max() > 1e-3
