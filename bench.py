@@ -397,7 +397,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification step is built and timed "
-              "on a single MI355X (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "on a single MI355X; sequences and KV heads would shard across GPUs with no "
+              "exchange, which is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
