@@ -230,6 +230,31 @@ def measure_feature_gather(torch, ev, W, steps):
             "bytes_per_launch": nbytes, "achieved_GBs": nbytes / t / 1e9, "bound": "latency"}
 
 
+def measure_stream_context(torch):
+    """Context for the roofline: what library kernels reach over 1 GiB on this
+    part (a copy, 1 GiB read + 1 GiB written; a sum, 1 GiB read), eager
+    launches timed with events (the launch overhead is under 0.1 %)."""
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: y.copy_(x), 2 << 30),
+                             ("sum", lambda: torch.sum(x), 1 << 30)):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 5
+        out[f"{name}_1GiB_GBs"] = nbytes / t / 1e9
+    del x, y
+    return out
+
+
 def measure_dynamic_tree(torch, ev, W, steps):
     """The EAGLE-2 tree built on the GPU at the mixtral-eagle2 shape (16
     sequences, top-10 expansion, depth 6, 60 nodes, V = 32000): root
@@ -425,6 +450,7 @@ def main():
     vocab_bytes = r1["walk_bytes"]  # target rows + the draft row of every rejected candidate
     fg = measure_feature_gather(torch, ev, W, args.steps)
     dtree = measure_dynamic_tree(torch, ev, W, args.steps)
+    stream = measure_stream_context(torch)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -450,6 +476,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic(attn_bytes),
                      "kernel": "tree_attn", "bytes_per_launch": attn_bytes,
                      "us_per_launch": r1["t_attn"] * 1e6},
+        "hbm_context": stream,
         "cpu_baseline": cpu,
         "kernels_us": {"tree_attn": r1["t_attn"] * 1e6, "verify_accept_compact": r1["t_verify"] * 1e6},
         "verify_roofline": {"bound": "hbm", "bytes_per_launch": vocab_bytes,
