@@ -747,3 +747,71 @@ def test_node_under_absent_parent_is_flagged():
     ev.tree_build(dev(parents), dev(s.kv_len), seq_flags=flags)
     torch.cuda.synchronize()
     assert flags.cpu().tolist() == [ev.binding.FLAG_BAD_PARENT, 0]
+
+
+# ---------------------------------------------------------------------------- caches past 2^31 elements
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8)], ids=["mha-ring", "gqa-group"])
+def test_cache_beyond_2g_elements(Hq, Hkv):
+    """K/V caches of 2 x 8 x (2^21 + N) x 128 bf16 (4.3 G elements, 8.6 GB each):
+    every head of sequence 1 starts past element 2^31, so an offset computed in
+    32 bits would read or write the wrong place.  Attention rows of both
+    sequences against the oracle on the heads' slices, then a compaction of
+    sequence 1 bit-exact against the oracle's."""
+    B, N, d = 2, 16, 128
+    Lmax = (1 << 21) + N
+    assert Hkv * Lmax * d >= 2 ** 31  # where sequence 1's first head starts
+    kv_len = np.array([700, 1234], dtype=np.int32)
+    rng = np.random.default_rng(2024)
+    parents = np.stack([trees.random_tree(rng, N, 5) for _ in range(B)])
+    say(f"cache beyond 2^31 elements: Hq {Hq} Hkv {Hkv} Lmax {Lmax}")
+    k = W.normal_bf16_device((B, Hkv, Lmax, d), 11)
+    v = W.normal_bf16_device((B, Hkv, Lmax, d), 12)
+    q = W.normal_bf16_device((B, N, Hq, d), 13)
+    kv_t, par_t = dev(kv_len), dev(parents)
+    out = ev.tree_attn_parents(q, k, v, kv_t, par_t)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    G = Hq // Hkv
+    qb = bits(q)
+    err = 0.0
+    for b, kvh in [(0, 0), (1, 0), (1, Hkv // 2), (1, Hkv - 1)]:
+        L = int(kv_len[b])
+        ks = bits(k[b, kvh, :L + N])[None, None]
+        vs = bits(v[b, kvh, :L + N])[None, None]
+        qs = qb[b:b + 1, :, kvh * G:(kvh + 1) * G]
+        rows = [(0, i, g) for i in (0, N // 2, N - 1) for g in range(G)]
+        ref = oracle.tree_attention(qs, ks, vs, kv_len[b:b + 1], parents[b:b + 1], rows=rows)
+        sub = np.stack([got[b, i, kvh * G + g] for _, i, g in rows])
+        err = max(err, float(np.abs(sub - ref).max()))
+    say(f"  sampled max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+    # compaction of sequence 1 along its deepest root path (path[j] >= j)
+    depth = trees.depths_of(parents[1])
+    leaf = int(np.argmax(depth))
+    path = [leaf]
+    while path[-1] != 0:
+        path.append(int(parents[1][path[-1]]))
+    path = path[::-1]
+    m = len(path) - 1
+    kv_src = np.full((B, N), -1, dtype=np.int32)
+    kv_src[0, 0] = kv_len[0]
+    kv_src[1, :m + 1] = kv_len[1] + np.array(path, dtype=np.int32)
+    accept = np.array([0, m], dtype=np.int32)
+    L1 = int(kv_len[1])
+    lo, hi = L1 - 4, L1 + N
+    before_k = bits(k[1:2, :, lo:hi])
+    before_v = bits(v[1:2, :, lo:hi])
+    new_len = ev.kv_compact(k, v, kv_t, dev(kv_src), dev(accept))
+    torch.cuda.synchronize()
+    src_rel = kv_src[1:2].copy()
+    src_rel[0, :m + 1] -= lo
+    want_k, want_v, _ = oracle.kv_compact(before_k, before_v, np.array([L1 - lo], dtype=np.int32),
+                                          src_rel, accept[1:2])
+    np.testing.assert_array_equal(bits(k[1:2, :, lo:hi]), want_k)
+    np.testing.assert_array_equal(bits(v[1:2, :, lo:hi]), want_v)
+    assert new_len.cpu().numpy().tolist() == [int(kv_len[0]) + 1, L1 + m + 1]
+    say(f"  compaction of {m + 1} rows at slot {L1} bit-exact")
+    del k, v
+    torch.cuda.empty_cache()

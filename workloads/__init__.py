@@ -5,5 +5,6 @@ generation only (shapes, random draws, tree topologies), none of the
 verification arithmetic.
 """
 from .configs import CONFIGS, VerifyConfig, get  # noqa: F401
-from .generate import StepInputs, default_seed, f32_to_bf16_bits, make_step, shrink  # noqa: F401
+from .generate import (StepInputs, default_seed, f32_to_bf16_bits, make_step,  # noqa: F401
+                       normal_bf16_device, shrink)
 from . import trees  # noqa: F401

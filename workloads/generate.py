@@ -242,6 +242,16 @@ def make_step(cfg: VerifyConfig, T: float, seed: Optional[int] = None, *,
     return step
 
 
+def normal_bf16_device(shape, seed: int, device="cuda"):
+    """N(0, 1) bf16 tensor drawn on the device from a seeded torch generator:
+    for caches too large to draw on the host (several GiB).  Tests copy back
+    the slices the oracle needs."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.bfloat16)
+
+
 def shrink(cfg: VerifyConfig, **kw) -> VerifyConfig:
     """A copy of cfg with some fields replaced (smaller parity cases)."""
     return dataclasses.replace(cfg, **kw)
