@@ -815,3 +815,45 @@ def test_cache_beyond_2g_elements(Hq, Hkv):
     say(f"  compaction of {m + 1} rows at slot {L1} bit-exact")
     del k, v
     torch.cuda.empty_cache()
+
+
+def test_fused_compaction_cache_beyond_2g_elements():
+    """The walk with its fused compaction on caches of 2 x 8 x (2^21 + 26) x 128
+    bf16: walk outputs against the oracle (near ties excused), the moved rows
+    of both sequences bit-exact against the oracle's compaction of the walk's
+    own kv_src.  Small draft noise so the walks accept and rows move."""
+    Hkv, d = 8, 128
+    cfg = W.shrink(W.get(1), B=2, V=1000, Hq=Hkv, Hkv=Hkv, sigma_d=0.05)
+    N = cfg.N
+    Lmax = (1 << 21) + N
+    assert Hkv * Lmax * d >= 2 ** 31
+    s = W.make_step(cfg, 1.0, seed=77, with_attention=False, kv_lens=[900, 2047])
+    say(f"fused compaction, cache beyond 2^31 elements: Lmax {Lmax}")
+    k = W.normal_bf16_device((cfg.B, Hkv, Lmax, d), 21)
+    v = W.normal_bf16_device((cfg.B, Hkv, Lmax, d), 22)
+    lo = [int(L) - 4 for L in s.kv_len]
+    before = [(bits(k[b:b + 1, :, lo[b]:lo[b] + N + 4]), bits(v[b:b + 1, :, lo[b]:lo[b] + N + 4]))
+              for b in range(cfg.B)]
+    out = ev.verify_accept_compact(dev(s.tokens), dev(s.draft_probs), dev(s.target_logits),
+                                   dev(s.parents), dev(s.kv_len), s.T, dev(s.uniforms), k, v)
+    torch.cuda.synchronize()
+    gpu = {key: t.cpu().numpy() for key, t in out.items()}
+    compared, excused = compare_walks(gpu, s, oracle_walks(s))
+    say(f"  walks compared {compared}, excused {excused}, accept_len {gpu['accept_len'].tolist()}")
+    for b in range(cfg.B):
+        m = int(gpu["accept_len"][b])
+        src_rel = gpu["kv_src"][b:b + 1].copy()
+        src_rel[0, :m + 1] -= lo[b]
+        want_k, want_v, _ = oracle.kv_compact(before[b][0], before[b][1],
+                                              np.array([4], dtype=np.int32), src_rel,
+                                              gpu["accept_len"][b:b + 1])
+        np.testing.assert_array_equal(bits(k[b:b + 1, :, lo[b]:lo[b] + N + 4]), want_k)
+        np.testing.assert_array_equal(bits(v[b:b + 1, :, lo[b]:lo[b] + N + 4]), want_v)
+    assert gpu["new_kv_len"].tolist() == [int(s.kv_len[b]) + int(gpu["accept_len"][b]) + 1
+                                          for b in range(cfg.B)]
+    moved = int(sum((gpu["path"][b, 1:gpu["accept_len"][b] + 1]
+                     != np.arange(1, gpu["accept_len"][b] + 1)).sum() for b in range(cfg.B)))
+    say(f"  moved rows {moved}")
+    assert moved > 0
+    del k, v
+    torch.cuda.empty_cache()
