@@ -231,3 +231,38 @@ def test_dynamic_tree_argument_errors():
                                                                FAKE, FAKE, None, None)
     assert rr(B=0) == binding.EAGLE_OK
     assert rr(N=65) == E and rr(used=20) == E and rr(used=70) == E
+
+
+def test_binding_rejects_mis_sized_tensors_on_the_host():
+    """Shapes are checked before any pointer is taken: a buffer smaller than
+    the sizes passed with it would be indexed out of its bounds."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((1, 4, 2, 64), dtype=bf)
+    k = torch.zeros((1, 2, 100, 64), dtype=bf)
+    kv_len = torch.zeros(1, dtype=torch.int32)
+    parents = torch.zeros((1, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="v_cache"):
+        ev.tree_attn_parents(q, k, torch.zeros((1, 2, 99, 64), dtype=bf), kv_len, parents)
+    with pytest.raises(ValueError, match="kv_len"):
+        ev.tree_attn_parents(q, k, k, torch.zeros(2, dtype=torch.int32), parents)
+    with pytest.raises(ValueError, match="parents"):
+        ev.tree_attn_parents(q, k, k, kv_len, torch.zeros((1, 5), dtype=torch.int32))
+    with pytest.raises(ValueError, match="k_cache"):
+        ev.tree_attn(q, torch.zeros((1, 2, 100, 128), dtype=bf), k, kv_len,
+                     torch.zeros((1, 4), dtype=torch.int64))
+    logits = torch.zeros((1, 4, 10), dtype=torch.float32)
+    toks = torch.zeros((1, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="uniforms"):
+        ev.verify_accept(toks, logits, logits, parents, kv_len, 1.0, torch.zeros((1, 3)))
+    with pytest.raises(ValueError, match="draft_probs"):
+        ev.verify_accept(toks, torch.zeros((1, 4, 9)), logits, parents, kv_len, 1.0,
+                         torch.zeros((1, 4)))
+    with pytest.raises(ValueError, match="accept_len"):
+        ev.kv_compact(k, k, kv_len, toks, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="accept_len"):
+        ev.feature_gather(torch.zeros((1, 4, 16)), toks, torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="parent_node"):
+        ev.dtree_expand(torch.zeros((1, 2, 10)), torch.zeros((1, 3), dtype=torch.int32),
+                        torch.zeros((1, 2)), 2, torch.zeros((1, 8), dtype=torch.int32),
+                        torch.zeros((1, 8), dtype=torch.int32), torch.zeros((1, 8)), 1)

@@ -104,6 +104,23 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor"):
     return t.data_ptr()
 
 
+def _expect(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """The kernels index these buffers by the sizes passed beside them, so a
+    tensor of another shape would be read or written out of its bounds."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_cache(q, k_cache, v_cache, kv_len, seq_flags):
+    B, N, Hq, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"k_cache must be [B, Hkv, Lmax, d] with B = {B}, d = {d}, "
+                         f"got {tuple(k_cache.shape)}")
+    _expect(v_cache, k_cache.shape, "v_cache")
+    _expect(kv_len, (B,), "kv_len")
+    _expect(seq_flags, (B,), "seq_flags")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -133,6 +150,10 @@ def tree_build(parents: torch.Tensor, kv_len: Optional[torch.Tensor] = None, *, 
                depth=None, pos=None, seq_flags=None, stream=None):
     """Ancestor masks (int64 tensor holding the uint64 bits), depth and position ids."""
     B, N = parents.shape
+    _expect(kv_len, (B,), "kv_len")
+    for t, name in ((anc, "anc"), (depth, "depth"), (pos, "pos")):
+        _expect(t, (B, N), name)
+    _expect(seq_flags, (B,), "seq_flags")
     if anc is None:
         anc = torch.empty((B, N), dtype=torch.int64, device=parents.device)
         depth = torch.empty((B, N), dtype=torch.int32, device=parents.device)
@@ -159,6 +180,9 @@ def tree_attn(q, k_cache, v_cache, kv_len, anc, *, sm_scale: float = 0.0, out=No
               workspace=None, seq_flags=None, stream=None):
     """q [B,N,Hq,d] bf16; k/v [B,Hkv,Lmax,d] bf16; kv_len [B] int32; anc [B,N] int64."""
     B, N, Hq, d = q.shape
+    _check_cache(q, k_cache, v_cache, kv_len, seq_flags)
+    _expect(anc, (B, N), "anc")
+    _expect(out, q.shape, "out")
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
     if out is None:
         out = torch.empty_like(q)
@@ -179,6 +203,10 @@ def tree_attn_parents(q, k_cache, v_cache, kv_len, parents, *, sm_scale: float =
     """Tree mask built from parents [B,N] int32 inside the attention launch; anc [B,N] int64,
     depth and pos [B,N] int32 are optional outputs.  Returns out."""
     B, N, Hq, d = q.shape
+    _check_cache(q, k_cache, v_cache, kv_len, seq_flags)
+    for t, name in ((parents, "parents"), (anc, "anc"), (depth, "depth"), (pos, "pos")):
+        _expect(t, (B, N), name)
+    _expect(out, q.shape, "out")
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
     if out is None:
         out = torch.empty_like(q)
@@ -195,6 +223,22 @@ def tree_attn_parents(q, k_cache, v_cache, kv_len, parents, *, sm_scale: float =
     return out
 
 
+def _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
+                       outputs, seq_flags):
+    B, N, V = target_logits.shape
+    for t, name in ((draft_tokens, "draft_tokens"), (parents, "parents"), (uniforms, "uniforms")):
+        _expect(t, (B, N), name)
+    _expect(draft_probs, (B, N, V), "draft_probs")
+    _expect(kv_len, (B,), "kv_len")
+    _expect(seq_flags, (B,), "seq_flags")
+    shapes = {"accept_len": (B,), "bonus": (B,), "new_kv_len": (B,), "path": (B, N),
+              "accepted_tokens": (B, N), "kv_src": (B, N), "ratio": (B, N),
+              "probs": (B, N, V), "final_dist": (B, V)}
+    for key, t in (outputs or {}).items():
+        if key in shapes:
+            _expect(t, shapes[key], key)
+
+
 def verify_accept_workspace_bytes(B, N, V) -> int:
     return int(lib().eagle_verify_accept_workspace(B, N, V))
 
@@ -204,6 +248,8 @@ def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, tem
                   workspace=None, seq_flags=None, stream=None):
     """Acceptance walk; returns a dict of device tensors (see include/eagle_verify.h)."""
     B, N, V = target_logits.shape
+    _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
+                       outputs, seq_flags)
     dev = target_logits.device
     o = outputs or {}
     if not o:
@@ -238,6 +284,12 @@ def verify_accept_compact(draft_tokens, draft_probs, target_logits, parents, kv_
     """Acceptance walk and KV compaction in one launch; returns the walk's
     outputs (as verify_accept) plus "new_kv_len"."""
     B, N, V = target_logits.shape
+    _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
+                       outputs, seq_flags)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B:
+        raise ValueError(f"k_cache must be [B, Hkv, Lmax, d] with B = {B}, got {tuple(k_cache.shape)}")
+    _expect(v_cache, k_cache.shape, "v_cache")
+    _expect(new_kv_len, (B,), "new_kv_len")
     _, Hkv, Lmax, d = k_cache.shape
     dev = target_logits.device
     o = dict(outputs) if outputs else {}
@@ -271,7 +323,13 @@ def verify_accept_compact(draft_tokens, draft_probs, target_logits, parents, kv_
 def kv_compact(k_cache, v_cache, kv_len, kv_src, accept_len, *, new_kv_len=None, seq_flags=None,
                stream=None):
     B, Hkv, Lmax, d = k_cache.shape
+    if kv_src.dim() != 2 or kv_src.shape[0] != B:
+        raise ValueError(f"kv_src must be [B, N] with B = {B}, got {tuple(kv_src.shape)}")
     N = kv_src.shape[1]
+    _expect(v_cache, k_cache.shape, "v_cache")
+    for t, name in ((kv_len, "kv_len"), (accept_len, "accept_len"), (new_kv_len, "new_kv_len"),
+                    (seq_flags, "seq_flags")):
+        _expect(t, (B,), name)
     if new_kv_len is None:
         new_kv_len = torch.empty_like(kv_len)
     _check(lib().eagle_kv_compact(
@@ -290,6 +348,8 @@ def feature_gather(features, path, accept_len, *, out=None, seq_flags=None, stre
     B, N = path.shape
     if features.dim() < 2 or tuple(features.shape[:2]) != (B, N):
         raise ValueError(f"features must be [B, N, ...] with B, N = {B}, {N}")
+    _expect(accept_len, (B,), "accept_len")
+    _expect(seq_flags, (B,), "seq_flags")
     row_bytes = features[0, 0].numel() * features.element_size()
     if out is None:
         out = torch.empty_like(features)
@@ -309,7 +369,13 @@ def dtree_expand(q, parent_node, parent_value, k, created_parent, created_token,
     base + r*k + j take the row's j-th most probable token (ties: lower id),
     parent parent_node[b, r] and value parent_value[b, r] * q[b, r, token]."""
     B, R, V = q.shape
+    if created_parent.dim() != 2 or created_parent.shape[0] != B:
+        raise ValueError(f"created arrays must be [B, T] with B = {B}")
     T = created_parent.shape[1]
+    _expect(parent_node, (B, R), "parent_node")
+    _expect(parent_value, (B, R), "parent_value")
+    _expect(created_token, (B, T), "created_token")
+    _expect(created_value, (B, T), "created_value")
     _check(lib().eagle_dtree_expand(
         _ptr(q, torch.float32, "q"), B, R, V, k, _ptr(parent_node, torch.int32, "parent_node"),
         _ptr(parent_value, torch.float32, "parent_value"),
@@ -322,6 +388,8 @@ def dtree_select(created_value, first, count, k, *, out_node=None, out_value=Non
     """The k most valuable created nodes among ids [first, first + count)
     (ties: lower id), most valuable first: (node ids [B, k], values [B, k])."""
     B, T = created_value.shape
+    _expect(out_node, (B, k), "out_node")
+    _expect(out_value, (B, k), "out_value")
     dev = created_value.device
     if out_node is None:
         out_node = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -340,6 +408,9 @@ def dtree_rerank(created_parent, created_token, created_value, used, N, *, seq_f
     renumbered in creation order: (parents [B, N], tokens [B, N], kept created
     ids [B, N])."""
     B, T = created_parent.shape
+    _expect(created_token, (B, T), "created_token")
+    _expect(created_value, (B, T), "created_value")
+    _expect(seq_flags, (B,), "seq_flags")
     dev = created_parent.device
     parents = torch.empty((B, N), dtype=torch.int32, device=dev)
     tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
