@@ -21,6 +21,8 @@ calibration copy of known size, for rocprofv3 counter passes; it prints one
 JSON line naming what it ran and does not time anything.  `--profile
 attn:<config>` / `--profile dtree` run the tree attention at another
 configuration, or the EAGLE-2 tree build, eagerly for a kernel trace.
+`--oracle-configs` times the CPU oracle per configuration and stage (no GPU
+work) and prints one JSON line.
 """
 from __future__ import annotations
 
@@ -397,6 +399,51 @@ def cpu_baseline(W, T, budget_s=12.0):
                 ms_per_stage={k: 1e3 * v / done for k, v in stage.items()})
 
 
+def oracle_per_config(W, repeats=3):
+    """The oracle, untuned, per configuration and stage on one host core: the
+    median of `repeats` runs of each stage (one run where a stage takes more
+    than 10 s).  Tokens/s = B * N / (sum of the stage medians)."""
+    import oracle
+    from oracle.walk import as_arrays
+    from threadpoolctl import threadpool_limits
+    limiter = threadpool_limits(limits=1)
+    rows = []
+    for cfg in W.CONFIGS:
+        T = cfg.temperatures[-1]
+        s = W.make_step(cfg, T)
+        walks = None
+
+        def attn():
+            oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+
+        def walk():
+            nonlocal walks
+            walks = oracle.verify_batch(s.tokens, s.draft_probs, s.target_logits, s.parents,
+                                        s.kv_len, T, s.uniforms)
+
+        def compact():
+            a = as_arrays(walks, cfg.N)
+            oracle.kv_compact(s.k_cache, s.v_cache, s.kv_len, a["kv_src"], a["accept_len"])
+
+        med = {}
+        for name, fn in (("tree_attention", attn), ("verify", walk), ("kv_compact", compact)):
+            ts = []
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                fn()
+                ts.append(time.perf_counter() - t0)
+                if ts[-1] > 10.0:
+                    break
+            med[name] = float(np.median(ts))
+        total = sum(med.values())
+        rows.append({"config": cfg.name, "T": T, "ms_per_stage": {k: v * 1e3 for k, v in med.items()},
+                     "tokens_per_s": cfg.B * cfg.N / total})
+        log(f"[oracle] {cfg.name}: {total:.2f} s per step")
+    limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"oracle_per_config": rows, "cores": 1,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def pmc_traffic(attn_bytes):
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -417,6 +464,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-capture", action="store_true")
+    ap.add_argument("--oracle-configs", action="store_true",
+                    help="time the CPU oracle per configuration and stage, print one JSON line")
     ap.add_argument("--profile", default=None,
                     help="attn:<config> or dtree: eager launches for a rocprofv3 trace")
     args = ap.parse_args()
@@ -430,6 +479,10 @@ def main():
 
     import tree_attention_verification_parent_amd as ev
     import workloads as W
+
+    if args.oracle_configs:
+        print(json.dumps(oracle_per_config(W)), flush=True)
+        return
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
