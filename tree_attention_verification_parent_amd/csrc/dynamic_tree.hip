@@ -11,9 +11,10 @@
 //
 // All three steps are top-k selections over (value, id) pairs, compared as
 // 64-bit keys that order by value, then by lower id.  Over a vocabulary row
-// (expansion) the k keys come in k rounds of a workgroup maximum: every
-// thread keeps the largest of its keys below the last one taken, and only
-// the thread whose key was taken looks again.  Over at most 2048 created
+// (expansion) every wave finds its own k largest keys in k rounds of a wave
+// maximum (no barrier: every lane keeps the largest of its keys below the
+// last one taken, and only the lane whose key was taken looks again); the
+// row's k largest are then the keys of rank below k among the waves' k each.  Over at most 2048 created
 // nodes (selection, rerank) each key's rank is counted against all the keys
 // in LDS, and the keys of rank below k are the selection.
 #include "common.h"
@@ -54,38 +55,29 @@ __device__ __forceinline__ unsigned long long lane_u64(unsigned long long x, int
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Workgroup maximum: within a wave by DPP row steps and the four rows' lanes,
-// then across the NW waves through LDS; `red` holds two sets of per-wave
-// slots used in turn, so one barrier per call suffices.
-template <int NW>
-__device__ __forceinline__ unsigned long long block_max_key(unsigned long long x,
-                                                            unsigned long long* red, int turn) {
+// Wave maximum: DPP row steps, then the four rows' lanes.
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long x) {
   x = dpp_max_u64<kDppXor1>(x);
   x = dpp_max_u64<kDppXor2>(x);
   x = dpp_max_u64<kDppHalfMirror>(x);
   x = dpp_max_u64<kDppMirror>(x);
-  {
-    const unsigned long long a = lane_u64(x, 0), b = lane_u64(x, 16);
-    const unsigned long long c = lane_u64(x, 32), d = lane_u64(x, 48);
-    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
-    x = ab > cd ? ab : cd;
-  }
-  unsigned long long* slot = red + (turn & 1) * NW;
-  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = x;
-  barrier_lds();  // orders LDS only: no wait for this workgroup's global stores
-  unsigned long long m = slot[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) m = slot[i] > m ? slot[i] : m;
-  return m;
+  const unsigned long long a = lane_u64(x, 0), b = lane_u64(x, 16);
+  const unsigned long long c = lane_u64(x, 32), d = lane_u64(x, 48);
+  const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
-// The k largest keys of the workgroup, largest first: emit(j, key) on every
-// thread for j = 0.. until k keys or no key is left.  A thread offers its
-// largest key not yet taken (m1) and keeps its second largest (m2) ready, so
-// it rescans its keys only when it wins a third time or more.
+// The k largest keys of the workgroup (keys distinct, k <= 64): each wave
+// writes its own k largest to cand[wave * k ..] (0 where it has fewer), in k
+// rounds of a wave maximum; a lane offers its largest key not yet taken (m1)
+// and keeps its second largest (m2) ready, so it rescans its keys only when
+// it wins a third time or more.  After one barrier, emit(rank, key) runs on
+// the thread holding each of the k largest of the waves' candidates, rank
+// 0 the largest: the row's k largest are all among them.
 template <int BLOCK, int EPT, typename KeyAt, typename Emit>
-__device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long long* red,
+__device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long long* cand,  // 16-byte aligned
                                            Emit&& emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   unsigned long long m1 = 0, m2 = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -99,12 +91,12 @@ __device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long 
   }
   bool m2_ready = true;
   for (int j = 0; j < k; ++j) {
-    const unsigned long long best = block_max_key<BLOCK / 64>(m1, red, j);
-    if (best == 0) break;  // uniform: fewer than k keys
-    emit(j, best);
-    // keys are distinct: only one thread held it; the other waves skip this
-    // with a wave-uniform branch (predicated, the rescan cost every wave)
-    const bool won = m1 == best;
+    const unsigned long long best = wave_max_key(m1);  // 0: the wave has no key left
+    if (lane == 0) cand[wave * k + j] = best;
+    // keys are distinct, so one lane at most holds best; the other lanes skip
+    // the update with a wave-uniform branch (predicated, every lane paid for
+    // the rescan)
+    const bool won = best != 0ull && m1 == best;
     if (__ballot(won)) {
       if (won) {
         if (m2_ready) {
@@ -121,6 +113,21 @@ __device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long 
       }
     }
   }
+  barrier_lds();
+  // nc is a multiple of 8: eight keys per step, their LDS reads issued together
+  const int nc = (BLOCK / 64) * k;
+  for (int t = threadIdx.x; t < nc; t += BLOCK) {
+    const unsigned long long mine = cand[t];
+    if (mine == 0ull) continue;
+    int rank = 0;
+    for (int i = 0; i < nc; i += 8) {
+      const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand + i);
+      const ulonglong2 a = c2[0], b = c2[1], c = c2[2], d = c2[3];
+      rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine) + (c.x > mine) +
+              (c.y > mine) + (d.x > mine) + (d.y > mine);
+    }
+    if (rank < k) emit(rank, mine);
+  }
 }
 
 // Expansion: one workgroup per (sequence, row); the keys of the row's
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(kExpandBlock) void eagle2_expand_kernel(
     const float* __restrict__ parent_value, int32_t* __restrict__ cpar,
     int32_t* __restrict__ ctok, float* __restrict__ cval, int T, int base) {
   constexpr int EPT = 32768 / kExpandBlock;
-  __shared__ unsigned long long red[2 * kExpandBlock / 64];
+  __shared__ __attribute__((aligned(16))) unsigned long long cand[(kExpandBlock / 64) * 64];
   __shared__ unsigned long long taken[64];
   const int row = blockIdx.x;
   const int b = row / R, r = row - b * R;
@@ -150,9 +157,8 @@ __global__ __launch_bounds__(kExpandBlock) void eagle2_expand_kernel(
   auto key_at = [&](int e) { return key[e]; };
   const float pv = parent_value[row];
   const int pn = parent_node[row];
-  block_topk<kExpandBlock, EPT>(key_at, k, red, [&](int j, unsigned long long best) {
-    if (threadIdx.x == 0) taken[j] = best;
-  });
+  block_topk<kExpandBlock, EPT>(key_at, k, cand,
+                                [&](int rank, unsigned long long key) { taken[rank] = key; });
   barrier_lds();
   // the children, written once all are known (k <= 64)
   if (threadIdx.x < k) {
