@@ -67,6 +67,31 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long x)
   return ab > cd ? ab : cd;
 }
 
+// Wave maximum of 32-bit values (the same row steps).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<kDppXor1>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppXor2>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppHalfMirror>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppMirror>((int)x));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Largest key of the wave: the maximum of the value halves (nonzero for
+// every real key), then, if one lane holds that value, its key; only a tie
+// between lanes needs the 64-bit maximum.
+__device__ __forceinline__ unsigned long long wave_best_key(unsigned long long m) {
+  const uint32_t hi = (uint32_t)(m >> 32);
+  const uint32_t vmax = wave_max_u32(hi);
+  if (vmax == 0u) return 0ull;  // uniform: no key left
+  const unsigned long long lanes = __ballot(hi == vmax);
+  if (__popcll(lanes) == 1) return lane_u64(m, __ffsll((long long)lanes) - 1);
+  return wave_max_key(hi == vmax ? m : 0ull);
+}
+
 // The k largest keys of the workgroup (keys distinct, k <= 64): each wave
 // writes its own k largest to cand[wave * k ..] (0 where it has fewer), in k
 // rounds of a wave maximum; a lane offers its largest key not yet taken (m1)
@@ -91,7 +116,7 @@ __device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long 
   }
   bool m2_ready = true;
   for (int j = 0; j < k; ++j) {
-    const unsigned long long best = wave_max_key(m1);  // 0: the wave has no key left
+    const unsigned long long best = wave_best_key(m1);  // 0: the wave has no key left
     if (lane == 0) cand[wave * k + j] = best;
     // keys are distinct, so one lane at most holds best; the other lanes skip
     // the update with a wave-uniform branch (predicated, every lane paid for
