@@ -62,10 +62,24 @@ struct AttnArgs {
 };
 
 // Swizzle of 16-byte slots within a key row of a 32-key chunk: slot p of row r
-// holds the global slot p ^ swz(r).  Conflict-free for both the K fragment
-// reads (8 rows {0-3, 8-11} or {4-7, 12-15}) and the transposed V reads
-// (4 consecutive rows, two adjacent slots each).
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
+// holds the global slot p ^ swz(r).  gfx950's LDS has 64 banks of 4 bytes; a
+// 16-byte read serves 16 lanes per cycle, an 8-byte transposed read 32.  The
+// K fragment reads of 16 lanes take rows {0-3, 8-11, 16-19, 24-27} (or the
+// same + 4) at one global slot: swz is distinct over them.  The transposed V
+// reads of 32 lanes take 8 rows {0-3, 8-11} (+4, +16) at two adjacent slots
+// each: swz >> 1 is distinct over them.  (D = 64: two rows share a 256-byte
+// bank row, so the conditions hold per row parity.)  Measured against the
+// earlier 2 (r & 3) + ((r >> 3) & 1), conflict-free only for half as many
+// lanes per cycle: bank-conflict cycles 48 % -> 32 % of the LDS-active
+// cycles in the grouped-query kernel (llama2-70b shape), 20 % -> 10 % in the
+// ring kernel (llama2-7b); the kernels' times did not change.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return 8 * ((r >> 3) & 1) + 2 * (r & 3) + ((r >> 4) & 1);
+  else
+    return 4 * ((r >> 3) & 1) + 2 * ((r >> 1) & 1) + ((r >> 4) & 1);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
@@ -451,7 +465,7 @@ __device__ __forceinline__ void chunk_qk(const uint8_t* slot, const bf16x8 (&qf)
   for (int hlf = 0; hlf < 2; ++hlf) {
     // MFMA row c holds key 8*(c/4) + 4*hlf + c%4, so output row 4g+r is key 8g+4*hlf+r.
     const int kr = 8 * (c >> 2) + 4 * hlf + (c & 3);
-    const int sw = swz(kr);
+    const int sw = swz<D>(kr);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kc + kr * D + (((ks * 4 + g) ^ sw) * 8));
@@ -498,7 +512,7 @@ __device__ __forceinline__ void chunk_pv(const uint8_t* slot, const bf16x8 (&pf)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int vr = 8 * g + 4 * h + (c >> 2);
-      const int ps = (2 * db + ((c & 3) >> 1)) ^ swz(vr);
+      const int ps = (2 * db + ((c & 3) >> 1)) ^ swz<D>(vr);
       const uint8_t* src = Vb + vr * D * 2 + ps * 16 + (c & 1) * 8;
       h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t*)(src));
@@ -575,14 +589,14 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
-      const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
+      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
       load_lds16<S::POLICY>(kp + off, slot + t * RPL * D * 2);
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
-      const size_t off = (size_t)key * D + (p_in ^ swz(r)) * 8;
+      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
       load_lds16<S::POLICY>(vp + off, slot + S::MAT_BYTES + t * RPL * D * 2);
     }
   };
@@ -606,7 +620,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
-      const size_t off = (size_t)min(key0 + r, key_max) * D + (p_in ^ swz(r)) * 8;
+      const size_t off = (size_t)min(key0 + r, key_max) * D + (p_in ^ swz<D>(r)) * 8;
       pre[t] = *reinterpret_cast<const u32x4*>(kp + off);
       pre[LPM + t] = *reinterpret_cast<const u32x4*>(vp + off);
     }
@@ -1102,7 +1116,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
       const int ch = li / (2 * LPM), mat = (li / LPM) & 1, t = li % LPM;
       const int r = t * RPL + r_in;
       const int key = min(key0 + ch * 32 + r, key_max);
-      const uint16_t* src = (mat ? vp : kp) + (size_t)key * D + (p_in ^ swz(r)) * 8;
+      const uint16_t* src = (mat ? vp : kp) + (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
       const uint32_t dst = lds_base + (uint32_t)((j % NBUF) * S::TILE_BYTES + ch * S::SLOT_BYTES +
                                                  mat * S::MAT_BYTES + t * RPL * D * 2);
       lds_dma16(src, __builtin_amdgcn_readfirstlane(dst));
