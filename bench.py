@@ -392,7 +392,7 @@ def cpu_baseline(W, T, budget_s=12.0):
             break
     limiter.unregister() if hasattr(limiter, "unregister") else None
     return dict(value=cfg.B * cfg.N * done / el, unit="tokens/s", cores=int(blas_threads),
-                kind="oracle",
+                host_cpus=len(os.sched_getaffinity(0)), kind="oracle",
                 sample=f"{done} whole steps of the {cfg.name} workload at T={T} "
                        f"(fp64 NumPy oracle, {el:.1f} s)",
                 near_ties_per_step=near_ties,
