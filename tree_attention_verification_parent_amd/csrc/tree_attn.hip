@@ -1052,7 +1052,7 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
       : "=&s"(save)
       : "s"(lds_addr), "v"(src)
       : "memory");
@@ -1234,11 +1234,14 @@ template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
   constexpr int C4 = D / 4;        // 16-byte columns per row
   constexpr int RPB = 256 / C4;    // rows per workgroup
-  const int grow = blockIdx.x * RPB + threadIdx.x / C4;  // row over units x RW
-  const int d4 = threadIdx.x % C4;
-  const int unit = grow / RW;
+  // a unit's RW / RPB workgroups run on the XCD whose workgroups wrote its
+  // partials (unit mod 8), so its reads can hit that XCD's L2
+  const int bpu = RW / RPB;
+  const int x = blockIdx.x % kNumXCDs, q = blockIdx.x / kNumXCDs;
+  const int unit = (q / bpu) * kNumXCDs + x;
   if (unit >= a.units) return;
-  const int rl = grow - unit * RW;
+  const int rl = (q % bpu) * RPB + threadIdx.x / C4;
+  const int d4 = threadIdx.x % C4;
   const int qgroup = unit % a.qgroups;
   const int pair = unit / a.qgroups;
   const int kvh = pair % a.Hkv;
@@ -1449,7 +1452,8 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   if (err != hipSuccess || plan.splits == 1 || ring) return err;
   const int rw = plan.rows_per_wg;
   const int rows_per_block = 256 / (plan.d / 4);
-  const dim3 mgrid((unsigned)((plan.units * rw + rows_per_block - 1) / rows_per_block));
+  const dim3 mgrid((unsigned)(((plan.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs *
+                               (rw / rows_per_block)));
   if (plan.d == 64)
     tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a, rw);
   else
