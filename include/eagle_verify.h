@@ -354,6 +354,21 @@ EAGLE_API eagle_status_t eagle_dtree_rerank(const int32_t* created_parent, const
                                        int N, int32_t* parents, int32_t* tokens,
                                        int32_t* kept_node, int32_t* seq_flags, void* stream);
 
+/*
+ * Testing hook, not for production use: forces the attention kernel and the
+ * work split of every later eagle_tree_attn / eagle_tree_attn_parents call
+ * and workspace query in this process, so that tests can run each kernel and
+ * piece count on the same inputs.  kernel: 0 = the planner's choice, 1 = the
+ * ring kernel (at most 32 query rows per KV head; larger shapes then return
+ * EAGLE_ERR_UNSUPPORTED), 2 = the group kernel.  pieces_per_unit: 0 = the
+ * planner's choice, else the number of key ranges per (sequence, KV head) at
+ * full cache length, 1..1024 (sequences shorter than the cache get fewer).
+ * Results are the same for every setting up to the rounding of the split
+ * merge.  Not thread-safe: set it while no attention call is being made.
+ * Returns EAGLE_ERR_INVALID_ARGUMENT for values out of range.
+ */
+EAGLE_API eagle_status_t eagle_testing_attn_plan(int kernel, int pieces_per_unit);
+
 #ifdef __cplusplus
 }
 #endif

@@ -89,13 +89,14 @@ def test_attention_matches_oracle(case):
     assert err < ATOL_ATTN
 
 
-@pytest.mark.parametrize("splits", ["1", "2", "3", "7", "32"])
-def test_attention_split_counts_agree(splits, monkeypatch):
+@pytest.mark.parametrize("kernel", ["ring", "group"])
+@pytest.mark.parametrize("pieces", [1, 2, 3, 7, 32])
+def test_attention_piece_counts_agree(pieces, kernel):
     cfg = W.shrink(W.get(1), B=2, L=600, Hq=8, Hkv=8, V=16)
     s = W.make_step(cfg, 1.0, seed=5, kv_lens=[600, 213])
-    monkeypatch.setenv("EAGLE_ATTN_SPLITS", splits)
-    say(f"attention splits={splits}")
-    got, _, _, _ = run_attention(s)
+    say(f"attention {kernel} pieces={pieces}")
+    with ev.attn_plan(kernel, pieces):
+        got, _, _, _ = run_attention(s)
     ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
     assert np.abs(got - ref).max() < ATOL_ATTN
 
@@ -165,39 +166,44 @@ def test_attention_full_configs_sampled(idx):
     assert err < ATOL_ATTN
 
 
-@pytest.mark.parametrize("variant", ["1", "4", "5", "6"])
+@pytest.mark.parametrize("kernel", ["ring", "group"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
-def test_attention_kernel_variants(case, variant, monkeypatch):
-    """Each kernel forced on every case: ring with one query group per KV head
-    (1), shared-tile (4), ring with query groups on one XCD (5), group kernel
-    with 256 rows sharing a ring of 64-key tiles (6); the ring variants split
-    G*N > 32 rows into query groups, and every kernel takes up to 64 tree
-    keys."""
+def test_attention_kernels(case, kernel):
+    """Each kernel forced on every case: the ring kernel (at most 32 query
+    rows per KV head: larger groups are refused with EAGLE_ERR_UNSUPPORTED)
+    and the group kernel (256 rows sharing a ring of 64-key tiles, any number
+    of rows); both take up to 64 tree keys."""
     name, B, N, Hq, Hkv, d, kv_lens = case
-    monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
     cfg = W.shrink(W.get(0), B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
     rng = np.random.default_rng(len(name) + 7)
     parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(B)])
     s = W.make_step(cfg, 1.0, seed=zlib.crc32(name.encode()) % 1000 + 3, kv_lens=kv_lens,
                     parents=parents)
-    say(f"attention {name} variant {variant}")
-    got = _fused_vs_two_calls(s)
+    say(f"attention {name} kernel {kernel}")
+    with ev.attn_plan(kernel):
+        if kernel == "ring" and (Hq // Hkv) * N > 32:
+            with pytest.raises(ev.EagleError) as e:
+                run_attention(s)
+            assert e.value.status == ev.binding.EAGLE_ERR_UNSUPPORTED
+            return
+        got = _fused_vs_two_calls(s)
     ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
     err = np.abs(got - ref).max()
     say(f"  max abs err {err:.3e}")
     assert err < ATOL_ATTN
 
 
-@pytest.mark.parametrize("variant", ["4", "5", "6"])
+@pytest.mark.parametrize("pieces", [1, 3, 8])
 @pytest.mark.parametrize("idx", [3, 4])
-def test_attention_gqa_full_configs_variants(idx, variant, monkeypatch):
-    """The grouped-query configurations at full size through each GQA kernel:
+def test_attention_gqa_full_configs_pieces(idx, pieces):
+    """The grouped-query configurations at full size with other piece counts
+    than the planner's (one piece: no merge; several: the merge kernel):
     sampled rows against the oracle, every output finite."""
-    monkeypatch.setenv("EAGLE_ATTN_VARIANT", variant)
     cfg = W.get(idx)
     s = W.make_step(cfg, cfg.temperatures[-1])
-    say(f"attention full config {cfg.name} variant {variant}")
-    got, _, _, _ = run_attention(s)
+    say(f"attention full config {cfg.name} pieces {pieces}")
+    with ev.attn_plan("group", pieces):
+        got, _, _, _ = run_attention(s)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(idx + 50)
     rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.N)), int(rng.integers(cfg.Hq)))
@@ -217,6 +223,72 @@ def test_attention_deterministic():
     a, _, _, _ = run_attention(s)
     b, _, _, _ = run_attention(s)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------- cache slots outside the keys J
+# bf16 patterns a preallocated or stale cache can hold: quiet and signalling
+# NaN, both infinities, the largest finite value of either sign
+GARBAGE_BF16 = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFFF, 0x7F81, 0x7F7F, 0xFF7F], dtype=np.uint16)
+
+
+def _with_capacity(s, Lmax):
+    """The step's caches moved into caches of capacity Lmax, every slot at or
+    past kv_len[b] + N (outside the keys J of sequence b) holding NaN, +-Inf
+    or the largest finite bf16 values."""
+    B, Hkv, L0, d = s.k_cache.shape
+    N = s.cfg.N
+    assert Lmax >= L0
+    out = []
+    for cache in (s.k_cache, s.v_cache):
+        big = np.resize(GARBAGE_BF16, (B, Hkv, Lmax, d)).astype(np.uint16)
+        for b in range(B):
+            end = int(s.kv_len[b]) + N
+            big[b, :, :end] = cache[b, :, :end]
+        out.append(big)
+    s.k_cache, s.v_cache = out
+    return s
+
+
+@pytest.mark.parametrize("pieces", [0, 5])
+@pytest.mark.parametrize("kernel,Hq,Hkv,d", [("ring", 8, 8, 128), ("ring", 4, 4, 64),
+                                             ("group", 16, 2, 128), ("group", 8, 4, 64)])
+def test_attention_ignores_slots_outside_keys(kernel, Hq, Hkv, d, pieces):
+    """Only J = [0, kv_len) and the tree's slots [kv_len, kv_len + N) may
+    reach the output: every other cache slot holds NaN / Inf / huge values
+    and the output still matches the oracle (which reads J only) and is
+    finite.  Capacity far above the longest sequence; one sequence empty."""
+    N = 26
+    cfg = W.shrink(W.get(0), B=3, N=N, Hq=Hq, Hkv=Hkv, d=d, V=16)
+    rng = np.random.default_rng(d + Hq)
+    parents = np.stack([trees.random_tree(rng, N, 6) for _ in range(3)])
+    s = W.make_step(cfg, 1.0, seed=11 + d, kv_lens=[333, 0, 1100], parents=parents)
+    s = _with_capacity(s, 1100 + N + 900)
+    say(f"attention outside-J garbage {kernel} Hq={Hq} Hkv={Hkv} d={d} pieces={pieces}")
+    with ev.attn_plan(kernel, pieces):
+        got = _fused_vs_two_calls(s)
+    assert np.isfinite(got).all()
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < ATOL_ATTN
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8)], ids=["mha-ring", "gqa-group"])
+def test_attention_ragged_capacity(Hq, Hkv):
+    """A ragged batch in a cache of capacity 8192 + N: kv_len 512, 1024,
+    2048, 8192, garbage in every slot outside J; every row against the
+    oracle."""
+    N = 26
+    cfg = W.shrink(W.get(3), B=4, N=N, Hq=Hq, Hkv=Hkv, V=16)
+    s = W.make_step(cfg, 1.0, seed=21, kv_lens=[512, 1024, 2048, 8192])
+    s = _with_capacity(s, 8192 + N)
+    say(f"attention ragged capacity Hq={Hq} Hkv={Hkv}")
+    got = _fused_vs_two_calls(s)
+    assert np.isfinite(got).all()
+    ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err < ATOL_ATTN
 
 
 # ------------------------------------------------- mask builder fused into attention
@@ -269,13 +341,13 @@ def test_attention_from_parents_full_configs(idx):
     _fused_vs_two_calls(s, outputs=idx != 2)
 
 
-def test_attention_from_parents_chain_scale_and_splits(monkeypatch):
+def test_attention_from_parents_chain_scale_and_pieces():
     cfg = W.shrink(W.get(1), B=2, L=600, Hq=8, Hkv=8, V=16)
     s = W.make_step(cfg, 1.0, seed=9, kv_lens=[600, 213], parents=np.stack([trees.chain(26)] * 2))
-    for splits in ("1", "3"):
-        monkeypatch.setenv("EAGLE_ATTN_SPLITS", splits)
-        say(f"attention from parents chain splits={splits}")
-        got = _fused_vs_two_calls(s, sm_scale=0.07)
+    for pieces in (1, 3):
+        say(f"attention from parents chain pieces={pieces}")
+        with ev.attn_plan("auto", pieces):
+            got = _fused_vs_two_calls(s, sm_scale=0.07)
         ref = oracle.tree_attention(s.q, s.k_cache, s.v_cache, s.kv_len, s.parents, sm_scale=0.07)
         assert np.abs(got - ref).max() < ATOL_ATTN
 

@@ -6,7 +6,8 @@ through the C ABI declared in include/eagle_verify.h and bound here with
 ctypes (binding.py).  Build with `python -m
 tree_attention_verification_parent_amd.build`.
 """
-from .binding import (EagleError, abi_version, alloc_workspace, dtree_expand,  # noqa: F401
+from .binding import (EagleError, abi_version, alloc_workspace, attn_plan,  # noqa: F401
+                      dtree_expand, testing_attn_plan,
                       dtree_rerank, dtree_select, feature_gather, kv_compact, lib,
                       tree_attn, tree_attn_parents, tree_attn_workspace_bytes, tree_build,
                       validate_tree_host,

@@ -48,6 +48,7 @@ _SIGNATURES = {
     "eagle_abi_version": (_I, []),
     "eagle_validate_tree_host": (_I, [_P, _I, _I]),
     "eagle_workspace_clear": (_I, [_P, _SZ, _P]),
+    "eagle_testing_attn_plan": (_I, [_I, _I]),
     "eagle_tree_build": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "eagle_tree_attn_workspace": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "eagle_tree_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P]),
@@ -139,6 +140,31 @@ def validate_tree_host(parents) -> None:
         arr = arr[None]
     B, N = arr.shape
     _check(lib().eagle_validate_tree_host(arr.ctypes.data, B, N))
+
+
+ATTN_KERNELS = {"auto": 0, "ring": 1, "group": 2}
+
+
+def testing_attn_plan(kernel: str = "auto", pieces: int = 0) -> None:
+    """Testing hook: force the attention kernel ("auto", "ring", "group") and
+    the pieces per (sequence, KV head) at full cache length (0 = planner) of
+    later attention calls in this process."""
+    _check(lib().eagle_testing_attn_plan(ATTN_KERNELS[kernel], int(pieces)))
+
+
+class attn_plan:
+    """Context manager around testing_attn_plan that restores the planner."""
+
+    def __init__(self, kernel: str = "auto", pieces: int = 0):
+        self.kernel, self.pieces = kernel, pieces
+
+    def __enter__(self):
+        testing_attn_plan(self.kernel, self.pieces)
+        return self
+
+    def __exit__(self, *exc):
+        testing_attn_plan("auto", 0)
+        return False
 
 
 def workspace_clear(ws: torch.Tensor, stream=None) -> None:

@@ -66,6 +66,15 @@ eagle_status_t eagle_workspace_clear(void* ptr, size_t bytes, void* stream) {
   return hip_status(eagle::launch_fill_zero(ptr, bytes, as_stream(stream)), "workspace clear");
 }
 
+eagle_status_t eagle_testing_attn_plan(int kernel, int pieces_per_unit) {
+  if (kernel < 0 || kernel > 2)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "kernel must be 0 (planner), 1 (ring) or 2 (group)");
+  if (pieces_per_unit < 0 || pieces_per_unit > 1024)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "pieces_per_unit must be in [0, 1024]");
+  eagle::set_attn_plan_override(kernel, pieces_per_unit);
+  return EAGLE_OK;
+}
+
 eagle_status_t eagle_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
                                 uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* seq_flags,
                                 void* stream) {
@@ -106,6 +115,9 @@ static eagle_status_t tree_attn_call(const uint16_t* q, const uint16_t* k_cache,
                                      int32_t* pos_out, void* workspace, size_t workspace_bytes,
                                      int32_t* seq_flags, void* stream) {
   const eagle::AttnPlan plan = eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax);
+  if (plan.kernel < 0)
+    return fail(EAGLE_ERR_UNSUPPORTED, "the forced ring kernel holds at most 32 query rows per KV head (G * N = %d)",
+                plan.M);
   const size_t need = eagle::tree_attn_workspace_bytes(plan);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(EAGLE_ERR_WORKSPACE, "tree attention needs %zu workspace bytes (got %zu)", need,

@@ -18,16 +18,21 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 // Tree attention -----------------------------------------------------------
 struct AttnPlan {
   int d;
-  int G;          // query heads per KV head
-  int M;          // query rows per (b, kv head) = G * N
-  int rows_per_wg;
-  int qgroups;    // ceil(M / rows_per_wg)
-  int units;      // B * Hkv * qgroups
-  int splits;     // KV splits per unit
-  int variant;    // kernel instantiation index
-  int kt;         // keys per tile
+  int G;           // query heads per KV head
+  int M;           // query rows per (b, kv head) = G * N
+  int kernel;      // 1: ring (M <= 32), 2: group; -1: shape not supported by the forced kernel
+  int rows_per_wg; // query rows per workgroup
+  int qgroups;     // ceil(M / rows_per_wg)
+  int units;       // B * Hkv * qgroups
+  int slots;       // workgroups launched (a multiple of 8)
+  int kg;          // keys per planning chunk
+  int max_pieces;  // pieces per unit at most
+  int full_pieces; // pieces per unit the device gives when every sequence fills the cache
 };
 
+// Test-only: force the kernel (0 planner, 1 ring, 2 group) and the pieces per
+// unit (0 planner) of later plans.
+void set_attn_plan_override(int kernel, int pieces);
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax);
 size_t tree_attn_workspace_bytes(const AttnPlan& p);
 

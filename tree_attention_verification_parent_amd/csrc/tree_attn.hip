@@ -3,37 +3,46 @@
 // The target verifies the whole draft tree in one forward pass: node i of
 // sequence b attends to the committed keys 0..L-1 and to the tree keys L+j of
 // its ancestors j (EAGLE, paperlayer.ai summary, §2 Preliminaries; §3 EAGLE:
-// tree attention).  This is decode-shaped attention: M = G*N query rows per
-// KV head against L+N keys, HBM-bound on the bf16 K/V stream.
+// tree attention; A.1 Tree Structure).  This is decode-shaped attention:
+// M = G*N query rows per KV head against L+N keys, HBM-bound on the bf16 K/V
+// stream.
+//
+// Only the keys of J are ever read: the committed keys [0, L) of the
+// sequence and its tree keys [L, L+N).  Chunks are laid over [0, L), not over
+// the cache capacity, and a load past the end of its range re-reads the last
+// key of that range (masked afterwards), so cache slots at or past L+N, which
+// may hold anything (a preallocated cache, the unused tail of a shorter
+// sequence in a ragged batch), never reach the scores or the V products.
 //
 // Work decomposition
-//   unit  = (b, kv head, group of RW query rows); split = a contiguous range of
-//   32-key chunks.  One 256-thread workgroup per (unit, split).  Workgroup ids
-//   are laid out so that all splits of a unit run on one XCD (blocks go to XCDs
-//   round robin), keeping a unit's partials in that XCD's caches.
+//   unit  = (b, KV head, group of RW query rows); piece = a contiguous range
+//   of key chunks of one unit.  The launch has a fixed number of workgroup
+//   slots (a multiple of 8, sized on the host from the cache capacity); every
+//   workgroup reads the batch's committed lengths and shares the slots out:
+//   each unit gets one, the rest go to the sequences in proportion to their
+//   lengths, so a ragged batch costs about the sum of its lengths.  Slots are
+//   numbered so that consecutive ones (the pieces of a unit) run on one XCD
+//   (workgroup i is dispatched to XCD i mod 8).
 //
 // Two kernels, picked by the number of query rows per KV head:
-//   ring  (M <= 32, e.g. multi-head attention): every wave owns a private ring
-//         of 32-key chunk slots in LDS, filled by direct-to-LDS loads
-//         (global_load_lds_dwordx4) issued ahead, so the whole split is in
-//         flight from the start with no staging registers and no barriers in
-//         the main loop.  Each wave computes all query rows against its own
-//         chunks; the four waves merge at the end.
-//   tile  (larger M, grouped-query attention): the 256 threads stage each tile
-//         of keys into LDS (K row-major, V transposed) and the waves split the
-//         query rows, so one copy of the tile serves all G*N queries.
+//   ring  (M <= 32, e.g. multi-head attention): every wave owns a 32-key
+//         chunk slot in LDS, filled by direct-to-LDS loads, so a piece's
+//         chunks are in flight from the start with no staging registers and
+//         no barriers in the main loop; the waves' states are folded at the
+//         end, and the unit's last piece to finish combines the pieces'
+//         partials (written and read with device-coherent accesses, so the
+//         combine does not depend on where the pieces ran).
+//   group (M > 32, grouped-query attention): eight waves each own 32 of up to
+//         256 query rows and compute every 64-key tile of the piece against
+//         them, so a tile is read from HBM once for the whole head group; a
+//         merge kernel combines the pieces.
 // Both compute S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16
 // (keys on MFMA rows: the K rows are permuted so each lane ends up holding 8
-// consecutive keys of one query column, exactly the k-slots of P^T), apply the
-// tree mask, and run the online softmax with cross-lane shuffles.
-//
-// With more than one split, every split writes its normalised rows O / l and
-// log2-sum-exp with coalesced stores.  Ring variants combine them in the
-// kernel: the unit's last split to finish (a per-unit ticket) reads the other
-// splits' partials from the XCD's L2 and writes the output.  Tile variants
-// leave them to a small merge kernel on the same stream (one wave per query
-// row), whose kernel boundary makes the partials visible.
-#include <stdlib.h>
+// consecutive keys of one query column, exactly the k-slots of P^T), apply
+// the tree mask, and run the online softmax with cross-lane shuffles.
+#include <limits.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "launch.h"
@@ -41,6 +50,7 @@
 namespace eagle {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   const uint16_t* q;
@@ -53,13 +63,199 @@ struct AttnArgs {
   int32_t* depth_out;
   int32_t* pos_out;
   uint16_t* out;
-  float* part_o;     // [units * splits * RW * D]  O / l of each split
-  float* part_lse;   // [units * splits * RW]      m + log2(l) of each split
+  float* part_o;      // [slots * RW * D]  O / l of each piece, by slot
+  float* part_lse;    // [slots * RW]      m + log2(l) of each piece
+  int32_t* tickets;   // [units] pieces finished (ring kernel; zero between calls)
+  int32_t* unit_info; // [units * 2] first slot and piece count (group kernel -> merge)
   int32_t* flags;
-  int32_t* tickets;  // [units] splits finished (ring variants; zero between calls)
-  int B, N, Hq, Hkv, Lmax, G, M, qgroups, units, splits;
+  int B, N, Hq, Hkv, Lmax, G, M, qgroups, slots, kg, max_pieces;
+  int full_pieces;  // pieces per unit when every sequence fills the cache (see the ring kernel)
   float scale_log2;
 };
+
+// ---- decomposition -------------------------------------------------------------
+// A unit's piece: which (sequence, KV head, query group), which of its
+// nsplit pieces, the slot of its first piece, and the committed length.
+struct Piece {
+  int b, kvh, qgroup, unit, split, nsplit, first, L;
+  bool bad;
+};
+
+// Logical slot of this workgroup: the launch's slots / 8 consecutive slots
+// share an XCD.
+__device__ __forceinline__ int logical_slot(const AttnArgs& a) {
+  const int per_xcd = a.slots / kNumXCDs;
+  return (int)(blockIdx.x % kNumXCDs) * per_xcd + (int)(blockIdx.x / kNumXCDs);
+}
+
+// A wave-uniform 32-bit value read with a scalar load (constant address
+// space), which the compiler tracks apart from the vector loads in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// The committed lengths of sequences 0..63 in lanes 0..63 (0 past B).  For
+// B <= 16 they are read with scalar loads (addresses clamped into the array),
+// which a wave can wait for without waiting for its vector loads in flight:
+// the kernels issue their first K/V loads before they know the plan.
+__device__ __forceinline__ int kv_len_lanes(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  if (a.B <= 16) {
+    int x[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) x[b] = load_uniform(a.kv_len + min(b, a.B - 1));
+    int v = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) v = lane == b ? x[b] : v;
+    return lane < a.B ? v : 0;
+  }
+  const int v = a.kv_len[min(lane, a.B - 1)];
+  return lane < a.B ? v : 0;
+}
+
+// Sum over the wave of a non-negative int (DPP within rows of 16, then the
+// four rows); every lane receives it.
+__device__ __forceinline__ int wave_allsum_i(int v) {
+  v += dpp_i<kDppXor1>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
+  return (lane_i(v, 0) + lane_i(v, 16)) + (lane_i(v, 32) + lane_i(v, 48));
+}
+
+// Committed length of sequence b (given as read) -> chunks of kg keys; a
+// length that leaves no room for the tree (or is negative) counts as 0.
+__device__ __forceinline__ int seq_chunks(const AttnArgs& a, bool in, int Lraw, int& L, bool& bad) {
+  bad = in && (Lraw < 0 || Lraw > a.Lmax - a.N);
+  L = in && !bad ? Lraw : 0;
+  return (L + a.kg - 1) / a.kg;
+}
+
+// Shares the launch's slots out and finds a piece.  Every unit of sequence b
+// gets s_b = ceil(c_b / T) pieces (at least one, at most max_pieces), where
+// c_b is its number of chunks of kg committed keys and T, the largest piece in
+// chunks, is the smallest value for which all pieces fit the launch's slots:
+// in closed form when every sequence has the same length, else by bisection
+// (the count only falls as T grows, and T = max c_b fits since the host
+// launches at least one slot per unit).  Slots are numbered sequence by
+// sequence, unit by unit, piece by piece; slots past the last piece are
+// unused.  Finds the piece in slot `key`; kvl0 holds the committed lengths of
+// sequences 0..63 by lane (kv_len_lanes).  A function of the committed
+// lengths and the launch shape alone, so every wave finds the same
+// decomposition.  All 64 lanes of the wave call it; the result is
+// wave-uniform.  Returns false for an unused slot.
+__device__ bool plan_piece(const AttnArgs& a, int key, int kvl0, Piece& p) {
+  const int lane = threadIdx.x & 63;
+  const int U = a.Hkv * a.qgroups;
+  int L0;
+  bool bad0;
+  const int c0 = seq_chunks(a, lane < a.B, kvl0, L0, bad0);
+  auto block_chunks = [&](int b0, int& L, bool& bad) {
+    const int b = b0 + lane;
+    const int raw = a.kv_len[min(b, a.B - 1)];
+    return seq_chunks(a, b < a.B, raw, L, bad);
+  };
+  int cmax = wave_allmax_i(c0);
+  int cmin = wave_allmin_i(lane < a.B ? c0 : INT_MAX);
+  for (int b0 = 64; b0 < a.B; b0 += 64) {
+    int L;
+    bool bad;
+    const int c = block_chunks(b0, L, bad);
+    cmax = max(cmax, wave_allmax_i(c));
+    cmin = min(cmin, wave_allmin_i(b0 + lane < a.B ? c : INT_MAX));
+  }
+  auto pieces_of = [&](int c, int t) { return max(1, min(a.max_pieces, (c + t - 1) / t)); };
+  int T;
+  if (cmin == cmax) {
+    // every unit alike: ceil(c / T) <= slots / units
+    const int per_unit = (int)((long long)a.slots / ((long long)a.B * U));
+    T = per_unit >= a.max_pieces ? 1 : max(1, (cmax + per_unit - 1) / per_unit);
+  } else {
+    auto fits = [&](int t) {
+      long long n = wave_allsum_i(lane < a.B ? min(U * pieces_of(c0, t), a.slots + 1) : 0);
+      for (int b0 = 64; b0 < a.B && n <= a.slots; b0 += 64) {
+        int L;
+        bool bad;
+        const int c = block_chunks(b0, L, bad);
+        n += wave_allsum_i(b0 + lane < a.B ? min(U * pieces_of(c, t), a.slots + 1) : 0);
+      }
+      return n <= a.slots;
+    };
+    int lo = 1, hi = max(cmax, 1);
+    while (lo < hi) {  // wave-uniform
+      const int mid = (lo + hi) >> 1;
+      if (fits(mid))
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    T = lo;
+  }
+  long long base = 0;  // slots of the sequences before this block
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    int L = L0, c = c0;
+    bool bad = bad0;
+    if (b0 > 0) c = block_chunks(b0, L, bad);
+    const int s = pieces_of(c, T);
+    const int n = b < a.B ? U * s : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const long long lo_slot = base + (incl - n);
+    const bool mine = b < a.B && key >= lo_slot && key < lo_slot + n;
+    const uint64_t m = __ballot(mine);
+    if (m) {
+      const int src = __ffsll((unsigned long long)m) - 1;
+      const int sb = __shfl(b, src), ss = __shfl(s, src);
+      p.L = __shfl(L, src);
+      p.bad = __shfl((int)bad, src) != 0;
+      const long long slo = __shfl(lo_slot, src);
+      const int r = (int)(key - slo);
+      const int uis = r / ss;  // unit within the sequence
+      p.b = sb;
+      p.nsplit = ss;
+      p.split = r - uis * ss;
+      p.kvh = uis / a.qgroups;
+      p.qgroup = uis - p.kvh * a.qgroups;
+      p.unit = sb * U + uis;
+      p.first = (int)(slo + (long long)uis * ss);
+      return true;
+    }
+    base += lane_i(incl, 63);
+  }
+  return false;
+}
+
+// Device-coherent 16- and 4-byte accesses (agent scope, the sc1 bit): they
+// bypass the caches that are not coherent between XCDs, so a partial stored
+// by a piece on one XCD is seen by the combining workgroup on any other once
+// the store has completed and the ticket that follows it has been taken.
+// The 16-byte store is a single instruction (inline assembly: a store has no
+// outputs); the caller's s_waitcnt vmcnt(0) covers it before the ticket.
+__device__ __forceinline__ void store_coherent(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// Raw buffer over `bytes` bytes at `base` (out-of-range offsets read 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0,
+                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                           0x00020000);
+}
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16));
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 
 // Swizzle of 16-byte slots within a key row of a 32-key chunk: slot p of row r
 // holds the global slot p ^ swz(r).  gfx950's LDS has 64 banks of 4 bytes; a
@@ -127,106 +323,6 @@ __device__ __forceinline__ bf16x8 softmax_step(const float (&x)[8], float& m_run
   return pf;
 }
 
-// Valid keys among key0..key0+7 as an 8-bit mask, without branches: committed
-// keys (< L) plus the ancestor bits of the query's node.  (A branchy form of
-// this test was miscompiled for the first of the eight scores.)
-__device__ __forceinline__ uint32_t key_mask8(int key0, int L, uint64_t anc) {
-  const int below = L - key0;
-  const uint32_t pre = below >= 8 ? 0xffu : below <= 0 ? 0u : (1u << below) - 1u;
-  const int tk0 = -below;
-  const uint32_t tre = tk0 >= 0 ? (tk0 < 64 ? (uint32_t)(anc >> tk0) & 0xffu : 0u)
-                                : (tk0 > -8 ? (uint32_t)(anc << -tk0) & 0xffu : 0u);
-  return pre | tre;
-}
-
-// Write the final bf16 rows (one split) or this split's partial (O / l and
-// log2-sum-exp).  acc/m/l hold the lane's query column for QBW blocks starting
-// at row r0 of the unit.
-template <int D, int RW, int QBW>
-__device__ void finish_split(const AttnArgs& a, int unit, int split, int qgroup, int b, int kvh,
-                             bool bad, bool active, int r0, f32x4 (&acc)[QBW][D / 16],
-                             float (&m_run)[QBW], float (&l_run)[QBW], uint8_t* lds) {
-  constexpr int NDB = D / 16;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int N = a.N, G = a.G, M = a.M;
-  if (a.splits == 1) {
-    if (active) {
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        const int row = qgroup * RW + r0 + qb * 16 + c;
-        if (row >= M) continue;
-        const int i = row / G;
-        const int h = kvh * G + (row - i * G);
-        uint16_t* orow = a.out + (((size_t)b * N + i) * a.Hq + h) * D;
-        const float inv = (bad || l_run[qb] == 0.f) ? 0.f : 1.f / l_run[qb];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const f32x4 o = acc[qb][db] * inv;
-          *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * g) =
-              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        }
-      }
-    }
-    return;
-  }
-
-  // Stage this split's normalised rows in LDS (row-major fp32) so that the
-  // partial stores are coalesced 16-byte stores; the merge kernel that
-  // follows on the stream combines the splits.
-  const int rows = min(RW, M - qgroup * RW);
-  float* stage = reinterpret_cast<float*>(lds);  // [RW][D + 4]: column D = log2-sum-exp
-  constexpr int SD = D + 4;
-  if (active) {
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      const int rl = r0 + qb * 16 + c;
-      const float inv = l_run[qb] == 0.f ? 0.f : 1.f / l_run[qb];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<f32x4*>(stage + rl * SD + db * 16 + 4 * g) = acc[qb][db] * inv;
-      if (g == 0) stage[rl * SD + D] = l_run[qb] == 0.f ? -INFINITY : m_run[qb] + __log2f(l_run[qb]);
-    }
-  }
-  __syncthreads();
-  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
-  constexpr int D4 = D / 4;
-  for (int it = tid; it < rows * D4; it += 256) {
-    const int rl = it / D4, d4 = it - rl * D4;
-    *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + 4 * d4) =
-        *reinterpret_cast<const f32x4*>(stage + rl * SD + 4 * d4);
-  }
-  for (int rl = tid; rl < rows; rl += 256) a.part_lse[pbase + rl] = stage[rl * SD + D];
-}
-
-// Workgroup -> (unit, split), XCD-aware; validates kv_len.
-struct UnitCtx {
-  int unit, split, qgroup, pair, kvh, b, L, total;
-  bool bad;
-};
-
-__device__ __forceinline__ bool decode_unit(const AttnArgs& a, UnitCtx& u) {
-  const int w = blockIdx.x;
-  const int xcd = w % kNumXCDs;
-  const int slot = w / kNumXCDs;
-  u.split = slot % a.splits;
-  u.unit = (slot / a.splits) * kNumXCDs + xcd;
-  if (u.unit >= a.units) return false;
-  u.qgroup = u.unit % a.qgroups;
-  u.pair = u.unit / a.qgroups;
-  u.kvh = u.pair % a.Hkv;
-  u.b = u.pair / a.Hkv;
-  int L = a.kv_len[u.b];
-  u.bad = L < 0 || L > a.Lmax - a.N;
-  if (u.bad) {
-    L = 0;
-    if (a.flags && u.split == 0 && u.qgroup == 0 && u.kvh == 0 && threadIdx.x == 0)
-      atomicOr(a.flags + u.b, EAGLE_FLAG_BAD_KV_LEN);
-  }
-  u.L = L;
-  u.total = L + a.N;
-  return true;
-}
-
 // The tree-mask builder's outputs (ancestor masks, depths, position ids
 // kv_len + depth) of sequence b, written by the one wave per sequence that
 // the kernel picks, when the masks were built from the parent links.
@@ -241,21 +337,22 @@ __device__ __forceinline__ void write_tree_outputs(const AttnArgs& a, int b, con
   if (__ballot(t.bad) && lane == 0 && a.flags) atomicOr(a.flags + b, EAGLE_FLAG_BAD_PARENT);
 }
 
-// Q fragments (MFMA B operand) and tree masks of QBW query blocks at unit row r0.
+// Q fragments (MFMA B operand) and tree masks of QBW query blocks at unit row
+// r0.  Rows past M hold zero queries and no tree bits.
 template <int D, int QBW, int RW>
-__device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u, int r0,
+__device__ __forceinline__ void load_queries(const AttnArgs& a, const Piece& u, int r0,
                                              bf16x8 (&qf)[QBW][D / 32], uint64_t (&anc_q)[QBW]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int N = a.N, G = a.G;
   const uint64_t nmask = N == 64 ? ~0ull : (1ull << N) - 1ull;
   // masks built from the parent links: every wave derives its sequence's
-  // tree (lane = node); wave 0 of the unit's last split for KV head 0 and
-  // query group 0 writes the builder's outputs
+  // tree (lane = node); wave 0 of the last piece of KV head 0, query group 0
+  // writes the builder's outputs
   uint64_t anc_w = 0;
   if (a.parents) {
     const TreeLinks t = tree_links_wave(a.parents + (size_t)u.b * N, N);
     anc_w = t.anc;
-    if (u.kvh == 0 && u.qgroup == 0 && u.split == a.splits - 1 && threadIdx.x < 64)
+    if (u.kvh == 0 && u.qgroup == 0 && u.split == u.nsplit - 1 && threadIdx.x < 64)
       write_tree_outputs(a, u.b, t);
   }
 #pragma unroll
@@ -278,94 +375,30 @@ __device__ __forceinline__ void load_queries(const AttnArgs& a, const UnitCtx& u
   }
 }
 
-// Merge the states of the waves that hold the same query rows (o-th such wave
-// at index base + o * stride), into wave 0 of the group, through LDS.
-template <int QBW, int NDB, int NW>
-__device__ __forceinline__ void merge_waves(f32x4 (&acc)[QBW][NDB], float (&m_run)[QBW],
-                                            float (&l_run)[QBW], float* mb, int me, int first,
-                                            int stride) {
-  constexpr int PER_WAVE = QBW * NDB * 256 + QBW * 32;
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  __syncthreads();
-  if (me != first) {
-    float* my = mb + me * PER_WAVE;
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<f32x4*>(my + ((qb * NDB + db) * 64 + lane) * 4) = acc[qb][db];
-      if (g == 0) {
-        my[QBW * NDB * 256 + qb * 32 + c] = m_run[qb];
-        my[QBW * NDB * 256 + qb * 32 + 16 + c] = l_run[qb];
-      }
-    }
-  }
-  __syncthreads();
-  if (me == first) {
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      float mt = m_run[qb];
-#pragma unroll
-      for (int o = 1; o < NW; ++o)
-        mt = fmaxf(mt, mb[(first + o * stride) * PER_WAVE + QBW * NDB * 256 + qb * 32 + c]);
-      const float mu = mt == -INFINITY ? 0.f : mt;
-      const float fs = __builtin_amdgcn_exp2f(m_run[qb] - mu);
-      float lt = l_run[qb] * fs;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[qb][db] *= fs;
-#pragma unroll
-      for (int o = 1; o < NW; ++o) {
-        const float* other = mb + (first + o * stride) * PER_WAVE;
-        const float fo = __builtin_amdgcn_exp2f(other[QBW * NDB * 256 + qb * 32 + c] - mu);
-        lt += other[QBW * NDB * 256 + qb * 32 + 16 + c] * fo;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          acc[qb][db] += *reinterpret_cast<const f32x4*>(other + ((qb * NDB + db) * 64 + lane) * 4) * fo;
-      }
-      m_run[qb] = mt;
-      l_run[qb] = lt;
-    }
-  }
-  __syncthreads();  // the merge buffers may now be reused
-}
-
 // ============================================================================
-// ring kernel: committed prefix only, one direct-to-LDS chunk slot per wave
+// ring kernel: one direct-to-LDS chunk slot per wave
 // ============================================================================
-// Eight waves, each with one 32-key K/V slot in LDS.  The chunks of a split
+// Eight waves, each with one 32-key K/V slot in LDS.  The chunks of a piece
 // are dealt to them round robin; a wave waits for its chunk, computes it and
 // refills the slot with its next chunk, while the other seven keep theirs in
 // flight (two waves per SIMD hide each other's MFMA and softmax latency).
-// The split ranges are laid over the cache capacity Lmax - N, not over
-// kv_len, so the first loads go out before anything else is read; keys at or
-// past kv_len are masked.  The tree keys (each query's ancestors and itself,
-// N <= 64 of them) are one or two more chunks, masked by the ancestor bits,
-// for one wave of the last split.
-//
-// A workgroup holds RW query rows.  With more rows per KV head (grouped-query
-// attention, G*N > RW) the rows are cut into query groups, each a unit of its
-// own that streams the same K/V; those units sit on one XCD so that the
-// repeats come from its L2, and their loads use the default cache policy
-// instead of the non-temporal one.
+// The tree keys (each query's ancestors and itself, N <= 64 of them) are one
+// or two more chunks, masked by the ancestor bits, for the wave of the last
+// piece with the fewest committed chunks.
 constexpr int kRingThreads = 64 * 8;
 constexpr int kNonTemporal = 2;  // cache-policy bits of a load: nt
 
-// One lane's 16-byte direct-to-LDS load; the cache policy is a literal in
-// each branch (a template-dependent policy argument made hipcc drop the
-// kernel instantiations without a diagnostic).
-template <int POLICY>
+// One lane's 16-byte direct-to-LDS load, non-temporal: the K/V stream is read
+// once, and per XCD it is about the size of the L2.
 __device__ __forceinline__ void load_lds16(const uint16_t* src, uint8_t* dst) {
-  if constexpr (POLICY == kNonTemporal)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, kNonTemporal);
-  else
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                   kNonTemporal);
 }
 
-template <int D_, int QBW_, int POLICY_ = kNonTemporal>
+template <int D_, int QBW_>
 struct RingShape {
   static constexpr int D = D_;
   static constexpr int QBW = QBW_;
-  static constexpr int POLICY = POLICY_;  // cache-policy bits of the K/V loads
   static constexpr int NWAVE = 8;
   static constexpr int THREADS = 64 * NWAVE;
   static constexpr int MAT_BYTES = 32 * D * 2;    // K (or V) of one 32-key chunk
@@ -429,12 +462,6 @@ __device__ __forceinline__ void fold_waves(const f32x4 (&acc)[QBW][NDB], const f
     const float inv = lt == 0.f ? 0.f : 1.f / lt;
     emit(rl, db, o * inv, lt == 0.f ? -INFINITY : mt + __log2f(lt));
   }
-}
-
-// A wave-uniform 32-bit value read with a scalar load (constant address
-// space), which the compiler tracks apart from the vector loads in flight.
-__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
 // Valid committed keys among key0..key0+7 (keys below L) as an 8-bit mask.
@@ -548,71 +575,96 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
 
-  // workgroup -> (unit, split): all splits of a unit on one XCD
-  const int xcd = blockIdx.x % kNumXCDs, slotw = blockIdx.x / kNumXCDs;
-  const int split = slotw % a.splits;
-  const int unit = (slotw / a.splits) * kNumXCDs + xcd;
-  if (unit >= a.units) return;
-  // unit -> (pair = b * Hkv + kvh, query group of RW rows).  The query groups
-  // of a pair are consecutive units of one XCD, so they are resident together
-  // and stream the same K/V through that XCD's L2 (read from HBM about once).
-  const int ux = unit / kNumXCDs;
-  const int qgroup = ux % a.qgroups;
-  const int pair = (ux / a.qgroups) * kNumXCDs + xcd;
-  if (pair >= a.B * a.Hkv) return;
-  const int kvh = pair % a.Hkv;
-  const int b = pair / a.Hkv;
-  const int row0 = qgroup * RW;  // first query row (of the pair's G*N) of this unit
+  const int slot_w = logical_slot(a);
+  const int r_in = lane / SPR, p_in = lane % SPR;
+  uint8_t* slot = lds + wave * S::SLOT_BYTES;
+  // Direct-to-LDS fill of 32 keys from key0: lane l writes 16 bytes at load
+  // base + 16 l, i.e. row t*RPL + l/SPR, slot l%SPR, which receives global
+  // slot (l%SPR)^swz(row).  Rows past key_max re-read it (a key of J, masked
+  // later).
+  auto issue_keys_at = [&](const uint16_t* kp, const uint16_t* vp, int key0, int key_max) {
+#pragma unroll
+    for (int t = 0; t < LPM; ++t) {
+      const int r = t * RPL + r_in;
+      const int key = min(key0 + r, key_max);
+      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
+      load_lds16(kp + off, slot + t * RPL * D * 2);
+    }
+#pragma unroll
+    for (int t = 0; t < LPM; ++t) {
+      const int r = t * RPL + r_in;
+      const int key = min(key0 + r, key_max);
+      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
+      load_lds16(vp + off, slot + S::MAT_BYTES + t * RPL * D * 2);
+    }
+  };
 
-  // this split's chunks of the capacity prefix; wave w takes cb + w, cb + w + NWAVE, ...
-  const int Lp = a.Lmax - a.N;
-  const int n_chunks = (Lp + 31) / 32;
-  const int cb = (int)((long long)split * n_chunks / a.splits);
-  const int ce = (int)((long long)(split + 1) * n_chunks / a.splits);
+  // The piece this slot would hold if every sequence filled the cache (the
+  // common case) needs no memory read: the wave issues its first chunk under
+  // that assumption while the committed lengths are read, and keeps it only
+  // if the real plan agrees (the chunk lies in [0, L) then); otherwise the
+  // loads are waited for and their data discarded before the slot is reused.
+  const int kvl0 = kv_len_lanes(a);  // scalar loads first (B <= 16): no wait behind the chunk
+  const int Lcap = a.Lmax - a.N;
+  const int cap_chunks = (Lcap + 31) / 32;
+  int spec_unit = -1, spec_split = 0, spec_chunk = -1;
+  if (a.full_pieces > 0 && slot_w < a.B * a.Hkv * a.full_pieces) {
+    spec_unit = slot_w / a.full_pieces;
+    spec_split = slot_w - spec_unit * a.full_pieces;
+    const int scb = (int)((long long)spec_split * cap_chunks / a.full_pieces);
+    const int sce = (int)((long long)(spec_split + 1) * cap_chunks / a.full_pieces);
+    if (scb + wave < sce) {
+      spec_chunk = scb + wave;
+      const size_t sbase = (size_t)spec_unit * (size_t)a.Lmax * D;  // unit = b * Hkv + kvh
+      issue_keys_at(a.k + sbase, a.v + sbase, spec_chunk * 32, Lcap - 1);
+    }
+  }
+
+  // slot -> piece (every wave finds it; the committed lengths decide it)
+  Piece pc;
+  if (!plan_piece(a, slot_w, kvl0, pc)) {
+    if (spec_chunk >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+  const int b = pc.b, kvh = pc.kvh, L = pc.L;
+  const bool bad = pc.bad;
+  if (bad && a.flags && pc.split == 0 && kvh == 0 && tid == 0)
+    atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+
+  // this piece's 32-key chunks of [0, L); wave w takes cb + w, cb + w + NWAVE, ...
+  const int n_chunks = (L + 31) / 32;
+  const int cb = (int)((long long)pc.split * n_chunks / pc.nsplit);
+  const int ce = (int)((long long)(pc.split + 1) * n_chunks / pc.nsplit);
   const int my_first = cb + wave;
   const int my_n = my_first < ce ? (ce - my_first + NWAVE - 1) / NWAVE : 0;
+  const bool last_piece = pc.split == pc.nsplit - 1;
 
   const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
   const uint16_t* kp = a.k + kv_base;
   const uint16_t* vp = a.v + kv_base;
-  uint8_t* slot = lds + wave * S::SLOT_BYTES;
-
-  // Direct-to-LDS fill of 32 keys from key0: lane l writes 16 bytes at load
-  // base + 16 l, i.e. row t*RPL + l/SPR, slot l%SPR, which receives global
-  // slot (l%SPR)^swz(row).  Rows past key_max re-read it (finite data, masked
-  // later).  The stream is read once: non-temporal loads (nt) keep it from
-  // evicting the split partials that the unit's last split reads back from
-  // this XCD's L2 (the stream per XCD is about the size of its L2).
-  const int r_in = lane / SPR, p_in = lane % SPR;
-  auto issue_keys = [&](int key0, int key_max) {
-#pragma unroll
-    for (int t = 0; t < LPM; ++t) {
-      const int r = t * RPL + r_in;
-      const int key = min(key0 + r, key_max);
-      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
-      load_lds16<S::POLICY>(kp + off, slot + t * RPL * D * 2);
-    }
-#pragma unroll
-    for (int t = 0; t < LPM; ++t) {
-      const int r = t * RPL + r_in;
-      const int key = min(key0 + r, key_max);
-      const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
-      load_lds16<S::POLICY>(vp + off, slot + S::MAT_BYTES + t * RPL * D * 2);
-    }
-  };
-  auto issue = [&](int gc) { issue_keys(gc * 32, Lp - 1); };
-  if (my_n > 0) issue(my_first);
+  auto issue_keys = [&](int key0, int key_max) { issue_keys_at(kp, vp, key0, key_max); };
+  auto issue = [&](int gc) { issue_keys(gc * 32, L - 1); };
   // The tree keys [L, L + N) are one or two more masked chunks (N <= 64),
-  // taken by the wave of the last split with the fewest prefix chunks.
-  const bool tree_wave = split == a.splits - 1 && wave == (ce - cb) % NWAVE;
+  // taken by the wave of the last piece with the fewest committed chunks.
+  const bool tree_wave = last_piece && wave == (ce - cb) % NWAVE;
+  const bool spec_kept = spec_chunk >= 0 && my_n > 0 && spec_chunk == my_first &&
+                         spec_unit == pc.unit && spec_split == pc.split &&
+                         pc.nsplit == a.full_pieces && L == Lcap;
+  if (!spec_kept) {
+    if (spec_chunk >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // discarded
+    if (my_n > 0)
+      issue(my_first);
+    else if (tree_wave)
+      issue_keys(L, L + a.N - 1);
+  }
 
   // A wave with three or more chunks loads its second one into registers
   // right away, so that it is in flight with the first instead of requested
   // once the first has been computed (the slot is busy until then); it is
   // written to the slot in the layout a direct-to-LDS load gives.  (Measured
   // on MI355X: llama2-13b shape, ~5 chunks per wave, 60.9 us against 62.7;
-  // with only two chunks, as at the llama2-7b shape, waiting for both before
-  // the first is computed costs more than it saves: 15.2 us against 14.2.)
+  // with two chunks, waiting for both before the first is computed costs more
+  // than it saves: 15.2 us against 14.2 at the llama2-7b shape.)
   const int my_chunks = my_n + (tree_wave ? (a.N + 31) / 32 : 0);
   const bool pre2 = my_chunks >= 3;  // wave-uniform
   u32x4 pre[2 * LPM];
@@ -625,19 +677,12 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       pre[LPM + t] = *reinterpret_cast<const u32x4*>(vp + off);
     }
   };
-  if (pre2 && 1 < my_n) load_pre((my_first + NWAVE) * 32, Lp - 1);
-
-  // committed length (a scalar load: waiting for it does not wait for the
-  // chunks' vector loads), then the queries, needed once the first chunk is in
-  int L = load_uniform(a.kv_len + b);
-  const bool bad = L < 0 || L > Lp;
-  if (bad) {
-    L = 0;
-    if (a.flags && split == 0 && kvh == 0 && qgroup == 0 && tid == 0)
-      atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+  if (pre2) {
+    if (1 < my_n)
+      load_pre((my_first + NWAVE) * 32, L - 1);
+    else
+      load_pre(L + 32 * (1 - my_n), L + a.N - 1);  // a tree chunk second
   }
-  if (tree_wave && my_n == 0) issue_keys(L, L + a.N - 1);
-  if (pre2 && my_n <= 1) load_pre(L + 32 * (1 - my_n), L + a.N - 1);  // a tree chunk second
   // the tree wave's rows' ancestor masks: bit t of anc[row] admits key L + t
   uint64_t anc_q[QBW];
   if (tree_wave) {
@@ -648,24 +693,24 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       const TreeLinks t = tree_links_wave(a.parents + (size_t)b * a.N, a.N);
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
-        const int row = row0 + qb * 16 + c;
+        const int row = qb * 16 + c;
         const uint64_t m = __shfl(t.anc, row < a.M ? row / a.G : 0);
         anc_q[qb] = row < a.M ? m & nmask : 0ull;
       }
-      if (kvh == 0 && qgroup == 0) write_tree_outputs(a, b, t);
+      if (kvh == 0) write_tree_outputs(a, b, t);
     } else {
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) {
-        const int row = row0 + qb * 16 + c;
+        const int row = qb * 16 + c;
         anc_q[qb] = row < a.M ? a.anc[(size_t)b * a.N + row / a.G] & nmask : 0ull;
       }
     }
   }
-  const int rows = min(RW, a.M - row0);
+  const int rows = a.M;  // <= RW
   bf16x8 qf[QBW][NKS];
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
-    const int row = row0 + qb * 16 + c;
+    const int row = qb * 16 + c;
     if (row < a.M) {
       const int i = row / a.G;
       const int h = kvh * a.G + (row - i * a.G);
@@ -720,17 +765,16 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
-  // the folded rows go from registers to the output (one split) or to this
-  // split's partial (O / l and log2-sum-exp)
+  // the folded rows go from registers to the output (one piece) or to this
+  // piece's partial (O / l and log2-sum-exp)
   float* ml = reinterpret_cast<float*>(lds + S::LDS_RING);
   constexpr int D4 = D / 4;
-  auto out_row = [&](int rl) {
-    const int row = row0 + rl;
+  auto out_row = [&](int row) {
     const int i = row / a.G;
     const int h = kvh * a.G + (row - i * a.G);
     return a.out + (((size_t)b * a.N + i) * a.Hq + h) * D;
   };
-  if (a.splits == 1) {
+  if (pc.nsplit == 1) {
     fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(
         acc, m_run, l_run, lds, ml, wave, rows, [&](int rl, int db, f32x4 o, float) {
           if (bad) o = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -739,38 +783,42 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
         });
     return;
   }
-  const size_t pbase = ((size_t)unit * a.splits + split) * RW;
+  const size_t pbase = (size_t)slot_w * RW;
   fold_waves<QBW, NDB, NWAVE, S::SLOT_BYTES>(
       acc, m_run, l_run, lds, ml, wave, rows, [&](int rl, int db, f32x4 o, float lse) {
-        *reinterpret_cast<f32x4*>(a.part_o + (pbase + rl) * D + db * 16 + 4 * g) = o;
-        if (db == 0 && g == 0) a.part_lse[pbase + rl] = lse;
+        store_coherent(a.part_o + (pbase + rl) * D + db * 16 + 4 * g, o);
+        if (db == 0 && g == 0) store_coherent(a.part_lse + pbase + rl, lse);
       });
 
-  // The unit's last split to finish combines the partials.  All splits of a
-  // unit run on one XCD, so its L2 is where they meet: each workgroup's
-  // stores have reached it (vmcnt) before the workgroup takes its ticket,
-  // and the combining workgroup's loads miss its own L1, which held none of
-  // these lines since the kernel started.
+  // The unit's last piece to finish combines the partials: each workgroup's
+  // coherent stores have completed (vmcnt) before it takes the unit's ticket,
+  // and the combining workgroup reads them with coherent loads issued after
+  // its ticket returned.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int* last = reinterpret_cast<int*>(ml);
   if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(a.tickets + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *last = done == a.splits - 1;
-    if (done == a.splits - 1) __hip_atomic_store(a.tickets + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int done =
+        __hip_atomic_fetch_add(a.tickets + pc.unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = done == pc.nsplit - 1;
+    if (done == pc.nsplit - 1)
+      __hip_atomic_store(a.tickets + pc.unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!*last) return;
   // (row, 4 columns) items: w_s = 2^(lse_s - max), o = sum w_s O_s / sum w_s.
-  // The splits go in batches of 8, and a thread's two items share a batch,
+  // The pieces go in batches of 8, and a thread's two items share a batch,
   // so that every load of a batch is issued before any is used.
-  const size_t ub = (size_t)unit * a.splits * RW;
+  const size_t ub = (size_t)pc.first * RW;
   const int total = rows * D4;
+  const int S_ = pc.nsplit;
+  // the unit's partials as one buffer range (its pieces' slots are consecutive)
+  const __amdgpu_buffer_rsrc_t po = buffer_rsrc(a.part_o + ub * D, (size_t)S_ * RW * D * 4);
   for (int it0 = tid; it0 < total; it0 += 2 * S::THREADS) {
     const int its[2] = {it0, it0 + S::THREADS};
     float mt[2] = {-INFINITY, -INFINITY}, lt[2] = {0.f, 0.f};
     f32x4 o[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+    for (int s0 = 0; s0 < S_; s0 += 8) {
       float ls[2][8];
       f32x4 os[2][8];
 #pragma unroll
@@ -779,10 +827,10 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
         const int rl = it / D4, d4 = it - rl * D4;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const bool in = s0 + q < a.splits;
-          const size_t r = ub + (size_t)(in ? s0 + q : 0) * RW + rl;  // in range either way
-          ls[u][q] = in ? a.part_lse[r] : -INFINITY;
-          os[u][q] = in ? *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * d4)
+          const bool in = s0 + q < S_;
+          const int sq = in ? s0 + q : 0;  // in range either way
+          ls[u][q] = in ? load_coherent(a.part_lse + ub + (size_t)sq * RW + rl) : -INFINITY;
+          os[u][q] = in ? load_coherent4(po, (uint32_t)(((sq * RW + rl) * D + 4 * d4) * 4))
                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
@@ -797,9 +845,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
         o[u] *= f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float w = ls[u][q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u][q] - mb);
-          lt[u] += w;
-          o[u] += os[u][q] * w;
+          const float wq = ls[u][q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u][q] - mb);
+          lt[u] += wq;
+          o[u] += os[u][q] * wq;
         }
         mt[u] = mb;
       }
@@ -816,200 +864,10 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
 }
 
 // ============================================================================
-// tile kernel: shared LDS tiles, waves split the query rows (grouped queries)
-// ============================================================================
-template <int D_, int QBW_, int WQ_, int KC_>
-struct TileShape {
-  static constexpr int D = D_;
-  static constexpr int QBW = QBW_;          // 16-row query blocks per wave
-  static constexpr int WQ = WQ_;            // waves across query blocks
-  static constexpr int WK = 4 / WQ_;        // waves across keys
-  static constexpr int KC = KC_;            // 32-key chunks per wave per tile
-  static constexpr int KT = 32 * KC * WK;   // keys per tile
-  static constexpr int RW = 16 * QBW * WQ;  // query rows per workgroup
-  static constexpr int KS = D + 8;          // K tile row stride (bf16 elements)
-  static constexpr int VS = KT + 8;         // V^T tile row stride (bf16 elements)
-  static constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  static constexpr int KG = 256 / CPR;      // key quads per staging pass
-  static constexpr int NQ = KT / 4;         // key quads per tile
-  static constexpr int PASSES = (NQ + KG - 1) / KG;
-  static constexpr int NKS = D / 32;
-  static constexpr int NDB = D / 16;
-  static constexpr int LDS_TILE = (KT * KS + D * VS) * 2;
-  static constexpr int LDS_MERGE = WK > 1 ? 4 * (QBW * NDB * 256 + QBW * 32) * 4 : 0;
-  static constexpr int LDS_STAGE = RW * (D + 4) * 4;
-  static constexpr int LDS_A = LDS_TILE > LDS_MERGE ? LDS_TILE : LDS_MERGE;
-  static constexpr int LDS_BYTES = LDS_A > LDS_STAGE ? LDS_A : LDS_STAGE;
-  static_assert(NQ >= 8 && (NQ & (NQ - 1)) == 0, "V^T swizzle needs >= 8 key quads, power of 2");
-};
-
-__device__ __forceinline__ uint32_t pick_half(uint32_t w, int hi) {
-  return hi ? (w >> 16) : (w & 0xffffu);
-}
-
-template <class S>
-__global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
-  constexpr int D = S::D, QBW = S::QBW, WQ = S::WQ, KC = S::KC, KT = S::KT, RW = S::RW;
-  constexpr int KS = S::KS, VS = S::VS, CPR = S::CPR, KG = S::KG, NQ = S::NQ;
-  constexpr int NKS = S::NKS, NDB = S::NDB;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::LDS_BYTES];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds_raw);
-  uint16_t* Vt = Ks + KT * KS;
-
-  UnitCtx u;
-  if (!decode_unit(a, u)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wq = wave % WQ;
-  const int wk = wave / WQ;
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  const int L = u.L, total = u.total;
-  const int n_tiles = (total + KT - 1) / KT;
-  const int t_begin = (int)((long long)u.split * n_tiles / a.splits);
-  const int t_end = (int)((long long)(u.split + 1) * n_tiles / a.splits);
-
-  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
-  const uint16_t* kp = a.k + kv_base;
-  const uint16_t* vp = a.v + kv_base;
-
-  const int r0 = wq * QBW * 16;
-  bf16x8 qf[QBW][NKS];
-  uint64_t anc_q[QBW];
-  load_queries<D, QBW, RW>(a, u, r0, qf, anc_q);
-
-  f32x4 acc[QBW][NDB];
-  float m_run[QBW], l_run[QBW];
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // staging: thread -> (16-byte chunk dc of a key row, key quad kq)
-  const int dc = tid % CPR;
-  const int kq0 = tid / CPR;
-  u32x4 kreg[S::PASSES][4], vreg[S::PASSES][4];
-
-  auto load_tile = [&](int t) {
-    const int base = t * KT;
-#pragma unroll
-    for (int p = 0; p < S::PASSES; ++p) {
-      const int kq = kq0 + p * KG;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = base + 4 * kq + i;
-        if (kq < NQ && key < total) {
-          const size_t off = (size_t)key * D + dc * 8;
-          kreg[p][i] = *reinterpret_cast<const u32x4*>(kp + off);
-          vreg[p][i] = *reinterpret_cast<const u32x4*>(vp + off);
-        } else {
-          kreg[p][i] = u32x4{0, 0, 0, 0};
-          vreg[p][i] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int p = 0; p < S::PASSES; ++p) {
-      const int kq = kq0 + p * KG;
-      if (kq < NQ) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4*>(Ks + (4 * kq + i) * KS + dc * 8) = kreg[p][i];
-        // V^T: element (d, key) at row d, key quad kq stored at quad kq ^ (d >> 4).
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int d = dc * 8 + j;
-          const int pq = kq ^ (d >> 4);
-          const int wsel = j >> 1, hi = j & 1;
-          const uint32_t lo = pick_half(vreg[p][0][wsel], hi) | (pick_half(vreg[p][1][wsel], hi) << 16);
-          const uint32_t up = pick_half(vreg[p][2][wsel], hi) | (pick_half(vreg[p][3][wsel], hi) << 16);
-          *reinterpret_cast<u32x2*>(Vt + d * VS + pq * 4) = u32x2{lo, up};
-        }
-      }
-    }
-  };
-
-  if (t_begin < t_end) load_tile(t_begin);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1);  // in flight while this tile is computed
-
-    const int tile_base = t * KT;
-    const bool need_mask = tile_base + KT > L;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int chunk = wk * KC + kc;
-      f32x4 s[QBW][2];
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int krow = chunk * 32 + 8 * (c >> 2) + 4 * hlf + (c & 3);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + krow * KS + ks * 32 + g * 8);
-#pragma unroll
-          for (int qb = 0; qb < QBW; ++qb)
-            s[qb][hlf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], s[qb][hlf], 0, 0, 0);
-        }
-      }
-      const int key0 = tile_base + chunk * 32 + 8 * g;
-      bf16x8 pf[QBW];
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = s[qb][j >> 2][j & 3] * a.scale_log2;
-        if (need_mask) {
-          const uint32_t ok = key_mask8(key0, L, anc_q[qb]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = ((ok >> j) & 1u) ? x[j] : -INFINITY;
-        }
-        pf[qb] = softmax_step<NDB>(x, m_run[qb], l_run[qb], acc[qb]);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = db * 16 + c;
-        const int q0 = chunk * 8 + 2 * g;
-        const int pq = (q0 ^ db) & ~1;
-        bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + d * VS + pq * 4);
-        if (db & 1) vf = __builtin_shufflevector(vf, vf, 4, 5, 6, 7, 0, 1, 2, 3);
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb)
-          acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], acc[qb][db], 0, 0, 0);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    l_run[qb] += __shfl_xor(l_run[qb], 16);
-    l_run[qb] += __shfl_xor(l_run[qb], 32);
-  }
-  if constexpr (S::WK > 1) {
-    merge_waves<QBW, NDB, S::WK>(acc, m_run, l_run, reinterpret_cast<float*>(lds_raw), wave, wq, WQ);
-  } else {
-    __syncthreads();  // tile buffers may be reused for the split weights
-  }
-  finish_split<D, RW, QBW>(a, u.unit, u.split, u.qgroup, u.b, u.kvh, u.bad, wk == 0, r0, acc,
-                           m_run, l_run, lds_raw);
-}
-
-// ============================================================================
 // group kernel: a head group's query rows share a ring of K/V tiles in LDS
 // ============================================================================
 // Grouped-query attention with up to 256 query rows per (b, KV head): eight
-// waves, each owning 32 of the rows, compute every 64-key tile of the split
+// waves, each owning 32 of the rows, compute every 64-key tile of the piece
 // against their own rows, so a tile is read from HBM once for the whole
 // head group and no wave has to merge with another.  The tiles stream
 // through NBUF LDS buffers, NBUF - 1 of them in flight while one is
@@ -1020,11 +878,11 @@ __global__ __launch_bounds__(256) void tree_attn_tile_kernel(AttnArgs a) {
 // tracked here instead: before tile i a wave waits until at most its own
 // loads of the tiles after i are outstanding (vector loads complete in
 // order), and one LDS-only barrier then makes tile i whole for all waves and
-// frees the buffer of tile i - 1 for tile i + NBUF - 1.  The last split
-// also computes the tree keys [L, L + N) as one more tile.  Rows O / l and
-// log2-sum-exp of a split go straight from registers to the partials (the
-// merge kernel combines splits: the unit's last split combining them, as the
-// ring kernel does, took longer, 63 against 59 us at the llama2-70b shape,
+// frees the buffer of tile i - 1 for tile i + NBUF - 1.  The last piece also
+// computes the tree keys [L, L + N) as one more tile.  Rows O / l and
+// log2-sum-exp of a piece go straight from registers to the partials, which
+// the merge kernel combines (the unit's last piece combining them, as the
+// ring kernel does, took longer: 63 against 59 us at the llama2-70b shape,
 // one workgroup reading 4 x 208 rows), or the bf16 rows to the output.
 template <int D_>
 struct GroupShape {
@@ -1078,38 +936,12 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
 
-  // workgroup -> (unit, split) as for the shared-tile kernel: the splits of a
-  // unit share an XCD; unit = pair * qgroups + qgroup
-  UnitCtx u;
-  {
-    const int xcd = blockIdx.x % kNumXCDs, slotw = blockIdx.x / kNumXCDs;
-    u.split = slotw % a.splits;
-    u.unit = (slotw / a.splits) * kNumXCDs + xcd;
-    if (u.unit >= a.units) return;
-    u.qgroup = u.unit % a.qgroups;
-    u.pair = u.unit / a.qgroups;
-    u.kvh = u.pair % a.Hkv;
-    u.b = u.pair / a.Hkv;
-  }
-  const int r0 = wave * QBW * 16;                  // this wave's first row in the unit
-  const bool active = u.qgroup * RW + r0 < a.M;   // wave-uniform: the wave has rows
-
-  // this split's 64-key tiles of the capacity prefix; the last split adds the tree tile
-  const int Lp = a.Lmax - a.N;
-  const int n_tiles = (Lp + S::TILE_KEYS - 1) / S::TILE_KEYS;
-  const int tb = (int)((long long)u.split * n_tiles / a.splits);
-  const int te = (int)((long long)(u.split + 1) * n_tiles / a.splits);
-  const int n_pre = te - tb;
-  const bool tree_split = u.split == a.splits - 1;
-  const int n_my = n_pre + (tree_split ? 1 : 0);
-
-  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
-  const uint16_t* kp = a.k + kv_base;
-  const uint16_t* vp = a.v + kv_base;
+  const int slot_w = logical_slot(a);
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
   const int r_in = lane / SPR, p_in = lane % SPR;
-  // tile position j: keys key0.. (chunk h at key0 + 32 h), rows past key_max re-read it
-  auto issue_tile = [&](int j, int key0, int key_max) {
+  // tile position j: keys key0.. (chunk h at key0 + 32 h), rows past key_max
+  // re-read it (a key of J, masked later)
+  auto issue_tile_at = [&](const uint16_t* kp, const uint16_t* vp, int j, int key0, int key_max) {
 #pragma unroll
     for (int e = 0; e < LPW; ++e) {
       const int li = wave * LPW + e;
@@ -1122,26 +954,66 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
       lds_dma16(src, __builtin_amdgcn_readfirstlane(dst));
     }
   };
-  int L = 0;
+
+  // As in the ring kernel: the first tiles of the piece this slot would hold
+  // if every sequence filled the cache go out before the plan is known, and
+  // are kept only if the real plan agrees (else waited for and discarded).
+  const int kvl0 = kv_len_lanes(a);
+  const int Lcap = a.Lmax - a.N;
+  const int cap_tiles = (Lcap + S::TILE_KEYS - 1) / S::TILE_KEYS;
+  const int U = a.Hkv * a.qgroups;
+  int spec_unit = -1, spec_split = 0, spec_n = 0;
+  if (a.full_pieces > 0 && slot_w < a.B * U * a.full_pieces) {
+    spec_unit = slot_w / a.full_pieces;
+    spec_split = slot_w - spec_unit * a.full_pieces;
+    const int stb = (int)((long long)spec_split * cap_tiles / a.full_pieces);
+    const int ste = (int)((long long)(spec_split + 1) * cap_tiles / a.full_pieces);
+    spec_n = min(NBUF - 1, ste - stb);
+    const size_t sbase = (size_t)(spec_unit / a.qgroups) * (size_t)a.Lmax * D;  // pair b * Hkv + kvh
+    for (int j = 0; j < spec_n; ++j)
+      issue_tile_at(a.k + sbase, a.v + sbase, j, (stb + j) * S::TILE_KEYS, Lcap - 1);
+  }
+  Piece u;
+  if (!plan_piece(a, slot_w, kvl0, u)) {
+    if (spec_n > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+  const int L = u.L;
+  if (tid == 0) {
+    if (u.bad && a.flags && u.split == 0 && u.qgroup == 0 && u.kvh == 0)
+      atomicOr(a.flags + u.b, EAGLE_FLAG_BAD_KV_LEN);
+    if (u.split == 0 && a.unit_info) {  // for the merge kernel (absent: one piece per unit)
+      a.unit_info[2 * u.unit] = u.first;
+      a.unit_info[2 * u.unit + 1] = u.nsplit;
+    }
+  }
+  const int r0 = wave * QBW * 16;                 // this wave's first row in the unit
+  const bool active = u.qgroup * RW + r0 < a.M;  // wave-uniform: the wave has rows
+
+  // this piece's 64-key tiles of [0, L); the last piece adds the tree tile
+  const int n_tiles = (L + S::TILE_KEYS - 1) / S::TILE_KEYS;
+  const int tb = (int)((long long)u.split * n_tiles / u.nsplit);
+  const int te = (int)((long long)(u.split + 1) * n_tiles / u.nsplit);
+  const int n_pre = te - tb;
+  const bool tree_split = u.split == u.nsplit - 1;
+  const int n_my = n_pre + (tree_split ? 1 : 0);
+
+  const size_t kv_base = ((size_t)u.b * a.Hkv + u.kvh) * (size_t)a.Lmax * D;
+  const uint16_t* kp = a.k + kv_base;
+  const uint16_t* vp = a.v + kv_base;
   auto issue = [&](int j) {
     if (j < n_pre)
-      issue_tile(j, (tb + j) * S::TILE_KEYS, Lp - 1);
+      issue_tile_at(kp, vp, j, (tb + j) * S::TILE_KEYS, L - 1);
     else
-      issue_tile(j, L, L + a.N - 1);  // the tree tile
+      issue_tile_at(kp, vp, j, L, L + a.N - 1);  // the tree tile
   };
-  // prefix tiles go out first; the tree tile needs kv_len
+  // the tiles the speculation issued are those of positions 0..spec_n - 1
+  // when the plans agree (then spec_n <= n_pre)
+  const bool spec_kept = spec_n > 0 && spec_unit == u.unit && spec_split == u.split &&
+                         u.nsplit == a.full_pieces && L == Lcap;
+  if (spec_n > 0 && !spec_kept) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // discarded
   const int n_pro = min(NBUF - 1, n_my);
-  for (int j = 0; j < min(n_pro, n_pre); ++j) issue(j);
-  L = load_uniform(a.kv_len + u.b);  // scalar: no wait for the tiles in flight
-  u.bad = L < 0 || L > Lp;
-  if (u.bad) {
-    L = 0;
-    if (a.flags && u.split == 0 && u.qgroup == 0 && u.kvh == 0 && tid == 0)
-      atomicOr(a.flags + u.b, EAGLE_FLAG_BAD_KV_LEN);
-  }
-  u.L = L;
-  u.total = L + a.N;
-  for (int j = n_pre; j < n_pro; ++j) issue(j);
+  for (int j = spec_kept ? spec_n : 0; j < n_pro; ++j) issue(j);
 
   // every wave computes (rows past M hold zero queries and no tree bits):
   // a wave-uniform skip inside the tile loop made the compiler copy the
@@ -1160,8 +1032,8 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // prefix tiles; the tree tile (position n_pre, if this split has it) after
-  // the loop, so that the loop body has no join for the compiler to copy at
+  // committed tiles; the tree tile (position n_pre, if this piece has it)
+  // after the loop, so that the loop body has no join for the compiler to copy at
   for (int i = 0; i < n_pre; ++i) {
     wait_tiles_after<LPW>(min(NBUF - 2, n_my - 1 - i));
     barrier_lds();  // tile i is whole; every wave is done with tile i - 1
@@ -1195,13 +1067,13 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
-  const size_t pbase = ((size_t)u.unit * a.splits + u.split) * RW;
+  const size_t pbase = (size_t)slot_w * RW;
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
     const int rl = r0 + qb * 16 + c;
     const int row = u.qgroup * RW + rl;
     if (row >= a.M) continue;
-    if (a.splits == 1) {
+    if (u.nsplit == 1) {
       const int i = row / a.G;
       const int h = u.kvh * a.G + (row - i * a.G);
       uint16_t* orow = a.out + (((size_t)u.b * a.N + i) * a.Hq + h) * D;
@@ -1224,22 +1096,29 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
 }
 
 // ============================================================================
-// merge (group and tile kernels): the splits' partials of a query row combined
+// merge (group kernel): the pieces' partials of a query row combined
 // ============================================================================
 // A thread per 16-byte column of a row (D / 4 threads per row): it loads the
-// log2-sum-exp and the O / l column of every split, eight splits at a time
+// log2-sum-exp and the O / l column of every piece, eight pieces at a time
 // with every load of a batch issued before any is used, rescales online, and
-// writes four bf16 outputs.
+// writes four bf16 outputs.  The pieces of a unit (first slot, count) come
+// from the group kernel through the workspace (scalar loads); the kernel
+// boundary makes them and the partials visible.  The first batch is loaded
+// for the pieces the unit has when every sequence fills the cache while the
+// piece table is read, and again only if the table disagrees.  Workgroup ids
+// are laid out so that a unit's workgroups run on the XCD whose slots held
+// its pieces in that case (slots are dealt to XCDs in equal consecutive runs).
 template <int D>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW) {
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW, int units) {
   constexpr int C4 = D / 4;        // 16-byte columns per row
   constexpr int RPB = 256 / C4;    // rows per workgroup
-  // a unit's RW / RPB workgroups run on the XCD whose workgroups wrote its
-  // partials (unit mod 8), so its reads can hit that XCD's L2
   const int bpu = RW / RPB;
-  const int x = blockIdx.x % kNumXCDs, q = blockIdx.x / kNumXCDs;
-  const int unit = (q / bpu) * kNumXCDs + x;
-  if (unit >= a.units) return;
+  const int per_xcd = (units + kNumXCDs - 1) / kNumXCDs;
+  const int q = (int)blockIdx.x / kNumXCDs;
+  const int unit = ((int)blockIdx.x % kNumXCDs) * per_xcd + q / bpu;
+  if (unit >= units || q / bpu >= per_xcd) return;
+  const int first = load_uniform(a.unit_info + 2 * unit);
+  const int S = load_uniform(a.unit_info + 2 * unit + 1);
   const int rl = (q % bpu) * RPB + threadIdx.x / C4;
   const int d4 = threadIdx.x % C4;
   const int qgroup = unit % a.qgroups;
@@ -1247,38 +1126,45 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW
   const int kvh = pair % a.Hkv;
   const int b = pair / a.Hkv;
   const int row = qgroup * RW + rl;
-  if (row >= a.M) return;
+  const bool has_row = row < a.M;
+  float ls[8];
+  f32x4 os[8];
+  auto load_batch = [&](int fst, int cnt, int s0) {
+    const size_t base = (size_t)fst * RW + rl;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool in = s0 + k < cnt;
+      const size_t r = base + (size_t)(in ? s0 + k : 0) * RW;  // in range either way
+      ls[k] = in ? a.part_lse[r] : -INFINITY;
+      os[k] = in ? *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  const int fp = a.full_pieces;
+  const bool guess = fp > 1 && (long long)(unit + 1) * fp <= a.slots;
+  if (guess && has_row) load_batch(unit * fp, fp, 0);
+  if (S <= 1 || !has_row) return;  // a single piece wrote the output itself
+  if (!guess || first != unit * fp || S != fp) load_batch(first, S, 0);
+  const int Lb = a.kv_len[b];
+  const bool bad = Lb < 0 || Lb > a.Lmax - a.N;
   const int i = row / a.G;
   const int h = kvh * a.G + (row - i * a.G);
-  const int S = a.splits;
-  const size_t base = (size_t)unit * S * RW + rl;
-  const int L = a.kv_len[b];
-  const bool bad = L < 0 || L > a.Lmax - a.N;
   float mt = -INFINITY, lt = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {
-    float ls[8];
-    f32x4 os[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool in = s0 + q < S;
-      const size_t r = base + (size_t)(in ? s0 + q : 0) * RW;  // in range either way
-      ls[q] = in ? a.part_lse[r] : -INFINITY;
-      os[q] = in ? *reinterpret_cast<const f32x4*>(a.part_o + r * D + 4 * d4)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    if (s0 > 0) load_batch(first, S, s0);
     float mb = mt;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) mb = fmaxf(mb, ls[q]);
+    for (int k = 0; k < 8; ++k) mb = fmaxf(mb, ls[k]);
     if (mb == -INFINITY) continue;
     const float f = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt - mb);
     lt *= f;
     o *= f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float w = ls[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[q] - mb);
+    for (int k = 0; k < 8; ++k) {
+      const float w = ls[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[k] - mb);
       lt += w;
-      o += os[q] * w;
+      o += os[k] * w;
     }
     mt = mb;
   }
@@ -1288,50 +1174,24 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW
       u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
 }
 
-// ---- variants ----------------------------------------------------------------
-// 0: ring, 1 query block      1: ring, 2 query blocks
-// 2: tile, 4 blocks (2x2)     3: tile, 8 blocks (4 query waves)   4: tile, 16 blocks
-// 5: ring, 2 query blocks per query group, default cache policy (grouped queries)
-// 6: group kernel, 256 rows per workgroup sharing a ring of 64-key tiles
-struct VariantInfo {
-  int rw;
-  int keys_per_piece;  // split granularity in keys
+// ---- host plan -------------------------------------------------------------------
+namespace {
+constexpr int kMaxPiecesPerUnit = 1024;
+
+// Test-only override of the planner's choices (eagle_testing_attn_plan).
+struct PlanOverride {
+  int kernel;  // 0: planner's choice, 1: ring, 2: group
+  int pieces;  // 0: planner's choice, else pieces per unit at full length
 };
+PlanOverride g_plan_override{0, 0};
 
-static VariantInfo variant_info(int variant) {
-  switch (variant) {
-    case 0: return {16, 32};
-    case 1: return {32, 32};
-    case 2: return {64, 64};
-    case 3: return {128, 64};
-    case 5: return {32, 32};
-    case 6: return {256, 64};
-    default: return {256, 64};
-  }
-}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int round8(long long x) { return (int)((x + kNumXCDs - 1) / kNumXCDs * kNumXCDs); }
+}  // namespace
 
-template <int D>
-static void* variant_kernel(int variant) {
-  static_assert(RingShape<D, 1>::THREADS == kRingThreads && RingShape<D, 2>::THREADS == kRingThreads &&
-                    RingShape<D, 2, 0>::THREADS == kRingThreads,
-                "ring launch size");
-  switch (variant) {
-    case 0: return (void*)tree_attn_ring_kernel<RingShape<D, 1>>;
-    case 1: return (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
-    case 2: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 2, 1>>;
-    case 3: return (void*)tree_attn_tile_kernel<TileShape<D, 2, 4, 2>>;
-    case 5: return (void*)tree_attn_ring_kernel<RingShape<D, 2, 0>>;
-    case 6: return (void*)tree_attn_group_kernel<GroupShape<D>>;
-    default: return (void*)tree_attn_tile_kernel<TileShape<D, 4, 4, 2>>;
-  }
-}
-
-static bool is_ring(int variant) { return variant <= 1 || variant == 5; }
-
-static int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
+void set_attn_plan_override(int kernel, int pieces) {
+  g_plan_override.kernel = kernel;
+  g_plan_override.pieces = pieces;
 }
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
@@ -1339,71 +1199,72 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   p.d = d;
   p.G = Hq / Hkv;
   p.M = p.G * N;
-  const int nqb = (p.M + 15) / 16;
-  const int pairs = B * Hkv;
-  int variant = nqb <= 1 ? 0 : nqb <= 2 ? 1 : nqb <= 4 ? 2 : nqb <= 8 ? 3 : 4;
-  // Grouped queries: the group kernel, whose 256 rows per workgroup share a
-  // ring of K/V tiles (measured on MI355X: llama2-70b shape 67 us against 79
-  // for ring query groups and 85 for the shared-tile kernel; mixtral shape
-  // 206 us against 266 and 249).
-  if (variant >= 2) variant = 6;
-  variant = env_int("EAGLE_ATTN_VARIANT", variant);
-  if (variant < 0 || variant > 6) variant = 4;
-  const VariantInfo vi = variant_info(variant);
-  p.variant = variant;
-  p.rows_per_wg = vi.rw;
-  p.kt = vi.keys_per_piece;
-  p.qgroups = (p.M + vi.rw - 1) / vi.rw;
-  // ring variants: the query groups of a (b, kv head) pair are consecutive
-  // units of the pair's XCD (pair mod 8), so the pairs are padded to a
-  // multiple of 8 and the padding units exit at once
-  p.units = is_ring(variant) ? ((pairs + kNumXCDs - 1) / kNumXCDs) * kNumXCDs * p.qgroups
-                             : pairs * p.qgroups;
-  const int pieces = (Lmax + vi.keys_per_piece - 1) / vi.keys_per_piece;
-  const int padded_units = ((p.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
-  // Aim for one workgroup per CU: a ring workgroup keeps up to eight 32-key
-  // chunks in flight and fills its CU's LDS; more splits only lengthen the
-  // merge, whose cost grows with splits x query rows.
-  const int target = kNumCUs;
-  int splits = (target + padded_units - 1) / padded_units;
-  if (is_ring(variant) && p.qgroups == 1) {
+  int kernel = p.M <= 32 ? 1 : 2;
+  if (g_plan_override.kernel == 1 || g_plan_override.kernel == 2) kernel = g_plan_override.kernel;
+  if (kernel == 1 && p.M > 32) {
+    p.kernel = -1;  // the ring kernel holds at most 32 query rows per KV head
+    return p;
+  }
+  p.kernel = kernel;
+  if (kernel == 1) {
+    p.rows_per_wg = p.M <= 16 ? 16 : 32;
+    p.kg = 32;
+    p.qgroups = 1;
+  } else {
+    p.rows_per_wg = 256;
+    p.kg = 64;
+    p.qgroups = (p.M + 255) / 256;
+  }
+  p.units = B * Hkv * p.qgroups;
+  p.max_pieces = kMaxPiecesPerUnit;
+  // Pieces per unit at full length (the cache capacity); the device shares
+  // the resulting slots out by the actual committed lengths.
+  const int cap_chunks = std::max(1, (Lmax - N + p.kg - 1) / p.kg);
+  int pieces;
+  if (kernel == 1) {
     // One ring workgroup per CU (its LDS): workgroups beyond kNumCUs run in
     // another round, so a half-empty last round costs as much as a full one.
-    // Pick the split count s minimising rounds(s) * chunks per split plus a
-    // merge cost of 1.75 chunk-times per split (fitted on MI355X: llama2-7b
-    // 6 splits, 14.9 us against 16.0 us at 8; llama2-13b 3 splits, 64 us
-    // against 85 us at 2).
-    const int n_chunks = (Lmax - N + 31) / 32;
+    // Pick the piece count s minimising rounds(s) * chunks per piece plus a
+    // combine cost of 1.75 chunk-times per piece (fitted on MI355X).
+    pieces = 1;
     float best = 0.f;
-    for (int sc = 1; sc <= 16 && sc <= n_chunks; ++sc) {
-      const int rounds = (padded_units * sc + kNumCUs - 1) / kNumCUs;
-      const float cost = (float)(rounds * ((n_chunks + sc - 1) / sc)) + 1.75f * sc;
+    for (int sc = 1; sc <= 16 && sc <= cap_chunks; ++sc) {
+      const long long slots = round8((long long)p.units * sc);
+      const int rounds = (int)((slots + kNumCUs - 1) / kNumCUs);
+      const float cost = (float)(rounds * ((cap_chunks + sc - 1) / sc)) + 1.75f * sc;
       if (sc == 1 || cost < best) {
         best = cost;
-        splits = sc;
+        pieces = sc;
       }
     }
+  } else {
+    // grouped queries: about one workgroup per CU (measured on MI355X:
+    // llama2-70b 4 pieces, 59.3 us against 68.2 at 3 and 74.9 at 8;
+    // mixtral shape 2 pieces, 186.8 us against 220.7 at 3)
+    pieces = (kNumCUs + round8(p.units) - 1) / round8(p.units);
   }
-  splits = env_int("EAGLE_ATTN_SPLITS", splits);
-  if (splits > pieces) splits = pieces;
-  if (splits > 64) splits = 64;  // the merge keeps one split weight per lane
-  if (splits < 1) splits = 1;
-  p.splits = splits;
+  if (g_plan_override.pieces > 0) pieces = g_plan_override.pieces;
+  pieces = std::max(1, std::min(pieces, std::min(cap_chunks, kMaxPiecesPerUnit)));
+  p.slots = round8((long long)p.units * pieces);
+  // what the device planner gives every unit when all sequences fill the
+  // cache: the smallest piece T (in chunks) with units * ceil(C / T) <= slots
+  const int per_unit = p.slots / p.units;
+  const int T = per_unit >= kMaxPiecesPerUnit ? 1 : std::max(1, (cap_chunks + per_unit - 1) / per_unit);
+  p.full_pieces = std::max(1, std::min(kMaxPiecesPerUnit, (cap_chunks + T - 1) / T));
   return p;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Workspace: [unit tickets (ring variants) | split log2-sum-exp | split O].
-static size_t ticket_bytes(const AttnPlan& p) {
-  return is_ring(p.variant) && p.splits > 1 ? align256((size_t)p.units * 4) : 0;
+size_t tree_attn_workspace_bytes(const AttnPlan& p) {
+  if (p.kernel < 0 || p.slots <= p.units) return 0;
+  return align256((size_t)p.units * 8) + align256((size_t)p.slots * p.rows_per_wg * 4) +
+         (size_t)p.slots * p.rows_per_wg * p.d * 4;
 }
 
-size_t tree_attn_workspace_bytes(const AttnPlan& p) {
-  if (p.splits <= 1) return 0;
-  const size_t lse = align256((size_t)p.units * p.splits * p.rows_per_wg * 4);
-  const size_t o = (size_t)p.units * p.splits * p.rows_per_wg * p.d * 4;
-  return ticket_bytes(p) + lse + o;
+template <int D>
+static void* attn_kernel(int kernel, int rows_per_wg) {
+  if (kernel == 2) return (void*)tree_attn_group_kernel<GroupShape<D>>;
+  return rows_per_wg == 16 ? (void*)tree_attn_ring_kernel<RingShape<D, 1>>
+                           : (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
@@ -1412,6 +1273,10 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
                             int32_t* pos_out,
                             int B, int N, int Hq, int Hkv, int Lmax, float scale_log2,
                             uint16_t* out, void* ws, int32_t* flags, hipStream_t s) {
+  static_assert(RingShape<64, 1>::THREADS == kRingThreads && RingShape<128, 2>::THREADS == kRingThreads &&
+                    GroupShape<128>::THREADS == kRingThreads && GroupShape<64>::THREADS == kRingThreads,
+                "launch size");
+  if (plan.kernel < 0) return hipErrorInvalidValue;
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -1423,13 +1288,16 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.depth_out = depth_out;
   a.pos_out = pos_out;
   a.out = out;
-  const bool ring = is_ring(plan.variant);
+  const bool pieces = plan.slots > plan.units;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const size_t tk = ticket_bytes(plan);
-  const size_t lse = align256((size_t)plan.units * plan.splits * plan.rows_per_wg * 4);
-  a.tickets = reinterpret_cast<int32_t*>(w);
-  a.part_lse = reinterpret_cast<float*>(w + tk);
-  a.part_o = reinterpret_cast<float*>(w + tk + lse);
+  if (pieces) {
+    const size_t head = align256((size_t)plan.units * 8);
+    const size_t lse = align256((size_t)plan.slots * plan.rows_per_wg * 4);
+    a.tickets = plan.kernel == 1 ? reinterpret_cast<int32_t*>(w) : nullptr;
+    a.unit_info = plan.kernel == 2 ? reinterpret_cast<int32_t*>(w) : nullptr;
+    a.part_lse = reinterpret_cast<float*>(w + head);
+    a.part_o = reinterpret_cast<float*>(w + head + lse);
+  }
   a.flags = flags;
   a.B = B;
   a.N = N;
@@ -1439,25 +1307,25 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.G = plan.G;
   a.M = plan.M;
   a.qgroups = plan.qgroups;
-  a.units = plan.units;
-  a.splits = plan.splits;
+  a.slots = plan.slots;
+  a.kg = plan.kg;
+  a.max_pieces = plan.max_pieces;
+  a.full_pieces = Lmax > N ? plan.full_pieces : 0;
   a.scale_log2 = scale_log2;
-  const int padded_units = ((plan.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs;
-  const dim3 grid((unsigned)(padded_units * plan.splits));
-  void* fn = plan.d == 64 ? variant_kernel<64>(plan.variant) : variant_kernel<128>(plan.variant);
+  void* fn = plan.d == 64 ? attn_kernel<64>(plan.kernel, plan.rows_per_wg)
+                          : attn_kernel<128>(plan.kernel, plan.rows_per_wg);
   void* args[] = {&a};
-  const int threads = ring ? kRingThreads : plan.variant == 6 ? GroupShape<128>::THREADS : 256;
-  hipError_t err = hipLaunchKernel(fn, grid, dim3(threads), args, 0, s);
-  // ring variants combine their splits in the kernel
-  if (err != hipSuccess || plan.splits == 1 || ring) return err;
+  hipError_t err = hipLaunchKernel(fn, dim3((unsigned)plan.slots), dim3(kRingThreads), args, 0, s);
+  // the ring kernel combines its pieces itself
+  if (err != hipSuccess || !pieces || plan.kernel == 1) return err;
   const int rw = plan.rows_per_wg;
   const int rows_per_block = 256 / (plan.d / 4);
-  const dim3 mgrid((unsigned)(((plan.units + kNumXCDs - 1) / kNumXCDs) * kNumXCDs *
-                               (rw / rows_per_block)));
+  const int per_xcd = (plan.units + kNumXCDs - 1) / kNumXCDs;
+  const dim3 mgrid((unsigned)(kNumXCDs * per_xcd * (rw / rows_per_block)));
   if (plan.d == 64)
-    tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a, rw);
+    tree_attn_merge_kernel<64><<<mgrid, 256, 0, s>>>(a, rw, plan.units);
   else
-    tree_attn_merge_kernel<128><<<mgrid, 256, 0, s>>>(a, rw);
+    tree_attn_merge_kernel<128><<<mgrid, 256, 0, s>>>(a, rw, plan.units);
   return hipGetLastError();
 }
 
