@@ -171,6 +171,28 @@ EAGLE_API eagle_status_t eagle_tree_attn_parents(const uint16_t* q, const uint16
                                int32_t* depth, int32_t* pos, void* workspace,
                                size_t workspace_bytes, int32_t* seq_flags, void* stream);
 
+/*
+ * eagle_tree_attn_parents without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus workspace),
+ * same kernels and bit-identical results.  The scratch the kernels need
+ * (piece tickets or piece table, split partials) lives in a static device
+ * array of the library, 64 MiB per GPU, held by each GPU the library runs on
+ * until the process ends; no hipMalloc, hipFree or other allocation happens
+ * on any call.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); each call that needs the tickets clears them with a
+ * small fill kernel on `stream` (no memset node).  A shape whose scratch
+ * would exceed 64 MiB (eagle_tree_attn_workspace above 67108864) returns
+ * EAGLE_ERR_UNSUPPORTED before anything is enqueued.  All calls on one GPU
+ * share the array: calls that overlap on that GPU (other streams or threads)
+ * race and must be serialised by the caller.
+ */
+EAGLE_API eagle_status_t eagle_tree_attn_parents_noalloc(const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* kv_len,
+                               const int32_t* parents, int B, int N, int Hq, int Hkv, int d,
+                               int Lmax, float sm_scale, uint16_t* out, uint64_t* anc,
+                               int32_t* depth, int32_t* pos, int32_t* seq_flags, void* stream);
+
 /* Workspace bytes eagle_verify_accept needs for this shape. */
 EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
 

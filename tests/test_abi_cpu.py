@@ -266,3 +266,29 @@ def test_binding_rejects_mis_sized_tensors_on_the_host():
         ev.dtree_expand(torch.zeros((1, 2, 10)), torch.zeros((1, 3), dtype=torch.int32),
                         torch.zeros((1, 2)), 2, torch.zeros((1, 8), dtype=torch.int32),
                         torch.zeros((1, 8), dtype=torch.int32), torch.zeros((1, 8)), 1)
+
+
+def test_attention_plan_hook_and_noalloc_limits():
+    """The testing hook checks its arguments; the attention entry point that
+    allocates nothing refuses, before touching a device, a shape whose scratch
+    exceeds its 64 MiB static array, and the forced ring kernel refuses more
+    than 32 query rows per KV head."""
+    assert _status("eagle_testing_attn_plan", 3, 0) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert _status("eagle_testing_attn_plan", 0, -1) == binding.EAGLE_ERR_INVALID_ARGUMENT
+    B, N, Hq, Hkv, d, Lmax = 32, 26, 64, 8, 128, 4096 + 26
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, B, N, Hq, Hkv, d, Lmax, ctypes.c_float(0.0), FAKE,
+            None, None, None, None, None)
+    try:
+        ev.testing_attn_plan("group", 8)
+        assert ev.tree_attn_workspace_bytes(B, N, Hq, Hkv, d, Lmax) > 64 << 20
+        assert _status("eagle_tree_attn_parents_noalloc", *args) == binding.EAGLE_ERR_UNSUPPORTED
+        assert b"67108864" in ev.lib().eagle_last_error()
+        ev.testing_attn_plan("ring", 0)
+        assert _status("eagle_tree_attn_parents_noalloc", *args) == binding.EAGLE_ERR_UNSUPPORTED
+        assert _status("eagle_tree_attn_parents", FAKE, FAKE, FAKE, FAKE, FAKE, B, N, Hq, Hkv, d,
+                       Lmax, ctypes.c_float(0.0), FAKE, None, None, None, FAKE, 1 << 40, None,
+                       None) == binding.EAGLE_ERR_UNSUPPORTED
+    finally:
+        ev.testing_attn_plan("auto", 0)
+    # the planner's own choice at this shape fits the static scratch
+    assert ev.tree_attn_workspace_bytes(B, N, Hq, Hkv, d, Lmax) <= 64 << 20

@@ -54,6 +54,8 @@ _SIGNATURES = {
     "eagle_tree_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P]),
     "eagle_tree_attn_parents": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                      _P, _P, _SZ, _P, _P]),
+    "eagle_tree_attn_parents_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P,
+                                             _P, _P, _P, _P, _P]),
     "eagle_verify_accept_workspace": (_SZ, [_I, _I, _I]),
     "eagle_verify_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _SZ, _P, _P]),
@@ -245,6 +247,29 @@ def tree_attn_parents(q, k_cache, v_cache, kv_len, parents, *, sm_scale: float =
         _ptr(out, torch.bfloat16, "out"), _ptr(anc, torch.int64, "anc"),
         _ptr(depth, torch.int32, "depth"), _ptr(pos, torch.int32, "pos"),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
+    return out
+
+
+def tree_attn_parents_noalloc(q, k_cache, v_cache, kv_len, parents, *, sm_scale: float = 0.0,
+                              out=None, anc=None, depth=None, pos=None, seq_flags=None,
+                              stream=None):
+    """tree_attn_parents with the library's static scratch instead of a
+    workspace (eagle_tree_attn_parents_noalloc).  Returns out."""
+    B, N, Hq, d = q.shape
+    _check_cache(q, k_cache, v_cache, kv_len, seq_flags)
+    for t, name in ((parents, "parents"), (anc, "anc"), (depth, "depth"), (pos, "pos")):
+        _expect(t, (B, N), name)
+    _expect(out, q.shape, "out")
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().eagle_tree_attn_parents_noalloc(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(kv_len, torch.int32, "kv_len"),
+        _ptr(parents, torch.int32, "parents"), B, N, Hq, Hkv, d, Lmax, float(sm_scale),
+        _ptr(out, torch.bfloat16, "out"), _ptr(anc, torch.int64, "anc"),
+        _ptr(depth, torch.int32, "depth"), _ptr(pos, torch.int32, "pos"),
         _ptr(seq_flags, torch.int32, "seq_flags"), _stream(stream)))
     return out
 

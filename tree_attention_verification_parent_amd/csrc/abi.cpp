@@ -166,6 +166,48 @@ eagle_status_t eagle_tree_attn_parents(const uint16_t* q, const uint16_t* k_cach
                         stream);
 }
 
+eagle_status_t eagle_tree_attn_parents_noalloc(const uint16_t* q, const uint16_t* k_cache,
+                                               const uint16_t* v_cache, const int32_t* kv_len,
+                                               const int32_t* parents, int B, int N, int Hq,
+                                               int Hkv, int d, int Lmax, float sm_scale,
+                                               uint16_t* out, uint64_t* anc, int32_t* depth,
+                                               int32_t* pos, int32_t* seq_flags, void* stream) {
+  eagle_status_t st = check_attn_shape(B, N, Hq, Hkv, d, Lmax);
+  if (st != EAGLE_OK) return st;
+  if (B == 0) return EAGLE_OK;
+  if (!q || !k_cache || !v_cache || !kv_len || !parents || !out)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT,
+                "q, k_cache, v_cache, kv_len, parents and out must be non-NULL");
+  if (!isfinite(sm_scale)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  const eagle::AttnPlan plan = eagle::plan_tree_attn(B, N, Hq, Hkv, d, Lmax);
+  if (plan.kernel < 0)
+    return fail(EAGLE_ERR_UNSUPPORTED, "the forced ring kernel holds at most 32 query rows per KV head (G * N = %d)",
+                plan.M);
+  const size_t need = eagle::tree_attn_workspace_bytes(plan);
+  if (need > eagle::kStaticScratchBytes)
+    return fail(EAGLE_ERR_UNSUPPORTED,
+                "this shape needs %zu scratch bytes; eagle_tree_attn_parents_noalloc holds at most "
+                "%zu (use eagle_tree_attn_parents with a workspace)",
+                need, eagle::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = hip_status(eagle::static_scratch(&ws), "static scratch lookup");
+    if (st != EAGLE_OK) return st;
+    // the tickets must start at zero: a fill kernel (no memset node)
+    const size_t zeroed = eagle::tree_attn_zeroed_bytes(plan);
+    if (zeroed > 0) {
+      st = hip_status(eagle::launch_fill_zero(ws, zeroed, as_stream(stream)), "scratch clear");
+      if (st != EAGLE_OK) return st;
+    }
+  }
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
+  return hip_status(eagle::launch_tree_attn(plan, q, k_cache, v_cache, kv_len, nullptr, parents,
+                                            anc, depth, pos, B, N, Hq, Hkv, Lmax,
+                                            scale * 1.4426950408889634f, out, ws, seq_flags,
+                                            as_stream(stream)),
+                    "tree attention launch");
+}
+
 static eagle_status_t check_verify_shape(int B, int N, int V) {
   if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
   if (!tree_size_ok(N)) return fail(EAGLE_ERR_INVALID_ARGUMENT, "N must be in [1, 64] (got %d)", N);

@@ -35,6 +35,15 @@ struct AttnPlan {
 void set_attn_plan_override(int kernel, int pieces);
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax);
 size_t tree_attn_workspace_bytes(const AttnPlan& p);
+// Leading workspace bytes that must be zero when a call starts (the ring
+// kernel's piece tickets, which every call leaves zero again).
+size_t tree_attn_zeroed_bytes(const AttnPlan& p);
+
+// Static scratch of eagle_tree_attn_parents_noalloc: its device address on
+// the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch(void** ptr);
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_len, const uint64_t* anc,

@@ -43,6 +43,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -1265,6 +1266,39 @@ static void* attn_kernel(int kernel, int rows_per_wg) {
   if (kernel == 2) return (void*)tree_attn_group_kernel<GroupShape<D>>;
   return rows_per_wg == 16 ? (void*)tree_attn_ring_kernel<RingShape<D, 1>>
                            : (void*)tree_attn_ring_kernel<RingShape<D, 2>>;
+}
+
+// ---- scratch of the entry point that allocates nothing ------------------------------
+// eagle_tree_attn_parents_noalloc keeps its workspace (piece tickets or table,
+// partials) here instead of in a caller's buffer.  Each device holds its own
+// copy for the life of the process; host code reaches it only through the
+// address hipGetSymbolAddress returns with that device current, recorded
+// once per device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t tree_attn_zeroed_bytes(const AttnPlan& p) {
+  return p.kernel == 1 && p.slots > p.units ? align256((size_t)p.units * 8) : 0;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint16_t* k,
