@@ -70,7 +70,10 @@ class Step:
         self.uniforms = t(s.uniforms)
         q0, k0, v0 = bf(s.q), bf(s.k_cache), bf(s.v_cache)
         lg0 = t(s.target_logits)
-        dp0 = t(s.draft_probs) if s.draft_probs is not None else None
+        # the drafter's layout: one draft row per drafting node, each node
+        # naming its parent's row (siblings drawn i.i.d. share it)
+        dp0 = t(s.draft_rows) if s.draft_rows is not None else None
+        self.draft_row = t(s.draft_row) if s.draft_rows is not None else None
         self.slots = []
         for i in range(copies):
             self.slots.append(dict(
@@ -102,8 +105,8 @@ class Step:
         sl = self.slots[i % len(self.slots)]
         self.ev.verify_accept_compact(self.tokens, sl["draft"], sl["logits"], self.parents,
                                       self.kv_len, self.T, self.uniforms, sl["k"], sl["v"],
-                                      outputs=self.res, new_kv_len=self.new_len,
-                                      workspace=self.ver_ws)
+                                      draft_row=self.draft_row, outputs=self.res,
+                                      new_kv_len=self.new_len, workspace=self.ver_ws)
 
     def run(self, i):
         ev = self.ev
@@ -113,8 +116,8 @@ class Step:
                              workspace=self.attn_ws)
         ev.verify_accept_compact(self.tokens, sl["draft"], sl["logits"], self.parents,
                                  self.kv_len, self.T, self.uniforms, sl["k"], sl["v"],
-                                 outputs=self.res, new_kv_len=self.new_len,
-                                 workspace=self.ver_ws)
+                                 draft_row=self.draft_row, outputs=self.res,
+                                 new_kv_len=self.new_len, workspace=self.ver_ws)
 
 
 def graph_of(torch, fn, count):
@@ -169,9 +172,15 @@ def measure(torch, ev, W, T, steps, warmup):
     # rejected one costs its draft row on top of the target rows
     sl = st.slots[0]
     o = ev.verify_accept(st.tokens, sl["draft"], sl["logits"], st.parents, st.kv_len, st.T,
-                         st.uniforms, want_ratio=True)
-    tested = int((~torch.isnan(o["ratio"])).sum().item())
+                         st.uniforms, draft_row=st.draft_row, want_ratio=True)
+    tested_mask = ~torch.isnan(o["ratio"])
+    tested = int(tested_mask.sum().item())
     rejected = tested - int(o["accept_len"].sum().item())
+    # the draft rows the tested candidates were drawn from (each read once)
+    rows_read = 0
+    if T > 0:
+        tm, dr = tested_mask.cpu().numpy(), s.draft_row
+        rows_read = sum(len(set(dr[b][tm[b]].tolist())) for b in range(cfg.B))
     # acceptance rate per depth: candidates tested at depth d (T > 0: their
     # ratio is set; T = 0: the same candidates, taken from the walk's path)
     depth = np.zeros(cfg.N, dtype=np.int64)
@@ -196,10 +205,10 @@ def measure(torch, ev, W, T, steps, warmup):
     g_ver = graph_of(torch, st.verify, steps)
     time_graph(torch, g_ver)
     t_ver = time_graph(torch, g_ver) / steps
-    walk_bytes = cfg.vocab_bytes() + (4 * cfg.V * rejected if T > 0 else 0)
+    walk_bytes = cfg.vocab_bytes() + 4 * cfg.V * rows_read
     return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, t_verify=t_ver, accept_len=int(acc[0]),
                 replays=replays, spread=spread, alpha={d: {"tested": t, "accepted": a_} for d, (t, a_) in sorted(alpha.items())},
-                copies=copies, walk_bytes=walk_bytes, rejected=rejected)
+                copies=copies, walk_bytes=walk_bytes, rejected=rejected, rows_read=rows_read)
 
 
 def measure_feature_gather(torch, ev, W, steps):
@@ -500,7 +509,7 @@ def main():
     tokens = cfg.B * cfg.N
     attn_bytes = cfg.attn_bytes()
     achieved = attn_bytes / r1["t_attn"] / 1e9
-    vocab_bytes = r1["walk_bytes"]  # target rows + the draft row of every rejected candidate
+    vocab_bytes = r1["walk_bytes"]  # target rows + the draft rows the tested candidates came from
     fg = measure_feature_gather(torch, ev, W, args.steps)
     dtree = measure_dynamic_tree(torch, ev, W, args.steps)
     stream = measure_stream_context(torch)
@@ -534,6 +543,7 @@ def main():
         "kernels_us": {"tree_attn": r1["t_attn"] * 1e6, "verify_accept_compact": r1["t_verify"] * 1e6},
         "verify_roofline": {"bound": "hbm", "bytes_per_launch": vocab_bytes,
                             "rejected_candidates": r1["rejected"],
+                            "draft_rows_read": r1["rows_read"],
                             "achieved": vocab_bytes / r1["t_verify"] / 1e9,
                             "frac": vocab_bytes / r1["t_verify"] / 1e9 / HBM_PEAK_GBS},
         "step_hbm_frac": (attn_bytes + vocab_bytes) / r1["t_step"] / 1e9 / HBM_PEAK_GBS,

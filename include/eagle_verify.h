@@ -63,16 +63,16 @@ typedef int eagle_status_t;
 #define EAGLE_FLAG_BAD_KV_LEN   2  /* kv_len[b] < 0 or kv_len[b] + N > Lmax */
 #define EAGLE_FLAG_BAD_TOKEN    4  /* a drafted token outside [0, V)        */
 #define EAGLE_FLAG_NONFINITE    8  /* NaN or Inf in a target logit row      */
-#define EAGLE_FLAG_TIMEOUT     16  /* a cross-workgroup wait gave up; the  */
-                                   /* sequence's walk outputs are in range */
-                                   /* but not meaningful                   */
+/* 16 is unused (no kernel waits for another workgroup) */
 #define EAGLE_FLAG_BAD_PATH    32  /* accepted path not as the walk emits  */
                                    /* it (eagle_feature_gather)            */
+#define EAGLE_FLAG_BAD_ROW     64  /* draft_row outside [0, N) on a tested */
+                                   /* node (eagle_verify_accept*)          */
 
 /* Message for the last non-zero status returned on this thread. */
 EAGLE_API const char* eagle_last_error(void);
 
-/* Version of this ABI (incremented on any signature change). */
+/* Version of this ABI (incremented on any signature change; 2: draft_row). */
 EAGLE_API int eagle_abi_version(void);
 
 /*
@@ -85,9 +85,8 @@ EAGLE_API eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B,
 /*
  * Zero-fill `bytes` of device memory at `ptr` with a kernel (no memset node,
  * so it may be captured in a HIP graph).  eagle_verify_accept's workspace
- * must be zero before its first use; each call leaves its counters and
- * exchange words zero again (the rest holds per-call scratch), so it is
- * cleared once.
+ * must be zero before its first use; each call leaves its tickets and argmax
+ * words zero again (the rest holds per-call scratch), so it is cleared once.
  */
 EAGLE_API eagle_status_t eagle_workspace_clear(void* ptr, size_t bytes, void* stream);
 
@@ -215,8 +214,18 @@ EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
  * (T = 0: the argmax).
  *
  *   draft_tokens  device [B, N] int32; [b, 0] is the root token (not tested)
- *   draft_probs   device [B, N, V] fp32; row i = distribution token i was drawn
- *                 from (row 0 unused); may be NULL when T == 0
+ *   draft_probs   device [B, N, V] fp32 draft distributions; may be NULL when
+ *                 T == 0
+ *   draft_row     device [B, N] int32 or NULL: node i's token was drawn from
+ *                 row draft_row[b, i] of draft_probs[b] (0 <= row < N).  NULL
+ *                 means row i (each node its own row; row 0 unused).  Siblings
+ *                 drawn i.i.d. from their parent's draft distribution name the
+ *                 same row (e.g. draft_row = parents, with row j holding the
+ *                 draft distribution after node j), and a node whose
+ *                 candidates all name one row is evaluated in closed form: each
+ *                 rejection costs one pass over the two rows in registers and
+ *                 no row is re-read.  A row outside [0, N) on a tested node sets
+ *                 EAGLE_FLAG_BAD_ROW and that node's own row is used instead.
  *   target_logits device [B, N, V] fp32; row i = target logits after node i
  *   parents       device [B, N] int32
  *   kv_len        device [B] int32 (for kv_src_slots)
@@ -232,17 +241,20 @@ EAGLE_API size_t eagle_verify_accept_workspace(int B, int N, int V);
  *   out_final_dist  [B, V] or NULL: the distribution the final token came from
  *   out_ratio       [B, N] or NULL: ratio used for each tested node, NaN for
  *                   untested ones (T = 0: 1 for a match, 0 otherwise)
- *   seq_flags       [B] int32 or NULL (BAD_TOKEN, NONFINITE, BAD_PARENT,
- *                   TIMEOUT)
+ *   seq_flags       [B] int32 or NULL (BAD_TOKEN, BAD_ROW, NONFINITE)
+ *   workspace       device, eagle_verify_accept_workspace() bytes: per-sequence
+ *                   and per-node tickets and maxima, which must be zero before
+ *                   the first call (eagle_workspace_clear) and are left zero by
+ *                   every call, and per-node scratch; calls that overlap must
+ *                   not share it
  * Supported: 1 <= V <= 32768; 1 <= N <= 64.
- * With T > 0, no out_* buffer, V % 4 == 0, 28672 < V <= 32768 and B * N <= 32
- * each node's row is split over 8 workgroups that exchange partial sums through
- * the workspace and wait for one another; they all fit the GPU at once, so the
- * waits end unless other work holds the compute units for a long time, in
- * which case a bounded wait gives up and sets EAGLE_FLAG_TIMEOUT.  Results of
- * the split path equal the unsplit one's up to the rounding of the masses.
+ * No workgroup waits for another (the nodes of a sequence meet only at an
+ * atomic ticket), so the results never depend on how many run at once.  At
+ * T = 0 without out_* buffers and V > 4096 each row's argmax is split over
+ * several workgroups; results are identical to the unsplit argmax.
  */
 EAGLE_API eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* draft_probs,
+                                   const int32_t* draft_row,
                                    const float* target_logits, const int32_t* parents,
                                    const int32_t* kv_len, int B, int N, int V, float temperature,
                                    const float* uniforms,
@@ -265,7 +277,8 @@ EAGLE_API eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const 
  * sequence's cache unchanged (new_kv_len = kv_len).
  */
 EAGLE_API eagle_status_t eagle_verify_accept_compact(
-    const int32_t* draft_tokens, const float* draft_probs, const float* target_logits,
+    const int32_t* draft_tokens, const float* draft_probs, const int32_t* draft_row,
+    const float* target_logits,
     const int32_t* parents, const int32_t* kv_len, int B, int N, int V, float temperature,
     const float* uniforms, int32_t* accept_len, int32_t* path, int32_t* accepted_tokens,
     int32_t* bonus_token, int32_t* kv_src_slots, uint16_t* k_cache, uint16_t* v_cache, int Hkv,

@@ -36,12 +36,25 @@ def run_attention(step, sm_scale=0.0):
     return out.float().cpu().numpy(), anc, depth, pos
 
 
-def run_verify(step, want_probs=False, want_final_dist=True, want_ratio=True, flags=None):
+def draft_args(step, rows="shared"):
+    """(draft_probs, draft_row) device tensors for the library: "shared" passes
+    one row per drafting node and each node's row index (its parent), so
+    siblings share a row (the closed-form chain); "node" passes one row per
+    node with no index (the step-by-step chain)."""
+    if step.draft_probs is None:
+        return None, None
+    if rows == "shared" and step.draft_rows is not None:
+        return dev(step.draft_rows), dev(step.draft_row)
+    return dev(step.draft_probs), None
+
+
+def run_verify(step, want_probs=False, want_final_dist=True, want_ratio=True, flags=None,
+               rows="shared"):
+    dp, dr = draft_args(step, rows)
     res = ev.verify_accept(
-        dev(step.tokens), None if step.draft_probs is None else dev(step.draft_probs),
-        dev(step.target_logits), dev(step.parents), dev(step.kv_len), step.T, dev(step.uniforms),
-        want_probs=want_probs, want_final_dist=want_final_dist, want_ratio=want_ratio,
-        seq_flags=flags)
+        dev(step.tokens), dp, dev(step.target_logits), dev(step.parents), dev(step.kv_len), step.T,
+        dev(step.uniforms), draft_row=dr, want_probs=want_probs, want_final_dist=want_final_dist,
+        want_ratio=want_ratio, seq_flags=flags)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in res.items()}
 

@@ -34,7 +34,7 @@ def test_header_symbols_are_exported():
 
 
 def test_abi_version():
-    assert ev.abi_version() == 1
+    assert ev.abi_version() == 2
 
 
 def test_validate_tree_host():
@@ -120,8 +120,9 @@ def test_verify_argument_errors():
     L = ev.lib()
 
     def call(B=1, N=8, V=1000, T=1.0, draft=FAKE, ws=FAKE, ws_bytes=1 << 30, outs=FAKE):
-        return L.eagle_verify_accept(FAKE, draft, FAKE, FAKE, FAKE, B, N, V, T, FAKE, outs, FAKE,
-                                     FAKE, FAKE, FAKE, None, None, None, ws, ws_bytes, None, None)
+        return L.eagle_verify_accept(FAKE, draft, None, FAKE, FAKE, FAKE, B, N, V, T, FAKE, outs,
+                                     FAKE, FAKE, FAKE, FAKE, None, None, None, ws, ws_bytes, None,
+                                     None)
 
     assert call(V=40000) == binding.EAGLE_ERR_UNSUPPORTED
     assert call(V=0) == binding.EAGLE_ERR_INVALID_ARGUMENT
@@ -145,9 +146,9 @@ def test_verify_compact_argument_errors():
 
     def call(B=1, N=8, V=1000, T=1.0, draft=FAKE, kcache=FAKE, Hkv=4, d=64, Lmax=136, kvl=FAKE,
              new_len=other, ws=FAKE, ws_bytes=1 << 30):
-        return L.eagle_verify_accept_compact(FAKE, draft, FAKE, FAKE, kvl, B, N, V, T, FAKE, FAKE,
-                                             FAKE, FAKE, FAKE, FAKE, kcache, FAKE, Hkv, d, Lmax,
-                                             new_len, ws, ws_bytes, None, None)
+        return L.eagle_verify_accept_compact(FAKE, draft, None, FAKE, FAKE, kvl, B, N, V, T, FAKE,
+                                             FAKE, FAKE, FAKE, FAKE, FAKE, kcache, FAKE, Hkv, d,
+                                             Lmax, new_len, ws, ws_bytes, None, None)
 
     assert call(V=40000) == binding.EAGLE_ERR_UNSUPPORTED
     assert call(T=-1.0) == binding.EAGLE_ERR_INVALID_ARGUMENT

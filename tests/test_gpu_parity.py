@@ -19,7 +19,8 @@ import workloads as W
 from oracle.walk import as_arrays
 from workloads import trees
 
-from gpu_util import bf, bits, compare_walks, dev, oracle_walks, run_attention, run_verify, say
+from gpu_util import (bf, bits, compare_walks, dev, draft_args, oracle_walks, run_attention,
+                      run_verify, say)
 
 pytestmark = pytest.mark.gpu
 ATOL_ATTN = 2e-2
@@ -411,12 +412,13 @@ def _check_probs(gpu_probs, step):
             np.testing.assert_allclose(gpu_probs[b, i].astype(np.float64), p, rtol=1e-5, atol=1e-35)
 
 
+@pytest.mark.parametrize("rows", ["shared", "node"])
 @pytest.mark.parametrize("idx,T", [(0, 1.0), (1, 0.0), (1, 1.0), (2, 1.0), (3, 0.0), (3, 1.0), (4, 1.0)])
-def test_verify_full_configs(idx, T):
+def test_verify_full_configs(idx, T, rows):
     cfg = W.get(idx)
     s = W.make_step(cfg, T, with_attention=False)
-    say(f"verify full config {cfg.name} T={T}")
-    gpu = run_verify(s, want_probs=idx <= 2)
+    say(f"verify full config {cfg.name} T={T} rows={rows}")
+    gpu = run_verify(s, want_probs=idx <= 2, rows=rows)
     walks = oracle_walks(s)
     compared, excused = compare_walks(gpu, s, walks)
     say(f"  compared {compared} sequences, {excused} excused near ties; "
@@ -426,13 +428,14 @@ def test_verify_full_configs(idx, T):
         _check_probs(gpu["probs"], s)
 
 
+@pytest.mark.parametrize("rows", ["shared", "node"])
 @pytest.mark.parametrize("V", [1, 2, 7, 1000, 1001, 4096, 4097, 32768])
 @pytest.mark.parametrize("T", [0.0, 0.6, 1.0])
-def test_verify_vocab_sizes(V, T):
+def test_verify_vocab_sizes(V, T, rows):
     cfg = W.shrink(W.get(0), B=6, N=12, V=V)
     s = W.make_step(cfg, T, seed=V * 7 + int(T * 10), with_attention=False)
-    say(f"verify V={V} T={T}")
-    gpu = run_verify(s, want_probs=True)
+    say(f"verify V={V} T={T} rows={rows}")
+    gpu = run_verify(s, want_probs=True, rows=rows)
     compared, excused = compare_walks(gpu, s, oracle_walks(s))
     assert compared + excused == cfg.B
     _check_probs(gpu["probs"], s)
@@ -457,7 +460,7 @@ def test_verify_zero_draft_mass_and_bad_tokens():
     for b in range(cfg.B):
         s.draft_probs[b, 1, s.tokens[b, 1]] = 0.0
     say("verify zero draft mass")
-    gpu = run_verify(s)
+    gpu = run_verify(s, rows="node")
     compare_walks(gpu, s, oracle_walks(s))
     assert np.isinf(gpu["ratio"][:, 1]).all()
     # an out-of-vocabulary token is flagged and rejected, never read out of bounds
@@ -465,7 +468,7 @@ def test_verify_zero_draft_mass_and_bad_tokens():
     s.tokens[3, 5] = -4
     flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
     say("verify bad tokens")
-    gpu = run_verify(s, flags=flags)
+    gpu = run_verify(s, flags=flags, rows="node")
     f = flags.cpu().numpy()
     assert f[2] & ev.binding.FLAG_BAD_TOKEN and f[3] & ev.binding.FLAG_BAD_TOKEN
     assert f[0] == 0 and f[1] == 0
@@ -492,17 +495,20 @@ def test_verify_deterministic():
         assert np.array_equal(a[k], b[k], equal_nan=True)
 
 
-# Split rows: at large vocabularies with at most 32 nodes the sampling path
-# without parity outputs spreads each node's row over 8 workgroups that
-# exchange fixed-point partial sums; the outputs must match the oracle, repeat
-# bit for bit, raise no flag and leave the workspace zero.
-SPLIT_CASES = {
+# Large vocabularies: candidates sharing their parent's draft row run the
+# closed-form chain, candidates with rows of their own the step-by-step chain;
+# both must match the oracle, repeat bit for bit, raise no flag and leave the
+# workspace's tickets and argmax words zero.
+ROW_CASES = {
     "7b-seed0": dict(B=1, N=26, V=32000, T=1.0, seed=0),
     "7b-seed1": dict(B=1, N=26, V=32000, T=1.0, seed=1),
     "7b-T0.6": dict(B=1, N=26, V=32000, T=0.6, seed=2),
+    "7b-T0": dict(B=1, N=26, V=32000, T=0.0, seed=8),
+    "7b-descending": dict(B=2, N=26, V=32000, T=1.0, seed=9, sigma_d=0.05),
     "32-nodes": dict(B=2, N=16, V=32768, T=1.0, seed=3),
-    "min-vocab": dict(B=1, N=26, V=28676, T=1.0, seed=4),
+    "odd-vocab": dict(B=1, N=26, V=28677, T=1.0, seed=4),
     "star": dict(B=1, N=32, V=32000, T=1.0, seed=5, parents="star"),
+    "star-shared-V32000-T0": dict(B=1, N=64, V=32000, T=0.0, seed=10, parents="star"),
     "chain": dict(B=1, N=20, V=32000, T=1.0, seed=6, parents="chain"),
     "one-node": dict(B=3, N=1, V=32000, T=1.0, seed=7, parents="chain"),
 }
@@ -512,44 +518,68 @@ def _al256(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("case", list(SPLIT_CASES))
-def test_verify_split_rows(case):
-    c = SPLIT_CASES[case]
+@pytest.mark.parametrize("rows", ["shared", "node"])
+@pytest.mark.parametrize("case", list(ROW_CASES))
+def test_verify_large_vocab_rows(case, rows):
+    c = ROW_CASES[case]
     B, N, V = c["B"], c["N"], c["V"]
     par = {"star": trees.star, "chain": trees.chain}[c["parents"]](N) if "parents" in c else None
-    cfg = W.shrink(W.get(1), B=B, N=N, V=V, sigma_d=0.5 if case == "star" else W.get(1).sigma_d)
+    sigma = c.get("sigma_d", 0.5 if case == "star" else W.get(1).sigma_d)
+    cfg = W.shrink(W.get(1), B=B, N=N, V=V, sigma_d=sigma)
     s = W.make_step(cfg, c["T"], seed=c["seed"], parents=par, with_attention=False)
     nbytes = ev.binding.verify_accept_workspace_bytes(B, N, V)
-    assert nbytes >= B * N * 72 * 9 * 8  # the plan reserved exchange words
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    dp, dr = draft_args(s, rows)
     outs = []
     for rep in range(2):
         flags = torch.zeros(B, dtype=torch.int32, device="cuda")
-        say(f"verify split rows {case} call {rep}")
-        res = ev.verify_accept(dev(s.tokens), dev(s.draft_probs), dev(s.target_logits), dev(s.parents),
-                               dev(s.kv_len), s.T, dev(s.uniforms), workspace=ws, seq_flags=flags)
+        say(f"verify large vocabulary {case} rows={rows} call {rep}")
+        res = ev.verify_accept(dev(s.tokens), dp, dev(s.target_logits), dev(s.parents),
+                               dev(s.kv_len), s.T, dev(s.uniforms), draft_row=dr, workspace=ws,
+                               seq_flags=flags)
         torch.cuda.synchronize()
         outs.append({k: v.cpu().numpy() for k, v in res.items()})
         assert flags.cpu().tolist() == [0] * B
-        # what must start at zero is zero again: the per-sequence tickets, the
-        # per-node phase counts and the exchange words (the workspace layout
-        # of csrc/verify.hip: tickets | per-node results | exchange words)
-        cnt, stats = _al256(4 * B), _al256(20 * B * N)
-        w = ws.cpu().numpy()
-        assert not w[:cnt].any()
-        assert not w[cnt + 16 * B * N: cnt + 20 * B * N].any()
-        assert not w[cnt + stats:].any()
+        # what must start at zero is zero again: the per-sequence tickets and
+        # the argmax words (the workspace layout of csrc/verify.hip: sequence
+        # tickets | argmax words | per-node results)
+        head = _al256(4 * B) + _al256(8 * B * N)
+        assert not ws[:head].cpu().numpy().any()
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
     compared, excused = compare_walks(outs[0], s, oracle_walks(s))
     say(f"  compared {compared}, excused {excused}; accept_len {outs[0]['accept_len'].tolist()}")
     assert compared + excused == B
+    if case == "7b-descending":
+        assert outs[0]["accept_len"].max() >= 2
 
 
-def test_verify_chi_square_on_gpu():
+def test_verify_bad_draft_row_flagged():
+    """A draft-row index outside [0, N) on a tested node is flagged and read
+    as the node's own row; the walk stays in range."""
+    cfg = W.shrink(W.get(0), B=3, N=8, V=64)
+    s = W.make_step(cfg, 1.0, seed=13, with_attention=False)
+    dr = s.draft_row.copy()
+    dr[1, 3] = 8
+    dr[2, 5] = -1
+    flags = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    say("verify bad draft rows")
+    res = ev.verify_accept(dev(s.tokens), dev(s.draft_rows), dev(s.target_logits), dev(s.parents),
+                           dev(s.kv_len), 1.0, dev(s.uniforms), draft_row=dev(dr), seq_flags=flags)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [0, ev.binding.FLAG_BAD_ROW, ev.binding.FLAG_BAD_ROW]
+    m = res["accept_len"].cpu().numpy()
+    assert ((m >= 0) & (m < cfg.N)).all()
+    bonus = res["bonus"].cpu().numpy()
+    assert ((bonus >= 0) & (bonus < cfg.V)).all()
+
+
+@pytest.mark.parametrize("rows", ["node", "shared"])
+def test_verify_chi_square_on_gpu(rows):
     """Distribution preservation on the device: the first emitted token of many
     independent tiny sequences (fresh drafts from q, fresh uniforms) follows
-    the root's target distribution."""
+    the root's target distribution, for the step-by-step chain (a row per
+    node) and the closed form (siblings naming their parent's row)."""
     import scipy.stats
     V, N, B = 8, 8, 200_000
     rng = np.random.default_rng(11)
@@ -566,9 +596,15 @@ def test_verify_chi_square_on_gpu():
         cdf = np.cumsum(q[c].astype(np.float64) / q[c].sum())
         toks[:, c] = np.minimum(np.searchsorted(cdf, rng.random(B), side="right"), V - 1)
     u = rng.random((B, N), dtype=np.float32)
-    say("verify chi-square B=200000")
-    res = ev.verify_accept(dev(toks), dev(np.broadcast_to(q, (B, N, V))), dev(np.broadcast_to(lg, (B, N, V))),
-                           dev(np.broadcast_to(parents, (B, N))), dev(np.zeros(B, np.int32)), 1.0, dev(u))
+    say(f"verify chi-square B=200000 rows={rows}")
+    if rows == "node":
+        dq, drow = dev(np.broadcast_to(q, (B, N, V))), None
+    else:
+        dq = dev(np.broadcast_to(qd, (B, N, V)))
+        drow = dev(np.broadcast_to(np.maximum(parents, 0).astype(np.int32), (B, N)))
+    res = ev.verify_accept(dev(toks), dq, dev(np.broadcast_to(lg, (B, N, V))),
+                           dev(np.broadcast_to(parents, (B, N))), dev(np.zeros(B, np.int32)), 1.0,
+                           dev(u), draft_row=drow)
     torch.cuda.synchronize()
     m = res["accept_len"].cpu().numpy()
     first = np.where(m >= 1, res["accepted_tokens"].cpu().numpy()[:, 0], res["bonus"].cpu().numpy())
@@ -611,9 +647,9 @@ def test_fused_compaction_matches_separate_calls(idx, T, sigma):
     k1, v1 = bf(s.k_cache), bf(s.v_cache)
     nl1 = ev.kv_compact(k1, v1, dev(s.kv_len), dev(gpu["kv_src"]), dev(gpu["accept_len"]))
     k2, v2 = bf(s.k_cache), bf(s.v_cache)
-    out = ev.verify_accept_compact(dev(s.tokens), None if s.draft_probs is None else dev(s.draft_probs),
-                                   dev(s.target_logits), dev(s.parents), dev(s.kv_len), s.T,
-                                   dev(s.uniforms), k2, v2)
+    dp, dr = draft_args(s, "shared")
+    out = ev.verify_accept_compact(dev(s.tokens), dp, dev(s.target_logits), dev(s.parents),
+                                   dev(s.kv_len), s.T, dev(s.uniforms), k2, v2, draft_row=dr)
     torch.cuda.synchronize()
     for key in ("accept_len", "path", "accepted_tokens", "bonus", "kv_src"):
         assert np.array_equal(out[key].cpu().numpy(), gpu[key]), key

@@ -26,8 +26,8 @@ FLAG_BAD_PARENT = 1
 FLAG_BAD_KV_LEN = 2
 FLAG_BAD_TOKEN = 4
 FLAG_NONFINITE = 8
-FLAG_TIMEOUT = 16
 FLAG_BAD_PATH = 32
+FLAG_BAD_ROW = 64
 
 
 class EagleError(RuntimeError):
@@ -57,10 +57,10 @@ _SIGNATURES = {
     "eagle_tree_attn_parents_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P,
                                              _P, _P, _P, _P, _P]),
     "eagle_verify_accept_workspace": (_SZ, [_I, _I, _I]),
-    "eagle_verify_accept": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
-                                 _P, _P, _P, _P, _SZ, _P, _P]),
-    "eagle_verify_accept_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
-                                         _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P, _P]),
+    "eagle_verify_accept": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "eagle_verify_accept_compact": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _I, _I, _I, _P, _P, _SZ, _P, _P]),
     "eagle_kv_compact": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "eagle_feature_gather": (_I, [_P, _P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]),
     "eagle_dtree_expand": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P]),
@@ -275,9 +275,10 @@ def tree_attn_parents_noalloc(q, k_cache, v_cache, kv_len, parents, *, sm_scale:
 
 
 def _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
-                       outputs, seq_flags):
+                       outputs, seq_flags, draft_row=None):
     B, N, V = target_logits.shape
-    for t, name in ((draft_tokens, "draft_tokens"), (parents, "parents"), (uniforms, "uniforms")):
+    for t, name in ((draft_tokens, "draft_tokens"), (parents, "parents"), (uniforms, "uniforms"),
+                    (draft_row, "draft_row")):
         _expect(t, (B, N), name)
     _expect(draft_probs, (B, N, V), "draft_probs")
     _expect(kv_len, (B,), "kv_len")
@@ -295,12 +296,13 @@ def verify_accept_workspace_bytes(B, N, V) -> int:
 
 
 def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, temperature, uniforms,
-                  *, want_probs=False, want_final_dist=False, want_ratio=False, outputs=None,
-                  workspace=None, seq_flags=None, stream=None):
-    """Acceptance walk; returns a dict of device tensors (see include/eagle_verify.h)."""
+                  *, draft_row=None, want_probs=False, want_final_dist=False, want_ratio=False,
+                  outputs=None, workspace=None, seq_flags=None, stream=None):
+    """Acceptance walk; returns a dict of device tensors (see include/eagle_verify.h).
+    draft_row [B, N] int32 (optional): the row of draft_probs each node was drawn from."""
     B, N, V = target_logits.shape
     _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
-                       outputs, seq_flags)
+                       outputs, seq_flags, draft_row)
     dev = target_logits.device
     o = outputs or {}
     if not o:
@@ -319,6 +321,7 @@ def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, tem
         workspace = alloc_workspace(verify_accept_workspace_bytes(B, N, V), dev)
     _check(lib().eagle_verify_accept(
         _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(draft_probs, torch.float32, "draft_probs"),
+        _ptr(draft_row, torch.int32, "draft_row"),
         _ptr(target_logits, torch.float32, "target_logits"), _ptr(parents, torch.int32, "parents"),
         _ptr(kv_len, torch.int32, "kv_len"), B, N, V, float(temperature),
         _ptr(uniforms, torch.float32, "uniforms"),
@@ -330,13 +333,13 @@ def verify_accept(draft_tokens, draft_probs, target_logits, parents, kv_len, tem
 
 
 def verify_accept_compact(draft_tokens, draft_probs, target_logits, parents, kv_len, temperature,
-                          uniforms, k_cache, v_cache, *, outputs=None, new_kv_len=None,
-                          workspace=None, seq_flags=None, stream=None):
+                          uniforms, k_cache, v_cache, *, draft_row=None, outputs=None,
+                          new_kv_len=None, workspace=None, seq_flags=None, stream=None):
     """Acceptance walk and KV compaction in one launch; returns the walk's
     outputs (as verify_accept) plus "new_kv_len"."""
     B, N, V = target_logits.shape
     _check_walk_inputs(draft_tokens, draft_probs, target_logits, parents, kv_len, uniforms,
-                       outputs, seq_flags)
+                       outputs, seq_flags, draft_row)
     if k_cache.dim() != 4 or k_cache.shape[0] != B:
         raise ValueError(f"k_cache must be [B, Hkv, Lmax, d] with B = {B}, got {tuple(k_cache.shape)}")
     _expect(v_cache, k_cache.shape, "v_cache")
@@ -359,6 +362,7 @@ def verify_accept_compact(draft_tokens, draft_probs, target_logits, parents, kv_
         workspace = alloc_workspace(verify_accept_workspace_bytes(B, N, V), dev)
     _check(lib().eagle_verify_accept_compact(
         _ptr(draft_tokens, torch.int32, "draft_tokens"), _ptr(draft_probs, torch.float32, "draft_probs"),
+        _ptr(draft_row, torch.int32, "draft_row"),
         _ptr(target_logits, torch.float32, "target_logits"), _ptr(parents, torch.int32, "parents"),
         _ptr(kv_len, torch.int32, "kv_len"), B, N, V, float(temperature),
         _ptr(uniforms, torch.float32, "uniforms"),

@@ -39,7 +39,7 @@ extern "C" {
 
 const char* eagle_last_error(void) { return g_last_error.c_str(); }
 
-int eagle_abi_version(void) { return 1; }
+int eagle_abi_version(void) { return 2; }
 
 eagle_status_t eagle_validate_tree_host(const int32_t* parents, int B, int N) {
   if (B < 0) return fail(EAGLE_ERR_INVALID_ARGUMENT, "B must be >= 0 (got %d)", B);
@@ -223,6 +223,7 @@ size_t eagle_verify_accept_workspace(int B, int N, int V) {
 }
 
 eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* draft_probs,
+                                   const int32_t* draft_row,
                                    const float* target_logits, const int32_t* parents,
                                    const int32_t* kv_len, int B, int N, int V, float temperature,
                                    const float* uniforms, int32_t* accept_len, int32_t* path,
@@ -246,7 +247,7 @@ eagle_status_t eagle_verify_accept(const int32_t* draft_tokens, const float* dra
   if (!workspace || workspace_bytes < need)
     return fail(EAGLE_ERR_WORKSPACE, "verification needs %zu workspace bytes (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
-  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, target_logits, parents,
+  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, draft_row, target_logits, parents,
                                          kv_len, B, N, temperature, uniforms, accept_len, path,
                                          accepted_tokens, bonus_token, kv_src_slots, out_probs,
                                          out_final_dist, out_ratio, workspace, seq_flags,
@@ -262,7 +263,8 @@ static eagle_status_t check_compact_shape(int N, int Hkv, int d, int Lmax) {
 }
 
 eagle_status_t eagle_verify_accept_compact(
-    const int32_t* draft_tokens, const float* draft_probs, const float* target_logits,
+    const int32_t* draft_tokens, const float* draft_probs, const int32_t* draft_row,
+    const float* target_logits,
     const int32_t* parents, const int32_t* kv_len, int B, int N, int V, float temperature,
     const float* uniforms, int32_t* accept_len, int32_t* path, int32_t* accepted_tokens,
     int32_t* bonus_token, int32_t* kv_src_slots, uint16_t* k_cache, uint16_t* v_cache, int Hkv,
@@ -291,7 +293,7 @@ eagle_status_t eagle_verify_accept_compact(
     return fail(EAGLE_ERR_WORKSPACE, "verification needs %zu workspace bytes (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
   const eagle::VerifyCompact kc{k_cache, v_cache, new_kv_len, Hkv, d, Lmax};
-  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, target_logits, parents,
+  return hip_status(eagle::launch_verify(plan, draft_tokens, draft_probs, draft_row, target_logits, parents,
                                          kv_len, B, N, temperature, uniforms, accept_len, path,
                                          accepted_tokens, bonus_token, kv_src_slots, nullptr,
                                          nullptr, nullptr, workspace, seq_flags, kc,

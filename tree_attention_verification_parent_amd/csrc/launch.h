@@ -55,12 +55,10 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
 // Verification (vocabulary statistics + acceptance walk) -------------------
 struct VerifyPlan {
   int V;
-  int chunks;          // vocabulary chunks per row in the statistics pass
-  int walk_threads;    // threads of the walk block
-  int parts;           // workgroups per node on the sampling path (split rows)
-  size_t ws_stats;     // per-row statistics
-  size_t ws_partials;  // exchange words of split rows
-  size_t ws_counters;  // per-row counters
+  int parts;                 // workgroups per node of the T = 0 argmax (1: one per node)
+  size_t ws_counters;        // per-sequence tickets
+  size_t ws_amax;            // per-node packed argmax words
+  size_t ws_stats;           // per-node outcomes
 };
 
 VerifyPlan plan_verify(int B, int N, int V);
@@ -75,7 +73,7 @@ struct VerifyCompact {
 };
 
 hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
-                         const float* logits, const int32_t* parents, const int32_t* kv_len,
+                         const int32_t* draft_row, const float* logits, const int32_t* parents, const int32_t* kv_len,
                          int B, int N, float T, const float* uniforms, int32_t* accept_len,
                          int32_t* path, int32_t* acc_tokens, int32_t* bonus, int32_t* kv_src,
                          float* out_probs, float* out_final, float* out_ratio, void* ws,

@@ -15,30 +15,42 @@
 // and the uniforms, never on the rest of the walk, so every node computes it
 // speculatively in parallel; the last node of a sequence to finish (atomic
 // ticket) then follows the accepted candidates from the root, a scalar walk.
+// No workgroup ever waits for another: a sequence's nodes only meet at the
+// ticket, and the one that draws the last ticket walks.
 //
 // Per node j with candidates c_1..c_k (ascending) and T > 0:
 //   U_0 = exp((l_j - max) / T) (unnormalised target), C_0 = sum U_0
 //   ratio_s = U_{s-1}[t_s] / (C_{s-1} q_s[t_s])       (accept iff u_s < ratio_s)
 //   U_s = max(0, U_{s-1} - C_{s-1} q_s),  C_s = sum U_s  (kept if C_s = 0)
 // U_s / C_s is the adjusted distribution norm(max(0, r - q)) after s
-// rejections.
+// rejections.  When the candidates share one draft row q (siblings drawn
+// i.i.d. from their parent's draft distribution) the recursion has a closed
+// form: with S_0 = 0 and S_s = S_{s-1} + C_{s-1},
+//   U_s = max(0, U_0 - S_s q),  C_s = F(S_s),  F(S) = sum_v max(0, U_v - S q_v)
+// (by induction: where U_{s-1} > 0 it equals U_0 - S_{s-1} q, and where it is
+// 0, U_0 - S_s q <= U_0 - S_{s-1} q <= 0).  Each rejection is then one pass
+// over the two rows held in registers and one workgroup reduction, with no
+// row reloaded and no residual row written.
 //
 // A node's critical path is a sequence of full-vocabulary passes, each ending
 // in a workgroup reduction, so the kernel is built around short passes:
-//   * the row lives in registers across the 1024-thread workgroup (8 float4
+//   * the rows live in registers across the 1024-thread workgroup (8 float4
 //     per thread at V <= 32768), entries past V padded so no pass needs a
 //     bounds check;
-//   * a candidate's draft row is prefetched into LDS with direct-to-LDS loads
-//     (each thread's float4 lands where that thread reads it back, so no
-//     barrier guards the buffer) and is read once: the pass builds the updated
-//     row W = max(0, U - C q) in a second register row (the two rows swap
-//     roles each candidate), and the next row's prefetch is issued as soon as
-//     this thread's reads are done;
+//   * without a shared row, a candidate's draft row is prefetched into LDS
+//     with direct-to-LDS loads (each thread's float4 lands where that thread
+//     reads it back, so no barrier guards the buffer) and is read once: the
+//     pass builds the updated row W = max(0, U - C q) in a second register
+//     row, and the next row's prefetch is issued as soon as this thread's
+//     reads are done;
 //   * wave reductions use DPP within rows of 16 lanes and readlane across the
 //     four rows; a workgroup reduction takes one barrier (two alternating
 //     LDS slot sets);
 //   * masses: fp32 pairwise sums per thread, fp64 across threads, in a fixed
 //     order (deterministic).  The final draw scans in fp64.
+// At T = 0 a node's outcome needs only its row's argmax: rows are split over
+// several workgroups that each publish their part's (value, lowest index) as
+// one 64-bit atomic maximum, and the walk reads the maxima.
 #include <float.h>
 #include <limits.h>
 #include <stdlib.h>
@@ -52,17 +64,18 @@ namespace eagle {
 
 // Per-node results published for the walk (device-coherent stores/loads).
 struct NodeResults {
-  int32_t* acc;      // [B*N] accepted candidate, -1 if none
-  int32_t* bonus;    // [B*N] token drawn if the walk ends here
-  float* ratio;      // [B*N] ratio of node c as tested by its parent's chain
-  int32_t* ntested;  // [B*N] candidates of the node that its chain tested
-  int32_t* nphase;   // [B*N] exchange phases the node used (split rows)
-  int32_t* counter;  // [B] per-sequence tickets (zero between calls)
+  int32_t* acc;       // [B*N] accepted candidate, -1 if none
+  int32_t* bonus;     // [B*N] token drawn if the walk ends here
+  float* ratio;       // [B*N] ratio of node c as tested by its parent's chain
+  int32_t* ntested;   // [B*N] candidates of the node that its chain tested
+  int32_t* counter;   // [B] per-sequence tickets (zero between calls)
+  unsigned long long* amax;  // [B*N] packed (value, lowest id) maxima (zero between calls)
 };
 
 struct VArgs {
   const int32_t* tokens;
   const float* draft;
+  const int32_t* draft_row;  // [B*N] row of `draft` node i was drawn from, or null: row i
   const float* logits;
   const int32_t* parents;
   const int32_t* kv_len;
@@ -77,11 +90,11 @@ struct VArgs {
   float* out_ratio;
   int32_t* flags;
   NodeResults nr;
-  VerifyCompact kc;            // compaction fused into the walk (kc.k == nullptr: none)
-  unsigned long long* xwords;  // [B*N][kXPhases][kXWords] exchange words (split rows; zero between calls)
+  VerifyCompact kc;  // compaction fused into the walk (kc.k == nullptr: none)
   int N, V;
   int nodes;  // B * N
-  int P;      // workgroups per node (split rows when > 1)
+  int P;      // workgroups per node (T = 0 split argmax)
+  int guess_row;  // issue each node's own draft row with its logits (see the node kernel)
   float T;
 };
 
@@ -100,15 +113,13 @@ __device__ __forceinline__ float ld_c(float* p) {
       __hip_atomic_load(reinterpret_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-constexpr int kMaxParts = 8;  // split rows: workgroups per node
-
 template <int BLOCK, int NPT>
 struct Shared {
   static constexpr int NW = BLOCK / 64;
-  int par[64], tok[64], kids[64];
+  int par[64], tok[64], kids[64], row[64];
   float u[64];
   float ratio[64];
-  float qt[64 * 64];  // qt[k*64 + i] = q_{kid k}(t_{kid i}) for k <= i (T > 0)
+  float qt[64 * 64];  // qt[k*64 + i] = q_{kid k}(t_{kid i}) for k <= i (T > 0, rows not shared)
   int nk;
   // workgroup reductions: two slot sets, used alternately (see rb below)
   double rd[2][NW];
@@ -117,32 +128,24 @@ struct Shared {
   double sel_before;
   int sel_entry;
   int pick;
-  double gd[2];  // split rows: broadcast of the cross-workgroup results
-  float gf[2];
-  double pm[kMaxParts];  // split rows: each part's mass of the current row
-  float mp[kMaxParts];   // split rows: each part's own logit maximum
-  float fp[kMaxParts];   // split rows: exp((m_p - max) / T), each part's scale
-  int xabort;    // split rows: a wait timed out, later waits are skipped
   int last, term;
-  int wacc[64], wbonus[64], wnt[64], wph[64];
+  int wacc[64], wbonus[64], wnt[64];
   int mv[64];      // fused compaction: the path positions whose K/V move
   int nmv, Lkv;
-  float l2sink[64];  // split rows: destination of the L2 prefetch (never read)
   int path[64];
 };
 
-// Workgroup reductions over the BLOCK row threads (a split-row workgroup's
-// extra exchange and prefetch waves hold no row data: they take part in the
-// barriers and read the result).  `rb` selects the slot set and flips on every call;
-// all threads make the same sequence of calls, so a slot set is rewritten
-// only after the barrier of the reduction in between, which every reader of
-// its previous contents has passed: one barrier per reduction suffices.
+// Workgroup reductions over the BLOCK threads.  `rb` selects the slot set and
+// flips on every call; all threads make the same sequence of calls, so a slot
+// set is rewritten only after the barrier of the reduction in between, which
+// every reader of its previous contents has passed: one barrier per reduction
+// suffices.
 template <int BLOCK, int NPT>
 __device__ __forceinline__ double block_sum(double v, Shared<BLOCK, NPT>& sh, int& rb) {
   v = wave_allsum(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.rd[buf][threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.rd[buf][threadIdx.x >> 6] = v;
   barrier_lds();
   double t = 0.0;
 #pragma unroll
@@ -155,7 +158,7 @@ __device__ __forceinline__ float block_max(float v, Shared<BLOCK, NPT>& sh, int&
   v = wave_allmax(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.rf[buf][threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.rf[buf][threadIdx.x >> 6] = v;
   barrier_lds();
   float t = -INFINITY;
 #pragma unroll
@@ -168,7 +171,7 @@ __device__ __forceinline__ int block_min_i(int v, Shared<BLOCK, NPT>& sh, int& r
   v = wave_allmin_i(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.ri[buf][threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
   barrier_lds();
   int t = INT_MAX;
 #pragma unroll
@@ -181,168 +184,12 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
   v = wave_allmax_i(v);
   const int buf = rb;
   rb ^= 1;
-  if ((threadIdx.x & 63) == 0 && threadIdx.x < BLOCK) sh.ri[buf][threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.ri[buf][threadIdx.x >> 6] = v;
   barrier_lds();
   int t = INT_MIN;
 #pragma unroll
   for (int i = 0; i < BLOCK / 64; ++i) t = max(t, sh.ri[buf][i]);
   return t;
-}
-
-// ---- split rows ----------------------------------------------------------------
-// With P > 1 the P workgroups of a node each hold a slice of the row and every
-// workgroup reduction is completed across them through exchange words in the
-// workspace (64-bit atomics, then polling; the P workgroups run on one XCD
-// and are all resident, which the host checks).  A split workgroup has two
-// waves beyond its BLOCK row threads.  One does the exchange: its polling
-// loads never queue behind a row prefetch (a wave's vector loads complete in
-// order), so the prefetch of the next draft row stays in flight across the
-// exchange.  The other only brings the node's later draft rows into L2 at
-// the start, for the same reason.
-// Sums travel as fixed point relative to a known bound: every row wave of
-// every part writes its partial (value << 8 | 1, never zero) to a slot of its
-// own, and the exchange wave reads the P x 4 slots until all are written, so
-// every part forms the same exact integer total, and the same per-part
-// masses, which the final draw uses to find the part that holds its crossing
-// without another exchange.  A max travels as an order-preserving 32-bit
-// key with a separate count.  A wait that exceeds kSpinCap polls sets
-// EAGLE_FLAG_TIMEOUT and skips later waits.
-constexpr int kXWords = kMaxParts * 5;  // words per phase: one per (part, row wave), one per part
-constexpr int kXPhases = 72;            // phases per node: row statistics, candidates
-constexpr int kSpinCap = 1 << 20;
-constexpr double kFix = 1125899906842624.0;  // 2^50
-
-// round(x) for 0 <= x < 2^51 as an integer: adding 1.5 * 2^52 leaves a sum
-// whose last mantissa bit weighs 1, so the addition itself rounds to nearest
-// (even), and the integer is the difference of the bit patterns.
-__device__ __forceinline__ unsigned long long fix_round(double x) {
-  constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
-  return (unsigned long long)(__double_as_longlong(x + kMagic) - __double_as_longlong(kMagic));
-}
-
-struct Grp {
-  unsigned long long* words;  // this node's exchange words
-  int P, part, phase;
-  int base, len;              // this part's slice of the row: ids [base, base + len)
-  int32_t* flags;
-  int b;
-  int xt;                     // the thread that exchanges (lane 0 of the exchange wave)
-};
-
-__device__ __forceinline__ unsigned long long* grp_phase_words(Grp& g) {
-  return g.words + (size_t)g.phase * kXWords;
-}
-
-// Polls *w until its low 8 bits reach `need`; returns the last value read.
-template <int BLOCK, int NPT>
-__device__ __forceinline__ unsigned long long grp_wait(unsigned long long* w, unsigned long long cur,
-                                                       int need, Grp& g, Shared<BLOCK, NPT>& sh) {
-  int it = 0;
-#pragma nounroll
-  while ((int)(cur & 0xffull) < need && !sh.xabort) {
-    if (++it > kSpinCap) {
-      sh.xabort = 1;
-      if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
-      break;
-    }
-    cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return cur;
-}
-
-// Sum over the node's workgroups of v >= 0, with 0 <= total <= scale; inv is
-// kFix / scale (computed by the caller ahead of the reduction).  mid() runs on
-// every thread while the exchange is in flight (after the workgroup reduction
-// when P = 1); it must issue no memory access from the exchange wave.
-// Split rows: every row wave adds its own partial (fixed point, count 1) to
-// the phase word of its wave index without waiting, so no workgroup barrier
-// precedes the exchange; the exchange wave polls the BLOCK / 64 words until
-// each holds P arrivals, and their integer total is the same in every
-// workgroup.
-template <int BLOCK, int NPT, typename F>
-__device__ __forceinline__ double grp_sum(double v, double scale, double inv, Grp& g,
-                                          Shared<BLOCK, NPT>& sh, int& rb, F&& mid) {
-  constexpr int NW = BLOCK / 64;
-  // (split rows run 256-thread workgroups; wider ones always have P = 1)
-  if (NW != 4 || g.P == 1) {
-    v = block_sum<BLOCK, NPT>(v, sh, rb);
-    mid();
-    return v;
-  }
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int slot = g.phase & 1;
-  unsigned long long* w = grp_phase_words(g);
-  if (tid < BLOCK) {
-    v = wave_allsum(v);
-    if (lane == 0)  // an add into a zero word: atomics meet at the memory side, as the polls do
-      __hip_atomic_fetch_add(w + g.part * NW + (tid >> 6), (fix_round(v * inv) << 8) | 1ull,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  mid();  // guarded by the caller: no loads from the exchange wave
-  if ((tid >> 6) == (g.xt >> 6)) {
-    // the exchange wave: lane l < P * NW reads slot l (part l / NW)
-    const int nslots = g.P * NW;
-    unsigned long long x = 1ull;
-    int it = 0;
-#pragma nounroll
-    for (;;) {
-      if (lane < nslots) x = __hip_atomic_load(w + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__all(x != 0ull) || sh.xabort) break;
-      if (++it > kSpinCap) {
-        if (lane == 0) {
-          sh.xabort = 1;
-          if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
-        }
-        break;
-      }
-    }
-    // integers below 2^53: exact in fp64, in any order
-    double q = lane < nslots ? (double)(x >> 8) : 0.0;
-    q += dpp_d<kDppXor1>(q);  // the NW = 4 waves of a part are one quad
-    q += dpp_d<kDppXor2>(q);
-    const double tot = wave_allsum(lane < nslots && (lane & 3) == 0 ? q : 0.0);
-    const double unit = scale / kFix;
-    if (tot > 0.0 && lane < nslots && (lane & 3) == 0) sh.pm[lane >> 2] = q * unit;
-    if (lane == 0) sh.gd[slot] = tot * unit;
-  }
-  ++g.phase;
-  barrier_lds();
-  return sh.gd[slot];
-}
-template <int BLOCK, int NPT>
-__device__ __forceinline__ double grp_sum(double v, double scale, double inv, Grp& g,
-                                          Shared<BLOCK, NPT>& sh, int& rb) {
-  return grp_sum<BLOCK, NPT>(v, scale, inv, g, sh, rb, [] {});
-}
-
-template <int BLOCK, int NPT>
-__device__ __forceinline__ float grp_max(float v, Grp& g, Shared<BLOCK, NPT>& sh, int& rb) {
-  v = block_max<BLOCK, NPT>(v, sh, rb);
-  if (g.P == 1) return v;
-  const int slot = g.phase & 1;
-  if (threadIdx.x == g.xt) {
-    unsigned long long* w = grp_phase_words(g);
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t key = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-    __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(w), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the key is in before the count
-    unsigned long long cur = __hip_atomic_fetch_add(w + 1, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1ull;
-    grp_wait<BLOCK, NPT>(w + 1, cur, g.P, g, sh);
-    const uint32_t k = __hip_atomic_load(reinterpret_cast<uint32_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.gf[slot] = __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-  }
-  ++g.phase;
-  barrier_lds();
-  return sh.gf[slot];
-}
-
-// True in the waves that hold row data (all but a split workgroup's exchange
-// wave).  Read from the first lane so the compiler sees a wave-uniform
-// branch: loads issued under it then land in their destination registers
-// without a merge copy that would wait for them.
-template <int BLOCK>
-__device__ __forceinline__ bool row_wave() {
-  return __builtin_amdgcn_readfirstlane(threadIdx.x) < BLOCK;
 }
 
 // ---- rows --------------------------------------------------------------------
@@ -357,40 +204,44 @@ __device__ __forceinline__ float comp(const float4& f, int e) {
   return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
 }
 
-// Logit row into registers; entries past V read as -FLT_MAX (no mass, never
-// the maximum of a row that has a finite entry).
+// `len` floats of a row into registers (len >= 1); entries past len read as
+// `pad` (-FLT_MAX for logits: no mass, never the maximum of a row that has a
+// finite entry; 0 for draft rows).  Every load is issued at an in-range
+// address and the padding selected afterwards, so the loads need no branches.
 template <int BLOCK, int NPT>
-__device__ __forceinline__ void load_logits(Row<BLOCK, NPT>& r, const float* src, int V) {
+__device__ __forceinline__ void load_row(Row<BLOCK, NPT>& r, const float* src, int len, float pad) {
   const int tid = threadIdx.x;
-  // every load is issued at an in-range address and the padding selected
-  // afterwards, so the loads need no branches
-  const bool row = tid < BLOCK;  // not an extra wave of a split workgroup
-  if ((V & 3) == 0) {
+  if ((len & 3) == 0) {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      const bool in = row && e0 < V;
+      const bool in = e0 < len;
       const float4 x = *reinterpret_cast<const float4*>(src + (in ? e0 : 0));
-      r.v[k] = in ? x : make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
+      r.v[k] = in ? x : make_float4(pad, pad, pad, pad);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      const float x0 = src[min(e0 + 0, V - 1)], x1 = src[min(e0 + 1, V - 1)];
-      const float x2 = src[min(e0 + 2, V - 1)], x3 = src[min(e0 + 3, V - 1)];
-      r.v[k].x = row && e0 + 0 < V ? x0 : -FLT_MAX;
-      r.v[k].y = row && e0 + 1 < V ? x1 : -FLT_MAX;
-      r.v[k].z = row && e0 + 2 < V ? x2 : -FLT_MAX;
-      r.v[k].w = row && e0 + 3 < V ? x3 : -FLT_MAX;
+      const float x0 = src[min(e0 + 0, len - 1)], x1 = src[min(e0 + 1, len - 1)];
+      const float x2 = src[min(e0 + 2, len - 1)], x3 = src[min(e0 + 3, len - 1)];
+      r.v[k].x = e0 + 0 < len ? x0 : pad;
+      r.v[k].y = e0 + 1 < len ? x1 : pad;
+      r.v[k].z = e0 + 2 < len ? x2 : pad;
+      r.v[k].w = e0 + 3 < len ? x3 : pad;
     }
   }
 }
 
-// exp(z) for z <= 0 as 2^(z log2 e) with the rounding error of the product
-// carried as a first-order correction (relative error ~2 ulp).  Arguments
-// below -110 (results below the fp32 range) are clamped, which keeps the
-// correction finite for the -FLT_MAX padding.
+// exp(z) for z <= 0, computed as 2^t with t = z log2(e) and the rounding of
+// that product carried separately: with log2(e) split into an fp32 head H and
+// tail L, the FMA fma(z, H, -t) gives the rounding error of z * H exactly
+// (the product of two fp32 values is exact in the FMA), z * L adds the tail,
+// and 2^(t + e) = 2^t (1 + e ln 2) to first order, so the result is
+// 2^t + 2^t * e * ln 2.  The hardware exp2 is within 1 ulp, so the whole is
+// within about 2 ulp of exp(z) (measured against fp64 on the device in the
+// tests).  Arguments below -110 (results below the fp32 range) are clamped,
+// which keeps the correction finite for the -FLT_MAX padding.
 __device__ __forceinline__ float exp_neg(float z) {
   z = fmaxf(z, -110.f);
   constexpr float kL2E = 1.44269502162933349609375f;  // log2(e), fp32 head
@@ -411,9 +262,13 @@ __device__ __forceinline__ float pairwise(const float (&s)[NPT]) {
            (((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15])));
   } else if constexpr (NPT == 8) {
     return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-  } else {
-    static_assert(NPT == 4, "rows of 4, 8 or 16 float4 per thread");
+  } else if constexpr (NPT == 4) {
     return (s[0] + s[1]) + (s[2] + s[3]);
+  } else if constexpr (NPT == 2) {
+    return s[0] + s[1];
+  } else {
+    static_assert(NPT == 1, "rows of 1, 2, 4, 8 or 16 float4 per thread");
+    return s[0];
   }
 }
 
@@ -424,88 +279,11 @@ __device__ __forceinline__ float target_entry(float x, float m, bool unit, float
   return exp_neg(unit ? x - m : (x - m) * invT);
 }
 
-// Split rows: a row's maximum and mass in one exchange.  Each part has
-// scaled its slice by its own maximum m_loc (U = exp((l - m_loc) / T),
-// entries <= 1, 1024 per row wave).  Every row wave adds its partial mass to
-// its slot and wave 0 also posts m_loc (an order-preserving key); every part
-// then forms, with the same operations, the maximum M, the factors
-// f_p = exp((m_p - M) / T), each part's mass f_p S_p and the total in a fixed
-// order.  The caller rescales its slice by f_part.  Returns the total.
+// Non-finite logits (NaN, +-Inf) are reported and given no mass: replaced by
+// -FLT_MAX in the row.  x * 0 is NaN exactly for non-finite x: one fma per
+// entry to detect them.
 template <int BLOCK, int NPT>
-__device__ __forceinline__ double grp_stats(double v, float m_loc, bool unit, float invT, Grp& g,
-                                            Shared<BLOCK, NPT>& sh) {
-  constexpr int NW = BLOCK / 64;
-  static_assert(NW == 4, "split rows: four row waves");
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int slot = g.phase & 1;
-  unsigned long long* w = grp_phase_words(g);
-  const int nsum = g.P * NW;
-  if (tid < BLOCK) {
-    v = wave_allsum(v);
-    if (lane == 0) {
-      __hip_atomic_fetch_add(w + g.part * NW + (tid >> 6), (fix_round(v * (kFix / 1024.0)) << 8) | 1ull,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tid == 0) {
-        const uint32_t bits = __float_as_uint(m_loc);
-        const uint32_t key = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-        __hip_atomic_fetch_add(w + nsum + g.part, ((unsigned long long)key << 8) | 1ull,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  if ((tid >> 6) == (g.xt >> 6)) {
-    // the exchange wave: lanes [0, nsum) read the mass slots, lanes
-    // [nsum, nsum + P) the maxima
-    const int nslots = nsum + g.P;
-    unsigned long long x = 1ull;
-    int it = 0;
-#pragma nounroll
-    for (;;) {
-      if (lane < nslots) x = __hip_atomic_load(w + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__all(x != 0ull) || sh.xabort) break;
-      if (++it > kSpinCap) {
-        if (lane == 0) {
-          sh.xabort = 1;
-          if (g.flags) atomicOr(g.flags + g.b, EAGLE_FLAG_TIMEOUT);
-        }
-        break;
-      }
-    }
-    const bool is_max = lane >= nsum && lane < nslots;
-    const uint32_t k = (uint32_t)(x >> 8);
-    const float mp = is_max ? __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k) : -INFINITY;
-    const float M = wave_allmax(mp);
-    const float f = is_max ? exp_neg(unit ? mp - M : (mp - M) * invT) : 0.f;
-    if (is_max) {
-      sh.mp[lane - nsum] = mp;
-      sh.fp[lane - nsum] = f;
-    }
-    // integers below 2^53: exact in fp64, in any order
-    double q = lane < nsum ? (double)(x >> 8) : 0.0;
-    q += dpp_d<kDppXor1>(q);  // the NW = 4 waves of a part are one quad
-    q += dpp_d<kDppXor2>(q);
-    const float fq = __shfl(f, nsum + (lane >> 2));  // the factor of this lane's part
-    const double mass = lane < nsum && (lane & 3) == 0 ? (double)fq * q * (1024.0 / kFix) : 0.0;
-    const double tot = wave_allsum(mass);
-    if (lane < nsum && (lane & 3) == 0) sh.pm[lane >> 2] = mass;
-    if (lane == 0) sh.gd[slot] = tot;
-  }
-  ++g.phase;
-  barrier_lds();
-  return sh.gd[slot];
-}
-
-// Target row statistics of one node from its logits (already in U): flags
-// non-finite logits (they are given no mass); T = 0 returns the lowest-index
-// argmax; T > 0 turns U into exp((l - max)/T) and returns its mass in C.
-// before_sum(buf, m, unit, invT) runs before the mass reduction, whose
-// barrier (slot set buf, also returned in sum_buf) publishes what it writes.
-template <int BLOCK, int NPT, bool GREEDY, typename F>
-__device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
-                                            double& C, int& sum_buf, F&& before_sum, Grp& grp,
-                                            Shared<BLOCK, NPT>& sh, int& rb) {
-  const int tid = threadIdx.x;
-  // x * 0 is NaN exactly for non-finite x: one fma per entry
+__device__ __forceinline__ void sanitize_logits(Row<BLOCK, NPT>& U, int b, int32_t* flags) {
   float bad = 0.f;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
@@ -525,33 +303,51 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
       f.w = isfinite(f.w) ? f.w : -FLT_MAX;
     }
   }
-  if (__ballot(nonfinite) && (tid & 63) == 0 && flags) atomicOr(flags + b, EAGLE_FLAG_NONFINITE);
+  if (__ballot(nonfinite) && (threadIdx.x & 63) == 0 && flags) atomicOr(flags + b, EAGLE_FLAG_NONFINITE);
+}
 
+// The lowest index of the row's maximum (this workgroup's row or slice):
+// every thread's first maximum in id order, then the workgroup's.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void row_argmax(const Row<BLOCK, NPT>& U, float& mx, int& am,
+                                           Shared<BLOCK, NPT>& sh, int& rb) {
+  const int tid = threadIdx.x;
+  float lm = -INFINITY;
+  int li = INT_MAX;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = comp(U.v[k], e);
+      const bool gt = x > lm;  // ids increase with (k, e): first maximum kept
+      lm = gt ? x : lm;
+      li = gt ? (k * BLOCK + tid) * 4 + e : li;
+    }
+  mx = block_max<BLOCK, NPT>(lm, sh, rb);
+  am = block_min_i<BLOCK, NPT>(lm == mx ? li : INT_MAX, sh, rb);
+}
+
+// Target row statistics of one node from its logits (already in U): T = 0
+// returns the lowest-index argmax; T > 0 turns U into exp((l - max)/T) and
+// returns its mass in C.  before_sum(m, unit, invT) runs before the mass
+// reduction, whose barrier publishes what it writes to LDS.
+template <int BLOCK, int NPT, bool GREEDY, typename F>
+__device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
+                                            double& C, F&& before_sum, Shared<BLOCK, NPT>& sh,
+                                            int& rb) {
+  sanitize_logits<BLOCK, NPT>(U, b, flags);
   if constexpr (GREEDY) {
-    float lm = -INFINITY;
-    int li = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < NPT; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = comp(U.v[k], e);
-        const bool gt = x > lm;  // ids increase with (k, e): first maximum kept
-        lm = gt ? x : lm;
-        li = gt ? (k * BLOCK + tid) * 4 + e : li;
-      }
-    const float mx = block_max<BLOCK, NPT>(lm, sh, rb);
-    const int am = block_min_i<BLOCK, NPT>(lm == mx ? li : INT_MAX, sh, rb);
+    float mx;
+    int am;
+    row_argmax<BLOCK, NPT>(U, mx, am, sh, rb);
     C = 1.0;
-    sum_buf = 0;
     return am == INT_MAX ? 0 : am;
   } else {
     float lm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
-    const bool split = BLOCK == 256 && grp.P > 1;
-    // split rows: this part's own maximum (the global one comes with the mass)
-    const float m = split ? block_max<BLOCK, NPT>(lm, sh, rb) : grp_max<BLOCK, NPT>(lm, grp, sh, rb);
+    const float m = block_max<BLOCK, NPT>(lm, sh, rb);
     const bool unit = T == 1.f;
     const float invT = 1.f / T;
     float s[NPT];
@@ -564,24 +360,8 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
       f.w = exp_neg(unit ? f.w - m : (f.w - m) * invT);
       s[k] = sum4(f);
     }
-    sum_buf = rb;
-    before_sum(sum_buf, m, unit, invT);
-    if constexpr (BLOCK == 256) {
-      if (split) {
-        C = grp_stats<BLOCK, NPT>((double)pairwise<NPT>(s), m, unit, invT, grp, sh);
-        const float f = sh.fp[grp.part];
-#pragma unroll
-        for (int k = 0; k < NPT; ++k) {
-          U.v[k].x *= f;
-          U.v[k].y *= f;
-          U.v[k].z *= f;
-          U.v[k].w *= f;
-        }
-        return 0;
-      }
-    }
-    // entries <= 1, V <= 32768
-    C = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(s), 32768.0, kFix / 32768.0, grp, sh, rb);
+    before_sum(m, unit, invT);
+    C = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s), sh, rb);  // entries <= 1
     return 0;
   }
 }
@@ -598,18 +378,8 @@ __device__ __forceinline__ void find_kids(int N, int j, Shared<BLOCK, NPT>& sh) 
   if (lane == 0) sh.nk = __popcll(mask);
 }
 
-// f(std::integral_constant<int, J>) for J = 0..N-1, unrolled.
-template <typename F, int... J>
-__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J...>) {
-  (f(std::integral_constant<int, J>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-  unroll_seq(f, std::make_integer_sequence<int, N>{});
-}
-
 // Position of q_{kid k}(t_{kid i}), k <= i < nk, in sh.qt.
-__device__ __forceinline__ int tri(int k, int i, int) { return k * 64 + i; }
+__device__ __forceinline__ int tri(int k, int i) { return k * 64 + i; }
 
 // A draft row -> LDS with direct-to-LDS loads: thread t's float4 k lands at
 // LDS float4 k*BLOCK + t, where only thread t reads it back.  Slots past V are
@@ -628,46 +398,16 @@ __device__ __forceinline__ void issue_row_lds(const float* row, int V, float4* q
 
 // The candidates of a node, one per lane (lane i < nk holds candidate i, in
 // every wave; lanes past nk hold tok = -1): node id, drafted token (-1 if
-// outside the vocabulary), its uniform and q_i(t_i).  Read with readlane, so
-// a chain step needs no LDS lookups to test its candidate.
+// outside the vocabulary), the draft row it was drawn from, its uniform, the
+// draft probability q_i(t_i) and (shared row) the target entry U_0(t_i).
+// Read with readlane, so a chain step needs no LDS lookups to test its
+// candidate.
 struct Cand {
-  int kid, tok;
-  float u, q;
+  int kid, tok, row;
+  float u, q, ut;
 };
 
-// Brings rows into this XCD's L2 ahead of use: one 4-byte direct-to-LDS load
-// per 128-byte line, into a scratch LDS word nothing reads.  Written as
-// inline assembly (M0 saved and restored around it) so the compiler does not
-// treat the transfer as a pending LDS write that every later LDS read must
-// wait for; the hardware counts it like any vector load, so later waits can
-// only become longer, never too short.
-__device__ __forceinline__ void l2_touch(const float* p, uint32_t sink_lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(sink_lds), "v"(p)
-      : "memory");
-}
-
-// True in a split workgroup's prefetch wave (the last one).
-template <int BLOCK>
-__device__ __forceinline__ bool prefetch_wave() {
-  return __builtin_amdgcn_readfirstlane(threadIdx.x) >= BLOCK + 64;
-}
-
-// Draft rows touched ahead of the chain by the prefetch wave: few enough that
-// its transfers are issued quickly (its workgroup's barriers wait for it).
-constexpr int kL2Ahead = 3;
-
-// One wave brings a row slice of len floats into L2 (one touch per line).
-__device__ __forceinline__ void l2_touch_slice(const float* row, int len, float* sink) {
-  const int lines = (len + 31) / 32;
-  const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) float*)sink;
-  for (int l = threadIdx.x & 63; l < lines; l += 64) l2_touch(row + l * 32, lds);
-}
-
+// ---- candidates with their own draft rows: the recursion step by step --------
 // One candidate of the multi-round chain at a node: the ratio test of
 // candidate s against the current row `cur` (mass C, entry ut at the
 // candidate's token) and, on rejection, the adjusted row into `nxt`.
@@ -676,20 +416,15 @@ __device__ __forceinline__ void l2_touch_slice(const float* row, int len, float*
 // update leaves no mass).  Lane i < nk of every wave carries `val`, the
 // current row's entry at candidate i's token, updated with the same fp32
 // operations as the row (so bit-identical to it) from the gathered sh.qt
-// table.  The next candidate's draft row is prefetched while this one's
-// reduction runs: with RP into the registers qn (split rows; row s is in qn
-// on entry and row s + 1 is loaded into it once read), else with VEC into
-// qlds by direct-to-LDS loads.
-template <int BLOCK, int NPT, bool VEC, bool RP, bool RATIO>
+// table.  With VEC the next candidate's draft row is prefetched into qlds by
+// direct-to-LDS loads while this one's reduction runs.
+template <int BLOCK, int NPT, bool VEC, bool RATIO>
 __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<BLOCK, NPT>& cur,
                                            Row<BLOCK, NPT>& nxt, double& C, float& ut, float& val,
-                                           const Cand& cd, float4 (&qn)[NPT], int s, int nk,
-                                           bool stop_at_accept, Grp& grp, Shared<BLOCK, NPT>& sh,
-                                           float4* qlds, int& rb) {
+                                           const Cand& cd, int s, int nk, bool stop_at_accept,
+                                           Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   const int tid = threadIdx.x, lane = tid & 63, V = a.V;
-  // this workgroup's slice of candidate i's draft row (the whole row when P = 1)
-  auto qrow = [&](int i) { return a.draft + (ob + lane_i(cd.kid, i)) * V + grp.base; };
-  const int len = grp.len;
+  auto qrow = [&](int i) { return a.draft + (ob + lane_i(cd.row, i)) * V; };
   const bool tok_ok = lane_i(cd.tok, s) >= 0;
   const double qt = tok_ok ? (double)lane_f(cd.q, s) : 0.0;
   const double num = tok_ok ? (double)ut : 0.0;
@@ -697,35 +432,25 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
   // (q = 0: ratio is +inf when num > 0, else 0)
   const double den = C * qt;
   const bool accept = qt > 0.0 ? (double)lane_f(cd.u, s) * den < num : num > 0.0;
-  const double inv = kFix / C;  // for the mass exchange; its latency hides behind the pass
   if (RATIO && tid == 0)
     sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
   if (stop_at_accept && accept) return true;
   // rejection: nxt = max(0, cur - C q_s) and its mass, one read of q_s
-  const float q_lane = sh.qt[tri(s, lane, nk)];  // q_s at candidate `lane`'s token
-  if (VEC && !RP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
+  const float q_lane = sh.qt[tri(s, lane)];  // q_s at candidate `lane`'s token
+  if (VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own prefetch landed
   const float cf = (float)C;
   const bool more = s + 1 < nk;
   float ps[NPT];
-  float4 qv[NPT];
+  // the draft row: from this thread's own LDS slots (VEC), or loaded into
+  // the output row first and consumed in place
+  if constexpr (!VEC) load_row<BLOCK, NPT>(nxt, qrow(s), V, 0.f);
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
-    const int e0 = (k * BLOCK + tid) * 4;
-    if constexpr (RP) {
-      qv[k] = tid < BLOCK && e0 < len ? qn[k] : make_float4(0.f, 0.f, 0.f, 0.f);
-    } else if constexpr (VEC) {
-      qv[k] = qlds[k * BLOCK + tid];
-    } else {
-      const float* qs = qrow(s);
-      const float x0 = qs[min(e0 + 0, len - 1)], x1 = qs[min(e0 + 1, len - 1)];
-      const float x2 = qs[min(e0 + 2, len - 1)], x3 = qs[min(e0 + 3, len - 1)];
-      qv[k] = make_float4(e0 + 0 < len ? x0 : 0.f, e0 + 1 < len ? x1 : 0.f, e0 + 2 < len ? x2 : 0.f,
-                          e0 + 3 < len ? x3 : 0.f);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    const float4 q = qv[k];
+    float4 q;
+    if constexpr (VEC)
+      q = qlds[k * BLOCK + tid];
+    else
+      q = nxt.v[k];
     float4& w = nxt.v[k];
     w.x = fmaxf(0.f, fmaf(-cf, q.x, cur.v[k].x));
     w.y = fmaxf(0.f, fmaf(-cf, q.y, cur.v[k].y));
@@ -734,29 +459,14 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
     ps[k] = sum4(w);
   }
   const float vnew = fmaxf(0.f, fmaf(-cf, q_lane, val));
-  if constexpr (VEC && !RP) {
+  if constexpr (VEC) {
     if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of q_s done
-      issue_row_lds<BLOCK, NPT>(qrow(s + 1), len, qlds);
+      issue_row_lds<BLOCK, NPT>(qrow(s + 1), V, qlds);
     }
   }
-  // RP: row s + 1's loads are issued once this workgroup's partial mass is
-  // handed to the exchange, so they overlap it (addresses clamped into the
-  // slice, len >= 4; the tail is zeroed on use)
-  const double Cn = grp_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), C, inv, grp, sh, rb, [&] {
-    if constexpr (RP) {
-      if (more && row_wave<BLOCK>()) {
-        const float* qs = qrow(s + 1);
-#pragma unroll
-        for (int k = 0; k < NPT; ++k)
-          qn[k] = *reinterpret_cast<const float4*>(qs + min((k * BLOCK + tid) * 4, len - 4));
-      } else if (s + 1 + kL2Ahead < nk && prefetch_wave<BLOCK>()) {
-        l2_touch_slice(qrow(s + 1 + kL2Ahead), len, sh.l2sink);
-      }
-    }
-  });  // Cn <= C
-  const bool commit = Cn > 0.0;
-  if (commit) {
+  const double Cn = block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);  // Cn <= C
+  if (Cn > 0.0) {
     C = Cn;
     if (lane > s) val = vnew;
   } else {
@@ -767,26 +477,24 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
   return false;
 }
 
-// The multi-round chain at one node: tests its candidates in order (stopping
-// at the first acceptance when `stop_at_accept`), leaving the adjusted row in
-// U (unnormalised, mass C).  ut is U's entry at the first candidate's token,
-// val the per-lane candidate entries (see chain_step).  Candidate s's ratio
-// goes to sh.ratio[s] (RATIO).  Returns the index of the accepted candidate,
-// or -1.  The first candidate's row prefetch (RP: into qn) must already be
-// issued.  One copy of the step's code (the loop is not unrolled: the step
-// is long, and a kernel that starts with a cold instruction cache pays for
-// every line of straight code once); the next row is moved into U after each
-// step.
-template <int BLOCK, int NPT, bool VEC, bool RP, bool RATIO>
-__device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, NPT>& U, double& C,
-                                         float ut, float val, const Cand& cd, float4 (&qn)[NPT],
-                                         int nk, bool stop_at_accept, Grp& grp,
+// The multi-round chain at one node, candidates with their own rows: tests
+// them in order (stopping at the first acceptance when `stop_at_accept`),
+// leaving the adjusted row in U (unnormalised, mass C).  ut is U's entry at
+// the first candidate's token, val the per-lane candidate entries.  Candidate
+// s's ratio goes to sh.ratio[s] (RATIO).  Returns the index of the accepted
+// candidate, or -1.  The first candidate's row prefetch (VEC) must already be
+// issued.  W is a second row buffer.  One copy of the step's code (the loop is
+// not unrolled: the step is long, and a kernel that starts with a cold
+// instruction cache pays for every line of straight code once).
+template <int BLOCK, int NPT, bool VEC, bool RATIO>
+__device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, NPT>& U,
+                                         Row<BLOCK, NPT>& W, double& C, float ut, float val,
+                                         const Cand& cd, int nk, bool stop_at_accept,
                                          Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
-  Row<BLOCK, NPT> W;
 #pragma nounroll
   for (int s = 0; s < nk; ++s) {
-    if (chain_step<BLOCK, NPT, VEC, RP, RATIO>(a, ob, U, W, C, ut, val, cd, qn, s, nk,
-                                               stop_at_accept, grp, sh, qlds, rb))
+    if (chain_step<BLOCK, NPT, VEC, RATIO>(a, ob, U, W, C, ut, val, cd, s, nk, stop_at_accept, sh,
+                                           qlds, rb))
       return s;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) U.v[k] = W.v[k];
@@ -794,97 +502,170 @@ __device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, N
   return -1;
 }
 
+// ---- candidates sharing one draft row: the closed form --------------------------
+// After s rejections the adjusted row is max(0, U - S q) with mass F(S)
+// (S = S_s, see the top of the file).  S is carried in fp64 and applied as an
+// fp32 pair (head + tail), so the row entry is exact to about one rounding
+// however large S grows relative to an entry; every entry and every
+// candidate's entry come from the same two FMAs, so a candidate's numerator
+// is bit-identical to its entry of the row.
+__device__ __forceinline__ float residual(float u, float q, float hs, float ls) {
+  return fmaxf(0.f, fmaf(-ls, q, fmaf(-hs, q, u)));
+}
+
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void split_s(double S, float& hs, float& ls) {
+  hs = (float)S;
+  ls = (float)(S - (double)hs);
+}
+
+// F(S): one pass over the two rows and one workgroup reduction.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ double residual_mass(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
+                                                double S, Shared<BLOCK, NPT>& sh, int& rb) {
+  float hs, ls;
+  split_s<BLOCK, NPT>(S, hs, ls);
+  float ps[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const float4 u = U.v[k], q = Q.v[k];
+    ps[k] = (residual(u.x, q.x, hs, ls) + residual(u.y, q.y, hs, ls)) +
+            (residual(u.z, q.z, hs, ls) + residual(u.w, q.w, hs, ls));
+  }
+  return block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);
+}
+
+// The adjusted row max(0, U - S q) materialised (for the final draw).
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void residual_row(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
+                                             double S, Row<BLOCK, NPT>& W) {
+  float hs, ls;
+  split_s<BLOCK, NPT>(S, hs, ls);
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const float4 u = U.v[k], q = Q.v[k];
+    W.v[k] = make_float4(residual(u.x, q.x, hs, ls), residual(u.y, q.y, hs, ls),
+                         residual(u.z, q.z, hs, ls), residual(u.w, q.w, hs, ls));
+  }
+}
+
+// The chain over candidates that share the draft row Q: S, C start at 0,
+// sum U; on a rejection S <- S + C and C <- F(S) (kept if F(S) = 0, as the
+// step-by-step form keeps the previous row).  Returns the accepted
+// candidate's index or -1; S and C describe the adjusted row afterwards.
+template <int BLOCK, int NPT, bool RATIO>
+__device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
+                                                double& S, double& C, const Cand& cd, int nk,
+                                                bool stop_at_accept, Shared<BLOCK, NPT>& sh,
+                                                int& rb) {
+  const int tid = threadIdx.x;
+#pragma nounroll
+  for (int s = 0; s < nk; ++s) {
+    float hs, ls;
+    split_s<BLOCK, NPT>(S, hs, ls);
+    const float wl = residual(cd.ut, cd.q, hs, ls);  // each lane's candidate entry
+    const bool tok_ok = lane_i(cd.tok, s) >= 0;
+    const double qt = tok_ok ? (double)lane_f(cd.q, s) : 0.0;
+    const double num = tok_ok ? (double)lane_f(wl, s) : 0.0;
+    const double den = C * qt;
+    const bool accept = qt > 0.0 ? (double)lane_f(cd.u, s) * den < num : num > 0.0;
+    if (RATIO && tid == 0)
+      sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
+    if (stop_at_accept && accept) return s;
+    const double Sn = S + C;
+    const double Cn = residual_mass<BLOCK, NPT>(U, Q, Sn, sh, rb);
+    if (Cn > 0.0) {
+      S = Sn;
+      C = Cn;
+    }
+  }
+  return -1;
+}
+
 // Set-up of one node's chain after the tree is in LDS and the node's logits
-// were issued into U: its children (sh.kids, and per lane in cd), the first
-// candidate's row prefetch, the table qt[k][i] = q_{kid k}(t_{kid i}) and
-// each candidate's own logit (gathered while the row pass runs), then the
-// row statistics.  Returns the argmax (T = 0); sets C, ut (U at the first
+// were issued into U (and, with q_guess, the node's own draft row into Q):
+// its children (sh.kids, and per lane in cd), whether they share one draft
+// row (`shared`) and then that row into Q, or else the
+// first candidate's row prefetch and the table qt[k][i] = q_{kid k}(t_{kid i});
+// each candidate's own logit (gathered while the row pass runs), then the row
+// statistics.  Returns the argmax (T = 0); sets C, ut (U at the first
 // candidate's token) and, on lane i < nk, val = U at candidate i's token.
-template <int BLOCK, int NPT, bool GREEDY, bool VEC, bool RP>
+template <int BLOCK, int NPT, bool GREEDY, bool VEC>
 __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, int b,
-                                          int32_t* flags, Row<BLOCK, NPT>& U, double& C, float& ut,
-                                          float& val, Cand& cd, float4 (&qn)[NPT], Grp& grp,
+                                          int32_t* flags, Row<BLOCK, NPT>& U,
+                                          Row<BLOCK, NPT>& Q, bool q_guess, double& C, float& ut,
+                                          float& val, Cand& cd, bool& shared,
                                           Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   const int tid = threadIdx.x, lane = tid & 63, V = a.V;
   find_kids<BLOCK, NPT>(a.N, node, sh);
   barrier_lds();
   const int nk = sh.nk;
-  int sum_buf = 0;
   ut = 0.f;
   val = 0.f;
+  shared = false;
   if constexpr (GREEDY) {
-    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, sum_buf,
-                                          [](int, float, bool, float) {}, grp, sh, rb);
+    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, [](float, bool, float) {}, sh, rb);
   } else {
     cd.kid = 0;
     cd.tok = -1;
+    cd.row = 0;
     cd.u = 0.f;
     cd.q = 0.f;
+    cd.ut = 0.f;
     if (lane < nk) {
       cd.kid = sh.kids[lane];
       const int t = sh.tok[cd.kid];
       cd.tok = t >= 0 && t < V ? t : -1;
       cd.u = sh.u[cd.kid];
+      cd.row = sh.row[cd.kid];
     }
-    if (nk > 0) {
-      const float* q0 = a.draft + (ob + lane_i(cd.kid, 0)) * V + grp.base;
-      if constexpr (RP) {
-        if (row_wave<BLOCK>()) {
+    const int r0 = lane_i(cd.row, 0);
+    shared = nk > 0 && __ballot(lane < nk && cd.row != r0) == 0;  // wave-uniform
+    if (shared) {
+      // the one draft row (unless already guessed right), and each
+      // candidate's probability in it
+      if (!(q_guess && r0 == node)) load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+      if (cd.tok >= 0) cd.q = a.draft[(ob + r0) * V + cd.tok];
+    } else if (nk > 0 && VEC) {
+      // slots past V are never loaded: zero this thread's (the pass reads them)
 #pragma unroll
-          for (int k = 0; k < NPT; ++k)
-            qn[k] = *reinterpret_cast<const float4*>(q0 + min((k * BLOCK + tid) * 4, grp.len - 4));
-        }
-      } else if constexpr (VEC) {
-        // slots past the slice are never loaded: zero this thread's (the pass reads them)
-#pragma unroll
-        for (int k = 0; k < NPT; ++k)
-          if ((k * BLOCK + tid) * 4 >= grp.len) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-        issue_row_lds<BLOCK, NPT>(q0, grp.len, qlds);
-      }
+      for (int k = 0; k < NPT; ++k)
+        if ((k * BLOCK + tid) * 4 >= V) qlds[k * BLOCK + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+      issue_row_lds<BLOCK, NPT>(a.draft + (ob + lane_i(cd.row, 0)) * V, V, qlds);
     }
     constexpr int G = (64 * 64 + BLOCK - 1) / BLOCK;
     float g[G];
+    if (!shared) {
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const int f = r * BLOCK + tid;
-      const int k = f / 64, i = f & 63;
-      g[r] = 0.f;
-      if (tid < BLOCK && k <= i && i < nk) {
-        const int t = sh.tok[sh.kids[i]];
-        if (t >= 0 && t < V) g[r] = a.draft[(ob + sh.kids[k]) * V + t];
+      for (int r = 0; r < G; ++r) {
+        const int f = r * BLOCK + tid;
+        const int k = f / 64, i = f & 63;
+        g[r] = 0.f;
+        if (k <= i && i < nk) {
+          const int t = sh.tok[sh.kids[i]];
+          if (t >= 0 && t < V) g[r] = a.draft[(ob + sh.row[sh.kids[k]]) * V + t];
+        }
       }
     }
     float lt = 0.f;
     if (cd.tok >= 0) lt = a.logits[(ob + node) * V + cd.tok];
     target_stats<BLOCK, NPT, false>(
-        U, a.T, b, flags, C, sum_buf,
-        [&](int, float m, bool unit, float invT) {
+        U, a.T, b, flags, C,
+        [&](float m, bool unit, float invT) {
+          if (!shared) {
 #pragma unroll
-          for (int r = 0; r < G; ++r) {
-            const int f = r * BLOCK + tid;
-            const int k = f / 64, i = f & 63;
-            if (tid < BLOCK && k <= i && i < nk) sh.qt[tri(k, i, nk)] = g[r];
+            for (int r = 0; r < G; ++r) {
+              const int f = r * BLOCK + tid;
+              const int k = f / 64, i = f & 63;
+              if (k <= i && i < nk) sh.qt[tri(k, i)] = g[r];
+            }
           }
-          if (lane < nk) val = target_entry(lt, m, unit, invT);  // (split rows: redone below)
+          if (lane < nk) val = target_entry(lt, m, unit, invT);
         },
-        grp, sh, rb);
-    if (RP && grp.P > 1 && lane < nk && cd.tok >= 0) {
-      // split rows: the entry as the part that holds the token computed it,
-      // from that part's maximum and scale
-      const int slice = (((V >> 2) + grp.P - 1) / grp.P) * 4;
-      const int pt = cd.tok / slice;
-      val = target_entry(lt, sh.mp[pt], a.T == 1.f, 1.f / a.T) * sh.fp[pt];
-    }
+        sh, rb);
     // the table is published by the mass reduction's barrier
-    if (lane < nk) cd.q = sh.qt[tri(lane, lane, nk)];
-    if (RP && prefetch_wave<BLOCK>()) {
-      // the prefetch wave: the next candidates' slices into L2, so that each
-      // step's one-row-ahead register prefetch finds them there; issued once
-      // this wave's own loads are consumed (a wave's transfers complete in
-      // order), and kept kL2Ahead rows ahead by the chain steps
-      for (int c = 1; c <= kL2Ahead && c < nk; ++c)
-        l2_touch_slice(a.draft + (ob + lane_i(cd.kid, c)) * V + grp.base, grp.len, sh.l2sink);
-    }
+    if (!shared && lane < nk) cd.q = sh.qt[tri(lane, lane)];
+    cd.ut = val;
     ut = lane_f(val, 0);
     return 0;
   }
@@ -897,17 +678,12 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
 // thread then owns NPT consecutive groups, each wave 64 threads of them: the
 // wave totals locate the wave, a lane scan the thread, its groups the group
 // and the group's owner the id.
-// With `given`, the row is one slice of a split row: the search starts at
-// mass `start` and stops at threshold `thr_given` instead of u * sum.
 template <int BLOCK, int NPT>
 __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V,
-                                           Shared<BLOCK, NPT>& sh, double* part, int& rb,
-                                           bool given = false, double start = 0.0,
-                                           double thr_given = 0.0) {
+                                           Shared<BLOCK, NPT>& sh, double* part, int& rb) {
   constexpr int NW = BLOCK / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool row = tid < BLOCK;  // not an extra wave of a split workgroup (no mass)
-  if (row) {
+  {
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
       part[k * BLOCK + tid] =
@@ -916,22 +692,22 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   barrier_lds();
   double e[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) e[i] = row ? part[tid * NPT + i] : 0.0;
+  for (int i = 0; i < NPT; ++i) e[i] = part[tid * NPT + i];
   double own = 0.0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i) own += e[i];
   const double wt = wave_allsum(own);
   const int wbuf = rb;
   rb ^= 1;
-  if (lane == 0 && row) sh.rd[wbuf][wave] = wt;
+  if (lane == 0) sh.rd[wbuf][wave] = wt;
   if (tid == 0) sh.pick = -1;
   barrier_lds();
   double Z = 0.0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) Z += sh.rd[wbuf][i];
-  const double thr = given ? thr_given : (double)u * Z;
+  const double thr = (double)u * Z;
   int ws = NW - 1;  // rounding may leave no crossing: then the last wave
-  double before_w = start, run = start;
+  double before_w = 0.0, run = 0.0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const double nx = run + sh.rd[wbuf][i];
@@ -1004,7 +780,7 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int idx = (k * BLOCK + tid) * 4 + c;
-        if (row && idx < V && comp(U.v[k], c) > 0.f) last = idx;
+        if (idx < V && comp(U.v[k], c) > 0.f) last = idx;
       }
     pick = block_max_i<BLOCK, NPT>(last, sh, rb);
     if (pick < 0) pick = 0;
@@ -1012,25 +788,6 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   return pick;
 }
 
-// Final draw over a split row.  The exchange that produced the row's mass
-// left every part's mass of it in sh.pm, identical in every part, so each
-// part knows the mass before its slice and the total without another
-// exchange; the one part whose slice holds u * total searches its slice.
-// Returns the drawn id in the owning part, -1 in the others.
-template <int BLOCK, int NPT>
-__device__ __forceinline__ int split_draw(const Row<BLOCK, NPT>& U, float u, Grp& g,
-                                          Shared<BLOCK, NPT>& sh, double* part, int& rb) {
-  double tot = 0.0, lo = 0.0;
-  for (int p = 0; p < g.P; ++p) {  // fixed order: the same sums in every part
-    if (p == g.part) lo = tot;
-    tot += sh.pm[p];
-  }
-  const double thr = (double)u * tot;
-  const bool own = lo <= thr && (thr < lo + sh.pm[g.part] || g.part == g.P - 1);
-  if (!own) return -1;
-  const int pick = inverse_cdf<BLOCK, NPT>(U, u, g.len, sh, part, rb, true, lo, thr);
-  return g.base + pick;
-}
 
 // KV compaction fused into the walk (the effect of eagle_kv_compact with this
 // call's kv_src_slots and accept_len): the K/V of path node path[j] move from
@@ -1081,72 +838,115 @@ __device__ inline void fused_compact(const VerifyCompact& kc, int b, int N, int 
   }
 }
 
-// BLOCK row threads; split rows add an exchange wave and a prefetch wave.
-template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC, bool SPLIT>
-__global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kernel(VArgs a) {
-  static_assert(!SPLIT || (!GREEDY && !PARITY && VEC), "split rows: sampling path only");
-  __shared__ Shared<BLOCK, NPT> sh;
-  __shared__ float4 qlds[GREEDY ? 1 : NPT * BLOCK];  // draft-row prefetch
-  const int N = a.N, V = a.V;
-  const int tid = threadIdx.x;
-  // Workgroup -> (node, part).  Split rows: workgroup i runs on XCD i % 8, and
-  // the P parts of a node take slots with the same i % 8 (one L2 for their
-  // exchange words); slots past the last node exit at once.
-  int node = blockIdx.x, part = 0;
-  if constexpr (SPLIT) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    part = slot % a.P;
-    node = (slot / a.P) * 8 + xcd;
-    if (node >= a.nodes) return;
-  }
-  const int b = node / N;
-  const int j = node - b * N;
+// Per-sequence set-up shared by the kernels, in two halves so that the
+// tree's few loads can be issued ahead of a row's: fetch_tree reads the tree
+// (parent links, tokens, uniforms, draft rows of sequence b, threads < N)
+// into registers; store_tree sanitises it into LDS and reports data errors
+// (bad token, draft row out of range).
+struct TreeRegs {
+  int par, tok, row, L;
+  float u;
+};
+
+__device__ __forceinline__ TreeRegs fetch_tree(const VArgs& a, int b) {
+  const int tid = threadIdx.x, N = a.N;
   const size_t ob = (size_t)b * N;
-  int rb = 0;
-  Grp grp{nullptr, 1, 0, 0, 0, V, a.flags, b, 0};
-  if constexpr (SPLIT) {
-    const int s4 = ((V >> 2) + a.P - 1) / a.P;  // float4 per part
-    grp.words = a.xwords + (size_t)node * kXPhases * kXWords;
-    grp.P = a.P;
-    grp.part = part;
-    grp.base = part * s4 * 4;
-    grp.len = min(V - grp.base, s4 * 4);
-    grp.xt = BLOCK;
-    if (tid == 0) sh.xabort = 0;
-  }
-
-  // the node's logit row (this part's slice) first: its latency overlaps the
-  // tree set-up
-  Row<BLOCK, NPT> U;
-  load_logits<BLOCK, NPT>(U, a.logits + (ob + j) * V + grp.base, grp.len);
-
-  // tree, tokens, uniforms; the committed length too (only the walk needs it,
-  // and it would be a round trip of its own there)
-  bool tok_bad = false;
-  int Lkv = 0;
+  TreeRegs t{-1, 0, 0, 0, 0.f};
   if (tid < N) {
-    Lkv = a.kv_len[b];
-    if (tid == 0) sh.Lkv = Lkv;
-    int par = a.parents[ob + tid];
+    t.par = a.parents[ob + tid];
+    t.tok = a.tokens[ob + tid];
+    t.u = a.uniforms[ob + tid];
+    t.row = a.draft_row ? a.draft_row[ob + tid] : tid;
+    if (tid == 0) t.L = a.kv_len[b];
+  }
+  return t;
+}
+
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void store_tree(const VArgs& a, int b, const TreeRegs& t, bool flag_here,
+                                           Shared<BLOCK, NPT>& sh) {
+  const int tid = threadIdx.x, N = a.N, V = a.V;
+  bool tok_bad = false, row_bad = false;
+  if (tid < N) {
+    if (tid == 0) sh.Lkv = t.L;
+    int par = t.par;
     if (tid == 0)
       par = -1;
     else if (par != -1 && (par < 0 || par >= tid))
       par = 0;  // a bad link hangs off the root; -1 (absent node) is nobody's child
-    const int tk = a.tokens[ob + tid];
+    const bool present = tid > 0 && par != -1;
+    tok_bad = present && (t.tok < 0 || t.tok >= V);
+    row_bad = present && (t.row < 0 || t.row >= N);
     sh.par[tid] = par;
-    sh.tok[tid] = tk;
-    sh.u[tid] = a.uniforms[ob + tid];
-    tok_bad = tid > 0 && par != -1 && (tk < 0 || tk >= V);
+    sh.tok[tid] = t.tok;
+    sh.u[tid] = t.u;
+    sh.row[tid] = t.row >= 0 && t.row < N ? t.row : tid;  // in range whatever the input
   }
-  if (j == 0 && part == 0 && __ballot(tok_bad) && (tid & 63) == 0 && a.flags)
-    atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
+  if (tid < 64) {  // N <= 64: the whole tree sits in wave 0
+    const uint64_t tb = __ballot(tok_bad), rbm = __ballot(row_bad);
+    if (flag_here && tid == 0 && a.flags) {
+      if (tb) atomicOr(a.flags + b, EAGLE_FLAG_BAD_TOKEN);
+      if (rbm && a.draft_row && a.T > 0.f) atomicOr(a.flags + b, EAGLE_FLAG_BAD_ROW);
+    }
+  }
+}
+
+// The walk's outputs for sequence b once sh.path[0..m] and the final token
+// are known: path, KV source slots, accepted tokens, accept length, final
+// token, then the compaction when fused.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void write_walk(const VArgs& a, int b, int m_acc, int pick,
+                                           Shared<BLOCK, NPT>& sh) {
+  const int tid = threadIdx.x, N = a.N;
+  const size_t ob = (size_t)b * N;
+  const int Lkv = sh.Lkv;
+  if (tid < N) {
+    const size_t o = ob + tid;
+    const bool on = tid <= m_acc;
+    const int pn = on ? sh.path[tid] : -1;
+    a.path[o] = pn;
+    a.kv_src[o] = on ? Lkv + pn : -1;
+    a.acc_tokens[o] = tid < m_acc ? sh.tok[sh.path[tid + 1]] : -1;
+  }
+  if (tid == 0) {
+    a.accept_len[b] = m_acc;
+    a.bonus[b] = pick;
+  }
+  if (a.kc.k) fused_compact(a.kc, b, N, m_acc, a.flags, sh);
+}
+
+template <int BLOCK, int NPT, bool GREEDY, bool PARITY, bool VEC>
+__global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
+  __shared__ Shared<BLOCK, NPT> sh;
+  __shared__ float4 qlds[GREEDY ? 1 : NPT * BLOCK];  // draft-row prefetch / final-draw scratch
+  const int N = a.N, V = a.V;
+  const int tid = threadIdx.x;
+  const int node = blockIdx.x;
+  const int b = node / N;
+  const int j = node - b * N;
+  const size_t ob = (size_t)b * N;
+  int rb = 0;
+
+  // the tree's few loads first, then the node's logit row (vector loads
+  // complete in order: the tree is not held up behind the row), and, when the
+  // batch is small enough to be latency-bound, the draft row the node's
+  // children most likely share (its own, when siblings name their parent's
+  // row) before the children are known
+  const TreeRegs tr = fetch_tree(a, b);
+  asm volatile("" ::: "memory");
+  Row<BLOCK, NPT> U;
+  load_row<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
+  Row<BLOCK, NPT> Q;  // the shared draft row, or the second row of the step-by-step chain
+  const bool q_guess = !GREEDY && a.guess_row;
+  if (q_guess) load_row<BLOCK, NPT>(Q, a.draft + (ob + j) * V, V, 0.f);
+  store_tree<BLOCK, NPT>(a, b, tr, j == 0, sh);
   barrier_lds();
   double C = 1.0;
   float ut = 0.f, val = 0.f;
-  Cand cd{0, -1, 0.f, 0.f};
-  float4 qn[NPT];  // split rows: draft-row prefetch registers
-  const int am = node_setup<BLOCK, NPT, GREEDY, VEC, SPLIT>(a, ob, j, b, a.flags, U, C, ut, val, cd,
-                                                             qn, grp, sh, qlds, rb);
+  Cand cd{0, -1, 0, 0.f, 0.f, 0.f};
+  bool shared;
+  const int am = node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, Q, q_guess, C, ut, val,
+                                                     cd, shared, sh, qlds, rb);
   const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
@@ -1173,13 +973,17 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
       }
     }
   } else {
-    const int si = run_chain<BLOCK, NPT, VEC, SPLIT, PARITY>(a, ob, U, C, ut, val, cd, qn, nk, true,
-                                                             grp, sh, qlds, rb);
+    int si;
+    if (shared) {
+      double S = 0.0;
+      si = run_chain_shared<BLOCK, NPT, PARITY>(U, Q, S, C, cd, nk, true, sh, rb);
+      if (si < 0) residual_row<BLOCK, NPT>(U, Q, S, U);  // the row the final token comes from
+    } else {
+      si = run_chain<BLOCK, NPT, VEC, PARITY>(a, ob, U, Q, C, ut, val, cd, nk, true, sh, qlds, rb);
+    }
     if (si >= 0) {
       acc = sh.kids[si];
       ntested = si + 1;
-    } else if constexpr (SPLIT) {
-      bonus = split_draw<BLOCK, NPT>(U, sh.u[0], grp, sh, reinterpret_cast<double*>(qlds), rb);
     } else {
       bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh, reinterpret_cast<double*>(qlds), rb);
     }
@@ -1188,38 +992,31 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
   if (!GREEDY && VEC) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // publish this node's outcome (split rows: part 0, and the part that drew
-  // the final token); the last workgroup of the sequence walks the tree
+  // publish this node's outcome; the last workgroup of the sequence walks the tree
   if (tid == 0) {
-    if (part == 0) {
-      st_c(a.nr.acc + ob + j, acc);
-      st_c(a.nr.ntested + ob + j, ntested);
-    }
-    if (!SPLIT || (acc >= 0 ? part == 0 : bonus >= 0)) st_c(a.nr.bonus + ob + j, bonus);
-    if (SPLIT)
-      __hip_atomic_fetch_max(a.nr.nphase + ob + j, grp.phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_c(a.nr.acc + ob + j, acc);
+    st_c(a.nr.ntested + ob + j, ntested);
+    st_c(a.nr.bonus + ob + j, bonus);
   }
   if (PARITY && tid < ntested) st_c(a.nr.ratio + ob + sh.kids[tid], sh.ratio[tid]);  // read by out_ratio only
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     const int ticket = __hip_atomic_fetch_add(a.nr.counter + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.last = ticket == N * grp.P - 1;
+    sh.last = ticket == N - 1;
   }
   __syncthreads();
   if (!sh.last) return;
 
   // ---- walk (last workgroup of sequence b) -----------------------------------
   if (tid < N) {
-    // all four loads in flight before any result is used
+    // all three loads in flight before any result is used
     const int r0 = ld_c(a.nr.acc + ob + tid);
     const int r1 = ld_c(a.nr.bonus + ob + tid);
     const int r2 = ld_c(a.nr.ntested + ob + tid);
-    const int r3 = SPLIT ? ld_c(a.nr.nphase + ob + tid) : 0;
     sh.wacc[tid] = r0;
     sh.wbonus[tid] = r1;
     sh.wnt[tid] = r2;
-    if (SPLIT) sh.wph[tid] = min(r3, kXPhases);
   }
   __syncthreads();
   if (tid == 0) {
@@ -1232,43 +1029,13 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
       cur = nx;
     }
     sh.term = cur;
-    // in range even if a timed-out exchange left the slot unwritten
     sh.pick = min(max(sh.wbonus[cur], 0), V - 1);
     sh.nk = m_acc;
     __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if constexpr (SPLIT) {
-    // every workgroup of the sequence is past its last exchange: zero the
-    // words its nodes used, and the phase counts, for the next call.  Wide
-    // streaming stores (a store instruction is slow to issue, so few and
-    // wide ones); the kernel's end makes them visible to the next call,
-    // whose exchanges read the words only with device-coherent atomics.
-    // Each wave takes whole nodes, so a lane issues only the stores of the
-    // nodes of its wave.
-    static_assert(kXWords % 2 == 0, "16-byte stores");
-    const int nwaves = (int)blockDim.x >> 6, wave = tid >> 6, lane = tid & 63;
-    for (int n = wave; n < N; n += nwaves) {
-      u32x4* w = reinterpret_cast<u32x4*>(a.xwords + (ob + n) * kXPhases * kXWords);
-      for (int i = lane; i < sh.wph[n] * (kXWords / 2); i += 64)
-        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, w + i);
-    }
-    if (tid < N) st_c(a.nr.nphase + ob + tid, 0);
-  }
   __syncthreads();
   const int m_acc = sh.nk;
-  if (tid < N) {
-    const size_t o = ob + tid;
-    const bool on = tid <= m_acc;
-    const int pn = on ? sh.path[tid] : -1;
-    a.path[o] = pn;
-    a.kv_src[o] = on ? Lkv + pn : -1;
-    a.acc_tokens[o] = tid < m_acc ? sh.tok[sh.path[tid + 1]] : -1;
-  }
-  if (tid == 0) {
-    a.accept_len[b] = m_acc;
-    a.bonus[b] = sh.pick;
-  }
-  if (a.kc.k) fused_compact(a.kc, b, N, m_acc, a.flags, sh);
+  write_walk<BLOCK, NPT>(a, b, m_acc, sh.pick, sh);
   if (PARITY && a.out_ratio) {
     // tested nodes: the candidates each path node's chain tested
     if (tid < N) {
@@ -1296,12 +1063,16 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
     if constexpr (GREEDY) {
       for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
     } else {
-      Grp whole{nullptr, 1, 0, 0, 0, V, nullptr, b, 0};
-      load_logits<BLOCK, NPT>(U, a.logits + (ob + term) * V, V);
-      node_setup<BLOCK, NPT, false, VEC, false>(a, ob, term, b, nullptr, U, C, ut, val, cd, qn, whole,
-                                                sh, qlds, rb);
-      run_chain<BLOCK, NPT, VEC, false, false>(a, ob, U, C, ut, val, cd, qn, sh.nk, false, whole, sh,
-                                               qlds, rb);
+      load_row<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
+      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, Q, false, C, ut, val, cd, shared,
+                                         sh, qlds, rb);
+      if (shared) {
+        double S = 0.0;
+        run_chain_shared<BLOCK, NPT, false>(U, Q, S, C, cd, sh.nk, false, sh, rb);
+        residual_row<BLOCK, NPT>(U, Q, S, U);
+      } else {
+        run_chain<BLOCK, NPT, VEC, false>(a, ob, U, Q, C, ut, val, cd, sh.nk, false, sh, qlds, rb);
+      }
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
 #pragma unroll
@@ -1313,47 +1084,166 @@ __global__ __launch_bounds__(SPLIT ? BLOCK + 128 : BLOCK) void verify_node_kerne
   }
 }
 
+// ---- temperature 0: the argmax over a split row ---------------------------------
+// At T = 0 a node's outcome is fixed by its row's argmax.  Each of the node's
+// P workgroups takes a slice of the row, finds the slice's maximum and its
+// lowest index, and posts them as one 64-bit key (order-preserving value bits
+// above the inverted index) with an atomic maximum, so the word ends up with
+// the row's maximum and its lowest index whatever the order of arrival.  No
+// workgroup waits for another: every workgroup then takes the sequence's
+// ticket, and the one that draws the last (of N * P) walks, reading the words
+// and zeroing them and the ticket for the next call.  Every workgroup fetches
+// the sequence's tree at its start (a few bytes), so the walker has it.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+
+template <int NPT>
+__global__ __launch_bounds__(256) void verify_argmax_kernel(VArgs a) {
+  constexpr int BLOCK = 256, NW = BLOCK / 64;
+  __shared__ Shared<BLOCK, NPT> sh;
+  __shared__ uint32_t wkey[NW], widx[NW];
+  const int N = a.N, V = a.V, P = a.P;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int node = blockIdx.x / P, part = blockIdx.x - node * P;
+  const int b = node / N;
+  const int j = node - b * N;
+  const size_t ob = (size_t)b * N;
+  const int s4 = ((V + 3) / 4 + P - 1) / P;  // float4 per part (the host keeps every slice non-empty)
+  const int base = part * s4 * 4;
+  const int len = min(V - base, s4 * 4);
+  const TreeRegs tr = fetch_tree(a, b);
+  asm volatile("" ::: "memory");
+  Row<BLOCK, NPT> U;
+  load_row<BLOCK, NPT>(U, a.logits + (ob + j) * V + base, len, -FLT_MAX);
+  sanitize_logits<BLOCK, NPT>(U, b, a.flags);
+  // the slice's maximum and its lowest index: per thread (ids increase with
+  // (k, e)), per wave (maximum key, then the lowest index holding it), then
+  // across the waves in one barrier
+  float lm = -INFINITY;
+  int li = INT_MAX;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = comp(U.v[k], e);
+      const bool gt = x > lm;
+      lm = gt ? x : lm;
+      li = gt ? (k * BLOCK + tid) * 4 + e : li;
+    }
+  const int sk = (int)(order_key(lm) ^ 0x80000000u);  // order-preserving as a signed int
+  const int wk = wave_allmax_i(sk);
+  const int wi = wave_allmin_i(sk == wk ? li : INT_MAX);
+  if (lane == 0) {
+    wkey[wave] = (uint32_t)wk;
+    widx[wave] = (uint32_t)wi;
+  }
+  barrier_lds();
+  if (tid == 0) {
+    int bk = (int)wkey[0], bi = (int)widx[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const int k = (int)wkey[w], i = (int)widx[w];
+      if (k > bk || (k == bk && i < bi)) {
+        bk = k;
+        bi = i;
+      }
+    }
+    const uint64_t key = ((uint64_t)((uint32_t)bk ^ 0x80000000u) << 32) |
+                         (uint64_t)(0xffffffffu - (uint32_t)(base + bi));
+    __hip_atomic_fetch_max(a.nr.amax + node, (unsigned long long)key, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the maximum is in before the ticket
+    const int ts = __hip_atomic_fetch_add(a.nr.counter + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = ts == N * P - 1;
+    if (last) __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.last = last;
+  }
+  barrier_lds();
+  if (!sh.last) return;
+
+  // ---- walk (last workgroup of sequence b) -----------------------------------
+  store_tree<BLOCK, NPT>(a, b, tr, true, sh);
+  if (tid < N) {
+    unsigned long long* w = a.nr.amax + ob + tid;
+    const unsigned long long k = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.wbonus[tid] = (int)(0xffffffffu - (uint32_t)(k & 0xffffffffull));  // the node's argmax
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int cur = 0, m_acc = 0;
+    sh.path[0] = 0;
+    for (;;) {
+      const int am_cur = sh.wbonus[cur];
+      int nx = -1;
+      for (int c = cur + 1; c < N && nx < 0; ++c)
+        if (sh.par[c] == cur && sh.tok[c] == am_cur) nx = c;
+      if (nx < 0) break;
+      sh.path[++m_acc] = nx;
+      cur = nx;
+    }
+    sh.pick = min(max(sh.wbonus[cur], 0), V - 1);
+    sh.nk = m_acc;
+  }
+  __syncthreads();
+  write_walk<BLOCK, NPT>(a, b, sh.nk, sh.pick, sh);
+}
+
 // ---------------------------------------------------------------------------
-// Split rows pay off where a node's chain is long per workgroup: large
-// vocabularies with few nodes, so that all B * N * P workgroups are resident
-// at once (one per CU at most), which the exchange waits rely on.
-static int verify_parts(int B, int N, int V) {
-  const size_t nodes = (size_t)B * N;
-  if ((V & 3) != 0 || V <= 28672 || V > 32768) return 1;
-  if (nodes * kMaxParts > (size_t)kNumCUs) return 1;
-  return kMaxParts;
+// T = 0 without parity outputs may split each row over P workgroups of 256
+// threads (at most 8 float4 per thread).  Splitting pays only while the batch
+// leaves most of the chip idle: the P slices of a row meet on one counter and
+// one packed max, so about 128 workgroups in all is the target, and a batch
+// with more nodes than that (or one that would need fewer slices than the
+// row's minimum) reads each row in one 512-thread workgroup instead.
+static int argmax_parts(int B, int N, int V) {
+  if (V <= 4096) return 1;
+  const long long nodes = (long long)B * N;
+  const int v4 = (V + 3) / 4;
+  const int min_parts = (v4 + 8 * 256 - 1) / (8 * 256);
+  const long long want = 128 / std::max<long long>(nodes, 1);
+  if (want < 2 || want < min_parts) return 1;
+  int P = (int)std::min<long long>(want, 16);
+  while (P > 1 && (long long)(P - 1) * ((v4 + P - 1) / P) >= v4) --P;  // no empty slice
+  return P < min_parts ? 1 : P;
+}
+
+static int argmax_npt(int V, int P) {
+  const int per = (((V + 3) / 4 + P - 1) / P + 255) / 256;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
 }
 
 VerifyPlan plan_verify(int B, int N, int V) {
   VerifyPlan p{};
   p.V = V;
-  p.parts = verify_parts(B, N, V);
-  p.walk_threads = p.parts > 1 ? 256 : V > 4096 ? 1024 : 256;
+  p.parts = argmax_parts(B, N, V);
   const size_t nodes = (size_t)B * N;
-  p.ws_stats = nodes * 20;  // acc, bonus, ratio, ntested, nphase
   p.ws_counters = (size_t)B * 4;
-  p.ws_partials = p.parts > 1 ? nodes * kXPhases * kXWords * 8 : 0;  // exchange words
-  p.chunks = 1;
+  p.ws_amax = nodes * 8;
+  p.ws_stats = nodes * 16;  // acc, bonus, ratio, ntested
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t verify_workspace_bytes(const VerifyPlan& p) {
-  return align256(p.ws_counters) + align256(p.ws_stats) + align256(p.ws_partials);
+  return align256(p.ws_counters) + align256(p.ws_amax) + align256(p.ws_stats);
 }
 
 hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const float* draft,
-                         const float* logits, const int32_t* parents, const int32_t* kv_len,
-                         int B, int N, float T, const float* uniforms, int32_t* accept_len,
-                         int32_t* path, int32_t* acc_tokens, int32_t* bonus, int32_t* kv_src,
-                         float* out_probs, float* out_final, float* out_ratio, void* ws,
-                         int32_t* flags, const VerifyCompact& kc, hipStream_t s) {
+                         const int32_t* draft_row, const float* logits, const int32_t* parents,
+                         const int32_t* kv_len, int B, int N, float T, const float* uniforms,
+                         int32_t* accept_len, int32_t* path, int32_t* acc_tokens, int32_t* bonus,
+                         int32_t* kv_src, float* out_probs, float* out_final, float* out_ratio,
+                         void* ws, int32_t* flags, const VerifyCompact& kc, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t nodes = (size_t)B * N;
   VArgs a{};
   a.tokens = tokens;
   a.draft = draft;
+  a.draft_row = draft_row;
   a.logits = logits;
   a.parents = parents;
   a.kv_len = kv_len;
@@ -1368,42 +1258,50 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   a.out_ratio = out_ratio;
   a.flags = flags;
   a.kc = kc;
-  a.nr.counter = reinterpret_cast<int32_t*>(w);
-  uint8_t* nb = w + align256(plan.ws_counters);
-  a.nr.acc = reinterpret_cast<int32_t*>(nb);
-  a.nr.bonus = reinterpret_cast<int32_t*>(nb + nodes * 4);
-  a.nr.ratio = reinterpret_cast<float*>(nb + nodes * 8);
-  a.nr.ntested = reinterpret_cast<int32_t*>(nb + nodes * 12);
-  a.nr.nphase = reinterpret_cast<int32_t*>(nb + nodes * 16);
-  a.xwords = reinterpret_cast<unsigned long long*>(nb + align256(plan.ws_stats));
+  size_t off = 0;
+  a.nr.counter = reinterpret_cast<int32_t*>(w + off);
+  off += align256(plan.ws_counters);
+  a.nr.amax = reinterpret_cast<unsigned long long*>(w + off);
+  off += align256(plan.ws_amax);
+  a.nr.acc = reinterpret_cast<int32_t*>(w + off);
+  a.nr.bonus = reinterpret_cast<int32_t*>(w + off + nodes * 4);
+  a.nr.ratio = reinterpret_cast<float*>(w + off + nodes * 8);
+  a.nr.ntested = reinterpret_cast<int32_t*>(w + off + nodes * 12);
   a.N = N;
   a.V = plan.V;
   a.nodes = (int)nodes;
-  a.P = 1;
+  a.P = plan.parts;
+  // a small batch is latency-bound: fetching a row that turns out unused
+  // (a leaf's) costs bandwidth, not time
+  a.guess_row = draft_row != nullptr && nodes <= (size_t)kNumCUs ? 1 : 0;
   a.T = T;
   const unsigned grid = (unsigned)nodes;
   const bool greedy = T == 0.f;
   const bool parity = out_probs || out_final || out_ratio;
   const bool vec = (plan.V & 3) == 0;
-  if (plan.parts > 1 && !greedy && !parity && vec) {
-    // node slots rounded up to a multiple of the 8 XCDs, P parts each
-    a.P = plan.parts;
-    const unsigned sgrid = (unsigned)(((nodes + 7) / 8) * 8 * plan.parts);
-    verify_node_kernel<256, 4, false, false, true, true><<<sgrid, 256 + 128, 0, s>>>(a);
+  if (greedy && !parity && plan.parts > 1) {
+    const unsigned sgrid = (unsigned)(nodes * plan.parts);
+    switch (argmax_npt(plan.V, plan.parts)) {
+      case 1: verify_argmax_kernel<1><<<sgrid, 256, 0, s>>>(a); break;
+      case 2: verify_argmax_kernel<2><<<sgrid, 256, 0, s>>>(a); break;
+      case 4: verify_argmax_kernel<4><<<sgrid, 256, 0, s>>>(a); break;
+      default: verify_argmax_kernel<8><<<sgrid, 256, 0, s>>>(a); break;
+    }
     return hipGetLastError();
   }
 #define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                        \
   do {                                                                                      \
-    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true, false><<<grid, BLK, 0, s>>>(a);    \
-    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true, false><<<grid, BLK, 0, s>>>(a);        \
-    else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true, false><<<grid, BLK, 0, s>>>(a); \
-    else if (parity) verify_node_kernel<BLK, NPT, false, true, false, false><<<grid, BLK, 0, s>>>(a);       \
-    else if (vec) verify_node_kernel<BLK, NPT, false, false, true, false><<<grid, BLK, 0, s>>>(a);          \
-    else verify_node_kernel<BLK, NPT, false, false, false, false><<<grid, BLK, 0, s>>>(a);                  \
+    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true><<<grid, BLK, 0, s>>>(a);    \
+    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true><<<grid, BLK, 0, s>>>(a);        \
+    else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true><<<grid, BLK, 0, s>>>(a); \
+    else if (parity) verify_node_kernel<BLK, NPT, false, true, false><<<grid, BLK, 0, s>>>(a);       \
+    else if (vec) verify_node_kernel<BLK, NPT, false, false, true><<<grid, BLK, 0, s>>>(a);          \
+    else verify_node_kernel<BLK, NPT, false, false, false><<<grid, BLK, 0, s>>>(a);                  \
   } while (0)
-  // the row must fit one workgroup unless it is split
+  // the row must fit one workgroup: 512 threads of 16 float4 leave 256 VGPRs
+  // per thread for the two resident rows (1024 threads would leave 128)
   if (plan.V > 4096)
-    EAGLE_LAUNCH_VERIFY(1024, 8);
+    EAGLE_LAUNCH_VERIFY(512, 16);
   else
     EAGLE_LAUNCH_VERIFY(256, 4);
 #undef EAGLE_LAUNCH_VERIFY

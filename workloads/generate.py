@@ -14,6 +14,14 @@ Layouts (all C-contiguous):
   tokens         int32  [B, N]        tokens[b,0] is the root token (never tested)
   draft_probs    fp32   [B, N, V]     row i = distribution token i was drawn from;
                                       row 0 zero; None at T == 0
+  draft_rows     fp32   [B, N, V]     the same distributions stored once per
+                                      drafting node: row j = the draft
+                                      distribution after node j (zero for a node
+                                      with no children); None at T == 0
+  draft_row      int32  [B, N]        row of draft_rows node i was drawn from
+                                      (its parent; 0 for the root and absent
+                                      nodes), so draft_rows[b, draft_row[b, i]]
+                                      == draft_probs[b, i] for every drafted node
   target_logits  fp32   [B, N, V]     row i = target logits after node i
   uniforms       fp32   [B, N]        in [0, 1)
   kv_len         int32  [B]
@@ -71,6 +79,8 @@ class StepInputs:
     q: Optional[np.ndarray] = None
     k_cache: Optional[np.ndarray] = None
     v_cache: Optional[np.ndarray] = None
+    draft_rows: Optional[np.ndarray] = None
+    draft_row: Optional[np.ndarray] = None
 
     @property
     def Lmax(self) -> int:
@@ -234,12 +244,38 @@ def make_step(cfg: VerifyConfig, T: float, seed: Optional[int] = None, *,
     uniforms = r_uni.random((B, N), dtype=np.float32)
     step = StepInputs(cfg=cfg, T=T, seed=seed, parents=par, tokens=tokens, draft_probs=draft,
                       target_logits=target, uniforms=uniforms, kv_len=kv_len)
+    step.draft_rows, step.draft_row = rows_by_parent(par, draft)
     if with_attention:
         Lmax = int(kv_len.max()) + N
         step.q = _normal_bf16(r_qkv, (B, N, cfg.Hq, cfg.d), cfg.qkv_sigma)
         step.k_cache = _normal_bf16(r_qkv, (B, cfg.Hkv, Lmax, cfg.d), cfg.qkv_sigma)
         step.v_cache = _normal_bf16(r_qkv, (B, cfg.Hkv, Lmax, cfg.d), cfg.qkv_sigma)
     return step
+
+
+def rows_by_parent(parents: np.ndarray, draft_probs: Optional[np.ndarray]):
+    """The per-node draft rows regrouped as the drafter produces them: one
+    row per drafting node j (the distribution its children were drawn from),
+    and each node's index into those rows (its parent).  Children of one node
+    share their parent's row in draft_probs, so nothing is lost; a node whose
+    own row differs from its siblings' cannot be expressed (None is returned
+    for the rows then)."""
+    B, N = parents.shape
+    idx = np.where(parents >= 0, parents, 0).astype(np.int32)
+    idx[:, 0] = 0
+    if draft_probs is None:
+        return None, idx
+    rows = np.zeros_like(draft_probs)
+    for b in range(B):
+        for c in range(1, N):
+            j = parents[b, c]
+            if j < 0:
+                continue
+            if not rows[b, j].any():
+                rows[b, j] = draft_probs[b, c]
+            elif not np.array_equal(rows[b, j], draft_probs[b, c]):
+                return None, idx
+    return rows, idx
 
 
 def normal_bf16_device(shape, seed: int, device="cuda"):
