@@ -22,7 +22,9 @@ JSON line naming what it ran and does not time anything.  `--profile
 attn:<config>` / `--profile dtree` run the tree attention at another
 configuration, or the EAGLE-2 tree build, eagerly for a kernel trace.
 `--oracle-configs` times the CPU oracle per configuration and stage (no GPU
-work) and prints one JSON line.
+work) and prints one JSON line.  `--per-config` times the step, the attention
+and the verify launch at every configuration and listed temperature (and the
+7B layer with a close draft) and prints one JSON line of rows.
 """
 from __future__ import annotations
 
@@ -120,17 +122,18 @@ class Step:
                                  new_kv_len=self.new_len, workspace=self.ver_ws)
 
 
-def graph_of(torch, fn, count):
+def graph_of(torch, fn, count, start=0):
+    """`count` calls fn(start), fn(start + 1), ... captured in one graph."""
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fn(0)  # warm the allocator / kernels outside capture
+        fn(start)  # warm the allocator / kernels outside capture
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
         for i in range(count):
-            fn(i)
+            fn(start + i)
     torch.cuda.synchronize()
     return g
 
@@ -147,24 +150,30 @@ def time_graph(torch, g, reps=1):
     return e0.elapsed_time(e1) * 1e-3  # seconds
 
 
-def measure(torch, ev, W, T, steps, warmup):
-    cfg = W.get(WORKLOAD)
+def measure(torch, ev, W, T, steps, warmup, name=WORKLOAD, sigma_d=None, detail=True):
+    cfg = W.get(name)
+    if sigma_d is not None:
+        cfg = W.shrink(cfg, sigma_d=sigma_d)
     s = W.make_step(cfg, T)
     per_slot = cfg.attn_bytes() + 2 * cfg.vocab_bytes()
     copies = max(2, math.ceil(ROTATE_BYTES / per_slot))
     st = Step(s, torch, ev, copies)
-    log(f"[bench] T={T}: {copies} rotation slots of {per_slot / 1e6:.1f} MB")
-    g_warm = graph_of(torch, st.run, max(1, warmup))
-    g_step = graph_of(torch, st.run, steps)
+    log(f"[bench] {cfg.name} T={T} sigma_d={cfg.sigma_d}: {copies} rotation slots of "
+        f"{per_slot / 1e6:.1f} MB")
+    # the timed graph starts on the slot after the warm-up's last one, so its
+    # first inputs are not the ones the warm-up just left in the caches
+    warm = max(1, warmup)
+    g_warm = graph_of(torch, st.run, warm)
+    g_step = graph_of(torch, st.run, steps, start=warm)
     time_graph(torch, g_warm)
     t_step = time_graph(torch, g_step) / steps
     # spread: the mean step of a few more replays of the same graph, and the
     # p10 / p50 / p90 of the mean step over 20 replays of a 10-step graph
-    replays = sorted(time_graph(torch, g_step) / steps for _ in range(5))
+    replays = sorted(time_graph(torch, g_step) / steps for _ in range(5 if detail else 2))
     chunk = min(10, steps)
     g_chunk = graph_of(torch, st.run, chunk)
     time_graph(torch, g_chunk)
-    per = np.array([time_graph(torch, g_chunk) / chunk for _ in range(20)])
+    per = np.array([time_graph(torch, g_chunk) / chunk for _ in range(20 if detail else 5)])
     spread = {"p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
               "p90": float(np.percentile(per, 90))}
     acc = st.res["accept_len"].cpu().numpy()
@@ -199,14 +208,15 @@ def measure(torch, ev, W, T, steps, warmup):
                 alpha[int(depth[c])] = (t + 1, a_ + (c in on))
     # attention alone and the walk alone, same rotation, back-to-back launches
     # in one graph each
-    g_attn = graph_of(torch, st.attention, steps)
+    g_attn = graph_of(torch, st.attention, steps, start=warm)
     time_graph(torch, g_attn)
     t_attn = time_graph(torch, g_attn) / steps
-    g_ver = graph_of(torch, st.verify, steps)
+    g_ver = graph_of(torch, st.verify, steps, start=warm)
     time_graph(torch, g_ver)
     t_ver = time_graph(torch, g_ver) / steps
     walk_bytes = cfg.vocab_bytes() + 4 * cfg.V * rows_read
     return dict(cfg=cfg, t_step=t_step, t_attn=t_attn, t_verify=t_ver, accept_len=int(acc[0]),
+                accept_lens=[int(x) for x in acc],
                 replays=replays, spread=spread, alpha={d: {"tested": t, "accepted": a_} for d, (t, a_) in sorted(alpha.items())},
                 copies=copies, walk_bytes=walk_bytes, rejected=rejected, rows_read=rows_read)
 
@@ -453,6 +463,39 @@ def oracle_per_config(W, repeats=3):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def config_row(r, T, sigma_d=None):
+    """One configuration's timings and roofline fractions from measure()."""
+    cfg = r["cfg"]
+    attn_bytes = cfg.attn_bytes()
+    tokens = cfg.B * cfg.N
+    return {"config": cfg.name, "T": T, "sigma_d": cfg.sigma_d if sigma_d is None else sigma_d,
+            "batch": cfg.B, "tree_nodes": cfg.N, "step_us": r["t_step"] * 1e6,
+            "tokens_per_s": tokens / r["t_step"],
+            "attn_us": r["t_attn"] * 1e6, "attn_bytes": attn_bytes,
+            "attn_frac": attn_bytes / r["t_attn"] / 1e9 / HBM_PEAK_GBS,
+            "verify_us": r["t_verify"] * 1e6, "verify_bytes": r["walk_bytes"],
+            "verify_frac": r["walk_bytes"] / r["t_verify"] / 1e9 / HBM_PEAK_GBS,
+            "step_frac": (attn_bytes + r["walk_bytes"]) / r["t_step"] / 1e9 / HBM_PEAK_GBS,
+            "rejected_candidates": r["rejected"], "accept_len": r["accept_lens"][:16],
+            "step_p50_us": r["spread"]["p50"] * 1e6}
+
+
+def per_config(torch, ev, W, steps, warmup):
+    """Every configuration at each of its listed temperatures, plus the
+    LLaMA2-7B layer with a close draft (noise sigma 0.05, so the walk
+    descends): step, attention and verify timed as in the headline."""
+    rows = []
+    runs = [(c.name, T, None) for c in W.CONFIGS for T in c.temperatures]
+    runs.append((WORKLOAD, 1.0, 0.05))
+    for name, T, sig in runs:
+        r = measure(torch, ev, W, T, steps, warmup, name=name, sigma_d=sig, detail=False)
+        rows.append(config_row(r, T, sig))
+        log(f"[bench] {json.dumps(rows[-1])}")
+        del r
+        torch.cuda.empty_cache()
+    return {"per_config": rows, "steps": steps, "warmup": warmup, "hbm_peak_GBs": HBM_PEAK_GBS}
+
+
 def pmc_traffic(attn_bytes):
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -477,6 +520,9 @@ def main():
                     help="time the CPU oracle per configuration and stage, print one JSON line")
     ap.add_argument("--profile", default=None,
                     help="attn:<config> or dtree: eager launches for a rocprofv3 trace")
+    ap.add_argument("--per-config", action="store_true",
+                    help="time the step, attention and verify per configuration and listed "
+                         "temperature, print one JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification step is built and timed "
@@ -503,8 +549,13 @@ def main():
     if args.profile:
         profile_run(torch, ev, W, args.profile, args.steps)
         return
+    if args.per_config:
+        print(json.dumps(per_config(torch, ev, W, min(args.steps, 50), min(args.warmup, 10))),
+              flush=True)
+        return
     r1 = measure(torch, ev, W, 1.0, args.steps, args.warmup)
     r0 = measure(torch, ev, W, 0.0, args.steps, args.warmup)
+    rd = measure(torch, ev, W, 1.0, args.steps, args.warmup, sigma_d=0.05, detail=False)
     cfg = r1["cfg"]
     tokens = cfg.B * cfg.N
     attn_bytes = cfg.attn_bytes()
@@ -551,6 +602,7 @@ def main():
                "attn_us": r0["t_attn"] * 1e6, "verify_us": r0["t_verify"] * 1e6,
                "accept_len": r0["accept_len"]},
         "accept_len_t1": r1["accept_len"],
+        "t1_close_draft": config_row(rd, 1.0, 0.05),
         "ms_per_step_replays": [t * 1e3 for t in r1["replays"]],
         "ms_per_step_p10_p50_p90": {k: v * 1e3 for k, v in r1["spread"].items()},
         "accepted_tokens_per_s": {"t1": cfg.B * (r1["accept_len"] + 1) / r1["t_step"],

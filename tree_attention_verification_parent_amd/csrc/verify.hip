@@ -192,6 +192,13 @@ __device__ __forceinline__ int block_max_i(int v, Shared<BLOCK, NPT>& sh, int& r
   return t;
 }
 
+// max(0, x) for the entries of an adjusted row.  Such an entry is the target
+// entry (at most 1: the row is exp((l - max) / T)) less a non-negative
+// multiple of a probability, so it never exceeds 1 and clamping to [0, 1]
+// gives the same value; the clamp folds into the FMA that produces x as its
+// output modifier, saving the separate max.
+__device__ __forceinline__ float pos01(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 1.f); }
+
 // ---- rows --------------------------------------------------------------------
 // A vocabulary row across the workgroup: thread t owns elements
 // (k * BLOCK + t) * 4 + e, k < NPT, e < 4 ("slab" k, coalesced float4 loads).
@@ -452,13 +459,13 @@ __device__ __forceinline__ bool chain_step(const VArgs& a, size_t ob, const Row<
     else
       q = nxt.v[k];
     float4& w = nxt.v[k];
-    w.x = fmaxf(0.f, fmaf(-cf, q.x, cur.v[k].x));
-    w.y = fmaxf(0.f, fmaf(-cf, q.y, cur.v[k].y));
-    w.z = fmaxf(0.f, fmaf(-cf, q.z, cur.v[k].z));
-    w.w = fmaxf(0.f, fmaf(-cf, q.w, cur.v[k].w));
+    w.x = pos01(fmaf(-cf, q.x, cur.v[k].x));
+    w.y = pos01(fmaf(-cf, q.y, cur.v[k].y));
+    w.z = pos01(fmaf(-cf, q.z, cur.v[k].z));
+    w.w = pos01(fmaf(-cf, q.w, cur.v[k].w));
     ps[k] = sum4(w);
   }
-  const float vnew = fmaxf(0.f, fmaf(-cf, q_lane, val));
+  const float vnew = pos01(fmaf(-cf, q_lane, val));
   if constexpr (VEC) {
     if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of q_s done
@@ -510,7 +517,11 @@ __device__ __forceinline__ int run_chain(const VArgs& a, size_t ob, Row<BLOCK, N
 // candidate's entry come from the same two FMAs, so a candidate's numerator
 // is bit-identical to its entry of the row.
 __device__ __forceinline__ float residual(float u, float q, float hs, float ls) {
-  return fmaxf(0.f, fmaf(-ls, q, fmaf(-hs, q, u)));
+  return pos01(fmaf(-ls, q, fmaf(-hs, q, u)));
+}
+__device__ __forceinline__ float4 residual4(const float4& u, const float4& q, float hs, float ls) {
+  return make_float4(residual(u.x, q.x, hs, ls), residual(u.y, q.y, hs, ls),
+                     residual(u.z, q.z, hs, ls), residual(u.w, q.w, hs, ls));
 }
 
 template <int BLOCK, int NPT>
@@ -535,18 +546,14 @@ __device__ __forceinline__ double residual_mass(const Row<BLOCK, NPT>& U, const 
   return block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);
 }
 
-// The adjusted row max(0, U - S q) materialised (for the final draw).
+// The adjusted row max(0, U - S q) materialised (for the final distribution output).
 template <int BLOCK, int NPT>
 __device__ __forceinline__ void residual_row(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
                                              double S, Row<BLOCK, NPT>& W) {
   float hs, ls;
   split_s<BLOCK, NPT>(S, hs, ls);
 #pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    const float4 u = U.v[k], q = Q.v[k];
-    W.v[k] = make_float4(residual(u.x, q.x, hs, ls), residual(u.y, q.y, hs, ls),
-                         residual(u.z, q.z, hs, ls), residual(u.w, q.w, hs, ls));
-  }
+  for (int k = 0; k < NPT; ++k) W.v[k] = residual4(U.v[k], Q.v[k], hs, ls);
 }
 
 // The chain over candidates that share the draft row Q: S, C start at 0,
@@ -671,101 +678,114 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
   }
 }
 
-// Inverse-CDF draw from U / sum(U) with uniform u: the smallest id whose
-// cumulative mass exceeds u * sum; if rounding leaves none, the last id with
-// mass.  fp64 cumulative sums in id order.  The masses of the 4-id groups are
-// laid out in LDS in id order (`part`, NPT*BLOCK doubles, free memory); each
-// thread then owns NPT consecutive groups, each wave 64 threads of them: the
-// wave totals locate the wave, a lane scan the thread, its groups the group
-// and the group's owner the id.
-template <int BLOCK, int NPT>
-__device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, int V,
-                                           Shared<BLOCK, NPT>& sh, double* part, int& rb) {
+// Inclusive prefix sum over the wave in lane order: shifts by 1, 2, 4, 8
+// within each row of 16, then the last lane of row 0 (of row 2) added to row 1
+// (row 3), then lane 31 added to rows 2 and 3.
+__device__ __forceinline__ double wave_incl_scan_d(double v) {
+  v += dpp_d<0x111>(v);  // row_shr:1
+  v += dpp_d<0x112>(v);  // row_shr:2
+  v += dpp_d<0x114>(v);  // row_shr:4
+  v += dpp_d<0x118>(v);  // row_shr:8
+  v += __hiloint2double(__builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x142, 0xa, 0xf, false),
+                        __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x142, 0xa, 0xf, false));
+  v += __hiloint2double(__builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x143, 0xc, 0xf, false),
+                        __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// Inverse-CDF draw from the row W / sum(W) with uniform u: the smallest id
+// whose cumulative mass exceeds u * sum, accumulated in id order.  `ent(k)`
+// gives this thread's four entries of slab k (ids (k * BLOCK + tid) * 4 + e,
+// entries past V zero), so the row can be the adjusted row computed on the
+// fly.  The cumulative sums are built in levels over consecutive ids: a
+// group (one thread's four entries, summed left to right in fp32), a lane
+// group (BLOCK / 64 consecutive groups, fp64), a slab (2048 or 1024 ids, a
+// wave's prefix scan of its lane groups), the row (slabs in order).  The draw
+// descends the levels: the first slab whose end exceeds the threshold, in it
+// the first lane group, in that the first group, in that the first entry; an
+// entry's cumulative sum is its group's start plus the group's own fp32
+// prefix, which ends exactly at the group's sum.  Where the levels' fp64
+// roundings leave no crossing inside the chosen lane group (a window of about
+// 1e-16 of the mass), or u rounds to the whole mass, the last entry with mass
+// in the chosen range (else the row) is taken.  `scratch` holds
+// NPT * BLOCK floats and NPT * 64 doubles of free LDS.
+template <int BLOCK, int NPT, typename E>
+__device__ __forceinline__ int inverse_cdf(E&& ent, float u, int V, Shared<BLOCK, NPT>& sh,
+                                           void* scratch, int& rb) {
   constexpr int NW = BLOCK / 64;
+  constexpr int GPL = BLOCK / 64;  // groups per lane group
+  static_assert(NPT % NW == 0, "whole slabs per wave");
+  constexpr int SPW = NPT / NW;    // slabs per wave
+  float* gbuf = static_cast<float*>(scratch);                       // [NPT][BLOCK]
+  double* lsc = reinterpret_cast<double*>(gbuf + NPT * BLOCK);      // [NPT][64]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k)
-      part[k * BLOCK + tid] =
-          (((double)U.v[k].x + (double)U.v[k].y) + (double)U.v[k].z) + (double)U.v[k].w;
+  for (int k = 0; k < NPT; ++k) {
+    const float4 w = ent(k);
+    gbuf[k * BLOCK + tid] = ((w.x + w.y) + w.z) + w.w;
   }
-  barrier_lds();
-  double e[NPT];
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) e[i] = part[tid * NPT + i];
-  double own = 0.0;
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) own += e[i];
-  const double wt = wave_allsum(own);
-  const int wbuf = rb;
-  rb ^= 1;
-  if (lane == 0) sh.rd[wbuf][wave] = wt;
   if (tid == 0) sh.pick = -1;
   barrier_lds();
-  double Z = 0.0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) Z += sh.rd[wbuf][i];
-  const double thr = (double)u * Z;
-  int ws = NW - 1;  // rounding may leave no crossing: then the last wave
-  double before_w = 0.0, run = 0.0;
+  for (int i = 0; i < SPW; ++i) {
+    const int k = wave * SPW + i;
+    double ls = 0.0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const double nx = run + sh.rd[wbuf][i];
-    if (ws == NW - 1 && i < NW - 1 && nx > thr) {
-      ws = i;
-      before_w = run;
-    }
-    if (i == NW - 1 && ws == NW - 1) before_w = run;
-    run = nx;
-  }
-  if (wave == ws) {
-    double incl = own;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const uint64_t hm = __ballot(before_w + incl > thr);
-    const int L = hm ? __ffsll((unsigned long long)hm) - 1 : 63;
-    if (lane == L) {
-      double f = before_w + (incl - own);
-      int sel = -1;
-      double before_e = 0.0;
-#pragma unroll
-      for (int i = 0; i < NPT; ++i) {
-        if (sel < 0 && f + e[i] > thr) {
-          sel = i;
-          before_e = f;
-        }
-        f += e[i];
-      }
-      if (sel < 0) {  // rounding: the lane's last group
-        sel = NPT - 1;
-        before_e = f - e[NPT - 1];
-      }
-      sh.sel_entry = tid * NPT + sel;
-      sh.sel_before = before_e;
-    }
+    for (int g = 0; g < GPL; ++g) ls += (double)gbuf[k * BLOCK + lane * GPL + g];
+    lsc[k * 64 + lane] = wave_incl_scan_d(ls);
   }
   barrier_lds();
-  {
-    const int entry = sh.sel_entry;
-    const int ks = entry / BLOCK, ts = entry - ks * BLOCK;
-    if (tid == ts) {
-      float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+  // every thread takes the same decisions from the same LDS values
+  double before[NPT], Z = 0.0;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    before[k] = Z;
+    Z += lsc[k * 64 + 63];
+  }
+  const double thr = (double)u * Z;
+  int ks = -1;
+  double bk = 0.0;
+#pragma unroll
+  for (int k = NPT - 1; k >= 0; --k)
+    if (before[k] + lsc[k * 64 + 63] > thr) {
+      ks = k;
+      bk = before[k];
+    }
+  if (ks >= 0) {
+    ks = __builtin_amdgcn_readfirstlane(ks);
+    const double incl = lsc[ks * 64 + lane];
+    const uint64_t cross = __ballot(bk + incl > thr);
+    const int L = cross ? __ffsll((unsigned long long)cross) - 1 : 63;
+    double base = bk + (L > 0 ? lsc[ks * 64 + L - 1] : 0.0);
+    int gsel = -1, glast = -1;
+    double gbase = base;
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const float gm = gbuf[ks * BLOCK + L * GPL + g];
+      if (gsel < 0 && base + (double)gm > thr) {
+        gsel = g;
+        gbase = base;
+      }
+      if (gm > 0.f) glast = g;
+      base += (double)gm;
+    }
+    const bool fallback = gsel < 0;
+    if (fallback) gsel = glast;
+    if (gsel >= 0 && tid == L * GPL + gsel) {
+      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
-        if (k == ks) rv = U.v[k];
-      const int id0 = entry * 4;
-      double f = sh.sel_before;
+        if (k == ks) w = ent(k);
+      const int id0 = (ks * BLOCK + tid) * 4;
+      float pre = 0.f;
       int cand = -1, lastpos = -1;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float x = comp(rv, c);
-        f += (double)x;
+        const float x = comp(w, c);
+        pre = c == 0 ? x : pre + x;
         if (id0 + c < V && x > 0.f) {
           lastpos = id0 + c;
-          if (cand < 0 && f > thr) cand = id0 + c;
+          if (cand < 0 && !fallback && gbase + (double)pre > thr) cand = id0 + c;
         }
       }
       sh.pick = cand >= 0 ? cand : lastpos;
@@ -776,12 +796,14 @@ __device__ __forceinline__ int inverse_cdf(const Row<BLOCK, NPT>& U, float u, in
   if (pick < 0) {
     int last = -1;
 #pragma unroll
-    for (int k = 0; k < NPT; ++k)
+    for (int k = 0; k < NPT; ++k) {
+      const float4 w = ent(k);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int idx = (k * BLOCK + tid) * 4 + c;
-        if (idx < V && comp(U.v[k], c) > 0.f) last = idx;
+        if (idx < V && comp(w, c) > 0.f) last = idx;
       }
+    }
     pick = block_max_i<BLOCK, NPT>(last, sh, rb);
     if (pick < 0) pick = 0;
   }
@@ -977,15 +999,20 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     if (shared) {
       double S = 0.0;
       si = run_chain_shared<BLOCK, NPT, PARITY>(U, Q, S, C, cd, nk, true, sh, rb);
-      if (si < 0) residual_row<BLOCK, NPT>(U, Q, S, U);  // the row the final token comes from
+      if (si < 0) {  // the final token from the adjusted row, computed on the fly
+        float hs, ls;
+        split_s<BLOCK, NPT>(S, hs, ls);
+        bonus = inverse_cdf<BLOCK, NPT>(
+            [&](int k) { return residual4(U.v[k], Q.v[k], hs, ls); }, sh.u[0], V, sh, qlds, rb);
+      }
     } else {
       si = run_chain<BLOCK, NPT, VEC, PARITY>(a, ob, U, Q, C, ut, val, cd, nk, true, sh, qlds, rb);
+      if (si < 0)
+        bonus = inverse_cdf<BLOCK, NPT>([&](int k) { return U.v[k]; }, sh.u[0], V, sh, qlds, rb);
     }
     if (si >= 0) {
       acc = sh.kids[si];
       ntested = si + 1;
-    } else {
-      bonus = inverse_cdf<BLOCK, NPT>(U, sh.u[0], V, sh, reinterpret_cast<double*>(qlds), rb);
     }
   }
   // a prefetch left in flight by an early acceptance must land before exit
