@@ -244,12 +244,6 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-// Raw buffer over `bytes` bytes at `base` (out-of-range offsets read 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0,
-                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
-                                           0x00020000);
-}
 __device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16));
 }

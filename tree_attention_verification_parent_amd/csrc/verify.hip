@@ -211,6 +211,27 @@ __device__ __forceinline__ float comp(const float4& f, int e) {
   return e == 0 ? f.x : e == 1 ? f.y : e == 2 ? f.z : f.w;
 }
 
+// `len` floats of a row into registers, len % 4 == 0: straight-line buffer
+// loads (no branches, so the compiler can count them and later waits name only
+// the loads they need); entries past len read 0 from the buffer without a
+// memory access and are then set to `pad`.  len = 0 loads nothing.
+template <int BLOCK, int NPT>
+__device__ __forceinline__ void load_row_vec(Row<BLOCK, NPT>& r, const float* src, int len,
+                                             float pad) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (size_t)len * 4);
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+    r.v[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (k * BLOCK + tid) * 16, 0, 0));
+  if (pad != 0.f) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      if ((k + 1) * BLOCK * 4 > len && (k * BLOCK + tid) * 4 >= len)
+        r.v[k] = make_float4(pad, pad, pad, pad);
+  }
+}
+
 // `len` floats of a row into registers (len >= 1); entries past len read as
 // `pad` (-FLT_MAX for logits: no mass, never the maximum of a row that has a
 // finite entry; 0 for draft rows).  Every load is issued at an in-range
@@ -631,7 +652,12 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
     if (shared) {
       // the one draft row (unless already guessed right), and each
       // candidate's probability in it
-      if (!(q_guess && r0 == node)) load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+      if (!(q_guess && r0 == node)) {
+        if constexpr (VEC)
+          load_row_vec<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+        else
+          load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+      }
       if (cd.tok >= 0) cd.q = a.draft[(ob + r0) * V + cd.tok];
     } else if (nk > 0 && VEC) {
       // slots past V are never loaded: zero this thread's (the pass reads them)
@@ -957,10 +983,16 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   const TreeRegs tr = fetch_tree(a, b);
   asm volatile("" ::: "memory");
   Row<BLOCK, NPT> U;
-  load_row<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
   Row<BLOCK, NPT> Q;  // the shared draft row, or the second row of the step-by-step chain
   const bool q_guess = !GREEDY && a.guess_row;
-  if (q_guess) load_row<BLOCK, NPT>(Q, a.draft + (ob + j) * V, V, 0.f);
+  if constexpr (VEC) {
+    load_row_vec<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
+    // without the guess the buffer is empty: no memory is read
+    if constexpr (!GREEDY) load_row_vec<BLOCK, NPT>(Q, a.draft + (ob + j) * V, q_guess ? V : 0, 0.f);
+  } else {
+    load_row<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
+    if (q_guess) load_row<BLOCK, NPT>(Q, a.draft + (ob + j) * V, V, 0.f);
+  }
   store_tree<BLOCK, NPT>(a, b, tr, j == 0, sh);
   barrier_lds();
   double C = 1.0;
@@ -1090,7 +1122,10 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
     if constexpr (GREEDY) {
       for (int v = tid; v < V; v += BLOCK) fo[v] = v == bt ? 1.f : 0.f;
     } else {
-      load_row<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
+      if constexpr (VEC)
+        load_row_vec<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
+      else
+        load_row<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
       node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, Q, false, C, ut, val, cd, shared,
                                          sh, qlds, rb);
       if (shared) {
@@ -1318,8 +1353,10 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   }
 #define EAGLE_LAUNCH_VERIFY(BLK, NPT)                                                        \
   do {                                                                                      \
-    if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, true><<<grid, BLK, 0, s>>>(a);    \
-    else if (greedy) verify_node_kernel<BLK, NPT, true, false, true><<<grid, BLK, 0, s>>>(a);        \
+    if (greedy && parity && vec) verify_node_kernel<BLK, NPT, true, true, true><<<grid, BLK, 0, s>>>(a); \
+    else if (greedy && parity) verify_node_kernel<BLK, NPT, true, true, false><<<grid, BLK, 0, s>>>(a); \
+    else if (greedy && vec) verify_node_kernel<BLK, NPT, true, false, true><<<grid, BLK, 0, s>>>(a);  \
+    else if (greedy) verify_node_kernel<BLK, NPT, true, false, false><<<grid, BLK, 0, s>>>(a);        \
     else if (parity && vec) verify_node_kernel<BLK, NPT, false, true, true><<<grid, BLK, 0, s>>>(a); \
     else if (parity) verify_node_kernel<BLK, NPT, false, true, false><<<grid, BLK, 0, s>>>(a);       \
     else if (vec) verify_node_kernel<BLK, NPT, false, false, true><<<grid, BLK, 0, s>>>(a);          \
