@@ -381,13 +381,27 @@ __device__ __forceinline__ void load_queries(const AttnArgs& a, const Piece& u, 
 // or two more chunks, masked by the ancestor bits, for the wave of the last
 // piece with the fewest committed chunks.
 constexpr int kRingThreads = 64 * 8;
-constexpr int kNonTemporal = 2;  // cache-policy bits of a load: nt
 
-// One lane's 16-byte direct-to-LDS load, non-temporal: the K/V stream is read
-// once, and per XCD it is about the size of the L2.
-__device__ __forceinline__ void load_lds16(const uint16_t* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                   kNonTemporal);
+// One lane's 16 bytes of global memory into LDS at lds_addr + 16 * lane
+// (lds_addr wave-uniform), non-temporal (the K/V stream is read once, and per
+// XCD it is about the size of the L2).  Inline assembly (M0 saved and restored
+// around it): the compiler treats a direct-to-LDS load of its own as a pending
+// LDS write that every later LDS read waits for, which would hold each chunk's
+// computation up behind every load issued after it.  The kernels track the
+// loads' completion themselves with s_waitcnt (vector loads complete in
+// order).
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(src)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p);
 }
 
 template <int D_, int QBW_>
@@ -583,101 +597,127 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
-      load_lds16(kp + off, slot + t * RPL * D * 2);
+      lds_dma16(kp + off, lds_addr(slot + t * RPL * D * 2));
     }
 #pragma unroll
     for (int t = 0; t < LPM; ++t) {
       const int r = t * RPL + r_in;
       const int key = min(key0 + r, key_max);
       const size_t off = (size_t)key * D + (p_in ^ swz<D>(r)) * 8;
-      load_lds16(vp + off, slot + S::MAT_BYTES + t * RPL * D * 2);
+      lds_dma16(vp + off, lds_addr(slot + S::MAT_BYTES + t * RPL * D * 2));
     }
   };
 
-  // The piece this slot would hold if every sequence filled the cache (the
-  // common case) needs no memory read: the wave issues its first chunk under
-  // that assumption while the committed lengths are read, and keeps it only
-  // if the real plan agrees (the chunk lies in [0, L) then); otherwise the
-  // loads are waited for and their data discarded before the slot is reused.
-  const int kvl0 = kv_len_lanes(a);  // scalar loads first (B <= 16): no wait behind the chunk
-  const int Lcap = a.Lmax - a.N;
-  const int cap_chunks = (Lcap + 31) / 32;
-  int spec_unit = -1, spec_split = 0, spec_chunk = -1;
-  if (a.full_pieces > 0 && slot_w < a.B * a.Hkv * a.full_pieces) {
-    spec_unit = slot_w / a.full_pieces;
-    spec_split = slot_w - spec_unit * a.full_pieces;
-    const int scb = (int)((long long)spec_split * cap_chunks / a.full_pieces);
-    const int sce = (int)((long long)(spec_split + 1) * cap_chunks / a.full_pieces);
-    if (scb + wave < sce) {
-      spec_chunk = scb + wave;
-      const size_t sbase = (size_t)spec_unit * (size_t)a.Lmax * D;  // unit = b * Hkv + kvh
-      issue_keys_at(a.k + sbase, a.v + sbase, spec_chunk * 32, Lcap - 1);
+  // The query rows of a unit (b, kvh): lane (c, g) holds row qb * 16 + c's
+  // 8 dims at ks * 32 + g * 8.
+  bf16x8 qf[QBW][NKS];
+  auto load_q = [&](int b, int kvh) {
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+      const int row = qb * 16 + c;
+      const int rr = row < a.M ? row : 0;  // in range either way; zeroed below
+      const int i = rr / a.G;
+      const int h = kvh * a.G + (rr - i * a.G);
+      const uint16_t* qrow = a.q + (((size_t)b * a.N + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
+        qf[qb][ks] = row < a.M ? x : bf16x8{};
+      }
     }
-  }
+  };
 
-  // slot -> piece (every wave finds it; the committed lengths decide it)
-  Piece pc;
-  if (!plan_piece(a, slot_w, kvl0, pc)) {
-    if (spec_chunk >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    return;
+  // A piece's chunks for this wave: 32-key chunks of [0, L), wave w taking
+  // cb + w, cb + w + NWAVE, ..., then (for the wave of the last piece with
+  // the fewest committed chunks) the tree keys [L, L + N) as one or two more
+  // masked chunks (N <= 64).
+  struct Run {
+    int L, my_first, my_n, my_chunks;
+    bool tree_wave;
+    const uint16_t* kp;
+    const uint16_t* vp;
+  };
+  auto run_of = [&](const Piece& p) {
+    Run r;
+    r.L = p.L;
+    const int n_chunks = (p.L + 31) / 32;
+    const int cb = (int)((long long)p.split * n_chunks / p.nsplit);
+    const int ce = (int)((long long)(p.split + 1) * n_chunks / p.nsplit);
+    r.my_first = cb + wave;
+    r.my_n = r.my_first < ce ? (ce - r.my_first + NWAVE - 1) / NWAVE : 0;
+    r.tree_wave = p.split == p.nsplit - 1 && wave == (ce - cb) % NWAVE;
+    r.my_chunks = r.my_n + (r.tree_wave ? (a.N + 31) / 32 : 0);
+    const size_t kv_base = ((size_t)p.b * a.Hkv + p.kvh) * (size_t)a.Lmax * D;
+    r.kp = a.k + kv_base;
+    r.vp = a.v + kv_base;
+    return r;
+  };
+  auto chunk_key0 = [&](const Run& r, int i) {
+    return i < r.my_n ? (r.my_first + NWAVE * i) * 32 : r.L + 32 * (i - r.my_n);
+  };
+  auto chunk_kmax = [&](const Run& r, int i) { return i < r.my_n ? r.L - 1 : r.L + a.N - 1; };
+  // The start of a piece: its query rows, then its first chunk into the slot
+  // and (a wave with two or more chunks) its second into registers, so that
+  // the second is in flight with the first instead of requested once the
+  // first has been computed (the slot is busy until then); it goes to the
+  // slot later in the layout a direct-to-LDS load gives.  Vector loads
+  // complete in order: the rows land before the chunk that needs them, and
+  // the first chunk can be waited for with the second's loads outstanding.
+  u32x4 pre[2 * LPM];
+  auto start = [&](const Piece& p, const Run& r) {
+    load_q(p.b, p.kvh);
+    if (r.my_chunks > 0) issue_keys_at(r.kp, r.vp, chunk_key0(r, 0), chunk_kmax(r, 0));
+    if (r.my_chunks >= 2) {
+      const int key0 = chunk_key0(r, 1), key_max = chunk_kmax(r, 1);
+#pragma unroll
+      for (int t = 0; t < LPM; ++t) {
+        const int rr = t * RPL + r_in;
+        const size_t off = (size_t)min(key0 + rr, key_max) * D + (p_in ^ swz<D>(rr)) * 8;
+        pre[t] = *reinterpret_cast<const u32x4*>(r.kp + off);
+        pre[LPM + t] = *reinterpret_cast<const u32x4*>(r.vp + off);
+      }
+    }
+  };
+
+  // The committed lengths, lane b holding sequence b's (a vector load issued
+  // first, so it completes before anything waited for later).
+  const int kvl0 = a.kv_len[min(lane, a.B - 1)];
+  const int Lcap = a.Lmax - a.N;
+  // When every sequence fills the cache (the common case) the planner gives
+  // this slot piece slot % full_pieces of unit slot / full_pieces: the wave
+  // starts that piece before the lengths are read, and the plan reduces to
+  // checking that every length is the full one.  Otherwise the started loads
+  // are waited for and dropped, and the planner finds the piece.
+  const bool spec = a.full_pieces > 0 && a.B <= 64 && slot_w < a.B * a.Hkv * a.full_pieces;
+  Piece pc{};
+  if (spec) {
+    pc.unit = slot_w / a.full_pieces;
+    pc.b = pc.unit / a.Hkv;
+    pc.kvh = pc.unit - pc.b * a.Hkv;
+    pc.qgroup = 0;
+    pc.nsplit = a.full_pieces;
+    pc.split = slot_w - pc.unit * a.full_pieces;
+    pc.first = pc.unit * a.full_pieces;
+    pc.L = Lcap;
+    pc.bad = false;
+    start(pc, run_of(pc));
   }
+  const bool full = spec && wave_allmin_i(lane < a.B ? (kvl0 == Lcap ? 1 : 0) : 1) == 1;
+  if (!full) {
+    if (spec) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // dropped
+    // slot -> piece (every wave finds it; the committed lengths decide it)
+    if (!plan_piece(a, slot_w, kvl0, pc)) return;
+    if (pc.bad && a.flags && pc.split == 0 && pc.kvh == 0 && tid == 0)
+      atomicOr(a.flags + pc.b, EAGLE_FLAG_BAD_KV_LEN);
+    start(pc, run_of(pc));
+  }
+  const Run R = run_of(pc);
   const int b = pc.b, kvh = pc.kvh, L = pc.L;
   const bool bad = pc.bad;
-  if (bad && a.flags && pc.split == 0 && kvh == 0 && tid == 0)
-    atomicOr(a.flags + b, EAGLE_FLAG_BAD_KV_LEN);
+  const int my_n = R.my_n, my_chunks = R.my_chunks;
+  const bool tree_wave = R.tree_wave;
+  const bool pre2 = my_chunks >= 2;  // wave-uniform
 
-  // this piece's 32-key chunks of [0, L); wave w takes cb + w, cb + w + NWAVE, ...
-  const int n_chunks = (L + 31) / 32;
-  const int cb = (int)((long long)pc.split * n_chunks / pc.nsplit);
-  const int ce = (int)((long long)(pc.split + 1) * n_chunks / pc.nsplit);
-  const int my_first = cb + wave;
-  const int my_n = my_first < ce ? (ce - my_first + NWAVE - 1) / NWAVE : 0;
-  const bool last_piece = pc.split == pc.nsplit - 1;
-
-  const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
-  const uint16_t* kp = a.k + kv_base;
-  const uint16_t* vp = a.v + kv_base;
-  auto issue_keys = [&](int key0, int key_max) { issue_keys_at(kp, vp, key0, key_max); };
-  auto issue = [&](int gc) { issue_keys(gc * 32, L - 1); };
-  // The tree keys [L, L + N) are one or two more masked chunks (N <= 64),
-  // taken by the wave of the last piece with the fewest committed chunks.
-  const bool tree_wave = last_piece && wave == (ce - cb) % NWAVE;
-  const bool spec_kept = spec_chunk >= 0 && my_n > 0 && spec_chunk == my_first &&
-                         spec_unit == pc.unit && spec_split == pc.split &&
-                         pc.nsplit == a.full_pieces && L == Lcap;
-  if (!spec_kept) {
-    if (spec_chunk >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // discarded
-    if (my_n > 0)
-      issue(my_first);
-    else if (tree_wave)
-      issue_keys(L, L + a.N - 1);
-  }
-
-  // A wave with three or more chunks loads its second one into registers
-  // right away, so that it is in flight with the first instead of requested
-  // once the first has been computed (the slot is busy until then); it is
-  // written to the slot in the layout a direct-to-LDS load gives.  (Measured
-  // on MI355X: llama2-13b shape, ~5 chunks per wave, 60.9 us against 62.7;
-  // with two chunks, waiting for both before the first is computed costs more
-  // than it saves: 15.2 us against 14.2 at the llama2-7b shape.)
-  const int my_chunks = my_n + (tree_wave ? (a.N + 31) / 32 : 0);
-  const bool pre2 = my_chunks >= 3;  // wave-uniform
-  u32x4 pre[2 * LPM];
-  auto load_pre = [&](int key0, int key_max) {
-#pragma unroll
-    for (int t = 0; t < LPM; ++t) {
-      const int r = t * RPL + r_in;
-      const size_t off = (size_t)min(key0 + r, key_max) * D + (p_in ^ swz<D>(r)) * 8;
-      pre[t] = *reinterpret_cast<const u32x4*>(kp + off);
-      pre[LPM + t] = *reinterpret_cast<const u32x4*>(vp + off);
-    }
-  };
-  if (pre2) {
-    if (1 < my_n)
-      load_pre((my_first + NWAVE) * 32, L - 1);
-    else
-      load_pre(L + 32 * (1 - my_n), L + a.N - 1);  // a tree chunk second
-  }
   // the tree wave's rows' ancestor masks: bit t of anc[row] admits key L + t
   uint64_t anc_q[QBW];
   if (tree_wave) {
@@ -702,22 +742,6 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     }
   }
   const int rows = a.M;  // <= RW
-  bf16x8 qf[QBW][NKS];
-#pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const int row = qb * 16 + c;
-    if (row < a.M) {
-      const int i = row / a.G;
-      const int h = kvh * a.G + (row - i * a.G);
-      const uint16_t* qrow = a.q + (((size_t)b * a.N + i) * a.Hq + h) * D;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] = bf16x8{};
-    }
-  }
 
   f32x4 acc[QBW][NDB];
   float m_run[QBW], l_run[QBW];
@@ -732,7 +756,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   for (int i = 0; i < my_chunks; ++i) {
     const bool tree_chunk = i >= my_n;
     const int tree_bit0 = 32 * (i - my_n);  // anc bit of the tree chunk's first key
-    const int gc = my_first + NWAVE * i;
+    const int key0 = chunk_key0(R, i);
     if (i == 1 && pre2) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the first chunk's reads are done
 #pragma unroll
@@ -740,18 +764,19 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
         *reinterpret_cast<u32x4*>(slot + t * RPL * D * 2 + lane * 16) = pre[t];
         *reinterpret_cast<u32x4*>(slot + S::MAT_BYTES + t * RPL * D * 2 + lane * 16) = pre[LPM + t];
       }
+    } else if (i == 0 && pre2) {
+      // the first chunk has landed: at most the 2 * LPM loads of the second
+      // (and any issued after them) are outstanding
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPM) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's chunk has landed
     }
-    const bool need_mask = tree_chunk || gc * 32 + 32 > L;
+    const bool need_mask = tree_chunk || key0 + 32 > L;
     chunk_step<D, QBW>(slot, qf, anc_q, acc, m_run, l_run, a.scale_log2, need_mask, tree_chunk,
-                       tree_bit0, prefix_mask8(gc * 32 + 8 * g, L));
+                       tree_bit0, prefix_mask8(key0 + 8 * g, L));
     if (i + 1 < my_chunks && !(i == 0 && pre2)) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot's reads are done
-      if (i + 1 < my_n)
-        issue(gc + NWAVE);
-      else
-        issue_keys(L + 32 * (i + 1 - my_n), L + a.N - 1);
+      issue_keys_at(R.kp, R.vp, chunk_key0(R, i + 1), chunk_kmax(R, i + 1));
     }
   }
 
@@ -899,17 +924,6 @@ struct GroupShape {
   static_assert(LPW * NWAVE == 4 * LPM, "a tile's loads split evenly over the waves");
 };
 
-// One lane's 16 bytes of global memory into LDS at lds_addr + 16 * lane (lds_addr
-// wave-uniform), issued as inline assembly (M0 saved and restored around it).
-__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off nt\n\ts_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds_addr), "v"(src)
-      : "memory");
-}
 
 // Waits until at most n of this wave's vector loads are outstanding.
 template <int LPW>
