@@ -486,6 +486,35 @@ def test_verify_nonfinite_logits_flagged():
     assert f[0] == 0 and f[1] & ev.binding.FLAG_NONFINITE and f[2] & ev.binding.FLAG_NONFINITE
 
 
+@pytest.mark.parametrize("V", [4096, 32768])
+def test_target_exp_within_ulps(V):
+    """The vocabulary pass's exp: with the row maximum at 0 (so the argument
+    x - max is exact) and the other logits spread over [-87, -16], the mass is
+    1 + O(1e-3) and out_probs = exp(x) / mass checks each exp against fp64.
+    The kernel computes 2^(x log2 e) with the product's rounding error carried
+    separately (an FMA recovers it exactly) and added back to first order;
+    its error is the hardware exp2's (about 1 ulp) plus that correction's, so
+    within 2 ulp, and the fp64 division and final rounding of out_probs add
+    half an ulp."""
+    rng = np.random.default_rng(11)
+    x = np.empty(V, dtype=np.float32)
+    x[0] = 0.0
+    x[1:] = rng.uniform(-87.0, -16.0, V - 1).astype(np.float32)
+    x[1:9] = np.float32([-1e-3, -0.25, -0.693, -1.0, -2.5, -7.0, -15.99, -86.9])
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    logits = d(x.reshape(1, 1, V))
+    say(f"exp pin V={V}")
+    o = ev.verify_accept(d(np.zeros((1, 1), np.int32)), d(np.zeros((1, 1, V), np.float32)), logits,
+                         d(np.full((1, 1), -1, np.int32)), d(np.array([16], np.int32)), 1.0,
+                         d(np.full((1, 1), 0.5, np.float32)), want_probs=True)
+    got = o["probs"].cpu().numpy()[0, 0].astype(np.float64)
+    e = np.exp(x.astype(np.float64))
+    ref = e / e.sum()
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    err_ulps = np.abs(got - ref) / ulp
+    assert err_ulps.max() <= 2.5, (float(err_ulps.max()), int(err_ulps.argmax()))
+
+
 def test_verify_deterministic():
     s = W.make_step(W.get(4), 1.0, with_attention=False)
     say("verify determinism")
