@@ -334,10 +334,23 @@ def profile_run(torch, ev, W, name, steps):
     """Eager launches of one workload for rocprofv3 (nothing is timed here):
     `attn:<config>` runs the tree attention with the mask built in at that
     configuration, rotating input copies as the timed runs do, then the
-    calibration copy for counter passes; `dtree` runs the EAGLE-2 tree build
-    at the mixtral-eagle2 shape."""
+    calibration copy for counter passes; `verify:<config>[:T]` runs the
+    verification with fused compaction the same way (T defaults to the
+    config's last listed temperature); `dtree` runs the EAGLE-2 tree build at
+    the mixtral-eagle2 shape."""
     if name == "dtree":
         measure_dynamic_tree(torch, ev, W, max(10, steps))
+    elif name.startswith("verify:"):
+        # verify:<config>[:T] -- the verification with fused compaction alone
+        parts = name.split(":")
+        cfg = W.get(parts[1])
+        T = float(parts[2]) if len(parts) > 2 else cfg.temperatures[-1]
+        s = W.make_step(cfg, T)
+        copies = max(2, math.ceil(ROTATE_BYTES / (cfg.attn_bytes() + 2 * cfg.vocab_bytes())))
+        st = Step(s, torch, ev, copies)
+        for i in range(steps):
+            st.verify(i)
+        torch.cuda.synchronize()
     elif name.startswith("attn:"):
         cfg = W.get(name[5:])
         s = W.make_step(cfg, cfg.temperatures[-1])
@@ -519,7 +532,8 @@ def main():
     ap.add_argument("--oracle-configs", action="store_true",
                     help="time the CPU oracle per configuration and stage, print one JSON line")
     ap.add_argument("--profile", default=None,
-                    help="attn:<config> or dtree: eager launches for a rocprofv3 trace")
+                    help="attn:<config>, verify:<config>[:T] or dtree: eager launches for a "
+                         "rocprofv3 trace")
     ap.add_argument("--per-config", action="store_true",
                     help="time the step, attention and verify per configuration and listed "
                          "temperature, print one JSON line")
