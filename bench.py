@@ -24,7 +24,8 @@ configuration, or the EAGLE-2 tree build, eagerly for a kernel trace.
 `--oracle-configs` times the CPU oracle per configuration and stage (no GPU
 work) and prints one JSON line.  `--per-config` times the step, the attention
 and the verify launch at every configuration and listed temperature (and the
-7B layer with a close draft) and prints one JSON line of rows.
+7B layer with a close draft) and prints one JSON line of rows; `--ragged`
+times the tree attention on a ragged batch against equal-length ones.
 """
 from __future__ import annotations
 
@@ -509,6 +510,54 @@ def per_config(torch, ev, W, steps, warmup):
     return {"per_config": rows, "steps": steps, "warmup": warmup, "hbm_peak_GBs": HBM_PEAK_GBS}
 
 
+def ragged_timing(torch, ev, W, steps):
+    """Tree attention on a ragged batch against equal-length batches (the
+    decomposition shares the launch's slots out by committed length, so the
+    time should follow the sum of the lengths): B = 4 sequences in a cache of
+    8192 + N slots with committed lengths 512/1024/2048/8192, all 8192, and
+    all 2944 (the ragged batch's mean, the same sum), then all 2944 in a
+    cache of 2944 + N slots (the same work at full length, launched for it),
+    at the llama2-13b heads (ring kernel) and the llama2-70b heads (group
+    kernel).  Graph-timed, rotating input copies as the timed runs do."""
+    rows = []
+    dev = torch.device("cuda")
+    for name in ("llama2-13b", "llama2-70b-gqa"):
+        base = W.shrink(W.get(name), B=4)
+        for lens, cap in (([512, 1024, 2048, 8192], 8192), ([8192] * 4, 8192),
+                          ([2944] * 4, 8192), ([2944] * 4, 2944)):
+            Lmax = cap + base.N
+            s = W.make_step(base, base.temperatures[-1], kv_lens=lens, with_attention=False)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(5)
+            B, N = base.B, base.N
+            kvb = B * base.Hkv * Lmax * base.d * 2 * 2
+            copies = max(2, math.ceil(ROTATE_BYTES / kvb))
+            slots = []
+            for _ in range(copies):
+                q = torch.randn((B, N, base.Hq, base.d), device=dev, generator=gen).to(torch.bfloat16)
+                k = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
+                v = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
+                slots.append((q, k, v))
+            parents = torch.from_numpy(s.parents).to(dev)
+            kv_len = torch.from_numpy(s.kv_len).to(dev)
+            ws = ev.alloc_workspace(ev.tree_attn_workspace_bytes(B, N, base.Hq, base.Hkv, base.d, Lmax))
+            out = torch.empty_like(slots[0][0])
+
+            def run(i):
+                qq, kk, vv = slots[i % copies]
+                ev.tree_attn_parents(qq, kk, vv, kv_len, parents, out=out, workspace=ws)
+            g = graph_of(torch, run, steps)
+            time_graph(torch, g)
+            t = min(time_graph(torch, g) / steps for _ in range(3))
+            nbytes = sum(base.Hkv * (L + N) * base.d * 4 for L in lens)
+            rows.append({"heads": name, "kv_len": lens, "cache_len": cap, "sum_kv_len": sum(lens),
+                         "us": t * 1e6, "kv_bytes": nbytes, "TB_per_s": nbytes / t / 1e12})
+            log(f"[bench] ragged {json.dumps(rows[-1])}")
+            del slots, g, ws
+            torch.cuda.empty_cache()
+    return {"ragged": rows, "steps": steps}
+
+
 def pmc_traffic(attn_bytes):
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -534,6 +583,9 @@ def main():
     ap.add_argument("--profile", default=None,
                     help="attn:<config>, verify:<config>[:T] or dtree: eager launches for a "
                          "rocprofv3 trace")
+    ap.add_argument("--ragged", action="store_true",
+                    help="time the tree attention on a ragged batch against equal-length "
+                         "batches, print one JSON line")
     ap.add_argument("--per-config", action="store_true",
                     help="time the step, attention and verify per configuration and listed "
                          "temperature, print one JSON line")
@@ -562,6 +614,9 @@ def main():
         return
     if args.profile:
         profile_run(torch, ev, W, args.profile, args.steps)
+        return
+    if args.ragged:
+        print(json.dumps(ragged_timing(torch, ev, W, min(args.steps, 50))), flush=True)
         return
     if args.per_config:
         print(json.dumps(per_config(torch, ev, W, min(args.steps, 50), min(args.warmup, 10))),

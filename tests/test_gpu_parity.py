@@ -72,6 +72,10 @@ ATTN_CASES = [
     ("max-nodes", 2, 64, 4, 2, 128, [190, 3]),
     ("wide-group", 1, 40, 32, 2, 64, [350]),
     ("gqa-ragged-edges", 3, 20, 16, 2, 128, [0, 1, 777]),
+    # many sequences of mixed lengths: the planner's searches over several
+    # blocks of four sequences (B <= 64) and its serial form (B > 64)
+    ("40-seqs-ragged", 40, 6, 4, 2, 64, [(53 * i) % 389 for i in range(40)]),
+    ("70-seqs-ragged", 70, 4, 4, 2, 64, [(37 * i + 5) % 301 for i in range(70)]),
 ]
 
 

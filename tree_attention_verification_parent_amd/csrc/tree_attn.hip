@@ -71,6 +71,7 @@ struct AttnArgs {
   int32_t* flags;
   int B, N, Hq, Hkv, Lmax, G, M, qgroups, slots, kg, max_pieces;
   int full_pieces;  // pieces per unit when every sequence fills the cache (see the ring kernel)
+  int ring_cost;    // 1: pick the piece length by the ring kernel's cost model (else the smallest that fits)
   float scale_log2;
 };
 
@@ -82,12 +83,11 @@ struct Piece {
   bool bad;
 };
 
-// Logical slot of this workgroup: the launch's slots / 8 consecutive slots
-// share an XCD.
-__device__ __forceinline__ int logical_slot(const AttnArgs& a) {
-  const int per_xcd = a.slots / kNumXCDs;
-  return (int)(blockIdx.x % kNumXCDs) * per_xcd + (int)(blockIdx.x / kNumXCDs);
-}
+// Slot of this workgroup: its id.  Workgroup ids go to the XCDs round robin,
+// so the used slots (0 .. pieces - 1 when the committed lengths leave some
+// unused) are spread over all XCDs; no piece relies on sharing an XCD with
+// another (the partials are merged through device-coherent memory).
+__device__ __forceinline__ int logical_slot(const AttnArgs& a) { return (int)blockIdx.x; }
 
 // A wave-uniform 32-bit value read with a scalar load (constant address
 // space), which the compiler tracks apart from the vector loads in flight.
@@ -124,6 +124,20 @@ __device__ __forceinline__ int wave_allsum_i(int v) {
   return (lane_i(v, 0) + lane_i(v, 16)) + (lane_i(v, 32) + lane_i(v, 48));
 }
 
+// The ring kernel's cost of a decomposition, in chunk-times: pieces of at
+// most T chunks, n_pieces of them in all, the longest sequence cut into
+// ceil(cmax / T) pieces.  A ring workgroup fills its CU's LDS, so workgroups
+// beyond the CU count run in another round that costs as much as a full one;
+// each piece of a unit adds a merge cost of 1.75 chunk-times (fitted on
+// MI355X).  The host (at full cache length) and the device (at the committed
+// lengths) evaluate the same expression, so at full length both choose the
+// same pieces.
+__host__ __device__ inline float ring_piece_cost(long long n_pieces, int T, int cmax) {
+  const long long slots = (n_pieces + kNumXCDs - 1) / kNumXCDs * kNumXCDs;
+  const long long rounds = (slots + kNumCUs - 1) / kNumCUs;
+  return (float)(rounds * T) + 1.75f * (float)((cmax + T - 1) / T);
+}
+
 // Committed length of sequence b (given as read) -> chunks of kg keys; a
 // length that leaves no room for the tree (or is negative) counts as 0.
 __device__ __forceinline__ int seq_chunks(const AttnArgs& a, bool in, int Lraw, int& L, bool& bad) {
@@ -132,13 +146,39 @@ __device__ __forceinline__ int seq_chunks(const AttnArgs& a, bool in, int Lraw, 
   return (L + a.kg - 1) / a.kg;
 }
 
+// Pieces of all units at 16 candidate piece lengths at once, B <= 64: lane j
+// holds candidate j & 15's length t and adds the pieces of sequences
+// j >> 4, (j >> 4) + 4, ... (c0: chunks by lane, as in plan_piece); the four
+// partial sums of a candidate meet across lanes j, j ^ 16, j ^ 32, j ^ 48.
+// Every lane returns its candidate's total.
+__device__ __forceinline__ long long count_pieces_x16(const AttnArgs& a, int c0, int t) {
+  const int part = (threadIdx.x & 63) >> 4;
+  int n = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 4) {  // wave-uniform
+    const int b = b0 + part;
+    const int cb = __shfl(c0, b & 63);
+    if (b < a.B) n += max(1, min(a.max_pieces, (cb + t - 1) / t));
+  }
+  n += __shfl_xor(n, 16);
+  n += __shfl_xor(n, 32);
+  return (long long)(a.Hkv * a.qgroups) * n;
+}
+
 // Shares the launch's slots out and finds a piece.  Every unit of sequence b
 // gets s_b = ceil(c_b / T) pieces (at least one, at most max_pieces), where
-// c_b is its number of chunks of kg committed keys and T, the largest piece in
-// chunks, is the smallest value for which all pieces fit the launch's slots:
-// in closed form when every sequence has the same length, else by bisection
+// c_b is its number of chunks of kg committed keys and T is the largest piece
+// in chunks.  Ring kernel: T = ceil(c_max / k) for the k in 1..16 of least
+// ring_piece_cost among those whose pieces fit the launch's slots (so short
+// committed lengths take fewer, not shorter, rounds of workgroups).
+// Otherwise T is the smallest value for which all pieces fit the slots: in
+// closed form when every sequence has the same length, else by bisection
 // (the count only falls as T grows, and T = max c_b fits since the host
-// launches at least one slot per unit).  Slots are numbered sequence by
+// launches at least one slot per unit).  With B <= 64 the 16 candidates of
+// the cost model are counted at once, one per group of lanes, and the
+// bisection becomes a 16-way search; both give the same T as the serial
+// forms (the first candidate of least cost; the least fitting T), at a
+// fraction of the instructions, which every workgroup spends before its
+// first loads when the lengths are not the full ones.  Slots are numbered sequence by
 // sequence, unit by unit, piece by piece; slots past the last piece are
 // unused.  Finds the piece in slot `key`; kvl0 holds the committed lengths of
 // sequences 0..63 by lane (kv_len_lanes).  A function of the committed
@@ -166,22 +206,67 @@ __device__ bool plan_piece(const AttnArgs& a, int key, int kvl0, Piece& p) {
     cmin = min(cmin, wave_allmin_i(b0 + lane < a.B ? c : INT_MAX));
   }
   auto pieces_of = [&](int c, int t) { return max(1, min(a.max_pieces, (c + t - 1) / t)); };
-  int T;
-  if (cmin == cmax) {
+  // all pieces at piece length t (capped just past the slots)
+  auto count_at = [&](int t) {
+    long long n = wave_allsum_i(lane < a.B ? min(U * pieces_of(c0, t), a.slots + 1) : 0);
+    for (int b0 = 64; b0 < a.B && n <= a.slots; b0 += 64) {
+      int L;
+      bool bad;
+      const int c = block_chunks(b0, L, bad);
+      n += wave_allsum_i(b0 + lane < a.B ? min(U * pieces_of(c, t), a.slots + 1) : 0);
+    }
+    return n;
+  };
+  int T = 0;
+  if (a.B <= 64 && a.ring_cost) {
+    const int cm = max(cmax, 1);
+    const int k = (lane & 15) + 1;
+    const int t = (cm + k - 1) / k;
+    const long long n = count_pieces_x16(a, c0, t);
+    const bool ok = k <= cm && n <= a.slots;
+    // costs are non-negative (or +inf): their bits order as integers
+    const int cost = __float_as_int(ok ? ring_piece_cost(n, t, cm) : INFINITY);
+    const int best = wave_allmin_i(cost);
+    const uint64_t m = __ballot(lane < 16 && ok && cost == best);  // k = 1 always fits
+    T = m ? lane_i(t, __ffsll((unsigned long long)m) - 1) : cm;
+  } else if (a.B <= 64 && cmin != cmax) {
+    // least fitting T in [lo, hi] (hi fits): candidate j = lo + (j + 1) step - 1,
+    // the last one hi; the first that fits bounds the next range
+    int lo = 1, hi = max(cmax, 1);
+    const int j = lane & 15;
+    while (lo < hi) {  // wave-uniform
+      const int step = (hi - lo + 16) / 16;
+      const int t = min(hi, lo + (j + 1) * step - 1);
+      const bool fit = count_pieces_x16(a, c0, t) <= a.slots;
+      const uint64_t m = __ballot(lane < 16 && fit);  // candidate 15 (= hi) fits
+      const int jf = m ? __ffsll((unsigned long long)m) - 1 : 15;
+      const int prev = lane_i(t, max(jf - 1, 0));
+      hi = lane_i(t, jf);
+      lo = jf > 0 ? prev + 1 : lo;
+    }
+    T = lo;
+  } else if (a.ring_cost) {
+    const int cm = max(cmax, 1);
+    float best = 0.f;
+    for (int k = 1; k <= min(16, cm); ++k) {  // wave-uniform
+      const int t = (cm + k - 1) / k;
+      const long long n = count_at(t);
+      if (n > a.slots) continue;
+      const float cost = ring_piece_cost(n, t, cm);
+      if (T == 0 || cost < best) {
+        best = cost;
+        T = t;
+      }
+    }
+  }
+  if (T > 0) {
+    // chosen by the cost model
+  } else if (cmin == cmax) {
     // every unit alike: ceil(c / T) <= slots / units
     const int per_unit = (int)((long long)a.slots / ((long long)a.B * U));
     T = per_unit >= a.max_pieces ? 1 : max(1, (cmax + per_unit - 1) / per_unit);
   } else {
-    auto fits = [&](int t) {
-      long long n = wave_allsum_i(lane < a.B ? min(U * pieces_of(c0, t), a.slots + 1) : 0);
-      for (int b0 = 64; b0 < a.B && n <= a.slots; b0 += 64) {
-        int L;
-        bool bad;
-        const int c = block_chunks(b0, L, bad);
-        n += wave_allsum_i(b0 + lane < a.B ? min(U * pieces_of(c, t), a.slots + 1) : 0);
-      }
-      return n <= a.slots;
-    };
+    auto fits = [&](int t) { return count_at(t) <= a.slots; };
     int lo = 1, hi = max(cmax, 1);
     while (lo < hi) {  // wave-uniform
       const int mid = (lo + hi) >> 1;
@@ -688,7 +773,14 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // starts that piece before the lengths are read, and the plan reduces to
   // checking that every length is the full one.  Otherwise the started loads
   // are waited for and dropped, and the planner finds the piece.
-  const bool spec = a.full_pieces > 0 && a.B <= 64 && slot_w < a.B * a.Hkv * a.full_pieces;
+  // Only the first round of workgroups (one per CU) guesses: when the lengths
+  // are not the full ones the launch's later slots are mostly unused, and a
+  // guess there costs an unused workgroup its loads' latency (llama2-13b
+  // heads, four sequences of 2944 keys in a 8192-key cache: 60.8 us against
+  // 95.8 when every slot guesses), while a later workgroup that plans first
+  // starts about 1.5 us later at full length (62.7 against 61.1 us).
+  const bool spec = a.full_pieces > 0 && a.B <= 64 && slot_w < kNumCUs &&
+                    slot_w < a.B * a.Hkv * a.full_pieces;
   Piece pc{};
   if (spec) {
     pc.unit = slot_w / a.full_pieces;
@@ -704,9 +796,12 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   }
   const bool full = spec && wave_allmin_i(lane < a.B ? (kvl0 == Lcap ? 1 : 0) : 1) == 1;
   if (!full) {
-    if (spec) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // dropped
-    // slot -> piece (every wave finds it; the committed lengths decide it)
-    if (!plan_piece(a, slot_w, kvl0, pc)) return;
+    // slot -> piece (every wave finds it; the committed lengths decide it),
+    // while the guessed piece's loads are still in flight; they are waited
+    // for and dropped before the slot is used again or the wave ends
+    const bool used = plan_piece(a, slot_w, kvl0, pc);
+    if (spec) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!used) return;
     if (pc.bad && a.flags && pc.split == 0 && pc.kvh == 0 && tid == 0)
       atomicOr(a.flags + pc.b, EAGLE_FLAG_BAD_KV_LEN);
     start(pc, run_of(pc));
@@ -1114,9 +1209,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
 // from the group kernel through the workspace (scalar loads); the kernel
 // boundary makes them and the partials visible.  The first batch is loaded
 // for the pieces the unit has when every sequence fills the cache while the
-// piece table is read, and again only if the table disagrees.  Workgroup ids
-// are laid out so that a unit's workgroups run on the XCD whose slots held
-// its pieces in that case (slots are dealt to XCDs in equal consecutive runs).
+// piece table is read, and again only if the table disagrees.  A unit's
+// workgroups are consecutive ids of one XCD (ids go to the XCDs round robin),
+// the units spread evenly over the XCDs.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int RW, int units) {
   constexpr int C4 = D / 4;        // 16-byte columns per row
@@ -1231,19 +1326,19 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   const int cap_chunks = std::max(1, (Lmax - N + p.kg - 1) / p.kg);
   int pieces;
   if (kernel == 1) {
-    // One ring workgroup per CU (its LDS): workgroups beyond kNumCUs run in
-    // another round, so a half-empty last round costs as much as a full one.
-    // Pick the piece count s minimising rounds(s) * chunks per piece plus a
-    // combine cost of 1.75 chunk-times per piece (fitted on MI355X).
+    // The ring kernel's cost model at full cache length (the device applies
+    // the same one to the committed lengths, see plan_piece).
     pieces = 1;
     float best = 0.f;
-    for (int sc = 1; sc <= 16 && sc <= cap_chunks; ++sc) {
-      const long long slots = round8((long long)p.units * sc);
-      const int rounds = (int)((slots + kNumCUs - 1) / kNumCUs);
-      const float cost = (float)(rounds * ((cap_chunks + sc - 1) / sc)) + 1.75f * sc;
-      if (sc == 1 || cost < best) {
+    int bestT = 0;
+    for (int k = 1; k <= 16 && k <= cap_chunks; ++k) {
+      const int t = (cap_chunks + k - 1) / k;
+      const int s = std::min((cap_chunks + t - 1) / t, kMaxPiecesPerUnit);
+      const float cost = ring_piece_cost((long long)p.units * s, t, cap_chunks);
+      if (bestT == 0 || cost < best) {
         best = cost;
-        pieces = sc;
+        bestT = t;
+        pieces = s;
       }
     }
   } else {
@@ -1252,14 +1347,23 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
     // mixtral shape 2 pieces, 186.8 us against 220.7 at 3)
     pieces = (kNumCUs + round8(p.units) - 1) / round8(p.units);
   }
+  // the ring kernel's device planner applies the cost model to the committed
+  // lengths unless a test fixed the piece count
+  p.ring_cost = kernel == 1 && g_plan_override.pieces <= 0 ? 1 : 0;
   if (g_plan_override.pieces > 0) pieces = g_plan_override.pieces;
   pieces = std::max(1, std::min(pieces, std::min(cap_chunks, kMaxPiecesPerUnit)));
   p.slots = round8((long long)p.units * pieces);
-  // what the device planner gives every unit when all sequences fill the
-  // cache: the smallest piece T (in chunks) with units * ceil(C / T) <= slots
-  const int per_unit = p.slots / p.units;
-  const int T = per_unit >= kMaxPiecesPerUnit ? 1 : std::max(1, (cap_chunks + per_unit - 1) / per_unit);
-  p.full_pieces = std::max(1, std::min(kMaxPiecesPerUnit, (cap_chunks + T - 1) / T));
+  if (p.ring_cost) {
+    // at full length the device's cost model makes the same choice
+    p.full_pieces = pieces;
+  } else {
+    // what the device planner gives every unit when all sequences fill the
+    // cache: the smallest piece T (in chunks) with units * ceil(C / T) <= slots
+    const int per_unit = p.slots / p.units;
+    const int T =
+        per_unit >= kMaxPiecesPerUnit ? 1 : std::max(1, (cap_chunks + per_unit - 1) / per_unit);
+    p.full_pieces = std::max(1, std::min(kMaxPiecesPerUnit, (cap_chunks + T - 1) / T));
+  }
   return p;
 }
 
@@ -1353,6 +1457,7 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.kg = plan.kg;
   a.max_pieces = plan.max_pieces;
   a.full_pieces = Lmax > N ? plan.full_pieces : 0;
+  a.ring_cost = plan.ring_cost;
   a.scale_log2 = scale_log2;
   void* fn = plan.d == 64 ? attn_kernel<64>(plan.kernel, plan.rows_per_wg)
                           : attn_kernel<128>(plan.kernel, plan.rows_per_wg);
