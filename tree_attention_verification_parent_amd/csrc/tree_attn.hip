@@ -73,7 +73,31 @@ struct AttnArgs {
   int full_pieces;  // pieces per unit when every sequence fills the cache (see the ring kernel)
   int ring_cost;    // 1: pick the piece length by the ring kernel's cost model (else the smallest that fits)
   float scale_log2;
+  // multipliers for div_magic by full_pieces, Hkv, qgroups and G
+  uint32_t fp_magic, hkv_magic, qg_magic, g_magic;
+  int xcd_group;  // 1: a unit's full_pieces slots share one XCD (logical_slot)
 };
+
+// n / d without a division, for n * d <= 2^32: the high half of n * m with
+// m = floor((2^32 - 1) / d) + 1 = (2^32 + e) / d, 0 <= e < d, is
+// floor(n / d + n e / (d 2^32)), and n e < 2^32 keeps the added fraction
+// below the distance 1/d to the next integer (Granlund and Montgomery,
+// division by invariant integers).  d = 1 passes n through (m would need 33
+// bits).  The host computes m once per launch.
+__device__ __forceinline__ int div_magic(int n, uint32_t m, int d) {
+  return d == 1 ? n : (int)__umulhi((uint32_t)n, m);
+}
+__host__ inline uint32_t magic_of(int d) {
+  return d <= 1 ? 0u : (uint32_t)(0xffffffffull / (unsigned long long)d + 1ull);
+}
+
+// a * b / c for non-negative ints, in 32 bits when a * b fits (wave-uniform
+// operands: a uniform branch)
+__device__ __forceinline__ int mul_div(int a, int b, int c) {
+  const unsigned long long p = (unsigned long long)(unsigned)a * (unsigned)b;
+  if ((p >> 32) == 0) return (int)((uint32_t)p / (uint32_t)c);
+  return (int)(p / (unsigned long long)c);
+}
 
 // ---- decomposition -------------------------------------------------------------
 // A unit's piece: which (sequence, KV head, query group), which of its
@@ -83,11 +107,23 @@ struct Piece {
   bool bad;
 };
 
-// Slot of this workgroup: its id.  Workgroup ids go to the XCDs round robin,
-// so the used slots (0 .. pieces - 1 when the committed lengths leave some
-// unused) are spread over all XCDs; no piece relies on sharing an XCD with
-// another (the partials are merged through device-coherent memory).
-__device__ __forceinline__ int logical_slot(const AttnArgs& a) { return (int)blockIdx.x; }
+// Slot of this workgroup.  Workgroup ids go to the XCDs round robin (id mod
+// 8).  With xcd_group (the ring kernel, units a multiple of 8, slots = units
+// x full_pieces) id 8 (q P + p) + x takes piece p of unit 8 q + x, so that at
+// full length the P pieces of a unit run on one XCD: measured faster on
+// MI355X (llama2-7b shape 14.8 against 15.3 us, llama2-13b 62.8 against
+// 63.4), though nothing depends on it, since the partials meet through
+// device-coherent memory whatever the placement.  Otherwise the slot is the
+// id: the used slots (0 .. pieces - 1 when the committed lengths leave some
+// unused) spread over all XCDs.
+__device__ __forceinline__ int div_magic(int n, uint32_t m, int d);
+__device__ __forceinline__ int logical_slot(const AttnArgs& a) {
+  const int bid = (int)blockIdx.x;
+  if (!a.xcd_group) return bid;
+  const int x = bid & (kNumXCDs - 1), j = bid / kNumXCDs;
+  const int q = div_magic(j, a.fp_magic, a.full_pieces);
+  return (kNumXCDs * q + x) * a.full_pieces + (j - q * a.full_pieces);
+}
 
 // A wave-uniform 32-bit value read with a scalar load (constant address
 // space), which the compiler tracks apart from the vector loads in flight.
@@ -694,21 +730,23 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   };
 
   // The query rows of a unit (b, kvh): lane (c, g) holds row qb * 16 + c's
-  // 8 dims at ks * 32 + g * 8.
+  // 8 dims at ks * 32 + g * 8.  Rows past M load row 0 again: each query row
+  // is a column of its own through the MFMAs, the softmax and the fold, and
+  // those rows are never stored.  (Zeroing them with a select made the
+  // compiler wait for every load in flight at the start of a piece, the
+  // second chunk's included, before anything else.)
   bf16x8 qf[QBW][NKS];
   auto load_q = [&](int b, int kvh) {
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       const int row = qb * 16 + c;
-      const int rr = row < a.M ? row : 0;  // in range either way; zeroed below
-      const int i = rr / a.G;
+      const int rr = row < a.M ? row : 0;
+      const int i = div_magic(rr, a.g_magic, a.G);
       const int h = kvh * a.G + (rr - i * a.G);
       const uint16_t* qrow = a.q + (((size_t)b * a.N + i) * a.Hq + h) * D;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
-        qf[qb][ks] = row < a.M ? x : bf16x8{};
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
     }
   };
 
@@ -722,20 +760,22 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     const uint16_t* kp;
     const uint16_t* vp;
   };
-  auto run_of = [&](const Piece& p) {
+  // (cb, ce: the piece's chunks of [0, L))
+  auto run_at = [&](const Piece& p, int cb, int ce) {
     Run r;
     r.L = p.L;
-    const int n_chunks = (p.L + 31) / 32;
-    const int cb = (int)((long long)p.split * n_chunks / p.nsplit);
-    const int ce = (int)((long long)(p.split + 1) * n_chunks / p.nsplit);
     r.my_first = cb + wave;
-    r.my_n = r.my_first < ce ? (ce - r.my_first + NWAVE - 1) / NWAVE : 0;
+    r.my_n = r.my_first < ce ? (ce - r.my_first + NWAVE - 1) / NWAVE : 0;  // NWAVE: a power of 2
     r.tree_wave = p.split == p.nsplit - 1 && wave == (ce - cb) % NWAVE;
     r.my_chunks = r.my_n + (r.tree_wave ? (a.N + 31) / 32 : 0);
     const size_t kv_base = ((size_t)p.b * a.Hkv + p.kvh) * (size_t)a.Lmax * D;
     r.kp = a.k + kv_base;
     r.vp = a.v + kv_base;
     return r;
+  };
+  auto run_of = [&](const Piece& p) {
+    const int n_chunks = (p.L + 31) >> 5;
+    return run_at(p, mul_div(p.split, n_chunks, p.nsplit), mul_div(p.split + 1, n_chunks, p.nsplit));
   };
   auto chunk_key0 = [&](const Run& r, int i) {
     return i < r.my_n ? (r.my_first + NWAVE * i) * 32 : r.L + 32 * (i - r.my_n);
@@ -764,9 +804,6 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     }
   };
 
-  // The committed lengths, lane b holding sequence b's (a vector load issued
-  // first, so it completes before anything waited for later).
-  const int kvl0 = a.kv_len[min(lane, a.B - 1)];
   const int Lcap = a.Lmax - a.N;
   // When every sequence fills the cache (the common case) the planner gives
   // this slot piece slot % full_pieces of unit slot / full_pieces: the wave
@@ -779,12 +816,15 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // heads, four sequences of 2944 keys in a 8192-key cache: 60.8 us against
   // 95.8 when every slot guesses), while a later workgroup that plans first
   // starts about 1.5 us later at full length (62.7 against 61.1 us).
-  const bool spec = a.full_pieces > 0 && a.B <= 64 && slot_w < kNumCUs &&
+  const bool spec = a.full_pieces > 0 && a.B <= 64 && (int)blockIdx.x < kNumCUs &&
                     slot_w < a.B * a.Hkv * a.full_pieces;
+  // (no division on the way to the first loads: a wave issues them about
+  // 0.5 us sooner at the llama2-7b shape than with the divisions)
   Piece pc{};
+  Run R{};
   if (spec) {
-    pc.unit = slot_w / a.full_pieces;
-    pc.b = pc.unit / a.Hkv;
+    pc.unit = div_magic(slot_w, a.fp_magic, a.full_pieces);
+    pc.b = div_magic(pc.unit, a.hkv_magic, a.Hkv);
     pc.kvh = pc.unit - pc.b * a.Hkv;
     pc.qgroup = 0;
     pc.nsplit = a.full_pieces;
@@ -792,8 +832,15 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     pc.first = pc.unit * a.full_pieces;
     pc.L = Lcap;
     pc.bad = false;
-    start(pc, run_of(pc));
+    const int n_chunks = (Lcap + 31) >> 5;
+    R = run_at(pc, div_magic(pc.split * n_chunks, a.fp_magic, a.full_pieces),
+               div_magic((pc.split + 1) * n_chunks, a.fp_magic, a.full_pieces));
+    start(pc, R);
   }
+  // The committed lengths, lane b holding sequence b's, read once the guess's
+  // loads are issued: scalar loads for B <= 16, so that waiting for them does
+  // not wait for those vector loads (vector loads complete in order).
+  const int kvl0 = kv_len_lanes(a);
   const bool full = spec && wave_allmin_i(lane < a.B ? (kvl0 == Lcap ? 1 : 0) : 1) == 1;
   if (!full) {
     // slot -> piece (every wave finds it; the committed lengths decide it),
@@ -804,9 +851,9 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     if (!used) return;
     if (pc.bad && a.flags && pc.split == 0 && pc.kvh == 0 && tid == 0)
       atomicOr(a.flags + pc.b, EAGLE_FLAG_BAD_KV_LEN);
-    start(pc, run_of(pc));
+    R = run_of(pc);
+    start(pc, R);
   }
-  const Run R = run_of(pc);
   const int b = pc.b, kvh = pc.kvh, L = pc.L;
   const bool bad = pc.bad;
   const int my_n = R.my_n, my_chunks = R.my_chunks;
@@ -1062,21 +1109,23 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_group_kernel(AttnArgs a)
   // As in the ring kernel: the first tiles of the piece this slot would hold
   // if every sequence filled the cache go out before the plan is known, and
   // are kept only if the real plan agrees (else waited for and discarded).
-  const int kvl0 = kv_len_lanes(a);
+  // (no division before those loads, and the lengths read after them)
   const int Lcap = a.Lmax - a.N;
   const int cap_tiles = (Lcap + S::TILE_KEYS - 1) / S::TILE_KEYS;
   const int U = a.Hkv * a.qgroups;
   int spec_unit = -1, spec_split = 0, spec_n = 0;
   if (a.full_pieces > 0 && slot_w < a.B * U * a.full_pieces) {
-    spec_unit = slot_w / a.full_pieces;
+    spec_unit = div_magic(slot_w, a.fp_magic, a.full_pieces);
     spec_split = slot_w - spec_unit * a.full_pieces;
-    const int stb = (int)((long long)spec_split * cap_tiles / a.full_pieces);
-    const int ste = (int)((long long)(spec_split + 1) * cap_tiles / a.full_pieces);
+    const int stb = div_magic(spec_split * cap_tiles, a.fp_magic, a.full_pieces);
+    const int ste = div_magic((spec_split + 1) * cap_tiles, a.fp_magic, a.full_pieces);
     spec_n = min(NBUF - 1, ste - stb);
-    const size_t sbase = (size_t)(spec_unit / a.qgroups) * (size_t)a.Lmax * D;  // pair b * Hkv + kvh
+    const int pair = div_magic(spec_unit, a.qg_magic, a.qgroups);  // b * Hkv + kvh
+    const size_t sbase = (size_t)pair * (size_t)a.Lmax * D;
     for (int j = 0; j < spec_n; ++j)
       issue_tile_at(a.k + sbase, a.v + sbase, j, (stb + j) * S::TILE_KEYS, Lcap - 1);
   }
+  const int kvl0 = kv_len_lanes(a);
   Piece u;
   if (!plan_piece(a, slot_w, kvl0, u)) {
     if (spec_n > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1458,6 +1507,25 @@ hipError_t launch_tree_attn(const AttnPlan& plan, const uint16_t* q, const uint1
   a.max_pieces = plan.max_pieces;
   a.full_pieces = Lmax > N ? plan.full_pieces : 0;
   a.ring_cost = plan.ring_cost;
+  {
+    // the guessed piece's quotients by div_magic need n * d <= 2^32: slot and
+    // piece bounds times the piece count, the unit times Hkv or qgroups
+    const long long P = std::max(1, a.full_pieces);
+    const long long cap = (long long)(Lmax - N) + 64;  // keys (chunks or tiles are fewer)
+    const long long units = (long long)B * Hkv * plan.qgroups;
+    const long long lim = 1ll << 32;
+    if ((long long)plan.slots * P > lim || cap * P * P > lim ||
+        units * std::max(Hkv, plan.qgroups) > lim)
+      a.full_pieces = 0;  // plan first instead of guessing
+  }
+  a.fp_magic = magic_of(a.full_pieces);
+  a.hkv_magic = magic_of(Hkv);
+  a.qg_magic = magic_of(plan.qgroups);
+  a.g_magic = magic_of(plan.G);
+  a.xcd_group = plan.kernel == 1 && a.full_pieces > 1 && plan.units % kNumXCDs == 0 &&
+                        (long long)plan.slots == (long long)plan.units * a.full_pieces
+                    ? 1
+                    : 0;
   a.scale_log2 = scale_log2;
   void* fn = plan.d == 64 ? attn_kernel<64>(plan.kernel, plan.rows_per_wg)
                           : attn_kernel<128>(plan.kernel, plan.rows_per_wg);
