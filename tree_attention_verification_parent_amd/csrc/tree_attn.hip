@@ -789,7 +789,7 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // complete in order: the rows land before the chunk that needs them, and
   // the first chunk can be waited for with the second's loads outstanding.
   u32x4 pre[2 * LPM];
-  auto start = [&](const Piece& p, const Run& r) {
+  auto start = [&](const Piece& p, const Run& r) __attribute__((always_inline)) {
     load_q(p.b, p.kvh);
     if (r.my_chunks > 0) issue_keys_at(r.kp, r.vp, chunk_key0(r, 0), chunk_kmax(r, 0));
     if (r.my_chunks >= 2) {
@@ -816,13 +816,15 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
   // heads, four sequences of 2944 keys in a 8192-key cache: 60.8 us against
   // 95.8 when every slot guesses), while a later workgroup that plans first
   // starts about 1.5 us later at full length (62.7 against 61.1 us).
-  const bool spec = a.full_pieces > 0 && a.B <= 64 && (int)blockIdx.x < kNumCUs &&
-                    slot_w < a.B * a.Hkv * a.full_pieces;
+  // A later workgroup still takes the closed form once the lengths are known
+  // to be the full ones, instead of planning.
+  const bool guessable = a.full_pieces > 0 && a.B <= 64 && slot_w < a.B * a.Hkv * a.full_pieces;
+  const bool spec = guessable && (int)blockIdx.x < kNumCUs;
   // (no division on the way to the first loads: a wave issues them about
   // 0.5 us sooner at the llama2-7b shape than with the divisions)
   Piece pc{};
   Run R{};
-  if (spec) {
+  auto guess = [&]() __attribute__((always_inline)) {
     pc.unit = div_magic(slot_w, a.fp_magic, a.full_pieces);
     pc.b = div_magic(pc.unit, a.hkv_magic, a.Hkv);
     pc.kvh = pc.unit - pc.b * a.Hkv;
@@ -835,13 +837,16 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     const int n_chunks = (Lcap + 31) >> 5;
     R = run_at(pc, div_magic(pc.split * n_chunks, a.fp_magic, a.full_pieces),
                div_magic((pc.split + 1) * n_chunks, a.fp_magic, a.full_pieces));
+  };
+  if (spec) {
+    guess();
     start(pc, R);
   }
   // The committed lengths, lane b holding sequence b's, read once the guess's
   // loads are issued: scalar loads for B <= 16, so that waiting for them does
   // not wait for those vector loads (vector loads complete in order).
   const int kvl0 = kv_len_lanes(a);
-  const bool full = spec && wave_allmin_i(lane < a.B ? (kvl0 == Lcap ? 1 : 0) : 1) == 1;
+  const bool full = guessable && wave_allmin_i(lane < a.B ? (kvl0 == Lcap ? 1 : 0) : 1) == 1;
   if (!full) {
     // slot -> piece (every wave finds it; the committed lengths decide it),
     // while the guessed piece's loads are still in flight; they are waited
@@ -852,8 +857,10 @@ __global__ __launch_bounds__(S::THREADS) void tree_attn_ring_kernel(AttnArgs a) 
     if (pc.bad && a.flags && pc.split == 0 && pc.kvh == 0 && tid == 0)
       atomicOr(a.flags + pc.b, EAGLE_FLAG_BAD_KV_LEN);
     R = run_of(pc);
-    start(pc, R);
+  } else if (!spec) {
+    guess();
   }
+  if (!(full && spec)) start(pc, R);
   const int b = pc.b, kvh = pc.kvh, L = pc.L;
   const bool bad = pc.bad;
   const int my_n = R.my_n, my_chunks = R.my_chunks;
