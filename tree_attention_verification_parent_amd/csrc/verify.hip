@@ -248,15 +248,22 @@ __device__ __forceinline__ void load_row(Row<BLOCK, NPT>& r, const float* src, i
       r.v[k] = in ? x : make_float4(pad, pad, pad, pad);
     }
   } else {
+    // one-dword buffer loads (the row need not be 16-byte aligned): offsets
+    // from the thread id and immediates, so no per-entry address registers;
+    // dwords past len read 0 and are then set to pad
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (size_t)len * 4);
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int e0 = (k * BLOCK + tid) * 4;
-      const float x0 = src[min(e0 + 0, len - 1)], x1 = src[min(e0 + 1, len - 1)];
-      const float x2 = src[min(e0 + 2, len - 1)], x3 = src[min(e0 + 3, len - 1)];
-      r.v[k].x = e0 + 0 < len ? x0 : pad;
-      r.v[k].y = e0 + 1 < len ? x1 : pad;
-      r.v[k].z = e0 + 2 < len ? x2 : pad;
-      r.v[k].w = e0 + 3 < len ? x3 : pad;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (e0 + e) * 4, 0, 0));
+      if ((k + 1) * BLOCK * 4 > len) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = e0 + e < len ? x[e] : pad;
+      }
+      r.v[k] = make_float4(x[0], x[1], x[2], x[3]);
     }
   }
 }
@@ -1004,13 +1011,16 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
+    // p = U / C through one fp64 reciprocal (within an fp64 ulp of the
+    // quotient, far below the fp32 result's rounding)
     float* po = a.out_probs + (ob + j) * V;
+    const double inv = 1.0 / C;
 #pragma unroll
     for (int k = 0; k < NPT; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = (k * BLOCK + tid) * 4 + e;
-        if (idx < V) po[idx] = GREEDY ? (idx == am ? 1.f : 0.f) : (float)((double)comp(U.v[k], e) / C);
+        if (idx < V) po[idx] = GREEDY ? (idx == am ? 1.f : 0.f) : (float)((double)comp(U.v[k], e) * inv);
       }
   }
 
@@ -1135,12 +1145,13 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
       } else {
         run_chain<BLOCK, NPT, VEC, false>(a, ob, U, Q, C, ut, val, cd, sh.nk, false, sh, qlds, rb);
       }
+      const double inv = 1.0 / C;
 #pragma unroll
       for (int k = 0; k < NPT; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int idx = (k * BLOCK + tid) * 4 + e;
-          if (idx < V) fo[idx] = (float)((double)comp(U.v[k], e) / C);
+          if (idx < V) fo[idx] = (float)((double)comp(U.v[k], e) * inv);
         }
     }
   }
