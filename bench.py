@@ -19,8 +19,10 @@ one JSON line on stdout.
 `--pmc-capture` runs the same steps eagerly (no graph) followed by a
 calibration copy of known size, for rocprofv3 counter passes; it prints one
 JSON line naming what it ran and does not time anything.  `--profile
-attn:<config>` / `--profile dtree` run the tree attention at another
-configuration, or the EAGLE-2 tree build, eagerly for a kernel trace.
+attn:<config>[:<lens>[:<cache>]]` / `--profile verify:<config>[:T]` /
+`--profile dtree` run the tree attention at another configuration (or on a
+batch of given committed lengths), the verification alone, or the EAGLE-2
+tree build, eagerly for a kernel trace.
 `--oracle-configs` times the CPU oracle per configuration and stage (no GPU
 work) and prints one JSON line.  `--per-config` times the step, the attention
 and the verify launch at every configuration and listed temperature (and the
@@ -335,7 +337,9 @@ def profile_run(torch, ev, W, name, steps):
     """Eager launches of one workload for rocprofv3 (nothing is timed here):
     `attn:<config>` runs the tree attention with the mask built in at that
     configuration, rotating input copies as the timed runs do, then the
-    calibration copy for counter passes; `verify:<config>[:T]` runs the
+    calibration copy for counter passes; `attn:<config>:<lens>[:<cache>]`
+    runs it on a batch of the given committed lengths (comma-separated) at
+    the config's heads in a cache of that many slots plus N; `verify:<config>[:T]` runs the
     verification with fused compaction the same way (T defaults to the
     config's last listed temperature); `dtree` runs the EAGLE-2 tree build at
     the mixtral-eagle2 shape."""
@@ -351,6 +355,16 @@ def profile_run(torch, ev, W, name, steps):
         st = Step(s, torch, ev, copies)
         for i in range(steps):
             st.verify(i)
+        torch.cuda.synchronize()
+    elif name.startswith("attn:") and name.count(":") >= 2:
+        # attn:<config>:<len,len,...>[:<cache len>] -- a batch of those
+        # committed lengths at the config's heads (cache: the longest length)
+        parts = name.split(":")
+        lens = [int(x) for x in parts[2].split(",")]
+        cap = int(parts[3]) if len(parts) > 3 else max(lens)
+        _, run = ragged_attention(torch, ev, W, parts[1], lens, cap)
+        for i in range(steps):
+            run(i)
         torch.cuda.synchronize()
     elif name.startswith("attn:"):
         cfg = W.get(name[5:])
@@ -520,42 +534,51 @@ def ragged_timing(torch, ev, W, steps):
     at the llama2-13b heads (ring kernel) and the llama2-70b heads (group
     kernel).  Graph-timed, rotating input copies as the timed runs do."""
     rows = []
-    dev = torch.device("cuda")
     for name in ("llama2-13b", "llama2-70b-gqa"):
-        base = W.shrink(W.get(name), B=4)
         for lens, cap in (([512, 1024, 2048, 8192], 8192), ([8192] * 4, 8192),
                           ([2944] * 4, 8192), ([2944] * 4, 2944)):
-            Lmax = cap + base.N
-            s = W.make_step(base, base.temperatures[-1], kv_lens=lens, with_attention=False)
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(5)
-            B, N = base.B, base.N
-            kvb = B * base.Hkv * Lmax * base.d * 2 * 2
-            copies = max(2, math.ceil(ROTATE_BYTES / kvb))
-            slots = []
-            for _ in range(copies):
-                q = torch.randn((B, N, base.Hq, base.d), device=dev, generator=gen).to(torch.bfloat16)
-                k = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
-                v = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
-                slots.append((q, k, v))
-            parents = torch.from_numpy(s.parents).to(dev)
-            kv_len = torch.from_numpy(s.kv_len).to(dev)
-            ws = ev.alloc_workspace(ev.tree_attn_workspace_bytes(B, N, base.Hq, base.Hkv, base.d, Lmax))
-            out = torch.empty_like(slots[0][0])
-
-            def run(i):
-                qq, kk, vv = slots[i % copies]
-                ev.tree_attn_parents(qq, kk, vv, kv_len, parents, out=out, workspace=ws)
+            base, run = ragged_attention(torch, ev, W, name, lens, cap)
             g = graph_of(torch, run, steps)
             time_graph(torch, g)
             t = min(time_graph(torch, g) / steps for _ in range(3))
-            nbytes = sum(base.Hkv * (L + N) * base.d * 4 for L in lens)
+            nbytes = sum(base.Hkv * (L + base.N) * base.d * 4 for L in lens)
             rows.append({"heads": name, "kv_len": lens, "cache_len": cap, "sum_kv_len": sum(lens),
                          "us": t * 1e6, "kv_bytes": nbytes, "TB_per_s": nbytes / t / 1e12})
             log(f"[bench] ragged {json.dumps(rows[-1])}")
-            del slots, g, ws
+            del g, run
             torch.cuda.empty_cache()
     return {"ragged": rows, "steps": steps}
+
+
+def ragged_attention(torch, ev, W, name, lens, cap):
+    """The tree attention (mask built in) of one batch: the heads of config
+    `name`, B = len(lens) sequences with committed lengths `lens` in a cache
+    of cap + N slots, random bf16 Q/K/V in enough copies to rotate through
+    1 GiB.  Returns (config, run(i)), run launching on copy i mod copies."""
+    dev = torch.device("cuda")
+    base = W.shrink(W.get(name), B=len(lens))
+    Lmax = cap + base.N
+    s = W.make_step(base, base.temperatures[-1], kv_lens=lens, with_attention=False)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    B, N = base.B, base.N
+    kvb = B * base.Hkv * Lmax * base.d * 2 * 2
+    copies = max(2, math.ceil(ROTATE_BYTES / kvb))
+    slots = []
+    for _ in range(copies):
+        q = torch.randn((B, N, base.Hq, base.d), device=dev, generator=gen).to(torch.bfloat16)
+        k = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
+        v = torch.randn((B, base.Hkv, Lmax, base.d), device=dev, generator=gen).to(torch.bfloat16)
+        slots.append((q, k, v))
+    parents = torch.from_numpy(s.parents).to(dev)
+    kv_len = torch.from_numpy(s.kv_len).to(dev)
+    ws = ev.alloc_workspace(ev.tree_attn_workspace_bytes(B, N, base.Hq, base.Hkv, base.d, Lmax))
+    out = torch.empty_like(slots[0][0])
+
+    def run(i):
+        qq, kk, vv = slots[i % copies]
+        ev.tree_attn_parents(qq, kk, vv, kv_len, parents, out=out, workspace=ws)
+    return base, run
 
 
 def pmc_traffic(attn_bytes):
@@ -581,8 +604,8 @@ def main():
     ap.add_argument("--oracle-configs", action="store_true",
                     help="time the CPU oracle per configuration and stage, print one JSON line")
     ap.add_argument("--profile", default=None,
-                    help="attn:<config>, verify:<config>[:T] or dtree: eager launches for a "
-                         "rocprofv3 trace")
+                    help="attn:<config>[:<lens>[:<cache>]], verify:<config>[:T] or dtree: "
+                         "eager launches for a rocprofv3 trace")
     ap.add_argument("--ragged", action="store_true",
                     help="time the tree attention on a ragged batch against equal-length "
                          "batches, print one JSON line")
