@@ -588,11 +588,17 @@ __device__ __forceinline__ void residual_row(const Row<BLOCK, NPT>& U, const Row
 // sum U; on a rejection S <- S + C and C <- F(S) (kept if F(S) = 0, as the
 // step-by-step form keeps the previous row).  Returns the accepted
 // candidate's index or -1; S and C describe the adjusted row afterwards.
+// With stop_at_accept (the walk's chain, whose row is then only drawn from)
+// the last candidate's rejection skips the pass for F: S becomes S + C and
+// Sprev keeps the previous S, C is left stale, and the draw, which sums the
+// row itself, goes back to Sprev if the row at S has no mass (the sums are
+// of non-negative entries: zero exactly when F would be).
 template <int BLOCK, int NPT, bool RATIO>
 __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
-                                                double& S, double& C, const Cand& cd, int nk,
-                                                bool stop_at_accept, Shared<BLOCK, NPT>& sh,
+                                                double& S, double& Sprev, double& C, const Cand& cd,
+                                                int nk, bool stop_at_accept, Shared<BLOCK, NPT>& sh,
                                                 int& rb) {
+  Sprev = S;
   const int tid = threadIdx.x;
 #pragma nounroll
   for (int s = 0; s < nk; ++s) {
@@ -608,6 +614,11 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
       sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
     if (stop_at_accept && accept) return s;
     const double Sn = S + C;
+    if (stop_at_accept && s == nk - 1) {
+      Sprev = S;
+      S = Sn;
+      return -1;
+    }
     const double Cn = residual_mass<BLOCK, NPT>(U, Q, Sn, sh, rb);
     if (Cn > 0.0) {
       S = Sn;
@@ -740,8 +751,8 @@ __device__ __forceinline__ double wave_incl_scan_d(double v) {
 // prefix, which ends exactly at the group's sum.  Where the levels' fp64
 // roundings leave no crossing inside the chosen lane group (a window of about
 // 1e-16 of the mass), or u rounds to the whole mass, the last entry with mass
-// in the chosen range (else the row) is taken.  `scratch` holds
-// NPT * BLOCK floats and NPT * 64 doubles of free LDS.
+// in the chosen range (else the row) is taken; a row without mass gives -1.
+// `scratch` holds NPT * BLOCK floats and NPT * 64 doubles of free LDS.
 template <int BLOCK, int NPT, typename E>
 __device__ __forceinline__ int inverse_cdf(E&& ent, float u, int V, Shared<BLOCK, NPT>& sh,
                                            void* scratch, int& rb) {
@@ -837,8 +848,7 @@ __device__ __forceinline__ int inverse_cdf(E&& ent, float u, int V, Shared<BLOCK
         if (idx < V && comp(w, c) > 0.f) last = idx;
       }
     }
-    pick = block_max_i<BLOCK, NPT>(last, sh, rb);
-    if (pick < 0) pick = 0;
+    pick = block_max_i<BLOCK, NPT>(last, sh, rb);  // -1: the row has no mass
   }
   return pick;
 }
@@ -1039,18 +1049,25 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   } else {
     int si;
     if (shared) {
-      double S = 0.0;
-      si = run_chain_shared<BLOCK, NPT, PARITY>(U, Q, S, C, cd, nk, true, sh, rb);
+      double S = 0.0, Sprev = 0.0;
+      si = run_chain_shared<BLOCK, NPT, PARITY>(U, Q, S, Sprev, C, cd, nk, true, sh, rb);
       if (si < 0) {  // the final token from the adjusted row, computed on the fly
         float hs, ls;
         split_s<BLOCK, NPT>(S, hs, ls);
         bonus = inverse_cdf<BLOCK, NPT>(
             [&](int k) { return residual4(U.v[k], Q.v[k], hs, ls); }, sh.u[0], V, sh, qlds, rb);
+        if (bonus < 0 && nk > 0) {  // the last rejection left no mass: the row before it
+          split_s<BLOCK, NPT>(Sprev, hs, ls);
+          bonus = inverse_cdf<BLOCK, NPT>(
+              [&](int k) { return residual4(U.v[k], Q.v[k], hs, ls); }, sh.u[0], V, sh, qlds, rb);
+        }
+        bonus = max(bonus, 0);
       }
     } else {
       si = run_chain<BLOCK, NPT, VEC, PARITY>(a, ob, U, Q, C, ut, val, cd, nk, true, sh, qlds, rb);
       if (si < 0)
-        bonus = inverse_cdf<BLOCK, NPT>([&](int k) { return U.v[k]; }, sh.u[0], V, sh, qlds, rb);
+        bonus = max(0, inverse_cdf<BLOCK, NPT>([&](int k) { return U.v[k]; }, sh.u[0], V, sh, qlds,
+                                               rb));
     }
     if (si >= 0) {
       acc = sh.kids[si];
@@ -1140,7 +1157,8 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
                                          sh, qlds, rb);
       if (shared) {
         double S = 0.0;
-        run_chain_shared<BLOCK, NPT, false>(U, Q, S, C, cd, sh.nk, false, sh, rb);
+        double Sprev = 0.0;
+        run_chain_shared<BLOCK, NPT, false>(U, Q, S, Sprev, C, cd, sh.nk, false, sh, rb);
         residual_row<BLOCK, NPT>(U, Q, S, U);
       } else {
         run_chain<BLOCK, NPT, VEC, false>(a, ob, U, Q, C, ut, val, cd, sh.nk, false, sh, qlds, rb);
