@@ -94,7 +94,6 @@ struct VArgs {
   int N, V;
   int nodes;  // B * N
   int P;      // workgroups per node (T = 0 split argmax)
-  int guess_row;  // issue each node's own draft row with its logits (see the node kernel)
   float T;
 };
 
@@ -364,12 +363,14 @@ __device__ __forceinline__ void row_argmax(const Row<BLOCK, NPT>& U, float& mx, 
 
 // Target row statistics of one node from its logits (already in U): T = 0
 // returns the lowest-index argmax; T > 0 turns U into exp((l - max)/T) and
-// returns its mass in C.  before_sum(m, unit, invT) runs before the mass
-// reduction, whose barrier publishes what it writes to LDS.
-template <int BLOCK, int NPT, bool GREEDY, typename F>
+// returns its mass in C.  after_max() runs once the row's maximum is known
+// (U has arrived: loads it issues no longer share the CU's bandwidth with
+// U's); before_sum(m, unit, invT) runs before the mass reduction, whose
+// barrier publishes what it writes to LDS.
+template <int BLOCK, int NPT, bool GREEDY, typename G, typename F>
 __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
-                                            double& C, F&& before_sum, Shared<BLOCK, NPT>& sh,
-                                            int& rb) {
+                                            double& C, G&& after_max, F&& before_sum,
+                                            Shared<BLOCK, NPT>& sh, int& rb) {
   sanitize_logits<BLOCK, NPT>(U, b, flags);
   if constexpr (GREEDY) {
     float mx;
@@ -383,6 +384,7 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
     for (int k = 0; k < NPT; ++k)
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
     const float m = block_max<BLOCK, NPT>(lm, sh, rb);
+    after_max();
     const bool unit = T == 1.f;
     const float invT = 1.f / T;
     float s[NPT];
@@ -629,9 +631,12 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
 }
 
 // Set-up of one node's chain after the tree is in LDS and the node's logits
-// were issued into U (and, with q_guess, the node's own draft row into Q):
-// its children (sh.kids, and per lane in cd), whether they share one draft
-// row (`shared`) and then that row into Q, or else the
+// were issued into U: its children (sh.kids, and per lane in cd), whether
+// they share one draft row (`shared`) and then that row into Q, issued once U
+// has arrived: the stats, which need all of U first, no longer wait for a
+// second row sharing the CU's bandwidth, and the row still lands in time for
+// the chain (whole verification, 32000-entry vocabulary: 26.3 -> 25.1 us at
+// 1 x 26 nodes, 21.4 -> 17.8 us at 8 x 26, 63.6 -> 57.2 us at 16 x 60); or else the
 // first candidate's row prefetch and the table qt[k][i] = q_{kid k}(t_{kid i});
 // each candidate's own logit (gathered while the row pass runs), then the row
 // statistics.  Returns the argmax (T = 0); sets C, ut (U at the first
@@ -639,7 +644,7 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
 template <int BLOCK, int NPT, bool GREEDY, bool VEC>
 __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, int b,
                                           int32_t* flags, Row<BLOCK, NPT>& U,
-                                          Row<BLOCK, NPT>& Q, bool q_guess, double& C, float& ut,
+                                          Row<BLOCK, NPT>& Q, double& C, float& ut,
                                           float& val, Cand& cd, bool& shared,
                                           Shared<BLOCK, NPT>& sh, float4* qlds, int& rb) {
   const int tid = threadIdx.x, lane = tid & 63, V = a.V;
@@ -650,7 +655,8 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
   val = 0.f;
   shared = false;
   if constexpr (GREEDY) {
-    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, [](float, bool, float) {}, sh, rb);
+    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, [] {}, [](float, bool, float) {}, sh,
+                                          rb);
   } else {
     cd.kid = 0;
     cd.tok = -1;
@@ -668,14 +674,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
     const int r0 = lane_i(cd.row, 0);
     shared = nk > 0 && __ballot(lane < nk && cd.row != r0) == 0;  // wave-uniform
     if (shared) {
-      // the one draft row (unless already guessed right), and each
-      // candidate's probability in it
-      if (!(q_guess && r0 == node)) {
-        if constexpr (VEC)
-          load_row_vec<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
-        else
-          load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
-      }
+      // each candidate's probability in the one draft row
       if (cd.tok >= 0) cd.q = a.draft[(ob + r0) * V + cd.tok];
     } else if (nk > 0 && VEC) {
       // slots past V are never loaded: zero this thread's (the pass reads them)
@@ -702,6 +701,14 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
     if (cd.tok >= 0) lt = a.logits[(ob + node) * V + cd.tok];
     target_stats<BLOCK, NPT, false>(
         U, a.T, b, flags, C,
+        [&] {
+          if (shared) {
+            if constexpr (VEC)
+              load_row_vec<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+            else
+              load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
+          }
+        },
         [&](float m, bool unit, float invT) {
           if (!shared) {
 #pragma unroll
@@ -993,31 +1000,23 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   int rb = 0;
 
   // the tree's few loads first, then the node's logit row (vector loads
-  // complete in order: the tree is not held up behind the row), and, when the
-  // batch is small enough to be latency-bound, the draft row the node's
-  // children most likely share (its own, when siblings name their parent's
-  // row) before the children are known
+  // complete in order: the tree is not held up behind the row)
   const TreeRegs tr = fetch_tree(a, b);
   asm volatile("" ::: "memory");
   Row<BLOCK, NPT> U;
   Row<BLOCK, NPT> Q;  // the shared draft row, or the second row of the step-by-step chain
-  const bool q_guess = !GREEDY && a.guess_row;
-  if constexpr (VEC) {
+  if constexpr (VEC)
     load_row_vec<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
-    // without the guess the buffer is empty: no memory is read
-    if constexpr (!GREEDY) load_row_vec<BLOCK, NPT>(Q, a.draft + (ob + j) * V, q_guess ? V : 0, 0.f);
-  } else {
+  else
     load_row<BLOCK, NPT>(U, a.logits + (ob + j) * V, V, -FLT_MAX);
-    if (q_guess) load_row<BLOCK, NPT>(Q, a.draft + (ob + j) * V, V, 0.f);
-  }
   store_tree<BLOCK, NPT>(a, b, tr, j == 0, sh);
   barrier_lds();
   double C = 1.0;
   float ut = 0.f, val = 0.f;
   Cand cd{0, -1, 0, 0.f, 0.f, 0.f};
   bool shared;
-  const int am = node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, Q, q_guess, C, ut, val,
-                                                     cd, shared, sh, qlds, rb);
+  const int am = node_setup<BLOCK, NPT, GREEDY, VEC>(a, ob, j, b, a.flags, U, Q, C, ut, val, cd,
+                                                     shared, sh, qlds, rb);
   const int nk = sh.nk;
 
   if (PARITY && a.out_probs) {
@@ -1153,8 +1152,8 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
         load_row_vec<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
       else
         load_row<BLOCK, NPT>(U, a.logits + (ob + term) * V, V, -FLT_MAX);
-      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, Q, false, C, ut, val, cd, shared,
-                                         sh, qlds, rb);
+      node_setup<BLOCK, NPT, false, VEC>(a, ob, term, b, nullptr, U, Q, C, ut, val, cd, shared, sh,
+                                         qlds, rb);
       if (shared) {
         double S = 0.0;
         double Sprev = 0.0;
@@ -1364,7 +1363,6 @@ hipError_t launch_verify(const VerifyPlan& plan, const int32_t* tokens, const fl
   a.P = plan.parts;
   // a small batch is latency-bound: fetching a row that turns out unused
   // (a leaf's) costs bandwidth, not time
-  a.guess_row = draft_row != nullptr && nodes <= (size_t)kNumCUs ? 1 : 0;
   a.T = T;
   const unsigned grid = (unsigned)nodes;
   const bool greedy = T == 0.f;
