@@ -28,7 +28,7 @@ struct AttnPlan {
   int kg;          // keys per planning chunk
   int max_pieces;  // pieces per unit at most
   int full_pieces; // pieces per unit the device gives when every sequence fills the cache
-  int ring_cost;   // 1: the device picks pieces by the ring kernel's cost model
+  int ring_cost;   // 1: the device picks pieces by the ring kernel's order of decompositions
 };
 
 // Test-only: force the kernel (0 planner, 1 ring, 2 group) and the pieces per

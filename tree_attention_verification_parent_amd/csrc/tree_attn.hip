@@ -71,7 +71,7 @@ struct AttnArgs {
   int32_t* flags;
   int B, N, Hq, Hkv, Lmax, G, M, qgroups, slots, kg, max_pieces;
   int full_pieces;  // pieces per unit when every sequence fills the cache (see the ring kernel)
-  int ring_cost;    // 1: pick the piece length by the ring kernel's cost model (else the smallest that fits)
+  int ring_cost;    // 1: pick the piece length by the ring kernel's order (else the smallest that fits)
   float scale_log2;
   // multipliers for div_magic by full_pieces, Hkv, qgroups and G
   uint32_t fp_magic, hkv_magic, qg_magic, g_magic;
@@ -160,18 +160,27 @@ __device__ __forceinline__ int wave_allsum_i(int v) {
   return (lane_i(v, 0) + lane_i(v, 16)) + (lane_i(v, 32) + lane_i(v, 48));
 }
 
-// The ring kernel's cost of a decomposition, in chunk-times: pieces of at
-// most T chunks, n_pieces of them in all, the longest sequence cut into
-// ceil(cmax / T) pieces.  A ring workgroup fills its CU's LDS, so workgroups
-// beyond the CU count run in another round that costs as much as a full one;
-// each piece of a unit adds a merge cost of 1.75 chunk-times (fitted on
-// MI355X).  The host (at full cache length) and the device (at the committed
-// lengths) evaluate the same expression, so at full length both choose the
-// same pieces.
-__host__ __device__ inline float ring_piece_cost(long long n_pieces, int T, int cmax) {
+// The ring kernel's order of decompositions (pieces of at most T chunks,
+// n_pieces of them in all, the longest sequence of cmax chunks): first the
+// fewest rounds of workgroups (a ring workgroup fills its CU's LDS, so
+// workgroups beyond the CU count wait for a whole round), then the shortest
+// piece, but no shorter than 8 chunks, one per wave (a shorter piece leaves
+// waves idle and only adds partials to combine).  Within one round a shorter
+// piece puts more CUs on the stream; measured on MI355X against the earlier
+// model (a round costing T chunk-times, each piece 1.75 more for its merge,
+// which took more pieces over two rounds): llama2-13b 61.8 -> 59.4 us with
+// one piece per head instead of three, four 8192-key sequences 128.8 ->
+// 106.1, a ragged batch of 512, 1024, 2048, 8192 keys 63.0 -> 52.4, the
+// llama2-7b shape 15.2 -> 14.8 with 8 pieces of 8 chunks instead of 6 of 11.
+// The host (at full cache length) and the device (at the committed lengths)
+// apply the same order, so at full length both choose the same pieces.
+__host__ __device__ inline int ring_rounds(long long n_pieces) {
   const long long slots = (n_pieces + kNumXCDs - 1) / kNumXCDs * kNumXCDs;
-  const long long rounds = (slots + kNumCUs - 1) / kNumCUs;
-  return (float)(rounds * T) + 1.75f * (float)((cmax + T - 1) / T);
+  return (int)((slots + kNumCUs - 1) / kNumCUs);
+}
+__host__ __device__ inline int ring_piece_len(int T, int cmax) {
+  const int floor8 = cmax < 8 ? cmax : 8;
+  return T > floor8 ? T : floor8;
 }
 
 // Committed length of sequence b (given as read) -> chunks of kg keys; a
@@ -203,16 +212,17 @@ __device__ __forceinline__ long long count_pieces_x16(const AttnArgs& a, int c0,
 // Shares the launch's slots out and finds a piece.  Every unit of sequence b
 // gets s_b = ceil(c_b / T) pieces (at least one, at most max_pieces), where
 // c_b is its number of chunks of kg committed keys and T is the largest piece
-// in chunks.  Ring kernel: T = ceil(c_max / k) for the k in 1..16 of least
-// ring_piece_cost among those whose pieces fit the launch's slots (so short
-// committed lengths take fewer, not shorter, rounds of workgroups).
+// in chunks.  Ring kernel: T = ceil(c_max / k) for the k in 1..16 first in
+// the order of ring_rounds, ring_piece_len among those whose pieces fit the
+// launch's slots (so short committed lengths take fewer, not shorter, rounds
+// of workgroups).
 // Otherwise T is the smallest value for which all pieces fit the slots: in
 // closed form when every sequence has the same length, else by bisection
 // (the count only falls as T grows, and T = max c_b fits since the host
 // launches at least one slot per unit).  With B <= 64 the 16 candidates of
-// the cost model are counted at once, one per group of lanes, and the
+// the ring order are counted at once, one per group of lanes, and the
 // bisection becomes a 16-way search; both give the same T as the serial
-// forms (the first candidate of least cost; the least fitting T), at a
+// forms (the first candidate first in the order; the least fitting T), at a
 // fraction of the instructions, which every workgroup spends before its
 // first loads when the lengths are not the full ones.  Slots are numbered sequence by
 // sequence, unit by unit, piece by piece; slots past the last piece are
@@ -260,10 +270,11 @@ __device__ bool plan_piece(const AttnArgs& a, int key, int kvl0, Piece& p) {
     const int t = (cm + k - 1) / k;
     const long long n = count_pieces_x16(a, c0, t);
     const bool ok = k <= cm && n <= a.slots;
-    // costs are non-negative (or +inf): their bits order as integers
-    const int cost = __float_as_int(ok ? ring_piece_cost(n, t, cm) : INFINITY);
-    const int best = wave_allmin_i(cost);
-    const uint64_t m = __ballot(lane < 16 && ok && cost == best);  // k = 1 always fits
+    const int r = ok ? ring_rounds(n) : INT_MAX;
+    const int best_r = wave_allmin_i(r);
+    const int te = ok && r == best_r ? ring_piece_len(t, cm) : INT_MAX;
+    const int best_t = wave_allmin_i(te);
+    const uint64_t m = __ballot(lane < 16 && ok && r == best_r && te == best_t);  // k = 1 always fits
     T = m ? lane_i(t, __ffsll((unsigned long long)m) - 1) : cm;
   } else if (a.B <= 64 && cmin != cmax) {
     // least fitting T in [lo, hi] (hi fits): candidate j = lo + (j + 1) step - 1,
@@ -283,20 +294,21 @@ __device__ bool plan_piece(const AttnArgs& a, int key, int kvl0, Piece& p) {
     T = lo;
   } else if (a.ring_cost) {
     const int cm = max(cmax, 1);
-    float best = 0.f;
+    int best_r = 0, best_t = 0;
     for (int k = 1; k <= min(16, cm); ++k) {  // wave-uniform
       const int t = (cm + k - 1) / k;
       const long long n = count_at(t);
       if (n > a.slots) continue;
-      const float cost = ring_piece_cost(n, t, cm);
-      if (T == 0 || cost < best) {
-        best = cost;
+      const int r = ring_rounds(n), te = ring_piece_len(t, cm);
+      if (T == 0 || r < best_r || (r == best_r && te < best_t)) {
+        best_r = r;
+        best_t = te;
         T = t;
       }
     }
   }
   if (T > 0) {
-    // chosen by the cost model
+    // chosen by the ring order
   } else if (cmin == cmax) {
     // every unit alike: ceil(c / T) <= slots / units
     const int per_unit = (int)((long long)a.slots / ((long long)a.B * U));
@@ -1383,18 +1395,17 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
   const int cap_chunks = std::max(1, (Lmax - N + p.kg - 1) / p.kg);
   int pieces;
   if (kernel == 1) {
-    // The ring kernel's cost model at full cache length (the device applies
-    // the same one to the committed lengths, see plan_piece).
+    // The ring kernel's order of decompositions at full cache length (the
+    // device applies the same one to the committed lengths, see plan_piece).
     pieces = 1;
-    float best = 0.f;
-    int bestT = 0;
+    int best_r = 0, best_t = 0;
     for (int k = 1; k <= 16 && k <= cap_chunks; ++k) {
       const int t = (cap_chunks + k - 1) / k;
       const int s = std::min((cap_chunks + t - 1) / t, kMaxPiecesPerUnit);
-      const float cost = ring_piece_cost((long long)p.units * s, t, cap_chunks);
-      if (bestT == 0 || cost < best) {
-        best = cost;
-        bestT = t;
+      const int r = ring_rounds((long long)p.units * s), te = ring_piece_len(t, cap_chunks);
+      if (best_t == 0 || r < best_r || (r == best_r && te < best_t)) {
+        best_r = r;
+        best_t = te;
         pieces = s;
       }
     }
@@ -1404,14 +1415,21 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int d, int Lmax) {
     // mixtral shape 2 pieces, 186.8 us against 220.7 at 3)
     pieces = (kNumCUs + round8(p.units) - 1) / round8(p.units);
   }
-  // the ring kernel's device planner applies the cost model to the committed
+  // the ring kernel's device planner applies its order to the committed
   // lengths unless a test fixed the piece count
   p.ring_cost = kernel == 1 && g_plan_override.pieces <= 0 ? 1 : 0;
   if (g_plan_override.pieces > 0) pieces = g_plan_override.pieces;
   pieces = std::max(1, std::min(pieces, std::min(cap_chunks, kMaxPiecesPerUnit)));
   p.slots = round8((long long)p.units * pieces);
+  // the ring kernel launches at least a round of workgroups (up to 16 pieces
+  // per unit) even when the units fill fewer CUs at full length: committed
+  // lengths below the capacity then cut their longest sequences into more
+  // pieces on the idle CUs (unused slots plan and return)
+  if (p.ring_cost)
+    p.slots = std::max(p.slots, round8(std::min<long long>(
+                                    kNumCUs, (long long)p.units * std::min(16, cap_chunks))));
   if (p.ring_cost) {
-    // at full length the device's cost model makes the same choice
+    // at full length the device's order makes the same choice
     p.full_pieces = pieces;
   } else {
     // what the device planner gives every unit when all sequences fill the
