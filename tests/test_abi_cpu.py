@@ -116,6 +116,27 @@ def test_workspace_sizes():
     assert L.eagle_verify_accept_workspace(1, 26, 40000) == 0
 
 
+def test_ring_plan_takes_one_round():
+    """The ring kernel's launch, read through its workspace size (tickets,
+    per-slot log-sum-exp and O partials of 32 rows): at the llama2-7b shape
+    8 pieces of 8 chunks fill one round of 256 workgroups; at llama2-13b
+    (160 heads x sequences) one piece per unit, with a full round of 256
+    slots launched so that shorter committed lengths can split the longest
+    sequences; with more units than CUs, one piece each, which write the
+    output themselves (no workspace)."""
+    L = ev.lib()
+
+    def ws(units, slots, rows=32, d=128):
+        a = lambda x: (x + 255) // 256 * 256
+        return a(units * 8) + a(slots * rows * 4) + slots * rows * d * 4
+
+    assert L.eagle_tree_attn_workspace(1, 26, 32, 32, 128, 2048 + 26) == ws(32, 256)
+    assert L.eagle_tree_attn_workspace(4, 26, 40, 40, 128, 4096 + 26) == ws(160, 256)
+    assert L.eagle_tree_attn_workspace(16, 26, 32, 32, 128, 2048 + 26) == 0
+    # a short cache: one piece of at most 8 chunks per unit, still a round launched
+    assert L.eagle_tree_attn_workspace(1, 26, 32, 32, 128, 256 + 26) == ws(32, 256)
+
+
 def test_verify_argument_errors():
     L = ev.lib()
 
