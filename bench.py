@@ -279,6 +279,25 @@ def measure_stream_context(torch):
     return out
 
 
+def measure_read_floor(torch, ev, nbytes, workgroups, steps):
+    """The attention stream's floor at the headline shape: the same bytes read
+    with the ring kernel's load structure and nothing else
+    (eagle_testing_read_floor: `workgroups` workgroups of 8 waves, 16 KB
+    chunks, one in flight per wave), rotating over ~1 GiB of windows as the
+    step's inputs do, `steps` launches in one graph."""
+    per = (nbytes + 255) // 256 * 256
+    copies = max(2, ROTATE_BYTES // per)
+    buf = torch.ones(copies * per // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(workgroups * 512, dtype=torch.int32, device="cuda")
+    win = [buf[i * per // 4: i * per // 4 + nbytes // 4] for i in range(copies)]
+    g = graph_of(torch, lambda i: ev.testing_read_floor(win[i % copies], workgroups, sink), steps)
+    time_graph(torch, g)
+    t = time_graph(torch, g) / steps
+    del g, buf, sink, win
+    return {"bytes": nbytes, "workgroups": workgroups, "us": t * 1e6,
+            "GBs": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+
 def measure_dynamic_tree(torch, ev, W, steps):
     """The EAGLE-2 tree built on the GPU at the mixtral-eagle2 shape (16
     sequences, top-10 expansion, depth 6, 60 nodes, V = 32000): root
@@ -656,6 +675,9 @@ def main():
     fg = measure_feature_gather(torch, ev, W, args.steps)
     dtree = measure_dynamic_tree(torch, ev, W, args.steps)
     stream = measure_stream_context(torch)
+    # the ring kernel's launch at this shape: 32 heads x 8 pieces
+    stream["read_floor_attention_bytes"] = measure_read_floor(torch, ev, attn_bytes // 16 * 16, 256,
+                                                              args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

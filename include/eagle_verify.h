@@ -404,6 +404,20 @@ EAGLE_API eagle_status_t eagle_dtree_rerank(const int32_t* created_parent, const
  */
 EAGLE_API eagle_status_t eagle_testing_attn_plan(int kernel, int pieces_per_unit);
 
+/*
+ * Measurement only (the roofline's context): reads `bytes` of device memory
+ * at `src` with the ring attention kernel's load structure and nothing else:
+ * `workgroups` workgroups of 512 threads, workgroup w reading its contiguous
+ * share bytes / workgroups (the remainder is not read) in 16 KB chunks, one
+ * chunk in flight per wave.  Its time is the floor of the attention's stream
+ * at that size and workgroup count.  sink: device, workgroups * 512 uint32
+ * written (the XOR of what each thread read).  Asynchronous on `stream`.
+ * EAGLE_ERR_INVALID_ARGUMENT for NULL pointers, workgroups outside
+ * [1, 65535], fewer than 16 or more than 2^31 - 1 bytes per workgroup.
+ */
+EAGLE_API eagle_status_t eagle_testing_read_floor(const void* src, size_t bytes, int workgroups,
+                                                  uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -290,6 +290,17 @@ def test_binding_rejects_mis_sized_tensors_on_the_host():
                         torch.zeros((1, 8), dtype=torch.int32), torch.zeros((1, 8)), 1)
 
 
+def test_read_floor_argument_errors():
+    """The measurement hook refuses bad arguments before touching a device."""
+    E = binding.EAGLE_ERR_INVALID_ARGUMENT
+    assert _status("eagle_testing_read_floor", None, 1 << 20, 64, FAKE, None) == E
+    assert _status("eagle_testing_read_floor", FAKE, 1 << 20, 64, None, None) == E
+    assert _status("eagle_testing_read_floor", FAKE, 1 << 20, 0, FAKE, None) == E
+    assert _status("eagle_testing_read_floor", FAKE, 1 << 20, 65536, FAKE, None) == E
+    assert _status("eagle_testing_read_floor", FAKE, 64 * 16 - 1, 64, FAKE, None) == E
+    assert _status("eagle_testing_read_floor", FAKE, 1 << 32, 1, FAKE, None) == E
+
+
 def test_attention_plan_hook_and_noalloc_limits():
     """The testing hook checks its arguments; the attention entry point that
     allocates nothing refuses, before touching a device, a shape whose scratch

@@ -407,6 +407,35 @@ def test_attention_workspace_reuse(idx):
     assert np.array_equal(outs[0], ref)
 
 
+def test_read_floor_reads_each_share_once():
+    """The measurement hook behind the attention's read floor: workgroup w
+    reads its share bytes / workgroups in 16 KB chunks (wave i: chunks i,
+    i + 8, ...), each thread XOR-ing its 16-byte pieces, nothing past the
+    share (a share of 20 000 bytes is not a whole number of chunks)."""
+    wgs, per = 6, 20000
+    rng = np.random.default_rng(5)
+    host = rng.integers(0, 2**32, size=wgs * per // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.empty(wgs * 512, dtype=torch.int32, device="cuda")
+    say("read floor hook")
+    ev.testing_read_floor(src, wgs, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32).reshape(wgs, 512)
+    words = host.reshape(wgs, per // 4)
+    want = np.zeros((wgs, 512), dtype=np.uint32)
+    for w in range(wgs):
+        for t in range(512):
+            wave, lane = t // 64, t % 64
+            acc = np.uint32(0)
+            for c in range(wave, (per + 16383) // 16384, 8):
+                for k in range(16):
+                    off = c * 16384 + k * 1024 + lane * 16
+                    if off + 16 <= per:
+                        acc ^= np.bitwise_xor.reduce(words[w, off // 4: off // 4 + 4])
+            want[w, t] = acc
+    assert np.array_equal(got, want)
+
+
 # ---------------------------------------------------------------------------- verification
 def _check_probs(gpu_probs, step):
     B, N, V = step.target_logits.shape

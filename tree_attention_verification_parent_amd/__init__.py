@@ -7,7 +7,7 @@ ctypes (binding.py).  Build with `python -m
 tree_attention_verification_parent_amd.build`.
 """
 from .binding import (EagleError, abi_version, alloc_workspace, attn_plan,  # noqa: F401
-                      dtree_expand, testing_attn_plan,
+                      dtree_expand, testing_attn_plan, testing_read_floor,
                       dtree_rerank, dtree_select, feature_gather, kv_compact, lib,
                       tree_attn, tree_attn_parents, tree_attn_parents_noalloc,
                       tree_attn_workspace_bytes, tree_build,

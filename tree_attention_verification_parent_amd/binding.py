@@ -49,6 +49,7 @@ _SIGNATURES = {
     "eagle_validate_tree_host": (_I, [_P, _I, _I]),
     "eagle_workspace_clear": (_I, [_P, _SZ, _P]),
     "eagle_testing_attn_plan": (_I, [_I, _I]),
+    "eagle_testing_read_floor": (_I, [_P, _SZ, _I, _P, _P]),
     "eagle_tree_build": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "eagle_tree_attn_workspace": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "eagle_tree_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P]),
@@ -152,6 +153,19 @@ def testing_attn_plan(kernel: str = "auto", pieces: int = 0) -> None:
     the pieces per (sequence, KV head) at full cache length (0 = planner) of
     later attention calls in this process."""
     _check(lib().eagle_testing_attn_plan(ATTN_KERNELS[kernel], int(pieces)))
+
+
+def testing_read_floor(src: torch.Tensor, workgroups: int, sink: torch.Tensor,
+                       stream=None) -> None:
+    """Measurement hook: read all of `src` (a contiguous device tensor) with
+    the ring attention kernel's load structure and nothing else, split over
+    `workgroups` workgroups; `sink` (int32, workgroups * 512) receives what
+    was read, XOR-ed per thread."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < workgroups * 512 * 4:
+        raise ValueError("sink must hold workgroups * 512 int32")
+    _check(lib().eagle_testing_read_floor(_ptr(src, name="src"), nbytes, int(workgroups),
+                                          _ptr(sink, torch.int32, "sink"), _stream(stream)))
 
 
 class attn_plan:

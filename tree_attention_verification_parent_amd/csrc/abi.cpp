@@ -75,6 +75,19 @@ eagle_status_t eagle_testing_attn_plan(int kernel, int pieces_per_unit) {
   return EAGLE_OK;
 }
 
+eagle_status_t eagle_testing_read_floor(const void* src, size_t bytes, int workgroups,
+                                        uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(EAGLE_ERR_INVALID_ARGUMENT, "src and sink must be non-NULL");
+  if (workgroups < 1 || workgroups > 65535)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "workgroups must be in [1, 65535] (got %d)", workgroups);
+  if (bytes / (size_t)workgroups > 0x7fffffffu)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "at most 2^31 - 1 bytes per workgroup");
+  if (bytes < (size_t)workgroups * 16)
+    return fail(EAGLE_ERR_INVALID_ARGUMENT, "at least 16 bytes per workgroup");
+  return hip_status(eagle::launch_read_floor(src, bytes, workgroups, sink, as_stream(stream)),
+                    "read floor launch");
+}
+
 eagle_status_t eagle_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
                                 uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* seq_flags,
                                 void* stream) {

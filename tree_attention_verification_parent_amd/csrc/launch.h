@@ -14,6 +14,8 @@ hipError_t launch_tree_build(const int32_t* parents, const int32_t* kv_len, int 
                              hipStream_t s);
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+hipError_t launch_read_floor(const void* src, size_t bytes, int workgroups, uint32_t* sink,
+                             hipStream_t s);
 
 // Tree attention -----------------------------------------------------------
 struct AttnPlan {

@@ -42,6 +42,40 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* __restrict__ p,
   for (size_t i = h + n16 * 16 + tid; i < bytes; i += stride) p[i] = 0;
 }
 
+// Read floor of the attention's load structure: `workgroups` workgroups of
+// 8 waves, workgroup w reading its own contiguous `per_wg` bytes in 16 KB
+// chunks (wave i taking chunks i, i + 8, ...), one chunk in flight per wave,
+// and nothing else: the time the ring kernel's stream would take if the
+// chunks cost no compute, fold or combine.  Each thread XORs what it read
+// into sink[w * 512 + thread] so the loads are kept.  Buffer loads past the
+// region read 0 without touching memory.
+__global__ __launch_bounds__(512) void read_floor_kernel(const uint8_t* src, size_t per_wg,
+                                                         uint32_t* sink) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* base = src + (size_t)blockIdx.x * per_wg;
+  const __amdgpu_buffer_rsrc_t r =
+      buffer_rsrc(reinterpret_cast<const float*>(base), per_wg);
+  const size_t chunks = (per_wg + 16383) / 16384;
+  uint32_t acc = 0;
+  for (size_t c = wave; c < chunks; c += 8) {
+    u32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, (int)(c * 16384 + k * 1024 + lane * 16), 0, 2));
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  sink[(size_t)blockIdx.x * 512 + tid] = acc;
+}
+
+hipError_t launch_read_floor(const void* src, size_t bytes, int workgroups, uint32_t* sink,
+                             hipStream_t s) {
+  const size_t per_wg = bytes / (size_t)workgroups;
+  read_floor_kernel<<<workgroups, 512, 0, s>>>(static_cast<const uint8_t*>(src), per_wg, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_tree_build(const int32_t* parents, const int32_t* kv_len, int B, int N,
                              uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* flags,
                              hipStream_t s) {
