@@ -23,7 +23,10 @@
 namespace eagle {
 
 constexpr int kTreeBlock = 1024;   // selection and rerank
-constexpr int kExpandBlock = 512;  // expansion: two waves per SIMD keep each round short
+// expansion: 16 waves of 32 keys per thread; against 8 waves of 64 the k
+// rounds of each wave overlap four to a SIMD and a winner's rescan covers
+// half the keys (the 12-launch build at the Mixtral shape: 125 -> 109 us)
+constexpr int kExpandBlock = 1024;
 
 // Larger value first, then lower id (ids below 2^31); key 0 is below every
 // real key and marks "none".
@@ -156,7 +159,7 @@ __device__ __forceinline__ void block_topk(KeyAt&& key_at, int k, unsigned long 
 }
 
 // Expansion: one workgroup per (sequence, row); the keys of the row's
-// V <= 32768 probabilities in registers (64 per thread).
+// V <= 32768 probabilities in registers (32 per thread).
 __global__ __launch_bounds__(kExpandBlock) void eagle2_expand_kernel(
     const float* __restrict__ q, int R, int V, int k, const int32_t* __restrict__ parent_node,
     const float* __restrict__ parent_value, int32_t* __restrict__ cpar,
@@ -167,18 +170,22 @@ __global__ __launch_bounds__(kExpandBlock) void eagle2_expand_kernel(
   const int row = blockIdx.x;
   const int b = row / R, r = row - b * R;
   const float* qr = q + (size_t)row * V;
-  // every load in flight before any is used (a guarded load each waited for)
+  // 16-byte buffer loads, every one in flight before any is used (ids past
+  // V read 0 and get no key); thread t holds ids 4 (f * BLOCK + t) + c
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(qr, (size_t)V * 4);
+  f32x4 x4[EPT / 4];
+#pragma unroll
+  for (int f = 0; f < EPT / 4; ++f)
+    x4[f] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, (f * kExpandBlock + (int)threadIdx.x) * 16, 0, 0));
   unsigned long long key[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const float x = qr[min(e * kExpandBlock + (int)threadIdx.x, V - 1)];
-    key[e] = __float_as_uint(x);  // every load in flight first, keys formed below
-  }
+  for (int f = 0; f < EPT / 4; ++f)
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int t = e * kExpandBlock + threadIdx.x;
-    key[e] = t < V ? vkey(__uint_as_float((uint32_t)key[e]), t) : 0ull;
-  }
+    for (int c = 0; c < 4; ++c) {
+      const int t = 4 * (f * kExpandBlock + (int)threadIdx.x) + c;
+      key[4 * f + c] = t < V ? vkey(x4[f][c], t) : 0ull;
+    }
   auto key_at = [&](int e) { return key[e]; };
   const float pv = parent_value[row];
   const int pn = parent_node[row];
