@@ -563,9 +563,7 @@ __device__ __forceinline__ void split_s(double S, float& hs, float& ls) {
 // F(S): one pass over the two rows and one workgroup reduction.
 template <int BLOCK, int NPT>
 __device__ __forceinline__ double residual_mass(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
-                                                double S, Shared<BLOCK, NPT>& sh, int& rb) {
-  float hs, ls;
-  split_s<BLOCK, NPT>(S, hs, ls);
+                                                float hs, float ls, Shared<BLOCK, NPT>& sh, int& rb) {
   float ps[NPT];
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
@@ -604,24 +602,30 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
   const int tid = threadIdx.x;
 #pragma nounroll
   for (int s = 0; s < nk; ++s) {
-    float hs, ls;
+    // the next row's S (and its fp32 pair) does not depend on the test: it
+    // is formed alongside it, and the test's operands are read without
+    // branches (selects after unconditional lane reads)
+    const double Sn = S + C;
+    float hs, ls, hn, ln;
     split_s<BLOCK, NPT>(S, hs, ls);
+    split_s<BLOCK, NPT>(Sn, hn, ln);
     const float wl = residual(cd.ut, cd.q, hs, ls);  // each lane's candidate entry
     const bool tok_ok = lane_i(cd.tok, s) >= 0;
-    const double qt = tok_ok ? (double)lane_f(cd.q, s) : 0.0;
-    const double num = tok_ok ? (double)lane_f(wl, s) : 0.0;
+    const double qraw = (double)lane_f(cd.q, s), nraw = (double)lane_f(wl, s);
+    const double uu = (double)lane_f(cd.u, s);
+    const double qt = tok_ok ? qraw : 0.0;
+    const double num = tok_ok ? nraw : 0.0;
     const double den = C * qt;
-    const bool accept = qt > 0.0 ? (double)lane_f(cd.u, s) * den < num : num > 0.0;
+    const bool accept = (qt > 0.0 && uu * den < num) || (!(qt > 0.0) && num > 0.0);
     if (RATIO && tid == 0)
       sh.ratio[s] = qt > 0.0 ? (float)(num / den) : (num > 0.0 ? INFINITY : 0.f);
     if (stop_at_accept && accept) return s;
-    const double Sn = S + C;
     if (stop_at_accept && s == nk - 1) {
       Sprev = S;
       S = Sn;
       return -1;
     }
-    const double Cn = residual_mass<BLOCK, NPT>(U, Q, Sn, sh, rb);
+    const double Cn = residual_mass<BLOCK, NPT>(U, Q, hn, ln, sh, rb);
     if (Cn > 0.0) {
       S = Sn;
       C = Cn;
