@@ -755,9 +755,12 @@ __device__ __forceinline__ double wave_incl_scan_d(double v) {
 // fly.  The cumulative sums are built in levels over consecutive ids: a
 // group (one thread's four entries, summed left to right in fp32), a lane
 // group (BLOCK / 64 consecutive groups, fp64), a slab (2048 or 1024 ids, a
-// wave's prefix scan of its lane groups), the row (slabs in order).  The draw
+// wave's prefix scan of its lane groups), the row (a scan of the slab
+// totals over one lane each, done alike by every wave).  The draw
 // descends the levels: the first slab whose end exceeds the threshold, in it
-// the first lane group, in that the first group, in that the first entry; an
+// the first lane group, in that the first group (its lane group's sums read
+// at once, then walked without further LDS round trips: whole verification
+// at the 7B shape 24.4 -> 23.4 us), in that the first entry; an
 // entry's cumulative sum is its group's start plus the group's own fp32
 // prefix, which ends exactly at the group's sum.  Where the levels' fp64
 // roundings leave no crossing inside the chosen lane group (a window of about
@@ -770,6 +773,7 @@ __device__ __forceinline__ int inverse_cdf(E&& ent, float u, int V, Shared<BLOCK
   constexpr int NW = BLOCK / 64;
   constexpr int GPL = BLOCK / 64;  // groups per lane group
   static_assert(NPT % NW == 0, "whole slabs per wave");
+  static_assert(GPL % 4 == 0 && NPT <= 64, "lane groups read as float4; slab totals one per lane");
   constexpr int SPW = NPT / NW;    // slabs per wave
   float* gbuf = static_cast<float*>(scratch);                       // [NPT][BLOCK]
   double* lsc = reinterpret_cast<double*>(gbuf + NPT * BLOCK);      // [NPT][64]
@@ -790,39 +794,41 @@ __device__ __forceinline__ int inverse_cdf(E&& ent, float u, int V, Shared<BLOCK
     lsc[k * 64 + lane] = wave_incl_scan_d(ls);
   }
   barrier_lds();
-  // every thread takes the same decisions from the same LDS values
-  double before[NPT], Z = 0.0;
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    before[k] = Z;
-    Z += lsc[k * 64 + 63];
-  }
+  // every wave takes the same decisions from the same LDS values: the slab
+  // totals' prefix by a scan over lanes 0..NPT-1, the crossing slab, then
+  // its crossing lane group and group
+  const double tot = lane < NPT ? lsc[lane * 64 + 63] : 0.0;
+  const double tinc = wave_incl_scan_d(tot);
+  const double Z = lane_d(tinc, NPT - 1);
   const double thr = (double)u * Z;
-  int ks = -1;
-  double bk = 0.0;
-#pragma unroll
-  for (int k = NPT - 1; k >= 0; --k)
-    if (before[k] + lsc[k * 64 + 63] > thr) {
-      ks = k;
-      bk = before[k];
-    }
+  const uint64_t over = __ballot(lane < NPT && tinc > thr);
+  int ks = over ? __ffsll((unsigned long long)over) - 1 : -1;
   if (ks >= 0) {
-    ks = __builtin_amdgcn_readfirstlane(ks);
+    const double bk = ks > 0 ? lane_d(tinc, ks - 1) : 0.0;
     const double incl = lsc[ks * 64 + lane];
     const uint64_t cross = __ballot(bk + incl > thr);
     const int L = cross ? __ffsll((unsigned long long)cross) - 1 : 63;
-    double base = bk + (L > 0 ? lsc[ks * 64 + L - 1] : 0.0);
+    double base = bk + (L > 0 ? lane_d(incl, L - 1) : 0.0);
+    // the lane group's GPL group sums, read before any is used
+    float gm[GPL];
+#pragma unroll
+    for (int h = 0; h < GPL / 4; ++h) {
+      const float4 q4 = reinterpret_cast<const float4*>(gbuf + ks * BLOCK + L * GPL)[h];
+      gm[4 * h] = q4.x;
+      gm[4 * h + 1] = q4.y;
+      gm[4 * h + 2] = q4.z;
+      gm[4 * h + 3] = q4.w;
+    }
     int gsel = -1, glast = -1;
     double gbase = base;
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
-      const float gm = gbuf[ks * BLOCK + L * GPL + g];
-      if (gsel < 0 && base + (double)gm > thr) {
-        gsel = g;
-        gbase = base;
-      }
-      if (gm > 0.f) glast = g;
-      base += (double)gm;
+      const double nb = base + (double)gm[g];
+      const bool hit = gsel < 0 && nb > thr;
+      gbase = hit ? base : gbase;
+      gsel = hit ? g : gsel;
+      glast = gm[g] > 0.f ? g : glast;
+      base = nb;
     }
     const bool fallback = gsel < 0;
     if (fallback) gsel = glast;
