@@ -1104,7 +1104,12 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   if (!sh.last) return;
 
   // ---- walk (last workgroup of sequence b) -----------------------------------
-  if (tid < N) {
+  // The walk starts at the root: when the last workgroup is the root's own and
+  // it accepted none of its children, the walk ends there and needs no other
+  // node's published outcome (the 7B step, whose root rejects all 15
+  // children, saves the loads' round trip: whole verification 23.5 -> 22.8 us)
+  const bool root_only = !PARITY && j == 0 && acc < 0;
+  if (!root_only && tid < N) {
     // all three loads in flight before any result is used
     const int r0 = ld_c(a.nr.acc + ob + tid);
     const int r1 = ld_c(a.nr.bonus + ob + tid);
@@ -1117,14 +1122,14 @@ __global__ __launch_bounds__(BLOCK) void verify_node_kernel(VArgs a) {
   if (tid == 0) {
     int cur = 0, m_acc = 0;
     sh.path[0] = 0;
-    for (;;) {
+    for (; !root_only;) {
       const int nx = sh.wacc[cur];
       if (nx < 0 || nx <= cur || nx >= N) break;  // nx > cur for any valid walk
       sh.path[++m_acc] = nx;
       cur = nx;
     }
     sh.term = cur;
-    sh.pick = min(max(sh.wbonus[cur], 0), V - 1);
+    sh.pick = min(max(root_only ? bonus : sh.wbonus[cur], 0), V - 1);
     sh.nk = m_acc;
     __hip_atomic_store(a.nr.counter + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
