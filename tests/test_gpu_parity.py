@@ -693,6 +693,19 @@ def test_full_step_with_compaction(idx, T):
     assert np.array_equal(new_len.cpu().numpy(), nl)
 
 
+@pytest.mark.parametrize("B,N,V", [(1, 8, 32000), (1, 6, 32768), (1, 7, 20000)])
+def test_verify_t0_few_nodes_split_rows(B, N, V):
+    """T = 0 with at most 8 nodes and no parity outputs: each row is split
+    over several workgroups meeting on a packed maximum; the walk against the
+    oracle's, bit-exact."""
+    cfg = W.shrink(W.get(1), B=B, N=N, V=V)
+    s = W.make_step(cfg, 0.0, seed=B * 100 + N * 10 + V % 7, with_attention=False)
+    say(f"verify T=0 split rows B={B} N={N} V={V}")
+    gpu = run_verify(s, want_final_dist=False, want_ratio=False)
+    compared, excused = compare_walks(gpu, s, oracle_walks(s))
+    assert compared == B and excused == 0
+
+
 # The fused entry point against the two separate calls it replaces: the same
 # walk outputs, the same cache bytes and new lengths.  Small draft noise makes
 # the walks accept, so path nodes actually move.

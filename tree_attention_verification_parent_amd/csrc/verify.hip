@@ -1298,14 +1298,17 @@ __global__ __launch_bounds__(256) void verify_argmax_kernel(VArgs a) {
 
 // ---------------------------------------------------------------------------
 // T = 0 without parity outputs may split each row over P workgroups of 256
-// threads (at most 8 float4 per thread).  Splitting pays only while the batch
-// leaves most of the chip idle: the P slices of a row meet on one counter and
-// one packed max, so about 128 workgroups in all is the target, and a batch
-// with more nodes than that (or one that would need fewer slices than the
-// row's minimum) reads each row in one 512-thread workgroup instead.
+// threads (at most 8 float4 per thread).  The P slices of a row meet on one
+// packed maximum before the sequence's ticket, a second round trip to memory
+// that the unsplit node kernel (one 512-thread workgroup per row, its
+// argmax published with the ticket) does not pay, so splitting pays only for
+// a handful of nodes (graph-timed, V = 32000, 7B layer: 8 nodes 5.8 us split
+// against 6.6 unsplit; 16 nodes 7.2 against 6.8; 26 nodes 9.1 against 7.7;
+// 52 nodes 9.3 either way).  About 128 workgroups in all is the target, and
+// a row needing more slices than that gives reads in one workgroup instead.
 static int argmax_parts(int B, int N, int V) {
-  if (V <= 4096) return 1;
   const long long nodes = (long long)B * N;
+  if (V <= 4096 || nodes > 8) return 1;
   const int v4 = (V + 3) / 4;
   const int min_parts = (v4 + 8 * 256 - 1) / (8 * 256);
   const long long want = 128 / std::max<long long>(nodes, 1);
