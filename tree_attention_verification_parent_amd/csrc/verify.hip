@@ -308,9 +308,9 @@ __device__ __forceinline__ float pairwise(const float (&s)[NPT]) {
 
 // The scaled exponent of one logit, exactly as the row pass computes it
 // (non-finite logits have no mass).
-__device__ __forceinline__ float target_entry(float x, float m, bool unit, float invT) {
+__device__ __forceinline__ float target_entry(float x, float m, float invT) {
   x = isfinite(x) ? x : -FLT_MAX;
-  return exp_neg(unit ? x - m : (x - m) * invT);
+  return exp_neg((x - m) * invT);
 }
 
 // Non-finite logits (NaN, +-Inf) are reported and given no mass: replaced by
@@ -365,7 +365,7 @@ __device__ __forceinline__ void row_argmax(const Row<BLOCK, NPT>& U, float& mx, 
 // returns the lowest-index argmax; T > 0 turns U into exp((l - max)/T) and
 // returns its mass in C.  after_max() runs once the row's maximum is known
 // (U has arrived: loads it issues no longer share the CU's bandwidth with
-// U's); before_sum(m, unit, invT) runs before the mass reduction, whose
+// U's); before_sum(m, invT) runs before the mass reduction, whose
 // barrier publishes what it writes to LDS.
 template <int BLOCK, int NPT, bool GREEDY, typename G, typename F>
 __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
@@ -385,19 +385,21 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
     const float m = block_max<BLOCK, NPT>(lm, sh, rb);
     after_max();
-    const bool unit = T == 1.f;
+    // (x - m) * (1 / T): at T = 1 the product is x - m exactly, so one form
+    // serves every temperature (a select between two forms cost an
+    // instruction per entry)
     const float invT = 1.f / T;
     float s[NPT];
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       float4& f = U.v[k];
-      f.x = exp_neg(unit ? f.x - m : (f.x - m) * invT);  // already finite
-      f.y = exp_neg(unit ? f.y - m : (f.y - m) * invT);
-      f.z = exp_neg(unit ? f.z - m : (f.z - m) * invT);
-      f.w = exp_neg(unit ? f.w - m : (f.w - m) * invT);
+      f.x = exp_neg((f.x - m) * invT);  // already finite
+      f.y = exp_neg((f.y - m) * invT);
+      f.z = exp_neg((f.z - m) * invT);
+      f.w = exp_neg((f.w - m) * invT);
       s[k] = sum4(f);
     }
-    before_sum(m, unit, invT);
+    before_sum(m, invT);
     C = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s), sh, rb);  // entries <= 1
     return 0;
   }
@@ -659,7 +661,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
   val = 0.f;
   shared = false;
   if constexpr (GREEDY) {
-    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, [] {}, [](float, bool, float) {}, sh,
+    return target_stats<BLOCK, NPT, true>(U, a.T, b, flags, C, [] {}, [](float, float) {}, sh,
                                           rb);
   } else {
     cd.kid = 0;
@@ -713,7 +715,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
               load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
           }
         },
-        [&](float m, bool unit, float invT) {
+        [&](float m, float invT) {
           if (!shared) {
 #pragma unroll
             for (int r = 0; r < G; ++r) {
@@ -722,7 +724,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
               if (k <= i && i < nk) sh.qt[tri(k, i)] = g[r];
             }
           }
-          if (lane < nk) val = target_entry(lt, m, unit, invT);
+          if (lane < nk) val = target_entry(lt, m, invT);
         },
         sh, rb);
     // the table is published by the mass reduction's barrier
