@@ -34,7 +34,7 @@
 //
 // A node's critical path is a sequence of full-vocabulary passes, each ending
 // in a workgroup reduction, so the kernel is built around short passes:
-//   * the rows live in registers across the 1024-thread workgroup (8 float4
+//   * the rows live in registers across the 512-thread workgroup (16 float4
 //     per thread at V <= 32768), entries past V padded so no pass needs a
 //     bounds check;
 //   * without a shared row, a candidate's draft row is prefetched into LDS
@@ -562,16 +562,22 @@ __device__ __forceinline__ void split_s(double S, float& hs, float& ls) {
   ls = (float)(S - (double)hs);
 }
 
-// F(S): one pass over the two rows and one workgroup reduction.
+// F(S): one pass over the two rows and one workgroup reduction.  The sum
+// applies S through its fp32 head alone: one clamped FMA per entry instead of
+// two.  Leaving out the tail moves each term by at most |S - hs| q <= 2^-24 S q,
+// under one ulp of a live entry (S q < U there), and an entry within that of
+// zero (S within 2^-24 of its ratio U/q) by no more, so the mass keeps the
+// accuracy of the fp32 sums; the entries themselves (a candidate's numerator,
+// the row of the final draw) keep both parts.
 template <int BLOCK, int NPT>
 __device__ __forceinline__ double residual_mass(const Row<BLOCK, NPT>& U, const Row<BLOCK, NPT>& Q,
-                                                float hs, float ls, Shared<BLOCK, NPT>& sh, int& rb) {
+                                                float hs, Shared<BLOCK, NPT>& sh, int& rb) {
   float ps[NPT];
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
     const float4 u = U.v[k], q = Q.v[k];
-    ps[k] = (residual(u.x, q.x, hs, ls) + residual(u.y, q.y, hs, ls)) +
-            (residual(u.z, q.z, hs, ls) + residual(u.w, q.w, hs, ls));
+    ps[k] = (pos01(fmaf(-hs, q.x, u.x)) + pos01(fmaf(-hs, q.y, u.y))) +
+            (pos01(fmaf(-hs, q.z, u.z)) + pos01(fmaf(-hs, q.w, u.w)));
   }
   return block_sum<BLOCK, NPT>((double)pairwise<NPT>(ps), sh, rb);
 }
@@ -608,9 +614,9 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
     // is formed alongside it, and the test's operands are read without
     // branches (selects after unconditional lane reads)
     const double Sn = S + C;
-    float hs, ls, hn, ln;
+    float hs, ls, hn;
     split_s<BLOCK, NPT>(S, hs, ls);
-    split_s<BLOCK, NPT>(Sn, hn, ln);
+    hn = (float)Sn;
     const float wl = residual(cd.ut, cd.q, hs, ls);  // each lane's candidate entry
     const bool tok_ok = lane_i(cd.tok, s) >= 0;
     const double qraw = (double)lane_f(cd.q, s), nraw = (double)lane_f(wl, s);
@@ -627,7 +633,7 @@ __device__ __forceinline__ int run_chain_shared(const Row<BLOCK, NPT>& U, const 
       S = Sn;
       return -1;
     }
-    const double Cn = residual_mass<BLOCK, NPT>(U, Q, hn, ln, sh, rb);
+    const double Cn = residual_mass<BLOCK, NPT>(U, Q, hn, sh, rb);
     if (Cn > 0.0) {
       S = Sn;
       C = Cn;
