@@ -126,6 +126,38 @@ __device__ __forceinline__ int wave_allmax_i(int v) {
   return max(max(lane_i(v, 0), lane_i(v, 16)), max(lane_i(v, 32), lane_i(v, 48)));
 }
 
+// Sums whose result one lane needs (a workgroup sum's partial per wave):
+// after the four row steps, row_bcast:15 adds the last lane of rows 0
+// and 2 into rows 1 and 3, then row_bcast:31 adds the last lane of row 1 into
+// rows 2 and 3, so the lanes of row 3 (48..63) hold the wave's result.  Two
+// DPP operations replace four readlanes whose results pass through scalar
+// registers.  Rows a broadcast skips keep `old`: the operation's identity.
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  v += __int_as_float(dpp_rows_i<kDppBcast15, 0xa>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_rows_i<kDppBcast31, 0xc>(0, __float_as_int(v)));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_last(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  v += __hiloint2double(dpp_rows_i<kDppBcast15, 0xa>(0, __double2hiint(v)),
+                        dpp_rows_i<kDppBcast15, 0xa>(0, __double2loint(v)));
+  v += __hiloint2double(dpp_rows_i<kDppBcast31, 0xc>(0, __double2hiint(v)),
+                        dpp_rows_i<kDppBcast31, 0xc>(0, __double2loint(v)));
+  return v;
+}
 // Sums of M values over the wave at once (the M reductions interleave, so
 // their latencies overlap); every lane receives every sum.
 template <int M>
