@@ -270,24 +270,26 @@ __device__ __forceinline__ void load_row(Row<BLOCK, NPT>& r, const float* src, i
   }
 }
 
-// exp(z) for z <= 0, computed as 2^t with t = z log2(e) and the rounding of
-// that product carried separately: with log2(e) split into an fp32 head H and
-// tail L, the FMA fma(z, H, -t) gives the rounding error of z * H exactly
-// (the product of two fp32 values is exact in the FMA), z * L adds the tail,
-// and 2^(t + e) = 2^t (1 + e ln 2) to first order, so the result is
-// 2^t + 2^t * e * ln 2.  The hardware exp2 is within 1 ulp, so the whole is
-// within about 2 ulp of exp(z) (measured against fp64 on the device in the
-// tests).  Arguments below -110 (results below the fp32 range) are clamped,
-// which keeps the correction finite for the -FLT_MAX padding.
+// exp(z) for z <= 0, computed as 2^t with t = z log2(e) rounded to fp32 and
+// the rest of the exponent carried in natural units: e = z - t ln 2, with
+// ln 2 split into an fp32 head and tail, is formed by two FMAs (the first
+// exact: its product is exact in the FMA and the difference, about 2^-24 z,
+// fits in fp32), and e^z = 2^t e^e = 2^t (1 + e) to within e^2/2 (below
+// 1e-11 relative over the range).  The hardware exp2 is within 1 ulp, so the
+// whole is within about 2 ulp of exp(z) (checked against fp64 on the device
+// in the tests).  One instruction fewer per entry than carrying the rounding
+// of t in log2 units (and scaling it by ln 2).  Arguments below -110
+// (results below the fp32 range) are clamped, which keeps the correction
+// finite for the -FLT_MAX padding.
 __device__ __forceinline__ float exp_neg(float z) {
   z = fmaxf(z, -110.f);
-  constexpr float kL2E = 1.44269502162933349609375f;  // log2(e), fp32 head
-  constexpr float kL2ELo = 1.925963033500011e-08f;    // log2(e) - kL2E
-  constexpr float kLn2 = 0.693147180559945309f;
+  constexpr float kL2E = 1.44269502162933349609375f;  // log2(e), fp32
+  constexpr float kLn2Hi = 0.693147182464599609375f;  // ln 2, fp32 head
+  constexpr float kLn2Lo = -1.9046542121259336e-09f;  // ln 2 - kLn2Hi
   const float t = z * kL2E;
-  const float err = fmaf(z, kL2ELo, fmaf(z, kL2E, -t));
+  const float e = fmaf(-t, kLn2Lo, fmaf(-t, kLn2Hi, z));
   const float r = __builtin_amdgcn_exp2f(t);
-  return fmaf(r, err * kLn2, r);
+  return fmaf(r, e, r);
 }
 
 __device__ __forceinline__ float sum4(const float4& f) { return (f.x + f.y) + (f.z + f.w); }
@@ -310,10 +312,10 @@ __device__ __forceinline__ float pairwise(const float (&s)[NPT]) {
 }
 
 // The scaled exponent of one logit, exactly as the row pass computes it
-// (non-finite logits have no mass).
-__device__ __forceinline__ float target_entry(float x, float m, float invT) {
+// (non-finite logits have no mass); nmi = -(m * invT).
+__device__ __forceinline__ float target_entry(float x, float nmi, float invT) {
   x = isfinite(x) ? x : -FLT_MAX;
-  return exp_neg((x - m) * invT);
+  return exp_neg(fmaf(x, invT, nmi));
 }
 
 // Non-finite logits (NaN, +-Inf) are reported and given no mass: replaced by
@@ -368,8 +370,8 @@ __device__ __forceinline__ void row_argmax(const Row<BLOCK, NPT>& U, float& mx, 
 // returns the lowest-index argmax; T > 0 turns U into exp((l - max)/T) and
 // returns its mass in C.  after_max() runs once the row's maximum is known
 // (U has arrived: loads it issues no longer share the CU's bandwidth with
-// U's); before_sum(m, invT) runs before the mass reduction, whose
-// barrier publishes what it writes to LDS.
+// U's); before_sum(nmi, invT), nmi = -(m * invT), runs before the mass
+// reduction, whose barrier publishes what it writes to LDS.
 template <int BLOCK, int NPT, bool GREEDY, typename G, typename F>
 __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, int32_t* flags,
                                             double& C, G&& after_max, F&& before_sum,
@@ -388,21 +390,22 @@ __device__ __forceinline__ int target_stats(Row<BLOCK, NPT>& U, float T, int b, 
       lm = fmaxf(lm, fmaxf(fmaxf(U.v[k].x, U.v[k].y), fmaxf(U.v[k].z, U.v[k].w)));
     const float m = block_max<BLOCK, NPT>(lm, sh, rb);
     after_max();
-    // (x - m) * (1 / T): at T = 1 the product is x - m exactly, so one form
-    // serves every temperature (a select between two forms cost an
-    // instruction per entry)
+    // (x - m) / T as one FMA, x (1 / T) - m (1 / T): at T = 1 it is x - m
+    // exactly, so one form serves every temperature (a select between two
+    // forms cost an instruction per entry)
     const float invT = 1.f / T;
+    const float nmi = -(m * invT);
     float s[NPT];
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       float4& f = U.v[k];
-      f.x = exp_neg((f.x - m) * invT);  // already finite
-      f.y = exp_neg((f.y - m) * invT);
-      f.z = exp_neg((f.z - m) * invT);
-      f.w = exp_neg((f.w - m) * invT);
+      f.x = exp_neg(fmaf(f.x, invT, nmi));  // already finite
+      f.y = exp_neg(fmaf(f.y, invT, nmi));
+      f.z = exp_neg(fmaf(f.z, invT, nmi));
+      f.w = exp_neg(fmaf(f.w, invT, nmi));
       s[k] = sum4(f);
     }
-    before_sum(m, invT);
+    before_sum(nmi, invT);
     C = block_sum<BLOCK, NPT>((double)pairwise<NPT>(s), sh, rb);  // entries <= 1
     return 0;
   }
@@ -736,7 +739,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
               load_row<BLOCK, NPT>(Q, a.draft + (ob + r0) * V, V, 0.f);
           }
         },
-        [&](float m, float invT) {
+        [&](float nmi, float invT) {
           if (!shared) {
 #pragma unroll
             for (int r = 0; r < G; ++r) {
@@ -745,7 +748,7 @@ __device__ __forceinline__ int node_setup(const VArgs& a, size_t ob, int node, i
               if (k <= i && i < nk) sh.qt[tri(k, i)] = g[r];
             }
           }
-          if (lane < nk) val = target_entry(lt, m, invT);
+          if (lane < nk) val = target_entry(lt, nmi, invT);
         },
         sh, rb);
     // the table is published by the mass reduction's barrier
