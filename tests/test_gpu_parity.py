@@ -524,11 +524,11 @@ def test_target_exp_within_ulps(V):
     """The vocabulary pass's exp: with the row maximum at 0 (so the argument
     x - max is exact) and the other logits spread over [-87, -16], the mass is
     1 + O(1e-3) and out_probs = exp(x) / mass checks each exp against fp64.
-    The kernel computes 2^(x log2 e) with the product's rounding error carried
-    separately (an FMA recovers it exactly) and added back to first order;
-    its error is the hardware exp2's (about 1 ulp) plus that correction's, so
-    within 2 ulp, and the fp64 division and final rounding of out_probs add
-    half an ulp."""
+    The kernel computes 2^t, t = x log2 e rounded to fp32, times 1 + r with
+    r = x - t ln 2 the exponent's remainder in natural units (two FMAs, ln 2
+    split into an fp32 head and tail); its error is the hardware exp2's
+    (about 1 ulp) plus that correction's, so within 2 ulp, and the fp64
+    division and final rounding of out_probs add half an ulp."""
     rng = np.random.default_rng(11)
     x = np.empty(V, dtype=np.float32)
     x[0] = 0.0
