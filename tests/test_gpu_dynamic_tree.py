@@ -22,8 +22,14 @@ def _dists(rng, n, V, ties=False):
     return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
+# The expansion keeps the keys at or above the k-th largest of its 16 waves'
+# maxima and ranks those; it falls back to k rounds of wave maxima when that
+# threshold is 0 (fewer than k keys, or waves without keys: V = 777, V = 5),
+# when k exceeds the 16 waves (k = 20), or when more keys survive than its
+# list holds (32000 coarse probabilities with thousands tied at the top).
 @pytest.mark.parametrize("B,R,V,k,ties", [(3, 10, 32000, 10, False), (2, 4, 777, 16, True),
-                                          (1, 1, 5, 5, True), (2, 3, 32768, 1, False)])
+                                          (1, 1, 5, 5, True), (2, 3, 32768, 1, False),
+                                          (1, 2, 32000, 10, True), (1, 2, 32000, 20, False)])
 def test_expand_matches_oracle(B, R, V, k, ties):
     rng = np.random.default_rng(V + k)
     q = _dists(rng, B * R, V, ties).reshape(B, R, V)
